@@ -1,0 +1,680 @@
+// api.cpp -- the C ABI of include/dt.h: argument checks, offset and tile
+// tables, bucket planning, work handles and the HSDP pipeline.  Every data
+// movement happens in the HIP kernels (reduce.hip, copy.hip, barrier.hip);
+// this file only validates, plans and enqueues.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "dt.h"
+#include "dt_launch.h"
+
+static_assert(sizeof(dt::ReduceArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+static_assert(sizeof(dt::PieceArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+static_assert(sizeof(dt::GatherArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+static_assert(sizeof(dt::AllToAllArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+static_assert(sizeof(dt::ExchangeArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+static_assert(DT_MAX_RANKS == dt::kMaxRanksHost, "rank limit mismatch");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dt_status fail(dt_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+dt_status check_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return DT_OK;
+    return fail(DT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dtype(dt_dtype d) { return d == DT_FLOAT32 || d == DT_BFLOAT16 || d == DT_INT32; }
+bool valid_op(dt_op o) { return o == DT_SUM || o == DT_MAX || o == DT_MIN; }
+size_t esize_of(dt_dtype d) { return d == DT_BFLOAT16 ? 2 : 4; }
+size_t vec_elems(dt_dtype d) { return 16 / esize_of(d); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+const char* cptr(const void* p) { return static_cast<const char*>(p); }
+
+dt_status check_ranks(int nranks) {
+    if (nranks < 1 || nranks > DT_MAX_RANKS)
+        return fail(DT_ERR_ARG, "nranks=%d outside [1, %d]", nranks, DT_MAX_RANKS);
+    return DT_OK;
+}
+
+template <typename T>
+dt_status check_ptr_array(T const* arr, int n, const char* name) {
+    if (arr == nullptr) return fail(DT_ERR_ARG, "%s is NULL", name);
+    for (int i = 0; i < n; i++)
+        if (arr[i] == nullptr) return fail(DT_ERR_ARG, "%s[%d] is NULL", name, i);
+    return DT_OK;
+}
+
+// Wall-clock ticks per nanosecond budget on the current device.
+uint64_t timeout_ticks(uint64_t timeout_ns) {
+    static std::mutex mu;
+    static int rate_khz[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int rate = 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        rate = rate_khz[dev];
+        if (rate == 0) {
+            if (hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, dev) != hipSuccess || rate <= 0)
+                rate = 100000;  // 100 MHz, the usual constant-rate counter
+            rate_khz[dev] = rate;
+        }
+    }
+    if (timeout_ns == 0) timeout_ns = 10ull * 1000 * 1000 * 1000;
+    const long double ticks = (long double)timeout_ns * (long double)rate / 1.0e6L;
+    return ticks > 1.8e19L ? UINT64_MAX : (uint64_t)ticks + 1;
+}
+
+// ------------------------------------------------------------ reductions --
+// Validated AllReduce over one contiguous range per rank.
+dt_status allreduce_impl(const void* const* send, void* const* recv, int nranks, size_t count, dt_dtype dtype,
+                         dt_op op, hipStream_t stream) {
+    dt::ReduceArgs a = {};
+    bool vec = true;
+    for (int r = 0; r < nranks; r++) {
+        a.src[r] = send[r];
+        a.dst[r] = recv[r];
+        vec = vec && aligned16(send[r]) && aligned16(recv[r]);
+    }
+    a.nranks = nranks;
+    a.rs = 0;
+    const size_t v = vec_elems(dtype);
+    size_t body = 0;
+    if (vec) {
+        a.first = 0;
+        a.count = count / v;
+        body = a.count * v;
+        if (a.count) {
+            dt_status st = check_hip(dt::launch_reduce_vec(a, dtype, op, stream), "allreduce launch");
+            if (st != DT_OK) return st;
+        }
+    }
+    if (body < count) {
+        a.first = body;
+        a.count = count - body;
+        return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "allreduce (element path) launch");
+    }
+    return DT_OK;
+}
+
+// ---------------------------------------------------------- bucket plan --
+struct Piece {
+    int tensor;
+    int bucket;
+    size_t offset, length, bucket_pos;
+};
+
+std::vector<Piece> plan_buckets(const size_t* numels, int ntensors, size_t per_bucket, size_t* nbuckets) {
+    std::vector<Piece> out;
+    size_t pos = 0;  // position in the flattened concatenation
+    for (int t = 0; t < ntensors; t++) {
+        size_t off = 0;
+        while (off < numels[t]) {
+            const size_t bucket = pos / per_bucket;
+            const size_t in_bucket = pos - bucket * per_bucket;
+            const size_t len = std::min(numels[t] - off, per_bucket - in_bucket);
+            out.push_back(Piece{t, int(bucket), off, len, in_bucket});
+            off += len;
+            pos += len;
+        }
+    }
+    *nbuckets = (pos + per_bucket - 1) / per_bucket;
+    return out;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dt_status_string(dt_status st) {
+    switch (st) {
+        case DT_OK: return "DT_OK";
+        case DT_ERR_ARG: return "DT_ERR_ARG: invalid argument";
+        case DT_ERR_UNSUPPORTED: return "DT_ERR_UNSUPPORTED: unsupported dtype/op combination";
+        case DT_ERR_HIP: return "DT_ERR_HIP: HIP runtime error";
+        case DT_ERR_TIMEOUT: return "DT_ERR_TIMEOUT: barrier wait exceeded its budget";
+    }
+    return "unknown dt_status";
+}
+
+const char* dt_last_error(void) { return g_last_error.c_str(); }
+
+const char* dt_version(void) { return "dtcoll 0.1 (gfx950)"; }
+
+dt_status dt_allreduce(const void* const* send, void* const* recv, int nranks, size_t count, dt_dtype dtype,
+                       dt_op op, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if (!valid_dtype(dtype) || !valid_op(op)) return fail(DT_ERR_ARG, "bad dtype %d or op %d", dtype, op);
+    if (send == nullptr || recv == nullptr) return fail(DT_ERR_ARG, "send/recv array is NULL");
+    if (count == 0) return DT_OK;  // empty buffers may carry NULL pointers
+    if ((st = check_ptr_array(send, nranks, "send")) != DT_OK) return st;
+    if ((st = check_ptr_array(recv, nranks, "recv")) != DT_OK) return st;
+    for (int q = 0; q < nranks; q++)
+        for (int r = 0; r < nranks; r++) {
+            if (r != q && recv[q] == send[r])
+                return fail(DT_ERR_ARG, "recv[%d] aliases send[%d]; only in place (recv[r] == send[r]) is allowed", q,
+                            r);
+            if (r != q && recv[q] == recv[r]) return fail(DT_ERR_ARG, "recv[%d] equals recv[%d]", q, r);
+        }
+    return allreduce_impl(send, recv, nranks, count, dtype, op, stream);
+}
+
+dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nranks, size_t recvcount,
+                            dt_dtype dtype, dt_op op, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if (!valid_dtype(dtype) || !valid_op(op)) return fail(DT_ERR_ARG, "bad dtype %d or op %d", dtype, op);
+    if (send == nullptr || recv == nullptr) return fail(DT_ERR_ARG, "send/recv array is NULL");
+    if (recvcount == 0) return DT_OK;  // empty buffers may carry NULL pointers
+    if ((st = check_ptr_array(send, nranks, "send")) != DT_OK) return st;
+    if ((st = check_ptr_array(recv, nranks, "recv")) != DT_OK) return st;
+    for (int q = 0; q < nranks; q++)
+        for (int r = 0; r < nranks; r++) {
+            if (recv[q] == send[r]) return fail(DT_ERR_ARG, "recv[%d] aliases send[%d]", q, r);
+            if (r != q && recv[q] == recv[r]) return fail(DT_ERR_ARG, "recv[%d] equals recv[%d]", q, r);
+        }
+    dt::ReduceArgs a = {};
+    bool vec = recvcount % vec_elems(dtype) == 0;
+    for (int r = 0; r < nranks; r++) {
+        a.src[r] = send[r];
+        a.dst[r] = recv[r];
+        vec = vec && aligned16(send[r]) && aligned16(recv[r]);
+    }
+    a.nranks = nranks;
+    a.rs = 1;
+    a.chunk_elems = recvcount;
+    if (vec) {
+        a.first = 0;
+        a.count = recvcount / vec_elems(dtype);
+        return check_hip(dt::launch_reduce_vec(a, dtype, op, stream), "reduce_scatter launch");
+    }
+    a.first = 0;
+    a.count = recvcount;
+    return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "reduce_scatter (element path) launch");
+}
+
+dt_status dt_all_gather(const void* const* send, void* const* recv, int nranks, const size_t* sendcounts,
+                        size_t equal_count, dt_dtype dtype, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if (!valid_dtype(dtype)) return fail(DT_ERR_ARG, "bad dtype %d", dtype);
+    if (send == nullptr || recv == nullptr) return fail(DT_ERR_ARG, "send/recv array is NULL");
+    const size_t es = esize_of(dtype);
+    size_t total = 0;
+    for (int r = 0; r < nranks; r++) {
+        const size_t c = sendcounts ? sendcounts[r] : equal_count;
+        if (c > (size_t(1) << 40)) return fail(DT_ERR_ARG, "sendcount[%d]=%zu too large", r, c);
+        if (c > 0 && send[r] == nullptr) return fail(DT_ERR_ARG, "send[%d] is NULL", r);
+        total += c;
+    }
+    if (total == 0) return DT_OK;  // nothing to gather; empty buffers may be NULL
+    if ((st = check_ptr_array(recv, nranks, "recv")) != DT_OK) return st;
+    dt::GatherArgs a = {};
+    a.nranks = nranks;
+    uint64_t off = 0, tiles = 0;
+    bool dst_aligned = true;
+    for (int q = 0; q < nranks; q++) dst_aligned = dst_aligned && aligned16(recv[q]);
+    for (int r = 0; r < nranks; r++) {
+        const size_t c = sendcounts ? sendcounts[r] : equal_count;
+        a.src[r] = send[r];
+        a.dst[r] = recv[r];
+        a.bytes[r] = c * es;
+        a.offset[r] = off;
+        a.tile_start[r] = uint32_t(tiles);
+        if (dst_aligned && aligned16(send[r]) && off % 16 == 0) a.aligned |= 1u << r;  // NULL (empty) is aligned
+        off += c * es;
+        tiles += (c * es + dt::kCopyTileBytes - 1) / dt::kCopyTileBytes;
+        if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "all_gather too large for one launch");
+    }
+    a.tile_start[nranks] = uint32_t(tiles);
+    // in place (NCCL-style) is send[r] == recv[r] + offset[r]; any other alias is refused
+    for (int q = 0; q < nranks; q++)
+        for (int r = 0; r < nranks; r++) {
+            if (a.bytes[r] && cptr(send[r]) >= cptr(recv[q]) && cptr(send[r]) < cptr(recv[q]) + off &&
+                !(q == r && cptr(send[r]) == cptr(recv[r]) + a.offset[r]))
+                return fail(DT_ERR_ARG, "send[%d] lies inside recv[%d] other than at its own slot", r, q);
+            if (r != q && recv[q] == recv[r]) return fail(DT_ERR_ARG, "recv[%d] equals recv[%d]", q, r);
+        }
+    if (tiles == 0) return DT_OK;
+    return check_hip(dt::launch_gather(a, uint32_t(tiles), stream), "all_gather launch");
+}
+
+dt_status dt_all_to_all(const void* const* send, void* const* recv, int nranks, const size_t* splits,
+                        dt_dtype dtype, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if (!valid_dtype(dtype)) return fail(DT_ERR_ARG, "bad dtype %d", dtype);
+    if (splits == nullptr) return fail(DT_ERR_ARG, "splits is NULL");
+    if (send == nullptr || recv == nullptr) return fail(DT_ERR_ARG, "send/recv array is NULL");
+    // a rank that sends (receives) nothing may pass NULL for its input (output)
+    std::vector<size_t> row(nranks, 0), col(nranks, 0);
+    for (int i = 0; i < nranks; i++)
+        for (int j = 0; j < nranks; j++) {
+            row[i] += splits[i * nranks + j];
+            col[j] += splits[i * nranks + j];
+        }
+    for (int r = 0; r < nranks; r++) {
+        if (row[r] > 0 && send[r] == nullptr) return fail(DT_ERR_ARG, "send[%d] is NULL", r);
+        if (col[r] > 0 && recv[r] == nullptr) return fail(DT_ERR_ARG, "recv[%d] is NULL", r);
+    }
+    for (int q = 0; q < nranks; q++)
+        for (int r = 0; r < nranks; r++) {
+            if (col[q] > 0 && row[r] > 0 && recv[q] == send[r])
+                return fail(DT_ERR_ARG, "recv[%d] aliases send[%d]", q, r);
+            if (r != q && col[q] > 0 && col[r] > 0 && recv[q] == recv[r])
+                return fail(DT_ERR_ARG, "recv[%d] equals recv[%d]", q, r);
+        }
+    const size_t es = esize_of(dtype);
+    dt::AllToAllArgs a = {};
+    a.nranks = nranks;
+    uint64_t tiles = 0;
+    for (int r = 0; r < nranks; r++) {
+        a.src[r] = send[r];
+        a.dst[r] = recv[r];
+    }
+    std::vector<uint64_t> recv_off(nranks, 0);  // running byte offsets down each column
+    for (int i = 0; i < nranks; i++) {
+        for (int j = 0; j < nranks; j++) {
+            const int s = i * nranks + j;
+            if (splits[s] > (size_t(1) << 40)) return fail(DT_ERR_ARG, "splits[%d]=%zu too large", s, splits[s]);
+            a.split[s] = splits[s] * es;
+            a.tile_start[s] = uint32_t(tiles);
+            tiles += (a.split[s] + dt::kCopyTileBytes - 1) / dt::kCopyTileBytes;
+            if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "all_to_all too large for one launch");
+        }
+    }
+    a.tile_start[nranks * nranks] = uint32_t(tiles);
+    // send offsets run along rows, receive offsets down columns
+    for (int i = 0; i < nranks; i++) {
+        uint64_t so = 0;
+        for (int j = 0; j < nranks; j++) {
+            const int s = i * nranks + j;
+            const uint64_t ro = recv_off[j];
+            if (aligned16(cptr(send[i]) + so) && aligned16(cptr(recv[j]) + ro)) a.aligned[s >> 5] |= 1u << (s & 31);
+            so += a.split[s];
+            recv_off[j] += a.split[s];
+        }
+    }
+    if (tiles == 0) return DT_OK;
+    return check_hip(dt::launch_all_to_all(a, uint32_t(tiles), stream), "all_to_all launch");
+}
+
+dt_status dt_bucket_plan(const size_t* numels, int ntensors, size_t elem_size, size_t bucket_bytes, dt_piece* pieces,
+                         size_t capacity, size_t* npieces, size_t* nbuckets) {
+    g_last_error.clear();
+    if (ntensors < 0 || (ntensors > 0 && numels == nullptr) || npieces == nullptr || nbuckets == nullptr)
+        return fail(DT_ERR_ARG, "bad arguments to dt_bucket_plan");
+    if (elem_size == 0 || bucket_bytes < elem_size) return fail(DT_ERR_ARG, "bucket_bytes smaller than one element");
+    if (capacity > 0 && pieces == nullptr) return fail(DT_ERR_ARG, "pieces is NULL");
+    size_t nb = 0;
+    std::vector<Piece> plan = plan_buckets(numels, ntensors, bucket_bytes / elem_size, &nb);
+    for (size_t i = 0; i < plan.size() && i < capacity; i++)
+        pieces[i] = dt_piece{plan[i].tensor, plan[i].bucket, plan[i].offset, plan[i].length, plan[i].bucket_pos};
+    *npieces = plan.size();
+    *nbuckets = nb;
+    return DT_OK;
+}
+
+dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int ntensors, int nranks, size_t bucket_bytes,
+                              void* const* bucket_ws, dt_dtype dtype, dt_op op, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if (!valid_dtype(dtype) || !valid_op(op)) return fail(DT_ERR_ARG, "bad dtype %d or op %d", dtype, op);
+    if (ntensors < 0) return fail(DT_ERR_ARG, "ntensors=%d", ntensors);
+    if (ntensors == 0) return DT_OK;
+    if (numels == nullptr) return fail(DT_ERR_ARG, "numels is NULL");
+    if (bucket_bytes == 0 || bucket_bytes % 16 != 0)
+        return fail(DT_ERR_ARG, "bucket_bytes=%zu must be a positive multiple of 16", bucket_bytes);
+    if ((st = check_ptr_array(grads, nranks * ntensors, "grads")) != DT_OK) return st;
+    if (bucket_ws && (st = check_ptr_array(bucket_ws, nranks, "bucket_ws")) != DT_OK) return st;
+    const size_t es = esize_of(dtype);
+    size_t nbuckets = 0;
+    const std::vector<Piece> plan = plan_buckets(numels, ntensors, bucket_bytes / es, &nbuckets);
+    const int per_launch = std::min(dt::kMaxPieces, dt::kPiecePtrs / nranks);
+    bool ws_aligned = true;
+    if (bucket_ws)
+        for (int r = 0; r < nranks; r++) ws_aligned = ws_aligned && aligned16(bucket_ws[r]);
+
+    size_t i = 0;
+    while (i < plan.size()) {
+        const int bucket = plan[i].bucket;
+        size_t end = i;
+        while (end < plan.size() && plan[end].bucket == bucket) end++;
+        size_t bucket_len = 0;
+        for (size_t k = i; k < end; k++) bucket_len = std::max(bucket_len, plan[k].bucket_pos + plan[k].length);
+        // groups of pieces that fit one argument block
+        std::vector<dt::PieceArgs> groups;
+        for (size_t g0 = i; g0 < end; g0 += per_launch) {
+            dt::PieceArgs a = {};
+            a.nranks = nranks;
+            a.npieces = int(std::min<size_t>(per_launch, end - g0));
+            uint64_t tiles = 0;
+            for (int k = 0; k < a.npieces; k++) {
+                const Piece& p = plan[g0 + k];
+                bool al = true;
+                for (int r = 0; r < nranks; r++) {
+                    char* base = static_cast<char*>(grads[size_t(r) * ntensors + p.tensor]) + p.offset * es;
+                    a.ptr[k * nranks + r] = base;
+                    al = al && aligned16(base);
+                }
+                if (bucket_ws) al = al && ws_aligned && (p.bucket_pos * es) % 16 == 0;
+                if (al) a.aligned |= 1u << k;
+                a.len[k] = p.length;
+                a.wpos[k] = p.bucket_pos;
+                a.tile_start[k] = uint32_t(tiles);
+                tiles += (p.length * es + dt::kPieceTileVecs * 16 - 1) / (dt::kPieceTileVecs * 16);
+                if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "bucket too large for one launch");
+            }
+            a.tile_start[a.npieces] = uint32_t(tiles);
+            if (bucket_ws)
+                for (int r = 0; r < nranks; r++) a.ws[r] = bucket_ws[r];
+            groups.push_back(a);
+        }
+        if (bucket_ws) {
+            for (const auto& a : groups)
+                if ((st = check_hip(dt::launch_copy_pieces(a, int(es), 1, stream), "bucket flatten launch")) != DT_OK)
+                    return st;
+            if ((st = allreduce_impl(bucket_ws, bucket_ws, nranks, bucket_len, dtype, op, stream)) != DT_OK) return st;
+            for (const auto& a : groups)
+                if ((st = check_hip(dt::launch_copy_pieces(a, int(es), 0, stream), "bucket unflatten launch")) != DT_OK)
+                    return st;
+        } else {
+            for (const auto& a : groups)
+                if ((st = check_hip(dt::launch_reduce_pieces(a, dtype, op, stream), "bucket reduce launch")) != DT_OK)
+                    return st;
+        }
+        i = end;
+    }
+    return DT_OK;
+}
+
+dt_status dt_barrier(int32_t* const* windows, int nranks, int32_t first_generation, int32_t generations,
+                     int32_t* status_dev, uint64_t timeout_ns, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if ((st = check_ptr_array(windows, nranks, "windows")) != DT_OK) return st;
+    if (status_dev == nullptr) return fail(DT_ERR_ARG, "status_dev is NULL");
+    if (first_generation < 1 || generations < 0 || int64_t(first_generation) + generations - 1 > INT32_MAX)
+        return fail(DT_ERR_ARG, "generations %d..%d out of range", first_generation, first_generation + generations - 1);
+    if (generations == 0) return DT_OK;
+    dt::BarrierArgs a = {};
+    for (int r = 0; r < nranks; r++) a.win[r] = windows[r];
+    a.status = status_dev;
+    a.timeout_ticks = timeout_ticks(timeout_ns);
+    a.nranks = nranks;
+    a.first_generation = first_generation;
+    a.generations = generations;
+    return check_hip(dt::launch_barrier(a, stream), "barrier cooperative launch");
+}
+
+dt_status dt_barrier_exchange(const void* const* src, void* const* stage, void* const* dst, size_t nbytes,
+                              int32_t* const* windows, int nranks, int32_t generation, int32_t* status_dev,
+                              uint64_t timeout_ns, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if ((st = check_ptr_array(windows, nranks, "windows")) != DT_OK) return st;
+    if ((st = check_ptr_array(src, nranks, "src")) != DT_OK) return st;
+    if ((st = check_ptr_array(stage, nranks, "stage")) != DT_OK) return st;
+    if ((st = check_ptr_array(dst, nranks, "dst")) != DT_OK) return st;
+    if (status_dev == nullptr) return fail(DT_ERR_ARG, "status_dev is NULL");
+    if (generation < 1) return fail(DT_ERR_ARG, "generation %d must be >= 1", generation);
+    dt::ExchangeArgs a = {};
+    for (int r = 0; r < nranks; r++) {
+        a.bar.win[r] = windows[r];
+        a.src[r] = src[r];
+        a.stage[r] = stage[r];
+        a.dst[r] = dst[r];
+    }
+    a.bar.status = status_dev;
+    a.bar.timeout_ticks = timeout_ticks(timeout_ns);
+    a.bar.nranks = nranks;
+    a.bar.first_generation = generation;
+    a.bar.generations = 1;
+    a.nbytes = nbytes;
+    return check_hip(dt::launch_exchange(a, stream), "barrier exchange cooperative launch");
+}
+
+// ------------------------------------------------------------ work handles --
+struct dt_work {
+    hipEvent_t start = nullptr;
+    hipEvent_t end = nullptr;
+};
+
+dt_status dt_work_begin(hipStream_t producer, hipStream_t comm, dt_work** work) {
+    g_last_error.clear();
+    if (work == nullptr) return fail(DT_ERR_ARG, "work is NULL");
+    dt_work* w = new dt_work();
+    dt_status st = check_hip(hipEventCreateWithFlags(&w->start, hipEventDisableTiming), "hipEventCreate");
+    if (st == DT_OK) st = check_hip(hipEventCreateWithFlags(&w->end, hipEventDisableTiming), "hipEventCreate");
+    if (st == DT_OK) st = check_hip(hipEventRecord(w->start, producer), "hipEventRecord(producer)");
+    if (st == DT_OK) st = check_hip(hipStreamWaitEvent(comm, w->start, 0), "hipStreamWaitEvent(comm)");
+    if (st != DT_OK) {
+        dt_work_free(w);
+        return st;
+    }
+    *work = w;
+    return DT_OK;
+}
+
+dt_status dt_work_end(dt_work* work, hipStream_t comm) {
+    g_last_error.clear();
+    if (work == nullptr) return fail(DT_ERR_ARG, "work is NULL");
+    return check_hip(hipEventRecord(work->end, comm), "hipEventRecord(comm)");
+}
+
+dt_status dt_work_wait(dt_work* work, hipStream_t consumer) {
+    g_last_error.clear();
+    if (work == nullptr) return fail(DT_ERR_ARG, "work is NULL");
+    return check_hip(hipStreamWaitEvent(consumer, work->end, 0), "hipStreamWaitEvent(consumer)");
+}
+
+int dt_work_query(dt_work* work) {
+    if (work == nullptr) return -1;
+    hipError_t e = hipEventQuery(work->end);
+    if (e == hipSuccess) return 1;
+    if (e == hipErrorNotReady) return 0;
+    g_last_error = hipGetErrorString(e);
+    return -1;
+}
+
+dt_status dt_work_free(dt_work* work) {
+    if (work == nullptr) return DT_OK;
+    if (work->start) (void)hipEventDestroy(work->start);
+    if (work->end) (void)hipEventDestroy(work->end);
+    delete work;
+    return DT_OK;
+}
+
+// ---------------------------------------------------------- HSDP pipeline --
+struct dt_hsdp {
+    int replicate = 1, shard = 1;
+    size_t bucket_bytes = 0;
+    dt_dtype dtype = DT_BFLOAT16;
+    dt_op op = DT_SUM;
+    hipStream_t rs_stream = nullptr, ar_stream = nullptr;
+    hipEvent_t produced = nullptr;   // producer stream position at post_backward
+    hipEvent_t rs_done[2] = {nullptr, nullptr};  // ping-pong: previous / current layer's RS end
+    int prev_slot = 0;
+    std::vector<hipEvent_t> ar_done;  // one per issued fused AllReduce
+    std::vector<hipEvent_t> spare;
+    bool has_prev = false;
+    std::vector<void*> prev_fused;    // previous layer's fused buffers (caller-owned)
+    size_t prev_total = 0;            // elements per fused buffer
+};
+
+namespace {
+
+// "wait prev RS": the AllReduce stream waits for the previous layer's
+// ReduceScatter.  Queued before the current layer re-records anything.
+dt_status hsdp_wait_prev_rs(dt_hsdp* h) {
+    return check_hip(hipStreamWaitEvent(h->ar_stream, h->rs_done[h->prev_slot], 0), "AR stream waits prev RS");
+}
+
+// "issue prev AR": the previous layer's fused buffers, AllReduced in place
+// inside each replicate group {j, shard+j, ...}, bucket by bucket.
+dt_status hsdp_issue_prev_allreduce(dt_hsdp* h) {
+    dt_status st;
+    const size_t es = esize_of(h->dtype);
+    const size_t per_bucket = h->bucket_bytes / es;
+    std::vector<const void*> src(h->replicate);
+    std::vector<void*> dst(h->replicate);
+    for (size_t start = 0; start < h->prev_total; start += per_bucket) {
+        const size_t len = std::min(per_bucket, h->prev_total - start);
+        for (int j = 0; j < h->shard; j++) {
+            for (int i = 0; i < h->replicate; i++) {
+                dst[i] = static_cast<char*>(h->prev_fused[size_t(i) * h->shard + j]) + start * es;
+                src[i] = dst[i];
+            }
+            if ((st = allreduce_impl(src.data(), dst.data(), h->replicate, len, h->dtype, h->op, h->ar_stream)) != DT_OK)
+                return st;
+        }
+    }
+    hipEvent_t ev = nullptr;
+    if (!h->spare.empty()) {
+        ev = h->spare.back();
+        h->spare.pop_back();
+    } else if ((st = check_hip(hipEventCreateWithFlags(&ev, hipEventDisableTiming), "hipEventCreate")) != DT_OK) {
+        return st;
+    }
+    h->ar_done.push_back(ev);
+    h->has_prev = false;
+    return check_hip(hipEventRecord(ev, h->ar_stream), "record AR done");
+}
+
+}  // namespace
+
+dt_status dt_hsdp_create(int replicate, int shard, size_t bucket_bytes, dt_dtype dtype, dt_op op, hipStream_t rs_stream,
+                         hipStream_t ar_stream, dt_hsdp** handle) {
+    g_last_error.clear();
+    if (handle == nullptr) return fail(DT_ERR_ARG, "handle is NULL");
+    if (replicate < 1 || shard < 1 || replicate * shard > DT_MAX_RANKS)
+        return fail(DT_ERR_ARG, "mesh %d x %d outside 1..%d ranks", replicate, shard, DT_MAX_RANKS);
+    if (!valid_dtype(dtype) || !valid_op(op)) return fail(DT_ERR_ARG, "bad dtype %d or op %d", dtype, op);
+    if (bucket_bytes == 0 || bucket_bytes % 16 != 0)
+        return fail(DT_ERR_ARG, "bucket_bytes=%zu must be a positive multiple of 16", bucket_bytes);
+    dt_hsdp* h = new dt_hsdp();
+    h->replicate = replicate;
+    h->shard = shard;
+    h->bucket_bytes = bucket_bytes;
+    h->dtype = dtype;
+    h->op = op;
+    h->rs_stream = rs_stream;
+    h->ar_stream = ar_stream;
+    dt_status st = check_hip(hipEventCreateWithFlags(&h->produced, hipEventDisableTiming), "hipEventCreate");
+    for (int k = 0; k < 2 && st == DT_OK; k++)
+        st = check_hip(hipEventCreateWithFlags(&h->rs_done[k], hipEventDisableTiming), "hipEventCreate");
+    if (st != DT_OK) {
+        dt_hsdp_destroy(h);
+        return st;
+    }
+    *handle = h;
+    return DT_OK;
+}
+
+dt_status dt_hsdp_post_backward(dt_hsdp* h, const void* const* grads, const size_t* numels, int ntensors,
+                                void* const* fused, hipStream_t producer) {
+    g_last_error.clear();
+    if (h == nullptr) return fail(DT_ERR_ARG, "handle is NULL");
+    const int nranks = h->replicate * h->shard;
+    dt_status st;
+    if (ntensors < 1 || numels == nullptr) return fail(DT_ERR_ARG, "no tensors");
+    if ((st = check_ptr_array(grads, nranks * ntensors, "grads")) != DT_OK) return st;
+    if ((st = check_ptr_array(fused, nranks, "fused")) != DT_OK) return st;
+    for (int t = 0; t < ntensors; t++)
+        if (numels[t] % size_t(h->shard) != 0)
+            return fail(DT_ERR_ARG, "numels[%d]=%zu not divisible by shard=%d", t, numels[t], h->shard);
+    const size_t es = esize_of(h->dtype);
+
+    // 1. wait prev RS
+    if (h->has_prev && (st = hsdp_wait_prev_rs(h)) != DT_OK) return st;
+    // 2. issue this layer's ReduceScatter, after everything the producer
+    //    queued: tensor t of shard group i lands in fused[r] at offset `at`
+    if ((st = check_hip(hipEventRecord(h->produced, producer), "record producer")) != DT_OK) return st;
+    if ((st = check_hip(hipStreamWaitEvent(h->rs_stream, h->produced, 0), "RS stream waits producer")) != DT_OK)
+        return st;
+    std::vector<const void*> src(h->shard);
+    std::vector<void*> dst(h->shard);
+    size_t at = 0;
+    for (int t = 0; t < ntensors; t++) {
+        const size_t m = numels[t] / size_t(h->shard);
+        for (int i = 0; i < h->replicate; i++) {
+            for (int j = 0; j < h->shard; j++) {
+                const int r = i * h->shard + j;
+                src[j] = grads[size_t(r) * ntensors + t];
+                dst[j] = static_cast<char*>(fused[r]) + at * es;
+            }
+            if ((st = dt_reduce_scatter(src.data(), dst.data(), h->shard, m, h->dtype, h->op, h->rs_stream)) != DT_OK)
+                return st;
+        }
+        at += m;
+    }
+    const int cur_slot = h->prev_slot ^ 1;
+    if ((st = check_hip(hipEventRecord(h->rs_done[cur_slot], h->rs_stream), "record RS done")) != DT_OK) return st;
+    // 3. issue the previous layer's fused AllReduce (its wait is queued above)
+    if (h->has_prev && (st = hsdp_issue_prev_allreduce(h)) != DT_OK) return st;
+    // this layer becomes the previous one
+    h->prev_slot = cur_slot;
+    h->prev_fused.assign(fused, fused + nranks);
+    h->prev_total = at;
+    h->has_prev = true;
+    return DT_OK;
+}
+
+dt_status dt_hsdp_finish(dt_hsdp* h, hipStream_t consumer) {
+    g_last_error.clear();
+    if (h == nullptr) return fail(DT_ERR_ARG, "handle is NULL");
+    dt_status st;
+    if (h->has_prev) {  // drain: the last layer's RS, then its fused AllReduce
+        if ((st = hsdp_wait_prev_rs(h)) != DT_OK) return st;
+        if ((st = hsdp_issue_prev_allreduce(h)) != DT_OK) return st;
+    }
+    for (hipEvent_t ev : h->ar_done) {
+        if ((st = check_hip(hipStreamWaitEvent(consumer, ev, 0), "consumer waits AR")) != DT_OK) return st;
+        h->spare.push_back(ev);
+    }
+    h->ar_done.clear();
+    return DT_OK;
+}
+
+dt_status dt_hsdp_destroy(dt_hsdp* h) {
+    if (h == nullptr) return DT_OK;
+    for (hipEvent_t ev : h->ar_done) {
+        (void)hipEventSynchronize(ev);
+        (void)hipEventDestroy(ev);
+    }
+    for (hipEvent_t ev : h->spare) {
+        (void)hipEventSynchronize(ev);
+        (void)hipEventDestroy(ev);
+    }
+    if (h->produced) (void)hipEventDestroy(h->produced);
+    for (hipEvent_t ev : h->rs_done)
+        if (ev) (void)hipEventDestroy(ev);
+    delete h;
+    return DT_OK;
+}
+
+}  // extern "C"

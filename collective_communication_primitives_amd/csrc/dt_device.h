@@ -1,0 +1,160 @@
+// dt_device.h -- device-side building blocks shared by the HIP kernels:
+// 16-byte vector memory access, bf16 <-> fp32 conversion and the element
+// operators of the rank fold.
+//
+// The fold follows the DTorch same-device AllReduce (page "集合通信组件",
+// sec. 2.3): start from rank 0's element and combine ranks 1..P-1 in rank
+// order.  Accumulation is fp32 for fp32 and bf16 data (one round to nearest
+// even at the end) and int32 (wrapping) for int32 data.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dt {
+
+enum : int { kF32 = 0, kBF16 = 1, kI32 = 2 };
+enum : int { kSum = 0, kMax = 1, kMin = 2 };
+
+constexpr int kMaxRanks = 16;
+constexpr int kBlock = 256;  // threads per workgroup: four 64-wide waves
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- memory --
+// Streaming data is touched exactly once per launch, so loads and stores
+// carry the non-temporal hint: it keeps the one-pass traffic from evicting
+// useful lines from L2 and the Infinity Cache.
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// ------------------------------------------------------------------- bf16 --
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_at(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// fp32 -> bf16 bits, round to nearest with ties to even, computed on the
+// integer pattern; a NaN keeps its sign and top payload bits and gets the
+// quiet bit; overflow to infinity comes out of the carry.
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    uint32_t quiet = (u >> 16) | 0x40u;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? quiet : rounded;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return to_bf16(lo) | (to_bf16(hi) << 16);
+}
+
+// -------------------------------------------------------------- operators --
+// Max/min: strict compare, the accumulator wins ties (earlier rank, also
+// between +0 and -0); the first NaN met is kept.
+template <int OP>
+__device__ __forceinline__ float combine(float a, float v) {
+    if constexpr (OP == kSum) {
+        return a + v;
+    } else {
+        const bool a_nan = a != a;
+        const bool v_nan = v != v;
+        const bool take = (OP == kMax) ? (v > a) : (v < a);
+        return a_nan ? a : ((v_nan || take) ? v : a);
+    }
+}
+
+template <int OP>
+__device__ __forceinline__ int32_t combine(int32_t a, int32_t v) {
+    if constexpr (OP == kSum) {
+        return int32_t(uint32_t(a) + uint32_t(v));
+    } else if constexpr (OP == kMax) {
+        return v > a ? v : a;
+    } else {
+        return v < a ? v : a;
+    }
+}
+
+// Elements per 16-byte vector.
+template <int DT>
+struct Elems {
+    static constexpr int value = DT == kBF16 ? 8 : 4;
+};
+
+template <int DT>
+constexpr size_t elem_bytes() { return DT == kBF16 ? 2 : 4; }
+
+// Fold P vectors (x[0..P-1]) element-wise in rank order.  NR = live ranks
+// (runtime, NR <= P); with NR == P the branches fold away.
+template <int DT, int OP, int P>
+__device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[P], int nr) {
+    u32x4 out;
+    if constexpr (DT == kBF16) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            acc[2 * i] = bf16_lo(x[0][i]);
+            acc[2 * i + 1] = bf16_hi(x[0][i]);
+        }
+#pragma unroll
+        for (int r = 1; r < P; r++) {
+            if (r < nr) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    acc[2 * i] = combine<OP>(acc[2 * i], bf16_lo(x[r][i]));
+                    acc[2 * i + 1] = combine<OP>(acc[2 * i + 1], bf16_hi(x[r][i]));
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) out[i] = pack_bf16(acc[2 * i], acc[2 * i + 1]);
+    } else if constexpr (DT == kF32) {
+        float acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc[i] = __uint_as_float(x[0][i]);
+#pragma unroll
+        for (int r = 1; r < P; r++) {
+            if (r < nr) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[i] = combine<OP>(acc[i], __uint_as_float(x[r][i]));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) out[i] = __float_as_uint(acc[i]);
+    } else {
+        int32_t acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc[i] = int32_t(x[0][i]);
+#pragma unroll
+        for (int r = 1; r < P; r++) {
+            if (r < nr) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[i] = combine<OP>(acc[i], int32_t(x[r][i]));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) out[i] = uint32_t(acc[i]);
+    }
+    return out;
+}
+
+// One element: fold element e of every live rank buffer (element-wise path).
+template <int DT, int OP>
+__device__ __forceinline__ void fold_elem(const void* const* src, int nr, size_t e, void* dst, size_t de) {
+    if constexpr (DT == kI32) {
+        int32_t acc = static_cast<const int32_t*>(src[0])[e];
+        for (int r = 1; r < nr; r++) acc = combine<OP>(acc, static_cast<const int32_t*>(src[r])[e]);
+        static_cast<int32_t*>(dst)[de] = acc;
+    } else if constexpr (DT == kF32) {
+        float acc = static_cast<const float*>(src[0])[e];
+        for (int r = 1; r < nr; r++) acc = combine<OP>(acc, static_cast<const float*>(src[r])[e]);
+        static_cast<float*>(dst)[de] = acc;
+    } else {
+        float acc = bf16_at(static_cast<const uint16_t*>(src[0])[e]);
+        for (int r = 1; r < nr; r++) acc = combine<OP>(acc, bf16_at(static_cast<const uint16_t*>(src[r])[e]));
+        static_cast<uint16_t*>(dst)[de] = uint16_t(to_bf16(acc));
+    }
+}
+
+}  // namespace dt

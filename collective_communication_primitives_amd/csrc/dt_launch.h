@@ -1,0 +1,94 @@
+// dt_launch.h -- kernel argument blocks and launchers (host side), shared by
+// the kernel sources and the C ABI in api.cpp.  Every argument block is
+// passed by value and stays below 4 KiB, so no device-side tables are
+// needed and the library allocates nothing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dt {
+
+constexpr int kMaxRanksHost = 16;
+
+// AllReduce / ReduceScatter over one contiguous range per rank.
+struct ReduceArgs {
+    const void* src[kMaxRanksHost];
+    void* dst[kMaxRanksHost];
+    uint64_t first;        // first element handled by this launch (element path)
+    uint64_t count;        // elements per chunk handled by this launch
+    uint64_t chunk_elems;  // ReduceScatter: elements per output chunk
+    int nranks;
+    int rs;                // 1: ReduceScatter (grid.y = chunk), 0: AllReduce
+};
+
+// Multi-tensor pieces of one bucket.  Piece k of rank r starts at
+// ptr[k*nranks + r]; ws[r] + wpos[k] is its place in rank r's bucket buffer.
+constexpr int kPiecePtrs = 320;
+constexpr int kMaxPieces = 32;
+struct PieceArgs {
+    void* ptr[kPiecePtrs];
+    void* ws[kMaxRanksHost];
+    uint64_t len[kMaxPieces];
+    uint64_t wpos[kMaxPieces];
+    uint32_t tile_start[kMaxPieces + 1];
+    uint32_t aligned;      // bit k: piece k may use 16-byte vectors
+    int npieces;
+    int nranks;
+};
+
+// AllGather: rank r's bytes [0, bytes[r]) land at offset[r] of every output.
+struct GatherArgs {
+    const void* src[kMaxRanksHost];
+    void* dst[kMaxRanksHost];
+    uint64_t bytes[kMaxRanksHost];
+    uint64_t offset[kMaxRanksHost];
+    uint32_t tile_start[kMaxRanksHost + 1];
+    uint32_t aligned;      // bit r: rank r's piece may use 16-byte vectors
+    int nranks;
+};
+
+// AllToAll: split[i*P+j] bytes travel from rank i to rank j.
+struct AllToAllArgs {
+    const void* src[kMaxRanksHost];
+    void* dst[kMaxRanksHost];
+    uint64_t split[kMaxRanksHost * kMaxRanksHost];
+    uint32_t tile_start[kMaxRanksHost * kMaxRanksHost + 1];
+    uint32_t aligned[kMaxRanksHost * kMaxRanksHost / 32];
+    int nranks;
+};
+
+struct BarrierArgs {
+    int32_t* win[kMaxRanksHost];
+    int32_t* status;
+    uint64_t timeout_ticks;  // wall-clock ticks per wait
+    int nranks;
+    int first_generation;
+    int generations;
+};
+
+struct ExchangeArgs {
+    BarrierArgs bar;
+    const void* src[kMaxRanksHost];
+    void* stage[kMaxRanksHost];
+    void* dst[kMaxRanksHost];
+    uint64_t nbytes;
+};
+
+// Tile sizes (bytes of one rank's data per workgroup).
+constexpr uint64_t kCopyTileBytes = 16384;   // gather / all-to-all
+constexpr uint64_t kPieceTileVecs = 512;     // bucket pieces: 512 x 16 B
+
+// Launchers: return the HIP error of the launch.  dtype/op are the dt_dtype /
+// dt_op enum values.  `vector` selects the 16-byte path (caller checked
+// alignment and divisibility).
+hipError_t launch_reduce_vec(const ReduceArgs& a, int dtype, int op, hipStream_t s);
+hipError_t launch_reduce_elems(const ReduceArgs& a, int dtype, int op, hipStream_t s);
+hipError_t launch_reduce_pieces(const PieceArgs& a, int dtype, int op, hipStream_t s);
+hipError_t launch_copy_pieces(const PieceArgs& a, int esize, int to_ws, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s);
+hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t s);
+hipError_t launch_barrier(const BarrierArgs& a, hipStream_t s);
+hipError_t launch_exchange(const ExchangeArgs& a, hipStream_t s);
+
+}  // namespace dt

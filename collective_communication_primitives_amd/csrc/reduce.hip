@@ -1,0 +1,303 @@
+// reduce.hip -- the rank-fold kernels: AllReduce (one-shot), ReduceScatter
+// and the multi-tensor bucket reduce.
+//
+// Work layout.  Rank buffers are P separate contiguous allocations in HBM.
+// Each thread owns whole 16-byte vectors: it issues the loads of its vectors
+// from every rank before folding, so a workgroup keeps P x U x 4 KiB of reads
+// in flight, then folds in rank order and writes the result (to every rank
+// for AllReduce, to the owning rank for ReduceScatter).  Every HBM byte is
+// touched once: AllReduce moves 2*P*S bytes, ReduceScatter (P+1)*S.
+//
+// The rank count is a template upper bound PMAX in {1, 2, 4, 8, 16}.  When
+// P equals PMAX (EXACT) the count is a compile-time constant and the kernel
+// is fully unrolled; other P pass the live count as an argument.
+#include "dt_device.h"
+#include "dt_launch.h"
+
+namespace dt {
+
+// ------------------------------------------------------------- one range --
+// grid.x covers a.count vectors in tiles of kBlock*U; grid.y = output chunk
+// (ReduceScatter) or 1 (AllReduce).
+template <int DT, int OP, int PMAX, bool EXACT, int U, bool RS>
+__global__ __launch_bounds__(kBlock) void k_reduce_vec(ReduceArgs a) {
+    const uint64_t chunk = RS ? blockIdx.y : 0;
+    const uint64_t in_off = chunk * a.count * 16;  // bytes into every rank's input
+    const uint64_t base = uint64_t(blockIdx.x) * (kBlock * U) + threadIdx.x;
+    const int nr = EXACT ? PMAX : a.nranks;
+    u32x4 x[U][PMAX];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const uint64_t v = base + uint64_t(u) * kBlock;
+        if (v < a.count) {
+#pragma unroll
+            for (int r = 0; r < PMAX; r++)
+                if (r < nr) x[u][r] = load16(static_cast<const char*>(a.src[r]) + in_off + v * 16);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const uint64_t v = base + uint64_t(u) * kBlock;
+        if (v < a.count) {
+            const u32x4 y = fold_vec<DT, OP, PMAX>(x[u], nr);
+            if constexpr (RS) {
+                store16(static_cast<char*>(a.dst[chunk]) + v * 16, y);
+            } else {
+#pragma unroll
+                for (int q = 0; q < PMAX; q++)
+                    if (q < nr) store16(static_cast<char*>(a.dst[q]) + v * 16, y);
+            }
+        }
+    }
+}
+
+// Element-wise path for ragged tails and unaligned buffers.  Elements
+// [a.first, a.first + a.count) of chunk blockIdx.y.
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_reduce_elems(ReduceArgs a) {
+    const uint64_t chunk = a.rs ? blockIdx.y : 0;
+    const uint64_t in_base = chunk * a.chunk_elems;
+    const int nr = a.nranks;
+    for (uint64_t i = uint64_t(blockIdx.x) * kBlock + threadIdx.x; i < a.count;
+         i += uint64_t(gridDim.x) * kBlock) {
+        const uint64_t e = a.first + i;
+        if (a.rs) {
+            fold_elem<DT, OP>(a.src, nr, in_base + e, a.dst[chunk], e);
+        } else {
+            fold_elem<DT, OP>(a.src, nr, e, a.dst[0], e);
+            const size_t es = elem_bytes<DT>();
+            for (int q = 1; q < nr; q++) {
+                if constexpr (DT == kBF16)
+                    static_cast<uint16_t*>(a.dst[q])[e] = static_cast<const uint16_t*>(a.dst[0])[e];
+                else
+                    static_cast<uint32_t*>(a.dst[q])[e] = static_cast<const uint32_t*>(a.dst[0])[e];
+            }
+            (void)es;
+        }
+    }
+}
+
+// ------------------------------------------------------ bucket pieces ----
+// One launch reduces every piece of a bucket in place: piece k's rank r
+// part starts at a.ptr[k*P + r].  grid.x = tiles over all pieces.
+template <int DT, int OP, int PMAX, bool EXACT>
+__global__ __launch_bounds__(kBlock) void k_reduce_pieces(PieceArgs a) {
+    constexpr int V = Elems<DT>::value;
+    const uint32_t b = blockIdx.x;
+    int k = 0;
+    while (k + 1 < a.npieces && a.tile_start[k + 1] <= b) k++;
+    const int nr = EXACT ? PMAX : a.nranks;
+    void* const* ptr = a.ptr + k * nr;
+    const uint64_t len = a.len[k];
+    const uint64_t e0 = uint64_t(b - a.tile_start[k]) * kPieceTileVecs * V;
+    const uint64_t e1 = min(len, e0 + kPieceTileVecs * V);
+    if ((a.aligned >> k) & 1u) {
+        constexpr int U = int(kPieceTileVecs / kBlock);
+        const uint64_t v0 = e0 / V, v1 = e1 / V;
+        u32x4 x[U][PMAX];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint64_t v = v0 + threadIdx.x + uint64_t(u) * kBlock;
+            if (v < v1) {
+#pragma unroll
+                for (int r = 0; r < PMAX; r++)
+                    if (r < nr) x[u][r] = load16(static_cast<const char*>(ptr[r]) + v * 16);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint64_t v = v0 + threadIdx.x + uint64_t(u) * kBlock;
+            if (v < v1) {
+                const u32x4 y = fold_vec<DT, OP, PMAX>(x[u], nr);
+#pragma unroll
+                for (int q = 0; q < PMAX; q++)
+                    if (q < nr) store16(static_cast<char*>(ptr[q]) + v * 16, y);
+            }
+        }
+        const uint64_t t = v1 * V + threadIdx.x;  // ragged end of the piece
+        if (t < e1) {
+            fold_elem<DT, OP>(ptr, nr, t, ptr[0], t);
+            for (int q = 1; q < nr; q++) {
+                if constexpr (DT == kBF16)
+                    static_cast<uint16_t*>(ptr[q])[t] = static_cast<const uint16_t*>(ptr[0])[t];
+                else
+                    static_cast<uint32_t*>(ptr[q])[t] = static_cast<const uint32_t*>(ptr[0])[t];
+            }
+        }
+    } else {
+        for (uint64_t e = e0 + threadIdx.x; e < e1; e += kBlock) {
+            fold_elem<DT, OP>(ptr, nr, e, ptr[0], e);
+            for (int q = 1; q < nr; q++) {
+                if constexpr (DT == kBF16)
+                    static_cast<uint16_t*>(ptr[q])[e] = static_cast<const uint16_t*>(ptr[0])[e];
+                else
+                    static_cast<uint32_t*>(ptr[q])[e] = static_cast<const uint32_t*>(ptr[0])[e];
+            }
+        }
+    }
+}
+
+// Flatten (to_ws = 1) or unflatten (to_ws = 0) the pieces of one bucket for
+// rank blockIdx.y: a byte copy between the tensors and the bucket buffer.
+__global__ __launch_bounds__(kBlock) void k_copy_pieces(PieceArgs a, int esize, int to_ws) {
+    const uint32_t b = blockIdx.x;
+    const int r = blockIdx.y;
+    int k = 0;
+    while (k + 1 < a.npieces && a.tile_start[k + 1] <= b) k++;
+    char* tensor = static_cast<char*>(a.ptr[k * a.nranks + r]);
+    char* bucket = static_cast<char*>(a.ws[r]) + a.wpos[k] * uint64_t(esize);
+    const char* from = to_ws ? tensor : bucket;
+    char* to = to_ws ? bucket : tensor;
+    const uint64_t bytes = a.len[k] * uint64_t(esize);
+    const uint64_t tile_bytes = kPieceTileVecs * 16;
+    const uint64_t b0 = uint64_t(b - a.tile_start[k]) * tile_bytes;
+    const uint64_t b1 = min(bytes, b0 + tile_bytes);
+    if ((a.aligned >> k) & 1u) {
+        const uint64_t v1 = b1 / 16;
+        for (uint64_t v = b0 / 16 + threadIdx.x; v < v1; v += kBlock) store16(to + v * 16, load16(from + v * 16));
+        const uint64_t t = v1 * 16 + threadIdx.x;
+        if (t < b1) to[t] = from[t];
+    } else {
+        for (uint64_t t = b0 + threadIdx.x; t < b1; t += kBlock) to[t] = from[t];
+    }
+}
+
+// ---------------------------------------------------------- dispatchers --
+namespace {
+
+int pmax_of(int nranks) {
+    return nranks <= 1 ? 1 : nranks <= 2 ? 2 : nranks <= 4 ? 4 : nranks <= 8 ? 8 : 16;
+}
+
+// Vectors per thread: enough independent 16-byte loads in flight per thread
+// (PMAX x U) while keeping the register footprint modest.
+template <int PMAX>
+constexpr int unroll_of() { return PMAX >= 8 ? 1 : PMAX == 4 ? 2 : 4; }
+
+template <int DT, int OP, int PMAX>
+hipError_t reduce_vec_p(const ReduceArgs& a, hipStream_t s) {
+    constexpr int U = unroll_of<PMAX>();
+    const uint64_t blocks = (a.count + kBlock * U - 1) / (kBlock * U);
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    dim3 grid(unsigned(blocks), a.rs ? unsigned(a.nranks) : 1u);
+    const bool exact = a.nranks == PMAX;
+    if (a.rs) {
+        if (exact)
+            k_reduce_vec<DT, OP, PMAX, true, U, true><<<grid, kBlock, 0, s>>>(a);
+        else
+            k_reduce_vec<DT, OP, PMAX, false, U, true><<<grid, kBlock, 0, s>>>(a);
+    } else {
+        if (exact)
+            k_reduce_vec<DT, OP, PMAX, true, U, false><<<grid, kBlock, 0, s>>>(a);
+        else
+            k_reduce_vec<DT, OP, PMAX, false, U, false><<<grid, kBlock, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+template <int DT, int OP>
+hipError_t reduce_vec_op(const ReduceArgs& a, hipStream_t s) {
+    switch (pmax_of(a.nranks)) {
+        case 1: return reduce_vec_p<DT, OP, 1>(a, s);
+        case 2: return reduce_vec_p<DT, OP, 2>(a, s);
+        case 4: return reduce_vec_p<DT, OP, 4>(a, s);
+        case 8: return reduce_vec_p<DT, OP, 8>(a, s);
+        default: return reduce_vec_p<DT, OP, 16>(a, s);
+    }
+}
+
+template <int DT>
+hipError_t reduce_vec_dt(const ReduceArgs& a, int op, hipStream_t s) {
+    switch (op) {
+        case kSum: return reduce_vec_op<DT, kSum>(a, s);
+        case kMax: return reduce_vec_op<DT, kMax>(a, s);
+        default: return reduce_vec_op<DT, kMin>(a, s);
+    }
+}
+
+template <int DT, int OP>
+hipError_t reduce_elems_op(const ReduceArgs& a, hipStream_t s) {
+    if (a.count == 0) return hipSuccess;
+    uint64_t blocks = (a.count + kBlock - 1) / kBlock;
+    if (blocks > 8192) blocks = 8192;
+    dim3 grid(unsigned(blocks), a.rs ? unsigned(a.nranks) : 1u);
+    k_reduce_elems<DT, OP><<<grid, kBlock, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t reduce_elems_dt(const ReduceArgs& a, int op, hipStream_t s) {
+    switch (op) {
+        case kSum: return reduce_elems_op<DT, kSum>(a, s);
+        case kMax: return reduce_elems_op<DT, kMax>(a, s);
+        default: return reduce_elems_op<DT, kMin>(a, s);
+    }
+}
+
+template <int DT, int OP, int PMAX>
+hipError_t reduce_pieces_p(const PieceArgs& a, hipStream_t s) {
+    const uint32_t tiles = a.tile_start[a.npieces];
+    if (tiles == 0) return hipSuccess;
+    if (a.nranks == PMAX)
+        k_reduce_pieces<DT, OP, PMAX, true><<<tiles, kBlock, 0, s>>>(a);
+    else
+        k_reduce_pieces<DT, OP, PMAX, false><<<tiles, kBlock, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int DT, int OP>
+hipError_t reduce_pieces_op(const PieceArgs& a, hipStream_t s) {
+    switch (pmax_of(a.nranks)) {
+        case 1: return reduce_pieces_p<DT, OP, 1>(a, s);
+        case 2: return reduce_pieces_p<DT, OP, 2>(a, s);
+        case 4: return reduce_pieces_p<DT, OP, 4>(a, s);
+        case 8: return reduce_pieces_p<DT, OP, 8>(a, s);
+        default: return reduce_pieces_p<DT, OP, 16>(a, s);
+    }
+}
+
+template <int DT>
+hipError_t reduce_pieces_dt(const PieceArgs& a, int op, hipStream_t s) {
+    switch (op) {
+        case kSum: return reduce_pieces_op<DT, kSum>(a, s);
+        case kMax: return reduce_pieces_op<DT, kMax>(a, s);
+        default: return reduce_pieces_op<DT, kMin>(a, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_reduce_vec(const ReduceArgs& a, int dtype, int op, hipStream_t s) {
+    switch (dtype) {
+        case kF32: return reduce_vec_dt<kF32>(a, op, s);
+        case kBF16: return reduce_vec_dt<kBF16>(a, op, s);
+        default: return reduce_vec_dt<kI32>(a, op, s);
+    }
+}
+
+hipError_t launch_reduce_elems(const ReduceArgs& a, int dtype, int op, hipStream_t s) {
+    switch (dtype) {
+        case kF32: return reduce_elems_dt<kF32>(a, op, s);
+        case kBF16: return reduce_elems_dt<kBF16>(a, op, s);
+        default: return reduce_elems_dt<kI32>(a, op, s);
+    }
+}
+
+hipError_t launch_reduce_pieces(const PieceArgs& a, int dtype, int op, hipStream_t s) {
+    switch (dtype) {
+        case kF32: return reduce_pieces_dt<kF32>(a, op, s);
+        case kBF16: return reduce_pieces_dt<kBF16>(a, op, s);
+        default: return reduce_pieces_dt<kI32>(a, op, s);
+    }
+}
+
+hipError_t launch_copy_pieces(const PieceArgs& a, int esize, int to_ws, hipStream_t s) {
+    const uint32_t tiles = a.tile_start[a.npieces];
+    if (tiles == 0) return hipSuccess;
+    dim3 grid(tiles, unsigned(a.nranks));
+    k_copy_pieces<<<grid, kBlock, 0, s>>>(a, esize, to_ws);
+    return hipGetLastError();
+}
+
+}  // namespace dt

@@ -91,6 +91,16 @@ def split_matrix(seed: int = 0, nranks: int = 8, high: int = 4096) -> np.ndarray
     return np.random.default_rng(seed + 1).integers(0, high + 1, (nranks, nranks))
 
 
+def uniform_rows(row_counts: Sequence[int], width: int = ROW_WIDTH, seed: int = 0,
+                 device="cpu") -> List[torch.Tensor]:
+    """Rank r: row_counts[r] rows of ``width`` fp32 values U[-1, 1), seed + r."""
+    out = []
+    for r, c in enumerate(row_counts):
+        t = torch.rand(int(c) * width, generator=_gen(device, seed + r), device=device, dtype=torch.float32)
+        out.append(t * 2 - 1)
+    return out
+
+
 def layer_grads(nranks: int, layer: int, seed: int = 0, device="cpu", std: float = 1e-3,
                 shapes=LAYER_SHAPES, dtype=torch.bfloat16) -> List[List[torch.Tensor]]:
     """grads[r][t] of one synthetic transformer layer, N(0, std^2) in bf16.

@@ -1,0 +1,86 @@
+"""GPU: stream/event ordering of async collectives (c10d page sec. 4.3-4.4 and
+the user rules of sec. 5).  A producer kernel that finishes late on the
+compute stream must still be seen by a collective queued on a side stream,
+and a consumer must see the collective's result after wait()."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import compare, note, to_np
+
+pytestmark = pytest.mark.gpu
+
+SPIN = 50_000_000  # cycles of torch's device sleep kernel: tens of ms
+
+
+@pytest.fixture(scope="module")
+def dt():
+    import collective_communication_primitives_amd as m
+    return m
+
+
+def test_async_allreduce_waits_for_late_producer(dt):
+    p, n = 4, 1 << 20
+    xs = [torch.zeros(n, device="cuda") for _ in range(p)]
+    ys = [torch.empty(n, device="cuda") for _ in range(p)]
+    vals = synth.uniform_ranks(p, n, seed=5, device="cuda")
+    torch.cuda.synchronize()
+    note("async allreduce after a delayed producer")
+    torch.cuda._sleep(SPIN)            # the compute stream is busy...
+    for x, v in zip(xs, vals):
+        x.copy_(v)                     # ...and only then writes the inputs
+    work = dt.dt_allreduce(xs, ys, async_op=True)
+    work.wait()                        # current stream waits for the end event
+    host = [to_np(y) for y in ys]      # consumer on the current stream
+    want = oracle.get().allreduce([to_np(v) for v in vals], "sum")
+    for q in range(p):
+        compare(host[q], want[q], f"rank {q}")
+    assert work.is_completed()
+
+
+def test_async_work_is_not_complete_before_producer(dt):
+    p, n = 2, 4096
+    xs = [torch.ones(n, device="cuda") for _ in range(p)]
+    torch.cuda.synchronize()
+    note("async work not complete while the producer still runs")
+    torch.cuda._sleep(SPIN)
+    work = dt.dt_allreduce(xs, async_op=True)
+    assert not work.is_completed()     # the side stream waits on the busy compute stream
+    work.wait()
+    torch.cuda.synchronize()
+    assert work.is_completed()
+    assert bool((xs[0] == 2).all())
+
+
+def test_third_stream_consumer(dt):
+    """Rule 3: a consumer on a third stream waits on the work itself."""
+    p, n = 3, 1 << 16
+    xs = [torch.full((n,), float(r + 1), device="cuda") for r in range(p)]
+    ys = [torch.empty(n, device="cuda") for _ in range(p)]
+    consumer = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    note("third-stream consumer")
+    torch.cuda._sleep(SPIN)
+    work = dt.dt_allreduce(xs, ys, async_op=True)
+    work.wait(stream=consumer)
+    with torch.cuda.stream(consumer):
+        total = torch.stack([y.sum() for y in ys]).sum()
+    consumer.synchronize()
+    assert float(total.item()) == p * n * (p * (p + 1) / 2)
+
+
+def test_sync_mode_is_stream_ordered(dt):
+    """Default mode queues on the current stream: ordered after the producer
+    and before the consumer without any event."""
+    p, n = 4, 1 << 18
+    xs = [torch.zeros(n, dtype=torch.int32, device="cuda") for _ in range(p)]
+    torch.cuda.synchronize()
+    note("sync mode ordering")
+    torch.cuda._sleep(SPIN)
+    for r, x in enumerate(xs):
+        x.fill_(r + 1)
+    dt.dt_allreduce(xs)
+    s = int(xs[2].sum().item())
+    assert s == n * p * (p + 1) // 2
