@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark: same-device ReduceScatter -> AllGather (Partial -> Shard(0) ->
+Replicate, i.e. an AllReduce) of P=8 bf16 [8192, 8192] rank tensors drawn
+N(0,1) on one MI355X, with fp32 accumulation in fixed rank order.
+
+One step = dt_reduce_scatter over the 8 rank inputs + dt_all_gather of the
+8 shards back into 8 full outputs.  The headline value is the AllReduce bus
+bandwidth of that step: algbw = S / t with S = 128 MiB per rank, busbw =
+algbw * 2(P-1)/P (the ring-AllReduce volume factor of the c10d page,
+sec. 6.1).  Every kernel launch of the timed region is bracketed by HIP
+events on the stream it runs on; the dominant kernel's algorithmic HBM bytes
+per launch over its mean duration give the roofline fraction against the
+MI355X's 8 TB/s.  The CPU oracle, timed on a bounded sample of the same
+workload on the host, is reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+P = 8
+SHAPE = (8192, 8192)
+METRIC = "AllReduce/ReduceScatter bus GB/s & % of HBM peak on 1 MI355X, P=8"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("collective_communication_primitives_amd/csrc/reduce.hip",
+                  "collective_communication_primitives_amd/csrc/copy.hip",
+                  "collective_communication_primitives_amd/csrc/dt_device.h",
+                  "collective_communication_primitives_amd/csrc/dt_launch.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"^source_hash:\s*(\S+)", text, re.M)
+    m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def time_launches(fn, steps, stream):
+    """Run fn() `steps` times with start/end events on `stream` around each."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    return evs
+
+
+def cpu_baseline(xs_dev, reps: int):
+    """The oracle, untouched, timed on the host: RS then AG on the full
+    workload copied back from the device, `reps` repetitions, median."""
+    import numpy as np
+    import oracle
+    orc = oracle.get()
+    host = [x.view(__import__("torch").int16).cpu().numpy().view(np.uint16).reshape(-1) for x in xs_dev]
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        shards = orc.reduce_scatter(host, "sum")
+        orc.all_gather(shards)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    s_bytes = host[0].nbytes
+    busbw = s_bytes / t * 2 * (P - 1) / P / 1e9
+    return {"value": round(busbw, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"full workload (P=8 bf16 {SHAPE[0]}x{SHAPE[1]} per rank), RS then AG, "
+                      f"median of {reps} single-threaded runs of {t:.2f} s each; same busbw formula",
+            "seconds_per_step": round(t, 3), "host_cpus": os.cpu_count()}
+
+
+def sweep(dt, torch, steps: int, warmup: int):
+    """fp32 one-shot AllReduce, P=16, per-rank sizes 4 KiB .. 1 GiB (x4), and
+    the alpha-beta fit T(S) = alpha + 2*P*S / B_eff (weights 1/T^2)."""
+    import numpy as np
+    import synth
+    rows = []
+    p = 16
+    for nbytes in synth.SWEEP_BYTES:
+        n = nbytes // 4
+        xs = synth.uniform_ranks(p, n, seed=0, device="cuda")
+        ys = [torch.empty_like(x) for x in xs]
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            dt.dt_allreduce(xs, ys)
+        evs = time_launches(lambda: dt.dt_allreduce(xs, ys), steps, stream)
+        torch.cuda.synchronize()
+        us = statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3
+        hbm = 2 * p * nbytes / (us * 1e-6) / 1e9
+        busbw = nbytes / (us * 1e-6) * 2 * (p - 1) / p / 1e9
+        rows.append({"bytes_per_rank": nbytes, "us": round(us, 3), "hbm_GBps": round(hbm, 1),
+                     "busbw_GBps": round(busbw, 1), "frac_of_peak": round(hbm / HBM_PEAK_GBPS, 4)})
+        print(json.dumps({"sweep": rows[-1]}), flush=True)
+        del xs, ys
+        torch.cuda.empty_cache()
+    s = np.array([r["bytes_per_rank"] for r in rows], dtype=np.float64)
+    t = np.array([r["us"] for r in rows], dtype=np.float64) * 1e-6
+    a = np.stack([np.ones_like(s), 2 * p * s], axis=1) / t[:, None]
+    coef, *_ = np.linalg.lstsq(a, np.ones_like(t), rcond=None)
+    alpha, inv_b = coef
+    fit = {"alpha_us": round(alpha * 1e6, 3), "B_eff_GBps": round(1 / inv_b / 1e9, 1) if inv_b > 0 else None}
+    print(json.dumps({"sweep_fit": fit}), flush=True)
+    return rows, fit
+
+
+def barrier_latency(dt, torch):
+    """P=16 signal-window barrier: 1000 generations in one launch, and 1000
+    single-generation launches."""
+    p = 16
+    ws = [torch.zeros(p, dtype=torch.int32, device="cuda") for _ in range(p)]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dt.dt_barrier(ws, status, 1, 10)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    dt.dt_barrier(ws, status, 11, 1000)
+    b.record()
+    torch.cuda.synchronize()
+    in_kernel = a.elapsed_time(b) * 1e3 / 1000
+    a.record()
+    for g in range(1011, 2011):
+        dt.dt_barrier(ws, status, g, 1)
+    b.record()
+    torch.cuda.synchronize()
+    per_launch = a.elapsed_time(b) * 1e3 / 1000
+    assert int(status.item()) == 0
+    out = {"P": p, "us_per_generation_in_kernel": round(in_kernel, 3), "us_per_launch": round(per_launch, 3)}
+    print(json.dumps({"barrier": out}), flush=True)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--sweep", action="store_true", help="also run the P=16 size sweep and barrier latency")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the same-device backend: all P logical ranks live on ONE GPU, so it runs "
+              "on exactly one GPU (--gpus 1); multi-GPU runs are not part of this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import collective_communication_primitives_amd as dt
+    import synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    xs = synth.normal_ranks(P, SHAPE, seed=0, device="cuda", dtype=torch.bfloat16)
+    n = SHAPE[0] * SHAPE[1]
+    shards = [torch.empty(n // P, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    full = [torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    s_bytes = n * 2
+
+    def rs():
+        dt.dt_reduce_scatter(xs, shards)
+
+    def ag():
+        dt.dt_all_gather(shards, full)
+
+    for _ in range(args.warmup):
+        rs()
+        ag()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each kernel bracketed by events on its stream
+    ev_rs, ev_ag = [], []
+    step_a, step_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    step_a.record(stream)
+    for _ in range(args.steps):
+        ev_rs += time_launches(rs, 1, stream)
+        ev_ag += time_launches(ag, 1, stream)
+    step_b.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    ms_total = step_a.elapsed_time(step_b)
+    ms_per_step = ms_total / args.steps
+    rs_us = [a.elapsed_time(b) * 1e3 for a, b in ev_rs]
+    ag_us = [a.elapsed_time(b) * 1e3 for a, b in ev_ag]
+
+    algbw = s_bytes / (ms_per_step * 1e-3) / 1e9
+    busbw = algbw * 2 * (P - 1) / P
+
+    rs_bytes = (P + 1) * s_bytes          # read P inputs, write one shard per rank
+    ag_bytes = (1 + P) * s_bytes          # read P shards, write P full outputs
+    kernels = {
+        "reduce_scatter": {"mean_us": round(statistics.mean(rs_us), 3), "median_us": round(statistics.median(rs_us), 3),
+                           "alg_bytes": rs_bytes,
+                           "hbm_GBps": round(rs_bytes / (statistics.mean(rs_us) * 1e-6) / 1e9, 1),
+                           "busbw_GBps": round(s_bytes / (statistics.mean(rs_us) * 1e-6) / 1e9 * (P - 1) / P, 1)},
+        "all_gather": {"mean_us": round(statistics.mean(ag_us), 3), "median_us": round(statistics.median(ag_us), 3),
+                       "alg_bytes": ag_bytes,
+                       "hbm_GBps": round(ag_bytes / (statistics.mean(ag_us) * 1e-6) / 1e9, 1),
+                       "busbw_GBps": round(s_bytes / (statistics.mean(ag_us) * 1e-6) / 1e9 * (P - 1) / P, 1)},
+    }
+    dom_name = max(kernels, key=lambda k: kernels[k]["mean_us"])
+    dom = kernels[dom_name]
+    achieved = dom["alg_bytes"] / (dom["mean_us"] * 1e-6) / 1e9
+    traffic = measured_traffic({"reduce_scatter": "reduce_scatter_bf16_p8", "all_gather": "all_gather_bf16_p8"}[dom_name])
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom_name,
+                "alg_bytes_per_launch": dom["alg_bytes"]}
+
+    # one-shot AllReduce on the same inputs, for reference
+    ar_out = [torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    for _ in range(args.warmup):
+        dt.dt_allreduce(xs, ar_out)
+    ev_ar = time_launches(lambda: dt.dt_allreduce(xs, ar_out), args.steps, stream)
+    torch.cuda.synchronize()
+    ar_us = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in ev_ar)
+    kernels["allreduce_oneshot"] = {"mean_us": round(ar_us, 3), "alg_bytes": 2 * P * s_bytes,
+                                    "hbm_GBps": round(2 * P * s_bytes / (ar_us * 1e-6) / 1e9, 1),
+                                    "busbw_GBps": round(s_bytes / (ar_us * 1e-6) / 1e9 * 2 * (P - 1) / P, 1)}
+    del ar_out
+
+    extra = {"kernels": kernels, "host_seconds_timed": round(t_host, 4), "kernel_source_hash": kernel_source_hash()}
+    if args.sweep:
+        rows, fit = sweep(dt, torch, steps=max(5, args.steps // 2), warmup=2)
+        extra["sweep_p16_fp32"] = rows
+        extra["alpha_beta_fit"] = fit
+        extra["barrier"] = barrier_latency(dt, torch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(xs, args.cpu_reps)
+
+    line = {
+        "metric": METRIC, "value": round(busbw, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "reduce_scatter_then_all_gather_bf16", "ranks": P, "shape_per_rank": list(SHAPE),
+                   "op": "sum", "accumulate": "fp32", "seed": 0, "distribution": "N(0,1)",
+                   "bytes_per_rank": s_bytes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
