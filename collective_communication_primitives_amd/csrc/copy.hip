@@ -1,7 +1,7 @@
 // copy.hip -- the gather and all-to-all copy engines.
 //
 // Both are byte copies driven by an offset table carried in the kernel
-// arguments (no device-side tables).  The work is cut into 16 KiB tiles of
+// arguments (no device-side tables).  The work is cut into 8 KiB tiles of
 // source data; one workgroup copies one tile, so uneven pieces (1 row or
 // 16384 rows, an empty all-to-all block or a 4096-row one) balance across the
 // whole chip.  A workgroup finds its piece from an exclusive prefix sum of
@@ -32,14 +32,14 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
 #pragma unroll
         for (int u = 0; u < kCopyU; u++) {
             const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
-            if (v < v1) x[u] = load16(src + v * 16);
+            if (v < v1) x[u] = load16_h<false>(src + v * 16);  // writes dominate 1:P
         }
         for (int q = 0; q < nr; q++) {
             char* dst = static_cast<char*>(a.dst[q]) + off;
 #pragma unroll
             for (int u = 0; u < kCopyU; u++) {
                 const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
-                if (v < v1) store16(dst + v * 16, x[u]);
+                if (v < v1) store16_h<true>(dst + v * 16, x[u]);
             }
         }
         const uint64_t t = v1 * 16 + threadIdx.x;  // ragged end: fewer than 16 bytes

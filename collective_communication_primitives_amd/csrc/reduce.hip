@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_vec(ReduceArgs a) {
         if (v < a.count) {
             const u32x4 y = fold_vec<DT, OP, PMAX>(x[u], nr);
             if constexpr (RS) {
-                store16(static_cast<char*>(a.dst[chunk]) + v * 16, y);
+                store16_h<false>(static_cast<char*>(a.dst[chunk]) + v * 16, y);  // reads dominate 8:1
             } else {
 #pragma unroll
                 for (int q = 0; q < PMAX; q++)
@@ -172,7 +172,7 @@ int pmax_of(int nranks) {
 // Vectors per thread: enough independent 16-byte loads in flight per thread
 // (PMAX x U) while keeping the register footprint modest.
 template <int PMAX>
-constexpr int unroll_of() { return PMAX >= 8 ? 1 : PMAX == 4 ? 2 : 4; }
+constexpr int unroll_of() { return PMAX >= 16 ? 1 : PMAX == 8 ? 2 : 4; }
 
 template <int DT, int OP, int PMAX>
 hipError_t reduce_vec_p(const ReduceArgs& a, hipStream_t s) {
