@@ -155,14 +155,35 @@ def barrier_latency(dt, torch):
     return out
 
 
+def probe(dt, torch, reps: int = 10):
+    """Workload for hardware-counter passes: the bench kernels and a plain
+    copy of known size (1 GiB read + 1 GiB written) to calibrate
+    FETCH_SIZE / WRITE_SIZE against known bytes."""
+    import synth
+    xs = synth.normal_ranks(P, SHAPE, seed=0, device="cuda", dtype=torch.bfloat16)
+    n = SHAPE[0] * SHAPE[1]
+    shards = [torch.empty(n // P, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    full = [torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        dt.dt_reduce_scatter(xs, shards)
+        dt.dt_all_gather(shards, full)
+        dt.dt_allreduce(xs, full)
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "done", "reps": reps, "copy_bytes_each_way": a.numel() * 4}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=25)
     ap.add_argument("--sweep", action="store_true", help="also run the P=16 size sweep and barrier latency")
+    ap.add_argument("--probe", action="store_true", help="only run the kernels for a hardware-counter pass")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -175,6 +196,9 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.probe:
+        probe(dt, torch)
+        return
     stream = torch.cuda.current_stream()
     xs = synth.normal_ranks(P, SHAPE, seed=0, device="cuda", dtype=torch.bfloat16)
     n = SHAPE[0] * SHAPE[1]
