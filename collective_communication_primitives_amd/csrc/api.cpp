@@ -347,7 +347,11 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
     if (numels == nullptr) return fail(DT_ERR_ARG, "numels is NULL");
     if (bucket_bytes == 0 || bucket_bytes % 16 != 0)
         return fail(DT_ERR_ARG, "bucket_bytes=%zu must be a positive multiple of 16", bucket_bytes);
-    if ((st = check_ptr_array(grads, nranks * ntensors, "grads")) != DT_OK) return st;
+    if (grads == nullptr) return fail(DT_ERR_ARG, "grads is NULL");
+    for (int r = 0; r < nranks; r++)  // an empty tensor may carry a NULL pointer
+        for (int t = 0; t < ntensors; t++)
+            if (numels[t] > 0 && grads[size_t(r) * ntensors + t] == nullptr)
+                return fail(DT_ERR_ARG, "grads[%d] (rank %d, tensor %d) is NULL", r * ntensors + t, r, t);
     if (bucket_ws && (st = check_ptr_array(bucket_ws, nranks, "bucket_ws")) != DT_OK) return st;
     const size_t es = esize_of(dtype);
     size_t nbuckets = 0;
@@ -601,9 +605,14 @@ dt_status dt_hsdp_post_backward(dt_hsdp* h, const void* const* grads, const size
     if (h == nullptr) return fail(DT_ERR_ARG, "handle is NULL");
     const int nranks = h->replicate * h->shard;
     dt_status st;
-    if (ntensors < 1 || numels == nullptr) return fail(DT_ERR_ARG, "no tensors");
-    if ((st = check_ptr_array(grads, nranks * ntensors, "grads")) != DT_OK) return st;
-    if ((st = check_ptr_array(fused, nranks, "fused")) != DT_OK) return st;
+    if (ntensors < 1 || numels == nullptr || grads == nullptr) return fail(DT_ERR_ARG, "no tensors");
+    size_t total = 0;
+    for (int t = 0; t < ntensors; t++) total += numels[t];
+    for (int r = 0; r < nranks; r++)  // an empty tensor may carry a NULL pointer
+        for (int t = 0; t < ntensors; t++)
+            if (numels[t] > 0 && grads[size_t(r) * ntensors + t] == nullptr)
+                return fail(DT_ERR_ARG, "grads[%d] (rank %d, tensor %d) is NULL", r * ntensors + t, r, t);
+    if (total > 0 && (st = check_ptr_array(fused, nranks, "fused")) != DT_OK) return st;
     for (int t = 0; t < ntensors; t++)
         if (numels[t] % size_t(h->shard) != 0)
             return fail(DT_ERR_ARG, "numels[%d]=%zu not divisible by shard=%d", t, numels[t], h->shard);
