@@ -17,9 +17,12 @@ namespace dt {
 
 constexpr int kCopyU = int(kCopyTileBytes / 16 / kBlock);  // 16-byte vectors per thread per tile
 
+// PMAX bounds the rank count; EXACT (P == PMAX) unrolls the P destination
+// stores.
+template <int PMAX, bool EXACT>
 __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
     const uint32_t b = blockIdx.x;
-    const int nr = a.nranks;
+    const int nr = EXACT ? PMAX : a.nranks;
     int r = 0;
     while (r + 1 < nr && a.tile_start[r + 1] <= b) r++;
     const char* src = static_cast<const char*>(a.src[r]);
@@ -34,12 +37,15 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
             const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
             if (v < v1) x[u] = load16_h<false>(src + v * 16);  // writes dominate 1:P
         }
-        for (int q = 0; q < nr; q++) {
-            char* dst = static_cast<char*>(a.dst[q]) + off;
 #pragma unroll
-            for (int u = 0; u < kCopyU; u++) {
-                const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
-                if (v < v1) store16_h<true>(dst + v * 16, x[u]);
+        for (int q = 0; q < PMAX; q++) {
+            if (q < nr) {
+                char* dst = static_cast<char*>(a.dst[q]) + off;
+#pragma unroll
+                for (int u = 0; u < kCopyU; u++) {
+                    const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
+                    if (v < v1) store16_h<true>(dst + v * 16, x[u]);
+                }
             }
         }
         const uint64_t t = v1 * 16 + threadIdx.x;  // ragged end: fewer than 16 bytes
@@ -96,10 +102,22 @@ __global__ __launch_bounds__(kBlock) void k_all_to_all(AllToAllArgs a) {
     }
 }
 
+namespace {
+template <int PMAX>
+hipError_t gather_p(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
+    if (a.nranks == PMAX)
+        k_gather<PMAX, true><<<tiles, kBlock, 0, s>>>(a);
+    else
+        k_gather<PMAX, false><<<tiles, kBlock, 0, s>>>(a);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     if (tiles == 0) return hipSuccess;
-    k_gather<<<tiles, kBlock, 0, s>>>(a);
-    return hipGetLastError();
+    const int p = a.nranks;
+    return p <= 1 ? gather_p<1>(a, tiles, s) : p <= 2 ? gather_p<2>(a, tiles, s) : p <= 4 ? gather_p<4>(a, tiles, s)
+           : p <= 8 ? gather_p<8>(a, tiles, s) : gather_p<16>(a, tiles, s);
 }
 
 hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t s) {

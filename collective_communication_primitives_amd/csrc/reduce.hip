@@ -19,6 +19,11 @@ namespace dt {
 // ------------------------------------------------------------- one range --
 // grid.x covers a.count vectors in tiles of kBlock*U; grid.y = output chunk
 // (ReduceScatter) or 1 (AllReduce).
+//
+// Issue order: all of rank 0's vectors, then rank 1's, ...; stores output by
+// output.  Each wave then sends U KiB-long runs to one buffer before moving to
+// the next, which the MI355X's HBM serves faster than interleaving the P
+// buffers vector by vector (measured: +3% for the P-to-P AllReduce pattern).
 template <int DT, int OP, int PMAX, bool EXACT, int U, bool RS>
 __global__ __launch_bounds__(kBlock) void k_reduce_vec(ReduceArgs a) {
     const uint64_t chunk = RS ? blockIdx.y : 0;
@@ -27,25 +32,33 @@ __global__ __launch_bounds__(kBlock) void k_reduce_vec(ReduceArgs a) {
     const int nr = EXACT ? PMAX : a.nranks;
     u32x4 x[U][PMAX];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const uint64_t v = base + uint64_t(u) * kBlock;
-        if (v < a.count) {
+    for (int r = 0; r < PMAX; r++) {
+        if (r < nr) {
 #pragma unroll
-            for (int r = 0; r < PMAX; r++)
-                if (r < nr) x[u][r] = load16(static_cast<const char*>(a.src[r]) + in_off + v * 16);
+            for (int u = 0; u < U; u++) {
+                const uint64_t v = base + uint64_t(u) * kBlock;
+                if (v < a.count) x[u][r] = load16(static_cast<const char*>(a.src[r]) + in_off + v * 16);
+            }
         }
     }
+    u32x4 y[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const uint64_t v = base + uint64_t(u) * kBlock;
-        if (v < a.count) {
-            const u32x4 y = fold_vec<DT, OP, PMAX>(x[u], nr);
-            if constexpr (RS) {
-                store16_h<false>(static_cast<char*>(a.dst[chunk]) + v * 16, y);  // reads dominate 8:1
-            } else {
+    for (int u = 0; u < U; u++) y[u] = fold_vec<DT, OP, PMAX>(x[u], nr);
+    if constexpr (RS) {
 #pragma unroll
-                for (int q = 0; q < PMAX; q++)
-                    if (q < nr) store16(static_cast<char*>(a.dst[q]) + v * 16, y);
+        for (int u = 0; u < U; u++) {
+            const uint64_t v = base + uint64_t(u) * kBlock;
+            if (v < a.count) store16_h<false>(static_cast<char*>(a.dst[chunk]) + v * 16, y[u]);  // reads dominate P:1
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < PMAX; q++) {
+            if (q < nr) {
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const uint64_t v = base + uint64_t(u) * kBlock;
+                    if (v < a.count) store16(static_cast<char*>(a.dst[q]) + v * 16, y[u]);
+                }
             }
         }
     }
@@ -96,22 +109,26 @@ __global__ __launch_bounds__(kBlock) void k_reduce_pieces(PieceArgs a) {
         const uint64_t v0 = e0 / V, v1 = e1 / V;
         u32x4 x[U][PMAX];
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const uint64_t v = v0 + threadIdx.x + uint64_t(u) * kBlock;
-            if (v < v1) {
+        for (int r = 0; r < PMAX; r++) {
+            if (r < nr) {
 #pragma unroll
-                for (int r = 0; r < PMAX; r++)
-                    if (r < nr) x[u][r] = load16(static_cast<const char*>(ptr[r]) + v * 16);
+                for (int u = 0; u < U; u++) {
+                    const uint64_t v = v0 + threadIdx.x + uint64_t(u) * kBlock;
+                    if (v < v1) x[u][r] = load16(static_cast<const char*>(ptr[r]) + v * 16);
+                }
             }
         }
+        u32x4 y[U];
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const uint64_t v = v0 + threadIdx.x + uint64_t(u) * kBlock;
-            if (v < v1) {
-                const u32x4 y = fold_vec<DT, OP, PMAX>(x[u], nr);
+        for (int u = 0; u < U; u++) y[u] = fold_vec<DT, OP, PMAX>(x[u], nr);
 #pragma unroll
-                for (int q = 0; q < PMAX; q++)
-                    if (q < nr) store16(static_cast<char*>(ptr[q]) + v * 16, y);
+        for (int q = 0; q < PMAX; q++) {
+            if (q < nr) {
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const uint64_t v = v0 + threadIdx.x + uint64_t(u) * kBlock;
+                    if (v < v1) store16(static_cast<char*>(ptr[q]) + v * 16, y[u]);
+                }
             }
         }
         const uint64_t t = v1 * V + threadIdx.x;  // ragged end of the piece
