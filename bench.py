@@ -95,9 +95,36 @@ def cpu_baseline(xs_dev, reps: int):
             "seconds_per_step": round(t, 3), "host_cpus": os.cpu_count()}
 
 
+def graph_time_us(torch, fn, per_graph: int = 20, replays: int = 5) -> float:
+    """GPU time per call of fn(): per_graph calls captured in one HIP graph,
+    replayed `replays` times back to back; host enqueue cost is excluded."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the launch path outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (per_graph * replays)
+
+
 def sweep(dt, torch, steps: int, warmup: int):
-    """fp32 one-shot AllReduce, P=16, per-rank sizes 4 KiB .. 1 GiB (x4), and
-    the alpha-beta fit T(S) = alpha + 2*P*S / B_eff (weights 1/T^2)."""
+    """fp32 one-shot AllReduce, P=16, per-rank sizes 4 KiB .. 1 GiB (x4).
+    Each point is timed two ways: eager launches bracketed by events (what a
+    Python caller sees, host enqueue included) and graph replay (GPU time per
+    launch).  The alpha-beta fit T(S) = alpha + 2*P*S / B_eff (weights 1/T^2)
+    uses the graph times."""
     import numpy as np
     import synth
     rows = []
@@ -111,11 +138,14 @@ def sweep(dt, torch, steps: int, warmup: int):
             dt.dt_allreduce(xs, ys)
         evs = time_launches(lambda: dt.dt_allreduce(xs, ys), steps, stream)
         torch.cuda.synchronize()
-        us = statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3
+        eager_us = statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3
+        per_graph = 20 if nbytes <= (16 << 20) else 4
+        us = graph_time_us(torch, lambda: dt.dt_allreduce(xs, ys), per_graph=per_graph, replays=5)
         hbm = 2 * p * nbytes / (us * 1e-6) / 1e9
         busbw = nbytes / (us * 1e-6) * 2 * (p - 1) / p / 1e9
-        rows.append({"bytes_per_rank": nbytes, "us": round(us, 3), "hbm_GBps": round(hbm, 1),
-                     "busbw_GBps": round(busbw, 1), "frac_of_peak": round(hbm / HBM_PEAK_GBPS, 4)})
+        rows.append({"bytes_per_rank": nbytes, "us": round(us, 3), "eager_us": round(eager_us, 3),
+                     "hbm_GBps": round(hbm, 1), "busbw_GBps": round(busbw, 1),
+                     "frac_of_peak": round(hbm / HBM_PEAK_GBPS, 4)})
         print(json.dumps({"sweep": rows[-1]}), flush=True)
         del xs, ys
         torch.cuda.empty_cache()
@@ -124,9 +154,75 @@ def sweep(dt, torch, steps: int, warmup: int):
     a = np.stack([np.ones_like(s), 2 * p * s], axis=1) / t[:, None]
     coef, *_ = np.linalg.lstsq(a, np.ones_like(t), rcond=None)
     alpha, inv_b = coef
-    fit = {"alpha_us": round(alpha * 1e6, 3), "B_eff_GBps": round(1 / inv_b / 1e9, 1) if inv_b > 0 else None}
+    fit = {"alpha_us": round(alpha * 1e6, 3), "B_eff_GBps": round(1 / inv_b / 1e9, 1) if inv_b > 0 else None,
+           "model": "T(S) = alpha + 2*P*S/B_eff, P=16, graph-replay times, weights 1/T^2"}
     print(json.dumps({"sweep_fit": fit}), flush=True)
     return rows, fit
+
+
+def hsdp(dt, torch):
+    """The gradient workload: P=8, 32 layers x 9 bf16 tensors per rank
+    (103.6 GB), 25 MiB buckets.
+      replicate2_shard4: the per-layer ReduceScatter -> fused AllReduce
+        pipeline (time from the first post_backward to the consumer's wait);
+      ddp_bucket: pure data parallel, each layer's tensors AllReduced in
+        place in 25 MiB buckets (dt_bucket_allreduce, no staging copies)."""
+    import numpy as np
+    import synth
+    out = {}
+    layers = [synth.layer_grads(P, layer=l, seed=0, device="cuda") for l in range(synth.NUM_LAYERS)]
+    numels = [int(np.prod(s)) for s in synth.LAYER_SHAPES]
+    per_rank_layer = sum(numels) * 2
+
+    def timed(run, reps=3):
+        times = []
+        for it in range(reps + 1):
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            a.record()
+            run()
+            b.record()
+            host_ms = (time.perf_counter() - t0) * 1e3
+            torch.cuda.synchronize()
+            if it > 0:  # the first pass warms up
+                times.append((a.elapsed_time(b), host_ms))
+        return statistics.median(t for t, _ in times), statistics.median(h for _, h in times)
+
+    rep, sh = 2, 4
+    fused = [[torch.empty(sum(numels) // sh, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+             for _ in range(synth.NUM_LAYERS)]
+    pipe = dt.HSDPPipeline(rep, sh, bucket_bytes=synth.BUCKET_BYTES)
+
+    def run_hsdp():
+        for l in reversed(range(synth.NUM_LAYERS)):
+            pipe.post_backward(layers[l], fused[l])
+        pipe.finish()
+
+    ms, host_ms = timed(run_hsdp)
+    # ReduceScatter: per shard group, shard reads + 1 write of one rank's layer
+    # bytes; fused AllReduce: read + write of every rank's fused buffer
+    total = synth.NUM_LAYERS * (rep * (sh + 1) * per_rank_layer + 2 * P * (per_rank_layer // sh))
+    out["replicate2_shard4"] = {"ms": round(ms, 3), "host_enqueue_ms": round(host_ms, 3), "alg_bytes": total,
+                                "hbm_GBps": round(total / (ms * 1e-3) / 1e9, 1),
+                                "frac_of_peak": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    print(json.dumps({"hsdp": out}), flush=True)
+    del fused, pipe
+    torch.cuda.empty_cache()
+
+    def run_ddp():
+        for l in reversed(range(synth.NUM_LAYERS)):
+            dt.dt_bucket_allreduce(layers[l], bucket_bytes=synth.BUCKET_BYTES)
+
+    ms, host_ms = timed(run_ddp)
+    total = synth.NUM_LAYERS * 2 * P * per_rank_layer
+    out["ddp_bucket"] = {"ms": round(ms, 3), "host_enqueue_ms": round(host_ms, 3), "alg_bytes": total,
+                         "hbm_GBps": round(total / (ms * 1e-3) / 1e9, 1),
+                         "frac_of_peak": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    print(json.dumps({"hsdp": out}), flush=True)
+    del layers
+    torch.cuda.empty_cache()
+    return out
 
 
 def barrier_latency(dt, torch):
@@ -184,6 +280,7 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=25)
     ap.add_argument("--sweep", action="store_true", help="also run the P=16 size sweep and barrier latency")
     ap.add_argument("--probe", action="store_true", help="only run the kernels for a hardware-counter pass")
+    ap.add_argument("--hsdp", action="store_true", help="also time the 32-layer gradient pipeline (103.6 GB)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -275,6 +372,8 @@ def main():
         extra["sweep_p16_fp32"] = rows
         extra["alpha_beta_fit"] = fit
         extra["barrier"] = barrier_latency(dt, torch)
+    if args.hsdp:
+        extra["hsdp"] = hsdp(dt, torch)
 
     cpu = None
     if not args.no_cpu_baseline:

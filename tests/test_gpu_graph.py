@@ -1,0 +1,54 @@
+"""GPU: the collectives captured in a HIP graph replay correctly.  The inputs
+are rewritten eagerly between replays, with synchronizations in between, and
+every replay is checked against the oracle on that replay's inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import compare, note, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dt():
+    import collective_communication_primitives_amd as m
+    return m
+
+
+def test_graph_replays_allreduce_rs_ag(dt):
+    orc = oracle.get()
+    p, n = 8, 8 * 4099
+    xs = [torch.empty(n, device="cuda") for _ in range(p)]
+    ys = [torch.empty(n, device="cuda") for _ in range(p)]
+    shards = [torch.empty(n // p, device="cuda") for _ in range(p)]
+    full = [torch.empty(n, device="cuda") for _ in range(p)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dt.dt_allreduce(xs, ys)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    note("graph capture of allreduce + reduce_scatter + all_gather")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dt.dt_allreduce(xs, ys)
+        dt.dt_reduce_scatter(xs, shards)
+        dt.dt_all_gather(shards, full)
+    for replay in range(4):
+        note(f"graph replay {replay}")
+        vals = synth.uniform_ranks(p, n, seed=50 + replay, device="cuda")
+        for x, v in zip(xs, vals):
+            x.copy_(v)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        host = [to_np(x) for x in xs]
+        want = orc.allreduce(host, "sum")
+        want_rs = orc.reduce_scatter(host, "sum")
+        for q in range(p):
+            compare(to_np(ys[q]), want[q], f"replay {replay} AR rank {q}")
+            compare(to_np(shards[q]), want_rs[q], f"replay {replay} RS rank {q}")
+            compare(to_np(full[q]), np.concatenate(want_rs), f"replay {replay} AG rank {q}")
