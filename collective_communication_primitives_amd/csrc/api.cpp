@@ -18,6 +18,7 @@ static_assert(sizeof(dt::PieceArgs) <= 4096, "kernel arguments must stay below 4
 static_assert(sizeof(dt::GatherArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::AllToAllArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::ExchangeArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+static_assert(sizeof(dt::SegReduceScatterArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(DT_MAX_RANKS == dt::kMaxRanksHost, "rank limit mismatch");
 
 namespace {
@@ -111,6 +112,48 @@ dt_status allreduce_impl(const void* const* send, void* const* recv, int nranks,
         return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "allreduce (element path) launch");
     }
     return DT_OK;
+}
+
+// ReduceScatter of many independent segments, as few launches as the
+// argument block allows.  seg_src[k][j] / seg_dst[k][j]: member j of segment k.
+dt_status reduce_scatter_segments(const std::vector<std::vector<const void*>>& seg_src,
+                                  const std::vector<std::vector<void*>>& seg_dst, const std::vector<size_t>& seg_m,
+                                  int nranks, dt_dtype dtype, dt_op op, hipStream_t stream) {
+    const size_t v = vec_elems(dtype);
+    const uint64_t tile_elems = dt::seg_rs_tile_vecs(nranks) * v;
+    const int per_launch = std::min(dt::kMaxSegs, dt::kSegPtrs / nranks);
+    dt::SegReduceScatterArgs a = {};
+    auto flush = [&]() -> dt_status {
+        if (a.nsegs == 0) return DT_OK;
+        dt_status st = check_hip(dt::launch_reduce_scatter_segs(a, dtype, op, stream), "segmented reduce_scatter");
+        a = dt::SegReduceScatterArgs{};
+        return st;
+    };
+    uint64_t tiles = 0;
+    for (size_t k = 0; k < seg_m.size(); k++) {
+        if (seg_m[k] == 0) continue;
+        if (a.nsegs == per_launch) {
+            dt_status st = flush();
+            if (st != DT_OK) return st;
+            tiles = 0;
+        }
+        const int i = a.nsegs++;
+        a.nranks = nranks;
+        bool al = seg_m[k] % v == 0;
+        for (int j = 0; j < nranks; j++) {
+            a.src[i * nranks + j] = seg_src[k][j];
+            a.dst[i * nranks + j] = seg_dst[k][j];
+            al = al && aligned16(seg_src[k][j]) && aligned16(seg_dst[k][j]);
+        }
+        if (al) a.aligned |= 1u << i;
+        a.m[i] = seg_m[k];
+        a.tiles_per_chunk[i] = uint32_t((seg_m[k] + tile_elems - 1) / tile_elems);
+        a.tile_start[i] = uint32_t(tiles);
+        tiles += uint64_t(a.tiles_per_chunk[i]) * nranks;
+        if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "segmented reduce_scatter too large for one launch");
+        a.tile_start[i + 1] = uint32_t(tiles);
+    }
+    return flush();
 }
 
 // ---------------------------------------------------------- bucket plan --
@@ -544,16 +587,31 @@ dt_status hsdp_issue_prev_allreduce(dt_hsdp* h) {
     dt_status st;
     const size_t es = esize_of(h->dtype);
     const size_t per_bucket = h->bucket_bytes / es;
-    std::vector<const void*> src(h->replicate);
-    std::vector<void*> dst(h->replicate);
+    // one launch per bucket covers every replicate group: piece j is group j's
+    // slice [start, start + len) of its members' fused buffers, reduced in place
+    const int per_launch = std::min(dt::kMaxPieces, dt::kPiecePtrs / h->replicate);
     for (size_t start = 0; start < h->prev_total; start += per_bucket) {
         const size_t len = std::min(per_bucket, h->prev_total - start);
-        for (int j = 0; j < h->shard; j++) {
-            for (int i = 0; i < h->replicate; i++) {
-                dst[i] = static_cast<char*>(h->prev_fused[size_t(i) * h->shard + j]) + start * es;
-                src[i] = dst[i];
+        for (int j0 = 0; j0 < h->shard; j0 += per_launch) {
+            dt::PieceArgs a = {};
+            a.nranks = h->replicate;
+            a.npieces = std::min(per_launch, h->shard - j0);
+            uint64_t tiles = 0;
+            for (int k = 0; k < a.npieces; k++) {
+                bool al = true;
+                for (int i = 0; i < h->replicate; i++) {
+                    char* p = static_cast<char*>(h->prev_fused[size_t(i) * h->shard + j0 + k]) + start * es;
+                    a.ptr[k * h->replicate + i] = p;
+                    al = al && aligned16(p);
+                }
+                if (al) a.aligned |= 1u << k;
+                a.len[k] = len;
+                a.tile_start[k] = uint32_t(tiles);
+                tiles += (len * es + dt::kPieceTileVecs * 16 - 1) / (dt::kPieceTileVecs * 16);
             }
-            if ((st = allreduce_impl(src.data(), dst.data(), h->replicate, len, h->dtype, h->op, h->ar_stream)) != DT_OK)
+            if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "bucket too large for one launch");
+            a.tile_start[a.npieces] = uint32_t(tiles);
+            if ((st = check_hip(dt::launch_reduce_pieces(a, h->dtype, h->op, h->ar_stream), "fused AllReduce")) != DT_OK)
                 return st;
         }
     }
@@ -625,22 +683,29 @@ dt_status dt_hsdp_post_backward(dt_hsdp* h, const void* const* grads, const size
     if ((st = check_hip(hipEventRecord(h->produced, producer), "record producer")) != DT_OK) return st;
     if ((st = check_hip(hipStreamWaitEvent(h->rs_stream, h->produced, 0), "RS stream waits producer")) != DT_OK)
         return st;
-    std::vector<const void*> src(h->shard);
-    std::vector<void*> dst(h->shard);
+    // every tensor of every shard group is one segment of one launch
+    std::vector<std::vector<const void*>> seg_src;
+    std::vector<std::vector<void*>> seg_dst;
+    std::vector<size_t> seg_m;
     size_t at = 0;
     for (int t = 0; t < ntensors; t++) {
         const size_t m = numels[t] / size_t(h->shard);
         for (int i = 0; i < h->replicate; i++) {
+            std::vector<const void*> src(h->shard);
+            std::vector<void*> dst(h->shard);
             for (int j = 0; j < h->shard; j++) {
                 const int r = i * h->shard + j;
                 src[j] = grads[size_t(r) * ntensors + t];
                 dst[j] = static_cast<char*>(fused[r]) + at * es;
             }
-            if ((st = dt_reduce_scatter(src.data(), dst.data(), h->shard, m, h->dtype, h->op, h->rs_stream)) != DT_OK)
-                return st;
+            seg_src.push_back(src);
+            seg_dst.push_back(dst);
+            seg_m.push_back(m);
         }
         at += m;
     }
+    if ((st = reduce_scatter_segments(seg_src, seg_dst, seg_m, h->shard, h->dtype, h->op, h->rs_stream)) != DT_OK)
+        return st;
     const int cur_slot = h->prev_slot ^ 1;
     if ((st = check_hip(hipEventRecord(h->rs_done[cur_slot], h->rs_stream), "record RS done")) != DT_OK) return st;
     // 3. issue the previous layer's fused AllReduce (its wait is queued above)

@@ -37,6 +37,22 @@ struct PieceArgs {
     int nranks;
 };
 
+// Several independent ReduceScatters in one launch (one per segment, all of
+// nranks members): segment k's member j reads src[k*nranks + j] (nranks*m[k]
+// elements) and writes chunk j of the fold to dst[k*nranks + j] (m[k]).
+constexpr int kSegPtrs = 160;
+constexpr int kMaxSegs = 32;
+struct SegReduceScatterArgs {
+    const void* src[kSegPtrs];
+    void* dst[kSegPtrs];
+    uint64_t m[kMaxSegs];
+    uint32_t tile_start[kMaxSegs + 1];
+    uint32_t tiles_per_chunk[kMaxSegs];
+    uint32_t aligned;      // bit k: segment k may use 16-byte vectors
+    int nsegs;
+    int nranks;
+};
+
 // AllGather: rank r's bytes [0, bytes[r]) land at offset[r] of every output.
 struct GatherArgs {
     const void* src[kMaxRanksHost];
@@ -85,6 +101,9 @@ constexpr uint64_t kPieceTileVecs = 512;     // bucket pieces: 512 x 16 B
 hipError_t launch_reduce_vec(const ReduceArgs& a, int dtype, int op, hipStream_t s);
 hipError_t launch_reduce_elems(const ReduceArgs& a, int dtype, int op, hipStream_t s);
 hipError_t launch_reduce_pieces(const PieceArgs& a, int dtype, int op, hipStream_t s);
+hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, int op, hipStream_t s);
+// Output vectors per workgroup tile of the segmented ReduceScatter for P ranks.
+uint64_t seg_rs_tile_vecs(int nranks);
 hipError_t launch_copy_pieces(const PieceArgs& a, int esize, int to_ws, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s);
 hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t s);

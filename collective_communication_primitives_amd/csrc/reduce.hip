@@ -154,6 +154,53 @@ __global__ __launch_bounds__(kBlock) void k_reduce_pieces(PieceArgs a) {
     }
 }
 
+// ------------------------------------------------ segmented ReduceScatter --
+// Many ReduceScatters (e.g. every tensor of one layer, in every shard group)
+// in one launch, so the chip never drains between small collectives.  A tile
+// is U*kBlock output vectors of one chunk j of one segment k; the workgroup
+// folds member 0..P-1's vectors of that chunk in rank order.
+template <int DT, int OP, int PMAX, bool EXACT, int U>
+__global__ __launch_bounds__(kBlock) void k_reduce_scatter_segs(SegReduceScatterArgs a) {
+    constexpr int V = Elems<DT>::value;
+    const uint32_t b = blockIdx.x;
+    int k = 0;
+    while (k + 1 < a.nsegs && a.tile_start[k + 1] <= b) k++;
+    const int nr = EXACT ? PMAX : a.nranks;
+    const uint32_t t = b - a.tile_start[k];
+    const uint32_t j = t / a.tiles_per_chunk[k];   // output chunk = member
+    const uint32_t tt = t - j * a.tiles_per_chunk[k];
+    const uint64_t m = a.m[k];
+    const void* const* src = a.src + k * nr;
+    void* dst = a.dst[k * nr + j];
+    if ((a.aligned >> k) & 1u) {
+        const uint64_t mv = m / V;
+        const uint64_t in_off = uint64_t(j) * mv * 16;
+        const uint64_t base = uint64_t(tt) * (kBlock * U) + threadIdx.x;
+        u32x4 x[U][PMAX];
+#pragma unroll
+        for (int r = 0; r < PMAX; r++) {
+            if (r < nr) {
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const uint64_t v = base + uint64_t(u) * kBlock;
+                    if (v < mv) x[u][r] = load16(static_cast<const char*>(src[r]) + in_off + v * 16);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint64_t v = base + uint64_t(u) * kBlock;
+            if (v < mv) store16_h<false>(static_cast<char*>(dst) + v * 16, fold_vec<DT, OP, PMAX>(x[u], nr));
+        }
+    } else {
+        const uint64_t per_tile = uint64_t(kBlock) * U * V;
+        const uint64_t e0 = uint64_t(tt) * per_tile;
+        const uint64_t e1 = min(m, e0 + per_tile);
+        for (uint64_t e = e0 + threadIdx.x; e < e1; e += kBlock)
+            fold_elem<DT, OP>(src, nr, uint64_t(j) * m + e, dst, e);
+    }
+}
+
 // Flatten (to_ws = 1) or unflatten (to_ws = 0) the pieces of one bucket for
 // rank blockIdx.y: a byte copy between the tensors and the bucket buffer.
 __global__ __launch_bounds__(kBlock) void k_copy_pieces(PieceArgs a, int esize, int to_ws) {
@@ -186,29 +233,31 @@ int pmax_of(int nranks) {
     return nranks <= 1 ? 1 : nranks <= 2 ? 2 : nranks <= 4 ? 4 : nranks <= 8 ? 8 : 16;
 }
 
-// Vectors per thread: enough independent 16-byte loads in flight per thread
-// (PMAX x U) while keeping the register footprint modest.
-template <int PMAX>
-constexpr int unroll_of() { return PMAX >= 16 ? 1 : PMAX == 8 ? 2 : 4; }
+// Vectors per thread (U), measured on the MI355X for 25-256 MiB per rank:
+// two per thread for every AllReduce and for ReduceScatter with P >= 8, four
+// for ReduceScatter with P <= 4 and for the plain copy of P = 1.
+template <int PMAX, bool RS>
+constexpr int unroll_of() { return PMAX == 1 ? 4 : (RS && PMAX <= 4) ? 4 : 2; }
 
 template <int DT, int OP, int PMAX>
 hipError_t reduce_vec_p(const ReduceArgs& a, hipStream_t s) {
-    constexpr int U = unroll_of<PMAX>();
-    const uint64_t blocks = (a.count + kBlock * U - 1) / (kBlock * U);
+    constexpr int URS = unroll_of<PMAX, true>(), UAR = unroll_of<PMAX, false>();
+    const uint64_t per_block = uint64_t(kBlock) * (a.rs ? URS : UAR);
+    const uint64_t blocks = (a.count + per_block - 1) / per_block;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
     dim3 grid(unsigned(blocks), a.rs ? unsigned(a.nranks) : 1u);
     const bool exact = a.nranks == PMAX;
     if (a.rs) {
         if (exact)
-            k_reduce_vec<DT, OP, PMAX, true, U, true><<<grid, kBlock, 0, s>>>(a);
+            k_reduce_vec<DT, OP, PMAX, true, URS, true><<<grid, kBlock, 0, s>>>(a);
         else
-            k_reduce_vec<DT, OP, PMAX, false, U, true><<<grid, kBlock, 0, s>>>(a);
+            k_reduce_vec<DT, OP, PMAX, false, URS, true><<<grid, kBlock, 0, s>>>(a);
     } else {
         if (exact)
-            k_reduce_vec<DT, OP, PMAX, true, U, false><<<grid, kBlock, 0, s>>>(a);
+            k_reduce_vec<DT, OP, PMAX, true, UAR, false><<<grid, kBlock, 0, s>>>(a);
         else
-            k_reduce_vec<DT, OP, PMAX, false, U, false><<<grid, kBlock, 0, s>>>(a);
+            k_reduce_vec<DT, OP, PMAX, false, UAR, false><<<grid, kBlock, 0, s>>>(a);
     }
     return hipGetLastError();
 }
@@ -283,7 +332,57 @@ hipError_t reduce_pieces_dt(const PieceArgs& a, int op, hipStream_t s) {
     }
 }
 
+template <int DT, int OP, int PMAX>
+hipError_t reduce_scatter_segs_p(const SegReduceScatterArgs& a, hipStream_t s) {
+    constexpr int U = unroll_of<PMAX, true>();
+    const uint32_t tiles = a.tile_start[a.nsegs];
+    if (tiles == 0) return hipSuccess;
+    if (a.nranks == PMAX)
+        k_reduce_scatter_segs<DT, OP, PMAX, true, U><<<tiles, kBlock, 0, s>>>(a);
+    else
+        k_reduce_scatter_segs<DT, OP, PMAX, false, U><<<tiles, kBlock, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int DT, int OP>
+hipError_t reduce_scatter_segs_op(const SegReduceScatterArgs& a, hipStream_t s) {
+    switch (pmax_of(a.nranks)) {
+        case 1: return reduce_scatter_segs_p<DT, OP, 1>(a, s);
+        case 2: return reduce_scatter_segs_p<DT, OP, 2>(a, s);
+        case 4: return reduce_scatter_segs_p<DT, OP, 4>(a, s);
+        case 8: return reduce_scatter_segs_p<DT, OP, 8>(a, s);
+        default: return reduce_scatter_segs_p<DT, OP, 16>(a, s);
+    }
+}
+
+template <int DT>
+hipError_t reduce_scatter_segs_dt(const SegReduceScatterArgs& a, int op, hipStream_t s) {
+    switch (op) {
+        case kSum: return reduce_scatter_segs_op<DT, kSum>(a, s);
+        case kMax: return reduce_scatter_segs_op<DT, kMax>(a, s);
+        default: return reduce_scatter_segs_op<DT, kMin>(a, s);
+    }
+}
+
 }  // namespace
+
+uint64_t seg_rs_tile_vecs(int nranks) {
+    switch (pmax_of(nranks)) {
+        case 1: return uint64_t(kBlock) * unroll_of<1, true>();
+        case 2: return uint64_t(kBlock) * unroll_of<2, true>();
+        case 4: return uint64_t(kBlock) * unroll_of<4, true>();
+        case 8: return uint64_t(kBlock) * unroll_of<8, true>();
+        default: return uint64_t(kBlock) * unroll_of<16, true>();
+    }
+}
+
+hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, int op, hipStream_t s) {
+    switch (dtype) {
+        case kF32: return reduce_scatter_segs_dt<kF32>(a, op, s);
+        case kBF16: return reduce_scatter_segs_dt<kBF16>(a, op, s);
+        default: return reduce_scatter_segs_dt<kI32>(a, op, s);
+    }
+}
 
 hipError_t launch_reduce_vec(const ReduceArgs& a, int dtype, int op, hipStream_t s) {
     switch (dtype) {
