@@ -226,27 +226,31 @@ def hsdp(dt, torch):
 
 
 def barrier_latency(dt, torch):
-    """P=16 signal-window barrier: 1000 generations in one launch, and 1000
-    single-generation launches."""
+    """P=16 signal-window barrier, both layouts: 1000 generations in one
+    launch (us per generation), and 1000 single-generation launches queued
+    eagerly from Python (us per launch).  Graph replay cannot time a barrier:
+    its thresholds would be frozen into the graph."""
     p = 16
-    ws = [torch.zeros(p, dtype=torch.int32, device="cuda") for _ in range(p)]
-    status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    dt.dt_barrier(ws, status, 1, 10)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    dt.dt_barrier(ws, status, 11, 1000)
-    b.record()
-    torch.cuda.synchronize()
-    in_kernel = a.elapsed_time(b) * 1e3 / 1000
-    a.record()
-    for g in range(1011, 2011):
-        dt.dt_barrier(ws, status, g, 1)
-    b.record()
-    torch.cuda.synchronize()
-    per_launch = a.elapsed_time(b) * 1e3 / 1000
-    assert int(status.item()) == 0
-    out = {"P": p, "us_per_generation_in_kernel": round(in_kernel, 3), "us_per_launch": round(per_launch, 3)}
+    out = {"P": p}
+    for layout in ("packed", "spread"):
+        ws = [torch.zeros(p, dtype=torch.int32, device="cuda") for _ in range(p)]
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        dt.dt_barrier(ws, status, 1, 10, layout=layout)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dt.dt_barrier(ws, status, 11, 1000, layout=layout)
+        b.record()
+        torch.cuda.synchronize()
+        in_kernel = a.elapsed_time(b) * 1e3 / 1000
+        a.record()
+        for g in range(1011, 2011):
+            dt.dt_barrier(ws, status, g, 1, layout=layout)
+        b.record()
+        torch.cuda.synchronize()
+        per_launch = a.elapsed_time(b) * 1e3 / 1000
+        out[layout] = {"us_per_generation_in_kernel": round(in_kernel, 3), "us_per_launch_eager": round(per_launch, 3)}
+        assert int(status.item()) == 0
     print(json.dumps({"barrier": out}), flush=True)
     return out
 

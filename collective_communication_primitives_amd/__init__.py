@@ -254,9 +254,15 @@ def dt_bucket_plan(numels: Sequence[int], elem_size: int, bucket_bytes: int = DE
 
 
 # ------------------------------------------------------------------ barrier --
+DT_BARRIER_PACKED, DT_BARRIER_SPREAD = 0, 1
+_LAYOUTS = {"packed": DT_BARRIER_PACKED, "spread": DT_BARRIER_SPREAD}
+
+
 def dt_barrier(windows: Sequence[torch.Tensor], status: torch.Tensor, first_generation: int, generations: int = 1,
-               timeout_ns: int = 0, stream=None) -> None:
-    """Signal-window barrier over int32 windows[p] (nranks cells each)."""
+               timeout_ns: int = 0, layout="packed", stream=None) -> None:
+    """Signal-window barrier over int32 windows[p] (nranks cells each);
+    layout "packed" (one workgroup, a wave per rank) or "spread" (a
+    workgroup per rank, cooperative launch)."""
     p = len(windows)
     for w in windows:
         if w.dtype != torch.int32 or w.numel() < p or not w.is_contiguous():
@@ -264,13 +270,13 @@ def dt_barrier(windows: Sequence[torch.Tensor], status: torch.Tensor, first_gene
     if status.dtype != torch.int32:
         raise ValueError("status must be an int32 device tensor")
     w_arr = _ptr_array(windows)
-    _check(_L.dt_barrier(w_arr, p, first_generation, generations, status.data_ptr(), timeout_ns,
+    _check(_L.dt_barrier(w_arr, p, first_generation, generations, status.data_ptr(), timeout_ns, _LAYOUTS[layout],
                          _stream_handle(stream)))
 
 
 def dt_barrier_exchange(src: Sequence[torch.Tensor], stage: Sequence[torch.Tensor], dst: Sequence[torch.Tensor],
                         windows: Sequence[torch.Tensor], status: torch.Tensor, generation: int, timeout_ns: int = 0,
-                        stream=None) -> None:
+                        layout="packed", stream=None) -> None:
     """Stage src[r], meet the barrier, then dst[r] = stage[(r+1) % P]."""
     p = len(src)
     nbytes = src[0].numel() * src[0].element_size()
@@ -278,7 +284,8 @@ def dt_barrier_exchange(src: Sequence[torch.Tensor], stage: Sequence[torch.Tenso
         if len(group) != p or any(t.numel() * t.element_size() != nbytes or not t.is_contiguous() for t in group):
             raise ValueError("src, stage and dst need one contiguous buffer of equal bytes per rank")
     _check(_L.dt_barrier_exchange(_ptr_array(src), _ptr_array(stage), _ptr_array(dst), nbytes, _ptr_array(windows),
-                                  p, generation, status.data_ptr(), timeout_ns, _stream_handle(stream)))
+                                  p, generation, status.data_ptr(), timeout_ns, _LAYOUTS[layout],
+                                  _stream_handle(stream)))
 
 
 # -------------------------------------------------------------- HSDP -------

@@ -37,8 +37,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         "dt_all_gather": [vp, vp, i32, vp, sz, i32, vp],
         "dt_all_to_all": [vp, vp, i32, vp, i32, vp],
         "dt_bucket_allreduce": [vp, vp, i32, i32, sz, vp, i32, i32, vp],
-        "dt_barrier": [vp, i32, ctypes.c_int32, ctypes.c_int32, vp, u64, vp],
-        "dt_barrier_exchange": [vp, vp, vp, sz, vp, i32, ctypes.c_int32, vp, u64, vp],
+        "dt_barrier": [vp, i32, ctypes.c_int32, ctypes.c_int32, vp, u64, i32, vp],
+        "dt_barrier_exchange": [vp, vp, vp, sz, vp, i32, ctypes.c_int32, vp, u64, i32, vp],
         "dt_bucket_plan": [vp, i32, sz, sz, vp, sz, vp, vp],
         "dt_work_begin": [vp, vp, vp],
         "dt_work_end": [vp, vp],

@@ -458,7 +458,7 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
 }
 
 dt_status dt_barrier(int32_t* const* windows, int nranks, int32_t first_generation, int32_t generations,
-                     int32_t* status_dev, uint64_t timeout_ns, hipStream_t stream) {
+                     int32_t* status_dev, uint64_t timeout_ns, int layout, hipStream_t stream) {
     g_last_error.clear();
     dt_status st = check_ranks(nranks);
     if (st != DT_OK) return st;
@@ -466,6 +466,7 @@ dt_status dt_barrier(int32_t* const* windows, int nranks, int32_t first_generati
     if (status_dev == nullptr) return fail(DT_ERR_ARG, "status_dev is NULL");
     if (first_generation < 1 || generations < 0 || int64_t(first_generation) + generations - 1 > INT32_MAX)
         return fail(DT_ERR_ARG, "generations %d..%d out of range", first_generation, first_generation + generations - 1);
+    if (layout != DT_BARRIER_PACKED && layout != DT_BARRIER_SPREAD) return fail(DT_ERR_ARG, "bad layout %d", layout);
     if (generations == 0) return DT_OK;
     dt::BarrierArgs a = {};
     for (int r = 0; r < nranks; r++) a.win[r] = windows[r];
@@ -474,12 +475,12 @@ dt_status dt_barrier(int32_t* const* windows, int nranks, int32_t first_generati
     a.nranks = nranks;
     a.first_generation = first_generation;
     a.generations = generations;
-    return check_hip(dt::launch_barrier(a, stream), "barrier cooperative launch");
+    return check_hip(dt::launch_barrier(a, layout == DT_BARRIER_SPREAD, stream), "barrier launch");
 }
 
 dt_status dt_barrier_exchange(const void* const* src, void* const* stage, void* const* dst, size_t nbytes,
                               int32_t* const* windows, int nranks, int32_t generation, int32_t* status_dev,
-                              uint64_t timeout_ns, hipStream_t stream) {
+                              uint64_t timeout_ns, int layout, hipStream_t stream) {
     g_last_error.clear();
     dt_status st = check_ranks(nranks);
     if (st != DT_OK) return st;
@@ -489,6 +490,7 @@ dt_status dt_barrier_exchange(const void* const* src, void* const* stage, void* 
     if ((st = check_ptr_array(dst, nranks, "dst")) != DT_OK) return st;
     if (status_dev == nullptr) return fail(DT_ERR_ARG, "status_dev is NULL");
     if (generation < 1) return fail(DT_ERR_ARG, "generation %d must be >= 1", generation);
+    if (layout != DT_BARRIER_PACKED && layout != DT_BARRIER_SPREAD) return fail(DT_ERR_ARG, "bad layout %d", layout);
     dt::ExchangeArgs a = {};
     for (int r = 0; r < nranks; r++) {
         a.bar.win[r] = windows[r];
@@ -502,7 +504,7 @@ dt_status dt_barrier_exchange(const void* const* src, void* const* stage, void* 
     a.bar.first_generation = generation;
     a.bar.generations = 1;
     a.nbytes = nbytes;
-    return check_hip(dt::launch_exchange(a, stream), "barrier exchange cooperative launch");
+    return check_hip(dt::launch_exchange(a, layout == DT_BARRIER_SPREAD, stream), "barrier exchange launch");
 }
 
 // ------------------------------------------------------------ work handles --

@@ -7,15 +7,19 @@
 // threshold by one per generation (the page's edge-case table), so nothing
 // has to be reset between calls.
 //
-// One workgroup per rank, launched cooperatively so that all P workgroups are
-// resident at once (a spin-wait across workgroups that were not co-resident
-// could never finish).  Within the rank's first wave, lane p notifies peer p
-// and lane s watches cell s, so the P-1 notifies and P-1 waits of the page's
-// cost card run in parallel.  The MI355X has eight XCDs, each with its own
-// L2: notifies are device-scope release atomics and waits device-scope
-// acquire loads, which make the signalling (and the data it guards) coherent
-// across XCDs.  Every wait is bounded by a wall-clock budget; on expiry the
-// workgroup records DT_ERR_TIMEOUT (4) and leaves, so no launch can hang.
+// Each rank is one 64-wide wave: lane p notifies peer p and lane s watches
+// cell s, so the P-1 notifies and P-1 waits of the page's cost card run in
+// parallel.  Two layouts:
+//   packed (default): all P waves in ONE workgroup (P <= 16 -> <= 1024
+//     threads).  A workgroup is always resident as a whole, so the spin-waits
+//     cannot starve, and the launch is an ordinary one.
+//   spread: one workgroup per rank, launched cooperatively so all P are
+//     resident at once; the ranks then sit on different CUs and XCDs.
+// Notifies are device-scope release atomics and waits device-scope acquire
+// loads: the MI355X's eight XCDs each have their own L2, and device scope is
+// what makes the window (and the data it guards) coherent across them.  Every
+// wait is bounded by a wall-clock budget; on expiry the wave records
+// DT_ERR_TIMEOUT (4) and leaves, so no launch can hang.
 #include "dt_device.h"
 #include "dt_launch.h"
 
@@ -23,10 +27,9 @@ namespace dt {
 
 constexpr int kTimeoutStatus = 4;
 
-// One generation for rank r, executed by one full wave.  Returns false on
-// timeout (wave-uniform).
-__device__ bool barrier_round(const BarrierArgs& a, int r, int g) {
-    const int lane = threadIdx.x;
+// One generation for rank r, executed by one full wave (lane = 0..63).
+// Returns false on timeout (wave-uniform).
+__device__ bool barrier_round(const BarrierArgs& a, int r, int g, int lane) {
     const bool peer = lane < a.nranks && lane != r;
     if (peer) __hip_atomic_fetch_add(a.win[lane] + r, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t start = wall_clock64();
@@ -41,53 +44,85 @@ __device__ bool barrier_round(const BarrierArgs& a, int r, int g) {
     }
 }
 
-__global__ __launch_bounds__(64) void k_barrier(BarrierArgs a) {
+// spread: blockIdx.x = rank, one wave per workgroup
+__global__ __launch_bounds__(64) void k_barrier_spread(BarrierArgs a) {
     const int r = blockIdx.x;
     for (int k = 0; k < a.generations; k++)
-        if (!barrier_round(a, r, a.first_generation + k)) return;
+        if (!barrier_round(a, r, a.first_generation + k, threadIdx.x)) return;
 }
 
-__device__ void copy_bytes(char* to, const char* from, uint64_t n) {
+// packed: one workgroup, wave w = rank w
+__global__ __launch_bounds__(1024) void k_barrier_packed(BarrierArgs a) {
+    const int r = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    for (int k = 0; k < a.generations; k++)
+        if (!barrier_round(a, r, a.first_generation + k, lane)) return;
+}
+
+// Byte copy by `n_threads` cooperating threads (index `tid`).
+__device__ void copy_bytes(char* to, const char* from, uint64_t n, uint32_t tid, uint32_t n_threads) {
     const bool vec = ((reinterpret_cast<uintptr_t>(to) | reinterpret_cast<uintptr_t>(from)) & 15) == 0;
     uint64_t done = 0;
     if (vec) {
         const uint64_t nv = n / 16;
-        for (uint64_t v = threadIdx.x; v < nv; v += blockDim.x)
+        for (uint64_t v = tid; v < nv; v += n_threads)
             *reinterpret_cast<u32x4*>(to + v * 16) = *reinterpret_cast<const u32x4*>(from + v * 16);
         done = nv * 16;
     }
-    for (uint64_t t = done + threadIdx.x; t < n; t += blockDim.x) to[t] = from[t];
+    for (uint64_t t = done + tid; t < n; t += n_threads) to[t] = from[t];
 }
 
-// Stage, barrier, then read the next rank's stage: dst[r] = src[(r+1) % P].
-__global__ __launch_bounds__(kBlock) void k_exchange(ExchangeArgs a) {
+// spread exchange: workgroup r stages src[r], meets the barrier, then reads
+// the next rank's stage: dst[r] = src[(r+1) % P].
+__global__ __launch_bounds__(kBlock) void k_exchange_spread(ExchangeArgs a) {
     __shared__ int passed;
     const int r = blockIdx.x;
-    copy_bytes(static_cast<char*>(a.stage[r]), static_cast<const char*>(a.src[r]), a.nbytes);
+    copy_bytes(static_cast<char*>(a.stage[r]), static_cast<const char*>(a.src[r]), a.nbytes, threadIdx.x, blockDim.x);
     __threadfence();  // this workgroup's staged bytes before its notifies
     __syncthreads();
     if (threadIdx.x < 64) {
-        const bool ok = barrier_round(a.bar, r, a.bar.first_generation);
+        const bool ok = barrier_round(a.bar, r, a.bar.first_generation, threadIdx.x);
         if (threadIdx.x == 0) passed = ok ? 1 : 0;
     }
     __syncthreads();
     if (!passed) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // peers' staged bytes are visible
     const int peer = (r + 1) % a.bar.nranks;
-    copy_bytes(static_cast<char*>(a.dst[r]), static_cast<const char*>(a.stage[peer]), a.nbytes);
+    copy_bytes(static_cast<char*>(a.dst[r]), static_cast<const char*>(a.stage[peer]), a.nbytes, threadIdx.x,
+               blockDim.x);
 }
 
-hipError_t launch_barrier(const BarrierArgs& a, hipStream_t s) {
+// packed exchange: wave r of the single workgroup does rank r's part.
+__global__ __launch_bounds__(1024) void k_exchange_packed(ExchangeArgs a) {
+    const int r = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    copy_bytes(static_cast<char*>(a.stage[r]), static_cast<const char*>(a.src[r]), a.nbytes, lane, 64);
+    __threadfence();  // the wave's staged bytes before its notifies
+    if (!barrier_round(a.bar, r, a.bar.first_generation, lane)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // peers' staged bytes are visible
+    const int peer = (r + 1) % a.bar.nranks;
+    copy_bytes(static_cast<char*>(a.dst[r]), static_cast<const char*>(a.stage[peer]), a.nbytes, lane, 64);
+}
+
+hipError_t launch_barrier(const BarrierArgs& a, int spread, hipStream_t s) {
+    if (!spread) {
+        k_barrier_packed<<<1, a.nranks * 64, 0, s>>>(a);
+        return hipGetLastError();
+    }
     BarrierArgs copy = a;
     void* params[] = {&copy};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_barrier), dim3(a.nranks), dim3(64), params,
-                                      0, s);
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_barrier_spread), dim3(a.nranks), dim3(64),
+                                      params, 0, s);
 }
 
-hipError_t launch_exchange(const ExchangeArgs& a, hipStream_t s) {
+hipError_t launch_exchange(const ExchangeArgs& a, int spread, hipStream_t s) {
+    if (!spread) {
+        k_exchange_packed<<<1, a.bar.nranks * 64, 0, s>>>(a);
+        return hipGetLastError();
+    }
     ExchangeArgs copy = a;
     void* params[] = {&copy};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_exchange), dim3(a.bar.nranks),
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_exchange_spread), dim3(a.bar.nranks),
                                       dim3(kBlock), params, 0, s);
 }
 

@@ -107,7 +107,7 @@ uint64_t seg_rs_tile_vecs(int nranks);
 hipError_t launch_copy_pieces(const PieceArgs& a, int esize, int to_ws, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s);
 hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t s);
-hipError_t launch_barrier(const BarrierArgs& a, hipStream_t s);
-hipError_t launch_exchange(const ExchangeArgs& a, hipStream_t s);
+hipError_t launch_barrier(const BarrierArgs& a, int spread, hipStream_t s);
+hipError_t launch_exchange(const ExchangeArgs& a, int spread, hipStream_t s);
 
 }  // namespace dt

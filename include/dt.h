@@ -109,30 +109,36 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
                               size_t bucket_bytes, void* const* bucket_ws, dt_dtype dtype, dt_op op,
                               hipStream_t stream);
 
+/* Where the ranks of a barrier launch run. */
+typedef enum {
+    DT_BARRIER_PACKED = 0, /* one workgroup, one 64-wide wave per rank: always co-resident, plain launch */
+    DT_BARRIER_SPREAD = 1  /* one workgroup per rank on different CUs, cooperative launch */
+} dt_barrier_layout;
+
 /* Signal-window barrier.  pypto page "Barrier：仅信号（Signals Only）",
  * "The idea" and "Walkthrough": windows[p] is rank p's window of nranks int32
- * cells (zeroed once by the caller before its first use).  In generation g
- * every rank r atomically adds 1 to cell r of every other rank's window
- * (release, device scope), then waits until every cell s != r of its own
- * window is >= g (acquire, device scope).  Generations first_generation ..
- * first_generation + generations - 1 run back to back in ONE cooperative
- * launch (one workgroup per rank, all resident).  Reusing a window means
- * passing the next generation number (the page's "Edge cases": raise the
- * threshold on reuse).  Each wait gives up after timeout_ns nanoseconds
- * (0 = 10 s): it then stores DT_ERR_TIMEOUT into *status_dev and its
- * workgroup stops; every workgroup exits normally.  *status_dev (device
- * int32) must hold DT_OK before the call. */
+ * cells in device memory (zeroed once by the caller before its first use).
+ * In generation g every rank r atomically adds 1 to cell r of every other
+ * rank's window (release, device scope), then waits until every cell s != r
+ * of its own window is >= g (acquire, device scope).  Generations
+ * first_generation .. first_generation + generations - 1 run back to back in
+ * ONE launch; `layout` places the ranks (dt_barrier_layout).  Reusing a
+ * window means passing the next generation number (the page's "Edge cases":
+ * raise the threshold on reuse).  Each wait gives up after timeout_ns
+ * nanoseconds (0 = 10 s): it then stores DT_ERR_TIMEOUT into *status_dev and
+ * that rank stops; every wave exits normally.  *status_dev (device int32)
+ * must hold DT_OK before the call. */
 dt_status dt_barrier(int32_t* const* windows, int nranks, int32_t first_generation, int32_t generations,
-                     int32_t* status_dev, uint64_t timeout_ns, hipStream_t stream);
+                     int32_t* status_dev, uint64_t timeout_ns, int layout, hipStream_t stream);
 
 /* The barrier ordering a data exchange, as in the pypto page's built-in
  * demonstration: every rank r copies src[r] (nbytes) to stage[r], meets the
  * barrier of generation `generation` on `windows`, then copies stage[(r+1) %
- * nranks] to dst[r].  Afterwards dst[r] == src[(r+1) % nranks].  Timeout and
- * status as dt_barrier. */
+ * nranks] to dst[r].  Afterwards dst[r] == src[(r+1) % nranks].  Timeout,
+ * status and layout as dt_barrier. */
 dt_status dt_barrier_exchange(const void* const* src, void* const* stage, void* const* dst, size_t nbytes,
                               int32_t* const* windows, int nranks, int32_t generation, int32_t* status_dev,
-                              uint64_t timeout_ns, hipStream_t stream);
+                              uint64_t timeout_ns, int layout, hipStream_t stream);
 
 /* ---- host planning (no GPU work) -------------------------------------- */
 

@@ -84,10 +84,11 @@ def test_validation_rejects_bad_enums_nulls_and_aliases():
     assert lib.dt_bucket_allreduce(a, None, 1, 2, 16, None, 0, 0, None) == 1
     sizes = (ctypes.c_size_t * 1)(4)
     assert lib.dt_bucket_allreduce(a, sizes, 1, 2, 24, None, 0, 0, None) == 1  # not a multiple of 16
-    assert lib.dt_barrier(None, 2, 1, 1, None, 0, None) == 1
+    assert lib.dt_barrier(None, 2, 1, 1, None, 0, 0, None) == 1
     w = (ctypes.c_void_p * 2)(0x1000, 0x2000)
-    assert lib.dt_barrier(w, 2, 0, 1, ctypes.c_void_p(0x5000), 0, None) == 1   # generation must be >= 1
-    assert lib.dt_barrier(w, 2, 1, 0, ctypes.c_void_p(0x5000), 0, None) == 0   # zero generations: no-op
+    assert lib.dt_barrier(w, 2, 0, 1, ctypes.c_void_p(0x5000), 0, 0, None) == 1   # generation must be >= 1
+    assert lib.dt_barrier(w, 2, 1, 1, ctypes.c_void_p(0x5000), 0, 7, None) == 1   # bad layout
+    assert lib.dt_barrier(w, 2, 1, 0, ctypes.c_void_p(0x5000), 0, 0, None) == 0   # zero generations: no-op
 
 
 def test_all_gather_rejects_overlapping_output():

@@ -24,23 +24,24 @@ def window_matrix(ws):
     return np.stack([w.cpu().numpy() for w in ws])
 
 
+@pytest.mark.parametrize("layout", ["packed", "spread"])
 @pytest.mark.parametrize("p", [1, 2, 3, 8, 16])
-def test_barrier_rows_after_generations(dt, p):
+def test_barrier_rows_after_generations(dt, p, layout):
     """After G generations every rank's row reads G except its own 0 -- the
     oracle's window model run on the same generations."""
     orc = oracle.get()
     ws = windows(p)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    note(f"barrier P={p} 1000 generations in one launch")
-    dt.dt_barrier(ws, status, first_generation=1, generations=1000)
+    note(f"barrier P={p} {layout} 1000 generations in one launch")
+    dt.dt_barrier(ws, status, first_generation=1, generations=1000, layout=layout)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     model = np.zeros((p, p), np.int32)
     assert orc.barrier(model, 1, 1000) == 1000
     assert np.array_equal(window_matrix(ws), model)
-    note(f"barrier P={p} 100 single-generation launches")
+    note(f"barrier P={p} {layout} 100 single-generation launches")
     for g in range(1001, 1101):
-        dt.dt_barrier(ws, status, first_generation=g, generations=1)
+        dt.dt_barrier(ws, status, first_generation=g, generations=1, layout=layout)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     orc.barrier(model, 1001, 100)
@@ -57,16 +58,17 @@ def test_barrier_golden_two_ranks(dt):
     assert window_matrix(ws).tolist() == [[0, 1], [1, 0]]
 
 
-def test_barrier_unreachable_generation_times_out(dt):
+@pytest.mark.parametrize("layout", ["packed", "spread"])
+def test_barrier_unreachable_generation_times_out(dt, layout):
     """A threshold two generations ahead can never be met: the bounded wait
     must give up, report DT_ERR_TIMEOUT in the status word, and exit."""
     p = 4
     ws = windows(p)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    dt.dt_barrier(ws, status, 1, 3)
+    dt.dt_barrier(ws, status, 1, 3, layout=layout)
     torch.cuda.synchronize()
-    note("barrier forced timeout (threshold unreachable, 20 ms budget)")
-    dt.dt_barrier(ws, status, first_generation=6, generations=1, timeout_ns=20_000_000)
+    note(f"barrier forced timeout {layout} (threshold unreachable, 20 ms budget)")
+    dt.dt_barrier(ws, status, first_generation=6, generations=1, timeout_ns=20_000_000, layout=layout)
     torch.cuda.synchronize()
     assert int(status.item()) == dt.DT_ERR_TIMEOUT
     # each rank still notified once: the windows read 4 off the diagonal
@@ -75,8 +77,9 @@ def test_barrier_unreachable_generation_times_out(dt):
     assert np.array_equal(window_matrix(ws), want)
 
 
+@pytest.mark.parametrize("layout", ["packed", "spread"])
 @pytest.mark.parametrize("p,nbytes", [(2, 64), (5, 4099), (16, 1 << 20)])
-def test_barrier_exchange_golden(dt, p, nbytes):
+def test_barrier_exchange_golden(dt, p, nbytes, layout):
     orc = oracle.get()
     n = nbytes // 4 if nbytes % 4 == 0 else nbytes
     dtype = torch.int32 if nbytes % 4 == 0 else torch.uint8
@@ -85,9 +88,9 @@ def test_barrier_exchange_golden(dt, p, nbytes):
     dst = [torch.full_like(s, 77) for s in src]
     ws = windows(p)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    note(f"barrier exchange P={p} bytes={nbytes}")
+    note(f"barrier exchange {layout} P={p} bytes={nbytes}")
     for g in (1, 2, 3):
-        dt.dt_barrier_exchange(src, stage, dst, ws, status, generation=g)
+        dt.dt_barrier_exchange(src, stage, dst, ws, status, generation=g, layout=layout)
         torch.cuda.synchronize()
         assert int(status.item()) == 0
         want = orc.barrier_exchange([s.cpu().numpy() for s in src])
