@@ -255,6 +255,58 @@ def barrier_latency(dt, torch):
     return out
 
 
+def other_rows(dt, torch, steps: int, warmup: int):
+    """The remaining workloads, each timed per launch (HIP events around every
+    launch; mean) against its algorithmic HBM bytes:
+      allreduce_p4: fp32 and int32, P=4, 1,048,576 elements per rank
+        (32 MiB per launch, within the Infinity Cache: latency-bound);
+      uneven_all_gather_p8: fp32 rows of 4096, row counts U[1, 16384];
+      all_to_all_p8: fp32 rows of 4096, split matrix U[0, 4096] rows."""
+    import numpy as np
+    import synth
+    stream = torch.cuda.current_stream()
+    out = {}
+
+    def measure(name, fn, alg_bytes):
+        for _ in range(warmup):
+            fn()
+        evs = time_launches(fn, steps, stream)
+        torch.cuda.synchronize()
+        us = statistics.mean(a.elapsed_time(b) for a, b in evs) * 1e3
+        graph_us = graph_time_us(torch, fn, per_graph=10, replays=3)
+        out[name] = {"mean_us": round(us, 3), "graph_us": round(graph_us, 3), "alg_bytes": int(alg_bytes),
+                     "hbm_GBps": round(alg_bytes / (us * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(alg_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+        print(json.dumps({name: out[name]}), flush=True)
+
+    n = 1 << 20
+    for dtype, xs in (("fp32", synth.uniform_ranks(4, n, seed=0, device="cuda")),
+                      ("int32", synth.int_ranks(4, n, seed=0, device="cuda"))):
+        ys = [torch.empty_like(x) for x in xs]
+        measure(f"allreduce_p4_{dtype}", lambda: dt.dt_allreduce(xs, ys), 2 * 4 * n * 4)
+        del xs, ys
+
+    w = synth.ROW_WIDTH
+    counts = synth.uneven_row_counts(seed=0)
+    xs = synth.uniform_rows(counts, w, seed=100, device="cuda")
+    total = int(counts.sum()) * w
+    ys = [torch.empty(total, device="cuda") for _ in range(P)]
+    measure("uneven_all_gather_p8", lambda: dt.dt_all_gather(xs, ys), (1 + P) * total * 4)
+    out["uneven_all_gather_p8"]["rows"] = counts.tolist()
+    del xs, ys
+    torch.cuda.empty_cache()
+
+    s_rows = synth.split_matrix(seed=0)
+    s_el = (s_rows * w).tolist()
+    xs = synth.uniform_rows([int(s_rows[i].sum()) for i in range(P)], w, seed=200, device="cuda")
+    ys = [torch.empty(int(s_rows[:, j].sum()) * w, device="cuda") for j in range(P)]
+    measure("all_to_all_p8", lambda: dt.dt_all_to_all(xs, ys, s_el), 2 * int(s_rows.sum()) * w * 4)
+    out["all_to_all_p8"]["total_rows"] = int(s_rows.sum())
+    del xs, ys
+    torch.cuda.empty_cache()
+    return out
+
+
 def probe(dt, torch, reps: int = 10):
     """Workload for hardware-counter passes: the bench kernels and a plain
     copy of known size (1 GiB read + 1 GiB written) to calibrate
@@ -285,6 +337,9 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also run the P=16 size sweep and barrier latency")
     ap.add_argument("--probe", action="store_true", help="only run the kernels for a hardware-counter pass")
     ap.add_argument("--hsdp", action="store_true", help="also time the 32-layer gradient pipeline (103.6 GB)")
+    ap.add_argument("--all", action="store_true",
+                    help="also time every other workload: small AllReduce, uneven AllGather, AllToAll, the size "
+                         "sweep, the barrier and the gradient pipeline")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -371,6 +426,9 @@ def main():
     del ar_out
 
     extra = {"kernels": kernels, "host_seconds_timed": round(t_host, 4), "kernel_source_hash": kernel_source_hash()}
+    if args.all:
+        args.sweep = args.hsdp = True
+        extra["rows"] = other_rows(dt, torch, steps=args.steps, warmup=args.warmup)
     if args.sweep:
         rows, fit = sweep(dt, torch, steps=max(5, args.steps // 2), warmup=2)
         extra["sweep_p16_fp32"] = rows

@@ -20,6 +20,7 @@ static_assert(sizeof(dt::AllToAllArgs) <= 4096, "kernel arguments must stay belo
 static_assert(sizeof(dt::ExchangeArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::SegReduceScatterArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(DT_MAX_RANKS == dt::kMaxRanksHost, "rank limit mismatch");
+static_assert(dt::kGatherTileBytes == uint64_t(dt::kGatherU) * 256 * 16, "gather tile = U vectors per thread");
 
 namespace {
 
@@ -272,6 +273,7 @@ dt_status dt_all_gather(const void* const* send, void* const* recv, int nranks, 
     }
     if (total == 0) return DT_OK;  // nothing to gather; empty buffers may be NULL
     if ((st = check_ptr_array(recv, nranks, "recv")) != DT_OK) return st;
+    const uint64_t tile_bytes = dt::kGatherTileBytes;
     dt::GatherArgs a = {};
     a.nranks = nranks;
     uint64_t off = 0, tiles = 0;
@@ -286,7 +288,7 @@ dt_status dt_all_gather(const void* const* send, void* const* recv, int nranks, 
         a.tile_start[r] = uint32_t(tiles);
         if (dst_aligned && aligned16(send[r]) && off % 16 == 0) a.aligned |= 1u << r;  // NULL (empty) is aligned
         off += c * es;
-        tiles += (c * es + dt::kCopyTileBytes - 1) / dt::kCopyTileBytes;
+        tiles += (c * es + tile_bytes - 1) / tile_bytes;
         if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "all_gather too large for one launch");
     }
     a.tile_start[nranks] = uint32_t(tiles);

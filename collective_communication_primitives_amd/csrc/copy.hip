@@ -1,7 +1,7 @@
 // copy.hip -- the gather and all-to-all copy engines.
 //
 // Both are byte copies driven by an offset table carried in the kernel
-// arguments (no device-side tables).  The work is cut into 8 KiB tiles of
+// arguments (no device-side tables).  The work is cut into 4-16 KiB tiles of
 // source data; one workgroup copies one tile, so uneven pieces (1 row or
 // 16384 rows, an empty all-to-all block or a 4096-row one) balance across the
 // whole chip.  A workgroup finds its piece from an exclusive prefix sum of
@@ -18,22 +18,23 @@ namespace dt {
 constexpr int kCopyU = int(kCopyTileBytes / 16 / kBlock);  // 16-byte vectors per thread per tile
 
 // PMAX bounds the rank count; EXACT (P == PMAX) unrolls the P destination
-// stores.
-template <int PMAX, bool EXACT>
+// stores.  A tile is U * 4 KiB of one rank's source (U = kGatherU).
+template <int PMAX, bool EXACT, int U>
 __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
+    constexpr uint64_t kTile = uint64_t(U) * kBlock * 16;
     const uint32_t b = blockIdx.x;
     const int nr = EXACT ? PMAX : a.nranks;
     int r = 0;
     while (r + 1 < nr && a.tile_start[r + 1] <= b) r++;
     const char* src = static_cast<const char*>(a.src[r]);
     const uint64_t off = a.offset[r];
-    const uint64_t b0 = uint64_t(b - a.tile_start[r]) * kCopyTileBytes;
-    const uint64_t b1 = min(a.bytes[r], b0 + kCopyTileBytes);
+    const uint64_t b0 = uint64_t(b - a.tile_start[r]) * kTile;
+    const uint64_t b1 = min(a.bytes[r], b0 + kTile);
     if ((a.aligned >> r) & 1u) {
         const uint64_t v1 = b1 / 16;
-        u32x4 x[kCopyU];
+        u32x4 x[U];
 #pragma unroll
-        for (int u = 0; u < kCopyU; u++) {
+        for (int u = 0; u < U; u++) {
             const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
             if (v < v1) x[u] = load16_h<false>(src + v * 16);  // writes dominate 1:P
         }
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
             if (q < nr) {
                 char* dst = static_cast<char*>(a.dst[q]) + off;
 #pragma unroll
-                for (int u = 0; u < kCopyU; u++) {
+                for (int u = 0; u < U; u++) {
                     const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
                     if (v < v1) store16_h<true>(dst + v * 16, x[u]);
                 }
@@ -103,12 +104,12 @@ __global__ __launch_bounds__(kBlock) void k_all_to_all(AllToAllArgs a) {
 }
 
 namespace {
-template <int PMAX>
-hipError_t gather_p(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
+template <int PMAX, int U>
+hipError_t gather_pu(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     if (a.nranks == PMAX)
-        k_gather<PMAX, true><<<tiles, kBlock, 0, s>>>(a);
+        k_gather<PMAX, true, U><<<tiles, kBlock, 0, s>>>(a);
     else
-        k_gather<PMAX, false><<<tiles, kBlock, 0, s>>>(a);
+        k_gather<PMAX, false, U><<<tiles, kBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 }  // namespace
@@ -116,8 +117,9 @@ hipError_t gather_p(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
 hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     if (tiles == 0) return hipSuccess;
     const int p = a.nranks;
-    return p <= 1 ? gather_p<1>(a, tiles, s) : p <= 2 ? gather_p<2>(a, tiles, s) : p <= 4 ? gather_p<4>(a, tiles, s)
-           : p <= 8 ? gather_p<8>(a, tiles, s) : gather_p<16>(a, tiles, s);
+    return p <= 1 ? gather_pu<1, kGatherU>(a, tiles, s) : p <= 2 ? gather_pu<2, kGatherU>(a, tiles, s)
+           : p <= 4 ? gather_pu<4, kGatherU>(a, tiles, s) : p <= 8 ? gather_pu<8, kGatherU>(a, tiles, s)
+           : gather_pu<16, kGatherU>(a, tiles, s);
 }
 
 hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t s) {

@@ -92,7 +92,9 @@ struct ExchangeArgs {
 };
 
 // Tile sizes (bytes of one rank's data per workgroup).
-constexpr uint64_t kCopyTileBytes = 8192;    // gather / all-to-all
+constexpr uint64_t kCopyTileBytes = 16384;   // all-to-all
+constexpr int kGatherU = 2;                   // gather: 2 vectors per thread,
+constexpr uint64_t kGatherTileBytes = 8192;   // 8 KiB source tiles
 constexpr uint64_t kPieceTileVecs = 512;     // bucket pieces: 512 x 16 B
 
 // Launchers: return the HIP error of the launch.  dtype/op are the dt_dtype /
