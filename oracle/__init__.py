@@ -28,8 +28,8 @@ GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", 
              "-Wall", "-Wextra"]
 
 FLOAT32, BFLOAT16, INT32 = 0, 1, 2
-SUM, MAX, MIN = 0, 1, 2
-OPS = {"sum": SUM, "max": MAX, "min": MIN}
+SUM, MAX, MIN, AVG = 0, 1, 2, 3
+OPS = {"sum": SUM, "max": MAX, "min": MIN, "avg": AVG}
 
 
 def build(source: str = SOURCE, output: str = LIBRARY, extra: Sequence[str] = ()) -> str:
@@ -89,11 +89,16 @@ class Oracle:
         lib.oracle_all_to_all.argtypes = [vp, vp, i32, vp, sz]
         lib.oracle_bucket_allreduce.argtypes = [vp, vp, i32, i32, sz, vp, i32, i32]
         lib.oracle_hsdp_layer.argtypes = [vp, vp, vp, i32, i32, i32, sz, vp, i32, i32]
+        lib.oracle_broadcast.argtypes = [vp, vp, i32, sz]
+        lib.oracle_replicate_to_shard.argtypes = [vp, vp, i32, sz, sz]
+        lib.oracle_all_gather_into_vec.argtypes = [vp, vp, i32, vp, sz]
+        lib.oracle_all_to_all_dims.argtypes = [vp, vp, i32, sz, sz, i32, i32, sz]
         lib.oracle_barrier.argtypes = [vp, i32, i32, i32]
         lib.oracle_barrier_exchange.argtypes = [vp, vp, i32, sz]
         for name in ("oracle_allreduce", "oracle_reduce_scatter", "oracle_all_gather",
                      "oracle_all_to_all", "oracle_bucket_allreduce", "oracle_hsdp_layer",
-                     "oracle_barrier", "oracle_barrier_exchange"):
+                     "oracle_barrier", "oracle_barrier_exchange", "oracle_broadcast", "oracle_replicate_to_shard",
+                     "oracle_all_gather_into_vec", "oracle_all_to_all_dims"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
 
@@ -143,6 +148,42 @@ class Oracle:
         ys = [np.empty(int(s[:, j].sum()), dtype=xs[0].dtype) for j in range(p)]
         rc = self.lib.oracle_all_to_all(_ptrs(xs), _ptrs(ys), p, _sizes(s.reshape(-1).tolist()),
                                         xs[0].itemsize)
+        assert rc == 0, rc
+        return ys
+
+    def broadcast(self, x_root: np.ndarray, nranks: int) -> List[np.ndarray]:
+        x = np.ascontiguousarray(x_root).reshape(-1)
+        ys = [np.empty_like(x) for _ in range(nranks)]
+        assert self.lib.oracle_broadcast(x.ctypes.data, _ptrs(ys), nranks, x.nbytes) == 0
+        return ys
+
+    def replicate_to_shard(self, xs: Sequence[np.ndarray]) -> List[np.ndarray]:
+        xs = [np.ascontiguousarray(x).reshape(-1) for x in xs]
+        p = len(xs)
+        assert xs[0].size % p == 0
+        m = xs[0].size // p
+        ys = [np.empty(m, dtype=xs[0].dtype) for _ in xs]
+        assert self.lib.oracle_replicate_to_shard(_ptrs(xs), _ptrs(ys), p, m, xs[0].itemsize) == 0
+        return ys
+
+    def all_gather_into_vec(self, xs: Sequence[np.ndarray]) -> List[List[np.ndarray]]:
+        xs = [np.ascontiguousarray(x).reshape(-1) for x in xs]
+        p = len(xs)
+        ys = [[np.empty_like(xs[r]) for r in range(p)] for _ in range(p)]
+        flat = [t for row in ys for t in row]
+        assert self.lib.oracle_all_gather_into_vec(_ptrs(xs), _ptrs(flat), p, _sizes([x.size for x in xs]),
+                                                   xs[0].itemsize) == 0
+        return ys
+
+    def all_to_all_dims(self, xs: Sequence[np.ndarray], rows: int, cols: int, src_dim: int,
+                        dst_dim: int) -> List[np.ndarray]:
+        """xs[i]: rank i's block of the [rows, cols] tensor under Shard(src_dim);
+        returns the blocks under Shard(dst_dim), flat."""
+        xs = [np.ascontiguousarray(x).reshape(-1) for x in xs]
+        p = len(xs)
+        n_out = (rows // p) * cols if dst_dim == 0 else rows * (cols // p)
+        ys = [np.empty(n_out, dtype=xs[0].dtype) for _ in range(p)]
+        rc = self.lib.oracle_all_to_all_dims(_ptrs(xs), _ptrs(ys), p, rows, cols, src_dim, dst_dim, xs[0].itemsize)
         assert rc == 0, rc
         return ys
 

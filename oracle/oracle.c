@@ -35,7 +35,7 @@
 #include <string.h>
 
 enum { OR_FLOAT32 = 0, OR_BFLOAT16 = 1, OR_INT32 = 2 };
-enum { OR_SUM = 0, OR_MAX = 1, OR_MIN = 2 };
+enum { OR_SUM = 0, OR_MAX = 1, OR_MIN = 2, OR_AVG = 3 };
 enum { OR_OK = 0, OR_BAD_ARG = 1 };
 
 /* ---------------------------------------------------------------- bf16 --- */
@@ -122,23 +122,31 @@ static size_t elem_size(int dtype)
 static int valid(int nranks, int dtype, int op)
 {
     return nranks >= 1 && (dtype == OR_FLOAT32 || dtype == OR_BFLOAT16 || dtype == OR_INT32) &&
-           (op == OR_SUM || op == OR_MAX || op == OR_MIN);
+           (op == OR_SUM || op == OR_MAX || op == OR_MIN || op == OR_AVG);
 }
 
 /* The fold of [DTorch] sec. 2.3: start from rank 0's element, then combine
- * ranks 1..P-1 in rank order.  Inputs are x[r] + offset, element e. */
+ * ranks 1..P-1 in rank order.  Inputs are x[r] + offset, element e.
+ * AVG ([HSDP] sec. 6 divides the summed gradient by the group size): the
+ * same sum, then one division by P in the accumulation type (IEEE binary32
+ * division; C's truncating division for int32) before the final rounding. */
 static void fold_one(const void* const* x, size_t offset, int nranks, size_t e, int dtype, int op,
                      void* out, size_t out_e)
 {
+    const int fold_op = op == OR_AVG ? OR_SUM : op;
     if (dtype == OR_INT32) {
         int32_t acc = ((const int32_t*)x[0])[offset + e];
         for (int r = 1; r < nranks; r++)
-            acc = combine_i(acc, ((const int32_t*)x[r])[offset + e], op);
+            acc = combine_i(acc, ((const int32_t*)x[r])[offset + e], fold_op);
+        if (op == OR_AVG)
+            acc = acc / nranks;
         ((int32_t*)out)[out_e] = acc;
     } else {
         float acc = load_as_float(x[0], offset + e, dtype);
         for (int r = 1; r < nranks; r++)
-            acc = combine_f(acc, load_as_float(x[r], offset + e, dtype), op);
+            acc = combine_f(acc, load_as_float(x[r], offset + e, dtype), fold_op);
+        if (op == OR_AVG)
+            acc = acc / (float)nranks;
         store_from_float(out, out_e, acc, dtype);
     }
 }
@@ -333,6 +341,76 @@ int oracle_hsdp_layer(const void* const* grads, void* const* out, const size_t* 
             size_t m = numels[t] / (size_t)shard;
             memcpy(out[(size_t)r * ntensors + t], (char*)work[r] + at * es, m * es);
             at += m;
+        }
+    }
+    return OR_OK;
+}
+
+/* Broadcast ([DTorch] sec. 2.2 lists it among the backend's collectives):
+ * every rank's output is a copy of the root rank's tensor. */
+int oracle_broadcast(const void* x_root, void* const* y, int nranks, size_t nbytes)
+{
+    if (nranks < 1)
+        return OR_BAD_ARG;
+    for (int q = 0; q < nranks; q++)
+        memcpy(y[q], x_root, nbytes);
+    return OR_OK;
+}
+
+/* ReplicateToShard, Replicate -> Shard(0) ([DTorch] sec. 2.1, sec. 2.5: no
+ * communication, each rank keeps its own slice): x_r holds P*m elements,
+ * y_r = slice r of x_r. */
+int oracle_replicate_to_shard(const void* const* x, void* const* y, int nranks, size_t m, size_t esize)
+{
+    if (nranks < 1 || esize == 0)
+        return OR_BAD_ARG;
+    for (int r = 0; r < nranks; r++)
+        memcpy(y[r], (const char*)x[r] + (size_t)r * m * esize, m * esize);
+    return OR_OK;
+}
+
+/* AllGatherIntoVec ([DTorch] sec. 2.1): the gathered pieces stay separate
+ * tensors; rank q's vector entry r is rank r's piece: y[q*P + r] = x_r. */
+int oracle_all_gather_into_vec(const void* const* x, void* const* y, int nranks, const size_t* counts,
+                               size_t esize)
+{
+    if (nranks < 1 || esize == 0)
+        return OR_BAD_ARG;
+    for (int q = 0; q < nranks; q++)
+        for (int r = 0; r < nranks; r++)
+            memcpy(y[(size_t)q * nranks + r], x[r], counts[r] * esize);
+    return OR_OK;
+}
+
+/* AllToAll between shard dimensions of a row-major [rows, cols] tensor G
+ * ([DTorch] sec. 2.1 AllToAll(input, srcDim, destDim), sec. 2.5 S -> S).
+ * Shard(0): rank i holds rows [i*rows/P, (i+1)*rows/P), a [rows/P, cols]
+ * block.  Shard(1): rank i holds columns [i*cols/P, (i+1)*cols/P), a
+ * [rows, cols/P] block.  Element by element: rebuild G's element (a, b)
+ * from its owner under src_dim, store it at its place under dst_dim. */
+int oracle_all_to_all_dims(const void* const* x, void* const* y, int nranks, size_t rows, size_t cols,
+                           int src_dim, int dst_dim, size_t esize)
+{
+    if (nranks < 1 || esize == 0 || src_dim < 0 || src_dim > 1 || dst_dim < 0 || dst_dim > 1)
+        return OR_BAD_ARG;
+    if ((src_dim == 0 || dst_dim == 0) && rows % (size_t)nranks != 0)
+        return OR_BAD_ARG;
+    if ((src_dim == 1 || dst_dim == 1) && cols % (size_t)nranks != 0)
+        return OR_BAD_ARG;
+    size_t rp = rows / (size_t)nranks, cp = cols / (size_t)nranks;
+    for (size_t a = 0; a < rows; a++) {
+        for (size_t b = 0; b < cols; b++) {
+            const char* from;
+            if (src_dim == 0)
+                from = (const char*)x[a / rp] + ((a % rp) * cols + b) * esize;
+            else
+                from = (const char*)x[b / cp] + (a * cp + b % cp) * esize;
+            char* to;
+            if (dst_dim == 0)
+                to = (char*)y[a / rp] + ((a % rp) * cols + b) * esize;
+            else
+                to = (char*)y[b / cp] + (a * cp + b % cp) * esize;
+            memcpy(to, from, esize);
         }
     }
     return OR_OK;

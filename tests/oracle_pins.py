@@ -410,6 +410,101 @@ def pin_barrier_exchange(orc):
             assert (ys[r] == 100 + (r + 1) % p).all()
 
 
+# ------------------------------------------------ placement-matrix extras --
+def pin_avg(orc):
+    """AVG = rank-order sum, then one division by P in the accumulation type:
+    numpy float32 fold / float32(P); int32 truncation toward zero of the
+    wrapped sum; bf16 = torch RNE of the fp32 mean; RS(avg) = chunk of AR(avg)."""
+    rng = np.random.default_rng(21)
+    for p in (1, 2, 3, 5, 8, 16):
+        xs = [(rng.random(301, dtype=np.float32) * 2 - 1) for _ in range(p)]
+        acc = xs[0].copy()
+        for x in xs[1:]:
+            acc = (acc + x).astype(np.float32)
+        want = (acc / np.float32(p)).astype(np.float32)
+        for y in orc.allreduce(xs, "avg"):
+            assert np.array_equal(_bits(y), _bits(want)), p
+        xi = [rng.integers(-(2 ** 31), 2 ** 31, 97, dtype=np.int64).astype(np.int32) for _ in range(p)]
+        got = orc.allreduce(xi, "avg")[0]
+        for e in range(97):
+            s_ = (sum(int(x[e]) for x in xi) + 2 ** 31) % 2 ** 32 - 2 ** 31
+            q = abs(s_) // p
+            assert int(got[e]) == (-q if s_ < 0 else q), (p, e)
+        h = [_torch_bf16(rng.standard_normal(200).astype(np.float32)) for _ in range(p)]
+        wide = [_bf16_to_f32(x) for x in h]
+        acc = wide[0].copy()
+        for w in wide[1:]:
+            acc = (acc + w).astype(np.float32)
+        assert np.array_equal(orc.allreduce(h, "avg")[0], _torch_bf16((acc / np.float32(p)).astype(np.float32)))
+        xr = [(rng.random(p * 11, dtype=np.float32) * 2 - 1) for _ in range(p)]
+        rs = orc.reduce_scatter(xr, "avg")
+        ar = orc.allreduce(xr, "avg")[0]
+        for r in range(p):
+            assert np.array_equal(_bits(rs[r]), _bits(ar[r * 11:(r + 1) * 11]))
+        ones = [np.full(9, r + 1, np.float32) for r in range(p)]
+        assert (orc.allreduce(ones, "avg")[0] == np.float32((p + 1) / 2)).all()
+
+
+def pin_broadcast(orc):
+    rng = np.random.default_rng(22)
+    for p in (1, 2, 7, 16):
+        x = rng.random(33, dtype=np.float32)
+        for y in orc.broadcast(x, p):
+            assert np.array_equal(y, x)
+        assert len(orc.broadcast(x, p)) == p
+
+
+def pin_replicate_to_shard(orc):
+    """R -> S keeps slice r on rank r (np.split); after an AllReduce it equals
+    the ReduceScatter of the same inputs, bit for bit (P->R->S == P->S)."""
+    rng = np.random.default_rng(23)
+    for p in (1, 2, 3, 8):
+        xs = [rng.random(p * 6, dtype=np.float32) for _ in range(p)]
+        ys = orc.replicate_to_shard(xs)
+        for r in range(p):
+            assert np.array_equal(ys[r], np.split(xs[r], p)[r])
+        hb = [_torch_bf16(rng.standard_normal(p * 10).astype(np.float32)) for _ in range(p)]
+        ar = orc.allreduce(hb, "sum")
+        rs = orc.reduce_scatter(hb, "sum")
+        for a, b in zip(orc.replicate_to_shard(ar), rs):
+            assert np.array_equal(a, b)
+
+
+def pin_all_gather_into_vec(orc):
+    """Rank q's vector entry r is rank r's piece; concatenated, it is the AllGather."""
+    rng = np.random.default_rng(24)
+    for p in (1, 2, 3, 5):
+        xs = [rng.integers(0, 1000, int(rng.integers(0, 7))).astype(np.int32) for _ in range(p)]
+        vec = orc.all_gather_into_vec(xs)
+        ag = orc.all_gather(xs)
+        for q in range(p):
+            for r in range(p):
+                assert np.array_equal(vec[q][r], xs[r])
+            assert np.array_equal(np.concatenate(vec[q]) if p else vec[q], ag[q])
+
+
+def _shard_blocks(g, p, dim):
+    return [np.ascontiguousarray(b).reshape(-1) for b in np.split(g, p, axis=dim)]
+
+
+def pin_all_to_all_dims(orc):
+    """Shard(i) -> Shard(j) equals np.split of the reassembled tensor along j;
+    0 -> 1 -> 0 returns every block; i -> i is the identity."""
+    rng = np.random.default_rng(25)
+    for p, rows, cols in ((1, 3, 5), (2, 4, 6), (3, 6, 9), (4, 8, 4), (8, 16, 24)):
+        g = rng.integers(0, 1 << 30, (rows, cols)).astype(np.int32)
+        for src in (0, 1):
+            xs = _shard_blocks(g, p, src)
+            for dst in (0, 1):
+                ys = orc.all_to_all_dims(xs, rows, cols, src, dst)
+                for got, want in zip(ys, _shard_blocks(g, p, dst)):
+                    assert np.array_equal(got, want), (p, src, dst)
+        x0 = _shard_blocks(g, p, 0)
+        back = orc.all_to_all_dims(orc.all_to_all_dims(x0, rows, cols, 0, 1), rows, cols, 1, 0)
+        for a, b in zip(back, x0):
+            assert np.array_equal(a, b)
+
+
 ALL_PINS = [
     pin_bf16_rounding_hand_values,
     pin_bf16_rounding_vs_torch,
@@ -427,4 +522,9 @@ ALL_PINS = [
     pin_hsdp_layer,
     pin_barrier,
     pin_barrier_exchange,
+    pin_avg,
+    pin_broadcast,
+    pin_replicate_to_shard,
+    pin_all_gather_into_vec,
+    pin_all_to_all_dims,
 ]

@@ -40,6 +40,15 @@ MUTANTS = {
     "barrier_notifies_self": ("if (p != r)\n                    window", "if (1)\n                    window"),
     "barrier_fixed_threshold": ("window[(size_t)r * nranks + s] < g)", "window[(size_t)r * nranks + s] < 1)"),
     "exchange_wrong_peer": ("x[(r + 1) % nranks]", "x[(r + nranks - 1) % nranks]"),
+    "avg_divides_by_p_minus_1": ("acc = acc / (float)nranks;", "acc = acc / (float)(nranks > 1 ? nranks - 1 : 1);"),
+    "avg_int_rounds_down": ("acc = acc / nranks;", "acc = (int32_t)((acc - (acc < 0 ? nranks - 1 : 0)) / nranks);"),
+    "r2s_wrong_slice": ("(const char*)x[r] + (size_t)r * m * esize", "(const char*)x[r] + (size_t)((r + 1) % nranks) * m * esize"),
+    "agvec_transposed": ("memcpy(y[(size_t)q * nranks + r], x[r], counts[r] * esize);",
+                         "memcpy(y[(size_t)r * nranks + q], x[r], counts[r] * esize);"),
+    "dims_wrong_owner": ("from = (const char*)x[b / cp] + (a * cp + b % cp) * esize;",
+                         "from = (const char*)x[b % nranks] + (a * cp + b / nranks) * esize;"),
+    "broadcast_skips_last": ("for (int q = 0; q < nranks; q++)\n        memcpy(y[q], x_root, nbytes);",
+                             "for (int q = 0; q + 1 < nranks; q++)\n        memcpy(y[q], x_root, nbytes);"),
 }
 
 
