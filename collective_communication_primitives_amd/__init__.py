@@ -27,13 +27,13 @@ from . import _lib
 _L = _lib.load()
 
 DT_FLOAT32, DT_BFLOAT16, DT_INT32 = 0, 1, 2
-DT_SUM, DT_MAX, DT_MIN = 0, 1, 2
+DT_SUM, DT_MAX, DT_MIN, DT_AVG = 0, 1, 2, 3
 DT_OK, DT_ERR_ARG, DT_ERR_UNSUPPORTED, DT_ERR_HIP, DT_ERR_TIMEOUT = 0, 1, 2, 3, 4
 DT_MAX_RANKS = 16
 DEFAULT_BUCKET_BYTES = 25 << 20
 
 _DTYPES = {torch.float32: DT_FLOAT32, torch.bfloat16: DT_BFLOAT16, torch.int32: DT_INT32}
-_OPS = {"sum": DT_SUM, "max": DT_MAX, "min": DT_MIN}
+_OPS = {"sum": DT_SUM, "max": DT_MAX, "min": DT_MIN, "avg": DT_AVG}
 
 LIBRARY_PATH = _lib.LIBRARY
 
@@ -214,6 +214,67 @@ def dt_all_to_all(send: Sequence[torch.Tensor], recv: Sequence[torch.Tensor], sp
     return w if async_op else list(recv)
 
 
+def dt_all_gather_into_vec(send: Sequence[torch.Tensor], recv: Sequence[Sequence[torch.Tensor]], stream=None,
+                           async_op: bool = False, comm_stream=None):
+    """AllGatherIntoVec: recv[q][r] receives a copy of send[r] for every rank q."""
+    p = len(send)
+    if len(recv) != p or any(len(row) != p for row in recv):
+        raise ValueError("recv must be P lists of P tensors")
+    for q in range(p):
+        for r in range(p):
+            if recv[q][r].numel() != send[r].numel():
+                raise ValueError(f"recv[{q}][{r}] must hold send[{r}].numel() elements")
+    flat = [t for row in recv for t in row]
+    code = _dtype_code(list(send) + flat)
+    counts = [t.numel() for t in send]
+    s, r, c = _ptr_array(send), _ptr_array(flat), _size_array(counts)
+    w = _launch(lambda st: _L.dt_all_gather_into_vec(s, r, p, c, 0, code, st), list(send) + flat, async_op,
+                stream, comm_stream)
+    return w if async_op else recv
+
+
+def dt_broadcast(root_send: torch.Tensor, recv: Sequence[torch.Tensor], stream=None, async_op: bool = False,
+                 comm_stream=None):
+    """Broadcast: every recv[q] receives a copy of root_send."""
+    n = root_send.numel()
+    if any(t.numel() != n for t in recv):
+        raise ValueError("every recv must hold root_send.numel() elements")
+    code = _dtype_code([root_send] + list(recv))
+    r = _ptr_array(recv)
+    w = _launch(lambda st: _L.dt_broadcast(root_send.data_ptr(), r, len(recv), n, code, st),
+                [root_send] + list(recv), async_op, stream, comm_stream)
+    return w if async_op else list(recv)
+
+
+def dt_replicate_to_shard(send: Sequence[torch.Tensor], recv: Sequence[torch.Tensor], stream=None,
+                          async_op: bool = False, comm_stream=None):
+    """ReplicateToShard: recv[r] = slice r of send[r] (send[r] holds P * recv[r].numel())."""
+    p = len(send)
+    m = recv[0].numel()
+    if len(recv) != p or any(t.numel() != p * m for t in send) or any(t.numel() != m for t in recv):
+        raise ValueError("send[r] must hold nranks * recvcount elements and recv[r] recvcount")
+    code = _dtype_code(list(send) + list(recv))
+    s, r = _ptr_array(send), _ptr_array(recv)
+    w = _launch(lambda st: _L.dt_replicate_to_shard(s, r, p, m, code, st), list(send) + list(recv), async_op,
+                stream, comm_stream)
+    return w if async_op else list(recv)
+
+
+def dt_all_to_all_dims(send: Sequence[torch.Tensor], recv: Sequence[torch.Tensor], rows: int, cols: int,
+                       src_dim: int, dst_dim: int, stream=None, async_op: bool = False, comm_stream=None):
+    """AllToAll between shard dimensions of a [rows, cols] tensor: send[r] is
+    rank r's block under Shard(src_dim), recv[r] its block under Shard(dst_dim)."""
+    p = len(send)
+    blk = {0: (rows // p) * cols, 1: rows * (cols // p)}
+    if len(recv) != p or any(t.numel() != blk[src_dim] for t in send) or any(t.numel() != blk[dst_dim] for t in recv):
+        raise ValueError("send/recv blocks do not match the [rows, cols] shard shapes")
+    code = _dtype_code(list(send) + list(recv))
+    s, r = _ptr_array(send), _ptr_array(recv)
+    w = _launch(lambda st: _L.dt_all_to_all_dims(s, r, p, rows, cols, src_dim, dst_dim, code, st),
+                list(send) + list(recv), async_op, stream, comm_stream)
+    return w if async_op else list(recv)
+
+
 def dt_bucket_allreduce(grads: Sequence[Sequence[torch.Tensor]], bucket_bytes: int = DEFAULT_BUCKET_BYTES,
                         bucket_ws: Optional[Sequence[torch.Tensor]] = None, op="sum", stream=None,
                         async_op: bool = False, comm_stream=None):
@@ -344,6 +405,7 @@ def shard_views(fused: torch.Tensor, numels: Sequence[int], shard: int) -> List[
 
 __all__ = [
     "dt_allreduce", "dt_reduce_scatter", "dt_all_gather", "dt_all_to_all", "dt_bucket_allreduce", "dt_bucket_plan",
+    "dt_all_gather_into_vec", "dt_broadcast", "dt_replicate_to_shard", "dt_all_to_all_dims",
     "dt_barrier", "dt_barrier_exchange", "HSDPPipeline", "Work", "DtError", "shard_views", "side_stream",
     "status_string", "version",
 ]

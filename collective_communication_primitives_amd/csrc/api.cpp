@@ -19,6 +19,8 @@ static_assert(sizeof(dt::GatherArgs) <= 4096, "kernel arguments must stay below 
 static_assert(sizeof(dt::AllToAllArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::ExchangeArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::SegReduceScatterArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+static_assert(sizeof(dt::SegCopyArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+static_assert(sizeof(dt::DimsArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(DT_MAX_RANKS == dt::kMaxRanksHost, "rank limit mismatch");
 static_assert(dt::kGatherTileBytes == uint64_t(dt::kGatherU) * 256 * 16, "gather tile = U vectors per thread");
 
@@ -42,7 +44,7 @@ dt_status check_hip(hipError_t e, const char* what) {
 }
 
 bool valid_dtype(dt_dtype d) { return d == DT_FLOAT32 || d == DT_BFLOAT16 || d == DT_INT32; }
-bool valid_op(dt_op o) { return o == DT_SUM || o == DT_MAX || o == DT_MIN; }
+bool valid_op(dt_op o) { return o == DT_SUM || o == DT_MAX || o == DT_MIN || o == DT_AVG; }
 size_t esize_of(dt_dtype d) { return d == DT_BFLOAT16 ? 2 : 4; }
 size_t vec_elems(dt_dtype d) { return 16 / esize_of(d); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -157,6 +159,65 @@ dt_status reduce_scatter_segments(const std::vector<std::vector<const void*>>& s
     return flush();
 }
 
+// Fan-out of `nsources` pieces (default: nranks): piece r (counts[r]
+// elements at src[r]) goes to table[r*nranks + q] for every q.
+dt_status fan_out(const void* const* src, const size_t* counts, void* const* table, int nranks, size_t es,
+                  hipStream_t stream, const char* what, int nsources = -1) {
+    if (nsources < 0) nsources = nranks;
+    dt::GatherArgs a = {};
+    a.nranks = nranks;
+    uint64_t tiles = 0;
+    for (int r = 0; r < nsources; r++) {
+        const uint64_t bytes = uint64_t(counts[r]) * es;
+        a.src[r] = src[r];
+        a.bytes[r] = bytes;
+        a.tile_start[r] = uint32_t(tiles);
+        bool al = aligned16(src[r]);
+        for (int q = 0; q < nranks; q++) {
+            void* d = bytes ? table[size_t(r) * nranks + q] : nullptr;
+            a.dst[r * nranks + q] = d;
+            al = al && aligned16(d);
+        }
+        if (al) a.aligned |= 1u << r;
+        tiles += (bytes + dt::kGatherTileBytes - 1) / dt::kGatherTileBytes;
+        if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "fan-out too large for one launch");
+    }
+    for (int r = nsources; r <= nranks; r++) a.tile_start[r] = uint32_t(tiles);
+    if (tiles == 0) return DT_OK;
+    return check_hip(dt::launch_gather(a, uint32_t(tiles), stream), what);
+}
+
+// Independent 1:1 byte copies, in as few launches as the argument block allows.
+dt_status copy_segments(const std::vector<const void*>& src, const std::vector<void*>& dst,
+                        const std::vector<size_t>& bytes, hipStream_t stream, const char* what) {
+    dt::SegCopyArgs a = {};
+    uint64_t tiles = 0;
+    auto flush = [&]() -> dt_status {
+        if (a.nsegs == 0) return DT_OK;
+        a.tile_start[a.nsegs] = uint32_t(tiles);
+        dt_status st = check_hip(dt::launch_copy_segments(a, stream), what);
+        a = dt::SegCopyArgs{};
+        tiles = 0;
+        return st;
+    };
+    for (size_t k = 0; k < src.size(); k++) {
+        if (bytes[k] == 0) continue;
+        if (a.nsegs == dt::kMaxCopySegs) {
+            dt_status st = flush();
+            if (st != DT_OK) return st;
+        }
+        const int i = a.nsegs++;
+        a.src[i] = src[k];
+        a.dst[i] = dst[k];
+        a.bytes[i] = bytes[k];
+        if (aligned16(src[k]) && aligned16(dst[k])) a.aligned |= 1ull << i;
+        a.tile_start[i] = uint32_t(tiles);
+        tiles += (bytes[k] + dt::kSegCopyTileBytes - 1) / dt::kSegCopyTileBytes;
+        if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "copy too large for one launch");
+    }
+    return flush();
+}
+
 // ---------------------------------------------------------- bucket plan --
 struct Piece {
     int tensor;
@@ -264,44 +325,159 @@ dt_status dt_all_gather(const void* const* send, void* const* recv, int nranks, 
     if (!valid_dtype(dtype)) return fail(DT_ERR_ARG, "bad dtype %d", dtype);
     if (send == nullptr || recv == nullptr) return fail(DT_ERR_ARG, "send/recv array is NULL");
     const size_t es = esize_of(dtype);
+    std::vector<size_t> counts(nranks);
     size_t total = 0;
     for (int r = 0; r < nranks; r++) {
-        const size_t c = sendcounts ? sendcounts[r] : equal_count;
-        if (c > (size_t(1) << 40)) return fail(DT_ERR_ARG, "sendcount[%d]=%zu too large", r, c);
-        if (c > 0 && send[r] == nullptr) return fail(DT_ERR_ARG, "send[%d] is NULL", r);
-        total += c;
+        counts[r] = sendcounts ? sendcounts[r] : equal_count;
+        if (counts[r] > (size_t(1) << 40)) return fail(DT_ERR_ARG, "sendcount[%d]=%zu too large", r, counts[r]);
+        if (counts[r] > 0 && send[r] == nullptr) return fail(DT_ERR_ARG, "send[%d] is NULL", r);
+        total += counts[r];
     }
     if (total == 0) return DT_OK;  // nothing to gather; empty buffers may be NULL
     if ((st = check_ptr_array(recv, nranks, "recv")) != DT_OK) return st;
-    const uint64_t tile_bytes = dt::kGatherTileBytes;
-    dt::GatherArgs a = {};
-    a.nranks = nranks;
-    uint64_t off = 0, tiles = 0;
-    bool dst_aligned = true;
-    for (int q = 0; q < nranks; q++) dst_aligned = dst_aligned && aligned16(recv[q]);
-    for (int r = 0; r < nranks; r++) {
-        const size_t c = sendcounts ? sendcounts[r] : equal_count;
-        a.src[r] = send[r];
-        a.dst[r] = recv[r];
-        a.bytes[r] = c * es;
-        a.offset[r] = off;
-        a.tile_start[r] = uint32_t(tiles);
-        if (dst_aligned && aligned16(send[r]) && off % 16 == 0) a.aligned |= 1u << r;  // NULL (empty) is aligned
-        off += c * es;
-        tiles += (c * es + tile_bytes - 1) / tile_bytes;
-        if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "all_gather too large for one launch");
-    }
-    a.tile_start[nranks] = uint32_t(tiles);
     // in place (NCCL-style) is send[r] == recv[r] + offset[r]; any other alias is refused
+    size_t off = 0;
+    std::vector<size_t> offset(nranks);
+    for (int r = 0; r < nranks; r++) {
+        offset[r] = off;
+        off += counts[r] * es;
+    }
     for (int q = 0; q < nranks; q++)
         for (int r = 0; r < nranks; r++) {
-            if (a.bytes[r] && cptr(send[r]) >= cptr(recv[q]) && cptr(send[r]) < cptr(recv[q]) + off &&
-                !(q == r && cptr(send[r]) == cptr(recv[r]) + a.offset[r]))
+            if (counts[r] && cptr(send[r]) >= cptr(recv[q]) && cptr(send[r]) < cptr(recv[q]) + off &&
+                !(q == r && cptr(send[r]) == cptr(recv[r]) + offset[r]))
                 return fail(DT_ERR_ARG, "send[%d] lies inside recv[%d] other than at its own slot", r, q);
             if (r != q && recv[q] == recv[r]) return fail(DT_ERR_ARG, "recv[%d] equals recv[%d]", q, r);
         }
-    if (tiles == 0) return DT_OK;
-    return check_hip(dt::launch_gather(a, uint32_t(tiles), stream), "all_gather launch");
+    std::vector<void*> table(size_t(nranks) * nranks);
+    for (int r = 0; r < nranks; r++)
+        for (int q = 0; q < nranks; q++) table[size_t(r) * nranks + q] = static_cast<char*>(recv[q]) + offset[r];
+    return fan_out(send, counts.data(), table.data(), nranks, es, stream, "all_gather launch");
+}
+
+dt_status dt_all_gather_into_vec(const void* const* send, void* const* recv, int nranks, const size_t* sendcounts,
+                                 size_t equal_count, dt_dtype dtype, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if (!valid_dtype(dtype)) return fail(DT_ERR_ARG, "bad dtype %d", dtype);
+    if (send == nullptr || recv == nullptr) return fail(DT_ERR_ARG, "send/recv array is NULL");
+    const size_t es = esize_of(dtype);
+    std::vector<size_t> counts(nranks);
+    std::vector<void*> table(size_t(nranks) * nranks);
+    for (int r = 0; r < nranks; r++) {
+        counts[r] = sendcounts ? sendcounts[r] : equal_count;
+        if (counts[r] > (size_t(1) << 40)) return fail(DT_ERR_ARG, "sendcount[%d]=%zu too large", r, counts[r]);
+        if (counts[r] == 0) continue;  // empty pieces may carry NULL pointers
+        if (send[r] == nullptr) return fail(DT_ERR_ARG, "send[%d] is NULL", r);
+        for (int q = 0; q < nranks; q++) {
+            void* d = recv[size_t(q) * nranks + r];
+            if (d == nullptr) return fail(DT_ERR_ARG, "recv[%d] (rank %d's copy of rank %d) is NULL", q * nranks + r, q, r);
+            if (d == send[r]) return fail(DT_ERR_ARG, "recv[%d] aliases send[%d]", q * nranks + r, r);
+            table[size_t(r) * nranks + q] = d;
+        }
+    }
+    return fan_out(send, counts.data(), table.data(), nranks, es, stream, "all_gather_into_vec launch");
+}
+
+dt_status dt_broadcast(const void* root_send, void* const* recv, int nranks, size_t count, dt_dtype dtype,
+                       hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if (!valid_dtype(dtype)) return fail(DT_ERR_ARG, "bad dtype %d", dtype);
+    if (recv == nullptr) return fail(DT_ERR_ARG, "recv array is NULL");
+    if (count == 0) return DT_OK;
+    if (count > (size_t(1) << 40)) return fail(DT_ERR_ARG, "count=%zu too large", count);
+    if (root_send == nullptr) return fail(DT_ERR_ARG, "root_send is NULL");
+    if ((st = check_ptr_array(recv, nranks, "recv")) != DT_OK) return st;
+    for (int q = 0; q < nranks; q++)
+        for (int r = 0; r < q; r++)
+            if (recv[q] == recv[r]) return fail(DT_ERR_ARG, "recv[%d] equals recv[%d]", q, r);
+    // the fan-out engine with one source: rank slot 0 carries the root's data
+    const void* src[1] = {root_send};
+    size_t counts[1] = {count};
+    return fan_out(src, counts, recv, nranks, esize_of(dtype), stream, "broadcast launch", /*nsources=*/1);
+}
+
+dt_status dt_replicate_to_shard(const void* const* send, void* const* recv, int nranks, size_t recvcount,
+                                dt_dtype dtype, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if (!valid_dtype(dtype)) return fail(DT_ERR_ARG, "bad dtype %d", dtype);
+    if (send == nullptr || recv == nullptr) return fail(DT_ERR_ARG, "send/recv array is NULL");
+    if (recvcount == 0) return DT_OK;
+    if ((st = check_ptr_array(send, nranks, "send")) != DT_OK) return st;
+    if ((st = check_ptr_array(recv, nranks, "recv")) != DT_OK) return st;
+    const size_t es = esize_of(dtype);
+    std::vector<const void*> src(nranks);
+    std::vector<void*> dst(nranks);
+    std::vector<size_t> bytes(nranks, recvcount * es);
+    for (int r = 0; r < nranks; r++) {
+        src[r] = cptr(send[r]) + size_t(r) * recvcount * es;
+        dst[r] = recv[r];
+    }
+    return copy_segments(src, dst, bytes, stream, "replicate_to_shard launch");
+}
+
+dt_status dt_all_to_all_dims(const void* const* send, void* const* recv, int nranks, size_t rows, size_t cols,
+                             int src_dim, int dst_dim, dt_dtype dtype, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if (!valid_dtype(dtype)) return fail(DT_ERR_ARG, "bad dtype %d", dtype);
+    if (src_dim < 0 || src_dim > 1 || dst_dim < 0 || dst_dim > 1)
+        return fail(DT_ERR_ARG, "src_dim %d / dst_dim %d must be 0 or 1", src_dim, dst_dim);
+    if (send == nullptr || recv == nullptr) return fail(DT_ERR_ARG, "send/recv array is NULL");
+    const size_t P = size_t(nranks);
+    if ((src_dim == 0 || dst_dim == 0) && rows % P != 0) return fail(DT_ERR_ARG, "rows=%zu not divisible by %d", rows, nranks);
+    if ((src_dim == 1 || dst_dim == 1) && cols % P != 0) return fail(DT_ERR_ARG, "cols=%zu not divisible by %d", cols, nranks);
+    if (rows == 0 || cols == 0) return DT_OK;
+    if (rows > (size_t(1) << 31) || cols > (size_t(1) << 31)) return fail(DT_ERR_ARG, "tensor too large");
+    if ((st = check_ptr_array(send, nranks, "send")) != DT_OK) return st;
+    if ((st = check_ptr_array(recv, nranks, "recv")) != DT_OK) return st;
+    for (int q = 0; q < nranks; q++)
+        for (int r = 0; r < nranks; r++)
+            if (recv[q] == send[r]) return fail(DT_ERR_ARG, "recv[%d] aliases send[%d]", q, r);
+    const size_t es = esize_of(dtype);
+    if (src_dim == dst_dim) {  // no exchange: each rank copies its own block
+        const size_t block = (src_dim == 0 ? rows / P * cols : rows * (cols / P)) * es;
+        std::vector<const void*> src(send, send + nranks);
+        std::vector<void*> dst(recv, recv + nranks);
+        std::vector<size_t> bytes(nranks, block);
+        return copy_segments(src, dst, bytes, stream, "all_to_all_dims copy launch");
+    }
+    dt::DimsArgs a = {};
+    bool vec = true;
+    for (int r = 0; r < nranks; r++) {
+        a.src[r] = send[r];
+        a.dst[r] = recv[r];
+        vec = vec && aligned16(send[r]) && aligned16(recv[r]);
+    }
+    a.rows = rows;
+    a.cols = cols;
+    a.rp = rows / P;
+    a.cp = cols / P;
+    a.esize = uint32_t(es);
+    a.nranks = nranks;
+    a.dir = src_dim == 0 ? 0 : 1;
+    a.nruns = uint64_t(rows) * P;
+    const uint64_t run_bytes = a.cp * es;
+    a.vec = (vec && run_bytes % 16 == 0) ? 1u : 0u;
+    uint64_t blocks;
+    if (run_bytes >= dt::kDimsTileBytes) {
+        a.tiles_per_run = uint32_t((run_bytes + dt::kDimsTileBytes - 1) / dt::kDimsTileBytes);
+        a.runs_per_block = 1;
+        blocks = a.nruns * a.tiles_per_run;
+    } else {
+        a.tiles_per_run = 1;
+        a.runs_per_block = uint32_t(std::min<uint64_t>(dt::kDimsMaxRunsPerBlock,
+                                                        std::max<uint64_t>(1, dt::kDimsTileBytes / run_bytes)));
+        blocks = (a.nruns + a.runs_per_block - 1) / a.runs_per_block;
+    }
+    if (blocks > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "all_to_all_dims too large for one launch");
+    return check_hip(dt::launch_all_to_all_dims(a, uint32_t(blocks), stream), "all_to_all_dims launch");
 }
 
 dt_status dt_all_to_all(const void* const* send, void* const* recv, int nranks, const size_t* splits,

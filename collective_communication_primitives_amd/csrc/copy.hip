@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
     int r = 0;
     while (r + 1 < nr && a.tile_start[r + 1] <= b) r++;
     const char* src = static_cast<const char*>(a.src[r]);
-    const uint64_t off = a.offset[r];
+    void* const* dsts = a.dst + r * nr;
     const uint64_t b0 = uint64_t(b - a.tile_start[r]) * kTile;
     const uint64_t b1 = min(a.bytes[r], b0 + kTile);
     if ((a.aligned >> r) & 1u) {
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
 #pragma unroll
         for (int q = 0; q < PMAX; q++) {
             if (q < nr) {
-                char* dst = static_cast<char*>(a.dst[q]) + off;
+                char* dst = static_cast<char*>(dsts[q]);
 #pragma unroll
                 for (int u = 0; u < U; u++) {
                     const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
@@ -52,12 +52,12 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
         const uint64_t t = v1 * 16 + threadIdx.x;  // ragged end: fewer than 16 bytes
         if (t < b1) {
             const char c = src[t];
-            for (int q = 0; q < nr; q++) static_cast<char*>(a.dst[q])[off + t] = c;
+            for (int q = 0; q < nr; q++) static_cast<char*>(dsts[q])[t] = c;
         }
     } else {
         for (uint64_t t = b0 + threadIdx.x; t < b1; t += kBlock) {
             const char c = src[t];
-            for (int q = 0; q < nr; q++) static_cast<char*>(a.dst[q])[off + t] = c;
+            for (int q = 0; q < nr; q++) static_cast<char*>(dsts[q])[t] = c;
         }
     }
 }
@@ -113,6 +113,127 @@ hipError_t gather_pu(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     return hipGetLastError();
 }
 }  // namespace
+
+// ------------------------------------------------------- segment copy --
+// Independent 1:1 byte copies, 16 KiB tiles; a workgroup finds its segment
+// by binary search over the tile prefix.
+__global__ __launch_bounds__(kBlock) void k_copy_segments(SegCopyArgs a) {
+    constexpr int U = int(kSegCopyTileBytes / 16 / kBlock);
+    const uint32_t b = blockIdx.x;
+    int lo = 0, hi = a.nsegs;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.tile_start[mid] <= b) lo = mid;
+        else hi = mid;
+    }
+    const int k = lo;
+    const char* src = static_cast<const char*>(a.src[k]);
+    char* dst = static_cast<char*>(a.dst[k]);
+    const uint64_t b0 = uint64_t(b - a.tile_start[k]) * kSegCopyTileBytes;
+    const uint64_t b1 = min(a.bytes[k], b0 + kSegCopyTileBytes);
+    if ((a.aligned >> k) & 1ull) {
+        const uint64_t v1 = b1 / 16;
+        u32x4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
+            if (v < v1) x[u] = load16(src + v * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
+            if (v < v1) store16(dst + v * 16, x[u]);
+        }
+        const uint64_t t = v1 * 16 + threadIdx.x;
+        if (t < b1) dst[t] = src[t];
+    } else {
+        for (uint64_t t = b0 + threadIdx.x; t < b1; t += kBlock) dst[t] = src[t];
+    }
+}
+
+// ------------------------------------------------- shard-dimension A2A --
+__device__ __forceinline__ void dims_run(const DimsArgs& a, uint64_t k, const char** src, char** dst) {
+    const uint64_t es = a.esize;
+    if (a.dir == 0) {
+        const uint64_t j = k / a.rows, row = k - j * a.rows, i = row / a.rp;
+        *src = static_cast<const char*>(a.src[i]) + ((row - i * a.rp) * a.cols + j * a.cp) * es;
+        *dst = static_cast<char*>(a.dst[j]) + row * a.cp * es;
+    } else {
+        const uint64_t P = uint64_t(a.nranks);
+        const uint64_t j = k / (a.rp * P), rem = k - j * a.rp * P, row = rem / P, i = rem - row * P;
+        *src = static_cast<const char*>(a.src[i]) + (j * a.rp + row) * a.cp * es;
+        *dst = static_cast<char*>(a.dst[j]) + (row * a.cols + i * a.cp) * es;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_all_to_all_dims(DimsArgs a) {
+    __shared__ const char* run_src[kDimsMaxRunsPerBlock];
+    __shared__ char* run_dst[kDimsMaxRunsPerBlock];
+    const uint64_t run_bytes = a.cp * a.esize;
+    const uint64_t b = blockIdx.x;
+    uint64_t k0, nk, lo, hi;  // runs [k0, k0 + nk), byte slice [lo, hi) of each
+    if (a.tiles_per_run > 1) {
+        k0 = b / a.tiles_per_run;
+        nk = 1;
+        lo = (b - k0 * a.tiles_per_run) * kDimsTileBytes;
+        hi = min(run_bytes, lo + kDimsTileBytes);
+    } else {
+        k0 = b * a.runs_per_block;
+        nk = min(uint64_t(a.runs_per_block), a.nruns - k0);
+        lo = 0;
+        hi = run_bytes;
+    }
+    if (threadIdx.x < nk) {  // decode each run once per workgroup
+        const char* from;
+        char* to;
+        dims_run(a, k0 + threadIdx.x, &from, &to);
+        run_src[threadIdx.x] = from + lo;
+        run_dst[threadIdx.x] = to + lo;
+    }
+    __syncthreads();
+    const uint64_t span = hi - lo;
+    if (a.vec) {
+        const uint32_t sv = uint32_t(span / 16);
+        const uint32_t total = uint32_t(nk) * sv;
+        constexpr int U = 4;
+        for (uint32_t t0 = threadIdx.x; t0 < total; t0 += kBlock * U) {
+            u32x4 x[U];
+            char* to[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const uint32_t t = t0 + u * kBlock;
+                to[u] = nullptr;
+                if (t < total) {
+                    const uint32_t rk = t / sv, v = t - rk * sv;
+                    x[u] = load16(run_src[rk] + uint64_t(v) * 16);
+                    to[u] = run_dst[rk] + uint64_t(v) * 16;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (to[u]) store16(to[u], x[u]);
+        }
+    } else {
+        const uint64_t total = nk * span;
+        for (uint64_t t = threadIdx.x; t < total; t += kBlock) {
+            const uint64_t rk = t / span, c = t - rk * span;
+            run_dst[rk][c] = run_src[rk][c];
+        }
+    }
+}
+
+hipError_t launch_copy_segments(const SegCopyArgs& a, hipStream_t s) {
+    const uint32_t tiles = a.tile_start[a.nsegs];
+    if (tiles == 0) return hipSuccess;
+    k_copy_segments<<<tiles, kBlock, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_t s) {
+    if (blocks == 0) return hipSuccess;
+    k_all_to_all_dims<<<blocks, kBlock, 0, s>>>(a);
+    return hipGetLastError();
+}
 
 hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     if (tiles == 0) return hipSuccess;

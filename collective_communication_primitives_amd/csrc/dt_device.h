@@ -14,7 +14,7 @@
 namespace dt {
 
 enum : int { kF32 = 0, kBF16 = 1, kI32 = 2 };
-enum : int { kSum = 0, kMax = 1, kMin = 2 };
+enum : int { kSum = 0, kMax = 1, kMin = 2, kAvg = 3 };
 
 constexpr int kMaxRanks = 16;
 constexpr int kBlock = 256;  // threads per workgroup: four 64-wide waves
@@ -65,10 +65,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 // -------------------------------------------------------------- operators --
 // Max/min: strict compare, the accumulator wins ties (earlier rank, also
-// between +0 and -0); the first NaN met is kept.
+// between +0 and -0); the first NaN met is kept.  Avg folds as a sum and
+// divides once at the end (finish()).
 template <int OP>
 __device__ __forceinline__ float combine(float a, float v) {
-    if constexpr (OP == kSum) {
+    if constexpr (OP == kSum || OP == kAvg) {
         return a + v;
     } else {
         const bool a_nan = a != a;
@@ -80,13 +81,26 @@ __device__ __forceinline__ float combine(float a, float v) {
 
 template <int OP>
 __device__ __forceinline__ int32_t combine(int32_t a, int32_t v) {
-    if constexpr (OP == kSum) {
+    if constexpr (OP == kSum || OP == kAvg) {
         return int32_t(uint32_t(a) + uint32_t(v));
     } else if constexpr (OP == kMax) {
         return v > a ? v : a;
     } else {
         return v < a ? v : a;
     }
+}
+
+// The mean: one IEEE division of the fp32 sum (correctly rounded), or C's
+// truncating division of the wrapped int32 sum, by the rank count.
+template <int OP>
+__device__ __forceinline__ float finish(float a, int nr) {
+    if constexpr (OP == kAvg) return a / float(nr);
+    else return a;
+}
+template <int OP>
+__device__ __forceinline__ int32_t finish(int32_t a, int nr) {
+    if constexpr (OP == kAvg) return a / nr;
+    else return a;
 }
 
 // Elements per 16-byte vector.
@@ -121,7 +135,7 @@ __device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[P], int nr) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; i++) out[i] = pack_bf16(acc[2 * i], acc[2 * i + 1]);
+        for (int i = 0; i < 4; i++) out[i] = pack_bf16(finish<OP>(acc[2 * i], nr), finish<OP>(acc[2 * i + 1], nr));
     } else if constexpr (DT == kF32) {
         float acc[4];
 #pragma unroll
@@ -134,7 +148,7 @@ __device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[P], int nr) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; i++) out[i] = __float_as_uint(acc[i]);
+        for (int i = 0; i < 4; i++) out[i] = __float_as_uint(finish<OP>(acc[i], nr));
     } else {
         int32_t acc[4];
 #pragma unroll
@@ -147,7 +161,7 @@ __device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[P], int nr) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; i++) out[i] = uint32_t(acc[i]);
+        for (int i = 0; i < 4; i++) out[i] = uint32_t(finish<OP>(acc[i], nr));
     }
     return out;
 }
@@ -158,15 +172,15 @@ __device__ __forceinline__ void fold_elem(const void* const* src, int nr, size_t
     if constexpr (DT == kI32) {
         int32_t acc = static_cast<const int32_t*>(src[0])[e];
         for (int r = 1; r < nr; r++) acc = combine<OP>(acc, static_cast<const int32_t*>(src[r])[e]);
-        static_cast<int32_t*>(dst)[de] = acc;
+        static_cast<int32_t*>(dst)[de] = finish<OP>(acc, nr);
     } else if constexpr (DT == kF32) {
         float acc = static_cast<const float*>(src[0])[e];
         for (int r = 1; r < nr; r++) acc = combine<OP>(acc, static_cast<const float*>(src[r])[e]);
-        static_cast<float*>(dst)[de] = acc;
+        static_cast<float*>(dst)[de] = finish<OP>(acc, nr);
     } else {
         float acc = bf16_at(static_cast<const uint16_t*>(src[0])[e]);
         for (int r = 1; r < nr; r++) acc = combine<OP>(acc, bf16_at(static_cast<const uint16_t*>(src[r])[e]));
-        static_cast<uint16_t*>(dst)[de] = uint16_t(to_bf16(acc));
+        static_cast<uint16_t*>(dst)[de] = uint16_t(to_bf16(finish<OP>(acc, nr)));
     }
 }
 

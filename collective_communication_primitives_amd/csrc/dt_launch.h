@@ -53,15 +53,49 @@ struct SegReduceScatterArgs {
     int nranks;
 };
 
-// AllGather: rank r's bytes [0, bytes[r]) land at offset[r] of every output.
+// Fan-out copy (AllGather, AllGatherIntoVec, Broadcast): rank r's bytes
+// [0, bytes[r]) are written to dst[r*nranks + q] for every q.
 struct GatherArgs {
     const void* src[kMaxRanksHost];
-    void* dst[kMaxRanksHost];
+    void* dst[kMaxRanksHost * kMaxRanksHost];
     uint64_t bytes[kMaxRanksHost];
-    uint64_t offset[kMaxRanksHost];
     uint32_t tile_start[kMaxRanksHost + 1];
-    uint32_t aligned;      // bit r: rank r's piece may use 16-byte vectors
+    uint32_t aligned;      // bit r: rank r's piece and its destinations allow 16-byte vectors
     int nranks;
+};
+
+// 1:1 copies of independent byte ranges (ReplicateToShard and other
+// per-rank copies): segment k copies bytes[k] from src[k] to dst[k].
+constexpr int kMaxCopySegs = 64;
+struct SegCopyArgs {
+    const void* src[kMaxCopySegs];
+    void* dst[kMaxCopySegs];
+    uint64_t bytes[kMaxCopySegs];
+    uint32_t tile_start[kMaxCopySegs + 1];
+    uint64_t aligned;      // bit k: segment k allows 16-byte vectors
+    int nsegs;
+};
+
+// AllToAll between shard dimensions of a row-major [rows, cols] tensor.
+// Every exchange is a set of runs of cp = cols/P contiguous elements:
+//   dir 0 (Shard(0) -> Shard(1)): run k = (j, a), j = k / rows, a = k % rows:
+//     x_{a/rp} + ((a % rp) * cols + j * cp)  ->  y_j + a * cp
+//   dir 1 (Shard(1) -> Shard(0)): run k = (j, a, i), j = k / (rp*P),
+//     a = (k / P) % rp, i = k % P:
+//     x_i + (j * rp + a) * cp  ->  y_j + a * cols + i * cp
+// A workgroup copies runs_per_block whole runs, or one 1/tiles_per_run
+// slice of a long run.
+struct DimsArgs {
+    const void* src[kMaxRanksHost];
+    void* dst[kMaxRanksHost];
+    uint64_t rows, cols, rp, cp;   // elements
+    uint32_t esize;
+    uint32_t runs_per_block;       // >= 1
+    uint32_t tiles_per_run;        // >= 1 (only one of the two exceeds 1)
+    uint32_t vec;                  // 1: runs and bases allow 16-byte vectors
+    uint64_t nruns;
+    int nranks;
+    int dir;
 };
 
 // AllToAll: split[i*P+j] bytes travel from rank i to rank j.
@@ -109,6 +143,11 @@ uint64_t seg_rs_tile_vecs(int nranks);
 hipError_t launch_copy_pieces(const PieceArgs& a, int esize, int to_ws, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s);
 hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t s);
+hipError_t launch_copy_segments(const SegCopyArgs& a, hipStream_t s);
+hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_t s);
+constexpr uint64_t kSegCopyTileBytes = 16384;
+constexpr uint64_t kDimsTileBytes = 16384;
+constexpr uint32_t kDimsMaxRunsPerBlock = 64;
 hipError_t launch_barrier(const BarrierArgs& a, int spread, hipStream_t s);
 hipError_t launch_exchange(const ExchangeArgs& a, int spread, hipStream_t s);
 

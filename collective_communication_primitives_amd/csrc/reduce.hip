@@ -278,7 +278,8 @@ hipError_t reduce_vec_dt(const ReduceArgs& a, int op, hipStream_t s) {
     switch (op) {
         case kSum: return reduce_vec_op<DT, kSum>(a, s);
         case kMax: return reduce_vec_op<DT, kMax>(a, s);
-        default: return reduce_vec_op<DT, kMin>(a, s);
+        case kMin: return reduce_vec_op<DT, kMin>(a, s);
+        default: return reduce_vec_op<DT, kAvg>(a, s);
     }
 }
 
@@ -297,7 +298,8 @@ hipError_t reduce_elems_dt(const ReduceArgs& a, int op, hipStream_t s) {
     switch (op) {
         case kSum: return reduce_elems_op<DT, kSum>(a, s);
         case kMax: return reduce_elems_op<DT, kMax>(a, s);
-        default: return reduce_elems_op<DT, kMin>(a, s);
+        case kMin: return reduce_elems_op<DT, kMin>(a, s);
+        default: return reduce_elems_op<DT, kAvg>(a, s);
     }
 }
 
@@ -328,7 +330,8 @@ hipError_t reduce_pieces_dt(const PieceArgs& a, int op, hipStream_t s) {
     switch (op) {
         case kSum: return reduce_pieces_op<DT, kSum>(a, s);
         case kMax: return reduce_pieces_op<DT, kMax>(a, s);
-        default: return reduce_pieces_op<DT, kMin>(a, s);
+        case kMin: return reduce_pieces_op<DT, kMin>(a, s);
+        default: return reduce_pieces_op<DT, kAvg>(a, s);
     }
 }
 
@@ -360,7 +363,8 @@ hipError_t reduce_scatter_segs_dt(const SegReduceScatterArgs& a, int op, hipStre
     switch (op) {
         case kSum: return reduce_scatter_segs_op<DT, kSum>(a, s);
         case kMax: return reduce_scatter_segs_op<DT, kMax>(a, s);
-        default: return reduce_scatter_segs_op<DT, kMin>(a, s);
+        case kMin: return reduce_scatter_segs_op<DT, kMin>(a, s);
+        default: return reduce_scatter_segs_op<DT, kAvg>(a, s);
     }
 }
 

@@ -48,7 +48,11 @@ extern "C" {
 #define DT_MAX_RANKS 16
 
 typedef enum { DT_FLOAT32 = 0, DT_BFLOAT16 = 1, DT_INT32 = 2 } dt_dtype;
-typedef enum { DT_SUM = 0, DT_MAX = 1, DT_MIN = 2 } dt_op;
+/* DT_AVG: the rank-order sum divided once by the number of ranks in the
+ * collective (fp32 IEEE division before the bf16 rounding; truncating
+ * division of the wrapped sum for int32).  The hyper-parallel issue's
+ * AllReduceParamGroup (sec. 6) divides the summed gradient by the group size. */
+typedef enum { DT_SUM = 0, DT_MAX = 1, DT_MIN = 2, DT_AVG = 3 } dt_op;
 typedef enum {
     DT_OK = 0,
     DT_ERR_ARG = 1,
@@ -82,6 +86,36 @@ dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nran
  * only sets the element size.  recv[q] holds sum(sendcounts) elements. */
 dt_status dt_all_gather(const void* const* send, void* const* recv, int nranks, const size_t* sendcounts,
                         size_t equal_count, dt_dtype dtype, hipStream_t stream);
+
+/* AllGatherIntoVec (DTorch page sec. 2.1): the gathered pieces stay separate
+ * tensors.  recv[q*nranks + r] (sendcounts[r] elements, or equal_count when
+ * sendcounts is NULL) receives a copy of send[r] for every rank q: one launch,
+ * each piece read once and written nranks times. */
+dt_status dt_all_gather_into_vec(const void* const* send, void* const* recv, int nranks, const size_t* sendcounts,
+                                 size_t equal_count, dt_dtype dtype, hipStream_t stream);
+
+/* Broadcast (DTorch page sec. 2.2 lists broadcast among the backend's
+ * collectives): recv[q] = root_send (count elements) for every q.  One read of
+ * the root's buffer, nranks writes.  recv[root] may equal root_send. */
+dt_status dt_broadcast(const void* root_send, void* const* recv, int nranks, size_t count, dt_dtype dtype,
+                       hipStream_t stream);
+
+/* ReplicateToShard, Replicate -> Shard(0) (DTorch page sec. 2.1 and 2.5; no
+ * exchange between ranks): recv[r] = elements [r*recvcount, (r+1)*recvcount)
+ * of send[r], where send[r] holds nranks*recvcount elements. */
+dt_status dt_replicate_to_shard(const void* const* send, void* const* recv, int nranks, size_t recvcount,
+                                dt_dtype dtype, hipStream_t stream);
+
+/* AllToAll between shard dimensions (DTorch page sec. 2.1 AllToAll(input,
+ * srcDim, destDim) and sec. 2.5 S -> S) of a row-major [rows, cols] tensor.
+ * Under Shard(0) rank r holds rows [r*rows/P, (r+1)*rows/P) as a contiguous
+ * [rows/P, cols] block; under Shard(1) it holds columns [r*cols/P,
+ * (r+1)*cols/P) as a contiguous [rows, cols/P] block.  send[r] is rank r's
+ * block under src_dim, recv[r] receives its block under dst_dim.  The
+ * sharded dimension(s) must divide by nranks (DT_ERR_ARG otherwise);
+ * src_dim == dst_dim copies each rank's block. */
+dt_status dt_all_to_all_dims(const void* const* send, void* const* recv, int nranks, size_t rows, size_t cols,
+                             int src_dim, int dst_dim, dt_dtype dtype, hipStream_t stream);
 
 /* AllToAll, Shard -> Shard, split-matrix form: splits is a host array of
  * nranks*nranks element counts, splits[i*nranks + j] = elements rank i sends

@@ -1,0 +1,159 @@
+"""GPU parity for the rest of the placement matrix: the AVG op, Broadcast,
+AllGatherIntoVec, ReplicateToShard and the AllToAll between shard
+dimensions, each against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import Guarded, compare, note, to_np
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}
+
+
+@pytest.fixture(scope="module")
+def dt():
+    import collective_communication_primitives_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def ranks(dtype, p, n, seed):
+    if dtype == "i32":
+        return synth.full_range_int_ranks(p, n, seed, device="cuda")
+    xs = synth.uniform_ranks(p, n, seed, device="cuda")
+    return xs if dtype == "f32" else [x.to(torch.bfloat16) for x in xs]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("p,n", [(1, 17), (3, 3003), (8, 8 * 4099), (16, 16 * 640)])
+def test_avg_allreduce_reduce_scatter_bucket(dt, orc, dtype, p, n):
+    note(f"avg {dtype} P={p} n={n}")
+    xs = ranks(dtype, p, n, seed=p + n)
+    host = [to_np(x) for x in xs]
+    ys = [Guarded(n, DTYPES[dtype]).poison() for _ in range(p)]
+    dt.dt_allreduce(xs, [y.t for y in ys], op="avg")
+    shards = [torch.empty(n // p, dtype=DTYPES[dtype], device="cuda") for _ in range(p)]
+    dt.dt_reduce_scatter(xs, shards, op="avg")
+    grads = [[x[:n // 2].clone(), x[n // 2:].clone()] for x in xs]
+    dt.dt_bucket_allreduce(grads, bucket_bytes=256, op="avg")
+    torch.cuda.synchronize()
+    want = orc.allreduce(host, "avg")
+    for q in range(p):
+        ys[q].check()
+        compare(to_np(ys[q].t), want[q], f"AR rank {q}")
+    want_rs = orc.reduce_scatter(host, "avg")
+    for r in range(p):
+        compare(to_np(shards[r]), want_rs[r], f"RS rank {r}")
+    want_b = orc.bucket_allreduce([[h[:n // 2], h[n // 2:]] for h in host], 256, "avg")
+    for r in range(p):
+        for t in range(2):
+            compare(to_np(grads[r][t]), want_b[r][t], f"bucket rank {r} tensor {t}")
+
+
+@pytest.mark.parametrize("p,n", [(1, 5), (2, 4097), (8, 1 << 20), (16, 333)])
+def test_broadcast(dt, orc, p, n):
+    note(f"broadcast P={p} n={n}")
+    root = torch.randint(-2 ** 31, 2 ** 31, (n,), dtype=torch.int64, device="cuda").to(torch.int32)
+    outs = [Guarded(n, torch.int32).poison() for _ in range(p)]
+    dt.dt_broadcast(root, [o.t for o in outs])
+    torch.cuda.synchronize()
+    want = orc.broadcast(to_np(root), p)
+    for q, o in enumerate(outs):
+        o.check()
+        compare(to_np(o.t), want[q], f"rank {q}")
+    note("broadcast unaligned root")
+    g = Guarded(n, torch.int32, offset_elems=1)
+    g.t.copy_(root)
+    outs2 = [Guarded(n, torch.int32, offset_elems=2).poison() for _ in range(p)]
+    dt.dt_broadcast(g.t, [o.t for o in outs2])
+    torch.cuda.synchronize()
+    for q, o in enumerate(outs2):
+        o.check()
+        compare(to_np(o.t), want[q], f"unaligned rank {q}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("counts", [[3, 0, 7], [4096] * 8, [1, 16383, 9, 4100], [8192] * 16])
+def test_all_gather_into_vec(dt, orc, dtype, counts):
+    p = len(counts)
+    note(f"all_gather_into_vec {dtype} counts={counts}")
+    xs = [ranks(dtype, 1, c, seed=10 + r)[0] if c else torch.empty(0, dtype=DTYPES[dtype], device="cuda")
+          for r, c in enumerate(counts)]
+    outs = [[Guarded(c, DTYPES[dtype]).poison() for c in counts] for _ in range(p)]
+    dt.dt_all_gather_into_vec(xs, [[o.t for o in row] for row in outs])
+    torch.cuda.synchronize()
+    want = orc.all_gather_into_vec([to_np(x) for x in xs])
+    for q in range(p):
+        for r in range(p):
+            outs[q][r].check()
+            compare(to_np(outs[q][r].t), want[q][r], f"rank {q} piece {r}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("p,m", [(1, 9), (3, 1001), (8, 1 << 17), (16, 64)])
+def test_replicate_to_shard(dt, orc, dtype, p, m):
+    note(f"replicate_to_shard {dtype} P={p} m={m}")
+    xs = ranks(dtype, p, p * m, seed=3 * p + m)
+    outs = [Guarded(m, DTYPES[dtype]).poison() for _ in range(p)]
+    dt.dt_replicate_to_shard(xs, [o.t for o in outs])
+    torch.cuda.synchronize()
+    want = orc.replicate_to_shard([to_np(x) for x in xs])
+    for r, o in enumerate(outs):
+        o.check()
+        compare(to_np(o.t), want[r], f"rank {r}")
+    # P -> R -> S equals P -> S, on the device
+    ar = [torch.empty_like(x) for x in xs]
+    dt.dt_allreduce(xs, ar)
+    s1 = [torch.empty(m, dtype=DTYPES[dtype], device="cuda") for _ in range(p)]
+    s2 = [torch.empty(m, dtype=DTYPES[dtype], device="cuda") for _ in range(p)]
+    dt.dt_replicate_to_shard(ar, s1)
+    dt.dt_reduce_scatter(xs, s2)
+    torch.cuda.synchronize()
+    for r in range(p):
+        assert torch.equal(s1[r].view(torch.uint8), s2[r].view(torch.uint8)), r
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("p,rows,cols", [(1, 3, 5), (2, 6, 10), (3, 9, 12), (4, 64, 4096), (8, 8192, 8),
+                                         (8, 16, 4096 * 8), (16, 32, 48)])
+def test_all_to_all_dims(dt, orc, dtype, p, rows, cols):
+    for src in (0, 1):
+        for dst in (0, 1):
+            if (0 in (src, dst) and rows % p) or (1 in (src, dst) and cols % p):
+                continue
+            note(f"all_to_all_dims {dtype} P={p} [{rows},{cols}] {src}->{dst}")
+            n_src = (rows // p) * cols if src == 0 else rows * (cols // p)
+            n_dst = (rows // p) * cols if dst == 0 else rows * (cols // p)
+            xs = ranks(dtype, p, n_src, seed=rows + cols + src)
+            outs = [Guarded(n_dst, DTYPES[dtype]).poison() for _ in range(p)]
+            dt.dt_all_to_all_dims(xs, [o.t for o in outs], rows, cols, src, dst)
+            torch.cuda.synchronize()
+            want = orc.all_to_all_dims([to_np(x) for x in xs], rows, cols, src, dst)
+            for r, o in enumerate(outs):
+                o.check()
+                np.testing.assert_array_equal(to_np(o.t).view(np.uint8), want[r].view(np.uint8))
+
+
+def test_all_to_all_dims_round_trip_full_size(dt, orc):
+    """P=8, bf16 [8192, 8192]: Shard(0) -> Shard(1) against the oracle, then
+    back to Shard(0) returns every block."""
+    p, rows, cols = 8, 8192, 8192
+    note("all_to_all_dims full size bf16 [8192, 8192]")
+    xs = synth.normal_ranks(p, (rows // p, cols), seed=0, device="cuda")
+    mid = [torch.empty(rows, cols // p, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    back = [torch.empty_like(x) for x in xs]
+    dt.dt_all_to_all_dims(xs, mid, rows, cols, 0, 1)
+    dt.dt_all_to_all_dims(mid, back, rows, cols, 1, 0)
+    torch.cuda.synchronize()
+    want = orc.all_to_all_dims([to_np(x) for x in xs], rows, cols, 0, 1)
+    for r in range(p):
+        compare(to_np(mid[r]), want[r], f"rank {r}")
+        assert torch.equal(back[r].view(torch.int16), xs[r].view(torch.int16)), r
