@@ -261,7 +261,11 @@ def other_rows(dt, torch, steps: int, warmup: int):
       allreduce_p4: fp32 and int32, P=4, 1,048,576 elements per rank
         (32 MiB per launch, within the Infinity Cache: latency-bound);
       uneven_all_gather_p8: fp32 rows of 4096, row counts U[1, 16384];
-      all_to_all_p8: fp32 rows of 4096, split matrix U[0, 4096] rows."""
+      all_to_all_p8: fp32 rows of 4096, split matrix U[0, 4096] rows;
+      the placement extras at P=8 bf16: AVG AllReduce and ReplicateToShard of
+        [8192, 8192] per rank, Broadcast of one such tensor, AllGatherIntoVec
+        of 16 MiB shards, and the AllToAll between shard dimensions of a
+        [32768, 16384] tensor (1 GiB) in both directions."""
     import numpy as np
     import synth
     stream = torch.cuda.current_stream()
@@ -293,6 +297,27 @@ def other_rows(dt, torch, steps: int, warmup: int):
     ys = [torch.empty(total, device="cuda") for _ in range(P)]
     measure("uneven_all_gather_p8", lambda: dt.dt_all_gather(xs, ys), (1 + P) * total * 4)
     out["uneven_all_gather_p8"]["rows"] = counts.tolist()
+    del xs, ys
+    torch.cuda.empty_cache()
+
+    # placement-matrix extras, P=8
+    xs = synth.normal_ranks(P, SHAPE, seed=0, device="cuda", dtype=torch.bfloat16)
+    ys = [torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    s_bytes = SHAPE[0] * SHAPE[1] * 2
+    measure("allreduce_avg_p8_bf16", lambda: dt.dt_allreduce(xs, ys, op="avg"), 2 * P * s_bytes)
+    shard = [torch.empty(SHAPE[0] * SHAPE[1] // P, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    measure("replicate_to_shard_p8_bf16", lambda: dt.dt_replicate_to_shard(xs, shard), 2 * s_bytes)
+    measure("broadcast_p8_bf16", lambda: dt.dt_broadcast(xs[0], ys), (1 + P) * s_bytes)
+    vec = [[torch.empty_like(shard[r]) for r in range(P)] for _ in range(P)]
+    measure("all_gather_into_vec_p8_bf16", lambda: dt.dt_all_gather_into_vec(shard, vec), (1 + P) * s_bytes)
+    del xs, ys, shard, vec
+    torch.cuda.empty_cache()
+    rows, cols = 32768, 16384  # bf16, 1 GiB in total
+    blk = rows * cols // P
+    xs = [torch.randn(blk, device="cuda").to(torch.bfloat16) for _ in range(P)]
+    ys = [torch.empty(blk, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    measure("all_to_all_dims_0to1_p8_bf16", lambda: dt.dt_all_to_all_dims(xs, ys, rows, cols, 0, 1), 2 * rows * cols * 2)
+    measure("all_to_all_dims_1to0_p8_bf16", lambda: dt.dt_all_to_all_dims(xs, ys, rows, cols, 1, 0), 2 * rows * cols * 2)
     del xs, ys
     torch.cuda.empty_cache()
 
