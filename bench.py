@@ -332,6 +332,81 @@ def other_rows(dt, torch, steps: int, warmup: int):
     return out
 
 
+def overlap(dt, torch, reps: int = 12):
+    """Compute/communication overlap on one GPU, after the probe of the c10d
+    page (sec. 6, sec. 10.4): a bf16 [8192,8192] x [8192,8192] GEMM
+    (torch.matmul, a library GEMM) on the compute stream and the fp32 25 MiB
+    bucket AllReduce of P=8 ranks on a side stream.  Events on both streams
+    put both kernels on one clock; medians over `reps` runs.
+      overlap = (t_gemm + t_ar - t_both) / min(t_gemm, t_ar)
+    (1 = the AllReduce fully hidden, 0 = serialized).  Two issue orders, and
+    one "killer" (wait() before the GEMM, which serializes by construction)."""
+    import synth
+    xs = synth.uniform_ranks(P, synth.BUCKET_BYTES // 4, seed=0, device="cuda")
+    ys = [torch.empty_like(x) for x in xs]
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    comp, side = torch.cuda.current_stream(), dt.side_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def run(order):
+        torch.cuda.synchronize()
+        t0, s0, s1, g0, g1, t1 = ev(), ev(), ev(), ev(), ev(), ev()
+        t0.record(comp)
+
+        def ar():
+            side.wait_stream(comp)
+            s0.record(side)
+            dt.dt_allreduce(xs, ys, stream=side)
+            s1.record(side)
+
+        def gemm():
+            g0.record(comp)
+            torch.matmul(a, b)
+            g1.record(comp)
+
+        if order == "gemm":
+            gemm()
+        elif order == "ar":
+            ar()
+        elif order == "ar_first":
+            ar()
+            gemm()
+        elif order == "gemm_first":
+            gemm()
+            ar()
+        elif order == "wait_too_early":
+            ar()
+            comp.wait_stream(side)
+            gemm()
+        comp.wait_stream(side)
+        t1.record(comp)
+        torch.cuda.synchronize()
+        out = {"total_ms": t0.elapsed_time(t1)}
+        if order != "gemm":
+            out["ar_start_ms"], out["ar_end_ms"] = t0.elapsed_time(s0), t0.elapsed_time(s1)
+        if order != "ar":
+            out["gemm_start_ms"], out["gemm_end_ms"] = t0.elapsed_time(g0), t0.elapsed_time(g1)
+        return out
+
+    orders = ("gemm", "ar", "ar_first", "gemm_first", "wait_too_early")
+    samples = {o: [] for o in orders}
+    for it in range(reps + 2):
+        for o in orders:  # interleaved, so clock drift hits every mode alike
+            r = run(o)
+            if it >= 2:
+                samples[o].append(r)
+    med = {o: {k: round(statistics.median(r[k] for r in samples[o]), 4) for k in samples[o][0]} for o in orders}
+    t_g, t_a = med["gemm"]["total_ms"], med["ar"]["total_ms"]
+    out = {"gemm_ms": t_g, "allreduce_ms": t_a, "gemm_tflops": round(2 * 8192 ** 3 / (t_g * 1e-3) / 1e12, 1)}
+    for o in ("ar_first", "gemm_first", "wait_too_early"):
+        out[o] = dict(med[o], overlap=round((t_g + t_a - med[o]["total_ms"]) / min(t_g, t_a), 3))
+    print(json.dumps({"overlap": out}), flush=True)
+    return out
+
+
 def probe(dt, torch, reps: int = 10):
     """Workload for hardware-counter passes: the bench kernels and a plain
     copy of known size (1 GiB read + 1 GiB written) to calibrate
@@ -362,6 +437,7 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also run the P=16 size sweep and barrier latency")
     ap.add_argument("--probe", action="store_true", help="only run the kernels for a hardware-counter pass")
     ap.add_argument("--hsdp", action="store_true", help="also time the 32-layer gradient pipeline (103.6 GB)")
+    ap.add_argument("--overlap", action="store_true", help="also run the GEMM / AllReduce overlap experiment")
     ap.add_argument("--all", action="store_true",
                     help="also time every other workload: small AllReduce, uneven AllGather, AllToAll, the size "
                          "sweep, the barrier and the gradient pipeline")
@@ -452,7 +528,7 @@ def main():
 
     extra = {"kernels": kernels, "host_seconds_timed": round(t_host, 4), "kernel_source_hash": kernel_source_hash()}
     if args.all:
-        args.sweep = args.hsdp = True
+        args.sweep = args.hsdp = args.overlap = True
         extra["rows"] = other_rows(dt, torch, steps=args.steps, warmup=args.warmup)
     if args.sweep:
         rows, fit = sweep(dt, torch, steps=max(5, args.steps // 2), warmup=2)
@@ -461,6 +537,8 @@ def main():
         extra["barrier"] = barrier_latency(dt, torch)
     if args.hsdp:
         extra["hsdp"] = hsdp(dt, torch)
+    if args.overlap:
+        extra["overlap"] = overlap(dt, torch)
 
     cpu = None
     if not args.no_cpu_baseline:
