@@ -407,6 +407,50 @@ def overlap(dt, torch, reps: int = 12):
     return out
 
 
+def coalescing(dt, torch):
+    """The three ways of the c10d page (sec. 6.5) to reduce many small
+    gradients, P=8, 1000 bf16 tensors of 25 KB per rank (25 MB in all):
+      per_tensor   one dt_allreduce per tensor (1000 launches);
+      coalesced    dt_allreduce_coalesced: one launch over a table of the
+                   non-contiguous tensors (512 per launch);
+      bucket_copy  DDP bucket with a staging buffer: flatten -> AllReduce ->
+                   unflatten (three multi-tensor launch groups, 3x the bytes);
+      bucket_inplace  the same buckets reduced in place (no staging copies).
+    Timed eagerly from Python and by graph replay (GPU time)."""
+    import synth
+    n_t, n_el = 1000, 12800
+    grads = [[torch.randn(n_el, device="cuda").to(torch.bfloat16) for _ in range(n_t)] for _ in range(P)]
+    ws = [torch.empty(synth.BUCKET_BYTES, dtype=torch.uint8, device="cuda") for _ in range(P)]
+    alg = 2 * P * n_t * n_el * 2
+
+    def per_tensor():
+        for t in range(n_t):
+            dt.dt_allreduce([grads[r][t] for r in range(P)])
+
+    styles = {"per_tensor": per_tensor,
+              "coalesced": lambda: dt.dt_allreduce_coalesced(grads),
+              "bucket_copy": lambda: dt.dt_bucket_allreduce(grads, synth.BUCKET_BYTES, bucket_ws=ws),
+              "bucket_inplace": lambda: dt.dt_bucket_allreduce(grads, synth.BUCKET_BYTES)}
+    out = {"tensors": n_t, "bytes_per_tensor": n_el * 2, "ranks": P, "alg_bytes": alg}
+    for name, fn in styles.items():
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(3):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        eager_us = a.elapsed_time(b) * 1e3 / 3
+        g_us = graph_time_us(torch, fn, per_graph=1, replays=5)
+        out[name] = {"eager_us": round(eager_us, 1), "graph_us": round(g_us, 1),
+                     "hbm_GBps_graph": round(alg / (g_us * 1e-6) / 1e9, 1)}
+        print(json.dumps({"coalescing": {name: out[name]}}), flush=True)
+    del grads, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def probe(dt, torch, reps: int = 10):
     """Workload for hardware-counter passes: the bench kernels and a plain
     copy of known size (1 GiB read + 1 GiB written) to calibrate
@@ -438,6 +482,7 @@ def main():
     ap.add_argument("--probe", action="store_true", help="only run the kernels for a hardware-counter pass")
     ap.add_argument("--hsdp", action="store_true", help="also time the 32-layer gradient pipeline (103.6 GB)")
     ap.add_argument("--overlap", action="store_true", help="also run the GEMM / AllReduce overlap experiment")
+    ap.add_argument("--coalescing", action="store_true", help="also compare the ways to reduce many small tensors")
     ap.add_argument("--all", action="store_true",
                     help="also time every other workload: small AllReduce, uneven AllGather, AllToAll, the size "
                          "sweep, the barrier and the gradient pipeline")
@@ -528,7 +573,7 @@ def main():
 
     extra = {"kernels": kernels, "host_seconds_timed": round(t_host, 4), "kernel_source_hash": kernel_source_hash()}
     if args.all:
-        args.sweep = args.hsdp = args.overlap = True
+        args.sweep = args.hsdp = args.overlap = args.coalescing = True
         extra["rows"] = other_rows(dt, torch, steps=args.steps, warmup=args.warmup)
     if args.sweep:
         rows, fit = sweep(dt, torch, steps=max(5, args.steps // 2), warmup=2)
@@ -539,6 +584,8 @@ def main():
         extra["hsdp"] = hsdp(dt, torch)
     if args.overlap:
         extra["overlap"] = overlap(dt, torch)
+    if args.coalescing:
+        extra["coalescing"] = coalescing(dt, torch)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -300,6 +300,23 @@ def dt_bucket_allreduce(grads: Sequence[Sequence[torch.Tensor]], bucket_bytes: i
     return w if async_op else grads
 
 
+def dt_allreduce_coalesced(tensors: Sequence[Sequence[torch.Tensor]], op="sum", stream=None, async_op: bool = False,
+                           comm_stream=None):
+    """Coalesced in-place AllReduce of tensors[r][t] (rank r, tensor t): one
+    launch for up to min(512, 4096 // P) tensors, no flattening."""
+    p, nt = len(tensors), len(tensors[0])
+    numels = [g.numel() for g in tensors[0]]
+    for rank in tensors:
+        if len(rank) != nt or [g.numel() for g in rank] != numels:
+            raise ValueError("every rank must list tensors of the same sizes")
+    flat = [g for rank in tensors for g in rank]
+    code = _dtype_code(flat)
+    g_arr, n_arr = _ptr_array(flat), _size_array(numels)
+    w = _launch(lambda st: _L.dt_allreduce_coalesced(g_arr, n_arr, nt, p, code, _op_code(op), st), flat, async_op,
+                stream, comm_stream)
+    return w if async_op else tensors
+
+
 def dt_bucket_plan(numels: Sequence[int], elem_size: int, bucket_bytes: int = DEFAULT_BUCKET_BYTES):
     """Host-side bucket plan: (pieces, nbuckets); each piece is a dict."""
     n_arr = _size_array(numels)
@@ -406,6 +423,6 @@ def shard_views(fused: torch.Tensor, numels: Sequence[int], shard: int) -> List[
 __all__ = [
     "dt_allreduce", "dt_reduce_scatter", "dt_all_gather", "dt_all_to_all", "dt_bucket_allreduce", "dt_bucket_plan",
     "dt_all_gather_into_vec", "dt_broadcast", "dt_replicate_to_shard", "dt_all_to_all_dims",
-    "dt_barrier", "dt_barrier_exchange", "HSDPPipeline", "Work", "DtError", "shard_views", "side_stream",
+    "dt_allreduce_coalesced", "dt_barrier", "dt_barrier_exchange", "HSDPPipeline", "Work", "DtError", "shard_views", "side_stream",
     "status_string", "version",
 ]

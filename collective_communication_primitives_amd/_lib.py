@@ -15,6 +15,7 @@ LIBRARY = os.path.join(PKG, "libdtcoll.so")
 EXPORTS = (
     "dt_allreduce", "dt_reduce_scatter", "dt_all_gather", "dt_all_to_all", "dt_bucket_allreduce",
     "dt_all_gather_into_vec", "dt_broadcast", "dt_replicate_to_shard", "dt_all_to_all_dims",
+    "dt_allreduce_coalesced",
     "dt_barrier", "dt_barrier_exchange", "dt_bucket_plan", "dt_work_begin", "dt_work_end",
     "dt_work_wait", "dt_work_query", "dt_work_free", "dt_hsdp_create", "dt_hsdp_post_backward",
     "dt_hsdp_finish", "dt_hsdp_destroy", "dt_status_string", "dt_last_error", "dt_version",
@@ -28,7 +29,7 @@ class DtPiece(ctypes.Structure):
 
 def load(path: str = LIBRARY) -> ctypes.CDLL:
     if not os.path.exists(path):
-        raise ImportError(f"{path} is not built; run `python -m collective_communication_primitives_amd.build` "
+        raise ImportError(f"{path} is not built; run `python collective_communication_primitives_amd/build.py` "
                           "(there is no non-HIP fallback)")
     lib = ctypes.CDLL(path)
     vp, sz, i32, u64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint64
@@ -42,6 +43,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         "dt_replicate_to_shard": [vp, vp, i32, sz, i32, vp],
         "dt_all_to_all_dims": [vp, vp, i32, sz, sz, i32, i32, i32, vp],
         "dt_bucket_allreduce": [vp, vp, i32, i32, sz, vp, i32, i32, vp],
+        "dt_allreduce_coalesced": [vp, vp, i32, i32, i32, i32, vp],
         "dt_barrier": [vp, i32, ctypes.c_int32, ctypes.c_int32, vp, u64, i32, vp],
         "dt_barrier_exchange": [vp, vp, vp, sz, vp, i32, ctypes.c_int32, vp, u64, i32, vp],
         "dt_bucket_plan": [vp, i32, sz, sz, vp, sz, vp, vp],

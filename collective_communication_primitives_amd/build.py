@@ -1,6 +1,9 @@
 """Build libdtcoll.so (the HIP library behind include/dt.h) in-tree for gfx950.
 
-    python -m collective_communication_primitives_amd.build
+    python collective_communication_primitives_amd/build.py
+
+(Run by path: importing the package loads the library, which may be the
+stale build this script replaces.)
 
 Each source is compiled on its own (in parallel) into ``_build/`` at the
 repository root, then linked into ``libdtcoll.so`` next to this file.

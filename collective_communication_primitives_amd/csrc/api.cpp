@@ -6,6 +6,8 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -21,6 +23,7 @@ static_assert(sizeof(dt::ExchangeArgs) <= 4096, "kernel arguments must stay belo
 static_assert(sizeof(dt::SegReduceScatterArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::SegCopyArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::DimsArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+static_assert(sizeof(dt::CoalescedArgs) <= 48 * 1024, "large piece table must stay well below the 64 KB verified");
 static_assert(DT_MAX_RANKS == dt::kMaxRanksHost, "rank limit mismatch");
 static_assert(dt::kGatherTileBytes == uint64_t(dt::kGatherU) * 256 * 16, "gather tile = U vectors per thread");
 
@@ -216,6 +219,81 @@ dt_status copy_segments(const std::vector<const void*>& src, const std::vector<v
         if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "copy too large for one launch");
     }
     return flush();
+}
+
+// ------------------------------------------------------------ piece lists --
+// One contiguous part of a tensor on every rank: ptr[r] is rank r's start.
+struct PieceRef {
+    void* ptr[DT_MAX_RANKS];
+    size_t len;   // elements
+    size_t wpos;  // element position inside the bucket buffer (staging only)
+};
+
+void set_aligned(dt::PieceArgs& a, int k) { a.aligned |= 1u << k; }
+void set_aligned(dt::CoalescedArgs& a, int k) { a.aligned[k >> 5] |= 1u << (k & 31); }
+
+// Fill a piece table with pieces [first, first + n).
+template <typename Args>
+dt_status fill_pieces(Args& a, const std::vector<PieceRef>& pieces, size_t first, int n, int nranks, size_t es,
+                      void* const* ws) {
+    a.nranks = nranks;
+    a.npieces = n;
+    uint64_t tiles = 0;
+    for (int k = 0; k < n; k++) {
+        const PieceRef& p = pieces[first + k];
+        bool al = true;
+        for (int r = 0; r < nranks; r++) {
+            a.ptr[k * nranks + r] = p.ptr[r];
+            al = al && aligned16(p.ptr[r]);
+        }
+        if (ws) {
+            for (int r = 0; r < nranks; r++) al = al && aligned16(ws[r]);
+            al = al && (p.wpos * es) % 16 == 0;
+        }
+        if (al) set_aligned(a, k);
+        a.len[k] = p.len;
+        a.wpos[k] = p.wpos;
+        a.tile_start[k] = uint32_t(tiles);
+        tiles += (p.len * es + dt::kPieceTileVecs * 16 - 1) / (dt::kPieceTileVecs * 16);
+        if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "piece table too large for one launch");
+    }
+    a.tile_start[n] = uint32_t(tiles);
+    if (ws)
+        for (int r = 0; r < nranks; r++) a.ws[r] = ws[r];
+    return DT_OK;
+}
+
+// What to do with a piece list: fold in place, or copy to / from the bucket
+// buffers.
+enum PieceAction { kFold, kFlatten, kUnflatten };
+
+// Run `action` over all pieces in as few launches as the tables allow: the
+// small table (3.3 KiB of kernel arguments) when the list fits in one, the
+// large one (about 43 KiB) otherwise.
+dt_status run_pieces(const std::vector<PieceRef>& pieces, int nranks, dt_dtype dtype, dt_op op, void* const* ws,
+                     PieceAction action, hipStream_t stream) {
+    const size_t es = esize_of(dtype);
+    const int small_cap = std::min(dt::kMaxPieces, dt::kPiecePtrs / nranks);
+    const int large_cap = std::min(dt::kCoalMaxPieces, dt::kCoalPtrs / nranks);
+    dt_status st = DT_OK;
+    if (pieces.size() <= size_t(small_cap)) {
+        dt::PieceArgs a = {};
+        if ((st = fill_pieces(a, pieces, 0, int(pieces.size()), nranks, es, ws)) != DT_OK) return st;
+        if (action == kFold) return check_hip(dt::launch_reduce_pieces(a, dtype, op, stream), "piece reduce launch");
+        return check_hip(dt::launch_copy_pieces(a, int(es), action == kFlatten, stream), "piece copy launch");
+    }
+    std::unique_ptr<dt::CoalescedArgs> a(new dt::CoalescedArgs());  // too large for a thread's stack
+    for (size_t first = 0; first < pieces.size(); first += large_cap) {
+        std::memset(a.get(), 0, sizeof(dt::CoalescedArgs));
+        const int n = int(std::min<size_t>(large_cap, pieces.size() - first));
+        if ((st = fill_pieces(*a, pieces, first, n, nranks, es, ws)) != DT_OK) return st;
+        if (action == kFold)
+            st = check_hip(dt::launch_reduce_coalesced(*a, dtype, op, stream), "coalesced reduce launch");
+        else
+            st = check_hip(dt::launch_copy_coalesced(*a, int(es), action == kFlatten, stream), "coalesced copy launch");
+        if (st != DT_OK) return st;
+    }
+    return DT_OK;
 }
 
 // ---------------------------------------------------------- bucket plan --
@@ -577,62 +655,59 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
     const size_t es = esize_of(dtype);
     size_t nbuckets = 0;
     const std::vector<Piece> plan = plan_buckets(numels, ntensors, bucket_bytes / es, &nbuckets);
-    const int per_launch = std::min(dt::kMaxPieces, dt::kPiecePtrs / nranks);
-    bool ws_aligned = true;
-    if (bucket_ws)
-        for (int r = 0; r < nranks; r++) ws_aligned = ws_aligned && aligned16(bucket_ws[r]);
-
     size_t i = 0;
+    std::vector<PieceRef> pieces;
     while (i < plan.size()) {
         const int bucket = plan[i].bucket;
         size_t end = i;
         while (end < plan.size() && plan[end].bucket == bucket) end++;
         size_t bucket_len = 0;
-        for (size_t k = i; k < end; k++) bucket_len = std::max(bucket_len, plan[k].bucket_pos + plan[k].length);
-        // groups of pieces that fit one argument block
-        std::vector<dt::PieceArgs> groups;
-        for (size_t g0 = i; g0 < end; g0 += per_launch) {
-            dt::PieceArgs a = {};
-            a.nranks = nranks;
-            a.npieces = int(std::min<size_t>(per_launch, end - g0));
-            uint64_t tiles = 0;
-            for (int k = 0; k < a.npieces; k++) {
-                const Piece& p = plan[g0 + k];
-                bool al = true;
-                for (int r = 0; r < nranks; r++) {
-                    char* base = static_cast<char*>(grads[size_t(r) * ntensors + p.tensor]) + p.offset * es;
-                    a.ptr[k * nranks + r] = base;
-                    al = al && aligned16(base);
-                }
-                if (bucket_ws) al = al && ws_aligned && (p.bucket_pos * es) % 16 == 0;
-                if (al) a.aligned |= 1u << k;
-                a.len[k] = p.length;
-                a.wpos[k] = p.bucket_pos;
-                a.tile_start[k] = uint32_t(tiles);
-                tiles += (p.length * es + dt::kPieceTileVecs * 16 - 1) / (dt::kPieceTileVecs * 16);
-                if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "bucket too large for one launch");
-            }
-            a.tile_start[a.npieces] = uint32_t(tiles);
-            if (bucket_ws)
-                for (int r = 0; r < nranks; r++) a.ws[r] = bucket_ws[r];
-            groups.push_back(a);
+        pieces.clear();
+        for (size_t k = i; k < end; k++) {
+            const Piece& p = plan[k];
+            PieceRef ref = {};
+            for (int r = 0; r < nranks; r++)
+                ref.ptr[r] = static_cast<char*>(grads[size_t(r) * ntensors + p.tensor]) + p.offset * es;
+            ref.len = p.length;
+            ref.wpos = p.bucket_pos;
+            pieces.push_back(ref);
+            bucket_len = std::max(bucket_len, p.bucket_pos + p.length);
         }
-        if (bucket_ws) {
-            for (const auto& a : groups)
-                if ((st = check_hip(dt::launch_copy_pieces(a, int(es), 1, stream), "bucket flatten launch")) != DT_OK)
-                    return st;
+        if (bucket_ws) {  // the page's flatten -> AllReduce -> unflatten
+            if ((st = run_pieces(pieces, nranks, dtype, op, bucket_ws, kFlatten, stream)) != DT_OK) return st;
             if ((st = allreduce_impl(bucket_ws, bucket_ws, nranks, bucket_len, dtype, op, stream)) != DT_OK) return st;
-            for (const auto& a : groups)
-                if ((st = check_hip(dt::launch_copy_pieces(a, int(es), 0, stream), "bucket unflatten launch")) != DT_OK)
-                    return st;
-        } else {
-            for (const auto& a : groups)
-                if ((st = check_hip(dt::launch_reduce_pieces(a, dtype, op, stream), "bucket reduce launch")) != DT_OK)
-                    return st;
+            if ((st = run_pieces(pieces, nranks, dtype, op, bucket_ws, kUnflatten, stream)) != DT_OK) return st;
+        } else {  // the bucket reduced in place, straight out of the tensors
+            if ((st = run_pieces(pieces, nranks, dtype, op, nullptr, kFold, stream)) != DT_OK) return st;
         }
         i = end;
     }
     return DT_OK;
+}
+
+dt_status dt_allreduce_coalesced(void* const* tensors, const size_t* numels, int ntensors, int nranks, dt_dtype dtype,
+                                 dt_op op, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = check_ranks(nranks);
+    if (st != DT_OK) return st;
+    if (!valid_dtype(dtype) || !valid_op(op)) return fail(DT_ERR_ARG, "bad dtype %d or op %d", dtype, op);
+    if (ntensors < 0) return fail(DT_ERR_ARG, "ntensors=%d", ntensors);
+    if (ntensors == 0) return DT_OK;
+    if (numels == nullptr || tensors == nullptr) return fail(DT_ERR_ARG, "tensors/numels is NULL");
+    for (int r = 0; r < nranks; r++)
+        for (int t = 0; t < ntensors; t++)
+            if (numels[t] > 0 && tensors[size_t(r) * ntensors + t] == nullptr)
+                return fail(DT_ERR_ARG, "tensors[%d] (rank %d, tensor %d) is NULL", r * ntensors + t, r, t);
+    std::vector<PieceRef> pieces;
+    for (int t = 0; t < ntensors; t++) {
+        if (numels[t] == 0) continue;
+        PieceRef ref = {};
+        for (int r = 0; r < nranks; r++) ref.ptr[r] = tensors[size_t(r) * ntensors + t];
+        ref.len = numels[t];
+        pieces.push_back(ref);
+    }
+    if (pieces.empty()) return DT_OK;
+    return run_pieces(pieces, nranks, dtype, op, nullptr, kFold, stream);
 }
 
 dt_status dt_barrier(int32_t* const* windows, int nranks, int32_t first_generation, int32_t generations,

@@ -37,6 +37,23 @@ struct PieceArgs {
     int nranks;
 };
 
+// Coalesced AllReduce of many separate tensors in one launch (in place).
+// Piece k of rank r starts at ptr[k*nranks + r].  The table travels in the
+// kernel arguments (about 39 KiB; launches with up to 64 KB of arguments
+// were verified on gfx950 with ROCm 7.2).
+constexpr int kCoalPtrs = 4096;
+constexpr int kCoalMaxPieces = 512;
+struct CoalescedArgs {
+    void* ptr[kCoalPtrs];
+    void* ws[kMaxRanksHost];          // bucket buffers (flatten / unflatten only)
+    uint64_t len[kCoalMaxPieces];
+    uint64_t wpos[kCoalMaxPieces];    // element position inside the bucket buffer
+    uint32_t tile_start[kCoalMaxPieces + 1];
+    uint32_t aligned[kCoalMaxPieces / 32];
+    int npieces;
+    int nranks;
+};
+
 // Several independent ReduceScatters in one launch (one per segment, all of
 // nranks members): segment k's member j reads src[k*nranks + j] (nranks*m[k]
 // elements) and writes chunk j of the fold to dst[k*nranks + j] (m[k]).
@@ -137,6 +154,8 @@ constexpr uint64_t kPieceTileVecs = 512;     // bucket pieces: 512 x 16 B
 hipError_t launch_reduce_vec(const ReduceArgs& a, int dtype, int op, hipStream_t s);
 hipError_t launch_reduce_elems(const ReduceArgs& a, int dtype, int op, hipStream_t s);
 hipError_t launch_reduce_pieces(const PieceArgs& a, int dtype, int op, hipStream_t s);
+hipError_t launch_reduce_coalesced(const CoalescedArgs& a, int dtype, int op, hipStream_t s);
+hipError_t launch_copy_coalesced(const CoalescedArgs& a, int esize, int to_ws, hipStream_t s);
 hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, int op, hipStream_t s);
 // Output vectors per workgroup tile of the segmented ReduceScatter for P ranks.
 uint64_t seg_rs_tile_vecs(int nranks);

@@ -91,20 +91,41 @@ __global__ __launch_bounds__(kBlock) void k_reduce_elems(ReduceArgs a) {
 }
 
 // ------------------------------------------------------ bucket pieces ----
-// One launch reduces every piece of a bucket in place: piece k's rank r
-// part starts at a.ptr[k*P + r].  grid.x = tiles over all pieces.
-template <int DT, int OP, int PMAX, bool EXACT>
-__global__ __launch_bounds__(kBlock) void k_reduce_pieces(PieceArgs a) {
-    constexpr int V = Elems<DT>::value;
-    const uint32_t b = blockIdx.x;
+// Piece tables come in two sizes: PieceArgs (32 pieces, 3.3 KiB of kernel
+// arguments, for buckets of a few large tensors) and CoalescedArgs (512
+// pieces, for many small tensors).  The kernels are shared.
+__device__ __forceinline__ int find_piece(const PieceArgs& a, uint32_t b) {
     int k = 0;
     while (k + 1 < a.npieces && a.tile_start[k + 1] <= b) k++;
+    return k;
+}
+__device__ __forceinline__ int find_piece(const CoalescedArgs& a, uint32_t b) {
+    int lo = 0, hi = a.npieces;  // largest k with tile_start[k] <= b
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.tile_start[mid] <= b) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+__device__ __forceinline__ bool piece_aligned(const PieceArgs& a, int k) { return (a.aligned >> k) & 1u; }
+__device__ __forceinline__ bool piece_aligned(const CoalescedArgs& a, int k) {
+    return (a.aligned[k >> 5] >> (k & 31)) & 1u;
+}
+
+// One launch reduces every piece of its table in place: piece k's rank r
+// part starts at a.ptr[k*P + r].  grid.x = tiles over all pieces.
+template <typename Args, int DT, int OP, int PMAX, bool EXACT>
+__global__ __launch_bounds__(kBlock) void k_reduce_pieces(Args a) {
+    constexpr int V = Elems<DT>::value;
+    const uint32_t b = blockIdx.x;
+    const int k = find_piece(a, b);
     const int nr = EXACT ? PMAX : a.nranks;
     void* const* ptr = a.ptr + k * nr;
     const uint64_t len = a.len[k];
     const uint64_t e0 = uint64_t(b - a.tile_start[k]) * kPieceTileVecs * V;
     const uint64_t e1 = min(len, e0 + kPieceTileVecs * V);
-    if ((a.aligned >> k) & 1u) {
+    if (piece_aligned(a, k)) {
         constexpr int U = int(kPieceTileVecs / kBlock);
         const uint64_t v0 = e0 / V, v1 = e1 / V;
         u32x4 x[U][PMAX];
@@ -203,11 +224,11 @@ __global__ __launch_bounds__(kBlock) void k_reduce_scatter_segs(SegReduceScatter
 
 // Flatten (to_ws = 1) or unflatten (to_ws = 0) the pieces of one bucket for
 // rank blockIdx.y: a byte copy between the tensors and the bucket buffer.
-__global__ __launch_bounds__(kBlock) void k_copy_pieces(PieceArgs a, int esize, int to_ws) {
+template <typename Args>
+__global__ __launch_bounds__(kBlock) void k_copy_pieces(Args a, int esize, int to_ws) {
     const uint32_t b = blockIdx.x;
     const int r = blockIdx.y;
-    int k = 0;
-    while (k + 1 < a.npieces && a.tile_start[k + 1] <= b) k++;
+    const int k = find_piece(a, b);
     char* tensor = static_cast<char*>(a.ptr[k * a.nranks + r]);
     char* bucket = static_cast<char*>(a.ws[r]) + a.wpos[k] * uint64_t(esize);
     const char* from = to_ws ? tensor : bucket;
@@ -216,7 +237,7 @@ __global__ __launch_bounds__(kBlock) void k_copy_pieces(PieceArgs a, int esize, 
     const uint64_t tile_bytes = kPieceTileVecs * 16;
     const uint64_t b0 = uint64_t(b - a.tile_start[k]) * tile_bytes;
     const uint64_t b1 = min(bytes, b0 + tile_bytes);
-    if ((a.aligned >> k) & 1u) {
+    if (piece_aligned(a, k)) {
         const uint64_t v1 = b1 / 16;
         for (uint64_t v = b0 / 16 + threadIdx.x; v < v1; v += kBlock) store16(to + v * 16, load16(from + v * 16));
         const uint64_t t = v1 * 16 + threadIdx.x;
@@ -303,36 +324,54 @@ hipError_t reduce_elems_dt(const ReduceArgs& a, int op, hipStream_t s) {
     }
 }
 
-template <int DT, int OP, int PMAX>
-hipError_t reduce_pieces_p(const PieceArgs& a, hipStream_t s) {
+template <typename Args, int DT, int OP, int PMAX>
+hipError_t reduce_pieces_p(const Args& a, hipStream_t s) {
     const uint32_t tiles = a.tile_start[a.npieces];
     if (tiles == 0) return hipSuccess;
     if (a.nranks == PMAX)
-        k_reduce_pieces<DT, OP, PMAX, true><<<tiles, kBlock, 0, s>>>(a);
+        k_reduce_pieces<Args, DT, OP, PMAX, true><<<tiles, kBlock, 0, s>>>(a);
     else
-        k_reduce_pieces<DT, OP, PMAX, false><<<tiles, kBlock, 0, s>>>(a);
+        k_reduce_pieces<Args, DT, OP, PMAX, false><<<tiles, kBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 
-template <int DT, int OP>
-hipError_t reduce_pieces_op(const PieceArgs& a, hipStream_t s) {
+template <typename Args, int DT, int OP>
+hipError_t reduce_pieces_op(const Args& a, hipStream_t s) {
     switch (pmax_of(a.nranks)) {
-        case 1: return reduce_pieces_p<DT, OP, 1>(a, s);
-        case 2: return reduce_pieces_p<DT, OP, 2>(a, s);
-        case 4: return reduce_pieces_p<DT, OP, 4>(a, s);
-        case 8: return reduce_pieces_p<DT, OP, 8>(a, s);
-        default: return reduce_pieces_p<DT, OP, 16>(a, s);
+        case 1: return reduce_pieces_p<Args, DT, OP, 1>(a, s);
+        case 2: return reduce_pieces_p<Args, DT, OP, 2>(a, s);
+        case 4: return reduce_pieces_p<Args, DT, OP, 4>(a, s);
+        case 8: return reduce_pieces_p<Args, DT, OP, 8>(a, s);
+        default: return reduce_pieces_p<Args, DT, OP, 16>(a, s);
     }
 }
 
-template <int DT>
-hipError_t reduce_pieces_dt(const PieceArgs& a, int op, hipStream_t s) {
+template <typename Args, int DT>
+hipError_t reduce_pieces_dt(const Args& a, int op, hipStream_t s) {
     switch (op) {
-        case kSum: return reduce_pieces_op<DT, kSum>(a, s);
-        case kMax: return reduce_pieces_op<DT, kMax>(a, s);
-        case kMin: return reduce_pieces_op<DT, kMin>(a, s);
-        default: return reduce_pieces_op<DT, kAvg>(a, s);
+        case kSum: return reduce_pieces_op<Args, DT, kSum>(a, s);
+        case kMax: return reduce_pieces_op<Args, DT, kMax>(a, s);
+        case kMin: return reduce_pieces_op<Args, DT, kMin>(a, s);
+        default: return reduce_pieces_op<Args, DT, kAvg>(a, s);
     }
+}
+
+template <typename Args>
+hipError_t reduce_pieces_any(const Args& a, int dtype, int op, hipStream_t s) {
+    switch (dtype) {
+        case kF32: return reduce_pieces_dt<Args, kF32>(a, op, s);
+        case kBF16: return reduce_pieces_dt<Args, kBF16>(a, op, s);
+        default: return reduce_pieces_dt<Args, kI32>(a, op, s);
+    }
+}
+
+template <typename Args>
+hipError_t copy_pieces_any(const Args& a, int esize, int to_ws, hipStream_t s) {
+    const uint32_t tiles = a.tile_start[a.npieces];
+    if (tiles == 0) return hipSuccess;
+    dim3 grid(tiles, unsigned(a.nranks));
+    k_copy_pieces<Args><<<grid, kBlock, 0, s>>>(a, esize, to_ws);
+    return hipGetLastError();
 }
 
 template <int DT, int OP, int PMAX>
@@ -405,19 +444,19 @@ hipError_t launch_reduce_elems(const ReduceArgs& a, int dtype, int op, hipStream
 }
 
 hipError_t launch_reduce_pieces(const PieceArgs& a, int dtype, int op, hipStream_t s) {
-    switch (dtype) {
-        case kF32: return reduce_pieces_dt<kF32>(a, op, s);
-        case kBF16: return reduce_pieces_dt<kBF16>(a, op, s);
-        default: return reduce_pieces_dt<kI32>(a, op, s);
-    }
+    return reduce_pieces_any(a, dtype, op, s);
+}
+
+hipError_t launch_reduce_coalesced(const CoalescedArgs& a, int dtype, int op, hipStream_t s) {
+    return reduce_pieces_any(a, dtype, op, s);
 }
 
 hipError_t launch_copy_pieces(const PieceArgs& a, int esize, int to_ws, hipStream_t s) {
-    const uint32_t tiles = a.tile_start[a.npieces];
-    if (tiles == 0) return hipSuccess;
-    dim3 grid(tiles, unsigned(a.nranks));
-    k_copy_pieces<<<grid, kBlock, 0, s>>>(a, esize, to_ws);
-    return hipGetLastError();
+    return copy_pieces_any(a, esize, to_ws, s);
+}
+
+hipError_t launch_copy_coalesced(const CoalescedArgs& a, int esize, int to_ws, hipStream_t s) {
+    return copy_pieces_any(a, esize, to_ws, s);
 }
 
 }  // namespace dt

@@ -149,6 +149,16 @@ typedef enum {
     DT_BARRIER_SPREAD = 1  /* one workgroup per rank on different CUs, cooperative launch */
 } dt_barrier_layout;
 
+/* Coalesced AllReduce, in place: many separate tensors reduced in one
+ * launch, the all_reduce_coalesced / _coalescing_manager form of the c10d
+ * page sec. 6.5 (several non-contiguous tensors, one launch and one event,
+ * no flattening).  tensors[r*ntensors + t] is rank r's tensor t with
+ * numels[t] elements; every tensor gets the same bits as dt_allreduce on it.
+ * Up to 4096/nranks tensors (at most 512) per launch; more take several
+ * launches.  Empty tensors may pass NULL. */
+dt_status dt_allreduce_coalesced(void* const* tensors, const size_t* numels, int ntensors, int nranks, dt_dtype dtype,
+                                 dt_op op, hipStream_t stream);
+
 /* Signal-window barrier.  pypto page "Barrier：仅信号（Signals Only）",
  * "The idea" and "Walkthrough": windows[p] is rank p's window of nranks int32
  * cells in device memory (zeroed once by the caller before its first use).

@@ -192,3 +192,23 @@ def test_hsdp_full_size(dt, orc):
     for l in range(nl):
         for j in range(sh):
             assert torch.equal(fused[l][j].view(torch.int16), fused[l][sh + j].view(torch.int16)), (l, j)
+
+
+# -------------------------------------------------------------- coalesced --
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("op", ["sum", "avg"])
+@pytest.mark.parametrize("p,nt", [(1, 3), (2, 600), (8, 513), (16, 300)])
+def test_allreduce_coalesced(dt, orc, dtype, op, p, nt):
+    """Many separate tensors in one (or a few) launches: each equals the
+    oracle's AllReduce of that tensor."""
+    rng = np.random.default_rng(p * 1000 + nt)
+    sizes = [int(v) for v in rng.integers(0, 700, nt)]
+    note(f"coalesced allreduce {dtype} {op} P={p} tensors={nt}")
+    grads = make_grads(p, sizes, dtype, seed=nt)
+    host = [[to_np(g) for g in rank] for rank in grads]
+    dt.dt_allreduce_coalesced(grads, op=op)
+    torch.cuda.synchronize()
+    for t in range(nt):
+        want = orc.allreduce([host[r][t] for r in range(p)], op)
+        for r in range(p):
+            compare(to_np(grads[r][t]), want[r], f"tensor {t} rank {r}")
