@@ -62,6 +62,65 @@ def measured_traffic(kernel: str):
     return float(m_bytes.group(1))
 
 
+def pct(xs, q: float) -> float:
+    """q-quantile (0..1) of a sample by linear interpolation."""
+    xs = sorted(xs)
+    i = q * (len(xs) - 1)
+    lo = int(i)
+    hi = min(lo + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (i - lo)
+
+
+def kernel_stats(us, alg_bytes, s_bytes, bus_factor):
+    """Per-launch durations (us) -> mean / median / p10 / p90 and rates."""
+    mean = statistics.mean(us)
+    return {"mean_us": round(mean, 3), "median_us": round(statistics.median(us), 3),
+            "p10_us": round(pct(us, 0.1), 3), "p90_us": round(pct(us, 0.9), 3), "alg_bytes": int(alg_bytes),
+            "hbm_GBps": round(alg_bytes / (mean * 1e-6) / 1e9, 1),
+            "busbw_GBps": round(s_bytes / (mean * 1e-6) / 1e9 * bus_factor, 1)}
+
+
+def copy_ceiling(torch, stream, steps: int = 10) -> dict:
+    """Context for the roofline: torch's own device-to-device copy of 1 GiB
+    (read 1 GiB + write 1 GiB), timed per launch like the collectives."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    evs = time_launches(lambda: dst.copy_(src), steps, stream)
+    torch.cuda.synchronize()
+    us = statistics.mean(a.elapsed_time(b) for a, b in evs) * 1e3
+    return {"bytes": 2 << 30, "mean_us": round(us, 3), "hbm_GBps": round((2 << 30) / (us * 1e-6) / 1e9, 1)}
+
+
+def int32_max_step(dt, torch, steps: int, warmup: int, stream) -> dict:
+    """The int32 variant of the same workload: P=8 [8192, 8192] int32 over
+    the whole int32 range, max op: ReduceScatter, AllGather and the one-shot
+    AllReduce, each timed per launch."""
+    import synth
+    n = SHAPE[0] * SHAPE[1]
+    xs = synth.full_range_int_ranks(P, n, seed=0, device="cuda")
+    shards = [torch.empty(n // P, dtype=torch.int32, device="cuda") for _ in range(P)]
+    full = [torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(P)]
+    s_bytes = n * 4
+    for _ in range(warmup):
+        dt.dt_reduce_scatter(xs, shards, op="max")
+        dt.dt_all_gather(shards, full)
+    ev_rs, ev_ag = [], []
+    for _ in range(steps):
+        ev_rs += time_launches(lambda: dt.dt_reduce_scatter(xs, shards, op="max"), 1, stream)
+        ev_ag += time_launches(lambda: dt.dt_all_gather(shards, full), 1, stream)
+    ev_ar = time_launches(lambda: dt.dt_allreduce(xs, full, op="max"), steps, stream)
+    torch.cuda.synchronize()
+    us = lambda evs: [a.elapsed_time(b) * 1e3 for a, b in evs]  # noqa: E731
+    out = {"reduce_scatter": kernel_stats(us(ev_rs), (P + 1) * s_bytes, s_bytes, (P - 1) / P),
+           "all_gather": kernel_stats(us(ev_ag), (1 + P) * s_bytes, s_bytes, (P - 1) / P),
+           "allreduce_oneshot": kernel_stats(us(ev_ar), 2 * P * s_bytes, s_bytes, 2 * (P - 1) / P)}
+    step_us = out["reduce_scatter"]["mean_us"] + out["all_gather"]["mean_us"]
+    out["step_busbw_GBps"] = round(s_bytes / (step_us * 1e-6) / 1e9 * 2 * (P - 1) / P, 1)
+    return out
+
+
 def time_launches(fn, steps, stream):
     """Run fn() `steps` times with start/end events on `stream` around each."""
     import torch
@@ -542,14 +601,8 @@ def main():
     rs_bytes = (P + 1) * s_bytes          # read P inputs, write one shard per rank
     ag_bytes = (1 + P) * s_bytes          # read P shards, write P full outputs
     kernels = {
-        "reduce_scatter": {"mean_us": round(statistics.mean(rs_us), 3), "median_us": round(statistics.median(rs_us), 3),
-                           "alg_bytes": rs_bytes,
-                           "hbm_GBps": round(rs_bytes / (statistics.mean(rs_us) * 1e-6) / 1e9, 1),
-                           "busbw_GBps": round(s_bytes / (statistics.mean(rs_us) * 1e-6) / 1e9 * (P - 1) / P, 1)},
-        "all_gather": {"mean_us": round(statistics.mean(ag_us), 3), "median_us": round(statistics.median(ag_us), 3),
-                       "alg_bytes": ag_bytes,
-                       "hbm_GBps": round(ag_bytes / (statistics.mean(ag_us) * 1e-6) / 1e9, 1),
-                       "busbw_GBps": round(s_bytes / (statistics.mean(ag_us) * 1e-6) / 1e9 * (P - 1) / P, 1)},
+        "reduce_scatter": kernel_stats(rs_us, rs_bytes, s_bytes, (P - 1) / P),
+        "all_gather": kernel_stats(ag_us, ag_bytes, s_bytes, (P - 1) / P),
     }
     dom_name = max(kernels, key=lambda k: kernels[k]["mean_us"])
     dom = kernels[dom_name]
@@ -565,13 +618,14 @@ def main():
         dt.dt_allreduce(xs, ar_out)
     ev_ar = time_launches(lambda: dt.dt_allreduce(xs, ar_out), args.steps, stream)
     torch.cuda.synchronize()
-    ar_us = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in ev_ar)
-    kernels["allreduce_oneshot"] = {"mean_us": round(ar_us, 3), "alg_bytes": 2 * P * s_bytes,
-                                    "hbm_GBps": round(2 * P * s_bytes / (ar_us * 1e-6) / 1e9, 1),
-                                    "busbw_GBps": round(s_bytes / (ar_us * 1e-6) / 1e9 * 2 * (P - 1) / P, 1)}
+    kernels["allreduce_oneshot"] = kernel_stats([a.elapsed_time(b) * 1e3 for a, b in ev_ar], 2 * P * s_bytes,
+                                                 s_bytes, 2 * (P - 1) / P)
     del ar_out
 
     extra = {"kernels": kernels, "host_seconds_timed": round(t_host, 4), "kernel_source_hash": kernel_source_hash()}
+    extra["int32_max"] = int32_max_step(dt, torch, args.steps, args.warmup, stream)
+    extra["copy_ceiling"] = copy_ceiling(torch, stream)
+    torch.cuda.empty_cache()
     if args.all:
         args.sweep = args.hsdp = args.overlap = args.coalescing = True
         extra["rows"] = other_rows(dt, torch, steps=args.steps, warmup=args.warmup)

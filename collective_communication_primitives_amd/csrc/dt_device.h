@@ -25,9 +25,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Every byte is touched once per launch.  Whether a side carries the
 // non-temporal hint is chosen per kernel from measurements on the MI355X
 // (1.1 GiB working sets, beyond the Infinity Cache): with reads dominating
-// (P-to-1 fold), non-temporal loads and plain stores are fastest; with writes
-// dominating (1-to-P fan-out), plain loads and non-temporal stores; for the
-// balanced P-to-P fold and for 1-to-1 copies, both non-temporal.
+// (P-to-1 fold), non-temporal loads and device-scope stores are fastest; with
+// writes dominating (1-to-P fan-out), plain loads and non-temporal
+// device-scope stores; for the balanced P-to-P fold and for 1-to-1 copies,
+// both non-temporal.
 __device__ __forceinline__ u32x4 load16(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -43,6 +44,32 @@ template <bool NT>
 __device__ __forceinline__ void store16_h(void* p, u32x4 v) {
     if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
     else *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Buffer-instruction access.  A workgroup describes each contiguous range it
+// touches with a buffer resource (base address in scalar registers, byte
+// range) and addresses lanes with 32-bit offsets.  The hardware checks every
+// access against the range: a 16-byte load at or past the end returns zeros
+// and a store there is dropped, so a ragged last tile needs no per-lane
+// branch.  The last operand selects the cache policy of the access:
+// bit 1 = non-temporal, bit 4 = device scope (the store is written through
+// the XCD's L2 towards memory instead of staying there dirty until the
+// kernel ends).  Ranges are at most a few tiles, far below the 4 GiB limit.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kPolNT = 2;
+constexpr int kPolDevice = 16;
+constexpr int kRsrcFlags = 0x00020000;  // word 3: 32-bit data format, raw (stride 0) addressing
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcFlags);
+}
+template <int POL>
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, POL);
+}
+template <int POL>
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, POL);
 }
 
 // ------------------------------------------------------------------- bf16 --

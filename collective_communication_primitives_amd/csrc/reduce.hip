@@ -16,18 +16,15 @@
 
 namespace dt {
 
-// ------------------------------------------------------------- one range --
-// grid.x covers a.count vectors in tiles of kBlock*U; grid.y = output chunk
-// (ReduceScatter) or 1 (AllReduce).
+// ------------------------------------------------------------- AllReduce --
+// grid.x covers a.count vectors in tiles of kBlock*U.
 //
 // Issue order: all of rank 0's vectors, then rank 1's, ...; stores output by
 // output.  Each wave then sends U KiB-long runs to one buffer before moving to
 // the next, which the MI355X's HBM serves faster than interleaving the P
 // buffers vector by vector (measured: +3% for the P-to-P AllReduce pattern).
-template <int DT, int OP, int PMAX, bool EXACT, int U, bool RS>
+template <int DT, int OP, int PMAX, bool EXACT, int U>
 __global__ __launch_bounds__(kBlock) void k_reduce_vec(ReduceArgs a) {
-    const uint64_t chunk = RS ? blockIdx.y : 0;
-    const uint64_t in_off = chunk * a.count * 16;  // bytes into every rank's input
     const uint64_t base = uint64_t(blockIdx.x) * (kBlock * U) + threadIdx.x;
     const int nr = EXACT ? PMAX : a.nranks;
     u32x4 x[U][PMAX];
@@ -37,31 +34,54 @@ __global__ __launch_bounds__(kBlock) void k_reduce_vec(ReduceArgs a) {
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const uint64_t v = base + uint64_t(u) * kBlock;
-                if (v < a.count) x[u][r] = load16(static_cast<const char*>(a.src[r]) + in_off + v * 16);
+                if (v < a.count) x[u][r] = load16(static_cast<const char*>(a.src[r]) + v * 16);
             }
         }
     }
     u32x4 y[U];
 #pragma unroll
     for (int u = 0; u < U; u++) y[u] = fold_vec<DT, OP, PMAX>(x[u], nr);
-    if constexpr (RS) {
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const uint64_t v = base + uint64_t(u) * kBlock;
-            if (v < a.count) store16_h<false>(static_cast<char*>(a.dst[chunk]) + v * 16, y[u]);  // reads dominate P:1
-        }
-    } else {
+    for (int q = 0; q < PMAX; q++) {
+        if (q < nr) {
 #pragma unroll
-        for (int q = 0; q < PMAX; q++) {
-            if (q < nr) {
-#pragma unroll
-                for (int u = 0; u < U; u++) {
-                    const uint64_t v = base + uint64_t(u) * kBlock;
-                    if (v < a.count) store16(static_cast<char*>(a.dst[q]) + v * 16, y[u]);
-                }
+            for (int u = 0; u < U; u++) {
+                const uint64_t v = base + uint64_t(u) * kBlock;
+                if (v < a.count) store16(static_cast<char*>(a.dst[q]) + v * 16, y[u]);
             }
         }
     }
+}
+
+// --------------------------------------------------------- ReduceScatter --
+// grid.x covers a.count vectors of one chunk in tiles of kBlock*U; grid.y =
+// output chunk.  Buffer instructions: one resource per rank for the tile's
+// range (the same lane offsets serve all P ranks), non-temporal loads and
+// device-scope stores; the resource range cuts off the last tile.  Measured
+// against the same kernel with 64-bit global addressing: 2-3% faster for
+// P=8 bf16 at 16 MiB per chunk.
+template <int DT, int OP, int PMAX, bool EXACT, int U>
+__global__ __launch_bounds__(kBlock) void k_reduce_scatter_vec(ReduceArgs a) {
+    constexpr uint64_t kTileVecs = uint64_t(kBlock) * U;
+    const uint64_t chunk = blockIdx.y;
+    const uint64_t t0 = uint64_t(blockIdx.x) * kTileVecs;       // < a.count by the grid
+    const uint64_t left = a.count - t0;
+    const uint32_t bytes = uint32_t((left < kTileVecs ? left : kTileVecs) * 16);
+    const uint64_t in_off = (chunk * a.count + t0) * 16;       // bytes into every rank's input
+    const uint32_t lane = threadIdx.x * 16;
+    const int nr = EXACT ? PMAX : a.nranks;
+    u32x4 x[U][PMAX];
+#pragma unroll
+    for (int r = 0; r < PMAX; r++) {
+        if (r < nr) {
+            const rsrc_t in = make_rsrc(static_cast<const char*>(a.src[r]) + in_off, bytes);
+#pragma unroll
+            for (int u = 0; u < U; u++) x[u][r] = bload16<kPolNT>(in, lane + u * (kBlock * 16));
+        }
+    }
+    const rsrc_t out = make_rsrc(static_cast<char*>(a.dst[chunk]) + t0 * 16, bytes);
+#pragma unroll
+    for (int u = 0; u < U; u++) bstore16<kPolDevice>(out, lane + u * (kBlock * 16), fold_vec<DT, OP, PMAX>(x[u], nr));
 }
 
 // Element-wise path for ragged tails and unaligned buffers.  Elements
@@ -194,25 +214,25 @@ __global__ __launch_bounds__(kBlock) void k_reduce_scatter_segs(SegReduceScatter
     const void* const* src = a.src + k * nr;
     void* dst = a.dst[k * nr + j];
     if ((a.aligned >> k) & 1u) {
+        constexpr uint64_t kTileVecs = uint64_t(kBlock) * U;
         const uint64_t mv = m / V;
-        const uint64_t in_off = uint64_t(j) * mv * 16;
-        const uint64_t base = uint64_t(tt) * (kBlock * U) + threadIdx.x;
+        const uint64_t t0 = uint64_t(tt) * kTileVecs;            // < mv by the tile count
+        const uint64_t left = mv - t0;
+        const uint32_t bytes = uint32_t((left < kTileVecs ? left : kTileVecs) * 16);
+        const uint64_t in_off = (uint64_t(j) * mv + t0) * 16;
+        const uint32_t lane = threadIdx.x * 16;
         u32x4 x[U][PMAX];
 #pragma unroll
         for (int r = 0; r < PMAX; r++) {
             if (r < nr) {
+                const rsrc_t in = make_rsrc(static_cast<const char*>(src[r]) + in_off, bytes);
 #pragma unroll
-                for (int u = 0; u < U; u++) {
-                    const uint64_t v = base + uint64_t(u) * kBlock;
-                    if (v < mv) x[u][r] = load16(static_cast<const char*>(src[r]) + in_off + v * 16);
-                }
+                for (int u = 0; u < U; u++) x[u][r] = bload16<kPolNT>(in, lane + u * (kBlock * 16));
             }
         }
+        const rsrc_t out = make_rsrc(static_cast<char*>(dst) + t0 * 16, bytes);
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const uint64_t v = base + uint64_t(u) * kBlock;
-            if (v < mv) store16_h<false>(static_cast<char*>(dst) + v * 16, fold_vec<DT, OP, PMAX>(x[u], nr));
-        }
+        for (int u = 0; u < U; u++) bstore16<kPolDevice>(out, lane + u * (kBlock * 16), fold_vec<DT, OP, PMAX>(x[u], nr));
     } else {
         const uint64_t per_tile = uint64_t(kBlock) * U * V;
         const uint64_t e0 = uint64_t(tt) * per_tile;
@@ -267,18 +287,18 @@ hipError_t reduce_vec_p(const ReduceArgs& a, hipStream_t s) {
     const uint64_t blocks = (a.count + per_block - 1) / per_block;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    dim3 grid(unsigned(blocks), a.rs ? unsigned(a.nranks) : 1u);
     const bool exact = a.nranks == PMAX;
     if (a.rs) {
+        const dim3 grid(unsigned(blocks), unsigned(a.nranks));
         if (exact)
-            k_reduce_vec<DT, OP, PMAX, true, URS, true><<<grid, kBlock, 0, s>>>(a);
+            k_reduce_scatter_vec<DT, OP, PMAX, true, URS><<<grid, kBlock, 0, s>>>(a);
         else
-            k_reduce_vec<DT, OP, PMAX, false, URS, true><<<grid, kBlock, 0, s>>>(a);
+            k_reduce_scatter_vec<DT, OP, PMAX, false, URS><<<grid, kBlock, 0, s>>>(a);
     } else {
         if (exact)
-            k_reduce_vec<DT, OP, PMAX, true, UAR, false><<<grid, kBlock, 0, s>>>(a);
+            k_reduce_vec<DT, OP, PMAX, true, UAR><<<unsigned(blocks), kBlock, 0, s>>>(a);
         else
-            k_reduce_vec<DT, OP, PMAX, false, UAR, false><<<grid, kBlock, 0, s>>>(a);
+            k_reduce_vec<DT, OP, PMAX, false, UAR><<<unsigned(blocks), kBlock, 0, s>>>(a);
     }
     return hipGetLastError();
 }
