@@ -398,8 +398,15 @@ def overlap(dt, torch, reps: int = 12):
     bucket AllReduce of P=8 ranks on a side stream.  Events on both streams
     put both kernels on one clock; medians over `reps` runs.
       overlap = (t_gemm + t_ar - t_both) / min(t_gemm, t_ar)
-    (1 = the AllReduce fully hidden, 0 = serialized).  Two issue orders, and
-    one "killer" (wait() before the GEMM, which serializes by construction)."""
+    with t_gemm and t_ar each kernel's own duration when it runs alone and
+    t_both the span from the first kernel's start to the last one's end
+    (1 = the AllReduce fully hidden, 0 = serialized, below 0 = a gap).  Two issue orders, and
+    the page's overlap "killers" placed between issuing the AllReduce and the
+    GEMM (sec. 6.3): wait() too early, .item() (a device-to-host read on the
+    compute stream), torch.cuda.synchronize(), the caching allocator
+    returning memory (empty_cache frees a cached block: an implicit device
+    synchronization, the page's cudaFree case) and the AllReduce on the
+    compute stream itself (async_op=False)."""
     import synth
     xs = synth.uniform_ranks(P, synth.BUCKET_BYTES // 4, seed=0, device="cuda")
     ys = [torch.empty_like(x) for x in xs]
@@ -411,15 +418,19 @@ def overlap(dt, torch, reps: int = 12):
         return torch.cuda.Event(enable_timing=True)
 
     def run(order):
+        if order == "frag":
+            spare = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+            del spare  # back in the caching allocator's free list
         torch.cuda.synchronize()
         t0, s0, s1, g0, g1, t1 = ev(), ev(), ev(), ev(), ev(), ev()
         t0.record(comp)
 
-        def ar():
-            side.wait_stream(comp)
-            s0.record(side)
-            dt.dt_allreduce(xs, ys, stream=side)
-            s1.record(side)
+        def ar(stream=side):
+            if stream is not comp:
+                stream.wait_stream(comp)
+            s0.record(stream)
+            dt.dt_allreduce(xs, ys, stream=stream)
+            s1.record(stream)
 
         def gemm():
             g0.record(comp)
@@ -440,6 +451,21 @@ def overlap(dt, torch, reps: int = 12):
             ar()
             comp.wait_stream(side)
             gemm()
+        elif order == "item":
+            ar()
+            xs[0][0].item()
+            gemm()
+        elif order == "sync":
+            ar()
+            torch.cuda.synchronize()
+            gemm()
+        elif order == "frag":
+            ar()
+            torch.cuda.empty_cache()  # releases the block freed below: hipFree, a device-wide wait
+            gemm()
+        elif order == "same_stream":
+            ar(stream=comp)
+            gemm()
         comp.wait_stream(side)
         t1.record(comp)
         torch.cuda.synchronize()
@@ -448,9 +474,13 @@ def overlap(dt, torch, reps: int = 12):
             out["ar_start_ms"], out["ar_end_ms"] = t0.elapsed_time(s0), t0.elapsed_time(s1)
         if order != "ar":
             out["gemm_start_ms"], out["gemm_end_ms"] = t0.elapsed_time(g0), t0.elapsed_time(g1)
+        starts = [v for k, v in out.items() if k.endswith("_start_ms")]
+        ends = [v for k, v in out.items() if k.endswith("_end_ms")]
+        out["span_ms"] = max(ends) - min(starts)
         return out
 
-    orders = ("gemm", "ar", "ar_first", "gemm_first", "wait_too_early")
+    killers = ("wait_too_early", "item", "sync", "frag", "same_stream")
+    orders = ("gemm", "ar", "ar_first", "gemm_first") + killers
     samples = {o: [] for o in orders}
     for it in range(reps + 2):
         for o in orders:  # interleaved, so clock drift hits every mode alike
@@ -458,10 +488,10 @@ def overlap(dt, torch, reps: int = 12):
             if it >= 2:
                 samples[o].append(r)
     med = {o: {k: round(statistics.median(r[k] for r in samples[o]), 4) for k in samples[o][0]} for o in orders}
-    t_g, t_a = med["gemm"]["total_ms"], med["ar"]["total_ms"]
+    t_g, t_a = med["gemm"]["span_ms"], med["ar"]["span_ms"]
     out = {"gemm_ms": t_g, "allreduce_ms": t_a, "gemm_tflops": round(2 * 8192 ** 3 / (t_g * 1e-3) / 1e12, 1)}
-    for o in ("ar_first", "gemm_first", "wait_too_early"):
-        out[o] = dict(med[o], overlap=round((t_g + t_a - med[o]["total_ms"]) / min(t_g, t_a), 3))
+    for o in ("ar_first", "gemm_first") + killers:
+        out[o] = dict(med[o], overlap=round((t_g + t_a - med[o]["span_ms"]) / min(t_g, t_a), 3))
     print(json.dumps({"overlap": out}), flush=True)
     return out
 
