@@ -243,7 +243,10 @@ dt_status dt_work_free(dt_work* work);
  * fused[r] holds sum(numels)/shard elements and must stay valid until the
  * consumer has waited.  numels[t] must be divisible by shard.  The handle
  * owns its events and keeps a host copy of the previous layer's fused
- * pointers and total size until it queues that layer's AllReduce. */
+ * pointers and total size until it queues that layer's AllReduce.
+ * rs_stream and ar_stream may be the same stream: the phases then run back
+ * to back in the order above, which on one device (both phases drawing on
+ * the same HBM) is the faster schedule. */
 typedef struct dt_hsdp dt_hsdp;
 dt_status dt_hsdp_create(int replicate, int shard, size_t bucket_bytes, dt_dtype dtype, dt_op op,
                          hipStream_t rs_stream, hipStream_t ar_stream, dt_hsdp** handle);

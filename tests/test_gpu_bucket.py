@@ -111,11 +111,15 @@ def test_bucket_one_layer_full_size(dt, orc):
 
 
 # ------------------------------------------------------------------ HSDP --
-def run_pipeline(dt, layers, rep, sh, bucket, shapes):
+def run_pipeline(dt, layers, rep, sh, bucket, shapes, one_stream=False):
     """Backward order: last layer first.  Returns fused buffers per layer."""
     p = rep * sh
     numels = [int(np.prod(s)) for s in shapes]
-    pipe = dt.HSDPPipeline(rep, sh, bucket_bytes=bucket)
+    if one_stream:
+        pipe = dt.HSDPPipeline(rep, sh, bucket_bytes=bucket)  # the default: one side stream for both phases
+    else:
+        pipe = dt.HSDPPipeline(rep, sh, bucket_bytes=bucket, rs_stream=torch.cuda.Stream(),
+                               ar_stream=torch.cuda.Stream())
     fused = {}
     for layer in reversed(range(len(layers))):
         fused[layer] = [torch.empty(sum(numels) // sh, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
@@ -124,15 +128,16 @@ def run_pipeline(dt, layers, rep, sh, bucket, shapes):
     return fused, numels
 
 
+@pytest.mark.parametrize("one_stream", [False, True])
 @pytest.mark.parametrize("rep,sh", [(2, 4), (8, 1), (1, 8), (2, 2), (4, 2)])
-def test_hsdp_pipeline_small(dt, orc, rep, sh):
+def test_hsdp_pipeline_small(dt, orc, rep, sh, one_stream):
     p = rep * sh
     shapes = [(16, 24), (40, 8), (8,), (24, 16)]
     nl = 5
-    note(f"hsdp pipeline small R={rep} S={sh} layers={nl}")
+    note(f"hsdp pipeline small R={rep} S={sh} layers={nl} one_stream={one_stream}")
     layers = [[[synth.normal_ranks(1, s, seed=(l * 64 + r) * 16 + t, device="cuda")[0] for t, s in enumerate(shapes)]
                for r in range(p)] for l in range(nl)]
-    fused, numels = run_pipeline(dt, layers, rep, sh, bucket=96, shapes=shapes)
+    fused, numels = run_pipeline(dt, layers, rep, sh, bucket=96, shapes=shapes, one_stream=one_stream)
     torch.cuda.synchronize()
     for l in range(nl):
         host = [[to_np(g) for g in rank] for rank in layers[l]]
