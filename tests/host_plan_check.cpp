@@ -1,0 +1,605 @@
+// Host-side check of the library's planning code under AddressSanitizer and
+// UndefinedBehaviorSanitizer (CPU only, no GPU, no HIP runtime).
+//
+// api.cpp (the C ABI: validation, offset and tile tables, bucket plan, work
+// handles, HSDP schedule) is compiled for the host and linked against this
+// file, which stands in for two things:
+//   * the kernel launchers of dt_launch.h: instead of launching, each one
+//     walks the grid it was given the way its kernel indexes memory and
+//     checks that every byte range a workgroup would read or write lies
+//     inside a buffer the test registered (reads: inputs or in-place
+//     buffers; writes: outputs), that tile tables start at 0, grow by the
+//     kernel's tile size and match the grid, and that every "aligned" flag
+//     is backed by 16-byte aligned addresses;
+//   * the few HIP runtime calls api.cpp makes (events, stream waits, device
+//     attributes), as no-ops.
+// The "device buffers" are host heap blocks of exact size, so the sanitizer
+// also catches any host-side overrun in the table builders themselves.
+// The program prints "ok <launches>" when every call behaved.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <random>
+#include <vector>
+
+#include "dt.h"
+#include "dt_launch.h"
+
+namespace {
+
+int g_fail = 0;
+long g_launches = 0;
+
+#define CHECK(cond, ...)                                                     \
+    do {                                                                     \
+        if (!(cond)) {                                                       \
+            fprintf(stderr, "%s:%d: ", __FILE__, __LINE__);                  \
+            fprintf(stderr, __VA_ARGS__);                                    \
+            fprintf(stderr, "\n");                                           \
+            ++g_fail;                                                        \
+            exit(1);                                                         \
+        }                                                                    \
+    } while (0)
+
+// ------------------------------------------------------------ registry --
+struct Buf {
+    size_t size;
+    bool writable;
+};
+std::map<const char*, Buf> g_bufs;  // by base address; the buffers never overlap
+
+void reg(const void* p, size_t n, bool writable) {
+    if (p) g_bufs[static_cast<const char*>(p)] = Buf{n, writable};
+}
+
+// [p + off, p + off + n) must lie inside one registered buffer.
+void touch(const void* p, uint64_t off, uint64_t n, bool write, const char* what) {
+    if (n == 0) return;
+    const char* lo = static_cast<const char*>(p) + off;
+    auto it = g_bufs.upper_bound(lo);  // first buffer starting after lo
+    if (it != g_bufs.begin()) {
+        --it;
+        if (lo + n <= it->first + it->second.size) {
+            CHECK(!write || it->second.writable, "%s writes a read-only buffer", what);
+            return;
+        }
+    }
+    CHECK(false, "%s touches %llu bytes at %p (offset %llu) outside every buffer", what, (unsigned long long)n,
+          static_cast<const void*>(lo), (unsigned long long)off);
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t esize(int dtype) { return dtype == DT_BFLOAT16 ? 2 : 4; }
+uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+// a tile table: starts at 0, piece k spans want[k] tiles, total = grid
+void check_tiles(const uint32_t* tile_start, const std::vector<uint64_t>& want, uint64_t grid, const char* what) {
+    CHECK(tile_start[0] == 0, "%s: tile_start[0] = %u", what, tile_start[0]);
+    for (size_t k = 0; k < want.size(); k++)
+        CHECK(tile_start[k + 1] - tile_start[k] == want[k], "%s: piece %zu has %u tiles, expected %llu", what, k,
+              tile_start[k + 1] - tile_start[k], (unsigned long long)want[k]);
+    CHECK(tile_start[want.size()] == grid, "%s: table ends at %u, grid %llu", what, tile_start[want.size()],
+          (unsigned long long)grid);
+}
+
+}  // namespace
+
+// ------------------------------------------------------ HIP stand-ins --
+extern "C" {
+hipError_t hipGetDevice(int* dev) {
+    *dev = 0;
+    return hipSuccess;
+}
+hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, int) {
+    *value = 100000;
+    return hipSuccess;
+}
+const char* hipGetErrorString(hipError_t) { return "stand-in"; }
+hipError_t hipEventCreateWithFlags(hipEvent_t* e, unsigned) {
+    *e = reinterpret_cast<hipEvent_t>(malloc(64));
+    return hipSuccess;
+}
+hipError_t hipEventDestroy(hipEvent_t e) {
+    free(e);
+    return hipSuccess;
+}
+hipError_t hipEventRecord(hipEvent_t e, hipStream_t) {
+    CHECK(e != nullptr, "record on a null event");
+    return hipSuccess;
+}
+hipError_t hipEventQuery(hipEvent_t e) {
+    CHECK(e != nullptr, "query of a null event");
+    return hipSuccess;
+}
+hipError_t hipEventSynchronize(hipEvent_t e) {
+    CHECK(e != nullptr, "sync on a null event");
+    return hipSuccess;
+}
+hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t e, unsigned) {
+    CHECK(e != nullptr, "wait on a null event");
+    return hipSuccess;
+}
+}
+
+// ------------------------------------------------- launcher stand-ins --
+namespace dt {
+
+// Output vectors per tile of the segmented ReduceScatter.  Deliberately not
+// the library's value: the planning code must take the tile size from this
+// function, never from a constant of its own.
+uint64_t seg_rs_tile_vecs(int) { return 384; }
+
+hipError_t launch_reduce_vec(const ReduceArgs& a, int, int, hipStream_t) {
+    g_launches++;
+    CHECK(a.nranks >= 1 && a.nranks <= kMaxRanksHost, "reduce_vec nranks %d", a.nranks);
+    const uint64_t bytes = a.count * 16;
+    for (int r = 0; r < a.nranks; r++) {
+        CHECK(al16(a.src[r]) && al16(a.dst[r]), "reduce_vec buffers not 16-byte aligned");
+        touch(a.src[r], 0, a.rs ? bytes * a.nranks : bytes, false, "reduce_vec read");
+        touch(a.dst[r], 0, bytes, true, "reduce_vec write");
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_reduce_elems(const ReduceArgs& a, int dtype, int, hipStream_t) {
+    g_launches++;
+    const size_t es = esize(dtype);
+    for (int r = 0; r < a.nranks; r++) {
+        if (a.rs) {
+            for (int c = 0; c < a.nranks; c++)
+                touch(a.src[r], (c * a.chunk_elems + a.first) * es, a.count * es, false, "reduce_elems read");
+        } else {
+            touch(a.src[r], a.first * es, a.count * es, false, "reduce_elems read");
+        }
+        touch(a.dst[r], a.first * es, a.count * es, true, "reduce_elems write");
+    }
+    return hipSuccess;
+}
+
+template <typename Args>
+void check_piece_table(const Args& a, int npieces_cap, int ptr_cap, size_t es, bool fold, int to_ws, const char* what) {
+    CHECK(a.npieces >= 1 && a.npieces <= npieces_cap, "%s: %d pieces", what, a.npieces);
+    CHECK(a.npieces * a.nranks <= ptr_cap, "%s: %d pointers", what, a.npieces * a.nranks);
+    std::vector<uint64_t> want;
+    for (int k = 0; k < a.npieces; k++) want.push_back(ceil_div(a.len[k] * es, kPieceTileVecs * 16));
+    check_tiles(a.tile_start, want, a.tile_start[a.npieces], what);
+    for (int k = 0; k < a.npieces; k++) {
+        CHECK(a.len[k] > 0, "%s: empty piece %d", what, k);
+        for (int r = 0; r < a.nranks; r++) {
+            const void* p = a.ptr[k * a.nranks + r];
+            if (fold) {
+                touch(p, 0, a.len[k] * es, true, what);  // reduced in place
+            } else {
+                touch(p, 0, a.len[k] * es, !to_ws, what);
+                touch(a.ws[r], a.wpos[k] * es, a.len[k] * es, to_ws != 0, what);
+            }
+        }
+    }
+}
+bool piece_aligned(const PieceArgs& a, int k) { return (a.aligned >> k) & 1u; }
+bool piece_aligned(const CoalescedArgs& a, int k) { return (a.aligned[k >> 5] >> (k & 31)) & 1u; }
+template <typename Args>
+void check_piece_alignment(const Args& a, size_t es, bool with_ws, const char* what) {
+    for (int k = 0; k < a.npieces; k++) {
+        if (!piece_aligned(a, k)) continue;
+        for (int r = 0; r < a.nranks; r++) {
+            CHECK(al16(a.ptr[k * a.nranks + r]), "%s: aligned flag on an unaligned piece", what);
+            if (with_ws) CHECK(al16(static_cast<const char*>(a.ws[r]) + a.wpos[k] * es), "%s: unaligned ws", what);
+        }
+    }
+}
+
+hipError_t launch_reduce_pieces(const PieceArgs& a, int dtype, int, hipStream_t) {
+    g_launches++;
+    check_piece_table(a, kMaxPieces, kPiecePtrs, esize(dtype), true, 0, "reduce_pieces");
+    check_piece_alignment(a, esize(dtype), false, "reduce_pieces");
+    return hipSuccess;
+}
+hipError_t launch_reduce_coalesced(const CoalescedArgs& a, int dtype, int, hipStream_t) {
+    g_launches++;
+    check_piece_table(a, kCoalMaxPieces, kCoalPtrs, esize(dtype), true, 0, "reduce_coalesced");
+    check_piece_alignment(a, esize(dtype), false, "reduce_coalesced");
+    return hipSuccess;
+}
+hipError_t launch_copy_pieces(const PieceArgs& a, int es, int to_ws, hipStream_t) {
+    g_launches++;
+    check_piece_table(a, kMaxPieces, kPiecePtrs, size_t(es), false, to_ws, "copy_pieces");
+    check_piece_alignment(a, size_t(es), true, "copy_pieces");
+    return hipSuccess;
+}
+hipError_t launch_copy_coalesced(const CoalescedArgs& a, int es, int to_ws, hipStream_t) {
+    g_launches++;
+    check_piece_table(a, kCoalMaxPieces, kCoalPtrs, size_t(es), false, to_ws, "copy_coalesced");
+    check_piece_alignment(a, size_t(es), true, "copy_coalesced");
+    return hipSuccess;
+}
+
+hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, int, hipStream_t) {
+    g_launches++;
+    const size_t es = esize(dtype), v = 16 / es;
+    CHECK(a.nsegs >= 1 && a.nsegs <= kMaxSegs && a.nsegs * a.nranks <= kSegPtrs, "segs: %d x %d", a.nsegs, a.nranks);
+    std::vector<uint64_t> want;
+    for (int k = 0; k < a.nsegs; k++) {
+        CHECK(a.tiles_per_chunk[k] == ceil_div(a.m[k], seg_rs_tile_vecs(a.nranks) * v), "segs: tiles per chunk");
+        want.push_back(uint64_t(a.tiles_per_chunk[k]) * a.nranks);
+        for (int j = 0; j < a.nranks; j++) {
+            touch(a.src[k * a.nranks + j], 0, a.m[k] * a.nranks * es, false, "segs read");
+            touch(a.dst[k * a.nranks + j], 0, a.m[k] * es, true, "segs write");
+            if ((a.aligned >> k) & 1u) {
+                CHECK(a.m[k] % v == 0, "segs: aligned flag with a ragged chunk");
+                CHECK(al16(a.src[k * a.nranks + j]) && al16(a.dst[k * a.nranks + j]), "segs: unaligned");
+            }
+        }
+    }
+    check_tiles(a.tile_start, want, a.tile_start[a.nsegs], "segs");
+    return hipSuccess;
+}
+
+hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t) {
+    g_launches++;
+    std::vector<uint64_t> want;
+    for (int r = 0; r < a.nranks; r++) want.push_back(ceil_div(a.bytes[r], kGatherTileBytes));
+    check_tiles(a.tile_start, want, tiles, "gather");
+    for (int r = 0; r < a.nranks; r++) {
+        if (a.bytes[r] == 0) continue;
+        touch(a.src[r], 0, a.bytes[r], false, "gather read");
+        for (int q = 0; q < a.nranks; q++) {
+            touch(a.dst[r * a.nranks + q], 0, a.bytes[r], true, "gather write");
+            if ((a.aligned >> r) & 1u) CHECK(al16(a.dst[r * a.nranks + q]), "gather: unaligned destination");
+        }
+        if ((a.aligned >> r) & 1u) CHECK(al16(a.src[r]), "gather: unaligned source");
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t) {
+    g_launches++;
+    const int p = a.nranks;
+    std::vector<uint64_t> want;
+    for (int s = 0; s < p * p; s++) want.push_back(ceil_div(a.split[s], kCopyTileBytes));
+    check_tiles(a.tile_start, want, tiles, "all_to_all");
+    for (int i = 0; i < p; i++)
+        for (int j = 0; j < p; j++) {
+            const int s = i * p + j;
+            if (a.split[s] == 0) continue;
+            uint64_t send_off = 0, recv_off = 0;
+            for (int jj = 0; jj < j; jj++) send_off += a.split[i * p + jj];
+            for (int ii = 0; ii < i; ii++) recv_off += a.split[ii * p + j];
+            touch(a.src[i], send_off, a.split[s], false, "all_to_all read");
+            touch(a.dst[j], recv_off, a.split[s], true, "all_to_all write");
+            if ((a.aligned[s >> 5] >> (s & 31)) & 1u)
+                CHECK(al16(static_cast<const char*>(a.src[i]) + send_off) &&
+                          al16(static_cast<const char*>(a.dst[j]) + recv_off),
+                      "all_to_all: aligned flag on an unaligned block");
+        }
+    return hipSuccess;
+}
+
+hipError_t launch_copy_segments(const SegCopyArgs& a, hipStream_t) {
+    g_launches++;
+    CHECK(a.nsegs >= 1 && a.nsegs <= kMaxCopySegs, "copy_segments: %d segments", a.nsegs);
+    std::vector<uint64_t> want;
+    for (int k = 0; k < a.nsegs; k++) {
+        want.push_back(ceil_div(a.bytes[k], kSegCopyTileBytes));
+        touch(a.src[k], 0, a.bytes[k], false, "copy_segments read");
+        touch(a.dst[k], 0, a.bytes[k], true, "copy_segments write");
+        if ((a.aligned >> k) & 1ull) CHECK(al16(a.src[k]) && al16(a.dst[k]), "copy_segments: unaligned");
+    }
+    check_tiles(a.tile_start, want, a.tile_start[a.nsegs], "copy_segments");
+    return hipSuccess;
+}
+
+hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_t) {
+    g_launches++;
+    const uint64_t es = a.esize, run_bytes = a.cp * es, P = uint64_t(a.nranks);
+    CHECK(a.rp * P == a.rows && a.cp * P == a.cols, "dims: shapes");
+    CHECK(a.nruns == a.rows * P, "dims: %llu runs", (unsigned long long)a.nruns);
+    CHECK(a.runs_per_block >= 1 && a.runs_per_block <= kDimsMaxRunsPerBlock && a.tiles_per_run >= 1,
+          "dims: blocking");
+    CHECK(a.tiles_per_run == (run_bytes >= kDimsTileBytes ? ceil_div(run_bytes, kDimsTileBytes) : 1),
+          "dims: tiles per run");
+    if (a.tiles_per_run > 1)
+        CHECK(blocks == a.nruns * a.tiles_per_run, "dims: grid %u", blocks);
+    else
+        CHECK(blocks == ceil_div(a.nruns, a.runs_per_block), "dims: grid %u", blocks);
+    // the run decode of dt_launch.h, for every run: a whole run of cp elements
+    const uint64_t block_src = (a.dir == 0 ? a.rp * a.cols : a.rows * a.cp) * es;
+    const uint64_t block_dst = (a.dir == 0 ? a.rows * a.cp : a.rp * a.cols) * es;
+    for (int r = 0; r < a.nranks; r++) {
+        touch(a.src[r], 0, block_src, false, "dims source block");
+        touch(a.dst[r], 0, block_dst, true, "dims destination block");
+    }
+    for (uint64_t k = 0; k < a.nruns; k++) {
+        uint64_t i, j, src_off, dst_off;
+        if (a.dir == 0) {
+            j = k / a.rows;
+            const uint64_t row = k % a.rows;
+            i = row / a.rp;
+            src_off = ((row % a.rp) * a.cols + j * a.cp) * es;
+            dst_off = row * a.cp * es;
+        } else {
+            j = k / (a.rp * P);
+            const uint64_t row = (k / P) % a.rp;
+            i = k % P;
+            src_off = (j * a.rp + row) * a.cp * es;
+            dst_off = (row * a.cols + i * a.cp) * es;
+        }
+        CHECK(i < P && j < P, "dims: run %llu decodes to ranks %llu, %llu", (unsigned long long)k,
+              (unsigned long long)i, (unsigned long long)j);
+        if (i >= P || j >= P) break;
+        touch(a.src[i], src_off, run_bytes, false, "dims run read");
+        touch(a.dst[j], dst_off, run_bytes, true, "dims run write");
+        if (a.vec)
+            CHECK(run_bytes % 16 == 0 && al16(static_cast<const char*>(a.src[i]) + src_off) &&
+                      al16(static_cast<const char*>(a.dst[j]) + dst_off),
+                  "dims: vector flag on an unaligned run");
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_barrier(const BarrierArgs& a, int, hipStream_t) {
+    g_launches++;
+    for (int r = 0; r < a.nranks; r++) touch(a.win[r], 0, uint64_t(a.nranks) * 4, true, "barrier window");
+    touch(a.status, 0, 4, true, "barrier status");
+    CHECK(a.timeout_ticks > 0, "barrier without a time budget");
+    return hipSuccess;
+}
+
+hipError_t launch_exchange(const ExchangeArgs& a, int spread, hipStream_t s) {
+    const hipError_t e = launch_barrier(a.bar, spread, s);
+    for (int r = 0; r < a.bar.nranks; r++) {
+        touch(a.src[r], 0, a.nbytes, false, "exchange read");
+        touch(a.stage[r], 0, a.nbytes, true, "exchange stage");
+        touch(a.dst[r], 0, a.nbytes, true, "exchange write");
+    }
+    return e;
+}
+
+}  // namespace dt
+
+// ---------------------------------------------------------------- driver --
+namespace {
+
+std::mt19937_64 rng(12345);
+size_t below(size_t n) { return n ? size_t(rng() % n) : 0; }
+
+// exact-size host blocks posing as device buffers, at an element offset
+struct Pool {
+    std::vector<char*> raw;
+    ~Pool() {
+        for (char* p : raw) free(p);
+    }
+    // a buffer of n bytes starting `skew` bytes into a 16-aligned block
+    char* get(size_t n, size_t skew, bool writable) {
+        char* p = static_cast<char*>(aligned_alloc(16, ((n + skew + 15) / 16) * 16 + 16));
+        raw.push_back(p);
+        reg(p + skew, n, writable);
+        return p + skew;
+    }
+};
+
+void expect(dt_status st, dt_status want, const char* what) {
+    CHECK(st == want, "%s returned %d (%s), expected %d", what, st, dt_last_error(), want);
+}
+
+void reductions() {
+    for (int it = 0; it < 120; it++) {
+        Pool pool;
+        g_bufs.clear();
+        const int p = 1 + int(below(16));
+        const dt_dtype dtype = dt_dtype(below(3));
+        const dt_op op = dt_op(below(4));
+        const size_t es = esize(dtype);
+        const size_t m = below(4) == 0 ? below(3) : below(3000);
+        const size_t skew = below(3) == 0 ? es * below(4) : 0;  // unaligned buffers sometimes
+        std::vector<const void*> send(p);
+        std::vector<void*> recv(p), shard(p);
+        for (int r = 0; r < p; r++) {
+            send[r] = pool.get(p * m * es, skew, false);
+            recv[r] = pool.get(p * m * es, skew, true);
+            shard[r] = pool.get(m * es, skew, true);
+        }
+        expect(dt_allreduce(send.data(), recv.data(), p, p * m, dtype, op, nullptr), DT_OK, "allreduce");
+        expect(dt_reduce_scatter(send.data(), shard.data(), p, m, dtype, op, nullptr), DT_OK, "reduce_scatter");
+        // in place
+        for (int r = 0; r < p; r++) send[r] = recv[r];
+        expect(dt_allreduce(send.data(), recv.data(), p, p * m, dtype, op, nullptr), DT_OK, "allreduce in place");
+        expect(dt_replicate_to_shard(send.data(), shard.data(), p, m, dtype, nullptr), DT_OK, "replicate_to_shard");
+    }
+}
+
+void copies() {
+    for (int it = 0; it < 120; it++) {
+        Pool pool;
+        g_bufs.clear();
+        const int p = 1 + int(below(16));
+        const dt_dtype dtype = dt_dtype(below(3));
+        const size_t es = esize(dtype);
+        const size_t skew = below(3) == 0 ? es * below(4) : 0;
+        std::vector<size_t> counts(p);
+        size_t total = 0;
+        for (int r = 0; r < p; r++) total += counts[r] = below(3) == 0 ? 0 : below(below(2) ? 5000 : 40);
+        std::vector<const void*> send(p);
+        std::vector<void*> recv(p), vec(size_t(p) * p), bcast(p);
+        for (int r = 0; r < p; r++) send[r] = counts[r] ? pool.get(counts[r] * es, skew, false) : nullptr;
+        for (int q = 0; q < p; q++) recv[q] = pool.get(total * es, skew, true);
+        expect(dt_all_gather(send.data(), recv.data(), p, counts.data(), 0, dtype, nullptr), DT_OK, "all_gather");
+        for (int q = 0; q < p; q++)
+            for (int r = 0; r < p; r++) vec[q * p + r] = counts[r] ? pool.get(counts[r] * es, skew, true) : nullptr;
+        expect(dt_all_gather_into_vec(send.data(), vec.data(), p, counts.data(), 0, dtype, nullptr), DT_OK,
+               "all_gather_into_vec");
+        const size_t n0 = 1 + below(3000);
+        const void* root = pool.get(n0 * es, skew, false);
+        for (int q = 0; q < p; q++) bcast[q] = pool.get(n0 * es, skew, true);
+        expect(dt_broadcast(root, bcast.data(), p, n0, dtype, nullptr), DT_OK, "broadcast");
+        // equal counts
+        const size_t c = 1 + below(2000);
+        std::vector<const void*> send_eq(p);
+        std::vector<void*> recv_eq(p);
+        for (int r = 0; r < p; r++) send_eq[r] = pool.get(c * es, skew, false);
+        for (int q = 0; q < p; q++) recv_eq[q] = pool.get(p * c * es, skew, true);
+        expect(dt_all_gather(send_eq.data(), recv_eq.data(), p, nullptr, c, dtype, nullptr), DT_OK,
+               "all_gather equal");
+
+        // all-to-all with a random split matrix (zero blocks, empty ranks)
+        std::vector<size_t> splits(size_t(p) * p);
+        std::vector<size_t> row(p, 0), col(p, 0);
+        const size_t hi = below(2) ? 3 : 1500;
+        for (int i = 0; i < p; i++)
+            for (int j = 0; j < p; j++) {
+                splits[i * p + j] = below(4) == 0 ? 0 : below(hi);
+                row[i] += splits[i * p + j];
+                col[j] += splits[i * p + j];
+            }
+        std::vector<const void*> a_send(p);
+        std::vector<void*> a_recv(p);
+        for (int r = 0; r < p; r++) {
+            a_send[r] = row[r] ? pool.get(row[r] * es, skew, false) : nullptr;
+            a_recv[r] = col[r] ? pool.get(col[r] * es, skew, true) : nullptr;
+        }
+        expect(dt_all_to_all(a_send.data(), a_recv.data(), p, splits.data(), dtype, nullptr), DT_OK, "all_to_all");
+
+        // shard-dimension all-to-all, every (src, dst) pair
+        const size_t rows = p * (1 + below(6)), cols = p * (1 + below(below(2) ? 6 : 3000));
+        for (int sd = 0; sd < 2; sd++)
+            for (int dd = 0; dd < 2; dd++) {
+                const size_t ns = sd == 0 ? rows / p * cols : rows * (cols / p);
+                const size_t nd = dd == 0 ? rows / p * cols : rows * (cols / p);
+                std::vector<const void*> ds(p);
+                std::vector<void*> dd_(p);
+                for (int r = 0; r < p; r++) {
+                    ds[r] = pool.get(ns * es, skew, false);
+                    dd_[r] = pool.get(nd * es, skew, true);
+                }
+                expect(dt_all_to_all_dims(ds.data(), dd_.data(), p, rows, cols, sd, dd, dtype, nullptr), DT_OK,
+                       "all_to_all_dims");
+            }
+    }
+}
+
+void buckets() {
+    for (int it = 0; it < 80; it++) {
+        Pool pool;
+        g_bufs.clear();
+        const int p = 1 + int(below(16));
+        const dt_dtype dtype = dt_dtype(below(3));
+        const dt_op op = dt_op(below(4));
+        const size_t es = esize(dtype);
+        const int nt = 1 + int(below(below(4) == 0 ? 700 : 40));
+        std::vector<size_t> numels(nt);
+        for (int t = 0; t < nt; t++) numels[t] = below(5) == 0 ? 0 : below(below(2) ? 50 : 5000);
+        std::vector<void*> grads(size_t(p) * nt);
+        for (int r = 0; r < p; r++)
+            for (int t = 0; t < nt; t++)
+                grads[r * nt + t] = numels[t] ? pool.get(numels[t] * es, es * below(4), true) : nullptr;
+        const size_t bucket = 16 * (below(2) ? 1 + below(8) : 64 + below(4000));
+        expect(dt_bucket_allreduce(grads.data(), numels.data(), nt, p, bucket, nullptr, dtype, op, nullptr), DT_OK,
+               "bucket in place");
+        std::vector<void*> ws(p);
+        for (int r = 0; r < p; r++) ws[r] = pool.get(bucket, 0, true);
+        expect(dt_bucket_allreduce(grads.data(), numels.data(), nt, p, bucket, ws.data(), dtype, op, nullptr), DT_OK,
+               "bucket staged");
+        expect(dt_allreduce_coalesced(grads.data(), numels.data(), nt, p, dtype, op, nullptr), DT_OK, "coalesced");
+
+        // the bucket plan: every element exactly once, buckets within bounds
+        size_t npieces = 0, nb = 0;
+        expect(dt_bucket_plan(numels.data(), nt, es, bucket, nullptr, 0, &npieces, &nb), DT_OK, "plan count");
+        std::vector<dt_piece> pieces(npieces + 1);
+        expect(dt_bucket_plan(numels.data(), nt, es, bucket, pieces.data(), npieces, &npieces, &nb), DT_OK, "plan");
+        std::vector<size_t> covered(nt, 0);
+        for (size_t k = 0; k < npieces; k++) {
+            const dt_piece& pc = pieces[k];
+            CHECK(pc.tensor >= 0 && pc.tensor < nt && size_t(pc.bucket) < nb, "plan: piece %zu", k);
+            CHECK(pc.offset == covered[pc.tensor], "plan: piece %zu out of order", k);
+            CHECK((pc.bucket_pos + pc.length) * es <= bucket, "plan: piece %zu overflows its bucket", k);
+            covered[pc.tensor] += pc.length;
+        }
+        for (int t = 0; t < nt; t++) CHECK(covered[t] == numels[t], "plan: tensor %d covered %zu", t, covered[t]);
+    }
+}
+
+void hsdp_and_sync() {
+    const int meshes[][2] = {{2, 4}, {1, 8}, {8, 1}, {4, 4}, {2, 2}, {1, 1}, {16, 1}, {1, 16}};
+    for (auto& mesh : meshes) {
+        Pool pool;
+        g_bufs.clear();
+        const int rep = mesh[0], sh = mesh[1], p = rep * sh;
+        const dt_dtype dtype = DT_BFLOAT16;
+        const size_t es = 2;
+        dt_hsdp* h = nullptr;
+        expect(dt_hsdp_create(rep, sh, 16 * (1 + below(100)), dtype, DT_SUM, nullptr, nullptr, &h), DT_OK, "hsdp");
+        for (int layer = 0; layer < 5; layer++) {
+            const int nt = 1 + int(below(9));
+            std::vector<size_t> numels(nt);
+            size_t total = 0;
+            for (int t = 0; t < nt; t++) total += numels[t] = sh * (below(4) == 0 ? 0 : 1 + below(700));
+            std::vector<void*> grads(size_t(p) * nt), fused(p);
+            for (int r = 0; r < p; r++) {
+                for (int t = 0; t < nt; t++) grads[r * nt + t] = numels[t] ? pool.get(numels[t] * es, 0, false) : nullptr;
+                fused[r] = pool.get(total / sh * es, 0, true);
+            }
+            expect(dt_hsdp_post_backward(h, grads.data(), numels.data(), nt, fused.data(), nullptr), DT_OK,
+                   "hsdp post_backward");
+        }
+        expect(dt_hsdp_finish(h, nullptr), DT_OK, "hsdp finish");
+        expect(dt_hsdp_destroy(h), DT_OK, "hsdp destroy");
+
+        // barrier and exchange
+        std::vector<int32_t*> win(p);
+        for (int r = 0; r < p; r++) win[r] = reinterpret_cast<int32_t*>(pool.get(size_t(p) * 4, 0, true));
+        int32_t* status = reinterpret_cast<int32_t*>(pool.get(4, 0, true));
+        for (int layout = 0; layout < 2; layout++)
+            expect(dt_barrier(win.data(), p, 1, 10, status, 0, layout, nullptr), DT_OK, "barrier");
+        const size_t nbytes = below(5000);
+        std::vector<const void*> src(p);
+        std::vector<void*> stage(p), dst(p);
+        for (int r = 0; r < p; r++) {
+            src[r] = pool.get(nbytes, 0, false);
+            stage[r] = pool.get(nbytes, 0, true);
+            dst[r] = pool.get(nbytes, 0, true);
+        }
+        expect(dt_barrier_exchange(src.data(), stage.data(), dst.data(), nbytes, win.data(), p, 11, status, 0,
+                                   DT_BARRIER_PACKED, nullptr),
+               DT_OK, "exchange");
+    }
+}
+
+void validation() {
+    Pool pool;
+    g_bufs.clear();
+    const void* a = pool.get(64, 0, false);
+    void* b = pool.get(64, 0, true);
+    const void* send[2] = {a, a};
+    void* recv[2] = {b, b};
+    expect(dt_allreduce(send, recv, 0, 4, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG, "nranks 0");
+    expect(dt_allreduce(send, recv, 17, 4, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG, "nranks 17");
+    expect(dt_allreduce(send, recv, 2, 4, dt_dtype(7), DT_SUM, nullptr), DT_ERR_ARG, "bad dtype");
+    expect(dt_allreduce(send, recv, 2, 4, DT_FLOAT32, dt_op(9), nullptr), DT_ERR_ARG, "bad op");
+    expect(dt_allreduce(send, recv, 2, 4, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG, "recv aliases");
+    size_t numels[1] = {4};
+    void* g[1] = {b};
+    expect(dt_bucket_allreduce(g, numels, 1, 1, 24, nullptr, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG,
+           "bucket not a multiple of 16");
+    size_t np = 0, nb = 0;
+    expect(dt_bucket_plan(numels, 1, 4, 2, nullptr, 0, &np, &nb), DT_ERR_ARG, "bucket smaller than an element");
+}
+
+}  // namespace
+
+int main() {
+    validation();
+    reductions();
+    copies();
+    buckets();
+    hsdp_and_sync();
+    if (g_fail) {
+        fprintf(stderr, "%d checks failed\n", g_fail);
+        return 1;
+    }
+    printf("ok %ld\n", g_launches);
+    return 0;
+}

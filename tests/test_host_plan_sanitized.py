@@ -1,0 +1,81 @@
+"""The C ABI's host-side planning code under AddressSanitizer and UBSan (CPU).
+
+``api.cpp`` is compiled for the host with g++ and linked against
+``host_plan_check.cpp``, which replaces the kernel launchers with checks of
+the argument blocks (every byte range a kernel would touch lies inside a
+buffer the caller passed, tile tables match the grid, alignment flags are
+true) and the few HIP runtime calls with no-ops.  The driver then calls every
+entry point on seeded random shapes with exact-size host buffers.  Planted
+planning bugs in copies of ``api.cpp`` must make the check fail.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+API = os.path.join(ROOT, "collective_communication_primitives_amd", "csrc", "api.cpp")
+CHECK = os.path.join(HERE, "host_plan_check.cpp")
+ROCM_INCLUDE = "/opt/rocm/include"
+FLAGS = ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+         "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I", ROCM_INCLUDE, "-I", os.path.join(ROOT, "include"),
+         "-I", os.path.join(ROOT, "collective_communication_primitives_amd", "csrc")]
+ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:halt_on_error=1:verify_asan_link_order=0",
+           UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+
+
+def _available() -> bool:
+    if shutil.which("g++") is None or not os.path.isdir(os.path.join(ROCM_INCLUDE, "hip")):
+        return False
+    out = subprocess.run(["g++", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    return os.path.isabs(out) and os.path.exists(out)
+
+
+pytestmark = pytest.mark.skipif(not _available(), reason="g++ with AddressSanitizer or the HIP headers missing")
+
+
+@pytest.fixture(scope="module")
+def check_obj(tmp_path_factory):
+    obj = str(tmp_path_factory.mktemp("plan") / "host_plan_check.o")
+    subprocess.run(["g++", *FLAGS, "-c", CHECK, "-o", obj], check=True, capture_output=True, text=True)
+    return obj
+
+
+def _build_and_run(api_source: str, check_obj: str, out_dir) -> subprocess.CompletedProcess:
+    exe = str(out_dir / "plan_check")
+    subprocess.run(["g++", *FLAGS, api_source, check_obj, "-o", exe], check=True, capture_output=True, text=True)
+    return subprocess.run([exe], capture_output=True, text=True, env=ENV, timeout=600)
+
+
+def test_planning_code_is_clean(check_obj, tmp_path):
+    res = _build_and_run(API, check_obj, tmp_path)
+    assert res.returncode == 0 and res.stdout.startswith("ok "), res.stdout[-2000:] + res.stderr[-4000:]
+    assert int(res.stdout.split()[1]) > 1000  # the driver really reached the launchers
+
+
+MUTANTS = {
+    # the gather grid drops the partial last tile of every source
+    "gather_drops_partial_tile": ("tiles += (bytes + dt::kGatherTileBytes - 1) / dt::kGatherTileBytes;",
+                                  "tiles += bytes / dt::kGatherTileBytes;"),
+    # bucket pieces start one element late: the last piece runs past its tensor
+    "bucket_piece_off_by_one": (
+        "ref.ptr[r] = static_cast<char*>(grads[size_t(r) * ntensors + p.tensor]) + p.offset * es;",
+        "ref.ptr[r] = static_cast<char*>(grads[size_t(r) * ntensors + p.tensor]) + (p.offset + 1) * es;"),
+    # one run too many for the shard-dimension exchange
+    "dims_extra_run": ("a.nruns = uint64_t(rows) * P;", "a.nruns = uint64_t(rows) * P + 1;"),
+    # every piece claimed 16-byte aligned
+    "pieces_always_aligned": ("if (al) set_aligned(a, k);", "set_aligned(a, k);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_planning_bug_is_caught(check_obj, tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(API).read()
+    assert src.count(old) == 1, name
+    mutated = tmp_path / "api_mutant.cpp"
+    mutated.write_text(src.replace(old, new))
+    res = _build_and_run(str(mutated), check_obj, tmp_path)
+    assert res.returncode != 0, f"{name} was not caught"
