@@ -15,11 +15,13 @@
 //     cannot starve, and the launch is an ordinary one.
 //   spread: one workgroup per rank, launched cooperatively so all P are
 //     resident at once; the ranks then sit on different CUs and XCDs.
-// Notifies are device-scope release atomics and waits device-scope acquire
-// loads: the MI355X's eight XCDs each have their own L2, and device scope is
-// what makes the window (and the data it guards) coherent across them.  Every
-// wait is bounded by a wall-clock budget; on expiry the wave records
-// DT_ERR_TIMEOUT (4) and leaves, so no launch can hang.
+// Notifies are release atomics and waits acquire loads at the narrowest
+// scope that holds every rank: device scope for the spread layout (the
+// MI355X's eight XCDs each have their own L2, and device scope is what makes
+// the window and the data it guards coherent across them), workgroup scope
+// for the packed layout, whose ranks all share one CU.  Every wait is bounded
+// by a wall-clock budget; on expiry the wave records DT_ERR_TIMEOUT (4) and
+// leaves, so no launch can hang.
 #include "dt_device.h"
 #include "dt_launch.h"
 
@@ -27,14 +29,16 @@ namespace dt {
 
 constexpr int kTimeoutStatus = 4;
 
-// One generation for rank r, executed by one full wave (lane = 0..63).
-// Returns false on timeout (wave-uniform).
+// One generation for rank r, executed by one full wave (lane = 0..63), with
+// the notifies and waits at memory scope SCOPE.  Returns false on timeout
+// (wave-uniform).
+template <int SCOPE>
 __device__ bool barrier_round(const BarrierArgs& a, int r, int g, int lane) {
     const bool peer = lane < a.nranks && lane != r;
-    if (peer) __hip_atomic_fetch_add(a.win[lane] + r, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (peer) __hip_atomic_fetch_add(a.win[lane] + r, 1, __ATOMIC_RELEASE, SCOPE);
     const uint64_t start = wall_clock64();
     while (true) {
-        const bool ok = !peer || __hip_atomic_load(a.win[r] + lane, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= g;
+        const bool ok = !peer || __hip_atomic_load(a.win[r] + lane, __ATOMIC_ACQUIRE, SCOPE) >= g;
         if (__all(ok)) return true;
         if (wall_clock64() - start > a.timeout_ticks) {
             if (lane == 0) __hip_atomic_store(a.status, kTimeoutStatus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -48,7 +52,7 @@ __device__ bool barrier_round(const BarrierArgs& a, int r, int g, int lane) {
 __global__ __launch_bounds__(64) void k_barrier_spread(BarrierArgs a) {
     const int r = blockIdx.x;
     for (int k = 0; k < a.generations; k++)
-        if (!barrier_round(a, r, a.first_generation + k, threadIdx.x)) return;
+        if (!barrier_round<__HIP_MEMORY_SCOPE_AGENT>(a, r, a.first_generation + k, threadIdx.x)) return;
 }
 
 // packed: one workgroup, wave w = rank w
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(1024) void k_barrier_packed(BarrierArgs a) {
     const int r = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     for (int k = 0; k < a.generations; k++)
-        if (!barrier_round(a, r, a.first_generation + k, lane)) return;
+        if (!barrier_round<__HIP_MEMORY_SCOPE_WORKGROUP>(a, r, a.first_generation + k, lane)) return;
 }
 
 // Byte copy by `n_threads` cooperating threads (index `tid`).
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(kBlock) void k_exchange_spread(ExchangeArgs a) {
     __threadfence();  // this workgroup's staged bytes before its notifies
     __syncthreads();
     if (threadIdx.x < 64) {
-        const bool ok = barrier_round(a.bar, r, a.bar.first_generation, threadIdx.x);
+        const bool ok = barrier_round<__HIP_MEMORY_SCOPE_AGENT>(a.bar, r, a.bar.first_generation, threadIdx.x);
         if (threadIdx.x == 0) passed = ok ? 1 : 0;
     }
     __syncthreads();
@@ -97,9 +101,9 @@ __global__ __launch_bounds__(1024) void k_exchange_packed(ExchangeArgs a) {
     const int r = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     copy_bytes(static_cast<char*>(a.stage[r]), static_cast<const char*>(a.src[r]), a.nbytes, lane, 64);
-    __threadfence();  // the wave's staged bytes before its notifies
-    if (!barrier_round(a.bar, r, a.bar.first_generation, lane)) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // peers' staged bytes are visible
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the wave's staged bytes before its notifies
+    if (!barrier_round<__HIP_MEMORY_SCOPE_WORKGROUP>(a.bar, r, a.bar.first_generation, lane)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // peers' staged bytes are visible
     const int peer = (r + 1) % a.bar.nranks;
     copy_bytes(static_cast<char*>(a.dst[r]), static_cast<const char*>(a.stage[peer]), a.nbytes, lane, 64);
 }

@@ -163,8 +163,9 @@ dt_status dt_allreduce_coalesced(void* const* tensors, const size_t* numels, int
  * "The idea" and "Walkthrough": windows[p] is rank p's window of nranks int32
  * cells in device memory (zeroed once by the caller before its first use).
  * In generation g every rank r atomically adds 1 to cell r of every other
- * rank's window (release, device scope), then waits until every cell s != r
- * of its own window is >= g (acquire, device scope).  Generations
+ * rank's window (release), then waits until every cell s != r of its own
+ * window is >= g (acquire), at device scope when the ranks are spread over
+ * workgroups and at workgroup scope when they share one.  Generations
  * first_generation .. first_generation + generations - 1 run back to back in
  * ONE launch; `layout` places the ranks (dt_barrier_layout).  Reusing a
  * window means passing the next generation number (the page's "Edge cases":
