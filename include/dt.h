@@ -163,9 +163,10 @@ dt_status dt_allreduce_coalesced(void* const* tensors, const size_t* numels, int
  * "The idea" and "Walkthrough": windows[p] is rank p's window of nranks int32
  * cells in device memory (zeroed once by the caller before its first use).
  * In generation g every rank r atomically adds 1 to cell r of every other
- * rank's window (release), then waits until every cell s != r of its own
- * window is >= g (acquire), at device scope when the ranks are spread over
- * workgroups and at workgroup scope when they share one.  Generations
+ * rank's window, then waits until every cell s != r of its own window is
+ * >= g, with atomics at device scope when the ranks are spread over
+ * workgroups and at workgroup scope when they share one.  The launch orders
+ * only the windows; dt_barrier_exchange below orders data.  Generations
  * first_generation .. first_generation + generations - 1 run back to back in
  * ONE launch; `layout` places the ranks (dt_barrier_layout).  Reusing a
  * window means passing the next generation number (the page's "Edge cases":
@@ -179,8 +180,10 @@ dt_status dt_barrier(int32_t* const* windows, int nranks, int32_t first_generati
 /* The barrier ordering a data exchange, as in the pypto page's built-in
  * demonstration: every rank r copies src[r] (nbytes) to stage[r], meets the
  * barrier of generation `generation` on `windows`, then copies stage[(r+1) %
- * nranks] to dst[r].  Afterwards dst[r] == src[(r+1) % nranks].  Timeout,
- * status and layout as dt_barrier. */
+ * nranks] to dst[r].  A release fence separates the staging from the
+ * notifies and an acquire fence the waits from the reads, so every rank's
+ * staged bytes are visible to its reader.  Afterwards dst[r] ==
+ * src[(r+1) % nranks].  Timeout, status and layout as dt_barrier. */
 dt_status dt_barrier_exchange(const void* const* src, void* const* stage, void* const* dst, size_t nbytes,
                               int32_t* const* windows, int nranks, int32_t generation, int32_t* status_dev,
                               uint64_t timeout_ns, int layout, hipStream_t stream);
