@@ -107,6 +107,18 @@ def side_stream(device: Optional[int] = None) -> torch.cuda.Stream:
     return _side_streams[dev]
 
 
+def join_streams(producers: Sequence[torch.cuda.Stream], stream=None) -> None:
+    """User rule 4 of the c10d page (sec. 5): inputs computed on streams other
+    than the current one must be joined into it before the collective is
+    issued, because an async collective orders itself after the current
+    stream only.  Makes ``stream`` (default: current) wait for everything
+    queued so far on each producer stream; the host does not block."""
+    target = torch.cuda.current_stream() if stream is None else stream
+    for p in producers:
+        if p is not None and p != target:
+            target.wait_stream(p)
+
+
 class Work:
     """Handle of an async collective: the start/end event pair plus the stash
     of tensors that must outlive the GPU work (released by ``wait``)."""

@@ -54,6 +54,29 @@ def test_async_work_is_not_complete_before_producer(dt):
     assert bool((xs[0] == 2).all())
 
 
+def test_producers_on_their_own_streams_are_joined(dt):
+    """Rule 4: each rank's input is written late on a stream of its own; after
+    join_streams the async collective sees every input."""
+    p, n = 4, 1 << 18
+    xs = [torch.zeros(n, device="cuda") for _ in range(p)]
+    ys = [torch.empty(n, device="cuda") for _ in range(p)]
+    vals = synth.uniform_ranks(p, n, seed=6, device="cuda")
+    producers = [torch.cuda.Stream() for _ in range(p)]
+    torch.cuda.synchronize()
+    note("producers on P streams joined before an async allreduce")
+    for r, s in enumerate(producers):
+        with torch.cuda.stream(s):
+            torch.cuda._sleep(SPIN // (r + 1))  # each producer finishes at its own time
+            xs[r].copy_(vals[r])
+    dt.join_streams(producers)
+    work = dt.dt_allreduce(xs, ys, async_op=True)
+    work.wait()
+    host = [to_np(y) for y in ys]
+    want = oracle.get().allreduce([to_np(v) for v in vals], "sum")
+    for q in range(p):
+        compare(host[q], want[q], f"rank {q}")
+
+
 def test_third_stream_consumer(dt):
     """Rule 3: a consumer on a third stream waits on the work itself."""
     p, n = 3, 1 << 16
