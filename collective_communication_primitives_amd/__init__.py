@@ -141,13 +141,37 @@ class Work:
     def __del__(self):
         h = getattr(self, "_h", None)
         if h:
-            _L.dt_work_free(h)
+            if getattr(self, "_stash", None):
+                # dropped without wait(): shelve the tensors until the GPU is done
+                _shelf.append((h, self._stash))
+            else:
+                _L.dt_work_free(h)
             self._h = None
+            self._stash = []
+
+
+# Works dropped without wait(): (handle, tensors).  As in the c10d page
+# (sec. 4.4), a forgotten wait() leaks nothing but may not free the tensors
+# while the collective can still touch them: they stay here until the work's
+# end event has completed, and are released by the next collective call.
+_shelf: List = []
+
+
+def _unshelve() -> None:
+    keep = []
+    for h, stash in _shelf:
+        if _L.dt_work_query(h) == 0:
+            keep.append((h, stash))
+        else:
+            _L.dt_work_free(h)
+    _shelf[:] = keep
 
 
 def _launch(fn, stash, async_op: bool, stream, comm_stream):
     """Queue ``fn(stream_handle)`` either on ``stream`` or, for async_op, on a
     side stream ordered after the current stream."""
+    if _shelf:
+        _unshelve()
     if not async_op:
         _check(fn(_stream_handle(stream)))
         return None

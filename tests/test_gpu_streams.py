@@ -77,6 +77,38 @@ def test_producers_on_their_own_streams_are_joined(dt):
         compare(host[q], want[q], f"rank {q}")
 
 
+def test_dropped_work_keeps_its_tensors_alive(dt):
+    """Rule 5: an async work dropped without wait() must not let its tensors be
+    freed and reused while the collective can still read or write them.  The
+    work is queued behind a long kernel on its side stream, then dropped
+    together with every reference to its inputs.  New tensors of the same
+    size allocated right away must not receive the inputs' blocks (torch's
+    allocator would hand them out at once if they were freed), and the
+    collective must still produce the original inputs' result."""
+    import gc
+    p, n = 4, 1 << 20
+    vals = synth.uniform_ranks(p, n, seed=7, device="cuda")
+    want = oracle.get().allreduce([to_np(v) for v in vals], "sum")
+    ys = [torch.empty(n, device="cuda") for _ in range(p)]
+    torch.cuda.synchronize()
+    note("async allreduce dropped without wait()")
+    xs = [v.clone() for v in vals]
+    held = {x.data_ptr() for x in xs}
+    with torch.cuda.stream(dt.side_stream()):
+        torch.cuda._sleep(SPIN)        # the collective starts only after this
+    work = dt.dt_allreduce(xs, ys, async_op=True)
+    del work, xs
+    gc.collect()
+    assert len(dt._shelf) == 1         # still running: its tensors are shelved
+    junk = [torch.full((n,), 1e30, device="cuda") for _ in range(2 * p)]
+    assert not held & {j.data_ptr() for j in junk}, "a dropped work's input block was reused"
+    torch.cuda.synchronize()
+    for q in range(p):
+        compare(to_np(ys[q]), want[q], f"rank {q}")
+    dt.dt_allreduce(junk[:p])           # the next call releases the finished work
+    assert not dt._shelf
+
+
 def test_third_stream_consumer(dt):
     """Rule 3: a consumer on a third stream waits on the work itself."""
     p, n = 3, 1 << 16
