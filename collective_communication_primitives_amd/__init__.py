@@ -59,29 +59,47 @@ def version() -> str:
 
 
 def _ptr_array(tensors: Sequence[torch.Tensor]):
-    arr = (ctypes.c_void_p * max(1, len(tensors)))()
-    for i, t in enumerate(tensors):
-        arr[i] = t.data_ptr()
-    return arr
+    return (ctypes.c_void_p * max(1, len(tensors)))(*[t.data_ptr() for t in tensors])
 
 
 def _size_array(values: Sequence[int]):
-    arr = (ctypes.c_size_t * max(1, len(values)))()
-    for i, v in enumerate(values):
-        arr[i] = int(v)
-    return arr
+    return (ctypes.c_size_t * max(1, len(values)))(*[int(v) for v in values])
 
 
 def _dtype_code(tensors: Sequence[torch.Tensor]) -> int:
-    dt = tensors[0].dtype
+    """The tensors' common dtype code, after checking that every tensor is a
+    contiguous tensor of that dtype on the current GPU (a host or
+    other-device pointer must never reach a kernel)."""
+    t0 = tensors[0]
+    dt = t0.dtype
     if dt not in _DTYPES:
         raise TypeError(f"unsupported dtype {dt}")
+    dev = torch.cuda.current_device()
     for t in tensors:
         if t.dtype != dt:
             raise TypeError("all rank tensors must share one dtype")
+        if t.get_device() != dev:
+            raise ValueError(f"rank tensors must live on the current GPU (cuda:{dev}), got {t.device}")
         if not t.is_contiguous():
             raise ValueError("rank tensors must be contiguous")
     return _DTYPES[dt]
+
+
+def _on_gpu(tensors: Sequence[torch.Tensor], what: str) -> None:
+    """Every tensor must be a contiguous tensor on the current GPU."""
+    dev = torch.cuda.current_device()
+    for t in tensors:
+        if t.get_device() != dev or not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous tensors on the current GPU (cuda:{dev}), got {t.device}")
+
+
+def _check_windows(windows: Sequence[torch.Tensor], status: torch.Tensor, p: int) -> None:
+    for w in windows:
+        if w.dtype != torch.int32 or w.numel() < p:
+            raise ValueError("each window must be an int32 tensor of at least nranks cells")
+    if status.dtype != torch.int32 or status.numel() < 1:
+        raise ValueError("status must be an int32 device tensor")
+    _on_gpu(list(windows) + [status], "windows and status")
 
 
 def _op_code(op) -> int:
@@ -328,6 +346,7 @@ def dt_bucket_allreduce(grads: Sequence[Sequence[torch.Tensor]], bucket_bytes: i
     if bucket_ws is not None:
         if len(bucket_ws) != p or any(w.numel() * w.element_size() < bucket_bytes for w in bucket_ws):
             raise ValueError("bucket_ws needs one buffer of at least bucket_bytes per rank")
+        _on_gpu(bucket_ws, "bucket_ws")
     g_arr, n_arr = _ptr_array(flat), _size_array(numels)
     ws_arr = _ptr_array(bucket_ws) if bucket_ws is not None else None
     stash = flat + (list(bucket_ws) if bucket_ws is not None else [])
@@ -378,11 +397,7 @@ def dt_barrier(windows: Sequence[torch.Tensor], status: torch.Tensor, first_gene
     layout "packed" (one workgroup, a wave per rank) or "spread" (a
     workgroup per rank, cooperative launch)."""
     p = len(windows)
-    for w in windows:
-        if w.dtype != torch.int32 or w.numel() < p or not w.is_contiguous():
-            raise ValueError("each window must be a contiguous int32 tensor of at least nranks cells")
-    if status.dtype != torch.int32:
-        raise ValueError("status must be an int32 device tensor")
+    _check_windows(windows, status, p)
     w_arr = _ptr_array(windows)
     _check(_L.dt_barrier(w_arr, p, first_generation, generations, status.data_ptr(), timeout_ns, _LAYOUTS[layout],
                          _stream_handle(stream)))
@@ -395,8 +410,12 @@ def dt_barrier_exchange(src: Sequence[torch.Tensor], stage: Sequence[torch.Tenso
     p = len(src)
     nbytes = src[0].numel() * src[0].element_size()
     for group in (src, stage, dst):
-        if len(group) != p or any(t.numel() * t.element_size() != nbytes or not t.is_contiguous() for t in group):
+        if len(group) != p or any(t.numel() * t.element_size() != nbytes for t in group):
             raise ValueError("src, stage and dst need one contiguous buffer of equal bytes per rank")
+        _on_gpu(group, "src, stage and dst")
+    if len(windows) != p:
+        raise ValueError("one window per rank")
+    _check_windows(windows, status, p)
     _check(_L.dt_barrier_exchange(_ptr_array(src), _ptr_array(stage), _ptr_array(dst), nbytes, _ptr_array(windows),
                                   p, generation, status.data_ptr(), timeout_ns, _LAYOUTS[layout],
                                   _stream_handle(stream)))
