@@ -144,14 +144,15 @@ class Work:
     def __init__(self, handle: ctypes.c_void_p, stash: List[torch.Tensor]):
         self._h = handle
         self._stash = stash
+        self._lib = _L  # kept for __del__, which may run during interpreter shutdown
 
     def wait(self, stream=None) -> None:
         """Make ``stream`` (default: current) wait for the end event; the host does not block."""
-        _check(_L.dt_work_wait(self._h, _stream_handle(stream)))
+        _check(self._lib.dt_work_wait(self._h, _stream_handle(stream)))
         self._stash = []
 
     def is_completed(self) -> bool:
-        rc = _L.dt_work_query(self._h)
+        rc = self._lib.dt_work_query(self._h)
         if rc < 0:
             raise DtError(DT_ERR_HIP, _L.dt_last_error().decode())
         return rc == 1
@@ -159,11 +160,11 @@ class Work:
     def __del__(self):
         h = getattr(self, "_h", None)
         if h:
-            if getattr(self, "_stash", None):
+            if getattr(self, "_stash", None) and _shelf is not None:
                 # dropped without wait(): shelve the tensors until the GPU is done
                 _shelf.append((h, self._stash))
             else:
-                _L.dt_work_free(h)
+                self._lib.dt_work_free(h)
             self._h = None
             self._stash = []
 
@@ -441,6 +442,7 @@ class HSDPPipeline:
         self.ar_stream = ar_stream if ar_stream is not None else torch.cuda.Stream()
         self._h = ctypes.c_void_p()
         self._stash: List[torch.Tensor] = []
+        self._lib = _L  # kept for __del__, which may run during interpreter shutdown
         _check(_L.dt_hsdp_create(replicate, shard, bucket_bytes, _DTYPES[dtype], _op_code(op),
                                  _stream_handle(self.rs_stream), _stream_handle(self.ar_stream),
                                  ctypes.byref(self._h)))
@@ -459,18 +461,18 @@ class HSDPPipeline:
         if any(f.numel() != sum(numels) // self.shard for f in fused):
             raise ValueError("fused[r] must hold sum(numels) / shard elements")
         self._stash.extend(flat + list(fused))
-        _check(_L.dt_hsdp_post_backward(self._h, _ptr_array(flat), _size_array(numels), nt, _ptr_array(fused),
+        _check(self._lib.dt_hsdp_post_backward(self._h, _ptr_array(flat), _size_array(numels), nt, _ptr_array(fused),
                                         _stream_handle(producer)))
 
     def finish(self, consumer=None) -> None:
-        _check(_L.dt_hsdp_finish(self._h, _stream_handle(consumer)))
+        _check(self._lib.dt_hsdp_finish(self._h, _stream_handle(consumer)))
         self._stash = []
 
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            _L.dt_hsdp_destroy(h)
-            self._h = ctypes.c_void_p()
+            self._lib.dt_hsdp_destroy(h)
+            self._h = None
 
 
 def shard_views(fused: torch.Tensor, numels: Sequence[int], shard: int) -> List[torch.Tensor]:
