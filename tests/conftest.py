@@ -9,4 +9,4 @@ for p in (ROOT, TESTS):
 
 
 def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (runs on the GPU box)")
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU")
