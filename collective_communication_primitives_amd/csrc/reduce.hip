@@ -54,15 +54,17 @@ __global__ __launch_bounds__(kBlock) void k_reduce_vec(ReduceArgs a) {
 }
 
 // --------------------------------------------------------- ReduceScatter --
-// grid.x covers a.count vectors of one chunk in tiles of kBlock*U; grid.y =
+// grid.x covers a.count vectors of one chunk in tiles of BLOCK*U; grid.y =
 // output chunk.  Buffer instructions: one resource per rank for the tile's
 // range (the same lane offsets serve all P ranks), non-temporal loads and
 // device-scope stores; the resource range cuts off the last tile.  Measured
 // against the same kernel with 64-bit global addressing: 2-3% faster for
-// P=8 bf16 at 16 MiB per chunk.
-template <int DT, int OP, int PMAX, bool EXACT, int U>
-__global__ __launch_bounds__(kBlock) void k_reduce_scatter_vec(ReduceArgs a) {
-    constexpr uint64_t kTileVecs = uint64_t(kBlock) * U;
+// P=8 bf16 at 16 MiB per chunk.  BLOCK threads x U vectors per tile: for
+// P >= 8 the tile is spread over 512 threads with one vector each, 1.3%
+// faster than 256 threads with two.
+template <int DT, int OP, int PMAX, bool EXACT, int BLOCK, int U>
+__global__ __launch_bounds__(BLOCK) void k_reduce_scatter_vec(ReduceArgs a) {
+    constexpr uint64_t kTileVecs = uint64_t(BLOCK) * U;
     const uint64_t chunk = blockIdx.y;
     const uint64_t t0 = uint64_t(blockIdx.x) * kTileVecs;       // < a.count by the grid
     const uint64_t left = a.count - t0;
@@ -76,12 +78,12 @@ __global__ __launch_bounds__(kBlock) void k_reduce_scatter_vec(ReduceArgs a) {
         if (r < nr) {
             const rsrc_t in = make_rsrc(static_cast<const char*>(a.src[r]) + in_off, bytes);
 #pragma unroll
-            for (int u = 0; u < U; u++) x[u][r] = bload16<kPolNT>(in, lane + u * (kBlock * 16));
+            for (int u = 0; u < U; u++) x[u][r] = bload16<kPolNT>(in, lane + u * (BLOCK * 16));
         }
     }
     const rsrc_t out = make_rsrc(static_cast<char*>(a.dst[chunk]) + t0 * 16, bytes);
 #pragma unroll
-    for (int u = 0; u < U; u++) bstore16<kPolDevice>(out, lane + u * (kBlock * 16), fold_vec<DT, OP, PMAX>(x[u], nr));
+    for (int u = 0; u < U; u++) bstore16<kPolDevice>(out, lane + u * (BLOCK * 16), fold_vec<DT, OP, PMAX>(x[u], nr));
 }
 
 // Element-wise path for ragged tails and unaligned buffers.  Elements
@@ -289,11 +291,14 @@ hipError_t reduce_vec_p(const ReduceArgs& a, hipStream_t s) {
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
     const bool exact = a.nranks == PMAX;
     if (a.rs) {
+        // same tile (kBlock*URS vectors); P >= 8 spreads it over 512 threads, one vector each
+        constexpr int RB = PMAX >= 8 ? kBlock * URS : kBlock;
+        constexpr int RU = PMAX >= 8 ? 1 : URS;
         const dim3 grid(unsigned(blocks), unsigned(a.nranks));
         if (exact)
-            k_reduce_scatter_vec<DT, OP, PMAX, true, URS><<<grid, kBlock, 0, s>>>(a);
+            k_reduce_scatter_vec<DT, OP, PMAX, true, RB, RU><<<grid, RB, 0, s>>>(a);
         else
-            k_reduce_scatter_vec<DT, OP, PMAX, false, URS><<<grid, kBlock, 0, s>>>(a);
+            k_reduce_scatter_vec<DT, OP, PMAX, false, RB, RU><<<grid, RB, 0, s>>>(a);
     } else {
         if (exact)
             k_reduce_vec<DT, OP, PMAX, true, UAR><<<unsigned(blocks), kBlock, 0, s>>>(a);

@@ -203,7 +203,9 @@ static void check_bucket(hipStream_t s) {
     for (int r = 0; r < P; r++) free(flat[r]);
 }
 
-/* barrier, P=16, 1000 generations in one launch: windows against the model */
+/* barrier, P=16, 1000 generations in one launch: windows against the model.
+ * The packed layout (a plain launch): this program runs beside another
+ * process on the GPU, where the runtime may refuse a cooperative launch. */
 static void check_barrier(hipStream_t s) {
     enum { P = 16 };
     int32_t* win[P];
@@ -214,7 +216,7 @@ static void check_barrier(hipStream_t s) {
         win[r] = (int32_t*)dev(P * 4);
         HIP_OK(hipMemset(win[r], 0, P * 4));
     }
-    DT_OK_(dt_barrier(win, P, 1, 1000, status, 0, DT_BARRIER_SPREAD, s));
+    DT_OK_(dt_barrier(win, P, 1, 1000, status, 0, DT_BARRIER_PACKED, s));
     HIP_OK(hipStreamSynchronize(s));
     int32_t st = -1;
     HIP_OK(hipMemcpy(&st, status, 4, hipMemcpyDeviceToHost));
