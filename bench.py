@@ -180,8 +180,9 @@ def graph_time_us(torch, fn, per_graph: int = 20, replays: int = 5) -> float:
 
 def sweep(dt, torch, steps: int, warmup: int):
     """fp32 one-shot AllReduce, P=16, per-rank sizes 4 KiB .. 1 GiB (x4).
-    Each point is timed two ways: eager launches bracketed by events (what a
-    Python caller sees, host enqueue included) and graph replay (GPU time per
+    Each point is timed three ways: eager launches bracketed by events (what a
+    Python caller sees, host enqueue included), a loop of one prepared call
+    (marshalled once) between two events, and graph replay (GPU time per
     launch).  The alpha-beta fit T(S) = alpha + 2*P*S / B_eff (weights 1/T^2)
     uses the graph times."""
     import numpy as np
@@ -198,11 +199,21 @@ def sweep(dt, torch, steps: int, warmup: int):
         evs = time_launches(lambda: dt.dt_allreduce(xs, ys), steps, stream)
         torch.cuda.synchronize()
         eager_us = statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3
+        prepared = dt.prepare(dt.dt_allreduce, xs, ys)   # marshalled once: the loop pays the C call only
+        a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(steps):
+            prepared()
+        b0.record(stream)
+        torch.cuda.synchronize()
+        prepared_us = a0.elapsed_time(b0) / steps * 1e3
+        del prepared
         per_graph = 20 if nbytes <= (16 << 20) else 4
         us = graph_time_us(torch, lambda: dt.dt_allreduce(xs, ys), per_graph=per_graph, replays=5)
         hbm = 2 * p * nbytes / (us * 1e-6) / 1e9
         busbw = nbytes / (us * 1e-6) * 2 * (p - 1) / p / 1e9
         rows.append({"bytes_per_rank": nbytes, "us": round(us, 3), "eager_us": round(eager_us, 3),
+                     "prepared_loop_us": round(prepared_us, 3),
                      "hbm_GBps": round(hbm, 1), "busbw_GBps": round(busbw, 1),
                      "frac_of_peak": round(hbm / HBM_PEAK_GBPS, 4)})
         print(json.dumps({"sweep": rows[-1]}), flush=True)

@@ -1,6 +1,7 @@
 """GPU: the binding refuses tensors a kernel must never see -- host tensors,
 non-contiguous views, mixed dtypes, windows off the device -- before any
 pointer reaches the C ABI."""
+import numpy as np
 import pytest
 import torch
 
@@ -40,3 +41,41 @@ def test_barrier_windows_on_the_host_are_refused(dt):
         dt.dt_barrier([w.cuda() for w in windows], torch.zeros(1, dtype=torch.int32), 1)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
+
+
+def test_prepared_calls_follow_the_buffers(dt):
+    """prepare() marshals once; every call enqueues the same collective on the
+    current buffers' contents, on any stream, and matches the oracle."""
+    import oracle
+    import synth
+    from gpu_util import compare, note, to_np
+    orc = oracle.get()
+    p, n = 8, 8 * 1001
+    note("prepared allreduce / reduce_scatter / all_gather")
+    xs = synth.uniform_ranks(p, n, seed=11, device="cuda")
+    ys = [torch.empty_like(x) for x in xs]
+    shards = [torch.empty(n // p, device="cuda") for _ in range(p)]
+    full = [torch.empty(n, device="cuda") for _ in range(p)]
+    ar = dt.prepare(dt.dt_allreduce, xs, ys, op="max")
+    rs = dt.prepare(dt.dt_reduce_scatter, xs, shards)
+    ag = dt.prepare(dt.dt_all_gather, shards, full)
+    side = torch.cuda.Stream()
+    for it in range(3):
+        for x, v in zip(xs, synth.uniform_ranks(p, n, seed=20 + it, device="cuda")):
+            x.copy_(v)                          # new contents, same buffers
+        ar()
+        side.wait_stream(torch.cuda.current_stream())
+        rs(stream=side)
+        ag(stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        host = [to_np(x) for x in xs]
+        want_ar = orc.allreduce(host, "max")
+        want_rs = orc.reduce_scatter(host, "sum")
+        cat = np.concatenate(want_rs)
+        for q in range(p):
+            compare(to_np(ys[q]), want_ar[q], f"pass {it} AR rank {q}")
+            compare(to_np(shards[q]), want_rs[q], f"pass {it} RS rank {q}")
+            compare(to_np(full[q]), cat, f"pass {it} AG rank {q}")
+    with pytest.raises(ValueError):
+        dt.prepare(dt.dt_allreduce, xs, ys, async_op=True)
