@@ -143,7 +143,10 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
                               size_t bucket_bytes, void* const* bucket_ws, dt_dtype dtype, dt_op op,
                               hipStream_t stream);
 
-/* Where the ranks of a barrier launch run. */
+/* Where the ranks of a barrier launch run.  The spread layout needs a
+ * cooperative launch, which the HIP runtime may refuse (DT_ERR_HIP, with its
+ * message in dt_last_error) while another process shares the GPU; the
+ * packed layout is an ordinary launch and always runs. */
 typedef enum {
     DT_BARRIER_PACKED = 0, /* one workgroup, one 64-wide wave per rank: always co-resident, plain launch */
     DT_BARRIER_SPREAD = 1  /* one workgroup per rank on different CUs, cooperative launch */
