@@ -26,9 +26,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // non-temporal hint is chosen per kernel from measurements on the MI355X
 // (1.1 GiB working sets, beyond the Infinity Cache): with reads dominating
 // (P-to-1 fold), non-temporal loads and device-scope stores are fastest; with
-// writes dominating (1-to-P fan-out), plain loads and non-temporal
-// device-scope stores; for the balanced P-to-P fold and for 1-to-1 copies,
-// both non-temporal.
+// writes dominating (1-to-P fan-out), plain loads and non-temporal stores;
+// for the balanced P-to-P fold and for 1-to-1 copies, both non-temporal.
 __device__ __forceinline__ u32x4 load16(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -135,9 +134,6 @@ template <int DT>
 struct Elems {
     static constexpr int value = DT == kBF16 ? 8 : 4;
 };
-
-template <int DT>
-constexpr size_t elem_bytes() { return DT == kBF16 ? 2 : 4; }
 
 // Fold P vectors (x[0..P-1]) element-wise in rank order.  NR = live ranks
 // (runtime, NR <= P); with NR == P the branches fold away.

@@ -100,14 +100,12 @@ __global__ __launch_bounds__(kBlock) void k_reduce_elems(ReduceArgs a) {
             fold_elem<DT, OP>(a.src, nr, in_base + e, a.dst[chunk], e);
         } else {
             fold_elem<DT, OP>(a.src, nr, e, a.dst[0], e);
-            const size_t es = elem_bytes<DT>();
             for (int q = 1; q < nr; q++) {
                 if constexpr (DT == kBF16)
                     static_cast<uint16_t*>(a.dst[q])[e] = static_cast<const uint16_t*>(a.dst[0])[e];
                 else
                     static_cast<uint32_t*>(a.dst[q])[e] = static_cast<const uint32_t*>(a.dst[0])[e];
             }
-            (void)es;
         }
     }
 }
