@@ -162,32 +162,83 @@ dt_status reduce_scatter_segments(const std::vector<std::vector<const void*>>& s
     return flush();
 }
 
-// Fan-out of `nsources` pieces (default: nranks): piece r (counts[r]
-// elements at src[r]) goes to table[r*nranks + q] for every q.
-dt_status fan_out(const void* const* src, const size_t* counts, void* const* table, int nranks, size_t es,
-                  hipStream_t stream, const char* what, int nsources = -1) {
-    if (nsources < 0) nsources = nranks;
+// One fan-out launch over pieces k < n: piece k is bytes[k] at src[k], going to
+// dst[k][q] for every q (host arrays, P entries each).
+dt_status fan_out_launch(const void* const* src, const uint64_t* bytes, void* const* const* dst, int n,
+                         int nranks, bool touch_first, hipStream_t stream, const char* what) {
     dt::GatherArgs a = {};
     a.nranks = nranks;
     uint64_t tiles = 0;
-    for (int r = 0; r < nsources; r++) {
-        const uint64_t bytes = uint64_t(counts[r]) * es;
-        a.src[r] = src[r];
-        a.bytes[r] = bytes;
-        a.tile_start[r] = uint32_t(tiles);
-        bool al = aligned16(src[r]);
+    for (int k = 0; k < n; k++) {
+        a.src[k] = src[k];
+        a.bytes[k] = bytes[k];
+        a.tile_start[k] = uint32_t(tiles);
+        bool al = aligned16(src[k]);
         for (int q = 0; q < nranks; q++) {
-            void* d = bytes ? table[size_t(r) * nranks + q] : nullptr;
-            a.dst[r * nranks + q] = d;
+            void* d = bytes[k] ? dst[k][q] : nullptr;
+            a.dst[k * nranks + q] = d;
             al = al && aligned16(d);
         }
-        if (al) a.aligned |= 1u << r;
-        tiles += (bytes + dt::kGatherTileBytes - 1) / dt::kGatherTileBytes;
+        if (al) a.aligned |= 1u << k;
+        tiles += (bytes[k] + dt::kGatherTileBytes - 1) / dt::kGatherTileBytes;
         if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "fan-out too large for one launch");
     }
-    for (int r = nsources; r <= nranks; r++) a.tile_start[r] = uint32_t(tiles);
+    for (int k = n; k <= nranks; k++) a.tile_start[k] = uint32_t(tiles);
     if (tiles == 0) return DT_OK;
+    dt_status st = DT_OK;
+    if (touch_first && (st = check_hip(dt::launch_gather_touch(a, uint32_t(tiles), stream), what)) != DT_OK) return st;
     return check_hip(dt::launch_gather(a, uint32_t(tiles), stream), what);
+}
+
+// Fan-out of `nsources` pieces (default: nranks): piece r (counts[r]
+// elements at src[r]) goes to table[r*nranks + q] for every q.  Sources up to
+// kFanOutDirectBytes go in one launch.  Larger ones go window by window: a
+// read pass pulls the window's source bytes into the Infinity Cache, then the
+// window fans out reading from there, so HBM serves the window's reads and its
+// writes in two separate phases instead of interleaved.
+dt_status fan_out(const void* const* src, const size_t* counts, void* const* table, int nranks, size_t es,
+                  hipStream_t stream, const char* what, int nsources = -1) {
+    if (nsources < 0) nsources = nranks;
+    uint64_t total = 0;
+    for (int r = 0; r < nsources; r++) total += uint64_t(counts[r]) * es;
+    const void* wsrc[dt::kMaxRanksHost];
+    uint64_t wbytes[dt::kMaxRanksHost];
+    void* wdst[dt::kMaxRanksHost][dt::kMaxRanksHost];
+    void* const* wdst_rows[dt::kMaxRanksHost];
+    for (int k = 0; k < dt::kMaxRanksHost; k++) wdst_rows[k] = wdst[k];
+    if (total <= dt::kFanOutDirectBytes) {
+        for (int r = 0; r < nsources; r++) {
+            wsrc[r] = src[r];
+            wbytes[r] = uint64_t(counts[r]) * es;
+            for (int q = 0; q < nranks; q++) wdst[r][q] = table[size_t(r) * nranks + q];
+        }
+        return fan_out_launch(wsrc, wbytes, wdst_rows, nsources, nranks, false, stream, what);
+    }
+    int n = 0;
+    uint64_t fill = 0;
+    dt_status st = DT_OK;
+    for (int r = 0; r < nsources; r++) {
+        const uint64_t bytes = uint64_t(counts[r]) * es;
+        uint64_t off = 0;
+        while (off < bytes) {
+            uint64_t take = std::min(bytes - off, dt::kFanOutWindowBytes - fill);
+            if (off + take < bytes) take &= ~uint64_t(15);  // cut inside a source on 16-byte boundaries
+            if (take == 0) take = std::min<uint64_t>(bytes - off, 16);
+            wsrc[n] = cptr(src[r]) + off;
+            wbytes[n] = take;
+            for (int q = 0; q < nranks; q++) wdst[n][q] = static_cast<char*>(table[size_t(r) * nranks + q]) + off;
+            n++;
+            off += take;
+            fill += take;
+            if (fill >= dt::kFanOutWindowBytes || n == nranks) {
+                if ((st = fan_out_launch(wsrc, wbytes, wdst_rows, n, nranks, true, stream, what)) != DT_OK) return st;
+                n = 0;
+                fill = 0;
+            }
+        }
+    }
+    if (n > 0) return fan_out_launch(wsrc, wbytes, wdst_rows, n, nranks, true, stream, what);
+    return DT_OK;
 }
 
 // Independent 1:1 byte copies, in as few launches as the argument block allows.

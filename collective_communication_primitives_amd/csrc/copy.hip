@@ -62,6 +62,30 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
     }
 }
 
+// Read pass over a gather table's source tiles: plain loads, which leave the
+// bytes in the Infinity Cache for the fan-out launched right after.  The
+// empty asm keeps the loads; nothing is stored.
+__global__ __launch_bounds__(kBlock) void k_gather_touch(GatherArgs a) {
+    constexpr int U = kGatherU;
+    constexpr uint64_t kTile = uint64_t(U) * kBlock * 16;
+    const uint32_t b = blockIdx.x;
+    const int nr = a.nranks;
+    int r = 0;
+    while (r + 1 < nr && a.tile_start[r + 1] <= b) r++;
+    if (!((a.aligned >> r) & 1u)) return;
+    const char* src = static_cast<const char*>(a.src[r]);
+    const uint64_t b0 = uint64_t(b - a.tile_start[r]) * kTile;
+    const uint64_t v1 = min(a.bytes[r], b0 + kTile) / 16;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
+        if (v < v1) {
+            const u32x4 x = load16_h<false>(src + v * 16);
+            asm volatile("" ::"v"(x));
+        }
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void k_all_to_all(AllToAllArgs a) {
     const uint32_t b = blockIdx.x;
     const int nr = a.nranks;
@@ -241,6 +265,12 @@ hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     return p <= 1 ? gather_pu<1, kGatherU>(a, tiles, s) : p <= 2 ? gather_pu<2, kGatherU>(a, tiles, s)
            : p <= 4 ? gather_pu<4, kGatherU>(a, tiles, s) : p <= 8 ? gather_pu<8, kGatherU>(a, tiles, s)
            : gather_pu<16, kGatherU>(a, tiles, s);
+}
+
+hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
+    if (tiles == 0) return hipSuccess;
+    k_gather_touch<<<tiles, kBlock, 0, s>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t s) {

@@ -239,8 +239,35 @@ hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, 
     return hipSuccess;
 }
 
+// Every gather piece launched since the last reset: (source, bytes, first
+// destination), for the coverage check of the windowed fan-out.
+struct GatherPiece {
+    const char* src;
+    uint64_t bytes;
+    const char* dst0;
+};
+std::vector<GatherPiece> g_gather_pieces;
+int g_touch_launches = 0;
+
+hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t) {
+    g_launches++;
+    g_touch_launches++;
+    std::vector<uint64_t> want;
+    for (int r = 0; r < a.nranks; r++) want.push_back(ceil_div(a.bytes[r], kGatherTileBytes));
+    check_tiles(a.tile_start, want, tiles, "gather touch");
+    for (int r = 0; r < a.nranks; r++) {
+        touch(a.src[r], 0, a.bytes[r], false, "gather touch read");
+        if ((a.aligned >> r) & 1u) CHECK(al16(a.src[r]), "gather touch: unaligned source");
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t) {
     g_launches++;
+    for (int r = 0; r < a.nranks; r++)
+        if (a.bytes[r])
+            g_gather_pieces.push_back(GatherPiece{static_cast<const char*>(a.src[r]), a.bytes[r],
+                                                  static_cast<const char*>(a.dst[r * a.nranks])});
     std::vector<uint64_t> want;
     for (int r = 0; r < a.nranks; r++) want.push_back(ceil_div(a.bytes[r], kGatherTileBytes));
     check_tiles(a.tile_start, want, tiles, "gather");
@@ -590,8 +617,62 @@ void validation() {
 
 }  // namespace
 
+// The windowed fan-out of large sources: fake device ranges (never touched)
+// of a few hundred MiB, odd sizes, one empty rank.  Every source byte must be
+// launched exactly once, at the matching destination offset, with a read
+// pass before each window.
+void big_fan_out() {
+    using dt::g_gather_pieces;
+    using dt::g_touch_launches;
+    using dt::GatherPiece;
+    g_bufs.clear();
+    const int p = 6;
+    const size_t counts[p] = {3, (size_t(40) << 20) + 1, 7, (size_t(100) << 20) + 3, 0, (size_t(35) << 20) + 5};
+    size_t total = 0;
+    for (int r = 0; r < p; r++) total += counts[r];
+    const size_t es = 2;  // bf16
+    char* base = reinterpret_cast<char*>(uintptr_t(1) << 44);  // a fake, 16-byte aligned address range
+    const void* send[p];
+    void* recv[p];
+    for (int r = 0; r < p; r++) {
+        send[r] = counts[r] ? base + (uint64_t(r) << 32) : nullptr;
+        if (counts[r]) reg(send[r], counts[r] * es, false);
+        recv[r] = base + (uint64_t(16 + r) << 32);
+        reg(recv[r], total * es, true);
+    }
+    g_gather_pieces.clear();
+    g_touch_launches = 0;
+    expect(dt_all_gather(send, recv, p, counts, 0, DT_BFLOAT16, nullptr), DT_OK, "big all_gather");
+    CHECK(g_touch_launches > 1, "big all_gather: %d read passes", g_touch_launches);
+    uint64_t at = 0;  // destination offset of rank r's piece
+    for (int r = 0; r < p; r++) {
+        const char* s0 = static_cast<const char*>(send[r]);
+        uint64_t covered = 0;
+        for (const GatherPiece& g : g_gather_pieces) {
+            if (!s0 || g.src < s0 || g.src >= s0 + counts[r] * es) continue;
+            CHECK(g.src == s0 + covered, "big all_gather: rank %d piece out of order", r);
+            CHECK(g.dst0 == static_cast<const char*>(recv[0]) + at + covered, "big all_gather: rank %d offset", r);
+            covered += g.bytes;
+        }
+        CHECK(covered == counts[r] * es, "big all_gather: rank %d covered %llu of %llu bytes", r,
+              (unsigned long long)covered, (unsigned long long)(counts[r] * es));
+        at += counts[r] * es;
+    }
+    // a large broadcast goes through the same windows
+    g_touch_launches = 0;
+    void* out[p];
+    for (int q = 0; q < p; q++) out[q] = recv[q];
+    const size_t root_count = size_t(150) << 20;  // 300 MiB of bf16
+    const char* root = base + (uint64_t(40) << 32);
+    reg(root, root_count * es, false);
+    expect(dt_broadcast(root, out, p, root_count, DT_BFLOAT16, nullptr), DT_OK, "big broadcast");
+    CHECK(g_touch_launches > 1, "big broadcast: %d read passes", g_touch_launches);
+    g_bufs.clear();
+}
+
 int main() {
     validation();
+    big_fan_out();
     reductions();
     copies();
     buckets();

@@ -95,6 +95,48 @@ def test_uneven_all_gather_full_size(dt, orc):
         compare(to_np(outs[q]), want, f"rank {q}")
 
 
+def test_all_gather_windowed_ragged_sources(dt, orc):
+    """Sources totalling more than 256 MiB go out window by window: odd bf16
+    counts (windows cut inside sources and pieces end mid-vector), an empty
+    source and one source 2 bytes off 16-byte alignment."""
+    mi = 1 << 20
+    counts = [3, 40 * mi + 1, 7, 100 * mi + 3, 0, 35 * mi + 5]
+    note(f"all_gather windowed bf16 counts={counts}")
+    xs = []
+    for r, c in enumerate(counts):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(500 + r)
+        bits16 = torch.randint(-2 ** 15, 2 ** 15, (c,), generator=g, device="cuda", dtype=torch.int32).to(torch.int16)
+        if r == 3:
+            buf = Guarded(c, torch.bfloat16, offset_elems=1)
+            buf.t.view(torch.int16).copy_(bits16)
+            xs.append(buf.t)
+        else:
+            xs.append(bits16.view(torch.bfloat16))
+    total = sum(counts)
+    outs = [Guarded(total, torch.bfloat16).poison() for _ in counts]
+    dt.dt_all_gather(xs, [o.t for o in outs])
+    torch.cuda.synchronize()
+    want = orc.all_gather([to_np(x) for x in xs])[0]
+    for q, o in enumerate(outs):
+        o.check()
+        np.testing.assert_array_equal(to_np(o.t), want, f"rank {q}")
+
+
+def test_broadcast_windowed(dt, orc):
+    """A 300 MiB root (beyond 256 MiB: windowed) to 3 ranks."""
+    n = 75 * (1 << 20) + 3
+    note(f"broadcast windowed int32 n={n}")
+    root = torch.randint(-2 ** 31, 2 ** 31, (n,), dtype=torch.int64, device="cuda").to(torch.int32)
+    outs = [Guarded(n, torch.int32).poison() for _ in range(3)]
+    dt.dt_broadcast(root, [o.t for o in outs])
+    torch.cuda.synchronize()
+    want = orc.broadcast(to_np(root), 3)
+    for q, o in enumerate(outs):
+        o.check()
+        np.testing.assert_array_equal(to_np(o.t), want[q], f"rank {q}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
 @pytest.mark.parametrize("p,hi,seed", [(1, 9, 0), (2, 5, 1), (3, 100, 2), (8, 40, 3), (16, 20, 4), (8, 0, 5)])
 def test_all_to_all(dt, orc, dtype, p, hi, seed):

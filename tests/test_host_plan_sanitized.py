@@ -57,8 +57,11 @@ def test_planning_code_is_clean(check_obj, tmp_path):
 
 MUTANTS = {
     # the gather grid drops the partial last tile of every source
-    "gather_drops_partial_tile": ("tiles += (bytes + dt::kGatherTileBytes - 1) / dt::kGatherTileBytes;",
-                                  "tiles += bytes / dt::kGatherTileBytes;"),
+    "gather_drops_partial_tile": ("tiles += (bytes[k] + dt::kGatherTileBytes - 1) / dt::kGatherTileBytes;",
+                                  "tiles += bytes[k] / dt::kGatherTileBytes;"),
+    # the windowed fan-out of large sources skips 16 bytes after every piece
+    "fan_out_window_skips_bytes": ("            off += take;\n            fill += take;",
+                                   "            off += take + 16;\n            fill += take;"),
     # bucket pieces start one element late: the last piece runs past its tensor
     "bucket_piece_off_by_one": (
         "ref.ptr[r] = static_cast<char*>(grads[size_t(r) * ntensors + p.tensor]) + p.offset * es;",
