@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
         }
 #pragma unroll
         for (int q = 0; q < PMAX; q++) {
-            if (q < nr) {
+            if (q < nr && dsts[q] != src) {  // an in-place piece already sits in its own slot
                 char* dst = static_cast<char*>(dsts[q]);
 #pragma unroll
                 for (int u = 0; u < U; u++) {
@@ -52,12 +52,14 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
         const uint64_t t = v1 * 16 + threadIdx.x;  // ragged end: fewer than 16 bytes
         if (t < b1) {
             const char c = src[t];
-            for (int q = 0; q < nr; q++) static_cast<char*>(dsts[q])[t] = c;
+            for (int q = 0; q < nr; q++)
+                if (dsts[q] != src) static_cast<char*>(dsts[q])[t] = c;
         }
     } else {
         for (uint64_t t = b0 + threadIdx.x; t < b1; t += kBlock) {
             const char c = src[t];
-            for (int q = 0; q < nr; q++) static_cast<char*>(dsts[q])[t] = c;
+            for (int q = 0; q < nr; q++)
+                if (dsts[q] != src) static_cast<char*>(dsts[q])[t] = c;
         }
     }
 }

@@ -670,9 +670,70 @@ void big_fan_out() {
     g_bufs.clear();
 }
 
+// The two-shot AllReduce (P >= 8; 128 MiB, or 32 MiB at P >= 16, up to
+// 256 MiB per rank): fake device ranges.  The ReduceScatter must write chunk
+// r of recv[r] only, and the gather must fan chunk r of recv[r] out to chunk
+// r of every output.  Sizes outside the window keep the one-shot launch.
+void two_shot() {
+    using dt::g_gather_pieces;
+    using dt::GatherPiece;
+    struct Case {
+        int p;
+        dt_dtype dtype;
+        size_t count;
+        bool in_place, two;
+    };
+    const Case cases[] = {
+        {8, DT_BFLOAT16, size_t(64) << 20, false, true},           // 128 MiB per rank
+        {8, DT_BFLOAT16, size_t(64) << 20, true, true},
+        {16, DT_FLOAT32, size_t(8) << 20, false, true},            // 32 MiB
+        {16, DT_FLOAT32, size_t(64) << 20, true, true},            // 256 MiB
+        {12, DT_INT32, size_t(48) << 20, false, true},             // 192 MiB
+        {8, DT_FLOAT32, size_t(16) << 20, false, false},           // 64 MiB at P=8
+        {8, DT_BFLOAT16, (size_t(64) << 20) + 8, false, false},    // not a multiple of P vectors
+        {16, DT_FLOAT32, (size_t(64) << 20) + 64, false, false},   // just beyond 256 MiB
+        {4, DT_FLOAT32, size_t(32) << 20, false, false},           // P=4
+    };
+    char* base = reinterpret_cast<char*>(uintptr_t(1) << 45);  // fake, never dereferenced
+    for (const Case& c : cases) {
+        g_bufs.clear();
+        const size_t es = esize(c.dtype), bytes = c.count * es;
+        const void* send[16];
+        void* recv[16];
+        for (int r = 0; r < c.p; r++) {
+            recv[r] = base + (uint64_t(r) << 33);
+            reg(recv[r], bytes, true);
+            if (c.in_place) {
+                send[r] = recv[r];
+            } else {
+                send[r] = base + (uint64_t(32 + r) << 33);
+                reg(send[r], bytes, false);
+            }
+        }
+        g_gather_pieces.clear();
+        const long before = g_launches;
+        expect(dt_allreduce(send, recv, c.p, c.count, c.dtype, DT_SUM, nullptr), DT_OK, "two-shot allreduce");
+        if (!c.two) {
+            CHECK(g_gather_pieces.empty(), "allreduce of %zu bytes per rank at P=%d took the two-shot form", bytes, c.p);
+            continue;
+        }
+        CHECK(g_launches - before == 2, "two-shot allreduce: %ld launches", g_launches - before);
+        const uint64_t cb = bytes / c.p;
+        CHECK(int(g_gather_pieces.size()) == c.p, "two-shot allreduce: %zu gather pieces", g_gather_pieces.size());
+        for (int r = 0; r < c.p; r++) {
+            const GatherPiece& g = g_gather_pieces[r];
+            CHECK(g.src == static_cast<const char*>(recv[r]) + r * cb && g.bytes == cb &&
+                      g.dst0 == static_cast<const char*>(recv[0]) + r * cb,
+                  "two-shot allreduce: piece %d", r);
+        }
+    }
+    g_bufs.clear();
+}
+
 int main() {
     validation();
     big_fan_out();
+    two_shot();
     reductions();
     copies();
     buckets();

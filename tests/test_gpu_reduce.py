@@ -87,6 +87,32 @@ def test_allreduce_full_size_fp32_and_int32(dt, orc):
                 compare(to_np(ys[q]), want[q], f"{dtype} seed {seed} rank {q}")
 
 
+@pytest.mark.parametrize("p,dtype,n,op,in_place", [
+    (8, "bf16", 64 << 20, "sum", False),      # 128 MiB per rank: the two-shot form
+    (8, "bf16", 64 << 20, "sum", True),
+    (16, "f32", 8 << 20, "avg", False),       # 32 MiB
+    (8, "i32", 32 << 20, "max", True),        # 128 MiB
+    (9, "f32", 33554448, "min", False),       # 128 MiB + 64 B, a multiple of 9 vectors; nine of sixteen slots
+    (8, "f32", (32 << 20) + 4, "sum", False), # 128 MiB + 16 B, not a multiple of 8 vectors: one-shot
+])
+def test_allreduce_two_shot_window(dt, orc, p, dtype, n, op, in_place):
+    """AllReduce sizes where the library runs a ReduceScatter into each
+    output's own chunk and then an in-place AllGather.  Rank 0's output is
+    compared with the oracle element by element; every other rank's output
+    must equal rank 0's bit for bit."""
+    note(f"allreduce two-shot window P={p} {dtype} n={n} {op} in_place={in_place}")
+    xs = rank_inputs(dtype, p, n, seed=40 + p)
+    host = [to_np(x) for x in xs]
+    ys = xs if in_place else [torch.empty_like(x) for x in xs]
+    dt.dt_allreduce(xs, ys, op=op)
+    torch.cuda.synchronize()
+    want = orc.allreduce(host, op)[0]
+    compare(to_np(ys[0]), want, f"rank 0")
+    bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
+    for q in range(1, p):
+        assert torch.equal(bits(ys[q]), bits(ys[0])), f"rank {q} differs from rank 0"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
 @pytest.mark.parametrize("op", ["sum", "max", "min"])
 @pytest.mark.parametrize("p,m", [(1, 5), (2, 4096), (3, 1001), (8, 8), (8, 4099), (16, 640)])

@@ -66,6 +66,9 @@ MUTANTS = {
     "bucket_piece_off_by_one": (
         "ref.ptr[r] = static_cast<char*>(grads[size_t(r) * ntensors + p.tensor]) + p.offset * es;",
         "ref.ptr[r] = static_cast<char*>(grads[size_t(r) * ntensors + p.tensor]) + (p.offset + 1) * es;"),
+    # the two-shot AllReduce writes its ReduceScatter chunks one chunk too far
+    "two_shot_chunk_offset": ("rs.dst[r] = static_cast<char*>(recv[r]) + r * cb;",
+                              "rs.dst[r] = static_cast<char*>(recv[r]) + (r + 1) * cb;"),
     # one run too many for the shard-dimension exchange
     "dims_extra_run": ("a.nruns = uint64_t(rows) * P;", "a.nruns = uint64_t(rows) * P + 1;"),
     # every piece claimed 16-byte aligned
