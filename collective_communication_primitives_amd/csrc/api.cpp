@@ -18,7 +18,7 @@
 static_assert(sizeof(dt::ReduceArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::PieceArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::GatherArgs) <= 4096, "kernel arguments must stay below 4 KiB");
-static_assert(sizeof(dt::AllToAllArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+static_assert(sizeof(dt::AllToAllArgs) <= 8192, "all-to-all block table must stay well below the 64 KB verified");
 static_assert(sizeof(dt::ExchangeArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::SegReduceScatterArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::SegCopyArgs) <= 4096, "kernel arguments must stay below 4 KiB");
@@ -675,39 +675,46 @@ dt_status dt_all_to_all(const void* const* send, void* const* recv, int nranks, 
             if (r != q && col[q] > 0 && col[r] > 0 && recv[q] == recv[r])
                 return fail(DT_ERR_ARG, "recv[%d] equals recv[%d]", q, r);
         }
+    for (int s = 0; s < nranks * nranks; s++)
+        if (splits[s] > (size_t(1) << 40)) return fail(DT_ERR_ARG, "splits[%d]=%zu too large", s, splits[s]);
     const size_t es = esize_of(dtype);
     dt::AllToAllArgs a = {};
-    a.nranks = nranks;
     uint64_t tiles = 0;
-    for (int r = 0; r < nranks; r++) {
-        a.src[r] = send[r];
-        a.dst[r] = recv[r];
-    }
-    std::vector<uint64_t> recv_off(nranks, 0);  // running byte offsets down each column
-    for (int i = 0; i < nranks; i++) {
-        for (int j = 0; j < nranks; j++) {
-            const int s = i * nranks + j;
-            if (splits[s] > (size_t(1) << 40)) return fail(DT_ERR_ARG, "splits[%d]=%zu too large", s, splits[s]);
-            a.split[s] = splits[s] * es;
-            a.tile_start[s] = uint32_t(tiles);
-            tiles += (a.split[s] + dt::kCopyTileBytes - 1) / dt::kCopyTileBytes;
-            if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "all_to_all too large for one launch");
-        }
-    }
-    a.tile_start[nranks * nranks] = uint32_t(tiles);
+    auto flush = [&]() -> dt_status {
+        if (a.nblocks == 0) return DT_OK;
+        a.tile_start[a.nblocks] = uint32_t(tiles);
+        for (int k = a.nblocks + 1; k <= dt::kA2ABlocks; k++) a.tile_start[k] = UINT32_MAX;
+        for (int g = 0; g < dt::kA2ABlocks / dt::kA2AGroup; g++) a.group_start[g] = a.tile_start[g * dt::kA2AGroup];
+        const dt_status st = check_hip(dt::launch_all_to_all(a, uint32_t(tiles), stream), "all_to_all launch");
+        a = dt::AllToAllArgs{};
+        tiles = 0;
+        return st;
+    };
     // send offsets run along rows, receive offsets down columns
+    std::vector<uint64_t> recv_off(nranks, 0);
     for (int i = 0; i < nranks; i++) {
         uint64_t so = 0;
         for (int j = 0; j < nranks; j++) {
-            const int s = i * nranks + j;
-            const uint64_t ro = recv_off[j];
-            if (aligned16(cptr(send[i]) + so) && aligned16(cptr(recv[j]) + ro)) a.aligned[s >> 5] |= 1u << (s & 31);
-            so += a.split[s];
-            recv_off[j] += a.split[s];
+            const uint64_t bytes = uint64_t(splits[i * nranks + j]) * es;
+            if (bytes > 0) {
+                const uint64_t t = (bytes + dt::kCopyTileBytes - 1) / dt::kCopyTileBytes;  // <= 2^30
+                if (a.nblocks == dt::kA2ABlocks || tiles + t > 0x7FFFFFFFull) {
+                    const dt_status st = flush();
+                    if (st != DT_OK) return st;
+                }
+                const int k = a.nblocks++;
+                a.from[k] = cptr(send[i]) + so;
+                a.to[k] = static_cast<char*>(recv[j]) + recv_off[j];
+                a.bytes[k] = bytes;
+                a.tile_start[k] = uint32_t(tiles);
+                if (aligned16(a.from[k]) && aligned16(a.to[k])) a.aligned[k >> 6] |= 1ull << (k & 63);
+                tiles += t;
+            }
+            so += bytes;
+            recv_off[j] += bytes;
         }
     }
-    if (tiles == 0) return DT_OK;
-    return check_hip(dt::launch_all_to_all(a, uint32_t(tiles), stream), "all_to_all launch");
+    return flush();
 }
 
 dt_status dt_bucket_plan(const size_t* numels, int ntensors, size_t elem_size, size_t bucket_bytes, dt_piece* pieces,

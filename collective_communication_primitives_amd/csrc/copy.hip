@@ -88,28 +88,37 @@ __global__ __launch_bounds__(kBlock) void k_gather_touch(GatherArgs a) {
     }
 }
 
+// Block of tile b: the last k with tile_start[k] <= b (blocks are non-empty,
+// so the starts increase, and padding entries never qualify), and that start.
+// Two rounds of one batched scalar load each: the sixteen group starts, then
+// the sixteen starts of the group.
+__device__ __forceinline__ int a2a_block(const AllToAllArgs& a, uint32_t b, uint32_t& start) {
+    constexpr int G = kA2AGroup;
+    int g = 0;
+#pragma unroll
+    for (int k = 1; k < kA2ABlocks / G; k++) g += a.group_start[k] <= b ? 1 : 0;
+    const int g0 = G * g;
+    int s = g0;
+    start = a.group_start[g];
+#pragma unroll
+    for (int j = 1; j < G; j++) {
+        const uint32_t ts = a.tile_start[g0 + j];
+        const bool in = ts <= b;
+        s += in ? 1 : 0;
+        start = in ? ts : start;
+    }
+    return s;
+}
+
 __global__ __launch_bounds__(kBlock) void k_all_to_all(AllToAllArgs a) {
     const uint32_t b = blockIdx.x;
-    const int nr = a.nranks;
-    // largest block index s with tile_start[s] <= b; that block is non-empty
-    int lo = 0, hi = nr * nr;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (a.tile_start[mid] <= b)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    const int s = lo, i = s / nr, j = s - i * nr;
-    uint64_t send_off = 0;  // blocks i -> 0..j-1 precede i -> j in rank i's input
-    for (int jj = 0; jj < j; jj++) send_off += a.split[i * nr + jj];
-    uint64_t recv_off = 0;  // blocks 0..i-1 -> j precede i -> j in rank j's output
-    for (int ii = 0; ii < i; ii++) recv_off += a.split[ii * nr + j];
-    const char* src = static_cast<const char*>(a.src[i]) + send_off;
-    char* dst = static_cast<char*>(a.dst[j]) + recv_off;
-    const uint64_t b0 = uint64_t(b - a.tile_start[s]) * kCopyTileBytes;
-    const uint64_t b1 = min(a.split[s], b0 + kCopyTileBytes);
-    if ((a.aligned[s >> 5] >> (s & 31)) & 1u) {
+    uint32_t start;
+    const int k = a2a_block(a, b, start);
+    const char* src = static_cast<const char*>(a.from[k]);
+    char* dst = static_cast<char*>(a.to[k]);
+    const uint64_t b0 = uint64_t(b - start) * kCopyTileBytes;
+    const uint64_t b1 = min(a.bytes[k], b0 + kCopyTileBytes);
+    if ((a.aligned[k >> 6] >> (k & 63)) & 1ull) {
         const uint64_t v1 = b1 / 16;
         u32x4 x[kCopyU];
 #pragma unroll

@@ -115,14 +115,24 @@ struct DimsArgs {
     int dir;
 };
 
-// AllToAll: split[i*P+j] bytes travel from rank i to rank j.
+// AllToAll: block k of a launch copies bytes[k] from `from[k]` to `to[k]`.
+// The blocks are the non-empty i -> j blocks of the split matrix in (i, j)
+// order, with their byte offsets resolved on the host; kA2ABlocks covers a
+// full 16 x 16 matrix, so one launch serves any rank count.
+// A workgroup finds its block in two rounds: group_start[g] = tile_start[16 g]
+// gives the group of sixteen blocks, then that group's sixteen starts give the
+// block.  Entries past the last block hold UINT32_MAX (after tile_start
+// [nblocks], the tile total), so no comparison needs a bound.
+constexpr int kA2ABlocks = kMaxRanksHost * kMaxRanksHost;
+constexpr int kA2AGroup = 16;
 struct AllToAllArgs {
-    const void* src[kMaxRanksHost];
-    void* dst[kMaxRanksHost];
-    uint64_t split[kMaxRanksHost * kMaxRanksHost];
-    uint32_t tile_start[kMaxRanksHost * kMaxRanksHost + 1];
-    uint32_t aligned[kMaxRanksHost * kMaxRanksHost / 32];
-    int nranks;
+    const void* from[kA2ABlocks];
+    void* to[kA2ABlocks];
+    uint64_t bytes[kA2ABlocks];
+    uint32_t tile_start[kA2ABlocks + 1];
+    uint32_t group_start[kA2ABlocks / kA2AGroup];
+    uint64_t aligned[kA2ABlocks / 64];  // bit k: block k allows 16-byte vectors
+    int nblocks;
 };
 
 struct BarrierArgs {
@@ -143,7 +153,7 @@ struct ExchangeArgs {
 };
 
 // Tile sizes (bytes of one rank's data per workgroup).
-constexpr uint64_t kCopyTileBytes = 16384;   // all-to-all
+constexpr uint64_t kCopyTileBytes = 4096;    // all-to-all: one vector per thread
 constexpr int kGatherU = 2;                   // gather: 2 vectors per thread,
 constexpr uint64_t kGatherTileBytes = 8192;   // 8 KiB source tiles
 constexpr uint64_t kPieceTileVecs = 512;     // bucket pieces: 512 x 16 B

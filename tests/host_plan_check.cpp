@@ -283,26 +283,34 @@ hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t) {
     return hipSuccess;
 }
 
+struct A2ABlock {
+    const char* from;
+    const char* to;
+    uint64_t bytes;
+};
+std::vector<A2ABlock> g_a2a_blocks;  // every block of every all-to-all launch, in launch order
+
 hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t) {
     g_launches++;
-    const int p = a.nranks;
+    CHECK(a.nblocks >= 1 && a.nblocks <= kA2ABlocks, "all_to_all: %d blocks", a.nblocks);
     std::vector<uint64_t> want;
-    for (int s = 0; s < p * p; s++) want.push_back(ceil_div(a.split[s], kCopyTileBytes));
+    for (int k = 0; k < a.nblocks; k++) {
+        CHECK(a.bytes[k] > 0, "all_to_all: empty block %d", k);
+        want.push_back(ceil_div(a.bytes[k], kCopyTileBytes));
+    }
     check_tiles(a.tile_start, want, tiles, "all_to_all");
-    for (int i = 0; i < p; i++)
-        for (int j = 0; j < p; j++) {
-            const int s = i * p + j;
-            if (a.split[s] == 0) continue;
-            uint64_t send_off = 0, recv_off = 0;
-            for (int jj = 0; jj < j; jj++) send_off += a.split[i * p + jj];
-            for (int ii = 0; ii < i; ii++) recv_off += a.split[ii * p + j];
-            touch(a.src[i], send_off, a.split[s], false, "all_to_all read");
-            touch(a.dst[j], recv_off, a.split[s], true, "all_to_all write");
-            if ((a.aligned[s >> 5] >> (s & 31)) & 1u)
-                CHECK(al16(static_cast<const char*>(a.src[i]) + send_off) &&
-                          al16(static_cast<const char*>(a.dst[j]) + recv_off),
-                      "all_to_all: aligned flag on an unaligned block");
-        }
+    for (int k = a.nblocks + 1; k <= kA2ABlocks; k++)
+        CHECK(a.tile_start[k] == UINT32_MAX, "all_to_all: tile_start[%d] = %u past the last block", k, a.tile_start[k]);
+    for (int g = 0; g < kA2ABlocks / kA2AGroup; g++)
+        CHECK(a.group_start[g] == a.tile_start[g * kA2AGroup], "all_to_all: group_start[%d] = %u", g, a.group_start[g]);
+    for (int k = 0; k < a.nblocks; k++) {
+        touch(a.from[k], 0, a.bytes[k], false, "all_to_all read");
+        touch(a.to[k], 0, a.bytes[k], true, "all_to_all write");
+        if ((a.aligned[k >> 6] >> (k & 63)) & 1ull)
+            CHECK(al16(a.from[k]) && al16(a.to[k]), "all_to_all: aligned flag on an unaligned block");
+        g_a2a_blocks.push_back(A2ABlock{static_cast<const char*>(a.from[k]), static_cast<const char*>(a.to[k]),
+                                        a.bytes[k]});
+    }
     return hipSuccess;
 }
 
@@ -440,6 +448,8 @@ void reductions() {
 }
 
 void copies() {
+    using dt::A2ABlock;
+    using dt::g_a2a_blocks;
     for (int it = 0; it < 120; it++) {
         Pool pool;
         g_bufs.clear();
@@ -488,7 +498,27 @@ void copies() {
             a_send[r] = row[r] ? pool.get(row[r] * es, skew, false) : nullptr;
             a_recv[r] = col[r] ? pool.get(col[r] * es, skew, true) : nullptr;
         }
+        g_a2a_blocks.clear();
         expect(dt_all_to_all(a_send.data(), a_recv.data(), p, splits.data(), dtype, nullptr), DT_OK, "all_to_all");
+        // the blocks, in (i, j) order: rank i's send offset runs along its row, rank j's receive offset down its column
+        size_t nb = 0;
+        std::vector<size_t> down(p, 0);
+        for (int i = 0; i < p; i++) {
+            size_t along = 0;
+            for (int j = 0; j < p; j++) {
+                const size_t bytes = splits[i * p + j] * es;
+                if (bytes) {
+                    CHECK(nb < g_a2a_blocks.size(), "all_to_all: block %d -> %d missing", i, j);
+                    const A2ABlock& g = g_a2a_blocks[nb++];
+                    CHECK(g.from == static_cast<const char*>(a_send[i]) + along &&
+                              g.to == static_cast<const char*>(a_recv[j]) + down[j] && g.bytes == bytes,
+                          "all_to_all: block %d -> %d misplaced", i, j);
+                }
+                along += bytes;
+                down[j] += bytes;
+            }
+        }
+        CHECK(nb == g_a2a_blocks.size(), "all_to_all: %zu blocks launched, %zu expected", g_a2a_blocks.size(), nb);
 
         // shard-dimension all-to-all, every (src, dst) pair
         const size_t rows = p * (1 + below(6)), cols = p * (1 + below(below(2) ? 6 : 3000));

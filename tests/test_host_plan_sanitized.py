@@ -69,6 +69,8 @@ MUTANTS = {
     # the two-shot AllReduce writes its ReduceScatter chunks one chunk too far
     "two_shot_chunk_offset": ("rs.dst[r] = static_cast<char*>(recv[r]) + r * cb;",
                               "rs.dst[r] = static_cast<char*>(recv[r]) + (r + 1) * cb;"),
+    # the all-to-all never advances a column's receive offset: blocks overwrite each other
+    "a2a_recv_offset_stuck": ("            recv_off[j] += bytes;\n", ""),
     # one run too many for the shard-dimension exchange
     "dims_extra_run": ("a.nruns = uint64_t(rows) * P;", "a.nruns = uint64_t(rows) * P + 1;"),
     # every piece claimed 16-byte aligned
