@@ -753,8 +753,23 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
     const size_t es = esize_of(dtype);
     size_t nbuckets = 0;
     const std::vector<Piece> plan = plan_buckets(numels, ntensors, bucket_bytes / es, &nbuckets);
-    size_t i = 0;
+    auto piece_ref = [&](const Piece& p) {
+        PieceRef ref = {};
+        for (int r = 0; r < nranks; r++)
+            ref.ptr[r] = static_cast<char*>(grads[size_t(r) * ntensors + p.tensor]) + p.offset * es;
+        ref.len = p.length;
+        ref.wpos = p.bucket_pos;
+        return ref;
+    };
     std::vector<PieceRef> pieces;
+    if (!bucket_ws) {
+        // Reduced in place, straight out of the tensors: each element's fold is
+        // independent, so the pieces of every bucket go out together, in as
+        // few launches as the piece tables allow, instead of one per bucket.
+        for (const Piece& p : plan) pieces.push_back(piece_ref(p));
+        return run_pieces(pieces, nranks, dtype, op, nullptr, kFold, stream);
+    }
+    size_t i = 0;
     while (i < plan.size()) {
         const int bucket = plan[i].bucket;
         size_t end = i;
@@ -762,22 +777,13 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
         size_t bucket_len = 0;
         pieces.clear();
         for (size_t k = i; k < end; k++) {
-            const Piece& p = plan[k];
-            PieceRef ref = {};
-            for (int r = 0; r < nranks; r++)
-                ref.ptr[r] = static_cast<char*>(grads[size_t(r) * ntensors + p.tensor]) + p.offset * es;
-            ref.len = p.length;
-            ref.wpos = p.bucket_pos;
-            pieces.push_back(ref);
-            bucket_len = std::max(bucket_len, p.bucket_pos + p.length);
+            pieces.push_back(piece_ref(plan[k]));
+            bucket_len = std::max(bucket_len, plan[k].bucket_pos + plan[k].length);
         }
-        if (bucket_ws) {  // the page's flatten -> AllReduce -> unflatten
-            if ((st = run_pieces(pieces, nranks, dtype, op, bucket_ws, kFlatten, stream)) != DT_OK) return st;
-            if ((st = allreduce_impl(bucket_ws, bucket_ws, nranks, bucket_len, dtype, op, stream)) != DT_OK) return st;
-            if ((st = run_pieces(pieces, nranks, dtype, op, bucket_ws, kUnflatten, stream)) != DT_OK) return st;
-        } else {  // the bucket reduced in place, straight out of the tensors
-            if ((st = run_pieces(pieces, nranks, dtype, op, nullptr, kFold, stream)) != DT_OK) return st;
-        }
+        // the page's flatten -> AllReduce -> unflatten, bucket by bucket through the workspace
+        if ((st = run_pieces(pieces, nranks, dtype, op, bucket_ws, kFlatten, stream)) != DT_OK) return st;
+        if ((st = allreduce_impl(bucket_ws, bucket_ws, nranks, bucket_len, dtype, op, stream)) != DT_OK) return st;
+        if ((st = run_pieces(pieces, nranks, dtype, op, bucket_ws, kUnflatten, stream)) != DT_OK) return st;
         i = end;
     }
     return DT_OK;

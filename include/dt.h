@@ -140,8 +140,10 @@ dt_status dt_all_to_all(const void* const* send, void* const* recv, int nranks, 
  *   bucket_ws != NULL: nranks device buffers of at least bucket_bytes each;
  *     each bucket is copied in by one multi-tensor launch, reduced in place,
  *     and copied back by one launch (the page's flatten/unflatten).
- *   bucket_ws == NULL: each bucket is reduced straight out of the tensors
- *     and back into them by one multi-tensor launch (no staging copies).
+ *   bucket_ws == NULL: the buckets are reduced straight out of the tensors
+ *     and back into them (no staging copies), all of them together in as
+ *     few multi-tensor launches as the piece tables allow: one for up to
+ *     min(32, 320 / nranks) pieces, else one per min(512, 4096 / nranks).
  * Both forms give the same bits as dt_allreduce on each tensor.  bucket_bytes
  * must be a positive multiple of 16. */
 dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int ntensors, int nranks,
