@@ -52,3 +52,38 @@ def test_graph_replays_allreduce_rs_ag(dt):
             compare(to_np(ys[q]), want[q], f"replay {replay} AR rank {q}")
             compare(to_np(shards[q]), want_rs[q], f"replay {replay} RS rank {q}")
             compare(to_np(full[q]), np.concatenate(want_rs), f"replay {replay} AG rank {q}")
+
+
+def test_graph_replays_two_shot_allreduce(dt):
+    """An AllReduce in the two-shot window (P=16, 32 MiB fp32 per rank: a
+    ReduceScatter into each output's own chunk, then an in-place AllGather)
+    captured in a graph; every replay checked against the oracle (rank 0 in
+    full, the other ranks bit-equal to rank 0)."""
+    orc = oracle.get()
+    p, n = 16, 8 << 20
+    xs = [torch.empty(n, device="cuda") for _ in range(p)]
+    ys = [torch.empty(n, device="cuda") for _ in range(p)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dt.dt_allreduce(xs, ys)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    note("graph capture of a two-shot allreduce P=16 32 MiB fp32")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dt.dt_allreduce(xs, ys)
+    for replay in range(3):
+        note(f"two-shot graph replay {replay}")
+        vals = synth.uniform_ranks(p, n, seed=70 + replay, device="cuda")
+        for x, v in zip(xs, vals):
+            x.copy_(v)
+        for y in ys:
+            y.fill_(float("nan"))  # eager work between replays; stale outputs cannot pass
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = orc.allreduce([to_np(x) for x in xs], "sum")[0]
+        compare(to_np(ys[0]), want, f"replay {replay} rank 0")
+        for q in range(1, p):
+            assert torch.equal(ys[q], ys[0]), f"replay {replay} rank {q} differs from rank 0"
