@@ -94,7 +94,7 @@ dt_status fan_out(const void* const* src, const size_t* counts, void* const* tab
 // ------------------------------------------------------------ reductions --
 // Whether the two-shot form of the AllReduce is the faster one: a
 // ReduceScatter that leaves chunk r of the result in recv[r], then an
-// in-place AllGather of the chunks.  It moves 2(P+1)S bytes against the
+// in-place AllGather of the chunks.  It moves (2P+1)S bytes against the
 // one-shot fold's 2PS, but as a P-to-1 fold and a 1-to-P fan-out whose
 // sources (S bytes in all) are still in the 256 MB Infinity Cache when the
 // fan-out reads them.  Measured on the MI355X against the one-shot kernel:
