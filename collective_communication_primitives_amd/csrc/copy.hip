@@ -18,10 +18,11 @@ namespace dt {
 constexpr int kCopyU = int(kCopyTileBytes / 16 / kBlock);  // 16-byte vectors per thread per tile
 
 // PMAX bounds the rank count; EXACT (P == PMAX) unrolls the P destination
-// stores.  A tile is U * 4 KiB of one rank's source (U = kGatherU).
-template <int PMAX, bool EXACT, int U>
-__global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
-    constexpr uint64_t kTile = uint64_t(U) * kBlock * 16;
+// stores.  A tile is U vectors per thread of BLOCK threads of one rank's
+// source.
+template <int PMAX, bool EXACT, int U, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
+    constexpr uint64_t kTile = uint64_t(U) * BLOCK * 16;
     const uint32_t b = blockIdx.x;
     const int nr = EXACT ? PMAX : a.nranks;
     int r = 0;
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
         u32x4 x[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
+            const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * BLOCK;
             if (v < v1) x[u] = load16_h<false>(src + v * 16);  // writes dominate 1:P
         }
 #pragma unroll
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
                 char* dst = static_cast<char*>(dsts[q]);
 #pragma unroll
                 for (int u = 0; u < U; u++) {
-                    const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
+                    const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * BLOCK;
                     if (v < v1) store16_h<true>(dst + v * 16, x[u]);
                 }
             }
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
                 if (dsts[q] != src) static_cast<char*>(dsts[q])[t] = c;
         }
     } else {
-        for (uint64_t t = b0 + threadIdx.x; t < b1; t += kBlock) {
+        for (uint64_t t = b0 + threadIdx.x; t < b1; t += BLOCK) {
             const char c = src[t];
             for (int q = 0; q < nr; q++)
                 if (dsts[q] != src) static_cast<char*>(dsts[q])[t] = c;
@@ -67,9 +68,9 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
 // Read pass over a gather table's source tiles: plain loads, which leave the
 // bytes in the Infinity Cache for the fan-out launched right after.  The
 // empty asm keeps the loads; nothing is stored.
-__global__ __launch_bounds__(kBlock) void k_gather_touch(GatherArgs a) {
+__global__ __launch_bounds__(kGatherWindowBlock) void k_gather_touch(GatherArgs a) {
     constexpr int U = kGatherU;
-    constexpr uint64_t kTile = uint64_t(U) * kBlock * 16;
+    constexpr uint64_t kTile = kGatherWindowTileBytes;
     const uint32_t b = blockIdx.x;
     const int nr = a.nranks;
     int r = 0;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(kBlock) void k_gather_touch(GatherArgs a) {
     const uint64_t v1 = min(a.bytes[r], b0 + kTile) / 16;
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kBlock;
+        const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kGatherWindowBlock;
         if (v < v1) {
             const u32x4 x = load16_h<false>(src + v * 16);
             asm volatile("" ::"v"(x));
@@ -139,13 +140,20 @@ __global__ __launch_bounds__(kBlock) void k_all_to_all(AllToAllArgs a) {
 }
 
 namespace {
-template <int PMAX, int U>
-hipError_t gather_pu(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
+template <int PMAX, int BLOCK>
+hipError_t gather_pb(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     if (a.nranks == PMAX)
-        k_gather<PMAX, true, U><<<tiles, kBlock, 0, s>>>(a);
+        k_gather<PMAX, true, kGatherU, BLOCK><<<tiles, BLOCK, 0, s>>>(a);
     else
-        k_gather<PMAX, false, U><<<tiles, kBlock, 0, s>>>(a);
+        k_gather<PMAX, false, kGatherU, BLOCK><<<tiles, BLOCK, 0, s>>>(a);
     return hipGetLastError();
+}
+template <int BLOCK>
+hipError_t gather_b(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
+    const int p = a.nranks;
+    return p <= 1 ? gather_pb<1, BLOCK>(a, tiles, s) : p <= 2 ? gather_pb<2, BLOCK>(a, tiles, s)
+           : p <= 4 ? gather_pb<4, BLOCK>(a, tiles, s) : p <= 8 ? gather_pb<8, BLOCK>(a, tiles, s)
+           : gather_pb<16, BLOCK>(a, tiles, s);
 }
 }  // namespace
 
@@ -270,17 +278,14 @@ hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
+hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, bool window_tiles, hipStream_t s) {
     if (tiles == 0) return hipSuccess;
-    const int p = a.nranks;
-    return p <= 1 ? gather_pu<1, kGatherU>(a, tiles, s) : p <= 2 ? gather_pu<2, kGatherU>(a, tiles, s)
-           : p <= 4 ? gather_pu<4, kGatherU>(a, tiles, s) : p <= 8 ? gather_pu<8, kGatherU>(a, tiles, s)
-           : gather_pu<16, kGatherU>(a, tiles, s);
+    return window_tiles ? gather_b<kGatherWindowBlock>(a, tiles, s) : gather_b<kGatherBlock>(a, tiles, s);
 }
 
 hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     if (tiles == 0) return hipSuccess;
-    k_gather_touch<<<tiles, kBlock, 0, s>>>(a);
+    k_gather_touch<<<tiles, kGatherWindowBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -154,8 +154,14 @@ struct ExchangeArgs {
 
 // Tile sizes (bytes of one rank's data per workgroup).
 constexpr uint64_t kCopyTileBytes = 4096;    // all-to-all: one vector per thread
-constexpr int kGatherU = 2;                   // gather: 2 vectors per thread,
-constexpr uint64_t kGatherTileBytes = 8192;   // 8 KiB source tiles
+// Gather (fan-out) tiles, 2 vectors per thread: a direct fan-out uses
+// 256-thread workgroups (8 KiB source tiles); the windows of a large
+// fan-out and their read passes use 64-thread workgroups (2 KiB tiles).
+constexpr int kGatherU = 2;
+constexpr int kGatherBlock = 256;
+constexpr int kGatherWindowBlock = 64;
+constexpr uint64_t kGatherTileBytes = uint64_t(kGatherU) * kGatherBlock * 16;
+constexpr uint64_t kGatherWindowTileBytes = uint64_t(kGatherU) * kGatherWindowBlock * 16;
 constexpr uint64_t kPieceTileVecs = 512;     // bucket pieces: 512 x 16 B
 
 // Launchers: return the HIP error of the launch.  dtype/op are the dt_dtype /
@@ -170,8 +176,10 @@ hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, 
 // Output vectors per workgroup tile of the segmented ReduceScatter for P ranks.
 uint64_t seg_rs_tile_vecs(int nranks);
 hipError_t launch_copy_pieces(const PieceArgs& a, int esize, int to_ws, hipStream_t s);
-hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s);
+// window_tiles: the table counts kGatherWindowTileBytes tiles (else kGatherTileBytes).
+hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, bool window_tiles, hipStream_t s);
 // Read pass over the gather's source tiles (plain loads, nothing stored).
+// Read pass over a table of kGatherWindowTileBytes tiles.
 hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t s);
 constexpr uint64_t kFanOutDirectBytes = 256ull << 20;  // sources up to this size: one launch
 constexpr uint64_t kFanOutWindowBytes = 64ull << 20;    // larger sources: windows of this size

@@ -57,8 +57,11 @@ def test_planning_code_is_clean(check_obj, tmp_path):
 
 MUTANTS = {
     # the gather grid drops the partial last tile of every source
-    "gather_drops_partial_tile": ("tiles += (bytes[k] + dt::kGatherTileBytes - 1) / dt::kGatherTileBytes;",
-                                  "tiles += bytes[k] / dt::kGatherTileBytes;"),
+    "gather_drops_partial_tile": ("tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;",
+                                  "tiles += bytes[k] / tile_bytes;"),
+    # the windows of a large fan-out counted in the direct fan-out's tiles
+    "gather_window_tile_mismatch": ("touch_first ? dt::kGatherWindowTileBytes : dt::kGatherTileBytes;",
+                                    "dt::kGatherTileBytes;"),
     # the windowed fan-out of large sources skips 16 bytes after every piece
     "fan_out_window_skips_bytes": ("            off += take;\n            fill += take;",
                                    "            off += take + 16;\n            fill += take;"),
