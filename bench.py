@@ -584,6 +584,73 @@ def probe(dt, torch, reps: int = 10):
     print(json.dumps({"probe": "done", "reps": reps, "copy_bytes_each_way": a.numel() * 4}), flush=True)
 
 
+def probe_rows(dt, torch, reps: int = 3):
+    """Workload for hardware-counter passes over the other scope rows, each
+    call repeated ``reps`` times with a synchronization in between, plus the
+    same 1 GiB copy as ``probe`` to calibrate the counters.  Each workload's
+    kernels are distinct template instances, so a counter CSV splits by
+    kernel name: the AllToAll (k_all_to_all), the uneven AllGather (the
+    windowed fan-out and its read pass), the two-shot AllReduce at the bench
+    step's shape (its ReduceScatter and gather), one layer of the in-place
+    bucket AllReduce (k_reduce_pieces at P=8) and one layer of the gradient
+    pipeline (the segmented ReduceScatter at P=4 and the bucket folds at
+    P=2).  Prints one JSON line per workload with its algorithmic bytes."""
+    import numpy as np
+    import synth
+    w = synth.ROW_WIDTH
+
+    def run(name, fn, alg_bytes, kernels):
+        for _ in range(reps):
+            fn()
+            torch.cuda.synchronize()
+        print(json.dumps({"probe_row": name, "reps": reps, "alg_bytes_per_call": int(alg_bytes),
+                          "kernels": kernels}), flush=True)
+
+    s_rows = np.random.default_rng(1).integers(0, 4097, (P, P))
+    xs = synth.uniform_rows(s_rows.sum(axis=1), w, seed=200, device="cuda")
+    ys = [torch.empty(int(s_rows[:, j].sum()) * w, device="cuda") for j in range(P)]
+    run("all_to_all_p8", lambda: dt.dt_all_to_all(xs, ys, (s_rows * w).tolist()), 2 * int(s_rows.sum()) * w * 4,
+        ["k_all_to_all"])
+    del xs, ys
+    counts = synth.uneven_row_counts(seed=0)
+    xs = synth.uniform_rows(counts, w, seed=100, device="cuda")
+    ys = [torch.empty(int(counts.sum()) * w, device="cuda") for _ in range(P)]
+    run("uneven_all_gather_p8", lambda: dt.dt_all_gather(xs, ys), (1 + P) * int(counts.sum()) * w * 4,
+        ["k_gather<8, true, 2, 64>", "k_gather_touch"])
+    del xs, ys
+    torch.cuda.empty_cache()
+    xs = synth.normal_ranks(P, SHAPE, seed=0, device="cuda", dtype=torch.bfloat16)
+    ys = [torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    s_bytes = SHAPE[0] * SHAPE[1] * 2
+    run("allreduce_two_shot_p8_bf16", lambda: dt.dt_allreduce(xs, ys), 2 * P * s_bytes,
+        ["k_reduce_scatter_vec<1, 0, 8, true, 512, 1>", "k_gather<8, true, 2, 256>"])
+    del xs, ys
+    torch.cuda.empty_cache()
+    layer = synth.layer_grads(P, layer=0, seed=0, device="cuda")
+    numels = [int(np.prod(sh)) for sh in synth.LAYER_SHAPES]
+    per_rank_layer = sum(numels) * 2
+    run("bucket_allreduce_layer_p8", lambda: dt.dt_bucket_allreduce(layer, bucket_bytes=synth.BUCKET_BYTES),
+        2 * P * per_rank_layer, ["k_reduce_pieces<dt::PieceArgs, 1, 0, 8, true>"])
+    rep, sh = 2, 4
+    fused = [torch.empty(sum(numels) // sh, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    pipe = dt.HSDPPipeline(rep, sh, bucket_bytes=synth.BUCKET_BYTES)
+
+    def one_layer():
+        pipe.post_backward(layer, fused)
+        pipe.finish()
+    run("gradient_pipeline_layer_r2s4", one_layer,
+        rep * (sh + 1) * per_rank_layer + 2 * P * (per_rank_layer // sh),
+        ["k_reduce_scatter_segs<1, 0, 4, true, 4>", "k_reduce_pieces<dt::PieceArgs, 1, 0, 2, true>"])
+    del pipe, fused, layer
+    torch.cuda.empty_cache()
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "done", "reps": reps, "copy_bytes_each_way": a.numel() * 4}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -593,6 +660,8 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=25)
     ap.add_argument("--sweep", action="store_true", help="also run the P=16 size sweep and barrier latency")
     ap.add_argument("--probe", action="store_true", help="only run the kernels for a hardware-counter pass")
+    ap.add_argument("--probe-rows", action="store_true",
+                    help="only run the other rows' workloads once each (x3) for a hardware-counter pass")
     ap.add_argument("--hsdp", action="store_true", help="also time the 32-layer gradient pipeline (103.6 GB)")
     ap.add_argument("--overlap", action="store_true", help="also run the GEMM / AllReduce overlap experiment")
     ap.add_argument("--coalescing", action="store_true", help="also compare the ways to reduce many small tensors")
@@ -613,6 +682,9 @@ def main():
     torch.cuda.set_device(0)
     if args.probe:
         probe(dt, torch)
+        return
+    if args.probe_rows:
+        probe_rows(dt, torch)
         return
     stream = torch.cuda.current_stream()
     xs = synth.normal_ranks(P, SHAPE, seed=0, device="cuda", dtype=torch.bfloat16)
