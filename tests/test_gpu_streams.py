@@ -2,7 +2,6 @@
 the user rules of sec. 5).  A producer kernel that finishes late on the
 compute stream must still be seen by a collective queued on a side stream,
 and a consumer must see the collective's result after wait()."""
-import numpy as np
 import pytest
 import torch
 

@@ -4,7 +4,6 @@ Each mutant is a one-spot textual edit of ``oracle/oracle.c`` (a dropped term,
 a wrong index, a transposed operand, a wrong rounding or compare), compiled
 into a temporary directory on the CPU.  The real oracle is never modified.
 """
-import os
 
 import pytest
 
