@@ -1,0 +1,44 @@
+"""CPU: bench.py's command line and the arithmetic of its figures (no GPU)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                          timeout=300)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = _run("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_help_lists_the_modes():
+    r = _run("--help")
+    assert r.returncode == 0
+    for flag in ("--steps", "--warmup", "--probe", "--probe-rows", "--all", "--no-cpu-baseline"):
+        assert flag in r.stdout
+
+
+def test_kernel_stats_rates():
+    # 1 GiB of algorithmic bytes in 200 us per launch: 5368.7 GB/s; an AllReduce's
+    # bus bandwidth of S = 128 MiB per rank over the same time, times 2(P-1)/P
+    st = bench.kernel_stats([190.0, 200.0, 210.0], 1 << 30, 128 << 20, 2 * 7 / 8)
+    assert st["mean_us"] == pytest.approx(200.0)
+    assert st["median_us"] == pytest.approx(200.0)
+    assert st["hbm_GBps"] == pytest.approx(round((1 << 30) / 200e-6 / 1e9, 1))
+    assert st["busbw_GBps"] == pytest.approx(round((128 << 20) / 200e-6 / 1e9 * 1.75, 1))
+    assert st["p10_us"] <= st["median_us"] <= st["p90_us"]
+
+
+def test_kernel_source_hash_is_stable():
+    assert bench.kernel_source_hash() == bench.kernel_source_hash()
+    assert len(bench.kernel_source_hash()) == 16
