@@ -152,7 +152,19 @@ def cpu_baseline(xs_dev, reps: int):
     return {"value": round(busbw, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"full workload (P=8 bf16 {SHAPE[0]}x{SHAPE[1]} per rank), RS then AG, "
                       f"median of {reps} single-threaded runs of {t:.2f} s each; same busbw formula",
-            "seconds_per_step": round(t, 3), "host_cpus": os.cpu_count()}
+            "seconds_per_step": round(t, 3), "host_cpus": os.cpu_count(), "host_cpu_model": host_cpu_model()}
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name, as /proc/cpuinfo reports it (empty if unknown)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 def graph_time_us(torch, fn, per_graph: int = 20, replays: int = 5) -> float:

@@ -42,3 +42,7 @@ def test_kernel_stats_rates():
 def test_kernel_source_hash_is_stable():
     assert bench.kernel_source_hash() == bench.kernel_source_hash()
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_host_cpu_model_is_a_string():
+    assert isinstance(bench.host_cpu_model(), str)
