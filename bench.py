@@ -628,7 +628,7 @@ def probe_rows(dt, torch, reps: int = 3):
     xs = synth.uniform_rows(counts, w, seed=100, device="cuda")
     ys = [torch.empty(int(counts.sum()) * w, device="cuda") for _ in range(P)]
     run("uneven_all_gather_p8", lambda: dt.dt_all_gather(xs, ys), (1 + P) * int(counts.sum()) * w * 4,
-        ["k_gather<8, true, 2, 64>", "k_gather_touch"])
+        ["k_gather<8, true, 1, 128>", "k_gather_touch"])
     del xs, ys
     torch.cuda.empty_cache()
     xs = synth.normal_ranks(P, SHAPE, seed=0, device="cuda", dtype=torch.bfloat16)

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
 // bytes in the Infinity Cache for the fan-out launched right after.  The
 // empty asm keeps the loads; nothing is stored.
 __global__ __launch_bounds__(kGatherWindowBlock) void k_gather_touch(GatherArgs a) {
-    constexpr int U = kGatherU;
+    constexpr int U = kGatherWindowU;
     constexpr uint64_t kTile = kGatherWindowTileBytes;
     const uint32_t b = blockIdx.x;
     const int nr = a.nranks;
@@ -140,20 +140,20 @@ __global__ __launch_bounds__(kBlock) void k_all_to_all(AllToAllArgs a) {
 }
 
 namespace {
-template <int PMAX, int BLOCK>
+template <int PMAX, int BLOCK, int U>
 hipError_t gather_pb(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     if (a.nranks == PMAX)
-        k_gather<PMAX, true, kGatherU, BLOCK><<<tiles, BLOCK, 0, s>>>(a);
+        k_gather<PMAX, true, U, BLOCK><<<tiles, BLOCK, 0, s>>>(a);
     else
-        k_gather<PMAX, false, kGatherU, BLOCK><<<tiles, BLOCK, 0, s>>>(a);
+        k_gather<PMAX, false, U, BLOCK><<<tiles, BLOCK, 0, s>>>(a);
     return hipGetLastError();
 }
-template <int BLOCK>
+template <int BLOCK, int U>
 hipError_t gather_b(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     const int p = a.nranks;
-    return p <= 1 ? gather_pb<1, BLOCK>(a, tiles, s) : p <= 2 ? gather_pb<2, BLOCK>(a, tiles, s)
-           : p <= 4 ? gather_pb<4, BLOCK>(a, tiles, s) : p <= 8 ? gather_pb<8, BLOCK>(a, tiles, s)
-           : gather_pb<16, BLOCK>(a, tiles, s);
+    return p <= 1 ? gather_pb<1, BLOCK, U>(a, tiles, s) : p <= 2 ? gather_pb<2, BLOCK, U>(a, tiles, s)
+           : p <= 4 ? gather_pb<4, BLOCK, U>(a, tiles, s) : p <= 8 ? gather_pb<8, BLOCK, U>(a, tiles, s)
+           : gather_pb<16, BLOCK, U>(a, tiles, s);
 }
 }  // namespace
 
@@ -280,7 +280,8 @@ hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_
 
 hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, bool window_tiles, hipStream_t s) {
     if (tiles == 0) return hipSuccess;
-    return window_tiles ? gather_b<kGatherWindowBlock>(a, tiles, s) : gather_b<kGatherBlock>(a, tiles, s);
+    return window_tiles ? gather_b<kGatherWindowBlock, kGatherWindowU>(a, tiles, s)
+                        : gather_b<kGatherBlock, kGatherU>(a, tiles, s);
 }
 
 hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t s) {

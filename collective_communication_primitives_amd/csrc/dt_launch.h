@@ -154,14 +154,16 @@ struct ExchangeArgs {
 
 // Tile sizes (bytes of one rank's data per workgroup).
 constexpr uint64_t kCopyTileBytes = 4096;    // all-to-all: one vector per thread
-// Gather (fan-out) tiles, 2 vectors per thread: a direct fan-out uses
-// 256-thread workgroups (8 KiB source tiles); the windows of a large
-// fan-out and their read passes use 64-thread workgroups (2 KiB tiles).
+// Gather (fan-out) tiles: a direct fan-out uses 256-thread workgroups with 2
+// vectors per thread (8 KiB source tiles); the windows of a large fan-out
+// and their read passes use 128-thread workgroups with 1 vector per thread
+// (2 KiB tiles).
 constexpr int kGatherU = 2;
 constexpr int kGatherBlock = 256;
-constexpr int kGatherWindowBlock = 64;
+constexpr int kGatherWindowBlock = 128;
+constexpr int kGatherWindowU = 1;
 constexpr uint64_t kGatherTileBytes = uint64_t(kGatherU) * kGatherBlock * 16;
-constexpr uint64_t kGatherWindowTileBytes = uint64_t(kGatherU) * kGatherWindowBlock * 16;
+constexpr uint64_t kGatherWindowTileBytes = uint64_t(kGatherWindowU) * kGatherWindowBlock * 16;
 constexpr uint64_t kPieceTileVecs = 512;     // bucket pieces: 512 x 16 B
 
 // Launchers: return the HIP error of the launch.  dtype/op are the dt_dtype /
