@@ -599,11 +599,12 @@ def probe(dt, torch, reps: int = 10):
 def probe_rows(dt, torch, reps: int = 3):
     """Workload for hardware-counter passes over the other scope rows, each
     call repeated ``reps`` times with a synchronization in between, plus the
-    same 1 GiB copy as ``probe`` to calibrate the counters.  Each workload's
-    kernels are distinct template instances, so a counter CSV splits by
-    kernel name: the AllToAll (k_all_to_all), the uneven AllGather (the
-    windowed fan-out and its read pass), the two-shot AllReduce at the bench
-    step's shape (its ReduceScatter and gather), one layer of the in-place
+    same 1 GiB copy as ``probe`` to calibrate the counters.  The workloads
+    run one after another, so a counter CSV splits by dispatch order (the
+    uneven AllGather and the two-shot AllReduce share the gather kernel): the
+    AllToAll (k_all_to_all), the uneven AllGather (the windowed fan-out and
+    its read pass), the two-shot AllReduce at the bench step's shape (its
+    ReduceScatter and gather), one layer of the in-place
     bucket AllReduce (k_reduce_pieces at P=8) and one layer of the gradient
     pipeline (the segmented ReduceScatter at P=4 and the bucket folds at
     P=2).  Prints one JSON line per workload with its algorithmic bytes."""
@@ -635,7 +636,7 @@ def probe_rows(dt, torch, reps: int = 3):
     ys = [torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
     s_bytes = SHAPE[0] * SHAPE[1] * 2
     run("allreduce_two_shot_p8_bf16", lambda: dt.dt_allreduce(xs, ys), 2 * P * s_bytes,
-        ["k_reduce_scatter_vec<1, 0, 8, true, 512, 1>", "k_gather<8, true, 2, 256>"])
+        ["k_reduce_scatter_vec<1, 0, 8, true, 512, 1>", "k_gather<8, true, 1, 128>"])
     del xs, ys
     torch.cuda.empty_cache()
     layer = synth.layer_grads(P, layer=0, seed=0, device="cuda")

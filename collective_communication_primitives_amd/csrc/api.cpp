@@ -25,7 +25,6 @@ static_assert(sizeof(dt::SegCopyArgs) <= 4096, "kernel arguments must stay below
 static_assert(sizeof(dt::DimsArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::CoalescedArgs) <= 48 * 1024, "large piece table must stay well below the 64 KB verified");
 static_assert(DT_MAX_RANKS == dt::kMaxRanksHost, "rank limit mismatch");
-static_assert(dt::kGatherWindowTileBytes < dt::kGatherTileBytes, "window tiles are the smaller ones");
 
 namespace {
 
@@ -208,8 +207,7 @@ dt_status fan_out_launch(const void* const* src, const uint64_t* bytes, void* co
                          int nranks, bool touch_first, hipStream_t stream, const char* what) {
     dt::GatherArgs a = {};
     a.nranks = nranks;
-    // a window (after its read pass) fans out in the small tiles, a direct fan-out in the large ones
-    const uint64_t tile_bytes = touch_first ? dt::kGatherWindowTileBytes : dt::kGatherTileBytes;
+    const uint64_t tile_bytes = dt::kGatherTileBytes;
     uint64_t tiles = 0;
     for (int k = 0; k < n; k++) {
         a.src[k] = src[k];
@@ -229,7 +227,7 @@ dt_status fan_out_launch(const void* const* src, const uint64_t* bytes, void* co
     if (tiles == 0) return DT_OK;
     dt_status st = DT_OK;
     if (touch_first && (st = check_hip(dt::launch_gather_touch(a, uint32_t(tiles), stream), what)) != DT_OK) return st;
-    return check_hip(dt::launch_gather(a, uint32_t(tiles), touch_first, stream), what);
+    return check_hip(dt::launch_gather(a, uint32_t(tiles), stream), what);
 }
 
 // Fan-out of `nsources` pieces (default: nranks): piece r (counts[r]

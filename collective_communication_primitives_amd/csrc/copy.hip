@@ -1,12 +1,13 @@
 // copy.hip -- the gather and all-to-all copy engines.
 //
 // Both are byte copies driven by an offset table carried in the kernel
-// arguments (no device-side tables).  The work is cut into 4-16 KiB tiles of
-// source data; one workgroup copies one tile, so uneven pieces (1 row or
-// 16384 rows, an empty all-to-all block or a 4096-row one) balance across the
-// whole chip.  A workgroup finds its piece from an exclusive prefix sum of
-// tile counts: a linear scan over at most 16 ranks for the gather, a binary
-// search over the P*P blocks for the all-to-all.
+// arguments (no device-side tables).  The work is cut into 2 KiB (gather) or
+// 4 KiB (all-to-all) tiles of source data; one workgroup copies one tile, so
+// uneven pieces (1 row or 16384 rows, an empty all-to-all block or a 4096-row
+// one) balance across the whole chip.  A workgroup finds its piece from an
+// exclusive prefix sum of tile counts: a linear scan over at most 16 ranks for
+// the gather, a two-level batched lookup over at most 256 non-empty blocks
+// for the all-to-all.
 //
 // AllGather fans out: each source tile is read once and written to every
 // rank's output, (1 + P) bytes of HBM traffic per gathered byte.
@@ -68,9 +69,9 @@ __global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
 // Read pass over a gather table's source tiles: plain loads, which leave the
 // bytes in the Infinity Cache for the fan-out launched right after.  The
 // empty asm keeps the loads; nothing is stored.
-__global__ __launch_bounds__(kGatherWindowBlock) void k_gather_touch(GatherArgs a) {
-    constexpr int U = kGatherWindowU;
-    constexpr uint64_t kTile = kGatherWindowTileBytes;
+__global__ __launch_bounds__(kGatherBlock) void k_gather_touch(GatherArgs a) {
+    constexpr int U = kGatherU;
+    constexpr uint64_t kTile = kGatherTileBytes;
     const uint32_t b = blockIdx.x;
     const int nr = a.nranks;
     int r = 0;
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kGatherWindowBlock) void k_gather_touch(GatherArgs 
     const uint64_t v1 = min(a.bytes[r], b0 + kTile) / 16;
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kGatherWindowBlock;
+        const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kGatherBlock;
         if (v < v1) {
             const u32x4 x = load16_h<false>(src + v * 16);
             asm volatile("" ::"v"(x));
@@ -140,20 +141,13 @@ __global__ __launch_bounds__(kBlock) void k_all_to_all(AllToAllArgs a) {
 }
 
 namespace {
-template <int PMAX, int BLOCK, int U>
-hipError_t gather_pb(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
+template <int PMAX>
+hipError_t gather_p(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     if (a.nranks == PMAX)
-        k_gather<PMAX, true, U, BLOCK><<<tiles, BLOCK, 0, s>>>(a);
+        k_gather<PMAX, true, kGatherU, kGatherBlock><<<tiles, kGatherBlock, 0, s>>>(a);
     else
-        k_gather<PMAX, false, U, BLOCK><<<tiles, BLOCK, 0, s>>>(a);
+        k_gather<PMAX, false, kGatherU, kGatherBlock><<<tiles, kGatherBlock, 0, s>>>(a);
     return hipGetLastError();
-}
-template <int BLOCK, int U>
-hipError_t gather_b(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
-    const int p = a.nranks;
-    return p <= 1 ? gather_pb<1, BLOCK, U>(a, tiles, s) : p <= 2 ? gather_pb<2, BLOCK, U>(a, tiles, s)
-           : p <= 4 ? gather_pb<4, BLOCK, U>(a, tiles, s) : p <= 8 ? gather_pb<8, BLOCK, U>(a, tiles, s)
-           : gather_pb<16, BLOCK, U>(a, tiles, s);
 }
 }  // namespace
 
@@ -278,15 +272,16 @@ hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, bool window_tiles, hipStream_t s) {
+hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     if (tiles == 0) return hipSuccess;
-    return window_tiles ? gather_b<kGatherWindowBlock, kGatherWindowU>(a, tiles, s)
-                        : gather_b<kGatherBlock, kGatherU>(a, tiles, s);
+    const int p = a.nranks;
+    return p <= 1 ? gather_p<1>(a, tiles, s) : p <= 2 ? gather_p<2>(a, tiles, s) : p <= 4 ? gather_p<4>(a, tiles, s)
+           : p <= 8 ? gather_p<8>(a, tiles, s) : gather_p<16>(a, tiles, s);
 }
 
 hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     if (tiles == 0) return hipSuccess;
-    k_gather_touch<<<tiles, kGatherWindowBlock, 0, s>>>(a);
+    k_gather_touch<<<tiles, kGatherBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -154,16 +154,12 @@ struct ExchangeArgs {
 
 // Tile sizes (bytes of one rank's data per workgroup).
 constexpr uint64_t kCopyTileBytes = 4096;    // all-to-all: one vector per thread
-// Gather (fan-out) tiles: a direct fan-out uses 256-thread workgroups with 2
-// vectors per thread (8 KiB source tiles); the windows of a large fan-out
-// and their read passes use 128-thread workgroups with 1 vector per thread
-// (2 KiB tiles).
-constexpr int kGatherU = 2;
-constexpr int kGatherBlock = 256;
-constexpr int kGatherWindowBlock = 128;
-constexpr int kGatherWindowU = 1;
+// Gather (fan-out) tiles: 128-thread workgroups with 1 vector per thread
+// (2 KiB source tiles), for a direct fan-out, the windows of a large one and
+// their read passes alike.
+constexpr int kGatherU = 1;
+constexpr int kGatherBlock = 128;
 constexpr uint64_t kGatherTileBytes = uint64_t(kGatherU) * kGatherBlock * 16;
-constexpr uint64_t kGatherWindowTileBytes = uint64_t(kGatherWindowU) * kGatherWindowBlock * 16;
 constexpr uint64_t kPieceTileVecs = 512;     // bucket pieces: 512 x 16 B
 
 // Launchers: return the HIP error of the launch.  dtype/op are the dt_dtype /
@@ -178,10 +174,9 @@ hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, 
 // Output vectors per workgroup tile of the segmented ReduceScatter for P ranks.
 uint64_t seg_rs_tile_vecs(int nranks);
 hipError_t launch_copy_pieces(const PieceArgs& a, int esize, int to_ws, hipStream_t s);
-// window_tiles: the table counts kGatherWindowTileBytes tiles (else kGatherTileBytes).
-hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, bool window_tiles, hipStream_t s);
+// The table counts kGatherTileBytes tiles.
+hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s);
 // Read pass over the gather's source tiles (plain loads, nothing stored).
-// Read pass over a table of kGatherWindowTileBytes tiles.
 hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t s);
 constexpr uint64_t kFanOutDirectBytes = 256ull << 20;  // sources up to this size: one launch
 constexpr uint64_t kFanOutWindowBytes = 64ull << 20;    // larger sources: windows of this size

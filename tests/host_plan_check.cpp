@@ -253,7 +253,7 @@ hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t)
     g_launches++;
     g_touch_launches++;
     std::vector<uint64_t> want;
-    for (int r = 0; r < a.nranks; r++) want.push_back(ceil_div(a.bytes[r], kGatherWindowTileBytes));
+    for (int r = 0; r < a.nranks; r++) want.push_back(ceil_div(a.bytes[r], kGatherTileBytes));
     check_tiles(a.tile_start, want, tiles, "gather touch");
     for (int r = 0; r < a.nranks; r++) {
         touch(a.src[r], 0, a.bytes[r], false, "gather touch read");
@@ -262,17 +262,14 @@ hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t)
     return hipSuccess;
 }
 
-int g_window_gathers = 0;  // gather launches over window tiles since the last reset
-
-hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, bool window_tiles, hipStream_t) {
-    if (window_tiles) g_window_gathers++;
+hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t) {
     g_launches++;
     for (int r = 0; r < a.nranks; r++)
         if (a.bytes[r])
             g_gather_pieces.push_back(GatherPiece{static_cast<const char*>(a.src[r]), a.bytes[r],
                                                   static_cast<const char*>(a.dst[r * a.nranks])});
     std::vector<uint64_t> want;
-    for (int r = 0; r < a.nranks; r++) want.push_back(ceil_div(a.bytes[r], window_tiles ? kGatherWindowTileBytes : kGatherTileBytes));
+    for (int r = 0; r < a.nranks; r++) want.push_back(ceil_div(a.bytes[r], kGatherTileBytes));
     check_tiles(a.tile_start, want, tiles, "gather");
     for (int r = 0; r < a.nranks; r++) {
         if (a.bytes[r] == 0) continue;
@@ -675,11 +672,8 @@ void big_fan_out() {
     }
     g_gather_pieces.clear();
     g_touch_launches = 0;
-    dt::g_window_gathers = 0;
     expect(dt_all_gather(send, recv, p, counts, 0, DT_BFLOAT16, nullptr), DT_OK, "big all_gather");
     CHECK(g_touch_launches > 1, "big all_gather: %d read passes", g_touch_launches);
-    CHECK(dt::g_window_gathers == g_touch_launches, "big all_gather: %d window fan-outs for %d read passes",
-          dt::g_window_gathers, g_touch_launches);
     uint64_t at = 0;  // destination offset of rank r's piece
     for (int r = 0; r < p; r++) {
         const char* s0 = static_cast<const char*>(send[r]);

@@ -59,9 +59,9 @@ MUTANTS = {
     # the gather grid drops the partial last tile of every source
     "gather_drops_partial_tile": ("tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;",
                                   "tiles += bytes[k] / tile_bytes;"),
-    # the windows of a large fan-out counted in the direct fan-out's tiles
-    "gather_window_tile_mismatch": ("touch_first ? dt::kGatherWindowTileBytes : dt::kGatherTileBytes;",
-                                    "dt::kGatherTileBytes;"),
+    # the windows of a large fan-out go out without their read passes
+    "window_skips_read_pass": ("if (touch_first && (st = check_hip(dt::launch_gather_touch(",
+                               "if (false && touch_first && (st = check_hip(dt::launch_gather_touch("),
     # the windowed fan-out of large sources skips 16 bytes after every piece
     "fan_out_window_skips_bytes": ("            off += take;\n            fill += take;",
                                    "            off += take + 16;\n            fill += take;"),
