@@ -636,7 +636,7 @@ def probe_rows(dt, torch, reps: int = 3):
     ys = [torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
     s_bytes = SHAPE[0] * SHAPE[1] * 2
     run("allreduce_two_shot_p8_bf16", lambda: dt.dt_allreduce(xs, ys), 2 * P * s_bytes,
-        ["k_reduce_scatter_vec<1, 0, 8, true, 512, 1>", "k_gather<8, true, 1, 128>"])
+        ["k_reduce_scatter_vec<1, 0, 8, true, 64, 1>", "k_gather<8, true, 1, 128>"])
     del xs, ys
     torch.cuda.empty_cache()
     layer = synth.layer_grads(P, layer=0, seed=0, device="cuda")
@@ -653,7 +653,7 @@ def probe_rows(dt, torch, reps: int = 3):
         pipe.finish()
     run("gradient_pipeline_layer_r2s4", one_layer,
         rep * (sh + 1) * per_rank_layer + 2 * P * (per_rank_layer // sh),
-        ["k_reduce_scatter_segs<1, 0, 4, true, 4>", "k_reduce_pieces<dt::PieceArgs, 1, 0, 2, true>"])
+        ["k_reduce_scatter_segs<1, 0, 4, true, 1>", "k_reduce_pieces<dt::PieceArgs, 1, 0, 2, true>"])
     del pipe, fused, layer
     torch.cuda.empty_cache()
     a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)

@@ -153,7 +153,7 @@ struct ExchangeArgs {
 };
 
 // Tile sizes (bytes of one rank's data per workgroup).
-constexpr uint64_t kCopyTileBytes = 4096;    // all-to-all: one vector per thread
+constexpr uint64_t kCopyTileBytes = 1024;    // all-to-all: one wave, one vector per thread
 // Gather (fan-out) tiles: 128-thread workgroups with 1 vector per thread
 // (2 KiB source tiles), for a direct fan-out, the windows of a large one and
 // their read passes alike.
@@ -183,7 +183,7 @@ constexpr uint64_t kFanOutWindowBytes = 64ull << 20;    // larger sources: windo
 hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t s);
 hipError_t launch_copy_segments(const SegCopyArgs& a, hipStream_t s);
 hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_t s);
-constexpr uint64_t kSegCopyTileBytes = 16384;
+constexpr uint64_t kSegCopyTileBytes = 1024;
 constexpr uint64_t kDimsTileBytes = 16384;
 constexpr uint32_t kDimsMaxRunsPerBlock = 64;
 hipError_t launch_barrier(const BarrierArgs& a, int spread, hipStream_t s);

@@ -17,15 +17,15 @@
 namespace dt {
 
 // ------------------------------------------------------------- AllReduce --
-// grid.x covers a.count vectors in tiles of kBlock*U.
+// grid.x covers a.count vectors in tiles of BLOCK*U.
 //
 // Issue order: all of rank 0's vectors, then rank 1's, ...; stores output by
 // output.  Each wave then sends U KiB-long runs to one buffer before moving to
 // the next, which the MI355X's HBM serves faster than interleaving the P
 // buffers vector by vector (measured: +3% for the P-to-P AllReduce pattern).
-template <int DT, int OP, int PMAX, bool EXACT, int U>
-__global__ __launch_bounds__(kBlock) void k_reduce_vec(ReduceArgs a) {
-    const uint64_t base = uint64_t(blockIdx.x) * (kBlock * U) + threadIdx.x;
+template <int DT, int OP, int PMAX, bool EXACT, int U, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_reduce_vec(ReduceArgs a) {
+    const uint64_t base = uint64_t(blockIdx.x) * (BLOCK * U) + threadIdx.x;
     const int nr = EXACT ? PMAX : a.nranks;
     u32x4 x[U][PMAX];
 #pragma unroll
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_vec(ReduceArgs a) {
         if (r < nr) {
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                const uint64_t v = base + uint64_t(u) * kBlock;
+                const uint64_t v = base + uint64_t(u) * BLOCK;
                 if (v < a.count) x[u][r] = load16(static_cast<const char*>(a.src[r]) + v * 16);
             }
         }
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_vec(ReduceArgs a) {
         if (q < nr) {
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                const uint64_t v = base + uint64_t(u) * kBlock;
+                const uint64_t v = base + uint64_t(u) * BLOCK;
                 if (v < a.count) store16(static_cast<char*>(a.dst[q]) + v * 16, y[u]);
             }
         }
@@ -59,9 +59,11 @@ __global__ __launch_bounds__(kBlock) void k_reduce_vec(ReduceArgs a) {
 // range (the same lane offsets serve all P ranks), non-temporal loads and
 // device-scope stores; the resource range cuts off the last tile.  Measured
 // against the same kernel with 64-bit global addressing: 2-3% faster for
-// P=8 bf16 at 16 MiB per chunk.  BLOCK threads x U vectors per tile: for
-// P >= 8 the tile is spread over 512 threads with one vector each, 1.3%
-// faster than 256 threads with two.
+// P=8 bf16 at 16 MiB per chunk.  BLOCK threads x U vectors per tile: one
+// wave with one vector per thread (1 KiB of every rank per workgroup) for
+// every P.  In-process A/B: 2.5% faster than 512 threads x 1 vector at P=8
+// bf16 and no slower at any of 13 placements of the inputs tried; 5-7%
+// faster than 256 threads x 4 vectors at P=4, even at P=2.
 template <int DT, int OP, int PMAX, bool EXACT, int BLOCK, int U>
 __global__ __launch_bounds__(BLOCK) void k_reduce_scatter_vec(ReduceArgs a) {
     constexpr uint64_t kTileVecs = uint64_t(BLOCK) * U;
@@ -198,10 +200,15 @@ __global__ __launch_bounds__(kBlock) void k_reduce_pieces(Args a) {
 // ------------------------------------------------ segmented ReduceScatter --
 // Many ReduceScatters (e.g. every tensor of one layer, in every shard group)
 // in one launch, so the chip never drains between small collectives.  A tile
-// is U*kBlock output vectors of one chunk j of one segment k; the workgroup
-// folds member 0..P-1's vectors of that chunk in rank order.
+// is U*kSegBlock output vectors of one chunk j of one segment k; the
+// workgroup folds member 0..P-1's vectors of that chunk in rank order.
+// Single-wave workgroups with one vector per thread (1 KiB of every member
+// per tile): the 32-layer gradient pipeline ran 4% faster than with 256
+// threads x 4 vectors (in-process A/B), where 256 threads with 2 or 1
+// vectors had been 0.5-1.3% slower.
+constexpr int kSegBlock = 64;
 template <int DT, int OP, int PMAX, bool EXACT, int U>
-__global__ __launch_bounds__(kBlock) void k_reduce_scatter_segs(SegReduceScatterArgs a) {
+__global__ __launch_bounds__(kSegBlock) void k_reduce_scatter_segs(SegReduceScatterArgs a) {
     constexpr int V = Elems<DT>::value;
     const uint32_t b = blockIdx.x;
     int k = 0;
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_scatter_segs(SegReduceScatter
     const void* const* src = a.src + k * nr;
     void* dst = a.dst[k * nr + j];
     if ((a.aligned >> k) & 1u) {
-        constexpr uint64_t kTileVecs = uint64_t(kBlock) * U;
+        constexpr uint64_t kTileVecs = uint64_t(kSegBlock) * U;
         const uint64_t mv = m / V;
         const uint64_t t0 = uint64_t(tt) * kTileVecs;            // < mv by the tile count
         const uint64_t left = mv - t0;
@@ -227,17 +234,17 @@ __global__ __launch_bounds__(kBlock) void k_reduce_scatter_segs(SegReduceScatter
             if (r < nr) {
                 const rsrc_t in = make_rsrc(static_cast<const char*>(src[r]) + in_off, bytes);
 #pragma unroll
-                for (int u = 0; u < U; u++) x[u][r] = bload16<kPolNT>(in, lane + u * (kBlock * 16));
+                for (int u = 0; u < U; u++) x[u][r] = bload16<kPolNT>(in, lane + u * (kSegBlock * 16));
             }
         }
         const rsrc_t out = make_rsrc(static_cast<char*>(dst) + t0 * 16, bytes);
 #pragma unroll
-        for (int u = 0; u < U; u++) bstore16<kPolDevice>(out, lane + u * (kBlock * 16), fold_vec<DT, OP, PMAX>(x[u], nr));
+        for (int u = 0; u < U; u++) bstore16<kPolDevice>(out, lane + u * (kSegBlock * 16), fold_vec<DT, OP, PMAX>(x[u], nr));
     } else {
-        const uint64_t per_tile = uint64_t(kBlock) * U * V;
+        const uint64_t per_tile = uint64_t(kSegBlock) * U * V;
         const uint64_t e0 = uint64_t(tt) * per_tile;
         const uint64_t e1 = min(m, e0 + per_tile);
-        for (uint64_t e = e0 + threadIdx.x; e < e1; e += kBlock)
+        for (uint64_t e = e0 + threadIdx.x; e < e1; e += kSegBlock)
             fold_elem<DT, OP>(src, nr, uint64_t(j) * m + e, dst, e);
     }
 }
@@ -274,35 +281,43 @@ int pmax_of(int nranks) {
     return nranks <= 1 ? 1 : nranks <= 2 ? 2 : nranks <= 4 ? 4 : nranks <= 8 ? 8 : 16;
 }
 
-// Vectors per thread (U), measured on the MI355X for 25-256 MiB per rank:
-// two per thread for every AllReduce and for ReduceScatter with P >= 8, four
-// for ReduceScatter with P <= 4 and for the plain copy of P = 1.
-template <int PMAX, bool RS>
-constexpr int unroll_of() { return PMAX == 1 ? 4 : (RS && PMAX <= 4) ? 4 : 2; }
+// One wave, one vector per thread: the tile of the ReduceScatter, and of a
+// one-shot AllReduce of P >= 8 ranks above kWaveAllReduceBytes per rank.
+constexpr int kWaveBlock = 64;
+// One-shot AllReduce with P >= 8 in one-wave tiles beyond this many bytes per
+// rank (above the two-shot window): in-process A/B 3-5% faster at 512 MiB
+// and 1 GiB per rank (P=8 bf16, P=16 fp32), but 2-12% slower at 4-64 MiB.
+constexpr uint64_t kWaveAllReduceBytes = 256ull << 20;
+
+// Vectors per thread of the one-shot AllReduce in kBlock-thread tiles,
+// measured on the MI355X for 25-256 MiB per rank: two, four for the plain
+// copy of P = 1.
+template <int PMAX>
+constexpr int ar_unroll() { return PMAX == 1 ? 4 : 2; }
+
+template <int DT, int OP, int PMAX, bool EXACT>
+void reduce_vec_launch(const ReduceArgs& a, uint64_t blocks, bool wave, hipStream_t s) {
+    if (a.rs) {
+        const dim3 grid(unsigned(blocks), unsigned(a.nranks));
+        k_reduce_scatter_vec<DT, OP, PMAX, EXACT, kWaveBlock, 1><<<grid, kWaveBlock, 0, s>>>(a);
+    } else if (wave) {
+        if constexpr (PMAX >= 8) k_reduce_vec<DT, OP, PMAX, EXACT, 1, kWaveBlock><<<unsigned(blocks), kWaveBlock, 0, s>>>(a);
+    } else {
+        k_reduce_vec<DT, OP, PMAX, EXACT, ar_unroll<PMAX>(), kBlock><<<unsigned(blocks), kBlock, 0, s>>>(a);
+    }
+}
 
 template <int DT, int OP, int PMAX>
 hipError_t reduce_vec_p(const ReduceArgs& a, hipStream_t s) {
-    constexpr int URS = unroll_of<PMAX, true>(), UAR = unroll_of<PMAX, false>();
-    const uint64_t per_block = uint64_t(kBlock) * (a.rs ? URS : UAR);
+    const bool wave = a.rs || (PMAX >= 8 && a.count * 16 > kWaveAllReduceBytes);
+    const uint64_t per_block = wave ? uint64_t(kWaveBlock) : uint64_t(kBlock) * ar_unroll<PMAX>();
     const uint64_t blocks = (a.count + per_block - 1) / per_block;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    const bool exact = a.nranks == PMAX;
-    if (a.rs) {
-        // same tile (kBlock*URS vectors); P >= 8 spreads it over 512 threads, one vector each
-        constexpr int RB = PMAX >= 8 ? kBlock * URS : kBlock;
-        constexpr int RU = PMAX >= 8 ? 1 : URS;
-        const dim3 grid(unsigned(blocks), unsigned(a.nranks));
-        if (exact)
-            k_reduce_scatter_vec<DT, OP, PMAX, true, RB, RU><<<grid, RB, 0, s>>>(a);
-        else
-            k_reduce_scatter_vec<DT, OP, PMAX, false, RB, RU><<<grid, RB, 0, s>>>(a);
-    } else {
-        if (exact)
-            k_reduce_vec<DT, OP, PMAX, true, UAR><<<unsigned(blocks), kBlock, 0, s>>>(a);
-        else
-            k_reduce_vec<DT, OP, PMAX, false, UAR><<<unsigned(blocks), kBlock, 0, s>>>(a);
-    }
+    if (a.nranks == PMAX)
+        reduce_vec_launch<DT, OP, PMAX, true>(a, blocks, wave, s);
+    else
+        reduce_vec_launch<DT, OP, PMAX, false>(a, blocks, wave, s);
     return hipGetLastError();
 }
 
@@ -399,13 +414,13 @@ hipError_t copy_pieces_any(const Args& a, int esize, int to_ws, hipStream_t s) {
 
 template <int DT, int OP, int PMAX>
 hipError_t reduce_scatter_segs_p(const SegReduceScatterArgs& a, hipStream_t s) {
-    constexpr int U = unroll_of<PMAX, true>();
+    constexpr int U = 1;
     const uint32_t tiles = a.tile_start[a.nsegs];
     if (tiles == 0) return hipSuccess;
     if (a.nranks == PMAX)
-        k_reduce_scatter_segs<DT, OP, PMAX, true, U><<<tiles, kBlock, 0, s>>>(a);
+        k_reduce_scatter_segs<DT, OP, PMAX, true, U><<<tiles, kSegBlock, 0, s>>>(a);
     else
-        k_reduce_scatter_segs<DT, OP, PMAX, false, U><<<tiles, kBlock, 0, s>>>(a);
+        k_reduce_scatter_segs<DT, OP, PMAX, false, U><<<tiles, kSegBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -432,15 +447,7 @@ hipError_t reduce_scatter_segs_dt(const SegReduceScatterArgs& a, int op, hipStre
 
 }  // namespace
 
-uint64_t seg_rs_tile_vecs(int nranks) {
-    switch (pmax_of(nranks)) {
-        case 1: return uint64_t(kBlock) * unroll_of<1, true>();
-        case 2: return uint64_t(kBlock) * unroll_of<2, true>();
-        case 4: return uint64_t(kBlock) * unroll_of<4, true>();
-        case 8: return uint64_t(kBlock) * unroll_of<8, true>();
-        default: return uint64_t(kBlock) * unroll_of<16, true>();
-    }
-}
+uint64_t seg_rs_tile_vecs(int) { return kSegBlock; }  // U = 1 for every rank count
 
 hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, int op, hipStream_t s) {
     switch (dtype) {
