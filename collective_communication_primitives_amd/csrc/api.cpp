@@ -96,14 +96,20 @@ dt_status fan_out(const void* const* src, const size_t* counts, void* const* tab
 // in-place AllGather of the chunks.  It moves (2P+1)S bytes against the
 // one-shot fold's 2PS, but as a P-to-1 fold and a 1-to-P fan-out whose
 // sources (S bytes in all) are still in the 256 MB Infinity Cache when the
-// fan-out reads them.  Measured on the MI355X against the one-shot kernel:
-// P=16 gains 2-7% from 32 to 256 MiB per rank, P=8 3-6% from 128 to 256 MiB;
-// both lose beyond 256 MiB, where the chunks no longer fit the cache, and
-// below, where the second launch costs more than the pattern saves; P <= 4
-// loses at every size.
+// fan-out reads them (beyond 256 MiB the fan-out pulls them back window by
+// window).  Measured on the MI355X against the one-shot kernel, each size
+// under two buffer placements: P >= 16 gains 4-10% from 16 MiB per rank up
+// to 1 GiB (one tie at 1 GiB); P = 8 gains 2-15% from 24 to 256 MiB (bf16
+// at 96 MiB loses 1-4%), ties at 384 MiB and loses 2% at 512 MiB in fp32;
+// P = 4 gains 0-7% at 128-192 MiB, is mixed at 96 and 256 MiB and loses
+// 18-26% at 320 MiB.  Below these windows the second launch costs more than
+// the pattern saves.  Other rank counts keep the one-shot form.
 bool two_shot_pays(int nranks, uint64_t bytes_per_rank) {
-    if (nranks < 8 || bytes_per_rank > (256ull << 20)) return false;
-    return bytes_per_rank >= (nranks >= 16 ? (32ull << 20) : (128ull << 20));
+    constexpr uint64_t MiB = 1ull << 20;
+    if (nranks >= 16) return bytes_per_rank >= 16 * MiB;
+    if (nranks >= 8) return bytes_per_rank >= 24 * MiB && bytes_per_rank <= 256 * MiB;
+    if (nranks == 4) return bytes_per_rank >= 128 * MiB && bytes_per_rank <= 192 * MiB;
+    return false;
 }
 
 // Validated AllReduce over one contiguous range per rank.

@@ -66,13 +66,14 @@ typedef enum {
  * sec. 2.3 (the same-device listing folds rank 0 then ranks 1..P-1 on one
  * rank and hands the result to all).  Usually one launch: each element is
  * read once per rank and written once per rank (the one-shot form of the
- * c10d page, sec. 9.4).  For P >= 8 and 128 MiB (P >= 16: 32 MiB) to 256 MiB
- * per rank, with count a multiple of P * (16 bytes / element size) and
- * 16-byte aligned buffers, it runs as a ReduceScatter into chunk r of
- * recv[r] followed by an in-place AllGather of the chunks, which is faster
- * there; both forms fold in the same order and give identical bits.  In
- * place is allowed (send[r] == recv[r]); any other overlap between buffers
- * is undefined.  send[r] and recv[r] hold `count` elements. */
+ * c10d page, sec. 9.4).  From 16 MiB per rank up for P >= 16, from 24 to
+ * 256 MiB for 8 <= P < 16 and from 128 to 192 MiB for P = 4, with count a
+ * multiple of P * (16 bytes / element size) and 16-byte aligned buffers, it
+ * runs as a ReduceScatter into chunk r of recv[r] followed by an in-place
+ * AllGather of the chunks, which is faster there; both forms fold in the
+ * same order and give identical bits.  In place is allowed (send[r] ==
+ * recv[r]); any other overlap between buffers is undefined.  send[r] and
+ * recv[r] hold `count` elements. */
 dt_status dt_allreduce(const void* const* send, void* const* recv, int nranks, size_t count,
                        dt_dtype dtype, dt_op op, hipStream_t stream);
 

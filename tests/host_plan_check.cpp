@@ -716,13 +716,23 @@ void two_shot() {
     const Case cases[] = {
         {8, DT_BFLOAT16, size_t(64) << 20, false, true},           // 128 MiB per rank
         {8, DT_BFLOAT16, size_t(64) << 20, true, true},
+        {8, DT_BFLOAT16, size_t(12) << 20, false, true},           // 24 MiB: the lower edge at P=8
+        {8, DT_BFLOAT16, (size_t(12) << 20) - 64, false, false},   // just below it
+        {8, DT_FLOAT32, size_t(64) << 20, false, true},            // 256 MiB: the upper edge at P=8
+        {8, DT_FLOAT32, (size_t(64) << 20) + 32, false, false},    // just beyond it
+        {16, DT_FLOAT32, size_t(4) << 20, false, true},            // 16 MiB: the lower edge at P=16
+        {16, DT_FLOAT32, (size_t(4) << 20) - 64, false, false},    // just below it
         {16, DT_FLOAT32, size_t(8) << 20, false, true},            // 32 MiB
         {16, DT_FLOAT32, size_t(64) << 20, true, true},            // 256 MiB
+        {16, DT_FLOAT32, (size_t(96) << 20) + 64, false, true},    // 384 MiB + 256 B: a windowed fan-out
         {12, DT_INT32, size_t(48) << 20, false, true},             // 192 MiB
-        {8, DT_FLOAT32, size_t(16) << 20, false, false},           // 64 MiB at P=8
         {8, DT_BFLOAT16, (size_t(64) << 20) + 8, false, false},    // not a multiple of P vectors
-        {16, DT_FLOAT32, (size_t(64) << 20) + 64, false, false},   // just beyond 256 MiB
-        {4, DT_FLOAT32, size_t(32) << 20, false, false},           // P=4
+        {4, DT_FLOAT32, size_t(32) << 20, false, true},            // 128 MiB at P=4
+        {4, DT_FLOAT32, size_t(48) << 20, true, true},             // 192 MiB at P=4
+        {4, DT_FLOAT32, size_t(16) << 20, false, false},           // 64 MiB at P=4
+        {4, DT_FLOAT32, (size_t(48) << 20) + 16, false, false},    // just beyond 192 MiB at P=4
+        {2, DT_FLOAT32, size_t(32) << 20, false, false},           // P=2
+        {6, DT_FLOAT32, size_t(48) << 20, false, false},           // P=6
     };
     char* base = reinterpret_cast<char*>(uintptr_t(1) << 45);  // fake, never dereferenced
     for (const Case& c : cases) {
@@ -747,14 +757,21 @@ void two_shot() {
             CHECK(g_gather_pieces.empty(), "allreduce of %zu bytes per rank at P=%d took the two-shot form", bytes, c.p);
             continue;
         }
-        CHECK(g_launches - before == 2, "two-shot allreduce: %ld launches", g_launches - before);
         const uint64_t cb = bytes / c.p;
-        CHECK(int(g_gather_pieces.size()) == c.p, "two-shot allreduce: %zu gather pieces", g_gather_pieces.size());
+        if (bytes <= dt::kFanOutDirectBytes)
+            CHECK(g_launches - before == 2, "two-shot allreduce: %ld launches", g_launches - before);
+        // every chunk r is fanned out from recv[r] + r * cb to offset r * cb, in order, once
         for (int r = 0; r < c.p; r++) {
-            const GatherPiece& g = g_gather_pieces[r];
-            CHECK(g.src == static_cast<const char*>(recv[r]) + r * cb && g.bytes == cb &&
-                      g.dst0 == static_cast<const char*>(recv[0]) + r * cb,
-                  "two-shot allreduce: piece %d", r);
+            const char* s0 = static_cast<const char*>(recv[r]) + r * cb;
+            uint64_t covered = 0;
+            for (const GatherPiece& g : g_gather_pieces) {
+                if (g.src < s0 || g.src >= s0 + cb) continue;
+                CHECK(g.src == s0 + covered && g.dst0 == static_cast<const char*>(recv[0]) + r * cb + covered,
+                      "two-shot allreduce: chunk %d piece out of place", r);
+                covered += g.bytes;
+            }
+            CHECK(covered == cb, "two-shot allreduce: chunk %d covered %llu of %llu bytes", r,
+                  (unsigned long long)covered, (unsigned long long)cb);
         }
     }
     g_bufs.clear();

@@ -94,6 +94,10 @@ def test_allreduce_full_size_fp32_and_int32(dt, orc):
     (8, "i32", 32 << 20, "max", True),        # 128 MiB
     (9, "f32", 33554448, "min", False),       # 128 MiB + 64 B, a multiple of 9 vectors; nine of sixteen slots
     (8, "f32", (32 << 20) + 4, "sum", False), # 128 MiB + 16 B, not a multiple of 8 vectors: one-shot
+    (8, "bf16", 12 << 20, "sum", False),      # 24 MiB: the lower edge at P=8
+    (16, "f32", 4 << 20, "max", False),       # 16 MiB: the lower edge at P=16
+    (4, "f32", 32 << 20, "sum", True),        # 128 MiB at P=4
+    (16, "f32", (64 << 20) + 64, "sum", False),  # 256 MiB + 256 B: the fan-out goes window by window
 ])
 def test_allreduce_two_shot_window(dt, orc, p, dtype, n, op, in_place):
     """AllReduce sizes where the library runs a ReduceScatter into each
