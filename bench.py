@@ -604,8 +604,9 @@ def probe_rows(dt, torch, reps: int = 3):
     uneven AllGather and the two-shot AllReduce share the gather kernel): the
     AllToAll (k_all_to_all), the uneven AllGather (the windowed fan-out and
     its read pass), the two-shot AllReduce at the bench step's shape (its
-    ReduceScatter and gather), one layer of the in-place
-    bucket AllReduce (k_reduce_pieces at P=8) and one layer of the gradient
+    ReduceScatter and gather), one layer of the in-place bucket AllReduce
+    (two-shot AllReduces of its large tensors, the fold of the small ones at
+    P=8) and one layer of the gradient
     pipeline (the segmented ReduceScatter at P=4 and the bucket folds at
     P=2).  Prints one JSON line per workload with its algorithmic bytes."""
     import numpy as np
@@ -643,7 +644,8 @@ def probe_rows(dt, torch, reps: int = 3):
     numels = [int(np.prod(sh)) for sh in synth.LAYER_SHAPES]
     per_rank_layer = sum(numels) * 2
     run("bucket_allreduce_layer_p8", lambda: dt.dt_bucket_allreduce(layer, bucket_bytes=synth.BUCKET_BYTES),
-        2 * P * per_rank_layer, ["k_reduce_pieces<dt::PieceArgs, 1, 0, 8, true>"])
+        2 * P * per_rank_layer, ["k_reduce_scatter_vec<1, 0, 8, true, 64, 1>", "k_gather<8, true, 1, 128>",
+                                 "k_reduce_pieces<dt::PieceArgs, 1, 0, 8, true>"])
     rep, sh = 2, 4
     fused = [torch.empty(sum(numels) // sh, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
     pipe = dt.HSDPPipeline(rep, sh, bucket_bytes=synth.BUCKET_BYTES)

@@ -739,6 +739,13 @@ dt_status dt_bucket_plan(const size_t* numels, int ntensors, size_t elem_size, s
     return DT_OK;
 }
 
+// Tensors at least this large (bytes per rank) get an AllReduce of their own
+// in the in-place bucket path.  Measured on the 32-layer data-parallel
+// workload (32 and 86 MiB tensors, P=8 bf16, in-process): one AllReduce per
+// tensor took 34.8 ms (35.4 ms with the one-shot kernel only) against 36.3
+// ms for the multi-tensor fold of every piece.
+constexpr size_t kOwnAllReduceBytes = size_t(16) << 20;
+
 dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int ntensors, int nranks, size_t bucket_bytes,
                               void* const* bucket_ws, dt_dtype dtype, dt_op op, hipStream_t stream) {
     g_last_error.clear();
@@ -770,9 +777,21 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
     std::vector<PieceRef> pieces;
     if (!bucket_ws) {
         // Reduced in place, straight out of the tensors: each element's fold is
-        // independent, so the pieces of every bucket go out together, in as
-        // few launches as the piece tables allow, instead of one per bucket.
-        for (const Piece& p : plan) pieces.push_back(piece_ref(p));
+        // independent, so bucket boundaries do not matter here.  A tensor of at
+        // least kOwnAllReduceBytes per rank is AllReduced on its own, as
+        // dt_allreduce does it (the two-shot form where that is faster); the
+        // pieces of all smaller tensors go out together, in as few launches as
+        // the piece tables allow.
+        auto own = [&](int t) { return numels[t] * es >= kOwnAllReduceBytes; };
+        for (int t = 0; t < ntensors; t++) {
+            if (!own(t)) continue;
+            void* ptrs[DT_MAX_RANKS];
+            for (int r = 0; r < nranks; r++) ptrs[r] = grads[size_t(r) * ntensors + t];
+            if ((st = allreduce_impl(ptrs, ptrs, nranks, numels[t], dtype, op, stream)) != DT_OK) return st;
+        }
+        for (const Piece& p : plan)
+            if (!own(p.tensor)) pieces.push_back(piece_ref(p));
+        if (pieces.empty()) return DT_OK;
         return run_pieces(pieces, nranks, dtype, op, nullptr, kFold, stream);
     }
     size_t i = 0;

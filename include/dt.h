@@ -142,8 +142,10 @@ dt_status dt_all_to_all(const void* const* send, void* const* recv, int nranks, 
  *     each bucket is copied in by one multi-tensor launch, reduced in place,
  *     and copied back by one launch (the page's flatten/unflatten).
  *   bucket_ws == NULL: the buckets are reduced straight out of the tensors
- *     and back into them (no staging copies), all of them together in as
- *     few multi-tensor launches as the piece tables allow: one for up to
+ *     and back into them (no staging copies).  A tensor of at least 16 MiB
+ *     per rank is AllReduced on its own, exactly as dt_allreduce would do
+ *     it; the pieces of the smaller tensors go out together in as few
+ *     multi-tensor launches as the piece tables allow: one for up to
  *     min(32, 320 / nranks) pieces, else one per min(512, 4096 / nranks).
  * Both forms give the same bits as dt_allreduce on each tensor.  bucket_bytes
  * must be a positive multiple of 16. */

@@ -128,6 +128,15 @@ hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t e, unsigned) {
 // ------------------------------------------------- launcher stand-ins --
 namespace dt {
 
+// While g_log_folds is set, the reduce, piece-fold and gather stand-ins
+// record every byte range they write on rank 0 (start, bytes): an in-place
+// AllReduce plan must write each element of rank 0's tensors exactly once.
+bool g_log_folds = false;
+std::vector<std::pair<const char*, uint64_t>> g_fold_log;
+void log_fold(const void* p, uint64_t bytes) {
+    if (g_log_folds && bytes) g_fold_log.push_back({static_cast<const char*>(p), bytes});
+}
+
 // Output vectors per tile of the segmented ReduceScatter.  Deliberately not
 // the library's value: the planning code must take the tile size from this
 // function, never from a constant of its own.
@@ -137,6 +146,7 @@ hipError_t launch_reduce_vec(const ReduceArgs& a, int, int, hipStream_t) {
     g_launches++;
     CHECK(a.nranks >= 1 && a.nranks <= kMaxRanksHost, "reduce_vec nranks %d", a.nranks);
     const uint64_t bytes = a.count * 16;
+    log_fold(a.dst[0], bytes);
     for (int r = 0; r < a.nranks; r++) {
         CHECK(al16(a.src[r]) && al16(a.dst[r]), "reduce_vec buffers not 16-byte aligned");
         touch(a.src[r], 0, a.rs ? bytes * a.nranks : bytes, false, "reduce_vec read");
@@ -148,6 +158,7 @@ hipError_t launch_reduce_vec(const ReduceArgs& a, int, int, hipStream_t) {
 hipError_t launch_reduce_elems(const ReduceArgs& a, int dtype, int, hipStream_t) {
     g_launches++;
     const size_t es = esize(dtype);
+    log_fold(static_cast<const char*>(a.dst[0]) + a.first * es, a.count * es);
     for (int r = 0; r < a.nranks; r++) {
         if (a.rs) {
             for (int c = 0; c < a.nranks; c++)
@@ -172,6 +183,7 @@ void check_piece_table(const Args& a, int npieces_cap, int ptr_cap, size_t es, b
         for (int r = 0; r < a.nranks; r++) {
             const void* p = a.ptr[k * a.nranks + r];
             if (fold) {
+                if (r == 0) log_fold(p, a.len[k] * es);
                 touch(p, 0, a.len[k] * es, true, what);  // reduced in place
             } else {
                 touch(p, 0, a.len[k] * es, !to_ws, what);
@@ -265,9 +277,11 @@ hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t)
 hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t) {
     g_launches++;
     for (int r = 0; r < a.nranks; r++)
-        if (a.bytes[r])
+        if (a.bytes[r]) {
             g_gather_pieces.push_back(GatherPiece{static_cast<const char*>(a.src[r]), a.bytes[r],
                                                   static_cast<const char*>(a.dst[r * a.nranks])});
+            if (a.dst[r * a.nranks] != a.src[r]) log_fold(a.dst[r * a.nranks], a.bytes[r]);
+        }
     std::vector<uint64_t> want;
     for (int r = 0; r < a.nranks; r++) want.push_back(ceil_div(a.bytes[r], kGatherTileBytes));
     check_tiles(a.tile_start, want, tiles, "gather");
@@ -579,6 +593,46 @@ void buckets() {
     }
 }
 
+// In place, tensors of at least 16 MiB per rank take an AllReduce of their
+// own (two-shot or one-shot with a ragged tail) and the rest one fold: rank
+// 0's copy of every tensor is written exactly once, with no gap or overlap.
+void bucket_big() {
+    const int p = 8, nt = 6;
+    const size_t es = 2;
+    const size_t numels[nt] = {size_t(16) << 20, 4096, (size_t(8) << 20) + 3, 100, size_t(44) << 20,
+                               (size_t(8) << 20) - 8};
+    g_bufs.clear();
+    char* base = reinterpret_cast<char*>(uintptr_t(1) << 44);  // fake, never dereferenced
+    std::vector<void*> grads(size_t(p) * nt);
+    for (int r = 0; r < p; r++)
+        for (int t = 0; t < nt; t++) {
+            grads[r * nt + t] = base + (uint64_t(r) << 36) + (uint64_t(t) << 30);
+            reg(grads[r * nt + t], numels[t] * es, true);
+        }
+    dt::g_fold_log.clear();
+    dt::g_log_folds = true;
+    expect(dt_bucket_allreduce(grads.data(), numels, nt, p, size_t(25) << 20, nullptr, DT_BFLOAT16, DT_SUM, nullptr),
+           DT_OK, "bucket in place, large tensors");
+    dt::g_log_folds = false;
+    for (int t = 0; t < nt; t++) {
+        const char* t0 = static_cast<const char*>(grads[t]);
+        const uint64_t bytes = numels[t] * es;
+        std::vector<std::pair<const char*, uint64_t>> in;
+        for (const auto& e : dt::g_fold_log)
+            if (e.first < t0 + bytes && e.first + e.second > t0) in.push_back(e);
+        std::sort(in.begin(), in.end());
+        uint64_t at = 0;
+        for (const auto& e : in) {
+            CHECK(e.first == t0 + at, "bucket in place: tensor %d written at +%lld, expected +%llu", t,
+                  (long long)(e.first - t0), (unsigned long long)at);
+            at += e.second;
+        }
+        CHECK(at == bytes, "bucket in place: tensor %d covered %llu of %llu bytes", t, (unsigned long long)at,
+              (unsigned long long)bytes);
+    }
+    g_bufs.clear();
+}
+
 void hsdp_and_sync() {
     const int meshes[][2] = {{2, 4}, {1, 8}, {8, 1}, {4, 4}, {2, 2}, {1, 1}, {16, 1}, {1, 16}};
     for (auto& mesh : meshes) {
@@ -784,6 +838,7 @@ int main() {
     reductions();
     copies();
     buckets();
+    bucket_big();
     hsdp_and_sync();
     if (g_fail) {
         fprintf(stderr, "%d checks failed\n", g_fail);

@@ -90,6 +90,27 @@ def test_bucket_unaligned_tensors(dt, orc):
             compare(to_np(grads[r][t]), want[r][t])
 
 
+@pytest.mark.parametrize("p,dtype,sizes", [
+    # 16 MiB + 20 B (its own one-shot AllReduce, ragged tail), 24 MiB (two-shot),
+    # 16 MiB - 16 B (folded with the small ones)
+    (8, "f32", [(4 << 20) + 5, 33, 6 << 20, (4 << 20) - 4]),
+    (16, "bf16", [8 << 20, 7, 1000]),  # 16 MiB: two-shot at P=16
+    (8, "i32", [1, (8 << 20) + 64]),   # 32 MiB + 256 B: two-shot, after a one-element tensor
+])
+def test_bucket_large_tensors_in_place(dt, orc, p, dtype, sizes):
+    """In place, tensors of at least 16 MiB per rank are AllReduced on their
+    own and the rest folded together; every element equals the oracle's."""
+    note(f"bucket allreduce large tensors P={p} {dtype} sizes={sizes}")
+    grads = make_grads(p, sizes, dtype, seed=77 + p)
+    host = [[to_np(g) for g in rank] for rank in grads]
+    dt.dt_bucket_allreduce(grads, bucket_bytes=synth.BUCKET_BYTES)
+    torch.cuda.synchronize()
+    want = orc.bucket_allreduce(host, synth.BUCKET_BYTES, "sum")
+    for r in range(p):
+        for t in range(len(sizes)):
+            compare(to_np(grads[r][t]), want[r][t], f"rank {r} tensor {t}")
+
+
 def test_bucket_one_layer_full_size(dt, orc):
     """Pure data-parallel variant of the gradient workload: P=8, one layer's
     9 bf16 tensors (386 MiB per rank), 25 MiB buckets, with and without the

@@ -62,6 +62,9 @@ MUTANTS = {
     # the windows of a large fan-out go out without their read passes
     "window_skips_read_pass": ("if (touch_first && (st = check_hip(dt::launch_gather_touch(",
                                "if (false && touch_first && (st = check_hip(dt::launch_gather_touch("),
+    # in place, a large tensor is both AllReduced on its own and folded with the small ones
+    "bucket_big_tensor_folded_twice": ("            if (!own(p.tensor)) pieces.push_back(piece_ref(p));",
+                                       "            pieces.push_back(piece_ref(p));"),
     # the windowed fan-out of large sources skips 16 bytes after every piece
     "fan_out_window_skips_bytes": ("            off += take;\n            fill += take;",
                                    "            off += take + 16;\n            fill += take;"),
