@@ -179,7 +179,7 @@ hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s);
 // Read pass over the gather's source tiles (plain loads, nothing stored).
 hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t s);
 constexpr uint64_t kFanOutDirectBytes = 256ull << 20;  // sources up to this size: one launch
-constexpr uint64_t kFanOutWindowBytes = 64ull << 20;    // larger sources: windows of this size
+constexpr uint64_t kFanOutWindowBytes = 128ull << 20;   // larger sources: windows of this size
 hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t s);
 hipError_t launch_copy_segments(const SegCopyArgs& a, hipStream_t s);
 hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_t s);

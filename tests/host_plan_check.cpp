@@ -754,8 +754,8 @@ void big_fan_out() {
     g_bufs.clear();
 }
 
-// The two-shot AllReduce (P >= 8; 128 MiB, or 32 MiB at P >= 16, up to
-// 256 MiB per rank): fake device ranges.  The ReduceScatter must write chunk
+// The two-shot AllReduce (P >= 16 from 16 MiB per rank, P = 8-15 at 24-256
+// MiB, P = 4 at 128-192 MiB): fake device ranges.  The ReduceScatter must write chunk
 // r of recv[r] only, and the gather must fan chunk r of recv[r] out to chunk
 // r of every output.  Sizes outside the window keep the one-shot launch.
 void two_shot() {
