@@ -117,6 +117,28 @@ def test_allreduce_two_shot_window(dt, orc, p, dtype, n, op, in_place):
         assert torch.equal(bits(ys[q]), bits(ys[0])), f"rank {q} differs from rank 0"
 
 
+@pytest.mark.parametrize("p,dtype,n,op", [
+    (8, "bf16", (128 << 20) + 5, "sum"),   # 256 MiB + 10 B: beyond the P=8 two-shot window, ragged tail
+    (12, "f32", (64 << 20) + 4, "max"),    # 256 MiB + 16 B at P=12 (twelve of sixteen slots)
+    (16, "f32", (64 << 20) + 1, "sum"),    # P=16, not a whole number of vectors per chunk
+])
+def test_allreduce_one_shot_wave_tiles(dt, orc, p, dtype, n, op):
+    """One-shot AllReduces of more than 256 MiB per rank at P >= 8, which run
+    in single-wave tiles (plus the element path for a ragged tail).  Rank 0's
+    output is compared with the oracle element by element; every other
+    rank's output must equal rank 0's bit for bit."""
+    note(f"allreduce one-shot wave tiles P={p} {dtype} n={n} {op}")
+    xs = rank_inputs(dtype, p, n, seed=90 + p)
+    ys = [torch.empty_like(x) for x in xs]
+    dt.dt_allreduce(xs, ys, op=op)
+    torch.cuda.synchronize()
+    want = orc.allreduce([to_np(x) for x in xs], op)[0]
+    compare(to_np(ys[0]), want, "rank 0")
+    bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
+    for q in range(1, p):
+        assert torch.equal(bits(ys[q]), bits(ys[0])), f"rank {q} differs from rank 0"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
 @pytest.mark.parametrize("op", ["sum", "max", "min"])
 @pytest.mark.parametrize("p,m", [(1, 5), (2, 4096), (3, 1001), (8, 8), (8, 4099), (16, 640)])
