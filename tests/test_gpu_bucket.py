@@ -57,6 +57,30 @@ def test_bucket_allreduce(dt, orc, use_ws, dtype, op, p, bucket):
             compare(to_np(grads[r][t]), want[r][t], f"rank {r} tensor {t}")
 
 
+@pytest.mark.parametrize("npieces", [1, 7, 8, 9, 16, 17, 24, 25, 31, 32])
+def test_bucket_piece_counts(dt, orc, npieces):
+    """In place, small tensors under one large bucket: each non-empty tensor is
+    one piece of one launch, so the launch's piece table holds exactly
+    `npieces` entries (the lookup's group edges are at 8, 16 and 24).  Empty
+    tensors in between yield no piece."""
+    p = 4
+    rng = np.random.default_rng(npieces)
+    sizes = []
+    for k in range(npieces):
+        sizes.append(int(rng.integers(1, 3000)))
+        if k % 5 == 2:
+            sizes.append(0)
+    note(f"bucket allreduce P={p} pieces={npieces}")
+    grads = make_grads(p, sizes, "f32", seed=300 + npieces)
+    host = [[to_np(g) for g in rank] for rank in grads]
+    dt.dt_bucket_allreduce(grads, bucket_bytes=synth.BUCKET_BYTES)
+    torch.cuda.synchronize()
+    want = orc.bucket_allreduce(host, synth.BUCKET_BYTES, "sum")
+    for r in range(p):
+        for t in range(len(sizes)):
+            compare(to_np(grads[r][t]), want[r][t], f"rank {r} tensor {t}")
+
+
 @pytest.mark.parametrize("use_ws", [False, True])
 def test_bucket_many_small_tensors(dt, orc, use_ws):
     """More pieces per bucket than one argument block holds: several launches per bucket."""
