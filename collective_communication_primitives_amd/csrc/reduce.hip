@@ -3,9 +3,10 @@
 //
 // Work layout.  Rank buffers are P separate contiguous allocations in HBM.
 // Each thread owns whole 16-byte vectors: it issues the loads of its vectors
-// from every rank before folding, so a workgroup keeps P x U x 4 KiB of reads
-// in flight, then folds in rank order and writes the result (to every rank
-// for AllReduce, to the owning rank for ReduceScatter).  Every HBM byte is
+// from every rank before folding, so a workgroup keeps P tiles of reads in
+// flight (one per rank, 1-8 KiB each by kernel), then folds in rank order and
+// writes the result (to every rank for AllReduce, to the owning rank for
+// ReduceScatter).  Every HBM byte is
 // touched once: AllReduce moves 2*P*S bytes, ReduceScatter (P+1)*S.
 //
 // The rank count is a template upper bound PMAX in {1, 2, 4, 8, 16}.  When
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(BLOCK) void k_reduce_vec(ReduceArgs a) {
 // wave with one vector per thread (1 KiB of every rank per workgroup) for
 // every P.  In-process A/B: 2.5% faster than 512 threads x 1 vector at P=8
 // bf16 and no slower at any of 13 placements of the inputs tried; 5-7%
-// faster than 256 threads x 4 vectors at P=4, even at P=2.
+// faster than 256 threads x 4 vectors at P=4 and no slower at P=2.
 template <int DT, int OP, int PMAX, bool EXACT, int BLOCK, int U>
 __global__ __launch_bounds__(BLOCK) void k_reduce_scatter_vec(ReduceArgs a) {
     constexpr uint64_t kTileVecs = uint64_t(BLOCK) * U;
