@@ -308,29 +308,38 @@ constexpr uint64_t kWaveAllReduceBytes = 256ull << 20;
 template <int PMAX>
 constexpr int ar_unroll() { return PMAX == 1 ? 4 : 2; }
 
+// True when the launch uses one-wave tiles (kWaveBlock vectors per workgroup).
+template <int PMAX>
+bool wave_tiles(const ReduceArgs& a) {
+    return a.rs || (PMAX >= 8 && a.count * 16 > kWaveAllReduceBytes);
+}
+
 template <int DT, int OP, int PMAX, bool EXACT>
-void reduce_vec_launch(const ReduceArgs& a, uint64_t blocks, bool wave, hipStream_t s) {
+void reduce_vec_launch(const ReduceArgs& a, uint64_t blocks, hipStream_t s) {
     if (a.rs) {
         const dim3 grid(unsigned(blocks), unsigned(a.nranks));
         k_reduce_scatter_vec<DT, OP, PMAX, EXACT, kWaveBlock, 1><<<grid, kWaveBlock, 0, s>>>(a);
-    } else if (wave) {
-        if constexpr (PMAX >= 8) k_reduce_vec<DT, OP, PMAX, EXACT, 1, kWaveBlock><<<unsigned(blocks), kWaveBlock, 0, s>>>(a);
-    } else {
-        k_reduce_vec<DT, OP, PMAX, EXACT, ar_unroll<PMAX>(), kBlock><<<unsigned(blocks), kBlock, 0, s>>>(a);
+        return;
     }
+    if constexpr (PMAX >= 8) {
+        if (wave_tiles<PMAX>(a)) {
+            k_reduce_vec<DT, OP, PMAX, EXACT, 1, kWaveBlock><<<unsigned(blocks), kWaveBlock, 0, s>>>(a);
+            return;
+        }
+    }
+    k_reduce_vec<DT, OP, PMAX, EXACT, ar_unroll<PMAX>(), kBlock><<<unsigned(blocks), kBlock, 0, s>>>(a);
 }
 
 template <int DT, int OP, int PMAX>
 hipError_t reduce_vec_p(const ReduceArgs& a, hipStream_t s) {
-    const bool wave = a.rs || (PMAX >= 8 && a.count * 16 > kWaveAllReduceBytes);
-    const uint64_t per_block = wave ? uint64_t(kWaveBlock) : uint64_t(kBlock) * ar_unroll<PMAX>();
+    const uint64_t per_block = wave_tiles<PMAX>(a) ? uint64_t(kWaveBlock) : uint64_t(kBlock) * ar_unroll<PMAX>();
     const uint64_t blocks = (a.count + per_block - 1) / per_block;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
     if (a.nranks == PMAX)
-        reduce_vec_launch<DT, OP, PMAX, true>(a, blocks, wave, s);
+        reduce_vec_launch<DT, OP, PMAX, true>(a, blocks, s);
     else
-        reduce_vec_launch<DT, OP, PMAX, false>(a, blocks, wave, s);
+        reduce_vec_launch<DT, OP, PMAX, false>(a, blocks, s);
     return hipGetLastError();
 }
 
