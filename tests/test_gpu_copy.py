@@ -161,6 +161,30 @@ def test_all_to_all(dt, orc, dtype, p, hi, seed):
         assert torch.equal(back[i].view(torch.uint8), xs[i].view(torch.uint8)), i
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_to_all_tile_edges(dt, orc, dtype):
+    """Blocks of one tile (1 KiB) and two, exactly and one element either
+    side, plus empty and one-element blocks: a block's last tile may hold a
+    single element, and with bf16 its end falls mid-vector."""
+    p = 4
+    es = 4 if dtype == "f32" else 2
+    t = 1024 // es  # elements per tile
+    choices = [0, 1, t - 1, t, t + 1, 2 * t - 1, 2 * t, 2 * t + 1, 3]
+    rng = np.random.default_rng(11)
+    s = rng.choice(choices, (p, p))
+    note(f"all_to_all tile edges {dtype} P={p} splits={s.tolist()}")
+    xs = _ranks(dtype if dtype != "bf16" else "i32", [int(s[i].sum()) for i in range(p)], 21)
+    if dtype == "bf16":
+        xs = [x.to(torch.int16).view(torch.bfloat16) for x in xs]
+    outs = [Guarded(int(s[:, j].sum()), DTYPES[dtype]).poison() for j in range(p)]
+    dt.dt_all_to_all(xs, [o.t for o in outs], s.tolist())
+    torch.cuda.synchronize()
+    want = orc.all_to_all([to_np(x) for x in xs], s)
+    for j, o in enumerate(outs):
+        o.check()
+        np.testing.assert_array_equal(to_np(o.t).view(np.uint8), want[j].view(np.uint8))
+
+
 def test_all_to_all_full_size(dt, orc):
     """P=8, fp32 rows of width 4096, split matrix U[0, 4096] rows (seeded)."""
     s_rows = synth.split_matrix(seed=0)
