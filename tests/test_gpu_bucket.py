@@ -193,6 +193,28 @@ def test_hsdp_pipeline_small(dt, orc, rep, sh, one_stream):
                 compare(to_np(views[t]), want[r][t], f"layer {l} rank {r} tensor {t}")
 
 
+@pytest.mark.parametrize("rep,sh", [(2, 4), (1, 8)])
+def test_hsdp_pipeline_tile_edges(dt, orc, rep, sh):
+    """Shard chunks that cross the segmented ReduceScatter's 1 KiB output
+    tiles (512 bf16 elements): one element past a tile, exactly two or four
+    tiles, and a chunk of a few elements, over 3 layers."""
+    p = rep * sh
+    shapes = [(8 * 129, 4), (8 * 64, 16), (8 * 3, 3)]  # chunks of 1032 / 2048 / 18 elements at S=4
+    nl = 3
+    note(f"hsdp pipeline tile edges R={rep} S={sh}")
+    layers = [[[synth.normal_ranks(1, s, seed=(l * 64 + r) * 16 + t + 7, device="cuda")[0] for t, s in enumerate(shapes)]
+               for r in range(p)] for l in range(nl)]
+    fused, numels = run_pipeline(dt, layers, rep, sh, bucket=4096, shapes=shapes, one_stream=True)
+    torch.cuda.synchronize()
+    for l in range(nl):
+        host = [[to_np(g) for g in rank] for rank in layers[l]]
+        want = orc.hsdp_layer(host, rep, sh, 4096, "sum")
+        for r in range(p):
+            views = dt.shard_views(fused[l][r], numels, sh)
+            for t in range(len(shapes)):
+                compare(to_np(views[t]), want[r][t], f"layer {l} rank {r} tensor {t}")
+
+
 def _sampled_layer_check(orc, grads, fused_r, numels, rep, sh, k_samples, rng):
     """Recompute K sampled outputs per tensor with the oracle from the actual
     device inputs: for shard index k of tensor t, each rank's elements
