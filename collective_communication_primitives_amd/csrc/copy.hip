@@ -45,15 +45,18 @@ __global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
             const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * BLOCK;
             if (v < v1) x[u] = load16_h<false>(src + v * 16);  // writes dominate 1:P
         }
+        // Buffer stores, non-temporal with device scope, one resource per
+        // destination over the tile's whole vectors (the range drops the lanes
+        // past them; the ragged bytes go below).  In-process A/B against plain
+        // non-temporal global stores: 1.4-4.3% faster on every fan-out workload
+        // on two machines, and no slower at any of 13 output placements.
+        const uint32_t vbytes = uint32_t(v1 * 16 - b0);
 #pragma unroll
         for (int q = 0; q < PMAX; q++) {
             if (q < nr && dsts[q] != src) {  // an in-place piece already sits in its own slot
-                char* dst = static_cast<char*>(dsts[q]);
+                const rsrc_t out = make_rsrc(static_cast<char*>(dsts[q]) + b0, vbytes);
 #pragma unroll
-                for (int u = 0; u < U; u++) {
-                    const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * BLOCK;
-                    if (v < v1) store16_h<true>(dst + v * 16, x[u]);
-                }
+                for (int u = 0; u < U; u++) bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * BLOCK) * 16, x[u]);
             }
         }
         const uint64_t t = v1 * 16 + threadIdx.x;  // ragged end: fewer than 16 bytes

@@ -26,8 +26,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // non-temporal hint is chosen per kernel from measurements on the MI355X
 // (1.1 GiB working sets, beyond the Infinity Cache): with reads dominating
 // (P-to-1 fold), non-temporal loads and device-scope stores are fastest; with
-// writes dominating (1-to-P fan-out), plain loads and non-temporal stores;
-// for the balanced P-to-P fold and for 1-to-1 copies, both non-temporal.
+// writes dominating (1-to-P fan-out), plain loads and non-temporal
+// device-scope stores; for the balanced P-to-P fold and for 1-to-1 copies,
+// both non-temporal.
 __device__ __forceinline__ u32x4 load16(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -38,11 +39,6 @@ template <bool NT>
 __device__ __forceinline__ u32x4 load16_h(const void* p) {
     if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     else return *reinterpret_cast<const u32x4*>(p);
-}
-template <bool NT>
-__device__ __forceinline__ void store16_h(void* p, u32x4 v) {
-    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-    else *reinterpret_cast<u32x4*>(p) = v;
 }
 
 // Buffer-instruction access.  A workgroup describes each contiguous range it
