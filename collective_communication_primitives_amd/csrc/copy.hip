@@ -136,11 +136,11 @@ __global__ __launch_bounds__(kA2AThreads) void k_all_to_all(AllToAllArgs a) {
             const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kA2AThreads;
             if (v < v1) x[u] = load16(src + v * 16);
         }
+        // stores: buffer instructions, non-temporal with device scope, over the
+        // tile's whole vectors (0.3-0.6% faster than non-temporal global stores)
+        const rsrc_t out = make_rsrc(dst + b0, uint32_t(v1 * 16 - b0));
 #pragma unroll
-        for (int u = 0; u < kCopyU; u++) {
-            const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kA2AThreads;
-            if (v < v1) store16(dst + v * 16, x[u]);
-        }
+        for (int u = 0; u < kCopyU; u++) bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * kA2AThreads) * 16, x[u]);
         const uint64_t t = v1 * 16 + threadIdx.x;
         if (t < b1) dst[t] = src[t];
     } else {
@@ -188,11 +188,12 @@ __global__ __launch_bounds__(kSegCopyBlock) void k_copy_segments(SegCopyArgs a) 
             const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kSegCopyBlock;
             if (v < v1) x[u] = load16(src + v * 16);
         }
+        // stores: buffer instructions, non-temporal with device scope, over the
+        // tile's whole vectors (ReplicateToShard 2.9-3.5% faster than with
+        // non-temporal global stores)
+        const rsrc_t out = make_rsrc(dst + b0, uint32_t(v1 * 16 - b0));
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kSegCopyBlock;
-            if (v < v1) store16(dst + v * 16, x[u]);
-        }
+        for (int u = 0; u < U; u++) bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * kSegCopyBlock) * 16, x[u]);
         const uint64_t t = v1 * 16 + threadIdx.x;
         if (t < b1) dst[t] = src[t];
     } else {

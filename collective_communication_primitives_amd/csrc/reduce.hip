@@ -17,6 +17,10 @@
 
 namespace dt {
 
+// One wave, one vector per thread: the tile of the ReduceScatter, and of a
+// one-shot AllReduce of P >= 8 ranks above kWaveAllReduceBytes per rank.
+constexpr int kWaveBlock = 64;
+
 // ------------------------------------------------------------- AllReduce --
 // grid.x covers a.count vectors in tiles of BLOCK*U.
 //
@@ -42,13 +46,31 @@ __global__ __launch_bounds__(BLOCK) void k_reduce_vec(ReduceArgs a) {
     u32x4 y[U];
 #pragma unroll
     for (int u = 0; u < U; u++) y[u] = fold_vec<DT, OP, PMAX>(x[u], nr);
+    if constexpr (BLOCK == kWaveBlock) {
+        // one-wave tiles (P >= 8 beyond 256 MiB per rank): buffer stores,
+        // non-temporal with device scope, 3% faster there than non-temporal
+        // global stores (in-process A/B, P=8 bf16 512 MiB); at 8-20 MiB with
+        // the larger tiles they measured 5-8% slower, so those keep global stores
+        const uint64_t t0 = uint64_t(blockIdx.x) * (BLOCK * U);
+        const uint64_t left = a.count - t0;
+        const uint32_t tb = uint32_t((left < uint64_t(BLOCK * U) ? left : uint64_t(BLOCK * U)) * 16);
 #pragma unroll
-    for (int q = 0; q < PMAX; q++) {
-        if (q < nr) {
+        for (int q = 0; q < PMAX; q++) {
+            if (q < nr) {
+                const rsrc_t out = make_rsrc(static_cast<char*>(a.dst[q]) + t0 * 16, tb);
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                const uint64_t v = base + uint64_t(u) * BLOCK;
-                if (v < a.count) store16(static_cast<char*>(a.dst[q]) + v * 16, y[u]);
+                for (int u = 0; u < U; u++) bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * BLOCK) * 16, y[u]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < PMAX; q++) {
+            if (q < nr) {
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const uint64_t v = base + uint64_t(u) * BLOCK;
+                    if (v < a.count) store16(static_cast<char*>(a.dst[q]) + v * 16, y[u]);
+                }
             }
         }
     }
@@ -294,9 +316,6 @@ int pmax_of(int nranks) {
     return nranks <= 1 ? 1 : nranks <= 2 ? 2 : nranks <= 4 ? 4 : nranks <= 8 ? 8 : 16;
 }
 
-// One wave, one vector per thread: the tile of the ReduceScatter, and of a
-// one-shot AllReduce of P >= 8 ranks above kWaveAllReduceBytes per rank.
-constexpr int kWaveBlock = 64;
 // One-shot AllReduce with P >= 8 in one-wave tiles beyond this many bytes per
 // rank (above the two-shot window): in-process A/B 3-5% faster at 512 MiB
 // and 1 GiB per rank (P=8 bf16, P=16 fp32), but 2-12% slower at 4-64 MiB.
