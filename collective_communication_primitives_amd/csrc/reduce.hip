@@ -28,7 +28,8 @@ constexpr int kWaveBlock = 64;
 // output.  Each wave then sends U KiB-long runs to one buffer before moving to
 // the next, which the MI355X's HBM serves faster than interleaving the P
 // buffers vector by vector (measured: +3% for the P-to-P AllReduce pattern).
-template <int DT, int OP, int PMAX, bool EXACT, int U, int BLOCK>
+// BST: store through buffer instructions (see the store loop).
+template <int DT, int OP, int PMAX, bool EXACT, int U, int BLOCK, bool BST = false>
 __global__ __launch_bounds__(BLOCK) void k_reduce_vec(ReduceArgs a) {
     const uint64_t base = uint64_t(blockIdx.x) * (BLOCK * U) + threadIdx.x;
     const int nr = EXACT ? PMAX : a.nranks;
@@ -46,11 +47,13 @@ __global__ __launch_bounds__(BLOCK) void k_reduce_vec(ReduceArgs a) {
     u32x4 y[U];
 #pragma unroll
     for (int u = 0; u < U; u++) y[u] = fold_vec<DT, OP, PMAX>(x[u], nr);
-    if constexpr (BLOCK == kWaveBlock) {
-        // one-wave tiles (P >= 8 beyond 256 MiB per rank): buffer stores,
-        // non-temporal with device scope, 3% faster there than non-temporal
-        // global stores (in-process A/B, P=8 bf16 512 MiB); at 8-20 MiB with
-        // the larger tiles they measured 5-8% slower, so those keep global stores
+    if constexpr (BLOCK == kWaveBlock || BST) {
+        // Buffer stores, non-temporal with device scope, where they measured
+        // faster than non-temporal global stores (in-process A/B): the one-wave
+        // tiles (P >= 8 beyond 256 MiB per rank, 3%) and P >= 8 up to
+        // kBufferStoreAllReduceBytes per rank (5-10% at 1-8 MiB).  Between the
+        // two (P=8 at 16-20 MiB, P=16 at 8 MiB in one run) they were up to 8%
+        // slower.
         const uint64_t t0 = uint64_t(blockIdx.x) * (BLOCK * U);
         const uint64_t left = a.count - t0;
         const uint32_t tb = uint32_t((left < uint64_t(BLOCK * U) ? left : uint64_t(BLOCK * U)) * 16);
@@ -321,6 +324,9 @@ int pmax_of(int nranks) {
 // and 1 GiB per rank (P=8 bf16, P=16 fp32), but 2-12% slower at 4-64 MiB.
 constexpr uint64_t kWaveAllReduceBytes = 256ull << 20;
 
+// One-shot AllReduce with P >= 8 up to this many bytes per rank: buffer stores.
+constexpr uint64_t kBufferStoreAllReduceBytes = 8ull << 20;
+
 // Vectors per thread of the one-shot AllReduce in kBlock-thread tiles,
 // measured on the MI355X for 25-256 MiB per rank: two, four for the plain
 // copy of P = 1.
@@ -343,6 +349,12 @@ void reduce_vec_launch(const ReduceArgs& a, uint64_t blocks, hipStream_t s) {
     if constexpr (PMAX >= 8) {
         if (wave_tiles<PMAX>(a)) {
             k_reduce_vec<DT, OP, PMAX, EXACT, 1, kWaveBlock><<<unsigned(blocks), kWaveBlock, 0, s>>>(a);
+            return;
+        }
+    }
+    if constexpr (PMAX >= 8) {
+        if (a.count * 16 <= kBufferStoreAllReduceBytes) {
+            k_reduce_vec<DT, OP, PMAX, EXACT, ar_unroll<PMAX>(), kBlock, true><<<unsigned(blocks), kBlock, 0, s>>>(a);
             return;
         }
     }
