@@ -50,8 +50,9 @@ __global__ __launch_bounds__(BLOCK) void k_reduce_vec(ReduceArgs a) {
     if constexpr (BLOCK == kWaveBlock || BST) {
         // Buffer stores, non-temporal with device scope, where they measured
         // faster than non-temporal global stores (in-process A/B): the one-wave
-        // tiles (P >= 8 beyond 256 MiB per rank, 3%) and P >= 8 up to
-        // kBufferStoreAllReduceBytes per rank (5-10% at 1-8 MiB).  Between the
+        // tiles (P >= 8 beyond 256 MiB per rank, 3%) and every P >= 2 up to
+        // kBufferStoreAllReduceBytes per rank (graph-replay times at 1-8 MiB:
+        // P=2 and P=4 6-20% faster, P=8 5-10% in eager loops).  Between the
         // two (P=8 at 16-20 MiB, P=16 at 8 MiB in one run) they were up to 8%
         // slower.
         const uint64_t t0 = uint64_t(blockIdx.x) * (BLOCK * U);
@@ -324,7 +325,7 @@ int pmax_of(int nranks) {
 // and 1 GiB per rank (P=8 bf16, P=16 fp32), but 2-12% slower at 4-64 MiB.
 constexpr uint64_t kWaveAllReduceBytes = 256ull << 20;
 
-// One-shot AllReduce with P >= 8 up to this many bytes per rank: buffer stores.
+// One-shot AllReduce with P >= 2 up to this many bytes per rank: buffer stores.
 constexpr uint64_t kBufferStoreAllReduceBytes = 8ull << 20;
 
 // Vectors per thread of the one-shot AllReduce in kBlock-thread tiles,
@@ -352,7 +353,7 @@ void reduce_vec_launch(const ReduceArgs& a, uint64_t blocks, hipStream_t s) {
             return;
         }
     }
-    if constexpr (PMAX >= 8) {
+    if constexpr (PMAX >= 2) {
         if (a.count * 16 <= kBufferStoreAllReduceBytes) {
             k_reduce_vec<DT, OP, PMAX, EXACT, ar_unroll<PMAX>(), kBlock, true><<<unsigned(blocks), kBlock, 0, s>>>(a);
             return;
