@@ -17,8 +17,10 @@ wait for the end event.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import threading
+import weakref
 from typing import Dict, List, Optional, Sequence
 
 import torch
@@ -154,7 +156,8 @@ class Work:
     def __init__(self, handle: ctypes.c_void_p, stash: List[torch.Tensor]):
         self._h = handle
         self._stash = stash
-        self._lib = _L  # kept for __del__, which may run during interpreter shutdown
+        self._lib = _L
+        _live_works.add(self)
 
     def wait(self, stream=None) -> None:
         """Make ``stream`` (default: current) wait for the end event; the host does not block."""
@@ -166,6 +169,17 @@ class Work:
         if rc < 0:
             raise DtError(DT_ERR_HIP, _L.dt_last_error().decode())
         return rc == 1
+
+    def _release(self) -> None:
+        """Free the handle now (at exit): wait for the work first if its
+        tensors are still held, so they are not released under it."""
+        h = getattr(self, "_h", None)
+        if h:
+            if getattr(self, "_stash", None):
+                torch.cuda.synchronize()
+            self._lib.dt_work_free(h)
+            self._h = None
+            self._stash = []
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -184,6 +198,33 @@ class Work:
 # while the collective can still touch them: they stay here until the work's
 # end event has completed, and are released by the next collective call.
 _shelf: List = []
+
+# Every object of this module that owns HIP handles, so that _release_all
+# can free them before the interpreter (and with it the HIP runtime and any
+# profiler attached to it) shuts down.
+_live_works: "weakref.WeakSet[Work]" = weakref.WeakSet()
+_live_pipelines: "weakref.WeakSet[HSDPPipeline]" = weakref.WeakSet()
+
+
+def _release_all() -> None:
+    """Free every HIP event the binding still owns, deterministically, while
+    the runtime is whole: live HSDP pipelines (their destroy waits for the
+    work they queued), live and shelved works.  Registered with atexit at
+    import; afterwards no destructor of this module calls into HIP.  The
+    tensors a work or pipeline kept alive are dropped only after its handle
+    has been released (the c10d page, sec. 5: a stash outlives its GPU work)."""
+    for pipe in list(_live_pipelines):
+        pipe.close()
+    for work in list(_live_works):
+        work._release()
+    if _shelf:
+        torch.cuda.synchronize()  # the shelved tensors may still be in use on the GPU
+        for h, _stash in _shelf:
+            _L.dt_work_free(h)
+        _shelf.clear()
+
+
+atexit.register(_release_all)
 
 
 def _unshelve() -> None:
@@ -483,7 +524,11 @@ class HSDPPipeline:
     one.  With every rank on one device both phases draw on the same HBM, and
     issuing them back to back on one stream, in the same order, measured 4%
     faster (30.5 vs 31.8 ms for the 32-layer workload), so one side stream
-    for both is the default; pass two streams for the split layout."""
+    for both is the default; pass two streams for the split layout.
+
+    A layer's fused buffers must not be passed again (as the next layer's)
+    before ``finish()``: the previous layer's AllReduce is still pending on
+    them, and the library refuses the overlap."""
 
     def __init__(self, replicate: int, shard: int, bucket_bytes: int = DEFAULT_BUCKET_BYTES,
                  dtype=torch.bfloat16, op="sum", rs_stream=None, ar_stream=None):
@@ -494,10 +539,11 @@ class HSDPPipeline:
         self.ar_stream = ar_stream if ar_stream is not None else torch.cuda.Stream()
         self._h = ctypes.c_void_p()
         self._stash: List[torch.Tensor] = []
-        self._lib = _L  # kept for __del__, which may run during interpreter shutdown
+        self._lib = _L
         _check(_L.dt_hsdp_create(replicate, shard, bucket_bytes, _DTYPES[dtype], _op_code(op),
                                  _stream_handle(self.rs_stream), _stream_handle(self.ar_stream),
                                  ctypes.byref(self._h)))
+        _live_pipelines.add(self)
 
     def post_backward(self, grads: Sequence[Sequence[torch.Tensor]], fused: Sequence[torch.Tensor],
                       producer=None) -> None:
@@ -520,11 +566,18 @@ class HSDPPipeline:
         _check(self._lib.dt_hsdp_finish(self._h, _stream_handle(consumer)))
         self._stash = []
 
-    def __del__(self):
+    def close(self) -> None:
+        """Release the handle: the library waits for the work it queued to
+        stop writing the buffers, then the buffers are let go.  A layer
+        posted without finish() gets no AllReduce."""
         h = getattr(self, "_h", None)
         if h is not None and h.value:
             self._lib.dt_hsdp_destroy(h)
-            self._h = None
+        self._h = None
+        self._stash = []
+
+    def __del__(self):
+        self.close()
 
 
 def shard_views(fused: torch.Tensor, numels: Sequence[int], shard: int) -> List[torch.Tensor]:

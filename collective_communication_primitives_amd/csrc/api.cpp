@@ -66,6 +66,48 @@ dt_status check_ptr_array(T const* arr, int n, const char* name) {
     return DT_OK;
 }
 
+// A byte range [lo, lo + n) of device memory, tagged for error messages:
+// `name`[`index`].
+struct Span {
+    uintptr_t lo;
+    size_t n;
+    const char* name;
+    int index;
+};
+
+void add_span(std::vector<Span>& v, const void* p, size_t n, const char* name, int index) {
+    if (p != nullptr && n > 0) v.push_back(Span{reinterpret_cast<uintptr_t>(p), n, name, index});
+}
+
+// Refuses (DT_ERR_ARG) when two written ranges overlap, or when a read range
+// overlaps a written one, unless the two are the very same range (an
+// in-place operand: the kernel reads each element before writing it, from
+// the same workgroup).  Kernels of different workgroups store and load
+// concurrently, so any other overlap would be a data race.  O(n log n).
+dt_status check_disjoint(std::vector<Span>& writes, const std::vector<Span>& reads, const char* what) {
+    std::sort(writes.begin(), writes.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < writes.size(); i++) {
+        const Span& a = writes[i - 1];
+        const Span& b = writes[i];
+        if (b.lo < a.lo + a.n)
+            return fail(DT_ERR_ARG, "%s: %s[%d] and %s[%d] overlap", what, a.name, a.index, b.name, b.index);
+    }
+    for (const Span& r : reads) {
+        // the last written range starting at or before r.lo, and the first one after it
+        auto it = std::upper_bound(writes.begin(), writes.end(), r.lo,
+                                   [](uintptr_t lo, const Span& s) { return lo < s.lo; });
+        if (it != writes.end() && it->lo < r.lo + r.n)
+            return fail(DT_ERR_ARG, "%s: %s[%d] overlaps %s[%d]", what, r.name, r.index, it->name, it->index);
+        if (it != writes.begin()) {
+            const Span& w = *(it - 1);
+            const bool same = w.lo == r.lo && w.n == r.n;
+            if (!same && r.lo < w.lo + w.n)
+                return fail(DT_ERR_ARG, "%s: %s[%d] overlaps %s[%d]", what, r.name, r.index, w.name, w.index);
+        }
+    }
+    return DT_OK;
+}
+
 // Wall-clock ticks per nanosecond budget on the current device.
 uint64_t timeout_ticks(uint64_t timeout_ns) {
     static std::mutex mu;
@@ -454,6 +496,15 @@ dt_status dt_allreduce(const void* const* send, void* const* recv, int nranks, s
                             r);
             if (r != q && recv[q] == recv[r]) return fail(DT_ERR_ARG, "recv[%d] equals recv[%d]", q, r);
         }
+    {
+        const size_t bytes = count * esize_of(dtype);
+        std::vector<Span> w, rd;
+        for (int r = 0; r < nranks; r++) {
+            add_span(w, recv[r], bytes, "recv", r);
+            add_span(rd, send[r], bytes, "send", r);
+        }
+        if ((st = check_disjoint(w, rd, "allreduce")) != DT_OK) return st;
+    }
     return allreduce_impl(send, recv, nranks, count, dtype, op, stream);
 }
 
@@ -472,6 +523,15 @@ dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nran
             if (recv[q] == send[r]) return fail(DT_ERR_ARG, "recv[%d] aliases send[%d]", q, r);
             if (r != q && recv[q] == recv[r]) return fail(DT_ERR_ARG, "recv[%d] equals recv[%d]", q, r);
         }
+    {
+        const size_t es = esize_of(dtype);
+        std::vector<Span> w, rd;
+        for (int r = 0; r < nranks; r++) {
+            add_span(w, recv[r], recvcount * es, "recv", r);
+            add_span(rd, send[r], size_t(nranks) * recvcount * es, "send", r);
+        }
+        if ((st = check_disjoint(w, rd, "reduce_scatter")) != DT_OK) return st;
+    }
     dt::ReduceArgs a = {};
     bool vec = recvcount % vec_elems(dtype) == 0;
     for (int r = 0; r < nranks; r++) {
@@ -524,6 +584,16 @@ dt_status dt_all_gather(const void* const* send, void* const* recv, int nranks, 
                 return fail(DT_ERR_ARG, "send[%d] lies inside recv[%d] other than at its own slot", r, q);
             if (r != q && recv[q] == recv[r]) return fail(DT_ERR_ARG, "recv[%d] equals recv[%d]", q, r);
         }
+    {
+        // a piece already in its own slot of its own output (in place) is not
+        // copied: it is read only, and only its own slot holds it
+        std::vector<Span> w, rd;
+        for (int r = 0; r < nranks; r++) {
+            add_span(w, recv[r], off, "recv", r);
+            if (cptr(send[r]) != cptr(recv[r]) + offset[r]) add_span(rd, send[r], counts[r] * es, "send", r);
+        }
+        if ((st = check_disjoint(w, rd, "all_gather")) != DT_OK) return st;
+    }
     std::vector<void*> table(size_t(nranks) * nranks);
     for (int r = 0; r < nranks; r++)
         for (int q = 0; q < nranks; q++) table[size_t(r) * nranks + q] = static_cast<char*>(recv[q]) + offset[r];
@@ -552,6 +622,15 @@ dt_status dt_all_gather_into_vec(const void* const* send, void* const* recv, int
             table[size_t(r) * nranks + q] = d;
         }
     }
+    {
+        std::vector<Span> w, rd;
+        for (int r = 0; r < nranks; r++) {
+            if (counts[r] == 0) continue;
+            add_span(rd, send[r], counts[r] * es, "send", r);
+            for (int q = 0; q < nranks; q++) add_span(w, recv[size_t(q) * nranks + r], counts[r] * es, "recv", q * nranks + r);
+        }
+        if ((st = check_disjoint(w, rd, "all_gather_into_vec")) != DT_OK) return st;
+    }
     return fan_out(send, counts.data(), table.data(), nranks, es, stream, "all_gather_into_vec launch");
 }
 
@@ -569,6 +648,13 @@ dt_status dt_broadcast(const void* root_send, void* const* recv, int nranks, siz
     for (int q = 0; q < nranks; q++)
         for (int r = 0; r < q; r++)
             if (recv[q] == recv[r]) return fail(DT_ERR_ARG, "recv[%d] equals recv[%d]", q, r);
+    {
+        // the root's buffer may be one of the outputs (it is then not copied onto itself)
+        std::vector<Span> w, rd;
+        for (int q = 0; q < nranks; q++) add_span(w, recv[q], count * esize_of(dtype), "recv", q);
+        add_span(rd, root_send, count * esize_of(dtype), "root_send", 0);
+        if ((st = check_disjoint(w, rd, "broadcast")) != DT_OK) return st;
+    }
     // the fan-out engine with one source: rank slot 0 carries the root's data
     const void* src[1] = {root_send};
     size_t counts[1] = {count};
@@ -589,10 +675,15 @@ dt_status dt_replicate_to_shard(const void* const* send, void* const* recv, int 
     std::vector<const void*> src(nranks);
     std::vector<void*> dst(nranks);
     std::vector<size_t> bytes(nranks, recvcount * es);
+    std::vector<Span> w, rd;
     for (int r = 0; r < nranks; r++) {
         src[r] = cptr(send[r]) + size_t(r) * recvcount * es;
         dst[r] = recv[r];
+        add_span(w, recv[r], recvcount * es, "recv", r);
+        add_span(rd, src[r], recvcount * es, "send slice", r);
     }
+    // only slice r of send[r] is read (an output that is exactly its own slice copies onto itself)
+    if ((st = check_disjoint(w, rd, "replicate_to_shard")) != DT_OK) return st;
     return copy_segments(src, dst, bytes, stream, "replicate_to_shard launch");
 }
 
@@ -616,6 +707,16 @@ dt_status dt_all_to_all_dims(const void* const* send, void* const* recv, int nra
         for (int r = 0; r < nranks; r++)
             if (recv[q] == send[r]) return fail(DT_ERR_ARG, "recv[%d] aliases send[%d]", q, r);
     const size_t es = esize_of(dtype);
+    {
+        const size_t sblock = (src_dim == 0 ? rows / P * cols : rows * (cols / P)) * es;
+        const size_t dblock = (dst_dim == 0 ? rows / P * cols : rows * (cols / P)) * es;
+        std::vector<Span> w, rd;
+        for (int r = 0; r < nranks; r++) {
+            add_span(w, recv[r], dblock, "recv", r);
+            add_span(rd, send[r], sblock, "send", r);
+        }
+        if ((st = check_disjoint(w, rd, "all_to_all_dims")) != DT_OK) return st;
+    }
     if (src_dim == dst_dim) {  // no exchange: each rank copies its own block
         const size_t block = (src_dim == 0 ? rows / P * cols : rows * (cols / P)) * es;
         std::vector<const void*> src(send, send + nranks);
@@ -684,6 +785,14 @@ dt_status dt_all_to_all(const void* const* send, void* const* recv, int nranks, 
     for (int s = 0; s < nranks * nranks; s++)
         if (splits[s] > (size_t(1) << 40)) return fail(DT_ERR_ARG, "splits[%d]=%zu too large", s, splits[s]);
     const size_t es = esize_of(dtype);
+    {
+        std::vector<Span> w, rd;
+        for (int r = 0; r < nranks; r++) {
+            add_span(w, recv[r], col[r] * es, "recv", r);
+            add_span(rd, send[r], row[r] * es, "send", r);
+        }
+        if ((st = check_disjoint(w, rd, "all_to_all")) != DT_OK) return st;
+    }
     dt::AllToAllArgs a = {};
     uint64_t tiles = 0;
     auto flush = [&]() -> dt_status {
@@ -746,9 +855,15 @@ dt_status dt_bucket_plan(const size_t* numels, int ntensors, size_t elem_size, s
 // ms for the multi-tensor fold of every piece.
 constexpr size_t kOwnAllReduceBytes = size_t(16) << 20;
 
-dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int ntensors, int nranks, size_t bucket_bytes,
-                              void* const* bucket_ws, dt_dtype dtype, dt_op op, hipStream_t stream) {
-    g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Arguments shared by the bucket AllReduce entry points.  Every tensor is
+// reduced in place, so no two of them (over all ranks) may overlap, and the
+// bucket buffers, when given, may overlap neither the tensors nor each other.
+dt_status bucket_check(void* const* grads, const size_t* numels, int ntensors, int nranks, size_t bucket_bytes,
+                       void* const* bucket_ws, dt_dtype dtype, dt_op op) {
     dt_status st = check_ranks(nranks);
     if (st != DT_OK) return st;
     if (!valid_dtype(dtype) || !valid_op(op)) return fail(DT_ERR_ARG, "bad dtype %d or op %d", dtype, op);
@@ -763,6 +878,20 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
             if (numels[t] > 0 && grads[size_t(r) * ntensors + t] == nullptr)
                 return fail(DT_ERR_ARG, "grads[%d] (rank %d, tensor %d) is NULL", r * ntensors + t, r, t);
     if (bucket_ws && (st = check_ptr_array(bucket_ws, nranks, "bucket_ws")) != DT_OK) return st;
+    const size_t es = esize_of(dtype);
+    std::vector<Span> w;
+    for (int r = 0; r < nranks; r++) {
+        for (int t = 0; t < ntensors; t++) add_span(w, grads[size_t(r) * ntensors + t], numels[t] * es, "grads", r * ntensors + t);
+        if (bucket_ws) add_span(w, bucket_ws[r], bucket_bytes, "bucket_ws", r);
+    }
+    return check_disjoint(w, {}, "bucket_allreduce");
+}
+
+// The bucket AllReduce after validation; bucket_ws is NULL (in place) or
+// nranks buffers of bucket_bytes.
+dt_status bucket_allreduce_impl(void* const* grads, const size_t* numels, int ntensors, int nranks, size_t bucket_bytes,
+                                void* const* bucket_ws, dt_dtype dtype, dt_op op, hipStream_t stream) {
+    dt_status st;
     const size_t es = esize_of(dtype);
     size_t nbuckets = 0;
     const std::vector<Piece> plan = plan_buckets(numels, ntensors, bucket_bytes / es, &nbuckets);
@@ -814,6 +943,18 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
     return DT_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int ntensors, int nranks, size_t bucket_bytes,
+                              void* const* bucket_ws, dt_dtype dtype, dt_op op, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = bucket_check(grads, numels, ntensors, nranks, bucket_bytes, bucket_ws, dtype, op);
+    if (st != DT_OK || ntensors == 0) return st;
+    return bucket_allreduce_impl(grads, numels, ntensors, nranks, bucket_bytes, bucket_ws, dtype, op, stream);
+}
+
 dt_status dt_allreduce_coalesced(void* const* tensors, const size_t* numels, int ntensors, int nranks, dt_dtype dtype,
                                  dt_op op, hipStream_t stream) {
     g_last_error.clear();
@@ -827,6 +968,14 @@ dt_status dt_allreduce_coalesced(void* const* tensors, const size_t* numels, int
         for (int t = 0; t < ntensors; t++)
             if (numels[t] > 0 && tensors[size_t(r) * ntensors + t] == nullptr)
                 return fail(DT_ERR_ARG, "tensors[%d] (rank %d, tensor %d) is NULL", r * ntensors + t, r, t);
+    {
+        // every tensor is reduced in place: no two may overlap
+        std::vector<Span> w;
+        for (int r = 0; r < nranks; r++)
+            for (int t = 0; t < ntensors; t++)
+                add_span(w, tensors[size_t(r) * ntensors + t], numels[t] * esize_of(dtype), "tensors", r * ntensors + t);
+        if ((st = check_disjoint(w, {}, "allreduce_coalesced")) != DT_OK) return st;
+    }
     std::vector<PieceRef> pieces;
     for (int t = 0; t < ntensors; t++) {
         if (numels[t] == 0) continue;
@@ -971,11 +1120,14 @@ dt_status hsdp_issue_prev_allreduce(dt_hsdp* h) {
     dt_status st;
     const size_t es = esize_of(h->dtype);
     const size_t per_bucket = h->bucket_bytes / es;
+    // with one replica the fused shards already are the result: the AllReduce
+    // of a group of one folds nothing, so only its end event is recorded
+    const size_t fold_total = h->replicate > 1 ? h->prev_total : 0;
     // one launch per bucket covers every replicate group: piece j is group j's
     // slice [start, start + len) of its members' fused buffers, reduced in place
     const int per_launch = std::min(dt::kMaxPieces, dt::kPiecePtrs / h->replicate);
-    for (size_t start = 0; start < h->prev_total; start += per_bucket) {
-        const size_t len = std::min(per_bucket, h->prev_total - start);
+    for (size_t start = 0; start < fold_total; start += per_bucket) {
+        const size_t len = std::min(per_bucket, fold_total - start);
         for (int j0 = 0; j0 < h->shard; j0 += per_launch) {
             dt::PieceArgs a = {};
             a.nranks = h->replicate;
@@ -1059,6 +1211,24 @@ dt_status dt_hsdp_post_backward(dt_hsdp* h, const void* const* grads, const size
         if (numels[t] % size_t(h->shard) != 0)
             return fail(DT_ERR_ARG, "numels[%d]=%zu not divisible by shard=%d", t, numels[t], h->shard);
     const size_t es = esize_of(h->dtype);
+    if (total > 0) {
+        // The ReduceScatter writes fused[r] while it reads the gradients, and
+        // the previous layer's fused buffers still wait for their AllReduce
+        // (queued below, after this ReduceScatter): reusing them before
+        // dt_hsdp_finish would overwrite shards that are not yet reduced.
+        std::vector<Span> w, rd;
+        for (int r = 0; r < nranks; r++) {
+            add_span(w, fused[r], total / size_t(h->shard) * es, "fused", r);
+            for (int t = 0; t < ntensors; t++) add_span(rd, grads[size_t(r) * ntensors + t], numels[t] * es, "grads", r * ntensors + t);
+            if (h->has_prev) add_span(rd, h->prev_fused[r], h->prev_total * es, "previous layer's fused", r);
+        }
+        // an exact match is an in-place operand for check_disjoint, never valid here
+        for (const Span& x : rd)
+            for (const Span& y : w)
+                if (x.lo == y.lo && x.n == y.n)
+                    return fail(DT_ERR_ARG, "hsdp post_backward: %s[%d] is %s[%d]", x.name, x.index, y.name, y.index);
+        if ((st = check_disjoint(w, rd, "hsdp post_backward")) != DT_OK) return st;
+    }
 
     // 1. wait prev RS
     if (h->has_prev && (st = hsdp_wait_prev_rs(h)) != DT_OK) return st;
@@ -1096,7 +1266,10 @@ dt_status dt_hsdp_post_backward(dt_hsdp* h, const void* const* grads, const size
     if (h->has_prev && (st = hsdp_issue_prev_allreduce(h)) != DT_OK) return st;
     // this layer becomes the previous one
     h->prev_slot = cur_slot;
-    h->prev_fused.assign(fused, fused + nranks);
+    if (fused)
+        h->prev_fused.assign(fused, fused + nranks);
+    else
+        h->prev_fused.assign(size_t(nranks), nullptr);  // an empty layer: nothing to reduce
     h->prev_total = at;
     h->has_prev = true;
     return DT_OK;
@@ -1129,8 +1302,14 @@ dt_status dt_hsdp_destroy(dt_hsdp* h) {
         (void)hipEventDestroy(ev);
     }
     if (h->produced) (void)hipEventDestroy(h->produced);
+    // a layer posted but never finished still has its ReduceScatter writing
+    // the caller's fused buffers: wait for it before the caller may free them
+    // (its AllReduce is dropped, not queued)
     for (hipEvent_t ev : h->rs_done)
-        if (ev) (void)hipEventDestroy(ev);
+        if (ev) {
+            (void)hipEventSynchronize(ev);
+            (void)hipEventDestroy(ev);
+        }
     delete h;
     return DT_OK;
 }

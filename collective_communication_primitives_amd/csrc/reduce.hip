@@ -325,7 +325,8 @@ int pmax_of(int nranks) {
 // and 1 GiB per rank (P=8 bf16, P=16 fp32), but 2-12% slower at 4-64 MiB.
 constexpr uint64_t kWaveAllReduceBytes = 256ull << 20;
 
-// One-shot AllReduce with P >= 2 up to this many bytes per rank: buffer stores.
+// One-shot AllReduce with P >= 2 up to this many bytes per rank: buffer stores
+// (for P > 8 only below it: P=16 at exactly 8 MiB measured up to 8% slower).
 constexpr uint64_t kBufferStoreAllReduceBytes = 8ull << 20;
 
 // Vectors per thread of the one-shot AllReduce in kBlock-thread tiles,
@@ -354,7 +355,8 @@ void reduce_vec_launch(const ReduceArgs& a, uint64_t blocks, hipStream_t s) {
         }
     }
     if constexpr (PMAX >= 2) {
-        if (a.count * 16 <= kBufferStoreAllReduceBytes) {
+        const uint64_t bytes = a.count * 16;
+        if (PMAX >= 16 ? bytes < kBufferStoreAllReduceBytes : bytes <= kBufferStoreAllReduceBytes) {
             k_reduce_vec<DT, OP, PMAX, EXACT, ar_unroll<PMAX>(), kBlock, true><<<unsigned(blocks), kBlock, 0, s>>>(a);
             return;
         }

@@ -27,8 +27,10 @@
  *  - Element types: fp32, bf16 (accumulated in fp32, rounded once to nearest
  *    even), int32 (sums wrap modulo 2^32).  Reductions fold the ranks in rank
  *    order 0, 1, ..., P-1 for every element, so results are deterministic.
- *  - Errors: DT_ERR_ARG for NULL pointers, bad enums, out-of-range sizes or a
- *    forbidden alias; DT_ERR_HIP when a launch fails.  Nothing throws across
+ *  - Errors: DT_ERR_ARG for NULL pointers, bad enums, out-of-range sizes or
+ *    buffers that overlap where a launch would race (a written byte range
+ *    meeting another written or read one; exact in-place operands are
+ *    allowed where a call says so); DT_ERR_HIP when a launch fails.  Nothing throws across
  *    the ABI; dt_last_error() gives this thread's last message.
  *  - Fast path: 16-byte aligned buffers and offsets.  Anything else is still
  *    correct but runs an element-wise path.
@@ -72,15 +74,15 @@ typedef enum {
  * runs as a ReduceScatter into chunk r of recv[r] followed by an in-place
  * AllGather of the chunks, which is faster there; both forms fold in the
  * same order and give identical bits.  In place is allowed (send[r] ==
- * recv[r]); any other overlap between buffers is undefined.  send[r] and
- * recv[r] hold `count` elements. */
+ * recv[r]); any other overlap of a recv buffer with a send or recv buffer
+ * is refused (DT_ERR_ARG).  send[r] and recv[r] hold `count` elements. */
 dt_status dt_allreduce(const void* const* send, void* const* recv, int nranks, size_t count,
                        dt_dtype dtype, dt_op op, hipStream_t stream);
 
 /* ReduceScatter, Partial -> Shard(0): send[r] holds nranks*recvcount
  * elements; recv[r][i] = fold_q send[q][r*recvcount + i].  DTorch page
  * sec. 2.1 (ReduceScatterTensor) and sec. 2.5 (P -> S0).  recv buffers must
- * not overlap any send buffer (DT_ERR_ARG when one equals a send pointer). */
+ * overlap neither any send buffer nor each other (DT_ERR_ARG). */
 dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nranks, size_t recvcount,
                             dt_dtype dtype, dt_op op, hipStream_t stream);
 
@@ -258,7 +260,13 @@ dt_status dt_work_free(dt_work* work);
  * wait for every AllReduce issued (the root backward hook); each parameter's
  * reduced shard is then the matching slice of its layer's fused buffers.
  * fused[r] holds sum(numels)/shard elements and must stay valid until the
- * consumer has waited.  numels[t] must be divisible by shard.  The handle
+ * consumer has waited.  numels[t] must be divisible by shard.  fused buffers
+ * may overlap neither each other, nor the layer's gradients, nor the previous
+ * layer's fused buffers while that layer's AllReduce is still pending, i.e.
+ * until dt_hsdp_finish (DT_ERR_ARG): reusing one fused set for every layer
+ * needs a finish between layers.  dt_hsdp_destroy waits until any queued
+ * ReduceScatter or AllReduce of the handle has finished writing; a layer
+ * posted but not finished gets no AllReduce.  The handle
  * owns its events and keeps a host copy of the previous layer's fused
  * pointers and total size until it queues that layer's AllReduce.
  * rs_stream and ar_stream may be the same stream: the phases then run back

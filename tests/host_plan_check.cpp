@@ -699,6 +699,96 @@ void validation() {
     expect(dt_bucket_plan(numels, 1, 4, 2, nullptr, 0, &np, &nb), DT_ERR_ARG, "bucket smaller than an element");
 }
 
+// Partial overlaps between buffers that a launch writes and buffers it reads
+// or writes elsewhere: the kernels would race, so every entry point refuses
+// them, while exact in-place operands stay allowed.
+void overlaps() {
+    Pool pool;
+    g_bufs.clear();
+    const size_t n = 1024;  // fp32 elements per rank
+    char* big = pool.get(16 * n * 4, 0, true);  // one block, carved into overlapping views
+    const void* send[2] = {big, big + 4 * n * 4};
+    void* recv[2] = {big + 8 * n * 4, big + 12 * n * 4};
+    expect(dt_allreduce(send, recv, 2, n, DT_FLOAT32, DT_SUM, nullptr), DT_OK, "allreduce, disjoint views");
+    recv[1] = big + 8 * n * 4 + 2048;  // inside recv[0]
+    expect(dt_allreduce(send, recv, 2, n, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG, "allreduce, recv overlap");
+    recv[1] = big + 12 * n * 4;
+    send[1] = big + 8 * n * 4 + 64;  // reads inside recv[0]
+    expect(dt_allreduce(send, recv, 2, n, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG, "allreduce, send inside recv");
+    void* inplace[2] = {big, big + 4 * n * 4};
+    const void* inplace_c[2] = {big, big + 4 * n * 4};
+    expect(dt_allreduce(inplace_c, inplace, 2, n, DT_FLOAT32, DT_SUM, nullptr), DT_OK, "allreduce in place");
+    const void* skewed[2] = {big + 64, big + 4 * n * 4};  // in place for rank 1 only; send[0] overlaps recv[0]
+    expect(dt_allreduce(skewed, inplace, 2, n, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG, "allreduce, shifted self");
+
+    // ReduceScatter: send[r] holds 2n, recv[r] n
+    const void* rs_send[2] = {big, big + 2 * n * 4};
+    void* rs_recv[2] = {big + 8 * n * 4, big + 3 * n * 4};  // recv[1] inside send[1]
+    expect(dt_reduce_scatter(rs_send, rs_recv, 2, n, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG, "rs, recv inside send");
+    rs_recv[1] = big + 10 * n * 4;
+    expect(dt_reduce_scatter(rs_send, rs_recv, 2, n, DT_FLOAT32, DT_SUM, nullptr), DT_OK, "rs, disjoint");
+
+    // AllGather: a source that starts before an output and runs into it
+    const void* ag_send[2] = {big + 8 * n * 4 - 64, big};
+    void* ag_recv[2] = {big + 8 * n * 4, big + 12 * n * 4};
+    expect(dt_all_gather(ag_send, ag_recv, 2, nullptr, n, DT_FLOAT32, nullptr), DT_ERR_ARG, "ag, send runs into recv");
+    const void* ag_inplace[2] = {big + 8 * n * 4, big + 12 * n * 4 + n * 4};  // each in its own slot
+    expect(dt_all_gather(ag_inplace, ag_recv, 2, nullptr, n, DT_FLOAT32, nullptr), DT_OK, "ag in place");
+
+    // AllToAll: recv[0] overlapping send[1]
+    const size_t splits[4] = {n, n, n, n};
+    const void* a_send[2] = {big, big + 2 * n * 4};
+    void* a_recv[2] = {big + 3 * n * 4, big + 8 * n * 4};
+    expect(dt_all_to_all(a_send, a_recv, 2, splits, DT_FLOAT32, nullptr), DT_ERR_ARG, "a2a, recv overlaps send");
+    a_recv[0] = big + 4 * n * 4;
+    expect(dt_all_to_all(a_send, a_recv, 2, splits, DT_FLOAT32, nullptr), DT_OK, "a2a, disjoint");
+
+    // bucket / coalesced: two tensors of one rank overlapping
+    size_t numels[2] = {n, n};
+    void* g[4] = {big, big + 2 * n * 4, big + 4 * n * 4, big + 4 * n * 4 + 8};
+    expect(dt_bucket_allreduce(g, numels, 2, 2, 4096, nullptr, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG,
+           "bucket, overlapping tensors");
+    expect(dt_allreduce_coalesced(g, numels, 2, 2, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG,
+           "coalesced, overlapping tensors");
+    g[3] = big + 6 * n * 4;
+    void* ws[2] = {big + 8 * n * 4, big + 6 * n * 4 + 16};  // ws[1] inside grads[3]
+    expect(dt_bucket_allreduce(g, numels, 2, 2, 4096, ws, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG,
+           "bucket, workspace inside a tensor");
+    ws[1] = big + 12 * n * 4;
+    expect(dt_bucket_allreduce(g, numels, 2, 2, 4096, ws, DT_FLOAT32, DT_SUM, nullptr), DT_OK, "bucket, disjoint");
+
+    // HSDP: one fused set reused for the next layer before finish() is refused
+    dt_hsdp* h = nullptr;
+    expect(dt_hsdp_create(2, 2, 4096, DT_BFLOAT16, DT_SUM, nullptr, nullptr, &h), DT_OK, "hsdp create");
+    const size_t hn[1] = {2 * n};  // bf16, shard 2: fused holds n elements
+    const void* hg[4] = {big, big + 4 * n, big + 8 * n, big + 12 * n};
+    void* fused_a[4] = {big + 16 * n, big + 18 * n, big + 20 * n, big + 22 * n};
+    void* fused_b[4] = {big + 24 * n, big + 26 * n, big + 28 * n, big + 30 * n};
+    expect(dt_hsdp_post_backward(h, hg, hn, 1, fused_a, nullptr), DT_OK, "hsdp layer 0");
+    expect(dt_hsdp_post_backward(h, hg, hn, 1, fused_a, nullptr), DT_ERR_ARG, "hsdp, fused reused before finish");
+    void* fused_c[4] = {big + 24 * n, big + 26 * n, big + 17 * n, big + 30 * n};  // fused[2] inside layer 0's fused[0]
+    expect(dt_hsdp_post_backward(h, hg, hn, 1, fused_c, nullptr), DT_ERR_ARG, "hsdp, fused overlaps previous");
+    expect(dt_hsdp_post_backward(h, hg, hn, 1, fused_b, nullptr), DT_OK, "hsdp layer 1");
+    expect(dt_hsdp_finish(h, nullptr), DT_OK, "hsdp finish");
+    expect(dt_hsdp_post_backward(h, hg, hn, 1, fused_a, nullptr), DT_OK, "hsdp, fused reused after finish");
+    void* fused_g[4] = {big + 2 * n, big + 26 * n, big + 28 * n, big + 30 * n};  // fused[0] inside grads[0]
+    expect(dt_hsdp_finish(h, nullptr), DT_OK, "hsdp finish");
+    expect(dt_hsdp_post_backward(h, hg, hn, 1, fused_g, nullptr), DT_ERR_ARG, "hsdp, fused overlaps a gradient");
+    expect(dt_hsdp_destroy(h), DT_OK, "hsdp destroy");
+
+    // HSDP with one replica: the fused AllReduce folds nothing, so it launches nothing
+    expect(dt_hsdp_create(1, 4, 4096, DT_BFLOAT16, DT_SUM, nullptr, nullptr, &h), DT_OK, "hsdp 1x4");
+    const size_t hn4[1] = {4 * n};
+    const void* hg4[4] = {big, big + 8 * n, big + 16 * n, big + 24 * n};
+    void* f4[4] = {big + 32 * n, big + 34 * n, big + 36 * n, big + 38 * n};
+    const long before = g_launches;
+    expect(dt_hsdp_post_backward(h, hg4, hn4, 1, f4, nullptr), DT_OK, "hsdp 1x4 layer");
+    expect(dt_hsdp_finish(h, nullptr), DT_OK, "hsdp 1x4 finish");
+    CHECK(g_launches - before == 1, "hsdp 1x4: %ld launches, expected the ReduceScatter only", g_launches - before);
+    expect(dt_hsdp_destroy(h), DT_OK, "hsdp 1x4 destroy");
+    g_bufs.clear();
+}
+
 }  // namespace
 
 // The windowed fan-out of large sources: fake device ranges (never touched)
@@ -833,6 +923,7 @@ void two_shot() {
 
 int main() {
     validation();
+    overlaps();
     big_fan_out();
     two_shot();
     reductions();

@@ -81,6 +81,12 @@ MUTANTS = {
     "dims_extra_run": ("a.nruns = uint64_t(rows) * P;", "a.nruns = uint64_t(rows) * P + 1;"),
     # every piece claimed 16-byte aligned
     "pieces_always_aligned": ("if (al) set_aligned(a, k);", "set_aligned(a, k);"),
+    # the previous layer's fused buffers, whose AllReduce is still pending, may be written again
+    "hsdp_fused_reuse_allowed": ("            if (h->has_prev) add_span(rd, h->prev_fused[r], h->prev_total * es, ",
+                                 "            if (false) add_span(rd, h->prev_fused[r], h->prev_total * es, "),
+    # only exact pointer equality is refused: a partial overlap of outputs slips through
+    "overlap_check_skipped": ("    for (size_t i = 1; i < writes.size(); i++) {",
+                              "    for (size_t i = writes.size(); i < writes.size(); i++) {"),
 }
 
 
