@@ -34,6 +34,7 @@ DT_SUM, DT_MAX, DT_MIN, DT_AVG = 0, 1, 2, 3
 DT_OK, DT_ERR_ARG, DT_ERR_UNSUPPORTED, DT_ERR_HIP, DT_ERR_TIMEOUT = 0, 1, 2, 3, 4
 DT_MAX_RANKS = 16
 DEFAULT_BUCKET_BYTES = 25 << 20
+SCRATCH_BYTES = 256 << 20  # DT_SCRATCH_BYTES: the static staging buffer of dt_bucket_allreduce_noalloc
 
 _DTYPES = {torch.float32: DT_FLOAT32, torch.bfloat16: DT_BFLOAT16, torch.int32: DT_INT32}
 _OPS = {"sum": DT_SUM, "max": DT_MAX, "min": DT_MIN, "avg": DT_AVG}
@@ -449,6 +450,26 @@ def dt_bucket_allreduce(grads: Sequence[Sequence[torch.Tensor]], bucket_bytes: i
     return w if async_op else grads
 
 
+def dt_bucket_allreduce_noalloc(grads: Sequence[Sequence[torch.Tensor]], bucket_bytes: int = DEFAULT_BUCKET_BYTES,
+                                op="sum", stream=None, async_op: bool = False, comm_stream=None):
+    """Staged fused-bucket AllReduce in place over grads[r][t], with the
+    buckets staged in the library's static device buffer (SCRATCH_BYTES)
+    instead of caller workspaces: nothing is allocated.  nranks *
+    bucket_bytes must fit that buffer.  Calls that may overlap in time on one
+    GPU share the buffer and must be ordered by the caller."""
+    p, nt = len(grads), len(grads[0])
+    numels = [g.numel() for g in grads[0]]
+    for rank in grads:
+        if len(rank) != nt or [g.numel() for g in rank] != numels:
+            raise ValueError("every rank must list tensors of the same sizes")
+    flat = [g for rank in grads for g in rank]
+    code = _dtype_code(flat)
+    g_arr, n_arr = _ptr_array(flat), _size_array(numels)
+    w = _launch(lambda st: _L.dt_bucket_allreduce_noalloc(g_arr, n_arr, nt, p, bucket_bytes, code, _op_code(op), st),
+                flat, async_op, stream, comm_stream)
+    return w if async_op else grads
+
+
 def dt_allreduce_coalesced(tensors: Sequence[Sequence[torch.Tensor]], op="sum", stream=None, async_op: bool = False,
                            comm_stream=None):
     """Coalesced in-place AllReduce of tensors[r][t] (rank r, tensor t): one
@@ -594,6 +615,6 @@ def shard_views(fused: torch.Tensor, numels: Sequence[int], shard: int) -> List[
 __all__ = [
     "dt_allreduce", "dt_reduce_scatter", "dt_all_gather", "dt_all_to_all", "dt_bucket_allreduce", "dt_bucket_plan",
     "dt_all_gather_into_vec", "dt_broadcast", "dt_replicate_to_shard", "dt_all_to_all_dims",
-    "dt_allreduce_coalesced", "dt_barrier", "dt_barrier_exchange", "HSDPPipeline", "Work", "DtError", "shard_views", "side_stream",
+    "dt_allreduce_coalesced", "dt_bucket_allreduce_noalloc", "dt_barrier", "dt_barrier_exchange", "HSDPPipeline", "Work", "DtError", "shard_views", "side_stream",
     "status_string", "version",
 ]

@@ -15,7 +15,7 @@ LIBRARY = os.path.join(PKG, "libdtcoll.so")
 EXPORTS = (
     "dt_allreduce", "dt_reduce_scatter", "dt_all_gather", "dt_all_to_all", "dt_bucket_allreduce",
     "dt_all_gather_into_vec", "dt_broadcast", "dt_replicate_to_shard", "dt_all_to_all_dims",
-    "dt_allreduce_coalesced",
+    "dt_allreduce_coalesced", "dt_bucket_allreduce_noalloc",
     "dt_barrier", "dt_barrier_exchange", "dt_bucket_plan", "dt_work_begin", "dt_work_end",
     "dt_work_wait", "dt_work_query", "dt_work_free", "dt_hsdp_create", "dt_hsdp_post_backward",
     "dt_hsdp_finish", "dt_hsdp_destroy", "dt_status_string", "dt_last_error", "dt_version",
@@ -44,6 +44,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         "dt_all_to_all_dims": [vp, vp, i32, sz, sz, i32, i32, i32, vp],
         "dt_bucket_allreduce": [vp, vp, i32, i32, sz, vp, i32, i32, vp],
         "dt_allreduce_coalesced": [vp, vp, i32, i32, i32, i32, vp],
+        "dt_bucket_allreduce_noalloc": [vp, vp, i32, i32, sz, i32, i32, vp],
         "dt_barrier": [vp, i32, ctypes.c_int32, ctypes.c_int32, vp, u64, i32, vp],
         "dt_barrier_exchange": [vp, vp, vp, sz, vp, i32, ctypes.c_int32, vp, u64, i32, vp],
         "dt_bucket_plan": [vp, i32, sz, sz, vp, sz, vp, vp],

@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libdtcoll.so")
-SOURCES = ("api.cpp", "reduce.hip", "copy.hip", "barrier.hip")
+SOURCES = ("api.cpp", "reduce.hip", "copy.hip", "barrier.hip", "scratch.hip")
 ARCH = os.environ.get("DT_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -25,6 +25,7 @@ static_assert(sizeof(dt::SegCopyArgs) <= 4096, "kernel arguments must stay below
 static_assert(sizeof(dt::DimsArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 static_assert(sizeof(dt::CoalescedArgs) <= 48 * 1024, "large piece table must stay well below the 64 KB verified");
 static_assert(DT_MAX_RANKS == dt::kMaxRanksHost, "rank limit mismatch");
+static_assert(DT_SCRATCH_BYTES == dt::kScratchBytes, "static staging size mismatch");
 
 namespace {
 
@@ -953,6 +954,23 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
     dt_status st = bucket_check(grads, numels, ntensors, nranks, bucket_bytes, bucket_ws, dtype, op);
     if (st != DT_OK || ntensors == 0) return st;
     return bucket_allreduce_impl(grads, numels, ntensors, nranks, bucket_bytes, bucket_ws, dtype, op, stream);
+}
+
+dt_status dt_bucket_allreduce_noalloc(void* const* grads, const size_t* numels, int ntensors, int nranks,
+                                      size_t bucket_bytes, dt_dtype dtype, dt_op op, hipStream_t stream) {
+    g_last_error.clear();
+    dt_status st = bucket_check(grads, numels, ntensors, nranks, bucket_bytes, nullptr, dtype, op);
+    if (st != DT_OK || ntensors == 0) return st;
+    if (uint64_t(nranks) * bucket_bytes > dt::kScratchBytes)
+        return fail(DT_ERR_ARG, "nranks * bucket_bytes = %d * %zu exceeds the %llu-byte static staging buffer", nranks,
+                    bucket_bytes, (unsigned long long)dt::kScratchBytes);
+    char* scratch = nullptr;
+    if ((st = check_hip(dt::scratch_base(reinterpret_cast<void**>(&scratch)), "static staging buffer")) != DT_OK)
+        return st;
+    // rank r stages its buckets at scratch + r * bucket_bytes (16-byte aligned: bucket_bytes is a multiple of 16)
+    void* ws[DT_MAX_RANKS];
+    for (int r = 0; r < nranks; r++) ws[r] = scratch + size_t(r) * bucket_bytes;
+    return bucket_allreduce_impl(grads, numels, ntensors, nranks, bucket_bytes, ws, dtype, op, stream);
 }
 
 dt_status dt_allreduce_coalesced(void* const* tensors, const size_t* numels, int ntensors, int nranks, dt_dtype dtype,

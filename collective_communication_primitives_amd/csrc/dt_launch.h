@@ -186,6 +186,11 @@ hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_
 constexpr uint64_t kSegCopyTileBytes = 1024;
 constexpr uint64_t kDimsTileBytes = 16384;
 constexpr uint32_t kDimsMaxRunsPerBlock = 64;
+// The static staging buffer of the allocation-free bucket AllReduce
+// (scratch.hip): its device address on the current device, looked up once per
+// device.  kScratchBytes holds eight ranks' 25 MiB buckets (or sixteen of 16 MiB).
+constexpr uint64_t kScratchBytes = 256ull << 20;
+hipError_t scratch_base(void** ptr);
 hipError_t launch_barrier(const BarrierArgs& a, int spread, hipStream_t s);
 hipError_t launch_exchange(const ExchangeArgs& a, int spread, hipStream_t s);
 

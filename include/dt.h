@@ -155,6 +155,26 @@ dt_status dt_bucket_allreduce(void* const* grads, const size_t* numels, int nten
                               size_t bucket_bytes, void* const* bucket_ws, dt_dtype dtype, dt_op op,
                               hipStream_t stream);
 
+/* Size of the static staging buffer of dt_bucket_allreduce_noalloc, bytes. */
+#define DT_SCRATCH_BYTES (256u << 20)
+
+/* dt_bucket_allreduce with staging (bucket_ws != NULL) for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Instead of caller workspaces,
+ * rank r's buckets are staged in a static device array of DT_SCRATCH_BYTES
+ * (256 MiB), at byte offset r * bucket_bytes, so nranks * bucket_bytes may
+ * not exceed DT_SCRATCH_BYTES (DT_ERR_ARG otherwise; eight ranks of the
+ * default 25 MiB bucket fit).  Everything else is as dt_bucket_allreduce with
+ * a workspace: the same plan, kernels and bits.  The call allocates nothing:
+ * each GPU holds its own copy of the array, set up by the first call with
+ * that device current (make that first call outside graph capture) and kept
+ * until the process ends.  All calls on one GPU share that GPU's array, so
+ * calls that may overlap in time on one GPU (other streams, other threads)
+ * race and must be ordered by the caller.  No part of the array needs to
+ * start at zero: every byte a call reads back was written by the same call. */
+dt_status dt_bucket_allreduce_noalloc(void* const* grads, const size_t* numels, int ntensors, int nranks,
+                                      size_t bucket_bytes, dt_dtype dtype, dt_op op, hipStream_t stream);
+
 /* Where the ranks of a barrier launch run.  The spread layout needs a
  * cooperative launch, which the HIP runtime may refuse (DT_ERR_HIP, with its
  * message in dt_last_error) while another process shares the GPU; the

@@ -137,6 +137,18 @@ void log_fold(const void* p, uint64_t bytes) {
     if (g_log_folds && bytes) g_fold_log.push_back({static_cast<const char*>(p), bytes});
 }
 
+// The static staging buffer: a fake device range (never dereferenced),
+// registered as writable on every lookup since the driver clears the
+// registry between cases.
+int g_scratch_lookups = 0;
+hipError_t scratch_base(void** ptr) {
+    g_scratch_lookups++;
+    char* p = reinterpret_cast<char*>(uintptr_t(3) << 44);
+    reg(p, kScratchBytes, true);
+    *ptr = p;
+    return hipSuccess;
+}
+
 // Output vectors per tile of the segmented ReduceScatter.  Deliberately not
 // the library's value: the planning code must take the tile size from this
 // function, never from a constant of its own.
@@ -574,6 +586,8 @@ void buckets() {
         for (int r = 0; r < p; r++) ws[r] = pool.get(bucket, 0, true);
         expect(dt_bucket_allreduce(grads.data(), numels.data(), nt, p, bucket, ws.data(), dtype, op, nullptr), DT_OK,
                "bucket staged");
+        expect(dt_bucket_allreduce_noalloc(grads.data(), numels.data(), nt, p, bucket, dtype, op, nullptr), DT_OK,
+               "bucket staged in the static buffer");
         expect(dt_allreduce_coalesced(grads.data(), numels.data(), nt, p, dtype, op, nullptr), DT_OK, "coalesced");
 
         // the bucket plan: every element exactly once, buckets within bounds
@@ -697,6 +711,16 @@ void validation() {
            "bucket not a multiple of 16");
     size_t np = 0, nb = 0;
     expect(dt_bucket_plan(numels, 1, 4, 2, nullptr, 0, &np, &nb), DT_ERR_ARG, "bucket smaller than an element");
+    // the static staging buffer holds nranks * bucket_bytes at most
+    void* g8[8];
+    size_t numels8[1] = {4};
+    for (int r = 0; r < 8; r++) g8[r] = pool.get(16, 0, true);
+    expect(dt_bucket_allreduce_noalloc(g8, numels8, 1, 8, size_t(32) << 20, DT_FLOAT32, DT_SUM, nullptr), DT_OK,
+           "noalloc, 8 x 32 MiB buckets");
+    expect(dt_bucket_allreduce_noalloc(g8, numels8, 1, 8, (size_t(32) << 20) + 16, DT_FLOAT32, DT_SUM, nullptr),
+           DT_ERR_ARG, "noalloc, buckets beyond the static buffer");
+    expect(dt_bucket_allreduce_noalloc(g8, numels8, 1, 8, 24, DT_FLOAT32, DT_SUM, nullptr), DT_ERR_ARG,
+           "noalloc, bucket not a multiple of 16");
 }
 
 // Partial overlaps between buffers that a launch writes and buffers it reads
