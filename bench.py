@@ -135,24 +135,37 @@ def time_launches(fn, steps, stream):
 
 def cpu_baseline(xs_dev, reps: int):
     """The oracle, untouched, timed on the host: RS then AG on the full
-    workload copied back from the device, `reps` repetitions, median."""
+    workload copied back from the device, median of `reps` repetitions, each
+    timed on its own.  Two legs of the same source: the plain single-threaded
+    build, and its OpenMP build over all host cores (every element still
+    folded by one thread in rank order: the same bytes).  `value` is the
+    all-cores leg; `single_thread` the other."""
     import numpy as np
     import oracle
-    orc = oracle.get()
     host = [x.view(__import__("torch").int16).cpu().numpy().view(np.uint16).reshape(-1) for x in xs_dev]
-    times = []
-    for _ in range(reps):
-        t0 = time.perf_counter()
-        shards = orc.reduce_scatter(host, "sum")
-        orc.all_gather(shards)
-        times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
     s_bytes = host[0].nbytes
-    busbw = s_bytes / t * 2 * (P - 1) / P / 1e9
-    return {"value": round(busbw, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"full workload (P=8 bf16 {SHAPE[0]}x{SHAPE[1]} per rank), RS then AG, "
-                      f"median of {reps} single-threaded runs of {t:.2f} s each; same busbw formula",
-            "seconds_per_step": round(t, 3), "host_cpus": os.cpu_count(), "host_cpu_model": host_cpu_model()}
+
+    def leg(orc, n):
+        times = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            shards = orc.reduce_scatter(host, "sum")
+            orc.all_gather(shards)
+            times.append(time.perf_counter() - t0)
+        t = statistics.median(times)
+        return t, s_bytes / t * 2 * (P - 1) / P / 1e9
+
+    t1, bw1 = leg(oracle.get(), reps)
+    omp = oracle.get_omp()
+    tn, bwn = leg(omp, max(reps, 25))
+    return {"value": round(bwn, 3), "unit": "GB/s", "cores": omp.threads(), "kind": "oracle",
+            "sample": f"full workload (P=8 bf16 {SHAPE[0]}x{SHAPE[1]} per rank), RS then AG, median of "
+                      f"{max(reps, 25)} runs of {tn:.3f} s on {omp.threads()} OpenMP threads (the oracle's loops "
+                      f"built with -fopenmp, same bytes); same busbw formula",
+            "seconds_per_step": round(tn, 4),
+            "single_thread": {"value": round(bw1, 3), "unit": "GB/s", "cores": 1, "seconds_per_step": round(t1, 3),
+                              "sample": f"the same workload, median of {reps} single-threaded runs"},
+            "host_cpus": os.cpu_count(), "host_cpu_model": host_cpu_model()}
 
 
 def host_cpu_model() -> str:
@@ -232,15 +245,43 @@ def sweep(dt, torch, steps: int, warmup: int):
         print(json.dumps({"sweep": rows[-1]}), flush=True)
         del xs, ys
         torch.cuda.empty_cache()
-    s = np.array([r["bytes_per_rank"] for r in rows], dtype=np.float64)
-    t = np.array([r["us"] for r in rows], dtype=np.float64) * 1e-6
-    a = np.stack([np.ones_like(s), 2 * p * s], axis=1) / t[:, None]
-    coef, *_ = np.linalg.lstsq(a, np.ones_like(t), rcond=None)
-    alpha, inv_b = coef
-    fit = {"alpha_us": round(alpha * 1e6, 3), "B_eff_GBps": round(1 / inv_b / 1e9, 1) if inv_b > 0 else None,
-           "model": "T(S) = alpha + 2*P*S/B_eff, P=16, graph-replay times, weights 1/T^2"}
+    fit = alpha_beta_fit([r["bytes_per_rank"] for r in rows], [r["us"] for r in rows], p)
     print(json.dumps({"sweep_fit": fit}), flush=True)
     return rows, fit
+
+
+MALL_BYTES = 256 * 1000 ** 2  # the Infinity Cache: 256 MB
+
+
+def alpha_beta_fit(sizes, us, p: int) -> dict:
+    """The single-device alpha-beta model T(S) = alpha + 2*P*S / B (the c10d
+    page's sec. 6.1 accounting; alpha dominates small messages, sec. 6.5),
+    fitted per regime from graph-replay times:
+      alpha: the mean time of the latency points (S <= 64 KiB per rank);
+      B_hbm: from the points whose footprint 2*P*S exceeds 512 MiB (twice the
+        Infinity Cache), T - alpha weighted 1/T^2;
+      B_cache: the same over the points whose footprint fits the Infinity
+        Cache and whose time is not latency (256 KiB .. footprint <= 256 MB).
+    Each B is a weighted mean of per-point rates, so it lies within them."""
+    s = [float(x) for x in sizes]
+    t = [float(x) * 1e-6 for x in us]
+    lat = [ti for si, ti in zip(s, t) if si <= 64 * 1024]
+    alpha = statistics.mean(lat) if lat else 0.0
+
+    def band(sel):
+        pts = [(2 * p * si, ti) for si, ti in zip(s, t) if sel(si)]
+        if not pts:
+            return None
+        num = sum(x * x / (ti * ti) for x, ti in pts)
+        den = sum(x * (ti - alpha) / (ti * ti) for x, ti in pts)
+        return {"B_GBps": round(num / den / 1e9, 1) if den > 0 else None, "points": len(pts),
+                "best_point_GBps": round(max(x / ti for x, ti in pts) / 1e9, 1)}
+
+    return {"alpha_us": round(alpha * 1e6, 3),
+            "hbm": band(lambda si: 2 * p * si > 512 * 2 ** 20),
+            "cache": band(lambda si: si >= 256 * 1024 and 2 * p * si <= MALL_BYTES),
+            "model": "T(S) = alpha + 2*P*S/B, P=16, graph-replay times; alpha from S <= 64 KiB, B per regime "
+                     "(weights 1/T^2): hbm = footprint > 512 MiB, cache = footprint within the 256 MB Infinity Cache"}
 
 
 def hsdp(dt, torch):
@@ -317,6 +358,127 @@ def hsdp(dt, torch):
                          "frac_of_peak": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     print(json.dumps({"hsdp": out}), flush=True)
     del layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def frac_of_peak(alg_bytes: float, us: float) -> float:
+    return round(alg_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+
+
+def configs(dt, torch, steps: int, warmup: int) -> dict:
+    """One timing of each workload besides the bench step, in bounded time:
+      c1_allreduce_p4: P=4, 1,048,576 fp32 and int32 elements per rank
+        (cache-resident, latency-bound: graph-replay us per call);
+      c3_uneven_all_gather_p8 / c3_all_to_all_p8: fp32 rows of 4096, row
+        counts U[1, 16384] / a U[0, 4096]-row split matrix;
+      c5_allreduce_p16: the sweep's HBM-resident points, fp32 16 MiB .. 1 GiB
+        per rank (graph replay);
+      c5_barrier_p16: 1000 generations of the packed barrier in one launch;
+      c4_pipeline_pass: one pass of the 32-layer gradient pipeline (replicate
+        2 x shard 4, one stream, 25 MiB buckets).
+    Every entry carries its algorithmic HBM bytes and fraction of peak."""
+    import numpy as np
+    import synth
+    stream = torch.cuda.current_stream()
+    out = {}
+
+    def measure(name, fn, alg_bytes, per_graph=10, replays=3, events=True):
+        for _ in range(warmup):
+            fn()
+        row = {"alg_bytes": int(alg_bytes)}
+        if events:
+            evs = time_launches(fn, steps, stream)
+            torch.cuda.synchronize()
+            us = statistics.mean(a.elapsed_time(b) for a, b in evs) * 1e3
+            row["mean_us"] = round(us, 3)
+        g = graph_time_us(torch, fn, per_graph=per_graph, replays=replays)
+        row["graph_us"] = round(g, 3)
+        row["frac_of_peak"] = frac_of_peak(alg_bytes, row.get("mean_us", g))
+        row["frac_of_peak_graph"] = frac_of_peak(alg_bytes, g)
+        out[name] = row
+        print(json.dumps({name: row}), flush=True)
+
+    n = 1 << 20
+    for dtype, xs in (("fp32", synth.uniform_ranks(4, n, seed=0, device="cuda")),
+                      ("int32", synth.int_ranks(4, n, seed=0, device="cuda"))):
+        ys = [torch.empty_like(x) for x in xs]
+        measure(f"c1_allreduce_p4_{dtype}", lambda: dt.dt_allreduce(xs, ys), 2 * 4 * n * 4, per_graph=20, replays=5)
+        out[f"c1_allreduce_p4_{dtype}"]["note"] = "32 MiB footprint: cache-resident, latency-bound"
+        del xs, ys
+
+    w = synth.ROW_WIDTH
+    counts = synth.uneven_row_counts(seed=0)
+    xs = synth.uniform_rows(counts, w, seed=100, device="cuda")
+    total = int(counts.sum()) * w
+    ys = [torch.empty(total, device="cuda") for _ in range(P)]
+    measure("c3_uneven_all_gather_p8", lambda: dt.dt_all_gather(xs, ys), (1 + P) * total * 4, per_graph=4)
+    del xs, ys
+    s_rows = synth.split_matrix(seed=0)
+    xs = synth.uniform_rows([int(s_rows[i].sum()) for i in range(P)], w, seed=200, device="cuda")
+    ys = [torch.empty(int(s_rows[:, j].sum()) * w, device="cuda") for j in range(P)]
+    measure("c3_all_to_all_p8", lambda: dt.dt_all_to_all(xs, ys, (s_rows * w).tolist()),
+            2 * int(s_rows.sum()) * w * 4, per_graph=4)
+    del xs, ys
+    torch.cuda.empty_cache()
+
+    rows = []
+    for nbytes in (16 << 20, 64 << 20, 256 << 20, 1 << 30):
+        xs = synth.uniform_ranks(16, nbytes // 4, seed=0, device="cuda")
+        ys = [torch.empty_like(x) for x in xs]
+        for _ in range(2):
+            dt.dt_allreduce(xs, ys)
+        g = graph_time_us(torch, lambda: dt.dt_allreduce(xs, ys), per_graph=2 if nbytes >= (256 << 20) else 4,
+                          replays=4)
+        alg = 2 * 16 * nbytes
+        rows.append({"bytes_per_rank": nbytes, "graph_us": round(g, 3), "alg_bytes": alg,
+                     "frac_of_peak": frac_of_peak(alg, g),
+                     "busbw_GBps": round(nbytes / (g * 1e-6) * 2 * 15 / 16 / 1e9, 1)})
+        print(json.dumps({"c5_allreduce_p16": rows[-1]}), flush=True)
+        del xs, ys
+        torch.cuda.empty_cache()
+    out["c5_allreduce_p16_fp32"] = rows
+
+    ws = [torch.zeros(16, dtype=torch.int32, device="cuda") for _ in range(16)]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dt.dt_barrier(ws, status, 1, 10)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    dt.dt_barrier(ws, status, 11, 1000)
+    b.record()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    out["c5_barrier_p16"] = {"us_per_generation": round(a.elapsed_time(b) * 1e3 / 1000, 3), "generations": 1000,
+                             "layout": "packed", "alg_bytes": 0}
+    print(json.dumps({"c5_barrier_p16": out["c5_barrier_p16"]}), flush=True)
+
+    layers = [synth.layer_grads(P, layer=l, seed=0, device="cuda") for l in range(synth.NUM_LAYERS)]
+    numels = [int(np.prod(sh)) for sh in synth.LAYER_SHAPES]
+    per_rank_layer = sum(numels) * 2
+    rep, sh = 2, 4
+    fused = [[torch.empty(sum(numels) // sh, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+             for _ in range(synth.NUM_LAYERS)]
+    pipe = dt.HSDPPipeline(rep, sh, bucket_bytes=synth.BUCKET_BYTES)
+    times = []
+    for it in range(3):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for l in reversed(range(synth.NUM_LAYERS)):
+            pipe.post_backward(layers[l], fused[l])
+        pipe.finish()
+        b.record()
+        torch.cuda.synchronize()
+        if it > 0:  # the first pass warms up
+            times.append(a.elapsed_time(b))
+    alg = synth.NUM_LAYERS * (rep * (sh + 1) * per_rank_layer + 2 * P * (per_rank_layer // sh))
+    ms = statistics.median(times)
+    out["c4_pipeline_pass"] = {"ms": round(ms, 3), "alg_bytes": alg, "frac_of_peak": frac_of_peak(alg, ms * 1e3),
+                               "mesh": "replicate 2 x shard 4, one stream", "passes_timed": len(times)}
+    print(json.dumps({"c4_pipeline_pass": out["c4_pipeline_pass"]}), flush=True)
+    pipe.close()
+    del layers, fused, pipe
     torch.cuda.empty_cache()
     return out
 
@@ -672,6 +834,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the one-timing-each pass over the other workloads (C1, C3, C4, C5)")
     ap.add_argument("--cpu-reps", type=int, default=25)
     ap.add_argument("--sweep", action="store_true", help="also run the P=16 size sweep and barrier latency")
     ap.add_argument("--probe", action="store_true", help="only run the kernels for a hardware-counter pass")
@@ -768,6 +932,8 @@ def main():
     extra["int32_max"] = int32_max_step(dt, torch, args.steps, args.warmup, stream)
     extra["copy_ceiling"] = copy_ceiling(torch, stream)
     torch.cuda.empty_cache()
+    if not args.no_configs:
+        extra["configs"] = configs(dt, torch, steps=args.steps, warmup=2)
     if args.all:
         args.sweep = args.hsdp = args.overlap = args.coalescing = True
         extra["rows"] = other_rows(dt, torch, steps=args.steps, warmup=args.warmup)

@@ -72,8 +72,12 @@ typedef enum {
  * 256 MiB for 8 <= P < 16 and from 128 to 192 MiB for P = 4, with count a
  * multiple of P * (16 bytes / element size) and 16-byte aligned buffers, it
  * runs as a ReduceScatter into chunk r of recv[r] followed by an in-place
- * AllGather of the chunks, which is faster there; both forms fold in the
- * same order and give identical bits.  In place is allowed (send[r] ==
+ * AllGather of the chunks, which is faster there.  Beyond 256 MiB per rank
+ * for P >= 8 and beyond 192 MiB for P = 4 it runs window by window (64 MiB
+ * per rank at P >= 16, 128 MiB otherwise), each window an AllReduce of its
+ * own in the two-shot form, so the window's chunks are still in the
+ * Infinity Cache when they fan out.  All forms fold in the same order and
+ * give identical bits.  In place is allowed (send[r] ==
  * recv[r]); any other overlap of a recv buffer with a send or recv buffer
  * is refused (DT_ERR_ARG).  send[r] and recv[r] hold `count` elements. */
 dt_status dt_allreduce(const void* const* send, void* const* recv, int nranks, size_t count,

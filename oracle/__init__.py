@@ -23,6 +23,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "oracle.c")
 LIBRARY = os.path.join(HERE, "liboracle.so")
+# The same source built with -fopenmp: the all-cores leg of the CPU timing.
+LIBRARY_OMP = os.path.join(HERE, "liboracle_omp.so")
 
 GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
              "-Wall", "-Wextra"]
@@ -38,6 +40,11 @@ def build(source: str = SOURCE, output: str = LIBRARY, extra: Sequence[str] = ()
     subprocess.run(cmd, check=True)
     os.replace(output + ".tmp", output)
     return output
+
+
+def build_omp() -> str:
+    """The OpenMP build of the same source (all host cores, same bits)."""
+    return build(output=LIBRARY_OMP, extra=["-fopenmp"])
 
 
 def _dtype_code(a: np.ndarray) -> int:
@@ -80,6 +87,8 @@ class Oracle:
         self.path = path
         lib = ctypes.CDLL(path)
         vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_float_to_bf16.argtypes = [ctypes.c_float]
         lib.oracle_float_to_bf16.restype = ctypes.c_uint16
         lib.oracle_float_to_bf16_array.argtypes = [vp, vp, sz]
@@ -101,6 +110,10 @@ class Oracle:
                      "oracle_all_gather_into_vec", "oracle_all_to_all_dims"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
+
+    def threads(self) -> int:
+        """Threads of the parallel loops: 1 unless this is the OpenMP build."""
+        return int(self.lib.oracle_threads())
 
     # -- conversions ------------------------------------------------------
     def float_to_bf16(self, values: np.ndarray) -> np.ndarray:
@@ -242,3 +255,16 @@ def get() -> Oracle:
     if _default is None:
         _default = Oracle()
     return _default
+
+
+_omp = None
+
+
+def get_omp() -> Oracle:
+    """The OpenMP build of the same oracle (built on first use)."""
+    global _omp
+    if _omp is None:
+        if not os.path.exists(LIBRARY_OMP):
+            build_omp()
+        _omp = Oracle(LIBRARY_OMP)
+    return _omp

@@ -25,6 +25,12 @@
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared.
  * No FMA contraction, no reassociation, SSE scalar float (IEEE binary32).
+ * The same source built with -fopenmp spreads the independent outer loops of
+ * the AllReduce, ReduceScatter and AllGather over the host's cores (the
+ * all-cores leg of the CPU timing).  Each thread takes whole elements (or
+ * whole outputs) and every element is still folded by one thread in rank
+ * order, so both builds give the same bits; without -fopenmp the loops are
+ * the plain single-threaded ones.
  *
  * Pins: every function here is checked by the CPU test suite against brute
  * force on tiny inputs, closed forms, numpy/torch library special cases,
@@ -34,9 +40,26 @@
 #include <stdint.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#define OR_PARALLEL_FOR _Pragma("omp parallel for schedule(static)")
+#else
+#define OR_PARALLEL_FOR
+#endif
+
 enum { OR_FLOAT32 = 0, OR_BFLOAT16 = 1, OR_INT32 = 2 };
 enum { OR_SUM = 0, OR_MAX = 1, OR_MIN = 2, OR_AVG = 3 };
 enum { OR_OK = 0, OR_BAD_ARG = 1 };
+
+/* Threads the parallel loops use: 1 unless built with -fopenmp. */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------- bf16 --- */
 
@@ -160,6 +183,7 @@ int oracle_allreduce(const void* const* x, void* const* y, int nranks, size_t co
 {
     if (!valid(nranks, dtype, op))
         return OR_BAD_ARG;
+    OR_PARALLEL_FOR
     for (size_t e = 0; e < count; e++) {
         fold_one(x, 0, nranks, e, dtype, op, y[0], e);
         for (int q = 1; q < nranks; q++)
@@ -176,9 +200,11 @@ int oracle_reduce_scatter(const void* const* x, void* const* y, int nranks, size
 {
     if (!valid(nranks, dtype, op))
         return OR_BAD_ARG;
-    for (int r = 0; r < nranks; r++)
+    for (int r = 0; r < nranks; r++) {
+        OR_PARALLEL_FOR
         for (size_t i = 0; i < m; i++)
             fold_one(x, (size_t)r * m, nranks, i, dtype, op, y[r], i);
+    }
     return OR_OK;
 }
 
@@ -191,6 +217,7 @@ int oracle_all_gather(const void* const* x, void* const* y, int nranks, const si
 {
     if (nranks < 1 || esize == 0)
         return OR_BAD_ARG;
+    OR_PARALLEL_FOR
     for (int q = 0; q < nranks; q++) {
         size_t at = 0;
         for (int r = 0; r < nranks; r++) {

@@ -154,8 +154,11 @@ hipError_t scratch_base(void** ptr) {
 // function, never from a constant of its own.
 uint64_t seg_rs_tile_vecs(int) { return 384; }
 
+int g_rs_launches = 0;  // ReduceScatter-mode launches (a.rs) since the last reset
+
 hipError_t launch_reduce_vec(const ReduceArgs& a, int, int, hipStream_t) {
     g_launches++;
+    if (a.rs) g_rs_launches++;
     CHECK(a.nranks >= 1 && a.nranks <= kMaxRanksHost, "reduce_vec nranks %d", a.nranks);
     const uint64_t bytes = a.count * 16;
     log_fold(a.dst[0], bytes);
@@ -869,9 +872,16 @@ void big_fan_out() {
 }
 
 // The two-shot AllReduce (P >= 16 from 16 MiB per rank, P = 8-15 at 24-256
-// MiB, P = 4 at 128-192 MiB): fake device ranges.  The ReduceScatter must write chunk
-// r of recv[r] only, and the gather must fan chunk r of recv[r] out to chunk
-// r of every output.  Sizes outside the window keep the one-shot launch.
+// MiB, P = 4 at 128-192 MiB) and, beyond that (P >= 16 above 256 MiB in 64
+// MiB windows, P = 8-15 above 256 MiB and P = 4 above 192 MiB in 128 MiB
+// windows), window by window: fake device ranges.  For every case, rank 0's
+// output is written exactly once (ReduceScatter chunk 0, fan-outs of the
+// other chunks, one-shot tails), each fan-out piece copies a range of rank
+// r's own output to the same offset of output 0, and the number of two-shot
+// windows (ReduceScatter launches) is the expected one.
+namespace dt {
+extern int g_rs_launches;
+}
 void two_shot() {
     using dt::g_gather_pieces;
     using dt::GatherPiece;
@@ -879,28 +889,35 @@ void two_shot() {
         int p;
         dt_dtype dtype;
         size_t count;
-        bool in_place, two;
+        bool in_place;
+        int windows;  // two-shot windows expected (0: one-shot only)
     };
+    const size_t M = size_t(1) << 20;
     const Case cases[] = {
-        {8, DT_BFLOAT16, size_t(64) << 20, false, true},           // 128 MiB per rank
-        {8, DT_BFLOAT16, size_t(64) << 20, true, true},
-        {8, DT_BFLOAT16, size_t(12) << 20, false, true},           // 24 MiB: the lower edge at P=8
-        {8, DT_BFLOAT16, (size_t(12) << 20) - 64, false, false},   // just below it
-        {8, DT_FLOAT32, size_t(64) << 20, false, true},            // 256 MiB: the upper edge at P=8
-        {8, DT_FLOAT32, (size_t(64) << 20) + 32, false, false},    // just beyond it
-        {16, DT_FLOAT32, size_t(4) << 20, false, true},            // 16 MiB: the lower edge at P=16
-        {16, DT_FLOAT32, (size_t(4) << 20) - 64, false, false},    // just below it
-        {16, DT_FLOAT32, size_t(8) << 20, false, true},            // 32 MiB
-        {16, DT_FLOAT32, size_t(64) << 20, true, true},            // 256 MiB
-        {16, DT_FLOAT32, (size_t(96) << 20) + 64, false, true},    // 384 MiB + 256 B: a windowed fan-out
-        {12, DT_INT32, size_t(48) << 20, false, true},             // 192 MiB
-        {8, DT_BFLOAT16, (size_t(64) << 20) + 8, false, false},    // not a multiple of P vectors
-        {4, DT_FLOAT32, size_t(32) << 20, false, true},            // 128 MiB at P=4
-        {4, DT_FLOAT32, size_t(48) << 20, true, true},             // 192 MiB at P=4
-        {4, DT_FLOAT32, size_t(16) << 20, false, false},           // 64 MiB at P=4
-        {4, DT_FLOAT32, (size_t(48) << 20) + 16, false, false},    // just beyond 192 MiB at P=4
-        {2, DT_FLOAT32, size_t(32) << 20, false, false},           // P=2
-        {6, DT_FLOAT32, size_t(48) << 20, false, false},           // P=6
+        {8, DT_BFLOAT16, 64 * M, false, 1},           // 128 MiB per rank
+        {8, DT_BFLOAT16, 64 * M, true, 1},
+        {8, DT_BFLOAT16, 12 * M, false, 1},           // 24 MiB: the lower edge at P=8
+        {8, DT_BFLOAT16, 12 * M - 64, false, 0},      // just below it
+        {8, DT_FLOAT32, 64 * M, false, 1},            // 256 MiB: the upper edge at P=8
+        {8, DT_FLOAT32, 64 * M + 32, false, 2},       // beyond it: two 128 MiB windows and a one-shot tail
+        {8, DT_BFLOAT16, 192 * M, true, 3},           // 384 MiB in place: three windows
+        {16, DT_FLOAT32, 4 * M, false, 1},            // 16 MiB: the lower edge at P=16
+        {16, DT_FLOAT32, 4 * M - 64, false, 0},       // just below it
+        {16, DT_FLOAT32, 8 * M, false, 1},            // 32 MiB
+        {16, DT_FLOAT32, 64 * M, true, 1},            // 256 MiB: still one call
+        {16, DT_FLOAT32, 96 * M + 64, false, 6},      // 384 MiB + 256 B: six 64 MiB windows and a one-shot tail
+        {16, DT_FLOAT32, 80 * M + 4096, true, 5},     // 320 MiB + 16 KiB: five windows and a one-shot tail
+        {12, DT_INT32, 48 * M, false, 1},             // 192 MiB
+        {12, DT_INT32, 72 * M, false, 3},             // 288 MiB at P=12: windows of whole vectors per chunk
+        {12, DT_BFLOAT16, 200 * M + 96, false, 3},    // 400 MiB + 192 B at P=12: three windows, a one-shot tail
+        {8, DT_BFLOAT16, 64 * M + 8, false, 0},       // not a multiple of P vectors
+        {4, DT_FLOAT32, 32 * M, false, 1},            // 128 MiB at P=4
+        {4, DT_FLOAT32, 48 * M, true, 1},             // 192 MiB at P=4
+        {4, DT_FLOAT32, 16 * M, false, 0},            // 64 MiB at P=4
+        {4, DT_FLOAT32, 48 * M + 16, false, 1},       // beyond 192 MiB at P=4: 128 MiB window + a 64 MiB one-shot window
+        {4, DT_FLOAT32, 64 * M, false, 2},            // 256 MiB at P=4: two 128 MiB windows
+        {2, DT_FLOAT32, 32 * M, false, 0},            // P=2
+        {6, DT_FLOAT32, 48 * M, false, 0},            // P=6
     };
     char* base = reinterpret_cast<char*>(uintptr_t(1) << 45);  // fake, never dereferenced
     for (const Case& c : cases) {
@@ -919,28 +936,36 @@ void two_shot() {
             }
         }
         g_gather_pieces.clear();
-        const long before = g_launches;
+        dt::g_rs_launches = 0;
+        dt::g_fold_log.clear();
+        dt::g_log_folds = true;
         expect(dt_allreduce(send, recv, c.p, c.count, c.dtype, DT_SUM, nullptr), DT_OK, "two-shot allreduce");
-        if (!c.two) {
-            CHECK(g_gather_pieces.empty(), "allreduce of %zu bytes per rank at P=%d took the two-shot form", bytes, c.p);
-            continue;
+        dt::g_log_folds = false;
+        CHECK(dt::g_rs_launches == c.windows, "allreduce of %zu bytes per rank at P=%d: %d two-shot windows, expected %d",
+              bytes, c.p, dt::g_rs_launches, c.windows);
+        if (c.windows == 0) CHECK(g_gather_pieces.empty(), "one-shot allreduce with a fan-out");
+        // every fan-out piece: a range of rank r's own output, copied to the same offset of output 0
+        for (const GatherPiece& g : g_gather_pieces) {
+            int owner = -1;
+            for (int r = 0; r < c.p; r++)
+                if (g.src >= static_cast<const char*>(recv[r]) && g.src < static_cast<const char*>(recv[r]) + bytes)
+                    owner = r;
+            CHECK(owner >= 0, "two-shot allreduce: a fan-out source outside the outputs");
+            const uint64_t off = uint64_t(g.src - static_cast<const char*>(recv[owner]));
+            CHECK(g.dst0 == static_cast<const char*>(recv[0]) + off, "two-shot allreduce: fan-out piece moved");
         }
-        const uint64_t cb = bytes / c.p;
-        if (bytes <= dt::kFanOutDirectBytes)
-            CHECK(g_launches - before == 2, "two-shot allreduce: %ld launches", g_launches - before);
-        // every chunk r is fanned out from recv[r] + r * cb to offset r * cb, in order, once
-        for (int r = 0; r < c.p; r++) {
-            const char* s0 = static_cast<const char*>(recv[r]) + r * cb;
-            uint64_t covered = 0;
-            for (const GatherPiece& g : g_gather_pieces) {
-                if (g.src < s0 || g.src >= s0 + cb) continue;
-                CHECK(g.src == s0 + covered && g.dst0 == static_cast<const char*>(recv[0]) + r * cb + covered,
-                      "two-shot allreduce: chunk %d piece out of place", r);
-                covered += g.bytes;
-            }
-            CHECK(covered == cb, "two-shot allreduce: chunk %d covered %llu of %llu bytes", r,
-                  (unsigned long long)covered, (unsigned long long)cb);
+        // rank 0's output: written exactly once, no gap, no overlap
+        std::vector<std::pair<const char*, uint64_t>> w = dt::g_fold_log;
+        std::sort(w.begin(), w.end());
+        uint64_t at = 0;
+        const char* r0 = static_cast<const char*>(recv[0]);
+        for (const auto& e : w) {
+            CHECK(e.first == r0 + at, "allreduce: output 0 written at +%lld, expected +%llu", (long long)(e.first - r0),
+                  (unsigned long long)at);
+            at += e.second;
         }
+        CHECK(at == bytes, "allreduce: output 0 covered %llu of %llu bytes", (unsigned long long)at,
+              (unsigned long long)bytes);
     }
     g_bufs.clear();
 }

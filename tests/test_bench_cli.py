@@ -46,3 +46,27 @@ def test_kernel_source_hash_is_stable():
 
 def test_host_cpu_model_is_a_string():
     assert isinstance(bench.host_cpu_model(), str)
+
+
+def test_alpha_beta_fit_by_regime():
+    """Points made from alpha = 3 us, a cache-resident rate of 9 TB/s and an
+    HBM rate of 6 TB/s: the fit recovers each, and the HBM figure never
+    exceeds the best measured HBM point."""
+    p, alpha = 16, 3e-6
+    sizes = [4 ** k for k in range(6, 16)]
+    us = []
+    for s in sizes:
+        b = 9e12 if 2 * p * s <= bench.MALL_BYTES else 6e12
+        t = alpha + 2 * p * s / b
+        us.append(t * 1e6)
+    fit = bench.alpha_beta_fit(sizes, us, p)
+    assert fit["alpha_us"] == pytest.approx(sum(us[:3]) / 3, abs=1e-3)
+    assert fit["hbm"]["points"] == 3  # 64 MiB, 256 MiB and 1 GiB per rank
+    assert fit["hbm"]["B_GBps"] <= fit["hbm"]["best_point_GBps"] * 1.01
+    assert fit["hbm"]["B_GBps"] == pytest.approx(6000, rel=0.01)
+    assert fit["cache"]["points"] == 3  # 256 KiB, 1 MiB and 4 MiB per rank
+    assert fit["cache"]["B_GBps"] == pytest.approx(9000, rel=0.05)
+    # measured-looking points: the HBM figure stays within the measured rates
+    us2 = [3.5, 3.6, 4.0, 5.2, 7.0, 14.0, 95.0, 356.0, 1371.0, 5718.0]
+    fit2 = bench.alpha_beta_fit(sizes, us2, p)
+    assert fit2["hbm"]["B_GBps"] <= fit2["hbm"]["best_point_GBps"]

@@ -117,13 +117,42 @@ def test_allreduce_two_shot_window(dt, orc, p, dtype, n, op, in_place):
         assert torch.equal(bits(ys[q]), bits(ys[0])), f"rank {q} differs from rank 0"
 
 
+@pytest.mark.parametrize("p,dtype,n,op,in_place", [
+    (8, "bf16", (128 << 20) + 5, "sum", False),   # 256 MiB + 10 B: two 128 MiB windows, a 5-element tail
+    (12, "f32", (64 << 20) + 4, "max", False),    # 256 MiB + 16 B at P=12: windows of whole vectors per chunk
+    (16, "f32", (64 << 20) + 1, "sum", False),    # four 64 MiB windows and a one-element tail
+    (16, "f32", (96 << 20) + 64, "avg", True),    # 384 MiB + 256 B in place: six windows, a one-shot tail
+    (4, "f32", (48 << 20) + 16, "sum", False),    # 192 MiB + 64 B at P=4: a 128 MiB window, then a one-shot one
+    (8, "i32", 96 << 20, "max", True),            # 384 MiB in place: three windows
+])
+def test_allreduce_windowed(dt, orc, p, dtype, n, op, in_place):
+    """AllReduces beyond the single-call range (P >= 8 above 256 MiB per rank,
+    P = 4 above 192 MiB) run window by window, each window in the two-shot
+    form where it fits, the last partial window one-shot.  Rank 0's output
+    is compared with the oracle element by element (every window boundary
+    and chunk edge included); every other rank's output must equal rank 0's
+    bit for bit."""
+    note(f"allreduce windowed P={p} {dtype} n={n} {op} in_place={in_place}")
+    xs = rank_inputs(dtype, p, n, seed=70 + p)
+    host = [to_np(x) for x in xs]
+    ys = xs if in_place else [torch.empty_like(x) for x in xs]
+    dt.dt_allreduce(xs, ys, op=op)
+    torch.cuda.synchronize()
+    want = orc.allreduce(host, op)[0]
+    del host
+    compare(to_np(ys[0]), want, "rank 0")
+    bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
+    for q in range(1, p):
+        assert torch.equal(bits(ys[q]), bits(ys[0])), f"rank {q} differs from rank 0"
+
+
 @pytest.mark.parametrize("p,dtype,n,op", [
-    (8, "bf16", (128 << 20) + 5, "sum"),   # 256 MiB + 10 B: beyond the P=8 two-shot window, ragged tail
-    (12, "f32", (64 << 20) + 4, "max"),    # 256 MiB + 16 B at P=12 (twelve of sixteen slots)
-    (16, "f32", (64 << 20) + 1, "sum"),    # P=16, not a whole number of vectors per chunk
+    (6, "bf16", (128 << 20) + 5, "sum"),   # 256 MiB + 10 B at P=6, ragged tail
+    (7, "f32", (64 << 20) + 4, "max"),     # 256 MiB + 16 B at P=7 (seven of eight slots)
+    (5, "f32", (64 << 20) + 1, "sum"),     # P=5, a one-element tail
 ])
 def test_allreduce_one_shot_wave_tiles(dt, orc, p, dtype, n, op):
-    """One-shot AllReduces of more than 256 MiB per rank at P >= 8, which run
+    """One-shot AllReduces of more than 256 MiB per rank at P = 5-7, which run
     in single-wave tiles (plus the element path for a ragged tail).  Rank 0's
     output is compared with the oracle element by element; every other
     rank's output must equal rank 0's bit for bit."""

@@ -1,8 +1,9 @@
 """GPU parity across the message-size sweep: fp32 AllReduce, P=16, per-rank
 sizes 4 KiB .. 1 GiB in powers of 4, values U[-1,1).  Up to 16 MiB every
-element is compared with the oracle; above that, 2^20 sampled positions are
-recomputed by the oracle from the device inputs and every rank's output is
-checked to be byte-identical to rank 0's."""
+element is compared with the oracle; above that, 2^20 sampled positions and
+the elements around every 1 MiB boundary (every window and chunk edge of the
+two-shot and windowed forms) are recomputed by the oracle from the device
+inputs, and every rank's output is checked to be byte-identical to rank 0's."""
 import numpy as np
 import pytest
 import torch
@@ -34,8 +35,15 @@ def test_sweep_point(dt, nbytes):
         for q in range(p):
             compare(to_np(ys[q]), want[q], f"rank {q}")
     else:
+        # 2^20 random positions, plus the elements around every 1 MiB boundary
+        # (which includes each window and chunk edge of a windowed or two-shot
+        # AllReduce: those are whole MiB multiples at these sizes)
         rng = np.random.default_rng(nbytes)
-        idx = torch.from_numpy(np.sort(rng.choice(n, size=1 << 20, replace=False))).cuda()
+        edges = np.arange(0, n, (1 << 20) // 4, dtype=np.int64)
+        near = (edges[:, None] + np.arange(-2, 3)[None, :]).reshape(-1)
+        near = near[(near >= 0) & (near < n)]
+        picks = np.union1d(rng.choice(n, size=1 << 20, replace=False), np.append(near, n - 1))
+        idx = torch.from_numpy(picks).cuda()
         want = orc.allreduce([to_np(x[idx]) for x in xs], "sum")
         for q in range(p):
             compare(to_np(ys[q][idx]), want[q], f"rank {q} sampled")
