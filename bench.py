@@ -781,6 +781,8 @@ def probe_rows(dt, torch, reps: int = 3):
             torch.cuda.synchronize()
         print(json.dumps({"probe_row": name, "reps": reps, "alg_bytes_per_call": int(alg_bytes),
                           "kernels": kernels}), flush=True)
+        torch.zeros(1, device="cuda")  # a fill kernel: marks the workload's end in the dispatch order
+        torch.cuda.synchronize()
 
     s_rows = np.random.default_rng(1).integers(0, 4097, (P, P))
     xs = synth.uniform_rows(s_rows.sum(axis=1), w, seed=200, device="cuda")
@@ -799,15 +801,15 @@ def probe_rows(dt, torch, reps: int = 3):
     ys = [torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
     s_bytes = SHAPE[0] * SHAPE[1] * 2
     run("allreduce_two_shot_p8_bf16", lambda: dt.dt_allreduce(xs, ys), 2 * P * s_bytes,
-        ["k_reduce_scatter_vec<1, 0, 8, true, 64, 1>", "k_gather<8, true, 1, 128>"])
+        ["k_reduce_scatter_vec<1, 0, 8, 64, 1>", "k_gather<8, true, 1, 128>"])
     del xs, ys
     torch.cuda.empty_cache()
     layer = synth.layer_grads(P, layer=0, seed=0, device="cuda")
     numels = [int(np.prod(sh)) for sh in synth.LAYER_SHAPES]
     per_rank_layer = sum(numels) * 2
     run("bucket_allreduce_layer_p8", lambda: dt.dt_bucket_allreduce(layer, bucket_bytes=synth.BUCKET_BYTES),
-        2 * P * per_rank_layer, ["k_reduce_scatter_vec<1, 0, 8, true, 64, 1>", "k_gather<8, true, 1, 128>",
-                                 "k_reduce_pieces<dt::PieceArgs, 1, 0, 8, true>"])
+        2 * P * per_rank_layer, ["k_reduce_scatter_vec<1, 0, 8, 64, 1>", "k_gather<8, true, 1, 128>",
+                                 "k_reduce_pieces<dt::PieceArgs, 1, 0, 8>"])
     rep, sh = 2, 4
     fused = [torch.empty(sum(numels) // sh, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
     pipe = dt.HSDPPipeline(rep, sh, bucket_bytes=synth.BUCKET_BYTES)
@@ -817,9 +819,37 @@ def probe_rows(dt, torch, reps: int = 3):
         pipe.finish()
     run("gradient_pipeline_layer_r2s4", one_layer,
         rep * (sh + 1) * per_rank_layer + 2 * P * (per_rank_layer // sh),
-        ["k_reduce_scatter_segs<1, 0, 4, true, 1>", "k_reduce_pieces<dt::PieceArgs, 1, 0, 2, true>"])
+        ["k_reduce_scatter_segs<1, 0, 4, 1>", "k_reduce_pieces<dt::PieceArgs, 1, 0, 2>"])
     del pipe, fused, layer
     torch.cuda.empty_cache()
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "done", "reps": reps, "copy_bytes_each_way": a.numel() * 4}), flush=True)
+
+
+def probe_sweep(dt, torch, reps: int = 3):
+    """Workload for hardware-counter passes over the HBM-resident points of
+    the P=16 fp32 AllReduce sweep (16 MiB, 64 MiB, 256 MiB and 1 GiB per
+    rank), each call repeated ``reps`` times with a synchronization in
+    between, then the 1 GiB copy that calibrates the counters.  Prints one
+    JSON line per point with its algorithmic bytes (2 * P * S) and the
+    number of kernel dispatches one call makes, so a counter CSV splits by
+    dispatch order."""
+    import synth
+    p = 16
+    for nbytes in (16 << 20, 64 << 20, 256 << 20, 1 << 30):
+        xs = synth.uniform_ranks(p, nbytes // 4, seed=0, device="cuda")
+        ys = [torch.empty_like(x) for x in xs]
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            dt.dt_allreduce(xs, ys)
+            torch.cuda.synchronize()
+        print(json.dumps({"probe_sweep": nbytes, "reps": reps, "alg_bytes_per_call": 2 * p * nbytes}), flush=True)
+        del xs, ys
+        torch.cuda.empty_cache()
     a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     for _ in range(reps):
@@ -841,6 +871,8 @@ def main():
     ap.add_argument("--probe", action="store_true", help="only run the kernels for a hardware-counter pass")
     ap.add_argument("--probe-rows", action="store_true",
                     help="only run the other rows' workloads once each (x3) for a hardware-counter pass")
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="only run the P=16 sweep's HBM-resident AllReduces (x3) for a hardware-counter pass")
     ap.add_argument("--hsdp", action="store_true", help="also time the 32-layer gradient pipeline (103.6 GB)")
     ap.add_argument("--overlap", action="store_true", help="also run the GEMM / AllReduce overlap experiment")
     ap.add_argument("--coalescing", action="store_true", help="also compare the ways to reduce many small tensors")
@@ -864,6 +896,9 @@ def main():
         return
     if args.probe_rows:
         probe_rows(dt, torch)
+        return
+    if args.probe_sweep:
+        probe_sweep(dt, torch)
         return
     stream = torch.cuda.current_stream()
     xs = synth.normal_ranks(P, SHAPE, seed=0, device="cuda", dtype=torch.bfloat16)

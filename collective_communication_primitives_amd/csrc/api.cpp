@@ -139,18 +139,22 @@ dt_status fan_out(const void* const* src, const size_t* counts, void* const* tab
 // in-place AllGather of the chunks.  It moves (2P+1)S bytes against the
 // one-shot fold's 2PS, but as a P-to-1 fold and a 1-to-P fan-out whose
 // sources (S bytes in all) are still in the 256 MB Infinity Cache when the
-// fan-out reads them (beyond 256 MiB the fan-out pulls them back window by
-// window).  Measured on the MI355X against the one-shot kernel, each size
-// under two buffer placements: P >= 16 gains 4-10% from 16 MiB per rank up
-// to 1 GiB (one tie at 1 GiB); P = 8 gains 2-15% from 24 to 256 MiB (bf16
-// at 96 MiB loses 1-4%), ties at 384 MiB and loses 2% at 512 MiB in fp32;
-// P = 4 gains 0-7% at 128-192 MiB, is mixed at 96 and 256 MiB and loses
-// 18-26% at 320 MiB.  Below these windows the second launch costs more than
-// the pattern saves.  Other rank counts keep the one-shot form.
+// fan-out reads them.  Measured on the MI355X against the one-shot kernel
+// (in-process A/B, graph replay, fp32 unless noted):
+//   P = 16: 4-10% faster from 16 MiB per rank up;
+//   P = 8: 2-15% faster from 24 to 256 MiB (bf16 at 96 MiB: 1-4% slower);
+//   P = 9, 12, 15: 3-15% faster from 24 MiB to 256 MiB, 2-14% slower at 8 MiB;
+//   P = 5-7: 2-11% faster from 32 to 256 MiB, 2-24% slower at 8-16 MiB,
+//     within 5% at 24 MiB;
+//   P = 4: 0-7% faster at 128-192 MiB, mixed at 96 and 256 MiB, 18-26%
+//     slower at 320 MiB.
+// P = 2-3 keep the one-shot form.  Below these windows the second launch
+// costs more than the pattern saves.
 bool two_shot_pays(int nranks, uint64_t bytes_per_rank) {
     constexpr uint64_t MiB = 1ull << 20;
     if (nranks >= 16) return bytes_per_rank >= 16 * MiB;
     if (nranks >= 8) return bytes_per_rank >= 24 * MiB && bytes_per_rank <= 256 * MiB;
+    if (nranks >= 5) return bytes_per_rank >= 32 * MiB && bytes_per_rank <= 256 * MiB;
     if (nranks == 4) return bytes_per_rank >= 128 * MiB && bytes_per_rank <= 192 * MiB;
     return false;
 }
@@ -159,22 +163,25 @@ bool two_shot_pays(int nranks, uint64_t bytes_per_rank) {
 // range.  Each element's result depends only on that element, so the
 // AllReduce of a long range is the AllReduces of consecutive windows of it.
 // A window runs in the two-shot form, and its ReduceScatter leaves the
-// window's chunks (window bytes in all) in the Infinity Cache for the fan-out
-// right after it, where one call over the whole range needs a read pass per
-// fan-out window and, at P = 4-15, the one-shot kernel.  Measured on the
-// MI355X, graph replay against one call, outputs bit-identical:
-//   P=16 fp32 1 GiB per rank 5942 -> 5718 us with 64 MiB windows (32 MiB:
-//     5804, 96: 5794, 128: 5803), 768 MiB 4409 -> 4270, 512 MiB 2977 -> 2906
-//     (128 MiB: 2884); at 256 MiB one call stays faster (1371 against 1404);
-//   P=8 bf16 512 MiB 1492 -> 1386 us and 1 GiB 2955 -> 2782 with 128 MiB
-//     windows (256 MiB: within 0.3%); fp32 1 GiB 4741 -> 2734;
-//   P=4 fp32 1 GiB 1507 -> 1419 us (64 MiB windows 1440, 192 MiB 1450).
+// window's chunks in the Infinity Cache for the fan-out right after it,
+// where one call over the whole range needs a read pass per fan-out window
+// (P >= 16) or runs the one-shot kernel (P = 5-15).  Measured on the MI355X,
+// in-process A/B under two buffer placements, graph replay, bit-identical:
+//   P=16 fp32, 64 MiB windows against one call: 2.0-4.8% faster at 320 MiB
+//     to 1 GiB per rank (1 GiB: 5516 against 5648 us, 5703 against 5816);
+//     128 MiB windows -1.3..+0.2% and 256 MiB windows -1.9..+2.1% against
+//     64 MiB ones; at 256 MiB one call stays faster (1371 against 1404 us);
+//   P=8 bf16, 128 MiB windows against the one-shot kernel: 0.4-1.9% slower
+//     at some placements, 7.6-9.5% faster at others (512 MiB, 1 GiB), so
+//     the windows are the steadier choice (0.775-0.797 of peak throughout);
+//     fp32 1 GiB 4741 -> 2734 us at one placement;
+//   P=4: no windows: the one-shot kernel is 3-5% faster at 224-256 MiB and
+//     within placement noise (+-8%) beyond.
 // Each window lies inside two_shot_pays' range for its rank count.
 uint64_t allreduce_window(int nranks, uint64_t bytes_per_rank) {
     constexpr uint64_t MiB = 1ull << 20;
     if (nranks >= 16) return bytes_per_rank > 256 * MiB ? 64 * MiB : 0;
-    if (nranks >= 8) return bytes_per_rank > 256 * MiB ? 128 * MiB : 0;
-    if (nranks == 4) return bytes_per_rank > 192 * MiB ? 128 * MiB : 0;
+    if (nranks >= 5) return bytes_per_rank > 256 * MiB ? 128 * MiB : 0;
     return 0;
 }
 
@@ -192,9 +199,20 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
     a.rs = 0;
     const size_t v = vec_elems(dtype);
     const size_t es = esize_of(dtype);
-    if (vec && count % (size_t(nranks) * v) == 0 && two_shot_pays(nranks, uint64_t(count) * es)) {
-        const size_t m = count / nranks;  // elements per chunk, a whole number of vectors
-        const uint64_t cb = uint64_t(m) * es;
+    // Two-shot chunks are whole multiples of kChunkVecs vectors (1 KiB, the
+    // ReduceScatter tile), all but the last, which takes the rest: every
+    // chunk then starts on a cache-line boundary at any rank count, so no
+    // line of an output is written by two workgroups.  Equal chunks of
+    // count / P elements (the earlier cut) put the chunk starts of P = 5-15
+    // off the lines, and the two-shot form then ran 15-80% slower than the
+    // one-shot kernel at most sizes (in-process A/B, P = 5-7, 9, 10, 12, 15).
+    constexpr uint64_t kChunkVecs = 64;
+    const uint64_t nv = count / v;
+    const uint64_t per = (nv + nranks - 1) / nranks;                      // vectors per chunk, rounded up
+    const uint64_t mc = (per + kChunkVecs - 1) / kChunkVecs * kChunkVecs;  // ... to whole tiles
+    if (vec && count % v == 0 && mc * uint64_t(nranks - 1) < nv && two_shot_pays(nranks, uint64_t(count) * es)) {
+        const uint64_t last = nv - mc * uint64_t(nranks - 1);  // 0 < last <= mc
+        const uint64_t cb = mc * 16;                           // chunk stride in bytes
         dt::ReduceArgs rs = a;
         const void* own[dt::kMaxRanksHost];
         size_t counts[dt::kMaxRanksHost];
@@ -202,13 +220,14 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
         for (int r = 0; r < nranks; r++) {
             rs.dst[r] = static_cast<char*>(recv[r]) + r * cb;
             own[r] = rs.dst[r];
-            counts[r] = m;
+            counts[r] = size_t((r + 1 < nranks ? mc : last) * v);
             for (int q = 0; q < nranks; q++) table[size_t(r) * nranks + q] = static_cast<char*>(recv[q]) + r * cb;
         }
         rs.rs = 1;
         rs.first = 0;
-        rs.count = m / v;
-        rs.chunk_elems = m;
+        rs.count = mc;
+        rs.last_count = last;
+        rs.chunk_elems = size_t(mc * v);
         dt_status st = check_hip(dt::launch_reduce_vec(rs, dtype, op, stream), "allreduce (reduce_scatter) launch");
         if (st != DT_OK) return st;
         return fan_out(own, counts, table, nranks, es, stream, "allreduce (all_gather) launch");
@@ -238,10 +257,7 @@ dt_status allreduce_impl(const void* const* send, void* const* recv, int nranks,
     const size_t es = esize_of(dtype);
     const uint64_t win = allreduce_window(nranks, uint64_t(count) * es);
     if (win == 0) return allreduce_one(send, recv, nranks, count, dtype, op, stream);
-    // a window is a whole number of vectors per chunk, so that every full
-    // window may take the two-shot form and keeps each buffer's alignment
-    const size_t unit = size_t(nranks) * vec_elems(dtype);
-    const size_t win_elems = std::max(unit, size_t(win / es) / unit * unit);
+    const size_t win_elems = size_t(win / es);  // whole vectors: every window keeps each buffer's alignment
     const void* s[dt::kMaxRanksHost];
     void* d[dt::kMaxRanksHost];
     for (size_t e0 = 0; e0 < count; e0 += win_elems) {
@@ -593,7 +609,7 @@ dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nran
     a.chunk_elems = recvcount;
     if (vec) {
         a.first = 0;
-        a.count = recvcount / vec_elems(dtype);
+        a.count = a.last_count = recvcount / vec_elems(dtype);
         return check_hip(dt::launch_reduce_vec(a, dtype, op, stream), "reduce_scatter launch");
     }
     a.first = 0;

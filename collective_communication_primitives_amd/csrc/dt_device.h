@@ -132,7 +132,11 @@ struct Elems {
 };
 
 // Fold P vectors (x[0..P-1]) element-wise in rank order.  NR = live ranks
-// (runtime, NR <= P); with NR == P the branches fold away.
+// (runtime, NR <= P); with NR == P the selects fold away.  A slot past the
+// live ranks is combined and its result discarded by a select, not skipped
+// by a branch: a branch lets the compiler sink that slot's load into it,
+// which then waits for every load in turn instead of keeping them all in
+// flight.
 template <int DT, int OP, int P>
 __device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[P], int nr) {
     u32x4 out;
@@ -145,12 +149,13 @@ __device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[P], int nr) {
         }
 #pragma unroll
         for (int r = 1; r < P; r++) {
-            if (r < nr) {
+            const bool live = r < nr;
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    acc[2 * i] = combine<OP>(acc[2 * i], bf16_lo(x[r][i]));
-                    acc[2 * i + 1] = combine<OP>(acc[2 * i + 1], bf16_hi(x[r][i]));
-                }
+            for (int i = 0; i < 4; i++) {
+                const float lo = combine<OP>(acc[2 * i], bf16_lo(x[r][i]));
+                const float hi = combine<OP>(acc[2 * i + 1], bf16_hi(x[r][i]));
+                acc[2 * i] = live ? lo : acc[2 * i];
+                acc[2 * i + 1] = live ? hi : acc[2 * i + 1];
             }
         }
 #pragma unroll
@@ -161,9 +166,11 @@ __device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[P], int nr) {
         for (int i = 0; i < 4; i++) acc[i] = __uint_as_float(x[0][i]);
 #pragma unroll
         for (int r = 1; r < P; r++) {
-            if (r < nr) {
+            const bool live = r < nr;
 #pragma unroll
-                for (int i = 0; i < 4; i++) acc[i] = combine<OP>(acc[i], __uint_as_float(x[r][i]));
+            for (int i = 0; i < 4; i++) {
+                const float c = combine<OP>(acc[i], __uint_as_float(x[r][i]));
+                acc[i] = live ? c : acc[i];
             }
         }
 #pragma unroll
@@ -174,9 +181,11 @@ __device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[P], int nr) {
         for (int i = 0; i < 4; i++) acc[i] = int32_t(x[0][i]);
 #pragma unroll
         for (int r = 1; r < P; r++) {
-            if (r < nr) {
+            const bool live = r < nr;
 #pragma unroll
-                for (int i = 0; i < 4; i++) acc[i] = combine<OP>(acc[i], int32_t(x[r][i]));
+            for (int i = 0; i < 4; i++) {
+                const int32_t c = combine<OP>(acc[i], int32_t(x[r][i]));
+                acc[i] = live ? c : acc[i];
             }
         }
 #pragma unroll

@@ -16,7 +16,9 @@ struct ReduceArgs {
     const void* src[kMaxRanksHost];
     void* dst[kMaxRanksHost];
     uint64_t first;        // first element handled by this launch (element path)
-    uint64_t count;        // elements per chunk handled by this launch
+    uint64_t count;        // elements per chunk handled by this launch (vector path: vectors);
+                           // ReduceScatter: also the stride between chunk starts
+    uint64_t last_count;   // vector ReduceScatter: vectors of the last chunk (<= count)
     uint64_t chunk_elems;  // ReduceScatter: elements per output chunk
     int nranks;
     int rs;                // 1: ReduceScatter (grid.y = chunk), 0: AllReduce

@@ -9,16 +9,19 @@
 // ReduceScatter).  Every HBM byte is
 // touched once: AllReduce moves 2*P*S bytes, ReduceScatter (P+1)*S.
 //
-// The rank count is a template upper bound PMAX in {1, 2, 4, 8, 16}.  When
-// P equals PMAX (EXACT) the count is a compile-time constant and the kernel
-// is fully unrolled; other P pass the live count as an argument.
+// The rank count P (1..16) is a template parameter of every fold kernel, so
+// each fold is fully unrolled with no per-rank predicate and the P loads of
+// a vector go out back to back.  (With a runtime count below a template
+// bound, the compiler turned the per-rank guards into branches and waited
+// for each load in turn: the ReduceScatter of P = 5-7 took 2x as long.)
+#include <type_traits>
+
 #include "dt_device.h"
 #include "dt_launch.h"
 
 namespace dt {
 
-// One wave, one vector per thread: the tile of the ReduceScatter, and of a
-// one-shot AllReduce of P >= 8 ranks above kWaveAllReduceBytes per rank.
+// One wave, one vector per thread: the tile of the ReduceScatter.
 constexpr int kWaveBlock = 64;
 
 // ------------------------------------------------------------- AllReduce --
@@ -29,52 +32,49 @@ constexpr int kWaveBlock = 64;
 // the next, which the MI355X's HBM serves faster than interleaving the P
 // buffers vector by vector (measured: +3% for the P-to-P AllReduce pattern).
 // BST: store through buffer instructions (see the store loop).
-template <int DT, int OP, int PMAX, bool EXACT, int U, int BLOCK, bool BST = false>
+template <int DT, int OP, int P, int U, int BLOCK, bool BST = false>
 __global__ __launch_bounds__(BLOCK) void k_reduce_vec(ReduceArgs a) {
     const uint64_t base = uint64_t(blockIdx.x) * (BLOCK * U) + threadIdx.x;
-    const int nr = EXACT ? PMAX : a.nranks;
-    u32x4 x[U][PMAX];
+    // Loads without branches, so that all P * U of them are in flight at
+    // once: a lane past the end re-reads the last vector (its result is not
+    // stored).  A per-lane guard around each load compiled into a wait after
+    // every load.
+    u32x4 x[U][P];
 #pragma unroll
-    for (int r = 0; r < PMAX; r++) {
-        if (r < nr) {
+    for (int r = 0; r < P; r++) {
+        const char* src = static_cast<const char*>(a.src[r]);
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                const uint64_t v = base + uint64_t(u) * BLOCK;
-                if (v < a.count) x[u][r] = load16(static_cast<const char*>(a.src[r]) + v * 16);
-            }
+        for (int u = 0; u < U; u++) {
+            const uint64_t v = base + uint64_t(u) * BLOCK;
+            x[u][r] = load16(src + (v < a.count ? v : a.count - 1) * 16);
         }
     }
     u32x4 y[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) y[u] = fold_vec<DT, OP, PMAX>(x[u], nr);
-    if constexpr (BLOCK == kWaveBlock || BST) {
+    for (int u = 0; u < U; u++) y[u] = fold_vec<DT, OP, P>(x[u], P);
+    if constexpr (BST) {
         // Buffer stores, non-temporal with device scope, where they measured
-        // faster than non-temporal global stores (in-process A/B): the one-wave
-        // tiles (P >= 8 beyond 256 MiB per rank, 3%) and every P >= 2 up to
-        // kBufferStoreAllReduceBytes per rank (graph-replay times at 1-8 MiB:
-        // P=2 and P=4 6-20% faster, P=8 5-10% in eager loops).  Between the
-        // two (P=8 at 16-20 MiB, P=16 at 8 MiB in one run) they were up to 8%
+        // faster than non-temporal global stores (in-process A/B): every P >= 2
+        // up to kBufferStoreAllReduceBytes per rank (graph-replay times at 1-8
+        // MiB: P=2 and P=4 6-20% faster, P=8 5-10% in eager loops).  Beyond
+        // that (P=8 at 16-20 MiB, P=16 at 8 MiB in one run) they were up to 8%
         // slower.
         const uint64_t t0 = uint64_t(blockIdx.x) * (BLOCK * U);
         const uint64_t left = a.count - t0;
         const uint32_t tb = uint32_t((left < uint64_t(BLOCK * U) ? left : uint64_t(BLOCK * U)) * 16);
 #pragma unroll
-        for (int q = 0; q < PMAX; q++) {
-            if (q < nr) {
-                const rsrc_t out = make_rsrc(static_cast<char*>(a.dst[q]) + t0 * 16, tb);
+        for (int q = 0; q < P; q++) {
+            const rsrc_t out = make_rsrc(static_cast<char*>(a.dst[q]) + t0 * 16, tb);
 #pragma unroll
-                for (int u = 0; u < U; u++) bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * BLOCK) * 16, y[u]);
-            }
+            for (int u = 0; u < U; u++) bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * BLOCK) * 16, y[u]);
         }
     } else {
 #pragma unroll
-        for (int q = 0; q < PMAX; q++) {
-            if (q < nr) {
+        for (int q = 0; q < P; q++) {
 #pragma unroll
-                for (int u = 0; u < U; u++) {
-                    const uint64_t v = base + uint64_t(u) * BLOCK;
-                    if (v < a.count) store16(static_cast<char*>(a.dst[q]) + v * 16, y[u]);
-                }
+            for (int u = 0; u < U; u++) {
+                const uint64_t v = base + uint64_t(u) * BLOCK;
+                if (v < a.count) store16(static_cast<char*>(a.dst[q]) + v * 16, y[u]);
             }
         }
     }
@@ -82,7 +82,10 @@ __global__ __launch_bounds__(BLOCK) void k_reduce_vec(ReduceArgs a) {
 
 // --------------------------------------------------------- ReduceScatter --
 // grid.x covers a.count vectors of one chunk in tiles of BLOCK*U; grid.y =
-// output chunk.  Buffer instructions: one resource per rank for the tile's
+// output chunk.  Chunk c starts c * a.count vectors into every input; the
+// last chunk holds a.last_count vectors (the two-shot AllReduce cuts its
+// chunks in whole tiles, so the last one may be shorter), and its tiles past
+// that end return at once.  Buffer instructions: one resource per rank for the tile's
 // range (the same lane offsets serve all P ranks), non-temporal loads and
 // device-scope stores; the resource range cuts off the last tile.  Measured
 // against the same kernel with 64-bit global addressing: 2-3% faster for
@@ -91,28 +94,27 @@ __global__ __launch_bounds__(BLOCK) void k_reduce_vec(ReduceArgs a) {
 // every P.  In-process A/B: 2.5% faster than 512 threads x 1 vector at P=8
 // bf16 and no slower at any of 13 placements of the inputs tried; 5-7%
 // faster than 256 threads x 4 vectors at P=4 and no slower at P=2.
-template <int DT, int OP, int PMAX, bool EXACT, int BLOCK, int U>
+template <int DT, int OP, int P, int BLOCK, int U>
 __global__ __launch_bounds__(BLOCK) void k_reduce_scatter_vec(ReduceArgs a) {
     constexpr uint64_t kTileVecs = uint64_t(BLOCK) * U;
     const uint64_t chunk = blockIdx.y;
+    const uint64_t cnt = chunk + 1 == gridDim.y ? a.last_count : a.count;
     const uint64_t t0 = uint64_t(blockIdx.x) * kTileVecs;       // < a.count by the grid
-    const uint64_t left = a.count - t0;
+    if (t0 >= cnt) return;                                      // past the end of a shorter last chunk
+    const uint64_t left = cnt - t0;
     const uint32_t bytes = uint32_t((left < kTileVecs ? left : kTileVecs) * 16);
     const uint64_t in_off = (chunk * a.count + t0) * 16;       // bytes into every rank's input
     const uint32_t lane = threadIdx.x * 16;
-    const int nr = EXACT ? PMAX : a.nranks;
-    u32x4 x[U][PMAX];
+    u32x4 x[U][P];
 #pragma unroll
-    for (int r = 0; r < PMAX; r++) {
-        if (r < nr) {
-            const rsrc_t in = make_rsrc(static_cast<const char*>(a.src[r]) + in_off, bytes);
+    for (int r = 0; r < P; r++) {
+        const rsrc_t in = make_rsrc(static_cast<const char*>(a.src[r]) + in_off, bytes);
 #pragma unroll
-            for (int u = 0; u < U; u++) x[u][r] = bload16<kPolNT>(in, lane + u * (BLOCK * 16));
-        }
+        for (int u = 0; u < U; u++) x[u][r] = bload16<kPolNT>(in, lane + u * (BLOCK * 16));
     }
     const rsrc_t out = make_rsrc(static_cast<char*>(a.dst[chunk]) + t0 * 16, bytes);
 #pragma unroll
-    for (int u = 0; u < U; u++) bstore16<kPolDevice>(out, lane + u * (BLOCK * 16), fold_vec<DT, OP, PMAX>(x[u], nr));
+    for (int u = 0; u < U; u++) bstore16<kPolDevice>(out, lane + u * (BLOCK * 16), fold_vec<DT, OP, P>(x[u], P));
 }
 
 // Element-wise path for ragged tails and unaligned buffers.  Elements
@@ -176,36 +178,37 @@ __device__ __forceinline__ bool piece_aligned(const CoalescedArgs& a, int k) {
 
 // One launch reduces every piece of its table in place: piece k's rank r
 // part starts at a.ptr[k*P + r].  grid.x = tiles over all pieces.
-template <typename Args, int DT, int OP, int PMAX, bool EXACT>
+template <typename Args, int DT, int OP, int P>
 __global__ __launch_bounds__(kBlock) void k_reduce_pieces(Args a) {
     constexpr int V = Elems<DT>::value;
     const uint32_t b = blockIdx.x;
     const int k = find_piece(a, b);
-    const int nr = EXACT ? PMAX : a.nranks;
+    constexpr int nr = P;
     void* const* ptr = a.ptr + k * nr;
     const uint64_t len = a.len[k];
     const uint64_t e0 = uint64_t(b - a.tile_start[k]) * kPieceTileVecs * V;
     const uint64_t e1 = min(len, e0 + kPieceTileVecs * V);
     if (piece_aligned(a, k)) {
         constexpr int U = int(kPieceTileVecs / kBlock);
-        const uint64_t v0 = e0 / V, v1 = e1 / V;
-        u32x4 x[U][PMAX];
+        const uint64_t v0 = e0 / V, v1 = e1 / V;  // e0 is a whole number of vectors
+        if (v1 > v0) {  // the tile holds whole vectors (not only a ragged end)
+            // branch-free loads, as in k_reduce_vec: a lane past the tile's last
+            // vector re-reads it (not stored)
+            u32x4 x[U][P];
 #pragma unroll
-        for (int r = 0; r < PMAX; r++) {
-            if (r < nr) {
+            for (int r = 0; r < P; r++) {
+                const char* src = static_cast<const char*>(ptr[r]);
 #pragma unroll
                 for (int u = 0; u < U; u++) {
                     const uint64_t v = v0 + threadIdx.x + uint64_t(u) * kBlock;
-                    if (v < v1) x[u][r] = load16(static_cast<const char*>(ptr[r]) + v * 16);
+                    x[u][r] = load16(src + (v < v1 ? v : v1 - 1) * 16);
                 }
             }
-        }
-        u32x4 y[U];
+            u32x4 y[U];
 #pragma unroll
-        for (int u = 0; u < U; u++) y[u] = fold_vec<DT, OP, PMAX>(x[u], nr);
+            for (int u = 0; u < U; u++) y[u] = fold_vec<DT, OP, P>(x[u], P);
 #pragma unroll
-        for (int q = 0; q < PMAX; q++) {
-            if (q < nr) {
+            for (int q = 0; q < P; q++) {
 #pragma unroll
                 for (int u = 0; u < U; u++) {
                     const uint64_t v = v0 + threadIdx.x + uint64_t(u) * kBlock;
@@ -246,13 +249,13 @@ __global__ __launch_bounds__(kBlock) void k_reduce_pieces(Args a) {
 // threads x 4 vectors (in-process A/B), where 256 threads with 2 or 1
 // vectors had been 0.5-1.3% slower.
 constexpr int kSegBlock = 64;
-template <int DT, int OP, int PMAX, bool EXACT, int U>
+template <int DT, int OP, int P, int U>
 __global__ __launch_bounds__(kSegBlock) void k_reduce_scatter_segs(SegReduceScatterArgs a) {
     constexpr int V = Elems<DT>::value;
     const uint32_t b = blockIdx.x;
     int k = 0;
     while (k + 1 < a.nsegs && a.tile_start[k + 1] <= b) k++;
-    const int nr = EXACT ? PMAX : a.nranks;
+    constexpr int nr = P;
     const uint32_t t = b - a.tile_start[k];
     const uint32_t j = t / a.tiles_per_chunk[k];   // output chunk = member
     const uint32_t tt = t - j * a.tiles_per_chunk[k];
@@ -267,18 +270,16 @@ __global__ __launch_bounds__(kSegBlock) void k_reduce_scatter_segs(SegReduceScat
         const uint32_t bytes = uint32_t((left < kTileVecs ? left : kTileVecs) * 16);
         const uint64_t in_off = (uint64_t(j) * mv + t0) * 16;
         const uint32_t lane = threadIdx.x * 16;
-        u32x4 x[U][PMAX];
+        u32x4 x[U][P];
 #pragma unroll
-        for (int r = 0; r < PMAX; r++) {
-            if (r < nr) {
-                const rsrc_t in = make_rsrc(static_cast<const char*>(src[r]) + in_off, bytes);
+        for (int r = 0; r < P; r++) {
+            const rsrc_t in = make_rsrc(static_cast<const char*>(src[r]) + in_off, bytes);
 #pragma unroll
-                for (int u = 0; u < U; u++) x[u][r] = bload16<kPolNT>(in, lane + u * (kSegBlock * 16));
-            }
+            for (int u = 0; u < U; u++) x[u][r] = bload16<kPolNT>(in, lane + u * (kSegBlock * 16));
         }
         const rsrc_t out = make_rsrc(static_cast<char*>(dst) + t0 * 16, bytes);
 #pragma unroll
-        for (int u = 0; u < U; u++) bstore16<kPolDevice>(out, lane + u * (kSegBlock * 16), fold_vec<DT, OP, PMAX>(x[u], nr));
+        for (int u = 0; u < U; u++) bstore16<kPolDevice>(out, lane + u * (kSegBlock * 16), fold_vec<DT, OP, P>(x[u], P));
     } else {
         const uint64_t per_tile = uint64_t(kSegBlock) * U * V;
         const uint64_t e0 = uint64_t(tt) * per_tile;
@@ -316,14 +317,30 @@ __global__ __launch_bounds__(kBlock) void k_copy_pieces(Args a, int esize, int t
 // ---------------------------------------------------------- dispatchers --
 namespace {
 
-int pmax_of(int nranks) {
-    return nranks <= 1 ? 1 : nranks <= 2 ? 2 : nranks <= 4 ? 4 : nranks <= 8 ? 8 : 16;
+// Calls fn(std::integral_constant<int, P>{}) for the run-time rank count
+// 1 <= nranks <= 16: every fold kernel is instantiated for each P.
+template <typename Fn>
+hipError_t with_ranks(int nranks, Fn&& fn) {
+    switch (nranks) {
+        case 1: return fn(std::integral_constant<int, 1>{});
+        case 2: return fn(std::integral_constant<int, 2>{});
+        case 3: return fn(std::integral_constant<int, 3>{});
+        case 4: return fn(std::integral_constant<int, 4>{});
+        case 5: return fn(std::integral_constant<int, 5>{});
+        case 6: return fn(std::integral_constant<int, 6>{});
+        case 7: return fn(std::integral_constant<int, 7>{});
+        case 8: return fn(std::integral_constant<int, 8>{});
+        case 9: return fn(std::integral_constant<int, 9>{});
+        case 10: return fn(std::integral_constant<int, 10>{});
+        case 11: return fn(std::integral_constant<int, 11>{});
+        case 12: return fn(std::integral_constant<int, 12>{});
+        case 13: return fn(std::integral_constant<int, 13>{});
+        case 14: return fn(std::integral_constant<int, 14>{});
+        case 15: return fn(std::integral_constant<int, 15>{});
+        case 16: return fn(std::integral_constant<int, 16>{});
+        default: return hipErrorInvalidValue;
+    }
 }
-
-// One-shot AllReduce with P >= 8 in one-wave tiles beyond this many bytes per
-// rank (above the two-shot window): in-process A/B 3-5% faster at 512 MiB
-// and 1 GiB per rank (P=8 bf16, P=16 fp32), but 2-12% slower at 4-64 MiB.
-constexpr uint64_t kWaveAllReduceBytes = 256ull << 20;
 
 // One-shot AllReduce with P >= 2 up to this many bytes per rank: buffer stores
 // (for P > 8 only below it: P=16 at exactly 8 MiB measured up to 8% slower).
@@ -332,60 +349,40 @@ constexpr uint64_t kBufferStoreAllReduceBytes = 8ull << 20;
 // Vectors per thread of the one-shot AllReduce in kBlock-thread tiles,
 // measured on the MI355X for 25-256 MiB per rank: two, four for the plain
 // copy of P = 1.
-template <int PMAX>
-constexpr int ar_unroll() { return PMAX == 1 ? 4 : 2; }
+template <int P>
+constexpr int ar_unroll() { return P == 1 ? 4 : 2; }
 
-// True when the launch uses one-wave tiles (kWaveBlock vectors per workgroup).
-template <int PMAX>
-bool wave_tiles(const ReduceArgs& a) {
-    return a.rs || (PMAX >= 8 && a.count * 16 > kWaveAllReduceBytes);
-}
-
-template <int DT, int OP, int PMAX, bool EXACT>
+template <int DT, int OP, int P>
 void reduce_vec_launch(const ReduceArgs& a, uint64_t blocks, hipStream_t s) {
     if (a.rs) {
-        const dim3 grid(unsigned(blocks), unsigned(a.nranks));
-        k_reduce_scatter_vec<DT, OP, PMAX, EXACT, kWaveBlock, 1><<<grid, kWaveBlock, 0, s>>>(a);
+        const dim3 grid{unsigned(blocks), unsigned(P), 1u};
+        k_reduce_scatter_vec<DT, OP, P, kWaveBlock, 1><<<grid, kWaveBlock, 0, s>>>(a);
         return;
     }
-    if constexpr (PMAX >= 8) {
-        if (wave_tiles<PMAX>(a)) {
-            k_reduce_vec<DT, OP, PMAX, EXACT, 1, kWaveBlock><<<unsigned(blocks), kWaveBlock, 0, s>>>(a);
-            return;
-        }
-    }
-    if constexpr (PMAX >= 2) {
+    if constexpr (P >= 2) {
         const uint64_t bytes = a.count * 16;
-        if (PMAX >= 16 ? bytes < kBufferStoreAllReduceBytes : bytes <= kBufferStoreAllReduceBytes) {
-            k_reduce_vec<DT, OP, PMAX, EXACT, ar_unroll<PMAX>(), kBlock, true><<<unsigned(blocks), kBlock, 0, s>>>(a);
+        if (P > 8 ? bytes < kBufferStoreAllReduceBytes : bytes <= kBufferStoreAllReduceBytes) {
+            k_reduce_vec<DT, OP, P, ar_unroll<P>(), kBlock, true><<<unsigned(blocks), kBlock, 0, s>>>(a);
             return;
         }
     }
-    k_reduce_vec<DT, OP, PMAX, EXACT, ar_unroll<PMAX>(), kBlock><<<unsigned(blocks), kBlock, 0, s>>>(a);
+    k_reduce_vec<DT, OP, P, ar_unroll<P>(), kBlock><<<unsigned(blocks), kBlock, 0, s>>>(a);
 }
 
-template <int DT, int OP, int PMAX>
+template <int DT, int OP, int P>
 hipError_t reduce_vec_p(const ReduceArgs& a, hipStream_t s) {
-    const uint64_t per_block = wave_tiles<PMAX>(a) ? uint64_t(kWaveBlock) : uint64_t(kBlock) * ar_unroll<PMAX>();
+    // the ReduceScatter runs one-wave tiles; the one-shot AllReduce kBlock threads x ar_unroll vectors
+    const uint64_t per_block = a.rs ? uint64_t(kWaveBlock) : uint64_t(kBlock) * ar_unroll<P>();
     const uint64_t blocks = (a.count + per_block - 1) / per_block;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    if (a.nranks == PMAX)
-        reduce_vec_launch<DT, OP, PMAX, true>(a, blocks, s);
-    else
-        reduce_vec_launch<DT, OP, PMAX, false>(a, blocks, s);
+    reduce_vec_launch<DT, OP, P>(a, blocks, s);
     return hipGetLastError();
 }
 
 template <int DT, int OP>
 hipError_t reduce_vec_op(const ReduceArgs& a, hipStream_t s) {
-    switch (pmax_of(a.nranks)) {
-        case 1: return reduce_vec_p<DT, OP, 1>(a, s);
-        case 2: return reduce_vec_p<DT, OP, 2>(a, s);
-        case 4: return reduce_vec_p<DT, OP, 4>(a, s);
-        case 8: return reduce_vec_p<DT, OP, 8>(a, s);
-        default: return reduce_vec_p<DT, OP, 16>(a, s);
-    }
+    return with_ranks(a.nranks, [&](auto p) { return reduce_vec_p<DT, OP, decltype(p)::value>(a, s); });
 }
 
 template <int DT>
@@ -418,26 +415,17 @@ hipError_t reduce_elems_dt(const ReduceArgs& a, int op, hipStream_t s) {
     }
 }
 
-template <typename Args, int DT, int OP, int PMAX>
+template <typename Args, int DT, int OP, int P>
 hipError_t reduce_pieces_p(const Args& a, hipStream_t s) {
     const uint32_t tiles = a.tile_start[a.npieces];
     if (tiles == 0) return hipSuccess;
-    if (a.nranks == PMAX)
-        k_reduce_pieces<Args, DT, OP, PMAX, true><<<tiles, kBlock, 0, s>>>(a);
-    else
-        k_reduce_pieces<Args, DT, OP, PMAX, false><<<tiles, kBlock, 0, s>>>(a);
+    k_reduce_pieces<Args, DT, OP, P><<<tiles, kBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 
 template <typename Args, int DT, int OP>
 hipError_t reduce_pieces_op(const Args& a, hipStream_t s) {
-    switch (pmax_of(a.nranks)) {
-        case 1: return reduce_pieces_p<Args, DT, OP, 1>(a, s);
-        case 2: return reduce_pieces_p<Args, DT, OP, 2>(a, s);
-        case 4: return reduce_pieces_p<Args, DT, OP, 4>(a, s);
-        case 8: return reduce_pieces_p<Args, DT, OP, 8>(a, s);
-        default: return reduce_pieces_p<Args, DT, OP, 16>(a, s);
-    }
+    return with_ranks(a.nranks, [&](auto p) { return reduce_pieces_p<Args, DT, OP, decltype(p)::value>(a, s); });
 }
 
 template <typename Args, int DT>
@@ -468,27 +456,18 @@ hipError_t copy_pieces_any(const Args& a, int esize, int to_ws, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int DT, int OP, int PMAX>
+template <int DT, int OP, int P>
 hipError_t reduce_scatter_segs_p(const SegReduceScatterArgs& a, hipStream_t s) {
     constexpr int U = 1;
     const uint32_t tiles = a.tile_start[a.nsegs];
     if (tiles == 0) return hipSuccess;
-    if (a.nranks == PMAX)
-        k_reduce_scatter_segs<DT, OP, PMAX, true, U><<<tiles, kSegBlock, 0, s>>>(a);
-    else
-        k_reduce_scatter_segs<DT, OP, PMAX, false, U><<<tiles, kSegBlock, 0, s>>>(a);
+    k_reduce_scatter_segs<DT, OP, P, U><<<tiles, kSegBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 
 template <int DT, int OP>
 hipError_t reduce_scatter_segs_op(const SegReduceScatterArgs& a, hipStream_t s) {
-    switch (pmax_of(a.nranks)) {
-        case 1: return reduce_scatter_segs_p<DT, OP, 1>(a, s);
-        case 2: return reduce_scatter_segs_p<DT, OP, 2>(a, s);
-        case 4: return reduce_scatter_segs_p<DT, OP, 4>(a, s);
-        case 8: return reduce_scatter_segs_p<DT, OP, 8>(a, s);
-        default: return reduce_scatter_segs_p<DT, OP, 16>(a, s);
-    }
+    return with_ranks(a.nranks, [&](auto p) { return reduce_scatter_segs_p<DT, OP, decltype(p)::value>(a, s); });
 }
 
 template <int DT>

@@ -69,15 +69,16 @@ typedef enum {
  * rank and hands the result to all).  Usually one launch: each element is
  * read once per rank and written once per rank (the one-shot form of the
  * c10d page, sec. 9.4).  From 16 MiB per rank up for P >= 16, from 24 to
- * 256 MiB for 8 <= P < 16 and from 128 to 192 MiB for P = 4, with count a
- * multiple of P * (16 bytes / element size) and 16-byte aligned buffers, it
- * runs as a ReduceScatter into chunk r of recv[r] followed by an in-place
- * AllGather of the chunks, which is faster there.  Beyond 256 MiB per rank
- * for P >= 8 and beyond 192 MiB for P = 4 it runs window by window (64 MiB
- * per rank at P >= 16, 128 MiB otherwise), each window an AllReduce of its
- * own in the two-shot form, so the window's chunks are still in the
- * Infinity Cache when they fan out.  All forms fold in the same order and
- * give identical bits.  In place is allowed (send[r] ==
+ * 256 MiB for 8 <= P < 16, from 32 to 256 MiB for 5 <= P <= 7 and from 128
+ * to 192 MiB for P = 4, with count a
+ * whole number of 16-byte vectors and 16-byte aligned buffers, it runs as a
+ * ReduceScatter into chunk r of recv[r] (chunks of whole 1 KiB tiles, the
+ * last one shorter) followed by an in-place AllGather of the chunks, which
+ * is faster there.  Beyond 256 MiB per rank for P >= 5 it runs window by
+ * window (64 MiB per rank at P >= 16, 128 MiB at P = 5-15), each window an
+ * AllReduce of its own in the two-shot form, so the window's chunks are
+ * still in the Infinity Cache when they fan out.  All forms fold in the
+ * same order and give identical bits.  In place is allowed (send[r] ==
  * recv[r]); any other overlap of a recv buffer with a send or recv buffer
  * is refused (DT_ERR_ARG).  send[r] and recv[r] hold `count` elements. */
 dt_status dt_allreduce(const void* const* send, void* const* recv, int nranks, size_t count,

@@ -161,11 +161,25 @@ hipError_t launch_reduce_vec(const ReduceArgs& a, int, int, hipStream_t) {
     if (a.rs) g_rs_launches++;
     CHECK(a.nranks >= 1 && a.nranks <= kMaxRanksHost, "reduce_vec nranks %d", a.nranks);
     const uint64_t bytes = a.count * 16;
-    log_fold(a.dst[0], bytes);
+    if (!a.rs) {
+        log_fold(a.dst[0], bytes);
+        for (int r = 0; r < a.nranks; r++) {
+            CHECK(al16(a.src[r]) && al16(a.dst[r]), "reduce_vec buffers not 16-byte aligned");
+            touch(a.src[r], 0, bytes, false, "reduce_vec read");
+            touch(a.dst[r], 0, bytes, true, "reduce_vec write");
+        }
+        return hipSuccess;
+    }
+    // ReduceScatter: chunk c starts c * count vectors into every input and holds
+    // count vectors, the last chunk last_count (the kernel's early exit)
+    CHECK(a.last_count >= 1 && a.last_count <= a.count, "reduce_scatter: last chunk %llu of %llu vectors",
+          (unsigned long long)a.last_count, (unsigned long long)a.count);
+    const uint64_t last = a.last_count * 16;
+    log_fold(a.dst[0], a.nranks == 1 ? last : bytes);
     for (int r = 0; r < a.nranks; r++) {
         CHECK(al16(a.src[r]) && al16(a.dst[r]), "reduce_vec buffers not 16-byte aligned");
-        touch(a.src[r], 0, a.rs ? bytes * a.nranks : bytes, false, "reduce_vec read");
-        touch(a.dst[r], 0, bytes, true, "reduce_vec write");
+        touch(a.src[r], 0, bytes * (a.nranks - 1) + last, false, "reduce_scatter read");
+        touch(a.dst[r], 0, r + 1 == a.nranks ? last : bytes, true, "reduce_scatter write");
     }
     return hipSuccess;
 }
@@ -872,8 +886,8 @@ void big_fan_out() {
 }
 
 // The two-shot AllReduce (P >= 16 from 16 MiB per rank, P = 8-15 at 24-256
-// MiB, P = 4 at 128-192 MiB) and, beyond that (P >= 16 above 256 MiB in 64
-// MiB windows, P = 8-15 above 256 MiB and P = 4 above 192 MiB in 128 MiB
+// MiB, P = 5-7 at 32-256 MiB, P = 4 at 128-192 MiB) and, beyond that (P >=
+// 16 above 256 MiB in 64 MiB windows, P = 5-15 above 256 MiB in 128 MiB
 // windows), window by window: fake device ranges.  For every case, rank 0's
 // output is written exactly once (ReduceScatter chunk 0, fan-outs of the
 // other chunks, one-shot tails), each fan-out piece copies a range of rank
@@ -910,14 +924,18 @@ void two_shot() {
         {12, DT_INT32, 48 * M, false, 1},             // 192 MiB
         {12, DT_INT32, 72 * M, false, 3},             // 288 MiB at P=12: windows of whole vectors per chunk
         {12, DT_BFLOAT16, 200 * M + 96, false, 3},    // 400 MiB + 192 B at P=12: three windows, a one-shot tail
-        {8, DT_BFLOAT16, 64 * M + 8, false, 0},       // not a multiple of P vectors
+        {8, DT_BFLOAT16, 64 * M + 8, false, 1},       // not a multiple of P vectors: a shorter last chunk
+        {12, DT_FLOAT32, 48 * M + 4, false, 1},       // 192 MiB + 16 B at P=12: chunks of whole 1 KiB tiles
+        {8, DT_BFLOAT16, 64 * M + 4, false, 0},       // not a whole number of vectors: one-shot
         {4, DT_FLOAT32, 32 * M, false, 1},            // 128 MiB at P=4
         {4, DT_FLOAT32, 48 * M, true, 1},             // 192 MiB at P=4
         {4, DT_FLOAT32, 16 * M, false, 0},            // 64 MiB at P=4
-        {4, DT_FLOAT32, 48 * M + 16, false, 1},       // beyond 192 MiB at P=4: 128 MiB window + a 64 MiB one-shot window
-        {4, DT_FLOAT32, 64 * M, false, 2},            // 256 MiB at P=4: two 128 MiB windows
+        {4, DT_FLOAT32, 48 * M + 16, false, 0},       // just beyond 192 MiB at P=4: one-shot
+        {4, DT_FLOAT32, 64 * M, false, 0},            // 256 MiB at P=4: one-shot, no windows
         {2, DT_FLOAT32, 32 * M, false, 0},            // P=2
-        {6, DT_FLOAT32, 48 * M, false, 0},            // P=6
+        {6, DT_FLOAT32, 48 * M, false, 1},            // 192 MiB at P=6: two-shot
+        {6, DT_FLOAT32, 4 * M, false, 0},             // 16 MiB at P=6: one-shot
+        {7, DT_FLOAT32, 96 * M + 4, false, 3},        // 384 MiB + 16 B at P=7: three 128 MiB windows, a one-shot tail
     };
     char* base = reinterpret_cast<char*>(uintptr_t(1) << 45);  // fake, never dereferenced
     for (const Case& c : cases) {
