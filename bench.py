@@ -261,7 +261,8 @@ def alpha_beta_fit(sizes, us, p: int) -> dict:
       B_hbm: from the points whose footprint 2*P*S exceeds 512 MiB (twice the
         Infinity Cache), T - alpha weighted 1/T^2;
       B_cache: the same over the points whose footprint fits the Infinity
-        Cache and whose time is not latency (256 KiB .. footprint <= 256 MB).
+        Cache and whose time is at least 2 * alpha (below that, T - alpha is
+        mostly noise).
     Each B is a weighted mean of per-point rates, so it lies within them."""
     s = [float(x) for x in sizes]
     t = [float(x) * 1e-6 for x in us]
@@ -269,7 +270,7 @@ def alpha_beta_fit(sizes, us, p: int) -> dict:
     alpha = statistics.mean(lat) if lat else 0.0
 
     def band(sel):
-        pts = [(2 * p * si, ti) for si, ti in zip(s, t) if sel(si)]
+        pts = [(2 * p * si, ti) for si, ti in zip(s, t) if sel(si, ti)]
         if not pts:
             return None
         num = sum(x * x / (ti * ti) for x, ti in pts)
@@ -278,10 +279,11 @@ def alpha_beta_fit(sizes, us, p: int) -> dict:
                 "best_point_GBps": round(max(x / ti for x, ti in pts) / 1e9, 1)}
 
     return {"alpha_us": round(alpha * 1e6, 3),
-            "hbm": band(lambda si: 2 * p * si > 512 * 2 ** 20),
-            "cache": band(lambda si: si >= 256 * 1024 and 2 * p * si <= MALL_BYTES),
+            "hbm": band(lambda si, ti: 2 * p * si > 512 * 2 ** 20),
+            "cache": band(lambda si, ti: 2 * p * si <= MALL_BYTES and si > 64 * 1024 and ti >= 2 * alpha),
             "model": "T(S) = alpha + 2*P*S/B, P=16, graph-replay times; alpha from S <= 64 KiB, B per regime "
-                     "(weights 1/T^2): hbm = footprint > 512 MiB, cache = footprint within the 256 MB Infinity Cache"}
+                     "(weights 1/T^2): hbm = footprint > 512 MiB, cache = footprint within the 256 MB Infinity Cache "
+                     "and T >= 2 alpha"}
 
 
 def hsdp(dt, torch):
@@ -419,6 +421,25 @@ def configs(dt, torch, steps: int, warmup: int) -> dict:
     ys = [torch.empty(int(s_rows[:, j].sum()) * w, device="cuda") for j in range(P)]
     measure("c3_all_to_all_p8", lambda: dt.dt_all_to_all(xs, ys, (s_rows * w).tolist()),
             2 * int(s_rows.sum()) * w * 4, per_graph=4)
+    del xs, ys
+    torch.cuda.empty_cache()
+
+    # misaligned buffers: the step's AllReduce on views 2 bytes past 16-byte
+    # alignment (every buffer off by the same amount), and the uneven
+    # AllGather in bf16 with odd counts (every later piece lands 2 bytes off)
+    n = SHAPE[0] * SHAPE[1]
+    base = [torch.randn(n + 8, device="cuda").to(torch.bfloat16) for _ in range(P)]
+    outb = [torch.empty(n + 8, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    xs, ys = [b[1:1 + n] for b in base], [b[1:1 + n] for b in outb]
+    measure("c2_allreduce_misaligned_p8_bf16", lambda: dt.dt_allreduce(xs, ys), 2 * P * n * 2, per_graph=4)
+    out["c2_allreduce_misaligned_p8_bf16"]["note"] = "every buffer 2 bytes past 16-byte alignment"
+    del base, outb, xs, ys
+    rows_odd = [int(c) * w + 2 * k + 1 for k, c in enumerate(counts)]
+    xs = [torch.randn(c, device="cuda").to(torch.bfloat16) for c in rows_odd]
+    ys = [torch.empty(sum(rows_odd), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    measure("c3_uneven_all_gather_odd_bf16", lambda: dt.dt_all_gather(xs, ys), (1 + P) * sum(rows_odd) * 2,
+            per_graph=4)
+    out["c3_uneven_all_gather_odd_bf16"]["note"] = "bf16, odd counts: every piece after the first 2 bytes off"
     del xs, ys
     torch.cuda.empty_cache()
 

@@ -210,7 +210,7 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
     const uint64_t nv = count / v;
     const uint64_t per = (nv + nranks - 1) / nranks;                      // vectors per chunk, rounded up
     const uint64_t mc = (per + kChunkVecs - 1) / kChunkVecs * kChunkVecs;  // ... to whole tiles
-    if (vec && count % v == 0 && mc * uint64_t(nranks - 1) < nv && two_shot_pays(nranks, uint64_t(count) * es)) {
+    if (vec && mc * uint64_t(nranks - 1) < nv && two_shot_pays(nranks, uint64_t(count) * es)) {
         const uint64_t last = nv - mc * uint64_t(nranks - 1);  // 0 < last <= mc
         const uint64_t cb = mc * 16;                           // chunk stride in bytes
         dt::ReduceArgs rs = a;
@@ -227,10 +227,15 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
         rs.first = 0;
         rs.count = mc;
         rs.last_count = last;
+        rs.chunk_stride = mc;
         rs.chunk_elems = size_t(mc * v);
         dt_status st = check_hip(dt::launch_reduce_vec(rs, dtype, op, stream), "allreduce (reduce_scatter) launch");
         if (st != DT_OK) return st;
-        return fan_out(own, counts, table, nranks, es, stream, "allreduce (all_gather) launch");
+        if ((st = fan_out(own, counts, table, nranks, es, stream, "allreduce (all_gather) launch")) != DT_OK) return st;
+        if (nv * v == count) return DT_OK;
+        a.first = size_t(nv * v);  // the ragged end, fewer than one vector per rank: element path
+        a.count = count - a.first;
+        return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "allreduce (element path) launch");
     }
     size_t body = 0;
     if (vec) {
@@ -250,11 +255,55 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
     return DT_OK;
 }
 
+// Bytes to peel off the front of every send and recv buffer so that the
+// fold kernels' tiles start on a 128-byte line: every buffer shares one
+// offset within a line, and `stride` (the bytes between the starts of the
+// ranges one launch folds, e.g. ReduceScatter chunks; 0 for none) keeps it.
+// Failing that, the bytes up to the next 16-byte boundary when every buffer
+// shares its offset within a vector.  0 when none of these applies or the
+// buffers are line-aligned already.
+size_t peel_bytes(const void* const* send, void* const* recv, int nranks, size_t stride) {
+    const uintptr_t line = reinterpret_cast<uintptr_t>(send[0]) & 127;
+    bool same_line = stride % 128 == 0, same_vec = stride % 16 == 0;
+    for (int r = 0; r < nranks; r++) {
+        const uintptr_t s = reinterpret_cast<uintptr_t>(send[r]), d = reinterpret_cast<uintptr_t>(recv[r]);
+        same_line = same_line && (s & 127) == line && (d & 127) == line;
+        same_vec = same_vec && (s & 15) == (line & 15) && (d & 15) == (line & 15);
+    }
+    if (same_line) return line ? 128 - line : 0;
+    if (same_vec && (line & 15) != 0) return 16 - (line & 15);
+    return 0;
+}
+
 // Validated AllReduce over one contiguous range per rank: window by window
-// where allreduce_window says so, else in one call.
+// where allreduce_window says so, else in one call.  When every buffer sits
+// at the same offset within a cache line (or a vector), the elements up to
+// the next boundary go to the element path and the rest, now aligned, the
+// usual way.
 dt_status allreduce_impl(const void* const* send, void* const* recv, int nranks, size_t count, dt_dtype dtype,
                          dt_op op, hipStream_t stream) {
     const size_t es = esize_of(dtype);
+    const size_t peel = peel_bytes(send, recv, nranks, 0);
+    if (peel != 0) {
+        const size_t h = peel / es;  // a whole number of elements for element-aligned buffers
+        if (count > h && peel % es == 0) {
+            dt::ReduceArgs a = {};
+            const void* s[dt::kMaxRanksHost];
+            void* d[dt::kMaxRanksHost];
+            for (int r = 0; r < nranks; r++) {
+                a.src[r] = send[r];
+                a.dst[r] = recv[r];
+                s[r] = cptr(send[r]) + h * es;
+                d[r] = static_cast<char*>(recv[r]) + h * es;
+            }
+            a.nranks = nranks;
+            a.first = 0;
+            a.count = h;
+            dt_status st = check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "allreduce (head) launch");
+            if (st != DT_OK) return st;
+            return allreduce_impl(s, d, nranks, count - h, dtype, op, stream);
+        }
+    }
     const uint64_t win = allreduce_window(nranks, uint64_t(count) * es);
     if (win == 0) return allreduce_one(send, recv, nranks, count, dtype, op, stream);
     const size_t win_elems = size_t(win / es);  // whole vectors: every window keeps each buffer's alignment
@@ -327,13 +376,23 @@ dt_status fan_out_launch(const void* const* src, const uint64_t* bytes, void* co
         a.bytes[k] = bytes[k];
         a.tile_start[k] = uint32_t(tiles);
         bool al = aligned16(src[k]);
+        bool same = true;  // every destination at the same offset within a 128-byte line
+        const uintptr_t md = bytes[k] ? reinterpret_cast<uintptr_t>(dst[k][0]) & (dt::kGridAlign - 1) : 0;
         for (int q = 0; q < nranks; q++) {
             void* d = bytes[k] ? dst[k][q] : nullptr;
             a.dst[k * nranks + q] = d;
             al = al && aligned16(d);
+            same = same && (reinterpret_cast<uintptr_t>(d) & (dt::kGridAlign - 1)) == md;
         }
-        if (al) a.aligned |= 1u << k;
-        tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;
+        if (al) {
+            a.aligned |= 1u << k;
+            tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;
+        } else if (same) {
+            a.shifted |= 1u << k;
+            tiles += dt::grid_tiles(bytes[k], md, tile_bytes);
+        } else {
+            tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;
+        }
         if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "fan-out too large for one launch");
     }
     for (int k = n; k <= nranks; k++) a.tile_start[k] = uint32_t(tiles);
@@ -417,9 +476,14 @@ dt_status copy_segments(const std::vector<const void*>& src, const std::vector<v
         a.src[i] = src[k];
         a.dst[i] = dst[k];
         a.bytes[i] = bytes[k];
-        if (aligned16(src[k]) && aligned16(dst[k])) a.aligned |= 1ull << i;
         a.tile_start[i] = uint32_t(tiles);
-        tiles += (bytes[k] + dt::kSegCopyTileBytes - 1) / dt::kSegCopyTileBytes;
+        if (aligned16(src[k]) && aligned16(dst[k])) {
+            a.aligned |= 1ull << i;
+            tiles += (bytes[k] + dt::kSegCopyTileBytes - 1) / dt::kSegCopyTileBytes;
+        } else {  // tiles over the destination's aligned grid
+            tiles += dt::grid_tiles(bytes[k], reinterpret_cast<uintptr_t>(dst[k]) & (dt::kGridAlign - 1),
+                                    dt::kSegCopyTileBytes);
+        }
         if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "copy too large for one launch");
     }
     return flush();
@@ -609,8 +673,34 @@ dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nran
     a.chunk_elems = recvcount;
     if (vec) {
         a.first = 0;
-        a.count = a.last_count = recvcount / vec_elems(dtype);
+        a.count = a.last_count = a.chunk_stride = recvcount / vec_elems(dtype);
         return check_hip(dt::launch_reduce_vec(a, dtype, op, stream), "reduce_scatter launch");
+    }
+    // Every buffer and chunk start at the same offset within a line (or a
+    // vector): the first h elements of each chunk go to the element path, the
+    // aligned body of every chunk to the vector kernel, the ragged end back
+    // to the element path.
+    const size_t es = esize_of(dtype), v = vec_elems(dtype);
+    const size_t peel = peel_bytes(send, recv, nranks, recvcount * es);
+    const size_t h = peel / es;
+    if (peel != 0 && peel % es == 0 && recvcount >= h + v) {
+        a.first = 0;
+        a.count = h;
+        if ((st = check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "reduce_scatter (head) launch")) != DT_OK)
+            return st;
+        dt::ReduceArgs body = a;
+        for (int r = 0; r < nranks; r++) {
+            body.src[r] = cptr(send[r]) + h * es;
+            body.dst[r] = static_cast<char*>(recv[r]) + h * es;
+        }
+        body.count = body.last_count = (recvcount - h) / v;
+        body.chunk_stride = recvcount / v;
+        if ((st = check_hip(dt::launch_reduce_vec(body, dtype, op, stream), "reduce_scatter (body) launch")) != DT_OK)
+            return st;
+        a.first = h + body.count * v;
+        a.count = recvcount - a.first;
+        if (a.count == 0) return DT_OK;
+        return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "reduce_scatter (tail) launch");
     }
     a.first = 0;
     a.count = recvcount;
@@ -877,17 +967,23 @@ dt_status dt_all_to_all(const void* const* send, void* const* recv, int nranks, 
         for (int j = 0; j < nranks; j++) {
             const uint64_t bytes = uint64_t(splits[i * nranks + j]) * es;
             if (bytes > 0) {
-                const uint64_t t = (bytes + dt::kCopyTileBytes - 1) / dt::kCopyTileBytes;  // <= 2^30
+                const char* from = cptr(send[i]) + so;
+                char* to = static_cast<char*>(recv[j]) + recv_off[j];
+                const bool al = aligned16(from) && aligned16(to);
+                // an unaligned block's tiles cover its destination's aligned grid
+                const uint64_t t = al ? (bytes + dt::kCopyTileBytes - 1) / dt::kCopyTileBytes
+                                      : dt::grid_tiles(bytes, reinterpret_cast<uintptr_t>(to) & (dt::kGridAlign - 1),
+                                                       dt::kCopyTileBytes);
                 if (a.nblocks == dt::kA2ABlocks || tiles + t > 0x7FFFFFFFull) {
                     const dt_status st = flush();
                     if (st != DT_OK) return st;
                 }
                 const int k = a.nblocks++;
-                a.from[k] = cptr(send[i]) + so;
-                a.to[k] = static_cast<char*>(recv[j]) + recv_off[j];
+                a.from[k] = from;
+                a.to[k] = to;
                 a.bytes[k] = bytes;
                 a.tile_start[k] = uint32_t(tiles);
-                if (aligned16(a.from[k]) && aligned16(a.to[k])) a.aligned[k >> 6] |= 1ull << (k & 63);
+                if (al) a.aligned[k >> 6] |= 1ull << (k & 63);
                 tiles += t;
             }
             so += bytes;

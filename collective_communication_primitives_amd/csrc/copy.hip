@@ -65,6 +65,37 @@ __global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
             for (int q = 0; q < nr; q++)
                 if (dsts[q] != src) static_cast<char*>(dsts[q])[t] = c;
         }
+    } else if ((a.shifted >> r) & 1u) {
+        // The destinations share one offset md within a 128-byte line: tile b
+        // covers bytes [b0, b0 + kTile) of their line grid, grid byte g being
+        // byte g - md of the piece.  A grid vector inside the piece is one
+        // aligned store to every destination, its source bytes joined from
+        // aligned loads (the source's misalignment is the same for all of
+        // them); the partial vectors at the two ends go byte by byte.
+        const uint32_t md = uint32_t(reinterpret_cast<uintptr_t>(dsts[0]) & (kGridAlign - 1));
+        const uint32_t sm = uint32_t((reinterpret_cast<uintptr_t>(src) - md) & 15u);
+        const int64_t bytes = int64_t(a.bytes[r]);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t p0 = int64_t(b0) + int64_t(threadIdx.x + u * BLOCK) * 16 - int64_t(md);
+            if (p0 >= 0 && p0 + 16 <= bytes) {
+                // the aligned path's stores: buffer stores, non-temporal with
+                // device scope, addressed from the tile's grid start
+                const u32x4 x = load16_any<false>(src + p0, sm);
+                for (int q = 0; q < nr; q++) {
+                    if (dsts[q] == src) continue;
+                    const rsrc_t out = make_rsrc(static_cast<char*>(dsts[q]) - md + b0, uint32_t(kTile));
+                    bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * BLOCK) * 16, x);
+                }
+            } else if (p0 + 16 > 0 && p0 < bytes) {
+                const int64_t e = p0 + 16 < bytes ? p0 + 16 : bytes;
+                for (int64_t i = p0 > 0 ? p0 : 0; i < e; i++) {
+                    const char c = src[i];
+                    for (int q = 0; q < nr; q++)
+                        if (dsts[q] != src) static_cast<char*>(dsts[q])[i] = c;
+                }
+            }
+        }
     } else {
         for (uint64_t t = b0 + threadIdx.x; t < b1; t += BLOCK) {
             const char c = src[t];
@@ -74,9 +105,33 @@ __global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
     }
 }
 
+// A 1:1 copy of `bytes` bytes from src to dst (not 16-byte aligned), tile
+// `tile` of TILE bytes over dst's 128-byte line grid (grid_tiles), THREADS
+// lanes with TILE / 16 / THREADS vectors each: aligned stores, sources joined
+// from aligned loads, the partial vectors at the two ends byte by byte.
+template <int THREADS, uint64_t TILE>
+__device__ __forceinline__ void copy_shifted(const char* src, char* dst, uint64_t bytes, uint64_t tile) {
+    constexpr int U = int(TILE / 16 / THREADS);
+    const uint32_t md = uint32_t(reinterpret_cast<uintptr_t>(dst) & (kGridAlign - 1));
+    const uint32_t sm = uint32_t((reinterpret_cast<uintptr_t>(src) - md) & 15u);
+    const int64_t n = int64_t(bytes);
+    const rsrc_t out = make_rsrc(dst - md + tile * TILE, uint32_t(TILE));  // the tile's grid start
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t p0 = int64_t(tile * TILE) + int64_t(threadIdx.x + u * THREADS) * 16 - int64_t(md);
+        if (p0 >= 0 && p0 + 16 <= n) {
+            bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * THREADS) * 16, load16_any<true>(src + p0, sm));
+        } else if (p0 + 16 > 0 && p0 < n) {
+            const int64_t e = p0 + 16 < n ? p0 + 16 : n;
+            for (int64_t i = p0 > 0 ? p0 : 0; i < e; i++) dst[i] = src[i];
+        }
+    }
+}
+
 // Read pass over a gather table's source tiles: plain loads, which leave the
 // bytes in the Infinity Cache for the fan-out launched right after.  The
-// empty asm keeps the loads; nothing is stored.
+// empty asm keeps the loads (each waits for its own, which a read pass can
+// afford: it only has to touch the lines); nothing is stored.
 __global__ __launch_bounds__(kGatherBlock) void k_gather_touch(GatherArgs a) {
     constexpr int U = kGatherU;
     constexpr uint64_t kTile = kGatherTileBytes;
@@ -84,16 +139,31 @@ __global__ __launch_bounds__(kGatherBlock) void k_gather_touch(GatherArgs a) {
     const int nr = a.nranks;
     int r = 0;
     while (r + 1 < nr && a.tile_start[r + 1] <= b) r++;
-    if (!((a.aligned >> r) & 1u)) return;
     const char* src = static_cast<const char*>(a.src[r]);
     const uint64_t b0 = uint64_t(b - a.tile_start[r]) * kTile;
-    const uint64_t v1 = min(a.bytes[r], b0 + kTile) / 16;
+    if ((a.aligned >> r) & 1u) {
+        const uint64_t v1 = min(a.bytes[r], b0 + kTile) / 16;
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kGatherBlock;
-        if (v < v1) {
-            const u32x4 x = load16_h<false>(src + v * 16);
-            asm volatile("" ::"v"(x));
+        for (int u = 0; u < U; u++) {
+            const uint64_t v = b0 / 16 + threadIdx.x + uint64_t(u) * kGatherBlock;
+            if (v < v1) {
+                const u32x4 x = load16_h<false>(src + v * 16);
+                asm volatile("" ::"v"(x));
+            }
+        }
+    } else if ((a.shifted >> r) & 1u) {
+        // the same grid as k_gather: each lane reads the aligned source vector
+        // holding the first byte its grid vector needs
+        const uint32_t md = uint32_t(reinterpret_cast<uintptr_t>(a.dst[r * nr]) & (kGridAlign - 1));
+        const int64_t bytes = int64_t(a.bytes[r]);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t p0 = int64_t(b0) + int64_t(threadIdx.x + u * kGatherBlock) * 16 - int64_t(md);
+            if (p0 + 16 > 0 && p0 < bytes) {
+                const char* at = src + (p0 > 0 ? p0 : 0);
+                const u32x4 x = load16_h<false>(at - (reinterpret_cast<uintptr_t>(at) & 15u));
+                asm volatile("" ::"v"(x));
+            }
         }
     }
 }
@@ -144,7 +214,7 @@ __global__ __launch_bounds__(kA2AThreads) void k_all_to_all(AllToAllArgs a) {
         const uint64_t t = v1 * 16 + threadIdx.x;
         if (t < b1) dst[t] = src[t];
     } else {
-        for (uint64_t t = b0 + threadIdx.x; t < b1; t += kA2AThreads) dst[t] = src[t];
+        copy_shifted<kA2AThreads, kCopyTileBytes>(src, dst, a.bytes[k], b - start);
     }
 }
 
@@ -197,7 +267,7 @@ __global__ __launch_bounds__(kSegCopyBlock) void k_copy_segments(SegCopyArgs a) 
         const uint64_t t = v1 * 16 + threadIdx.x;
         if (t < b1) dst[t] = src[t];
     } else {
-        for (uint64_t t = b0 + threadIdx.x; t < b1; t += kSegCopyBlock) dst[t] = src[t];
+        copy_shifted<kSegCopyBlock, kSegCopyTileBytes>(src, dst, a.bytes[k], b - a.tile_start[k]);
     }
 }
 

@@ -67,6 +67,55 @@ __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, POL);
 }
 
+// Bytes [s, s + 16) of the 32 bytes lo:hi (little endian), 0 <= s <= 15,
+// s the same in every lane: a 16-byte vector of a source that is not
+// 16-byte aligned, built from the two aligned vectors around it.  The word
+// selection branches on the uniform s / 4; v_alignbyte joins two words.
+__device__ __forceinline__ u32x4 funnel16(u32x4 lo, u32x4 hi, uint32_t s) {
+    const uint32_t b = s & 3u;
+    u32x4 o;
+    switch (s >> 2) {
+        case 0:
+            o[0] = __builtin_amdgcn_alignbyte(lo[1], lo[0], b);
+            o[1] = __builtin_amdgcn_alignbyte(lo[2], lo[1], b);
+            o[2] = __builtin_amdgcn_alignbyte(lo[3], lo[2], b);
+            o[3] = __builtin_amdgcn_alignbyte(hi[0], lo[3], b);
+            break;
+        case 1:
+            o[0] = __builtin_amdgcn_alignbyte(lo[2], lo[1], b);
+            o[1] = __builtin_amdgcn_alignbyte(lo[3], lo[2], b);
+            o[2] = __builtin_amdgcn_alignbyte(hi[0], lo[3], b);
+            o[3] = __builtin_amdgcn_alignbyte(hi[1], hi[0], b);
+            break;
+        case 2:
+            o[0] = __builtin_amdgcn_alignbyte(lo[3], lo[2], b);
+            o[1] = __builtin_amdgcn_alignbyte(hi[0], lo[3], b);
+            o[2] = __builtin_amdgcn_alignbyte(hi[1], hi[0], b);
+            o[3] = __builtin_amdgcn_alignbyte(hi[2], hi[1], b);
+            break;
+        default:
+            o[0] = __builtin_amdgcn_alignbyte(hi[0], lo[3], b);
+            o[1] = __builtin_amdgcn_alignbyte(hi[1], hi[0], b);
+            o[2] = __builtin_amdgcn_alignbyte(hi[2], hi[1], b);
+            o[3] = __builtin_amdgcn_alignbyte(hi[3], hi[2], b);
+            break;
+    }
+    return o;
+}
+
+// The 16 bytes at p, any alignment, from aligned loads only: the one aligned
+// vector holding them, or the two around them.  Each of those aligned
+// vectors holds at least one of the 16 requested bytes, so none reaches a
+// page that the requested bytes do not touch.  `misalign` is p & 15, passed
+// in because it is uniform across the lanes of a copy.
+template <bool NT>
+__device__ __forceinline__ u32x4 load16_any(const char* p, uint32_t misalign) {
+    const char* a = p - misalign;
+    const u32x4 lo = load16_h<NT>(a);
+    if (misalign == 0) return lo;
+    return funnel16(lo, load16_h<NT>(a + 16), misalign);
+}
+
 // ------------------------------------------------------------------- bf16 --
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

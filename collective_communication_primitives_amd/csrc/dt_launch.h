@@ -16,9 +16,9 @@ struct ReduceArgs {
     const void* src[kMaxRanksHost];
     void* dst[kMaxRanksHost];
     uint64_t first;        // first element handled by this launch (element path)
-    uint64_t count;        // elements per chunk handled by this launch (vector path: vectors);
-                           // ReduceScatter: also the stride between chunk starts
+    uint64_t count;        // elements per chunk handled by this launch (vector path: vectors)
     uint64_t last_count;   // vector ReduceScatter: vectors of the last chunk (<= count)
+    uint64_t chunk_stride; // vector ReduceScatter: vectors between chunk starts in each input (>= count)
     uint64_t chunk_elems;  // ReduceScatter: elements per output chunk
     int nranks;
     int rs;                // 1: ReduceScatter (grid.y = chunk), 0: AllReduce
@@ -80,8 +80,20 @@ struct GatherArgs {
     uint64_t bytes[kMaxRanksHost];
     uint32_t tile_start[kMaxRanksHost + 1];
     uint32_t aligned;      // bit r: rank r's piece and its destinations allow 16-byte vectors
+    uint32_t shifted;      // bit r (not aligned): rank r's destinations share one offset within a
+                           // 128-byte line; its tiles then follow their line grid (grid_tiles)
     int nranks;
 };
+
+// Tiles of a copy whose destination is not 16-byte aligned: the tiles cover
+// a grid that starts at the 128-byte line holding the destination's first
+// byte, md = dst & (kGridAlign - 1) bytes before it, so that no line is
+// written by two workgroups, and every interior 16-byte vector is one aligned
+// store, built from aligned loads of the source (funnel16).
+constexpr uint64_t kGridAlign = 128;
+inline uint64_t grid_tiles(uint64_t bytes, uint64_t md, uint64_t tile_bytes) {
+    return (md + bytes + tile_bytes - 1) / tile_bytes;
+}
 
 // 1:1 copies of independent byte ranges (ReplicateToShard and other
 // per-rank copies): segment k copies bytes[k] from src[k] to dst[k].

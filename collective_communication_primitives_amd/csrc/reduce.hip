@@ -82,10 +82,11 @@ __global__ __launch_bounds__(BLOCK) void k_reduce_vec(ReduceArgs a) {
 
 // --------------------------------------------------------- ReduceScatter --
 // grid.x covers a.count vectors of one chunk in tiles of BLOCK*U; grid.y =
-// output chunk.  Chunk c starts c * a.count vectors into every input; the
-// last chunk holds a.last_count vectors (the two-shot AllReduce cuts its
-// chunks in whole tiles, so the last one may be shorter), and its tiles past
-// that end return at once.  Buffer instructions: one resource per rank for the tile's
+// output chunk.  Chunk c starts c * a.chunk_stride vectors into every input
+// and holds a.count vectors; the last chunk holds a.last_count (the two-shot
+// AllReduce cuts its chunks in whole tiles, so the last one may be shorter),
+// and its tiles past that end return at once.  The stride exceeds the count
+// when a misaligned head of every chunk went to the element path.  Buffer instructions: one resource per rank for the tile's
 // range (the same lane offsets serve all P ranks), non-temporal loads and
 // device-scope stores; the resource range cuts off the last tile.  Measured
 // against the same kernel with 64-bit global addressing: 2-3% faster for
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(BLOCK) void k_reduce_scatter_vec(ReduceArgs a) {
     if (t0 >= cnt) return;                                      // past the end of a shorter last chunk
     const uint64_t left = cnt - t0;
     const uint32_t bytes = uint32_t((left < kTileVecs ? left : kTileVecs) * 16);
-    const uint64_t in_off = (chunk * a.count + t0) * 16;       // bytes into every rank's input
+    const uint64_t in_off = (chunk * a.chunk_stride + t0) * 16;  // bytes into every rank's input
     const uint32_t lane = threadIdx.x * 16;
     u32x4 x[U][P];
 #pragma unroll

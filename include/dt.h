@@ -32,8 +32,12 @@
  *    meeting another written or read one; exact in-place operands are
  *    allowed where a call says so); DT_ERR_HIP when a launch fails.  Nothing throws across
  *    the ABI; dt_last_error() gives this thread's last message.
- *  - Fast path: 16-byte aligned buffers and offsets.  Anything else is still
- *    correct but runs an element-wise path.
+ *  - Fast path: 16-byte aligned buffers and offsets.  A fold whose buffers
+ *    are all off alignment by the same amount folds the elements up to the
+ *    next 16-byte boundary element by element and the rest the fast way; the
+ *    copy engines build aligned stores from aligned loads whatever the source
+ *    offset (the fan-out when all destinations of a piece share one
+ *    misalignment).  Anything else is still correct but runs element-wise.
  */
 #ifndef DT_H
 #define DT_H
@@ -70,11 +74,11 @@ typedef enum {
  * read once per rank and written once per rank (the one-shot form of the
  * c10d page, sec. 9.4).  From 16 MiB per rank up for P >= 16, from 24 to
  * 256 MiB for 8 <= P < 16, from 32 to 256 MiB for 5 <= P <= 7 and from 128
- * to 192 MiB for P = 4, with count a
- * whole number of 16-byte vectors and 16-byte aligned buffers, it runs as a
+ * to 192 MiB for P = 4, with 16-byte aligned buffers, it runs as a
  * ReduceScatter into chunk r of recv[r] (chunks of whole 1 KiB tiles, the
  * last one shorter) followed by an in-place AllGather of the chunks, which
- * is faster there.  Beyond 256 MiB per rank for P >= 5 it runs window by
+ * is faster there (elements past the last whole vector take the element
+ * path).  Beyond 256 MiB per rank for P >= 5 it runs window by
  * window (64 MiB per rank at P >= 16, 128 MiB at P = 5-15), each window an
  * AllReduce of its own in the two-shot form, so the window's chunks are
  * still in the Infinity Cache when they fan out.  All forms fold in the

@@ -170,15 +170,18 @@ hipError_t launch_reduce_vec(const ReduceArgs& a, int, int, hipStream_t) {
         }
         return hipSuccess;
     }
-    // ReduceScatter: chunk c starts c * count vectors into every input and holds
-    // count vectors, the last chunk last_count (the kernel's early exit)
+    // ReduceScatter: chunk c starts c * chunk_stride vectors into every input and
+    // holds count vectors, the last chunk last_count (the kernel's early exit)
     CHECK(a.last_count >= 1 && a.last_count <= a.count, "reduce_scatter: last chunk %llu of %llu vectors",
           (unsigned long long)a.last_count, (unsigned long long)a.count);
+    CHECK(a.chunk_stride >= a.count, "reduce_scatter: chunk stride %llu below the count %llu",
+          (unsigned long long)a.chunk_stride, (unsigned long long)a.count);
     const uint64_t last = a.last_count * 16;
     log_fold(a.dst[0], a.nranks == 1 ? last : bytes);
     for (int r = 0; r < a.nranks; r++) {
         CHECK(al16(a.src[r]) && al16(a.dst[r]), "reduce_vec buffers not 16-byte aligned");
-        touch(a.src[r], 0, bytes * (a.nranks - 1) + last, false, "reduce_scatter read");
+        for (int c = 0; c < a.nranks; c++)
+            touch(a.src[r], c * a.chunk_stride * 16, c + 1 == a.nranks ? last : bytes, false, "reduce_scatter read");
         touch(a.dst[r], 0, r + 1 == a.nranks ? last : bytes, true, "reduce_scatter write");
     }
     return hipSuccess;
@@ -290,11 +293,25 @@ struct GatherPiece {
 std::vector<GatherPiece> g_gather_pieces;
 int g_touch_launches = 0;
 
+// Tiles of gather piece r: over its bytes, or, for a shifted piece, over its
+// destinations' aligned 16-byte grid (all of them off alignment by md).
+uint64_t gather_tiles(const GatherArgs& a, int r) {
+    if (((a.shifted >> r) & 1u) && a.bytes[r]) {
+        CHECK(!((a.aligned >> r) & 1u), "gather: piece %d both aligned and shifted", r);
+        const uintptr_t md = reinterpret_cast<uintptr_t>(a.dst[r * a.nranks]) & (kGridAlign - 1);
+        for (int q = 0; q < a.nranks; q++)
+            CHECK((reinterpret_cast<uintptr_t>(a.dst[r * a.nranks + q]) & (kGridAlign - 1)) == md,
+                  "gather: shifted piece %d with destinations of different alignment", r);
+        return ceil_div(md + a.bytes[r], kGatherTileBytes);
+    }
+    return ceil_div(a.bytes[r], kGatherTileBytes);
+}
+
 hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t) {
     g_launches++;
     g_touch_launches++;
     std::vector<uint64_t> want;
-    for (int r = 0; r < a.nranks; r++) want.push_back(ceil_div(a.bytes[r], kGatherTileBytes));
+    for (int r = 0; r < a.nranks; r++) want.push_back(gather_tiles(a, r));
     check_tiles(a.tile_start, want, tiles, "gather touch");
     for (int r = 0; r < a.nranks; r++) {
         touch(a.src[r], 0, a.bytes[r], false, "gather touch read");
@@ -312,7 +329,7 @@ hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t) {
             if (a.dst[r * a.nranks] != a.src[r]) log_fold(a.dst[r * a.nranks], a.bytes[r]);
         }
     std::vector<uint64_t> want;
-    for (int r = 0; r < a.nranks; r++) want.push_back(ceil_div(a.bytes[r], kGatherTileBytes));
+    for (int r = 0; r < a.nranks; r++) want.push_back(gather_tiles(a, r));
     check_tiles(a.tile_start, want, tiles, "gather");
     for (int r = 0; r < a.nranks; r++) {
         if (a.bytes[r] == 0) continue;
@@ -339,7 +356,8 @@ hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t)
     std::vector<uint64_t> want;
     for (int k = 0; k < a.nblocks; k++) {
         CHECK(a.bytes[k] > 0, "all_to_all: empty block %d", k);
-        want.push_back(ceil_div(a.bytes[k], kCopyTileBytes));
+        const bool al = (a.aligned[k >> 6] >> (k & 63)) & 1ull;  // else tiles over the destination's aligned grid
+        want.push_back(ceil_div((al ? 0 : reinterpret_cast<uintptr_t>(a.to[k]) & (kGridAlign - 1)) + a.bytes[k], kCopyTileBytes));
     }
     check_tiles(a.tile_start, want, tiles, "all_to_all");
     for (int k = a.nblocks + 1; k <= kA2ABlocks; k++)
@@ -362,7 +380,8 @@ hipError_t launch_copy_segments(const SegCopyArgs& a, hipStream_t) {
     CHECK(a.nsegs >= 1 && a.nsegs <= kMaxCopySegs, "copy_segments: %d segments", a.nsegs);
     std::vector<uint64_t> want;
     for (int k = 0; k < a.nsegs; k++) {
-        want.push_back(ceil_div(a.bytes[k], kSegCopyTileBytes));
+        const bool al = (a.aligned >> k) & 1ull;  // else tiles over the destination's aligned grid
+        want.push_back(ceil_div((al ? 0 : reinterpret_cast<uintptr_t>(a.dst[k]) & (kGridAlign - 1)) + a.bytes[k], kSegCopyTileBytes));
         touch(a.src[k], 0, a.bytes[k], false, "copy_segments read");
         touch(a.dst[k], 0, a.bytes[k], true, "copy_segments write");
         if ((a.aligned >> k) & 1ull) CHECK(al16(a.src[k]) && al16(a.dst[k]), "copy_segments: unaligned");
@@ -926,7 +945,8 @@ void two_shot() {
         {12, DT_BFLOAT16, 200 * M + 96, false, 3},    // 400 MiB + 192 B at P=12: three windows, a one-shot tail
         {8, DT_BFLOAT16, 64 * M + 8, false, 1},       // not a multiple of P vectors: a shorter last chunk
         {12, DT_FLOAT32, 48 * M + 4, false, 1},       // 192 MiB + 16 B at P=12: chunks of whole 1 KiB tiles
-        {8, DT_BFLOAT16, 64 * M + 4, false, 0},       // not a whole number of vectors: one-shot
+        {8, DT_BFLOAT16, 64 * M + 4, false, 1},       // not a whole number of vectors: two-shot, an element tail
+        {8, DT_BFLOAT16, 12 * M + 3, false, 1},       // 24 MiB + 6 B
         {4, DT_FLOAT32, 32 * M, false, 1},            // 128 MiB at P=4
         {4, DT_FLOAT32, 48 * M, true, 1},             // 192 MiB at P=4
         {4, DT_FLOAT32, 16 * M, false, 0},            // 64 MiB at P=4

@@ -1,0 +1,166 @@
+"""GPU: buffers that are not 16-byte aligned.
+
+When every buffer of an AllReduce or ReduceScatter is off alignment by the
+same amount, the library folds the elements up to the next 16-byte boundary
+on the element path and the aligned rest with the vector kernels.  The copy
+engines (fan-out, AllToAll, segment copy) run unaligned pieces over their
+destination's aligned 16-byte grid, building each vector from aligned loads
+of the source.  Every case is compared with the oracle element by element
+(bit for bit: copies and fixed-order folds), and guard bands around every
+output prove that nothing is written outside it."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import Guarded, compare, note, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dt():
+    import collective_communication_primitives_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def _views(src, offset):
+    """Copies of src placed `offset` elements past a 16-byte aligned start."""
+    out = []
+    for x in src:
+        g = Guarded(x.numel(), x.dtype, offset_elems=offset)
+        g.t.copy_(x.reshape(-1))
+        out.append(g)
+    return out
+
+
+@pytest.mark.parametrize("p,dtype,n,off,op", [
+    (8, torch.bfloat16, 8192 * 8192, 1, "sum"),     # the RS -> AG workload's shape, 2 bytes off: two-shot body
+    (8, torch.bfloat16, 8192 * 8192 + 5, 3, "max"), # ragged too
+    (16, torch.float32, (16 << 20) + 3, 1, "sum"),  # 64 MiB + 12 B, 4 bytes off
+    (4, torch.float32, 1 << 20, 2, "avg"),          # the small AllReduce, 8 bytes off
+    (3, torch.bfloat16, 1000, 7, "min"),            # shorter than a vector after the head
+])
+def test_allreduce_shared_misalignment(dt, orc, p, dtype, n, off, op):
+    note(f"misaligned allreduce P={p} {dtype} n={n} off={off} {op}")
+    src = (synth.normal_ranks(p, (n,), seed=p + off, device="cuda", dtype=dtype) if dtype == torch.bfloat16
+           else synth.uniform_ranks(p, n, seed=p + off, device="cuda"))
+    xs = _views(src, off)
+    ys = [Guarded(n, dtype, offset_elems=off).poison() for _ in range(p)]
+    dt.dt_allreduce([g.t for g in xs], [g.t for g in ys], op=op)
+    torch.cuda.synchronize()
+    want = orc.allreduce([to_np(x) for x in src], op)[0]
+    compare(to_np(ys[0].t), want, "rank 0")
+    view = (lambda t: t.view(torch.int16)) if dtype == torch.bfloat16 else (lambda t: t.view(torch.int32))
+    for q in range(p):
+        ys[q].check()
+        assert torch.equal(view(ys[q].t), view(ys[0].t)), f"rank {q} differs from rank 0"
+
+
+@pytest.mark.parametrize("p,dtype,m,off", [
+    (8, torch.bfloat16, 8192 * 1024, 1),   # chunks of whole vectors, 2 bytes off: head, body, tail per chunk
+    (8, torch.float32, 4096 + 8, 3),       # 12 bytes off
+    (5, torch.bfloat16, 4099, 2),          # chunk bytes not a multiple of 16: element path
+])
+def test_reduce_scatter_shared_misalignment(dt, orc, p, dtype, m, off):
+    note(f"misaligned reduce_scatter P={p} {dtype} m={m} off={off}")
+    src = (synth.normal_ranks(p, (p * m,), seed=3 * p, device="cuda", dtype=dtype) if dtype == torch.bfloat16
+           else synth.uniform_ranks(p, p * m, seed=3 * p, device="cuda"))
+    xs = _views(src, off)
+    ys = [Guarded(m, dtype, offset_elems=off).poison() for _ in range(p)]
+    dt.dt_reduce_scatter([g.t for g in xs], [g.t for g in ys])
+    torch.cuda.synchronize()
+    want = orc.reduce_scatter([to_np(x) for x in src], "sum")
+    for r in range(p):
+        ys[r].check()
+        compare(to_np(ys[r].t), want[r], f"rank {r}")
+
+
+def test_uneven_all_gather_odd_bf16_counts(dt, orc):
+    """The uneven AllGather workload's row counts, in bf16, each count odd:
+    every piece after the first lands at an odd element offset, so its
+    destinations are 2 bytes off alignment (the shifted fan-out)."""
+    p = 8
+    rows = synth.uneven_row_counts(seed=0)
+    counts = [int(r) * 4096 + 2 * k + 1 for k, r in enumerate(rows)]
+    note(f"uneven bf16 all_gather odd counts total={sum(counts)}")
+    xs = [synth.normal_ranks(1, (c,), seed=50 + k, device="cuda", dtype=torch.bfloat16)[0] for k, c in enumerate(counts)]
+    total = sum(counts)
+    ys = [Guarded(total, torch.bfloat16).poison() for _ in range(p)]
+    dt.dt_all_gather(xs, [g.t for g in ys])
+    torch.cuda.synchronize()
+    want = np.concatenate([to_np(x) for x in xs])
+    for q in range(p):
+        ys[q].check()
+        assert np.array_equal(to_np(ys[q].t), want), f"output {q}"
+
+
+@pytest.mark.parametrize("dtype,off_send,off_recv", [(torch.bfloat16, 0, 3), (torch.float32, 1, 2), (torch.int32, 3, 0)])
+def test_all_to_all_odd_splits(dt, orc, dtype, off_send, off_recv):
+    """A split matrix of odd element counts: blocks start at every offset
+    inside their source and destination (shifted 1:1 copies)."""
+    p = 6
+    rng = np.random.default_rng(11)
+    s = rng.integers(0, 40000, (p, p)) * 2 + 1
+    s[1, 2] = 0
+    note(f"all_to_all odd splits {dtype} offsets {off_send}/{off_recv}")
+    xs = []
+    for i in range(p):
+        n = int(s[i].sum())
+        t = torch.arange(n, dtype=torch.int32, device="cuda").to(dtype) if dtype != torch.bfloat16 else \
+            synth.normal_ranks(1, (n,), seed=70 + i, device="cuda", dtype=dtype)[0]
+        g = Guarded(n, dtype, offset_elems=off_send)
+        g.t.copy_(t)
+        xs.append(g)
+    ys = [Guarded(int(s[:, j].sum()), dtype, offset_elems=off_recv).poison() for j in range(p)]
+    dt.dt_all_to_all([g.t for g in xs], [g.t for g in ys], s.tolist())
+    torch.cuda.synchronize()
+    want = orc.all_to_all([to_np(g.t) for g in xs], s)
+    for j in range(p):
+        ys[j].check()
+        assert np.array_equal(to_np(ys[j].t), want[j]), f"rank {j}"
+
+
+def test_broadcast_and_gather_into_vec_misaligned(dt, orc):
+    p, n = 8, (3 << 20) + 7
+    root = synth.normal_ranks(1, (n,), seed=90, device="cuda", dtype=torch.bfloat16)[0]
+    src = Guarded(n, torch.bfloat16, offset_elems=5)
+    src.t.copy_(root)
+    outs = [Guarded(n, torch.bfloat16, offset_elems=3).poison() for _ in range(p)]
+    note("misaligned broadcast")
+    dt.dt_broadcast(src.t, [g.t for g in outs])
+    counts = [1000 + 17 * r for r in range(p)]
+    pieces = [Guarded(c, torch.bfloat16, offset_elems=r % 8) for r, c in enumerate(counts)]
+    for r, g in enumerate(pieces):
+        g.t.copy_(synth.normal_ranks(1, (counts[r],), seed=95 + r, device="cuda", dtype=torch.bfloat16)[0])
+    vec = [[Guarded(counts[r], torch.bfloat16, offset_elems=1).poison() for r in range(p)] for _ in range(p)]
+    note("misaligned all_gather_into_vec")
+    dt.dt_all_gather_into_vec([g.t for g in pieces], [[g.t for g in row] for row in vec])
+    torch.cuda.synchronize()
+    want = to_np(root)
+    for q in range(p):
+        outs[q].check()
+        assert np.array_equal(to_np(outs[q].t), want), f"broadcast {q}"
+        for r in range(p):
+            vec[q][r].check()
+            assert np.array_equal(to_np(vec[q][r].t), to_np(pieces[r].t)), f"vec {q} {r}"
+
+
+def test_replicate_to_shard_misaligned(dt, orc):
+    p, m = 8, (1 << 18) + 3
+    src = synth.normal_ranks(p, (p * m,), seed=7, device="cuda", dtype=torch.bfloat16)
+    xs = _views(src, 1)
+    ys = [Guarded(m, torch.bfloat16, offset_elems=6).poison() for _ in range(p)]
+    note("misaligned replicate_to_shard")
+    dt.dt_replicate_to_shard([g.t for g in xs], [g.t for g in ys])
+    torch.cuda.synchronize()
+    want = orc.replicate_to_shard([to_np(x) for x in src])
+    for r in range(p):
+        ys[r].check()
+        assert np.array_equal(to_np(ys[r].t), want[r]), f"rank {r}"

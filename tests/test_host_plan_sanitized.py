@@ -57,8 +57,15 @@ def test_planning_code_is_clean(check_obj, tmp_path):
 
 MUTANTS = {
     # the gather grid drops the partial last tile of every source
-    "gather_drops_partial_tile": ("tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;",
-                                  "tiles += bytes[k] / tile_bytes;"),
+    "gather_drops_partial_tile": ("a.aligned |= 1u << k;\n            tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;",
+                                  "a.aligned |= 1u << k;\n            tiles += bytes[k] / tile_bytes;"),
+    # a shifted fan-out piece counts its tiles without the destinations' misalignment
+    "shifted_gather_tiles_short": ("tiles += dt::grid_tiles(bytes[k], md, tile_bytes);",
+                                   "tiles += dt::grid_tiles(bytes[k], 0, tile_bytes);"),
+    # an unaligned all-to-all block counts its tiles over its bytes, not its destination's grid
+    "shifted_a2a_tiles_short": ("grid_tiles(bytes, reinterpret_cast<uintptr_t>(to) & (dt::kGridAlign - 1),",
+                                "grid_tiles(bytes, 0 & (dt::kGridAlign - 1),"),
+
     # the windows of a large fan-out go out without their read passes
     "window_skips_read_pass": ("if (touch_first && (st = check_hip(dt::launch_gather_touch(",
                                "if (false && touch_first && (st = check_hip(dt::launch_gather_touch("),
