@@ -55,6 +55,8 @@ def compare(got: np.ndarray, want: np.ndarray, what: str = "") -> None:
     """Bit equality; where the oracle's result is a NaN only NaN-ness is
     compared, because IEEE 754 leaves the payload of a NaN produced by an
     addition to the implementation (x86 and the GPU may pick differently)."""
+    if got.shape == want.shape and got.dtype == want.dtype and np.array_equal(got.view(np.uint8), want.view(np.uint8)):
+        return  # identical bits pass every bar below; large arrays take only this test
     if want.dtype == np.uint16:
         assert_bf16_within(got, want, what)
     elif want.dtype == np.float32:

@@ -87,3 +87,62 @@ def test_graph_replays_two_shot_allreduce(dt):
         compare(to_np(ys[0]), want, f"replay {replay} rank 0")
         for q in range(1, p):
             assert torch.equal(ys[q], ys[0]), f"replay {replay} rank {q} differs from rank 0"
+
+
+def test_graph_replays_large_argument_tables(dt):
+    """Launches whose kernel arguments exceed 4 KiB, captured in one graph:
+    the coalesced AllReduce of 600 tensors at P=2 (a piece table of about
+    43 KiB per launch), the in-place bucket AllReduce of the same tensors
+    and an AllToAll over a full 16 x 16 split matrix (a 7.3 KiB block
+    table).  The inputs are rewritten eagerly between replays, and every
+    replay is checked against the oracle on that replay's inputs."""
+    orc = oracle.get()
+    rng = np.random.default_rng(5)
+    p2, nt = 2, 600
+    sizes = [int(x) for x in rng.integers(1, 3000, nt)]
+    coal = [[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in sizes] for _ in range(p2)]
+    buck = [[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in sizes] for _ in range(p2)]
+    p16 = 16
+    split = rng.integers(0, 600, (p16, p16)) + 1
+    a_in = [torch.empty(int(split[i].sum()), dtype=torch.int32, device="cuda") for i in range(p16)]
+    a_out = [torch.empty(int(split[:, j].sum()), dtype=torch.int32, device="cuda") for j in range(p16)]
+
+    def work():
+        dt.dt_allreduce_coalesced(coal, op="max")
+        dt.dt_bucket_allreduce(buck, bucket_bytes=64 << 10)
+        dt.dt_all_to_all(a_in, a_out, split.tolist())
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()  # the launch path warmed outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    note("graph capture of coalesced / bucket / all-to-all launches")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for replay in range(3):
+        note(f"graph replay {replay} (large argument tables)")
+        for r in range(p2):
+            for t, n in enumerate(sizes):
+                v = synth.normal_ranks(1, (n,), seed=1000 * replay + 10 * r + t % 10, device="cuda",
+                                       dtype=torch.bfloat16)[0]
+                coal[r][t].copy_(v)
+                buck[r][t].copy_(v)
+        for i in range(p16):
+            a_in[i].copy_(torch.randint(-2**31, 2**31 - 1, (a_in[i].numel(),), dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        host_c = [[to_np(t) for t in rank] for rank in coal]
+        host_a = [to_np(x) for x in a_in]
+        g.replay()
+        torch.cuda.synchronize()
+        want_max = [[orc.allreduce([host_c[r][t] for r in range(p2)], "max")[0] for t in range(nt)]]
+        want_sum = orc.bucket_allreduce(host_c, 64 << 10, "sum")
+        for r in range(p2):
+            for t in range(nt):
+                compare(to_np(coal[r][t]), want_max[0][t], f"replay {replay} coalesced rank {r} tensor {t}")
+                compare(to_np(buck[r][t]), want_sum[r][t], f"replay {replay} bucket rank {r} tensor {t}")
+        want_a = orc.all_to_all(host_a, split)
+        for j in range(p16):
+            compare(to_np(a_out[j]), want_a[j], f"replay {replay} all_to_all rank {j}")
