@@ -897,7 +897,12 @@ dt_status dt_all_to_all_dims(const void* const* send, void* const* recv, int nra
     const uint64_t run_bytes = a.cp * es;
     a.vec = (vec && run_bytes % 16 == 0) ? 1u : 0u;
     uint64_t blocks;
-    if (run_bytes >= dt::kDimsTileBytes) {
+    if (a.vec && run_bytes >= dt::kDimsWaveTileBytes) {
+        a.wave = 1;
+        a.tiles_per_run = uint32_t((run_bytes + dt::kDimsWaveTileBytes - 1) / dt::kDimsWaveTileBytes);
+        a.runs_per_block = 1;
+        blocks = a.nruns * a.tiles_per_run;
+    } else if (run_bytes >= dt::kDimsTileBytes) {
         a.tiles_per_run = uint32_t((run_bytes + dt::kDimsTileBytes - 1) / dt::kDimsTileBytes);
         a.runs_per_block = 1;
         blocks = a.nruns * a.tiles_per_run;

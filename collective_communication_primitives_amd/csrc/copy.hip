@@ -342,6 +342,29 @@ __global__ __launch_bounds__(kBlock) void k_all_to_all_dims(DimsArgs a) {
     }
 }
 
+// Runs of at least one tile with 16-byte aligned bases and lengths: one
+// workgroup of a single wave per 1 KiB slice of one run, the copy engine of
+// the split-matrix all-to-all (a vector per lane, buffer stores that are
+// non-temporal with device scope).  The last slice of a run may be shorter:
+// its store range ends at the run's end, which drops the lanes past it.
+constexpr int kDimsWaveThreads = 64;
+static_assert(kDimsWaveTileBytes == uint64_t(kDimsWaveThreads) * 16, "one vector per lane");
+__global__ __launch_bounds__(kDimsWaveThreads) void k_all_to_all_dims_wave(DimsArgs a) {
+    const uint64_t run_bytes = a.cp * a.esize;
+    const uint64_t b = blockIdx.x;
+    const uint64_t k = b / a.tiles_per_run;
+    const uint64_t lo = (b - k * a.tiles_per_run) * kDimsWaveTileBytes;
+    const uint64_t hi = min(run_bytes, lo + kDimsWaveTileBytes);
+    const char* from;
+    char* to;
+    dims_run(a, k, &from, &to);
+    const uint32_t off = threadIdx.x * 16;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (lo + off < hi) x = load16(from + lo + off);
+    const rsrc_t out = make_rsrc(to + lo, uint32_t(hi - lo));
+    bstore16<kPolNT | kPolDevice>(out, off, x);
+}
+
 hipError_t launch_copy_segments(const SegCopyArgs& a, hipStream_t s) {
     const uint32_t tiles = a.tile_start[a.nsegs];
     if (tiles == 0) return hipSuccess;
@@ -351,7 +374,10 @@ hipError_t launch_copy_segments(const SegCopyArgs& a, hipStream_t s) {
 
 hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_t s) {
     if (blocks == 0) return hipSuccess;
-    k_all_to_all_dims<<<blocks, kBlock, 0, s>>>(a);
+    if (a.wave)
+        k_all_to_all_dims_wave<<<blocks, kDimsWaveThreads, 0, s>>>(a);
+    else
+        k_all_to_all_dims<<<blocks, kBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -124,6 +124,7 @@ struct DimsArgs {
     uint32_t runs_per_block;       // >= 1
     uint32_t tiles_per_run;        // >= 1 (only one of the two exceeds 1)
     uint32_t vec;                  // 1: runs and bases allow 16-byte vectors
+    uint32_t wave;                 // 1: one kDimsWaveTileBytes slice of one run per single-wave workgroup
     uint64_t nruns;
     int nranks;
     int dir;
@@ -200,6 +201,7 @@ hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_
 constexpr uint64_t kSegCopyTileBytes = 1024;
 constexpr uint64_t kDimsTileBytes = 16384;
 constexpr uint32_t kDimsMaxRunsPerBlock = 64;
+constexpr uint64_t kDimsWaveTileBytes = 1024;  // the single-wave path: 64 lanes x 16 bytes
 // The static staging buffer of the allocation-free bucket AllReduce
 // (scratch.hip): its device address on the current device, looked up once per
 // device.  kScratchBytes holds eight ranks' 25 MiB buckets (or sixteen of 16 MiB).

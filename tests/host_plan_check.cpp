@@ -397,9 +397,15 @@ hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_
     CHECK(a.nruns == a.rows * P, "dims: %llu runs", (unsigned long long)a.nruns);
     CHECK(a.runs_per_block >= 1 && a.runs_per_block <= kDimsMaxRunsPerBlock && a.tiles_per_run >= 1,
           "dims: blocking");
-    CHECK(a.tiles_per_run == (run_bytes >= kDimsTileBytes ? ceil_div(run_bytes, kDimsTileBytes) : 1),
-          "dims: tiles per run");
-    if (a.tiles_per_run > 1)
+    if (a.wave) {
+        CHECK(a.vec && run_bytes >= kDimsWaveTileBytes && a.runs_per_block == 1, "dims: single-wave path");
+        CHECK(a.tiles_per_run == ceil_div(run_bytes, kDimsWaveTileBytes), "dims: wave tiles per run");
+    } else {
+        CHECK(!(a.vec && run_bytes >= kDimsWaveTileBytes), "dims: vector runs of a tile or more take the wave path");
+        CHECK(a.tiles_per_run == (run_bytes >= kDimsTileBytes ? ceil_div(run_bytes, kDimsTileBytes) : 1),
+              "dims: tiles per run");
+    }
+    if (a.wave || a.tiles_per_run > 1)
         CHECK(blocks == a.nruns * a.tiles_per_run, "dims: grid %u", blocks);
     else
         CHECK(blocks == ceil_div(a.nruns, a.runs_per_block), "dims: grid %u", blocks);

@@ -123,7 +123,9 @@ def test_replicate_to_shard(dt, orc, dtype, p, m):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("p,rows,cols", [(1, 3, 5), (2, 6, 10), (3, 9, 12), (4, 64, 4096), (8, 8192, 8),
-                                         (8, 16, 4096 * 8), (16, 32, 48)])
+                                         (8, 16, 4096 * 8), (16, 32, 48),
+                                         # runs of a tile and more with a shorter last tile
+                                         (4, 12, 2400), (5, 10, 1320)])
 def test_all_to_all_dims(dt, orc, dtype, p, rows, cols):
     for src in (0, 1):
         for dst in (0, 1):

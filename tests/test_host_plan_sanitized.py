@@ -86,6 +86,8 @@ MUTANTS = {
     "a2a_recv_offset_stuck": ("            recv_off[j] += bytes;\n", ""),
     # one run too many for the shard-dimension exchange
     "dims_extra_run": ("a.nruns = uint64_t(rows) * P;", "a.nruns = uint64_t(rows) * P + 1;"),
+    "dims_wave_tiles_short": ("a.tiles_per_run = uint32_t((run_bytes + dt::kDimsWaveTileBytes - 1) / dt::kDimsWaveTileBytes);",
+                              "a.tiles_per_run = uint32_t(run_bytes / dt::kDimsWaveTileBytes);"),
     # every piece claimed 16-byte aligned
     "pieces_always_aligned": ("if (al) set_aligned(a, k);", "set_aligned(a, k);"),
     # the previous layer's fused buffers, whose AllReduce is still pending, may be written again
