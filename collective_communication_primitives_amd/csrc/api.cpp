@@ -364,12 +364,15 @@ dt_status reduce_scatter_segments(const std::vector<std::vector<const void*>>& s
 }
 
 // One fan-out launch over pieces k < n: piece k is bytes[k] at src[k], going to
-// dst[k][q] for every q (host arrays, P entries each).
+// dst[k][q] for every q (host arrays, P entries each), in single-wave 1 KiB
+// tiles (`wave`) or 128-thread 2 KiB ones; a read pass (`touch_first`, 2 KiB
+// tiles only) goes first.
 dt_status fan_out_launch(const void* const* src, const uint64_t* bytes, void* const* const* dst, int n,
-                         int nranks, bool touch_first, hipStream_t stream, const char* what) {
+                         int nranks, bool touch_first, bool wave, hipStream_t stream, const char* what) {
     dt::GatherArgs a = {};
     a.nranks = nranks;
-    const uint64_t tile_bytes = dt::kGatherTileBytes;
+    const uint64_t tile_bytes = wave ? dt::kGatherWaveTileBytes : dt::kGatherTileBytes;
+    a.tile_bytes = uint32_t(tile_bytes);
     uint64_t tiles = 0;
     for (int k = 0; k < n; k++) {
         a.src[k] = src[k];
@@ -424,7 +427,8 @@ dt_status fan_out(const void* const* src, const size_t* counts, void* const* tab
             wbytes[r] = uint64_t(counts[r]) * es;
             for (int q = 0; q < nranks; q++) wdst[r][q] = table[size_t(r) * nranks + q];
         }
-        return fan_out_launch(wsrc, wbytes, wdst_rows, nsources, nranks, false, stream, what);
+        return fan_out_launch(wsrc, wbytes, wdst_rows, nsources, nranks, false, total <= dt::kGatherWaveBytes, stream,
+                              what);
     }
     int n = 0;
     uint64_t fill = 0;
@@ -443,13 +447,13 @@ dt_status fan_out(const void* const* src, const size_t* counts, void* const* tab
             off += take;
             fill += take;
             if (fill >= dt::kFanOutWindowBytes || n == nranks) {
-                if ((st = fan_out_launch(wsrc, wbytes, wdst_rows, n, nranks, true, stream, what)) != DT_OK) return st;
+                if ((st = fan_out_launch(wsrc, wbytes, wdst_rows, n, nranks, true, false, stream, what)) != DT_OK) return st;
                 n = 0;
                 fill = 0;
             }
         }
     }
-    if (n > 0) return fan_out_launch(wsrc, wbytes, wdst_rows, n, nranks, true, stream, what);
+    if (n > 0) return fan_out_launch(wsrc, wbytes, wdst_rows, n, nranks, true, false, stream, what);
     return DT_OK;
 }
 

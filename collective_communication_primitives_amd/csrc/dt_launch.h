@@ -82,6 +82,7 @@ struct GatherArgs {
     uint32_t aligned;      // bit r: rank r's piece and its destinations allow 16-byte vectors
     uint32_t shifted;      // bit r (not aligned): rank r's destinations share one offset within a
                            // 128-byte line; its tiles then follow their line grid (grid_tiles)
+    uint32_t tile_bytes;   // kGatherTileBytes or kGatherWaveTileBytes: the launch's workgroup shape
     int nranks;
 };
 
@@ -169,12 +170,16 @@ struct ExchangeArgs {
 
 // Tile sizes (bytes of one rank's data per workgroup).
 constexpr uint64_t kCopyTileBytes = 1024;    // all-to-all: one wave, one vector per thread
-// Gather (fan-out) tiles: 128-thread workgroups with 1 vector per thread
-// (2 KiB source tiles), for a direct fan-out, the windows of a large one and
-// their read passes alike.
+// Gather (fan-out) tiles, one vector per thread: single-wave workgroups (1
+// KiB source tiles) for a direct fan-out of at most kGatherWaveBytes of
+// sources; 128-thread workgroups (2 KiB) for a larger direct one, for the
+// windows of a large one and for their read passes.
 constexpr int kGatherU = 1;
 constexpr int kGatherBlock = 128;
 constexpr uint64_t kGatherTileBytes = uint64_t(kGatherU) * kGatherBlock * 16;
+constexpr int kGatherWaveBlock = 64;
+constexpr uint64_t kGatherWaveTileBytes = uint64_t(kGatherU) * kGatherWaveBlock * 16;
+constexpr uint64_t kGatherWaveBytes = 128ull << 20;
 constexpr uint64_t kPieceTileVecs = 512;     // bucket pieces: 512 x 16 B
 
 // Launchers: return the HIP error of the launch.  dtype/op are the dt_dtype /

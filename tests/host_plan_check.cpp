@@ -296,20 +296,23 @@ int g_touch_launches = 0;
 // Tiles of gather piece r: over its bytes, or, for a shifted piece, over its
 // destinations' aligned 16-byte grid (all of them off alignment by md).
 uint64_t gather_tiles(const GatherArgs& a, int r) {
+    CHECK(a.tile_bytes == kGatherTileBytes || a.tile_bytes == kGatherWaveTileBytes, "gather: tile of %u bytes",
+          a.tile_bytes);
     if (((a.shifted >> r) & 1u) && a.bytes[r]) {
         CHECK(!((a.aligned >> r) & 1u), "gather: piece %d both aligned and shifted", r);
         const uintptr_t md = reinterpret_cast<uintptr_t>(a.dst[r * a.nranks]) & (kGridAlign - 1);
         for (int q = 0; q < a.nranks; q++)
             CHECK((reinterpret_cast<uintptr_t>(a.dst[r * a.nranks + q]) & (kGridAlign - 1)) == md,
                   "gather: shifted piece %d with destinations of different alignment", r);
-        return ceil_div(md + a.bytes[r], kGatherTileBytes);
+        return ceil_div(md + a.bytes[r], a.tile_bytes);
     }
-    return ceil_div(a.bytes[r], kGatherTileBytes);
+    return ceil_div(a.bytes[r], a.tile_bytes);
 }
 
 hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t) {
     g_launches++;
     g_touch_launches++;
+    CHECK(a.tile_bytes == kGatherTileBytes, "gather touch: %u-byte tiles", a.tile_bytes);
     std::vector<uint64_t> want;
     for (int r = 0; r < a.nranks; r++) want.push_back(gather_tiles(a, r));
     check_tiles(a.tile_start, want, tiles, "gather touch");
