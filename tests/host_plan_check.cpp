@@ -273,6 +273,7 @@ hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, 
         for (int j = 0; j < a.nranks; j++) {
             touch(a.src[k * a.nranks + j], 0, a.m[k] * a.nranks * es, false, "segs read");
             touch(a.dst[k * a.nranks + j], 0, a.m[k] * es, true, "segs write");
+            if (j == 0) log_fold(a.dst[k * a.nranks], a.m[k] * es);  // member 0's folded chunk
             if ((a.aligned >> k) & 1u) {
                 CHECK(a.m[k] % v == 0, "segs: aligned flag with a ragged chunk");
                 CHECK(al16(a.src[k * a.nranks + j]) && al16(a.dst[k * a.nranks + j]), "segs: unaligned");
@@ -655,11 +656,10 @@ void buckets() {
 // In place, tensors of at least 16 MiB per rank take an AllReduce of their
 // own (two-shot or one-shot with a ragged tail) and the rest one fold: rank
 // 0's copy of every tensor is written exactly once, with no gap or overlap.
-void bucket_big() {
-    const int p = 8, nt = 6;
+void bucket_big_case(int p, const std::vector<size_t>& numel_list) {
+    const int nt = int(numel_list.size());
     const size_t es = 2;
-    const size_t numels[nt] = {size_t(16) << 20, 4096, (size_t(8) << 20) + 3, 100, size_t(44) << 20,
-                               (size_t(8) << 20) - 8};
+    const size_t* numels = numel_list.data();
     g_bufs.clear();
     char* base = reinterpret_cast<char*>(uintptr_t(1) << 44);  // fake, never dereferenced
     std::vector<void*> grads(size_t(p) * nt);
@@ -690,6 +690,16 @@ void bucket_big() {
               (unsigned long long)bytes);
     }
     g_bufs.clear();
+}
+
+void bucket_big() {
+    const size_t MiE = size_t(1) << 20;  // elements
+    // two-shot 32 and 88 MiB tensors, a ragged one, small ones folded
+    bucket_big_case(8, {16 * MiE, 4096, 8 * MiE + 3, 100, 44 * MiE, 8 * MiE - 8});
+    // P=16: five two-shot 40 MiB tensors, one of 16 MiB, a small one
+    bucket_big_case(16, {20 * MiE, 20 * MiE, 20 * MiE, 20 * MiE, 20 * MiE, 8 * MiE, 7});
+    // P=4: one-shot 48 MiB tensors
+    bucket_big_case(4, {24 * MiE, 24 * MiE, 24 * MiE});
 }
 
 void hsdp_and_sync() {
