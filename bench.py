@@ -789,9 +789,12 @@ def probe_rows(dt, torch, reps: int = 3):
     its read pass), the two-shot AllReduce at the bench step's shape (its
     ReduceScatter and gather), one layer of the in-place bucket AllReduce
     (two-shot AllReduces of its large tensors, the fold of the small ones at
-    P=8) and one layer of the gradient
-    pipeline (the segmented ReduceScatter at P=4 and the bucket folds at
-    P=2).  Prints one JSON line per workload with its algorithmic bytes."""
+    P=8), one layer of the gradient pipeline (the segmented ReduceScatter
+    at P=4 and the bucket folds at P=2), the AllToAll between shard
+    dimensions of the bf16 [32768, 16384] tensor in both directions, the
+    ReplicateToShard of [8192, 8192] bf16 per rank and the AllReduce of the
+    bench step's inputs 2 bytes off alignment.  Prints one JSON line per
+    workload with its algorithmic bytes."""
     import numpy as np
     import synth
     w = synth.ROW_WIDTH
@@ -822,14 +825,14 @@ def probe_rows(dt, torch, reps: int = 3):
     ys = [torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
     s_bytes = SHAPE[0] * SHAPE[1] * 2
     run("allreduce_two_shot_p8_bf16", lambda: dt.dt_allreduce(xs, ys), 2 * P * s_bytes,
-        ["k_reduce_scatter_vec<1, 0, 8, 64, 1>", "k_gather<8, true, 1, 128>"])
+        ["k_reduce_scatter_vec<1, 0, 8, 64, 1>", "k_gather<8, true, 1, 64>"])
     del xs, ys
     torch.cuda.empty_cache()
     layer = synth.layer_grads(P, layer=0, seed=0, device="cuda")
     numels = [int(np.prod(sh)) for sh in synth.LAYER_SHAPES]
     per_rank_layer = sum(numels) * 2
     run("bucket_allreduce_layer_p8", lambda: dt.dt_bucket_allreduce(layer, bucket_bytes=synth.BUCKET_BYTES),
-        2 * P * per_rank_layer, ["k_reduce_scatter_vec<1, 0, 8, 64, 1>", "k_gather<8, true, 1, 128>",
+        2 * P * per_rank_layer, ["k_reduce_scatter_vec<1, 0, 8, 64, 1>", "k_gather<8, true, 1, 64>",
                                  "k_reduce_pieces<dt::PieceArgs, 1, 0, 8>"])
     rep, sh = 2, 4
     fused = [torch.empty(sum(numels) // sh, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
@@ -842,6 +845,28 @@ def probe_rows(dt, torch, reps: int = 3):
         rep * (sh + 1) * per_rank_layer + 2 * P * (per_rank_layer // sh),
         ["k_reduce_scatter_segs<1, 0, 4, 1>", "k_reduce_pieces<dt::PieceArgs, 1, 0, 2>"])
     del pipe, fused, layer
+    torch.cuda.empty_cache()
+    rows, cols = 32768, 16384
+    blk = rows * cols // P
+    xs = [torch.randn(blk, device="cuda").to(torch.bfloat16) for _ in range(P)]
+    ys = [torch.empty(blk, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    for sd, dd in ((0, 1), (1, 0)):
+        run(f"all_to_all_dims_{sd}to{dd}_p8_bf16", lambda: dt.dt_all_to_all_dims(xs, ys, rows, cols, sd, dd),
+            2 * rows * cols * 2, ["k_all_to_all_dims_wave"])
+    del xs, ys
+    torch.cuda.empty_cache()
+    xs = synth.normal_ranks(P, SHAPE, seed=0, device="cuda", dtype=torch.bfloat16)
+    shard = [torch.empty(SHAPE[0] * SHAPE[1] // P, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    run("replicate_to_shard_p8_bf16", lambda: dt.dt_replicate_to_shard(xs, shard), 2 * s_bytes, ["k_copy_segments"])
+    del shard
+    n = SHAPE[0] * SHAPE[1]
+    xo = [torch.empty(n + 8, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    yo = [torch.empty(n + 8, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    for x, src in zip(xo, xs):
+        x[1:n + 1].copy_(src.reshape(-1))
+    run("allreduce_misaligned_p8_bf16", lambda: dt.dt_allreduce([x[1:n + 1] for x in xo], [y[1:n + 1] for y in yo]),
+        2 * P * s_bytes, ["k_reduce_elems", "k_reduce_scatter_vec<1, 0, 8, 64, 1>", "k_gather<8, true, 1, 64>"])
+    del xs, xo, yo
     torch.cuda.empty_cache()
     a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
