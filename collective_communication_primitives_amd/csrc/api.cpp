@@ -255,55 +255,88 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
     return DT_OK;
 }
 
-// Bytes to peel off the front of every send and recv buffer so that the
-// fold kernels' tiles start on a 128-byte line: every buffer shares one
-// offset within a line, and `stride` (the bytes between the starts of the
-// ranges one launch folds, e.g. ReduceScatter chunks; 0 for none) keeps it.
-// Failing that, the bytes up to the next 16-byte boundary when every buffer
-// shares its offset within a vector.  0 when none of these applies or the
-// buffers are line-aligned already.
-size_t peel_bytes(const void* const* send, void* const* recv, int nranks, size_t stride) {
-    const uintptr_t line = reinterpret_cast<uintptr_t>(send[0]) & 127;
-    bool same_line = stride % 128 == 0, same_vec = stride % 16 == 0;
-    for (int r = 0; r < nranks; r++) {
-        const uintptr_t s = reinterpret_cast<uintptr_t>(send[r]), d = reinterpret_cast<uintptr_t>(recv[r]);
-        same_line = same_line && (s & 127) == line && (d & 127) == line;
-        same_vec = same_vec && (s & 15) == (line & 15) && (d & 15) == (line & 15);
-    }
-    if (same_line) return line ? 128 - line : 0;
-    if (same_vec && (line & 15) != 0) return 16 - (line & 15);
+// Bytes to peel off the front of every send and recv buffer of a fold whose
+// buffers are not 128-byte aligned, so that the vector kernels' tiles start
+// on an alignment boundary: the largest grain of 4096, 1024 or 128 bytes at
+// which every buffer shares one offset and `stride` (the bytes between the
+// starts of the ranges one launch folds, e.g. ReduceScatter chunks; 0 for
+// none) keeps it; failing that, the bytes up to the next 16-byte boundary
+// when every buffer shares its offset within a vector.  0 when none of these
+// applies or the buffers are line-aligned already, except that with
+// `to_tile`, line-aligned buffers that share a nonzero offset within 1 KiB
+// (the fold kernels' tile) peel up to the next 1 KiB boundary.  Tiles that
+// straddle 1 KiB boundaries cost the two-shot AllReduce 4-6% (P=8 bf16 at
+// 128 MiB per rank, in-process A/B: buffers at 128 to 512 bytes past a
+// 1 KiB boundary 0.753-0.761 of peak, at 0, 1 or 2 KiB 0.799-0.805); the
+// 1 KiB peel wins that back less its element launch (0.781-0.785), but
+// costs the one-shot kernel 1-4%.
+size_t peel_bytes(const void* const* send, void* const* recv, int nranks, size_t stride, bool to_tile = false) {
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(send[0]);
+    auto shared = [&](uintptr_t grain) {
+        if (stride % grain != 0) return false;
+        for (int r = 0; r < nranks; r++)
+            if ((reinterpret_cast<uintptr_t>(send[r]) & (grain - 1)) != (s0 & (grain - 1)) ||
+                (reinterpret_cast<uintptr_t>(recv[r]) & (grain - 1)) != (s0 & (grain - 1)))
+                return false;
+        return true;
+    };
+    if (shared(128) && (s0 & 127) == 0)
+        return to_tile && shared(1024) && (s0 & 1023) != 0 ? size_t(1024 - (s0 & 1023)) : 0;
+    for (const uintptr_t grain : {uintptr_t(4096), uintptr_t(1024), uintptr_t(128)})
+        if (shared(grain)) return size_t(grain - (s0 & (grain - 1)));
+    if (shared(16) && (s0 & 15) != 0) return size_t(16 - (s0 & 15));
     return 0;
 }
 
-// Validated AllReduce over one contiguous range per rank: window by window
-// where allreduce_window says so, else in one call.  When every buffer sits
-// at the same offset within a cache line (or a vector), the elements up to
-// the next boundary go to the element path and the rest, now aligned, the
-// usual way.
+dt_status allreduce_windows(const void* const* send, void* const* recv, int nranks, size_t count, dt_dtype dtype,
+                            dt_op op, hipStream_t stream);
+
+// Validated AllReduce over one contiguous range per rank.  When every buffer
+// sits at the same offset past an alignment boundary (peel_bytes), the whole
+// vectors from that boundary on take the vector path (allreduce_windows) and
+// the elements before it, with the ragged end, one element launch.
 dt_status allreduce_impl(const void* const* send, void* const* recv, int nranks, size_t count, dt_dtype dtype,
                          dt_op op, hipStream_t stream) {
-    const size_t es = esize_of(dtype);
-    const size_t peel = peel_bytes(send, recv, nranks, 0);
+    const size_t es = esize_of(dtype), v = vec_elems(dtype);
+    const uint64_t bytes = uint64_t(count) * es;
+    const bool two_shot = two_shot_pays(nranks, bytes) || allreduce_window(nranks, bytes) != 0;
+    const size_t peel = peel_bytes(send, recv, nranks, 0, two_shot);
     if (peel != 0) {
         const size_t h = peel / es;  // a whole number of elements for element-aligned buffers
         if (count > h && peel % es == 0) {
-            dt::ReduceArgs a = {};
+            // the whole vectors after the head on the vector path; the head
+            // and the ragged end together in one element launch (each
+            // extra launch here cost 2-3% of the AllReduce at 128 MiB)
+            const size_t body = (count - h) / v * v;
             const void* s[dt::kMaxRanksHost];
             void* d[dt::kMaxRanksHost];
+            dt::ReduceArgs a = {};
             for (int r = 0; r < nranks; r++) {
                 a.src[r] = send[r];
                 a.dst[r] = recv[r];
                 s[r] = cptr(send[r]) + h * es;
                 d[r] = static_cast<char*>(recv[r]) + h * es;
             }
+            if (body != 0) {
+                const dt_status st = allreduce_windows(s, d, nranks, body, dtype, op, stream);
+                if (st != DT_OK) return st;
+            }
             a.nranks = nranks;
             a.first = 0;
             a.count = h;
-            dt_status st = check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "allreduce (head) launch");
-            if (st != DT_OK) return st;
-            return allreduce_impl(s, d, nranks, count - h, dtype, op, stream);
+            a.first2 = h + body;
+            a.count2 = count - h - body;
+            return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "allreduce (head and tail) launch");
         }
     }
+    return allreduce_windows(send, recv, nranks, count, dtype, op, stream);
+}
+
+// The AllReduce of buffers that need no peel: window by window where
+// allreduce_window says so, else in one call.
+dt_status allreduce_windows(const void* const* send, void* const* recv, int nranks, size_t count, dt_dtype dtype,
+                            dt_op op, hipStream_t stream) {
+    const size_t es = esize_of(dtype);
     const uint64_t win = allreduce_window(nranks, uint64_t(count) * es);
     if (win == 0) return allreduce_one(send, recv, nranks, count, dtype, op, stream);
     const size_t win_elems = size_t(win / es);  // whole vectors: every window keeps each buffer's alignment
@@ -688,10 +721,6 @@ dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nran
     const size_t peel = peel_bytes(send, recv, nranks, recvcount * es);
     const size_t h = peel / es;
     if (peel != 0 && peel % es == 0 && recvcount >= h + v) {
-        a.first = 0;
-        a.count = h;
-        if ((st = check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "reduce_scatter (head) launch")) != DT_OK)
-            return st;
         dt::ReduceArgs body = a;
         for (int r = 0; r < nranks; r++) {
             body.src[r] = cptr(send[r]) + h * es;
@@ -701,10 +730,11 @@ dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nran
         body.chunk_stride = recvcount / v;
         if ((st = check_hip(dt::launch_reduce_vec(body, dtype, op, stream), "reduce_scatter (body) launch")) != DT_OK)
             return st;
-        a.first = h + body.count * v;
-        a.count = recvcount - a.first;
-        if (a.count == 0) return DT_OK;
-        return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "reduce_scatter (tail) launch");
+        a.first = 0;  // the head and the ragged end of every chunk, one launch
+        a.count = h;
+        a.first2 = h + body.count * v;
+        a.count2 = recvcount - a.first2;
+        return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "reduce_scatter (head and tail) launch");
     }
     a.first = 0;
     a.count = recvcount;

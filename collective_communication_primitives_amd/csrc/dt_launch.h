@@ -17,6 +17,8 @@ struct ReduceArgs {
     void* dst[kMaxRanksHost];
     uint64_t first;        // first element handled by this launch (element path)
     uint64_t count;        // elements per chunk handled by this launch (vector path: vectors)
+    uint64_t first2;       // element path: a second range [first2, first2 + count2) in the same
+    uint64_t count2;       //   launch (a misaligned buffer's head and ragged tail together)
     uint64_t last_count;   // vector ReduceScatter: vectors of the last chunk (<= count)
     uint64_t chunk_stride; // vector ReduceScatter: vectors between chunk starts in each input (>= count)
     uint64_t chunk_elems;  // ReduceScatter: elements per output chunk

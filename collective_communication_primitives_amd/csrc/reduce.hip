@@ -119,15 +119,17 @@ __global__ __launch_bounds__(BLOCK) void k_reduce_scatter_vec(ReduceArgs a) {
 }
 
 // Element-wise path for ragged tails and unaligned buffers.  Elements
-// [a.first, a.first + a.count) of chunk blockIdx.y.
+// [a.first, a.first + a.count) and [a.first2, a.first2 + a.count2) of chunk
+// blockIdx.y.
 template <int DT, int OP>
 __global__ __launch_bounds__(kBlock) void k_reduce_elems(ReduceArgs a) {
     const uint64_t chunk = a.rs ? blockIdx.y : 0;
     const uint64_t in_base = chunk * a.chunk_elems;
     const int nr = a.nranks;
-    for (uint64_t i = uint64_t(blockIdx.x) * kBlock + threadIdx.x; i < a.count;
+    const uint64_t total = a.count + a.count2;
+    for (uint64_t i = uint64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
          i += uint64_t(gridDim.x) * kBlock) {
-        const uint64_t e = a.first + i;
+        const uint64_t e = i < a.count ? a.first + i : a.first2 + (i - a.count);
         if (a.rs) {
             fold_elem<DT, OP>(a.src, nr, in_base + e, a.dst[chunk], e);
         } else {
@@ -398,8 +400,9 @@ hipError_t reduce_vec_dt(const ReduceArgs& a, int op, hipStream_t s) {
 
 template <int DT, int OP>
 hipError_t reduce_elems_op(const ReduceArgs& a, hipStream_t s) {
-    if (a.count == 0) return hipSuccess;
-    uint64_t blocks = (a.count + kBlock - 1) / kBlock;
+    const uint64_t total = a.count + a.count2;
+    if (total == 0) return hipSuccess;
+    uint64_t blocks = (total + kBlock - 1) / kBlock;
     if (blocks > 8192) blocks = 8192;
     dim3 grid(unsigned(blocks), a.rs ? unsigned(a.nranks) : 1u);
     k_reduce_elems<DT, OP><<<grid, kBlock, 0, s>>>(a);

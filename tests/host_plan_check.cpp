@@ -190,16 +190,22 @@ hipError_t launch_reduce_vec(const ReduceArgs& a, int, int, hipStream_t) {
 hipError_t launch_reduce_elems(const ReduceArgs& a, int dtype, int, hipStream_t) {
     g_launches++;
     const size_t es = esize(dtype);
-    log_fold(static_cast<const char*>(a.dst[0]) + a.first * es, a.count * es);
-    for (int r = 0; r < a.nranks; r++) {
-        if (a.rs) {
-            for (int c = 0; c < a.nranks; c++)
-                touch(a.src[r], (c * a.chunk_elems + a.first) * es, a.count * es, false, "reduce_elems read");
-        } else {
-            touch(a.src[r], a.first * es, a.count * es, false, "reduce_elems read");
+    const uint64_t firsts[2] = {a.first, a.first2}, counts[2] = {a.count, a.count2};
+    for (int k = 0; k < 2; k++) {  // the launch's two element ranges
+        const uint64_t first = firsts[k], count = counts[k];
+        if (count == 0) continue;
+        log_fold(static_cast<const char*>(a.dst[0]) + first * es, count * es);
+        for (int r = 0; r < a.nranks; r++) {
+            if (a.rs) {
+                for (int c = 0; c < a.nranks; c++)
+                    touch(a.src[r], (c * a.chunk_elems + first) * es, count * es, false, "reduce_elems read");
+            } else {
+                touch(a.src[r], first * es, count * es, false, "reduce_elems read");
+            }
+            touch(a.dst[r], first * es, count * es, true, "reduce_elems write");
         }
-        touch(a.dst[r], a.first * es, a.count * es, true, "reduce_elems write");
     }
+    CHECK(a.count2 == 0 || a.first2 >= a.first + a.count, "reduce_elems: ranges overlap or out of order");
     return hipSuccess;
 }
 
@@ -942,7 +948,8 @@ void two_shot() {
         dt_dtype dtype;
         size_t count;
         bool in_place;
-        int windows;  // two-shot windows expected (0: one-shot only)
+        int windows;     // two-shot windows expected (0: one-shot only)
+        size_t skew = 0; // bytes past a 4 KiB boundary, the same for every buffer: a peeled head
     };
     const size_t M = size_t(1) << 20;
     const Case cases[] = {
@@ -975,6 +982,13 @@ void two_shot() {
         {6, DT_FLOAT32, 48 * M, false, 1},            // 192 MiB at P=6: two-shot
         {6, DT_FLOAT32, 4 * M, false, 0},             // 16 MiB at P=6: one-shot
         {7, DT_FLOAT32, 96 * M + 4, false, 3},        // 384 MiB + 16 B at P=7: three 128 MiB windows, a one-shot tail
+        {8, DT_BFLOAT16, 64 * M, false, 1, 2},        // 2 bytes off: a 4094-byte head, a ragged end, one element launch
+        {8, DT_BFLOAT16, 64 * M + 3, true, 1, 130},   // in place, 130 bytes off
+        {16, DT_FLOAT32, 96 * M + 64, false, 6, 12},  // windows after a peeled head
+        {5, DT_INT32, 40 * M, false, 1, 1028},        // 1028 bytes off: the 4 KiB grain
+        {8, DT_BFLOAT16, 64 * M, false, 1, 512},      // line-aligned, 512 bytes into a 1 KiB tile: a 1 KiB peel
+        {16, DT_FLOAT32, 96 * M, true, 6, 256},       // the same before windows, in place
+        {4, DT_FLOAT32, 16 * M, false, 0, 512},       // one-shot: no peel for line-aligned buffers
     };
     char* base = reinterpret_cast<char*>(uintptr_t(1) << 45);  // fake, never dereferenced
     for (const Case& c : cases) {
@@ -983,12 +997,12 @@ void two_shot() {
         const void* send[16];
         void* recv[16];
         for (int r = 0; r < c.p; r++) {
-            recv[r] = base + (uint64_t(r) << 33);
+            recv[r] = base + (uint64_t(r) << 33) + c.skew;
             reg(recv[r], bytes, true);
             if (c.in_place) {
                 send[r] = recv[r];
             } else {
-                send[r] = base + (uint64_t(32 + r) << 33);
+                send[r] = base + (uint64_t(32 + r) << 33) + c.skew;
                 reg(send[r], bytes, false);
             }
         }

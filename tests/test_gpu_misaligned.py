@@ -164,3 +164,54 @@ def test_replicate_to_shard_misaligned(dt, orc):
     for r in range(p):
         ys[r].check()
         assert np.array_equal(to_np(ys[r].t), want[r]), f"rank {r}"
+
+
+def _carved(p, n, dtype, off_bytes):
+    """p views of n elements in one allocation, each off_bytes past a 1 KiB
+    (in fact 4 KiB) boundary: every buffer shares its offset modulo 4 KiB,
+    which selects the deeper peels.  Returns (views, the whole allocation)."""
+    es = torch.tensor([], dtype=dtype).element_size()
+    stride = -(-(n * es + off_bytes + 4096) // 4096) * 4096  # bytes between view starts, a 4 KiB multiple
+    big = torch.empty(p * stride + 8192, dtype=torch.uint8, device="cuda")
+    big.fill_(0xA5)
+    lead = (-big.data_ptr()) % 4096
+    views = [big[lead + q * stride + off_bytes:lead + q * stride + off_bytes + n * es].view(dtype) for q in range(p)]
+    return views, big
+
+
+@pytest.mark.parametrize("p,dtype,n,off,in_place", [
+    (8, torch.bfloat16, 64 << 20, 512, False),      # line-aligned, half a tile in: the 1 KiB peel before the two-shot
+    (16, torch.float32, 96 << 20, 256, True),       # the same before 64 MiB windows, in place
+    (8, torch.bfloat16, (64 << 20) + 5, 2, False),  # 2 bytes off, shared within 4 KiB: the 4 KiB peel, a ragged end
+    (4, torch.float32, 4 << 20, 512, False),        # one-shot size: no peel for line-aligned buffers
+])
+def test_allreduce_shared_offset_peels(dt, p, dtype, n, off, in_place):
+    note(f"allreduce carved views P={p} {dtype} n={n} off={off} in_place={in_place}")
+    xs, xbig = _carved(p, n, dtype, off)
+    src = (synth.normal_ranks(p, (n,), seed=11 + p, device="cuda", dtype=dtype) if dtype == torch.bfloat16
+           else synth.uniform_ranks(p, n, seed=11 + p, device="cuda"))
+    for x, s in zip(xs, src):
+        x.copy_(s)
+    if in_place:
+        ys, ybig = xs, xbig
+    else:
+        ys, ybig = _carved(p, n, dtype, off)
+    outside = ybig.clone()
+    dt.dt_allreduce(xs, ys)
+    torch.cuda.synchronize()
+    orc_omp = oracle.get_omp()
+    step = 1 << 26
+    for a in range(0, n, step):
+        b = min(n, a + step)
+        want = orc_omp.allreduce([to_np(s[a:b]) for s in src], "sum")[0]
+        compare(to_np(ys[0][a:b]), want, f"rank 0 elements [{a}, {b})")
+    view = (lambda t: t.view(torch.int16)) if dtype == torch.bfloat16 else (lambda t: t.view(torch.int32))
+    for q in range(1, p):
+        assert torch.equal(view(ys[q]), view(ys[0])), f"rank {q} differs from rank 0"
+    # nothing outside the outputs was written: every gap between them unchanged
+    base = ybig.data_ptr()
+    spans = sorted((y.data_ptr() - base, y.data_ptr() - base + y.numel() * y.element_size()) for y in ys)
+    at = 0
+    for lo, hi in spans + [(ybig.numel(), ybig.numel())]:
+        assert torch.equal(ybig[at:lo], outside[at:lo]), f"bytes [{at}, {lo}) outside the outputs changed"
+        at = hi
