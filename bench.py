@@ -611,7 +611,7 @@ def other_rows(dt, torch, steps: int, warmup: int):
     return out
 
 
-def overlap(dt, torch, reps: int = 12):
+def overlap(dt, torch, reps: int = 40):
     """Compute/communication overlap on one GPU, after the probe of the c10d
     page (sec. 6, sec. 10.4): a bf16 [8192,8192] x [8192,8192] GEMM
     (torch.matmul, a library GEMM) on the compute stream and the fp32 25 MiB
@@ -632,6 +632,9 @@ def overlap(dt, torch, reps: int = 12):
     ys = [torch.empty_like(x) for x in xs]
     a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
     b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    # the "previous layer" for the .item() killer: a GEMM still queued on the
+    # compute stream when the host reads a scalar it produces (a loss)
+    pa = torch.randn(4096, 4096, device="cuda").to(torch.bfloat16)
     comp, side = torch.cuda.current_stream(), dt.side_stream()
 
     def ev():
@@ -672,8 +675,9 @@ def overlap(dt, torch, reps: int = 12):
             comp.wait_stream(side)
             gemm()
         elif order == "item":
+            loss = torch.matmul(pa, pa)[0, 0]  # queued on the compute stream before the AllReduce
             ar()
-            xs[0][0].item()
+            loss.item()  # the host waits for that GEMM before it can issue the next one
             gemm()
         elif order == "sync":
             ar()
@@ -711,7 +715,9 @@ def overlap(dt, torch, reps: int = 12):
     t_g, t_a = med["gemm"]["span_ms"], med["ar"]["span_ms"]
     out = {"gemm_ms": t_g, "allreduce_ms": t_a, "gemm_tflops": round(2 * 8192 ** 3 / (t_g * 1e-3) / 1e12, 1)}
     for o in ("ar_first", "gemm_first") + killers:
-        out[o] = dict(med[o], overlap=round((t_g + t_a - med[o]["span_ms"]) / min(t_g, t_a), 3))
+        per = [(t_g + t_a - r["span_ms"]) / min(t_g, t_a) for r in samples[o]]
+        out[o] = dict(med[o], overlap=round((t_g + t_a - med[o]["span_ms"]) / min(t_g, t_a), 3),
+                      overlap_p25_p75=[round(pct(per, 0.25), 3), round(pct(per, 0.75), 3)])
     print(json.dumps({"overlap": out}), flush=True)
     return out
 
