@@ -545,7 +545,10 @@ class HSDPPipeline:
     one.  With every rank on one device both phases draw on the same HBM, and
     issuing them back to back on one stream, in the same order, measured 4%
     faster (30.5 vs 31.8 ms for the 32-layer workload), so one side stream
-    for both is the default; pass two streams for the split layout.
+    for both is the default; pass two streams for the split layout, or the
+    stream that produces the gradients as both, for a pipeline without
+    cross-stream events (its collectives then queue behind the producer's
+    work, in order).
 
     A layer's fused buffers must not be passed again (as the next layer's)
     before ``finish()``: the previous layer's AllReduce is still pending on

@@ -1328,6 +1328,9 @@ namespace {
 // "wait prev RS": the AllReduce stream waits for the previous layer's
 // ReduceScatter.  Queued before the current layer re-records anything.
 dt_status hsdp_wait_prev_rs(dt_hsdp* h) {
+    // on one stream the order of issue already puts the ReduceScatter first;
+    // a wait there would only add a barrier packet (and its gap) to the queue
+    if (h->ar_stream == h->rs_stream) return DT_OK;
     return check_hip(hipStreamWaitEvent(h->ar_stream, h->rs_done[h->prev_slot], 0), "AR stream waits prev RS");
 }
 
@@ -1451,9 +1454,11 @@ dt_status dt_hsdp_post_backward(dt_hsdp* h, const void* const* grads, const size
     if (h->has_prev && (st = hsdp_wait_prev_rs(h)) != DT_OK) return st;
     // 2. issue this layer's ReduceScatter, after everything the producer
     //    queued: tensor t of shard group i lands in fused[r] at offset `at`
-    if ((st = check_hip(hipEventRecord(h->produced, producer), "record producer")) != DT_OK) return st;
-    if ((st = check_hip(hipStreamWaitEvent(h->rs_stream, h->produced, 0), "RS stream waits producer")) != DT_OK)
-        return st;
+    if (producer != h->rs_stream) {  // on the producer's own stream the order already holds
+        if ((st = check_hip(hipEventRecord(h->produced, producer), "record producer")) != DT_OK) return st;
+        if ((st = check_hip(hipStreamWaitEvent(h->rs_stream, h->produced, 0), "RS stream waits producer")) != DT_OK)
+            return st;
+    }
     // every tensor of every shard group is one segment of one launch
     std::vector<std::vector<const void*>> seg_src;
     std::vector<std::vector<void*>> seg_dst;

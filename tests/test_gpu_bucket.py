@@ -156,11 +156,14 @@ def test_bucket_one_layer_full_size(dt, orc):
 
 
 # ------------------------------------------------------------------ HSDP --
-def run_pipeline(dt, layers, rep, sh, bucket, shapes, one_stream=False):
+def run_pipeline(dt, layers, rep, sh, bucket, shapes, one_stream=False, producer_stream=False):
     """Backward order: last layer first.  Returns fused buffers per layer."""
     p = rep * sh
     numels = [int(np.prod(s)) for s in shapes]
-    if one_stream:
+    if producer_stream:  # both phases on the stream that produced the gradients: no events at all
+        cur = torch.cuda.current_stream()
+        pipe = dt.HSDPPipeline(rep, sh, bucket_bytes=bucket, rs_stream=cur, ar_stream=cur)
+    elif one_stream:
         pipe = dt.HSDPPipeline(rep, sh, bucket_bytes=bucket)  # the default: one side stream for both phases
     else:
         pipe = dt.HSDPPipeline(rep, sh, bucket_bytes=bucket, rs_stream=torch.cuda.Stream(),
@@ -173,16 +176,17 @@ def run_pipeline(dt, layers, rep, sh, bucket, shapes, one_stream=False):
     return fused, numels
 
 
-@pytest.mark.parametrize("one_stream", [False, True])
+@pytest.mark.parametrize("streams", ["two", "one", "producer"])
 @pytest.mark.parametrize("rep,sh", [(2, 4), (8, 1), (1, 8), (2, 2), (4, 2)])
-def test_hsdp_pipeline_small(dt, orc, rep, sh, one_stream):
+def test_hsdp_pipeline_small(dt, orc, rep, sh, streams):
     p = rep * sh
     shapes = [(16, 24), (40, 8), (8,), (24, 16)]
     nl = 5
-    note(f"hsdp pipeline small R={rep} S={sh} layers={nl} one_stream={one_stream}")
+    note(f"hsdp pipeline small R={rep} S={sh} layers={nl} streams={streams}")
     layers = [[[synth.normal_ranks(1, s, seed=(l * 64 + r) * 16 + t, device="cuda")[0] for t, s in enumerate(shapes)]
                for r in range(p)] for l in range(nl)]
-    fused, numels = run_pipeline(dt, layers, rep, sh, bucket=96, shapes=shapes, one_stream=one_stream)
+    fused, numels = run_pipeline(dt, layers, rep, sh, bucket=96, shapes=shapes, one_stream=streams == "one",
+                                 producer_stream=streams == "producer")
     torch.cuda.synchronize()
     for l in range(nl):
         host = [[to_np(g) for g in rank] for rank in layers[l]]
