@@ -1336,7 +1336,7 @@ dt_status hsdp_wait_prev_rs(dt_hsdp* h) {
 
 // "issue prev AR": the previous layer's fused buffers, AllReduced in place
 // inside each replicate group {j, shard+j, ...}, bucket by bucket.
-dt_status hsdp_issue_prev_allreduce(dt_hsdp* h) {
+dt_status hsdp_issue_prev_allreduce(dt_hsdp* h, bool last) {
     dt_status st;
     const size_t es = esize_of(h->dtype);
     const size_t per_bucket = h->bucket_bytes / es;
@@ -1371,6 +1371,10 @@ dt_status hsdp_issue_prev_allreduce(dt_hsdp* h) {
                 return st;
         }
     }
+    h->has_prev = false;
+    // on one stream only the last AllReduce of a pass needs an end event: the
+    // stream's order covers the ones before it (each record is a queue entry)
+    if (h->ar_stream == h->rs_stream && !last) return DT_OK;
     hipEvent_t ev = nullptr;
     if (!h->spare.empty()) {
         ev = h->spare.back();
@@ -1379,7 +1383,6 @@ dt_status hsdp_issue_prev_allreduce(dt_hsdp* h) {
         return st;
     }
     h->ar_done.push_back(ev);
-    h->has_prev = false;
     return check_hip(hipEventRecord(ev, h->ar_stream), "record AR done");
 }
 
@@ -1483,9 +1486,12 @@ dt_status dt_hsdp_post_backward(dt_hsdp* h, const void* const* grads, const size
     if ((st = reduce_scatter_segments(seg_src, seg_dst, seg_m, h->shard, h->dtype, h->op, h->rs_stream)) != DT_OK)
         return st;
     const int cur_slot = h->prev_slot ^ 1;
-    if ((st = check_hip(hipEventRecord(h->rs_done[cur_slot], h->rs_stream), "record RS done")) != DT_OK) return st;
+    // the AllReduce stream's wait for this ReduceScatter (one stream: its order)
+    if (h->ar_stream != h->rs_stream &&
+        (st = check_hip(hipEventRecord(h->rs_done[cur_slot], h->rs_stream), "record RS done")) != DT_OK)
+        return st;
     // 3. issue the previous layer's fused AllReduce (its wait is queued above)
-    if (h->has_prev && (st = hsdp_issue_prev_allreduce(h)) != DT_OK) return st;
+    if (h->has_prev && (st = hsdp_issue_prev_allreduce(h, false)) != DT_OK) return st;
     // this layer becomes the previous one
     h->prev_slot = cur_slot;
     if (fused)
@@ -1503,10 +1509,12 @@ dt_status dt_hsdp_finish(dt_hsdp* h, hipStream_t consumer) {
     dt_status st;
     if (h->has_prev) {  // drain: the last layer's RS, then its fused AllReduce
         if ((st = hsdp_wait_prev_rs(h)) != DT_OK) return st;
-        if ((st = hsdp_issue_prev_allreduce(h)) != DT_OK) return st;
+        if ((st = hsdp_issue_prev_allreduce(h, true)) != DT_OK) return st;
     }
     for (hipEvent_t ev : h->ar_done) {
-        if ((st = check_hip(hipStreamWaitEvent(consumer, ev, 0), "consumer waits AR")) != DT_OK) return st;
+        if (consumer != h->ar_stream &&
+            (st = check_hip(hipStreamWaitEvent(consumer, ev, 0), "consumer waits AR")) != DT_OK)
+            return st;
         h->spare.push_back(ev);
     }
     h->ar_done.clear();
@@ -1526,7 +1534,9 @@ dt_status dt_hsdp_destroy(dt_hsdp* h) {
     if (h->produced) (void)hipEventDestroy(h->produced);
     // a layer posted but never finished still has its ReduceScatter writing
     // the caller's fused buffers: wait for it before the caller may free them
-    // (its AllReduce is dropped, not queued)
+    // (its AllReduce is dropped, not queued); on one stream, whose unfinished
+    // work carries no events, wait for the stream
+    if (h->ar_stream == h->rs_stream) (void)hipStreamSynchronize(h->rs_stream);
     for (hipEvent_t ev : h->rs_done)
         if (ev) {
             (void)hipEventSynchronize(ev);

@@ -24,6 +24,7 @@
 #include <algorithm>
 #include <map>
 #include <random>
+#include <set>
 #include <vector>
 
 #include "dt.h"
@@ -99,18 +100,25 @@ hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, int) {
     return hipSuccess;
 }
 const char* hipGetErrorString(hipError_t) { return "stand-in"; }
+// Events the library has recorded since they were created: a stream wait on
+// one it never recorded would order nothing, a planning bug.
+std::set<hipEvent_t> g_recorded;
 hipError_t hipEventCreateWithFlags(hipEvent_t* e, unsigned) {
     *e = reinterpret_cast<hipEvent_t>(malloc(64));
+    g_recorded.erase(*e);
     return hipSuccess;
 }
 hipError_t hipEventDestroy(hipEvent_t e) {
+    g_recorded.erase(e);
     free(e);
     return hipSuccess;
 }
 hipError_t hipEventRecord(hipEvent_t e, hipStream_t) {
     CHECK(e != nullptr, "record on a null event");
+    g_recorded.insert(e);
     return hipSuccess;
 }
+hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 hipError_t hipEventQuery(hipEvent_t e) {
     CHECK(e != nullptr, "query of a null event");
     return hipSuccess;
@@ -121,6 +129,7 @@ hipError_t hipEventSynchronize(hipEvent_t e) {
 }
 hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t e, unsigned) {
     CHECK(e != nullptr, "wait on a null event");
+    CHECK(g_recorded.count(e) == 1, "a stream waits on an event that was never recorded");
     return hipSuccess;
 }
 }
@@ -716,8 +725,15 @@ void hsdp_and_sync() {
         const int rep = mesh[0], sh = mesh[1], p = rep * sh;
         const dt_dtype dtype = DT_BFLOAT16;
         const size_t es = 2;
+        // stream layouts (fake handles, never dereferenced): everything on one
+        // stream; one side stream apart from the producer; two side streams
+        const hipStream_t s1 = reinterpret_cast<hipStream_t>(uintptr_t(0x1000)),
+                          s2 = reinterpret_cast<hipStream_t>(uintptr_t(0x2000)),
+                          s3 = reinterpret_cast<hipStream_t>(uintptr_t(0x3000));
+        const hipStream_t layouts[3][3] = {{nullptr, nullptr, nullptr}, {s1, s1, s3}, {s1, s2, s3}};
+        for (const auto& lay : layouts) {
         dt_hsdp* h = nullptr;
-        expect(dt_hsdp_create(rep, sh, 16 * (1 + below(100)), dtype, DT_SUM, nullptr, nullptr, &h), DT_OK, "hsdp");
+        expect(dt_hsdp_create(rep, sh, 16 * (1 + below(100)), dtype, DT_SUM, lay[0], lay[1], &h), DT_OK, "hsdp");
         for (int layer = 0; layer < 5; layer++) {
             const int nt = 1 + int(below(9));
             std::vector<size_t> numels(nt);
@@ -728,11 +744,12 @@ void hsdp_and_sync() {
                 for (int t = 0; t < nt; t++) grads[r * nt + t] = numels[t] ? pool.get(numels[t] * es, 0, false) : nullptr;
                 fused[r] = pool.get(total / sh * es, 0, true);
             }
-            expect(dt_hsdp_post_backward(h, grads.data(), numels.data(), nt, fused.data(), nullptr), DT_OK,
+            expect(dt_hsdp_post_backward(h, grads.data(), numels.data(), nt, fused.data(), lay[2]), DT_OK,
                    "hsdp post_backward");
         }
-        expect(dt_hsdp_finish(h, nullptr), DT_OK, "hsdp finish");
+        expect(dt_hsdp_finish(h, lay[2]), DT_OK, "hsdp finish");
         expect(dt_hsdp_destroy(h), DT_OK, "hsdp destroy");
+        }
 
         // barrier and exchange
         std::vector<int32_t*> win(p);

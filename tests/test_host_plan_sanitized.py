@@ -88,6 +88,8 @@ MUTANTS = {
     "dims_extra_run": ("a.nruns = uint64_t(rows) * P;", "a.nruns = uint64_t(rows) * P + 1;"),
     "gather_tile_shape_mismatch": ("a.tile_bytes = uint32_t(tile_bytes);", "a.tile_bytes = uint32_t(dt::kGatherWaveTileBytes);"),
     "elems_second_range_dropped": ("            a.count2 = count - h - body;", "            a.count2 = 0;"),
+    "hsdp_rs_done_never_recorded": ("    if (h->ar_stream != h->rs_stream &&\n        (st = check_hip(hipEventRecord(h->rs_done[cur_slot]",
+                                    "    if (false &&\n        (st = check_hip(hipEventRecord(h->rs_done[cur_slot]"),
     "dims_wave_tiles_short": ("a.tiles_per_run = uint32_t((run_bytes + dt::kDimsWaveTileBytes - 1) / dt::kDimsWaveTileBytes);",
                               "a.tiles_per_run = uint32_t(run_bytes / dt::kDimsWaveTileBytes);"),
     # every piece claimed 16-byte aligned
