@@ -215,3 +215,34 @@ def test_allreduce_shared_offset_peels(dt, p, dtype, n, off, in_place):
     for lo, hi in spans + [(ybig.numel(), ybig.numel())]:
         assert torch.equal(ybig[at:lo], outside[at:lo]), f"bytes [{at}, {lo}) outside the outputs changed"
         at = hi
+
+
+@pytest.mark.parametrize("p,dtype,m,off", [
+    (8, torch.bfloat16, 8 << 20, 2),        # 2 bytes past a 4 KiB boundary in every buffer: the 4 KiB peel
+    (4, torch.float32, (1 << 20) + 256, 516),  # 516 bytes, chunks 4 MiB + 1 KiB apart: the 1 KiB peel, a ragged end
+])
+def test_reduce_scatter_shared_offset_peels(dt, p, dtype, m, off):
+    """ReduceScatter on views that all sit at one offset past a 4 KiB boundary
+    (inputs and outputs carved from single allocations): the head and the
+    ragged end of every chunk go out in one element launch, the body on the
+    vector kernel.  Compared with the oracle element by element; the bytes
+    around the outputs stay untouched."""
+    note(f"reduce_scatter carved views P={p} {dtype} m={m} off={off}")
+    xs, _ = _carved(p, p * m, dtype, off)
+    src = (synth.normal_ranks(p, (p * m,), seed=21 + p, device="cuda", dtype=dtype) if dtype == torch.bfloat16
+           else synth.uniform_ranks(p, p * m, seed=21 + p, device="cuda"))
+    for x, s in zip(xs, src):
+        x.copy_(s)
+    ys, ybig = _carved(p, m, dtype, off)
+    outside = ybig.clone()
+    dt.dt_reduce_scatter(xs, ys)
+    torch.cuda.synchronize()
+    want = oracle.get_omp().reduce_scatter([to_np(s) for s in src], "sum")
+    for r in range(p):
+        compare(to_np(ys[r]), want[r], f"rank {r}")
+    base = ybig.data_ptr()
+    spans = sorted((y.data_ptr() - base, y.data_ptr() - base + y.numel() * y.element_size()) for y in ys)
+    at = 0
+    for lo, hi in spans + [(ybig.numel(), ybig.numel())]:
+        assert torch.equal(ybig[at:lo], outside[at:lo]), f"bytes [{at}, {lo}) outside the outputs changed"
+        at = hi
