@@ -33,11 +33,15 @@
  *    allowed where a call says so); DT_ERR_HIP when a launch fails.  Nothing throws across
  *    the ABI; dt_last_error() gives this thread's last message.
  *  - Fast path: 16-byte aligned buffers and offsets.  A fold whose buffers
- *    are all off alignment by the same amount folds the elements up to the
- *    next 16-byte boundary element by element and the rest the fast way; the
- *    copy engines build aligned stores from aligned loads whatever the source
- *    offset (the fan-out when all destinations of a piece share one
- *    misalignment).  Anything else is still correct but runs element-wise.
+ *    all sit at one offset past an alignment boundary (4 KiB, 1 KiB, 128 or
+ *    16 bytes: the deepest one they share) folds the elements before that
+ *    boundary, with the ragged end, in one element launch and the rest the
+ *    fast way; a two-shot AllReduce does the same for line-aligned buffers
+ *    that share an offset within 1 KiB (its tiles then start on 1 KiB
+ *    boundaries).  The copy engines build aligned stores from aligned loads
+ *    whatever the source offset (the fan-out when all destinations of a
+ *    piece share one offset within a 128-byte line).  Anything else is
+ *    still correct but runs element-wise.
  */
 #ifndef DT_H
 #define DT_H
