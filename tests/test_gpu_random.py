@@ -135,3 +135,62 @@ def test_random_buckets(dt, orc, case):
         for t in range(nt):
             compare(to_np(grads[r][t]), want[r][t], f"bucket rank {r} tensor {t}")
             compare(to_np(coal[r][t]), want[r][t], f"coalesced rank {r} tensor {t}")
+
+
+def _carved(p, n, dtype, off_bytes):
+    """p views of n elements cut from one allocation, each off_bytes past a
+    4 KiB boundary, the allocation filled with a canary byte: every buffer
+    shares its offset, which selects the deeper peels of the folds."""
+    es = torch.tensor([], dtype=dtype).element_size()
+    stride = -(-(n * es + off_bytes + 4096) // 4096) * 4096
+    big = torch.empty(p * stride + 8192, dtype=torch.uint8, device="cuda")
+    big.fill_(0xA5)
+    lead = (-big.data_ptr()) % 4096
+    views = [big[lead + q * stride + off_bytes:lead + q * stride + off_bytes + n * es].view(dtype) for q in range(p)]
+    return views, big
+
+
+def _outside_unchanged(views, big, before):
+    base = big.data_ptr()
+    spans = sorted((v.data_ptr() - base, v.data_ptr() - base + v.numel() * v.element_size()) for v in views)
+    at = 0
+    for lo, hi in spans + [(big.numel(), big.numel())]:
+        assert torch.equal(big[at:lo], before[at:lo]), f"bytes [{at}, {lo}) outside the outputs changed"
+        at = hi
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_shared_offsets(dt, orc, case):
+    """Every buffer at one random offset past a 4 KiB boundary (any multiple
+    of the element size below 4 KiB), random rank count, dtype, op and size,
+    a quarter of the cases large enough for the two-shot form: AllReduce
+    and ReduceScatter against the oracle, nothing written outside."""
+    rng = np.random.default_rng(9000 + case)
+    dtype = ["f32", "bf16", "i32"][case % 3]
+    es = 2 if dtype == "bf16" else 4
+    op = ["sum", "max", "min", "avg"][int(rng.integers(0, 4))]
+    if case % 4 == 3:
+        p = int(rng.choice([8, 12, 16]))
+        m = (24 << 20) // es // p + int(rng.integers(0, 4096))  # 24 MiB per rank and more: two-shot
+    else:
+        p = int(rng.integers(1, 17))
+        m = int(rng.choice([1, int(rng.integers(2, 3000)), int(rng.integers(3000, 200000))]))
+    off = int(rng.integers(0, 4096 // es)) * es
+    note(f"random shared offsets case={case} {dtype} {op} P={p} m={m} off={off}")
+    xs, _ = _carved(p, p * m, DTYPES[dtype], off)
+    for x in xs:
+        x.copy_(_data(rng, dtype, p * m))
+    host = [to_np(x) for x in xs]
+    ar, arbig = _carved(p, p * m, DTYPES[dtype], off)
+    rs, rsbig = _carved(p, m, DTYPES[dtype], off)
+    ar_before, rs_before = arbig.clone(), rsbig.clone()
+    dt.dt_allreduce(xs, ar, op=op)
+    dt.dt_reduce_scatter(xs, rs, op=op)
+    torch.cuda.synchronize()
+    want_ar = orc.allreduce(host, op)[0]
+    want_rs = orc.reduce_scatter(host, op)
+    for q in range(p):
+        compare(to_np(ar[q]), want_ar, f"AR rank {q}")
+        compare(to_np(rs[q]), want_rs[q], f"RS rank {q}")
+    _outside_unchanged(ar, arbig, ar_before)
+    _outside_unchanged(rs, rsbig, rs_before)
