@@ -396,6 +396,17 @@ dt_status reduce_scatter_segments(const std::vector<std::vector<const void*>>& s
     return flush();
 }
 
+// Workgroups per fan-out source tile, as a power of two: each writes the
+// destinations q with q mod 2^s equal to its part.  From 9 ranks on, two
+// single-wave workgroups per tile, each with half the destinations: in-process
+// A/B, P=16 fp32 AllGather 0.742 -> 0.815 of peak at 64 MiB and 0.818 ->
+// 0.843 at 256 MiB per rank, P=12 0.782 -> 0.827, the P=16 two-shot
+// AllReduce 0.749 -> 0.783 at 64 MiB and 0.748 -> 0.764 at 1 GiB; four
+// workgroups lost to two everywhere, and splitting at P=8 cost 4-17%.
+uint32_t gather_split_log2(int nranks) {
+    return nranks >= 9 ? 1u : 0u;
+}
+
 // One fan-out launch over pieces k < n: piece k is bytes[k] at src[k], going to
 // dst[k][q] for every q (host arrays, P entries each), in single-wave 1 KiB
 // tiles (`wave`) or 128-thread 2 KiB ones; a read pass (`touch_first`, 2 KiB
@@ -406,6 +417,7 @@ dt_status fan_out_launch(const void* const* src, const uint64_t* bytes, void* co
     a.nranks = nranks;
     const uint64_t tile_bytes = wave ? dt::kGatherWaveTileBytes : dt::kGatherTileBytes;
     a.tile_bytes = uint32_t(tile_bytes);
+    a.split_log2 = gather_split_log2(nranks);
     uint64_t tiles = 0;
     for (int k = 0; k < n; k++) {
         a.src[k] = src[k];
@@ -429,7 +441,7 @@ dt_status fan_out_launch(const void* const* src, const uint64_t* bytes, void* co
         } else {
             tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;
         }
-        if (tiles > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "fan-out too large for one launch");
+        if ((tiles << a.split_log2) > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "fan-out too large for one launch");
     }
     for (int k = n; k <= nranks; k++) a.tile_start[k] = uint32_t(tiles);
     if (tiles == 0) return DT_OK;

@@ -29,7 +29,11 @@ static_assert(kCopyU >= 1, "an all-to-all tile holds at least one vector per thr
 template <int PMAX, bool EXACT, int U, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
     constexpr uint64_t kTile = uint64_t(U) * BLOCK * 16;
-    const uint32_t b = blockIdx.x;
+    // 2^split_log2 workgroups share one source tile, each writing the
+    // destinations q with q mod 2^split_log2 == its part
+    const uint32_t b = blockIdx.x >> a.split_log2;
+    const int part = int(blockIdx.x & ((1u << a.split_log2) - 1u));
+    const int nparts = 1 << a.split_log2;
     const int nr = EXACT ? PMAX : a.nranks;
     int r = 0;
     while (r + 1 < nr && a.tile_start[r + 1] <= b) r++;
@@ -53,18 +57,20 @@ __global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
         const uint32_t vbytes = uint32_t(v1 * 16 - b0);
 #pragma unroll
         for (int q = 0; q < PMAX; q++) {
-            if (q < nr && dsts[q] != src) {  // an in-place piece already sits in its own slot
+            if (q < nr && (q & (nparts - 1)) == part && dsts[q] != src) {  // an in-place piece sits in its slot
                 const rsrc_t out = make_rsrc(static_cast<char*>(dsts[q]) + b0, vbytes);
 #pragma unroll
                 for (int u = 0; u < U; u++) bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * BLOCK) * 16, x[u]);
             }
         }
         const uint64_t t = v1 * 16 + threadIdx.x;  // ragged end: fewer than 16 bytes
-        if (t < b1) {
+        if (t < b1 && part == 0) {
             const char c = src[t];
             for (int q = 0; q < nr; q++)
                 if (dsts[q] != src) static_cast<char*>(dsts[q])[t] = c;
         }
+    } else if (part != 0) {
+        return;  // the shifted and byte paths run in the tile's first part only
     } else if ((a.shifted >> r) & 1u) {
         // The destinations share one offset md within a 128-byte line: tile b
         // covers bytes [b0, b0 + kTile) of their line grid, grid byte g being
@@ -221,10 +227,11 @@ __global__ __launch_bounds__(kA2AThreads) void k_all_to_all(AllToAllArgs a) {
 namespace {
 template <int PMAX, int BLOCK>
 hipError_t gather_pb(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
+    const uint32_t grid = tiles << a.split_log2;  // the host keeps tiles << split_log2 below 2^31
     if (a.nranks == PMAX)
-        k_gather<PMAX, true, kGatherU, BLOCK><<<tiles, BLOCK, 0, s>>>(a);
+        k_gather<PMAX, true, kGatherU, BLOCK><<<grid, BLOCK, 0, s>>>(a);
     else
-        k_gather<PMAX, false, kGatherU, BLOCK><<<tiles, BLOCK, 0, s>>>(a);
+        k_gather<PMAX, false, kGatherU, BLOCK><<<grid, BLOCK, 0, s>>>(a);
     return hipGetLastError();
 }
 // The two workgroup shapes, measured by in-process A/B over output placements
@@ -394,6 +401,7 @@ hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_
 hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t s) {
     if (tiles == 0) return hipSuccess;
     if (a.tile_bytes != kGatherTileBytes && a.tile_bytes != kGatherWaveTileBytes) return hipErrorInvalidValue;
+    if (a.split_log2 > 2 || (uint64_t(tiles) << a.split_log2) > 0x7FFFFFFFull) return hipErrorInvalidValue;
     const int p = a.nranks;
     return p <= 1 ? gather_p<1>(a, tiles, s) : p <= 2 ? gather_p<2>(a, tiles, s) : p <= 4 ? gather_p<4>(a, tiles, s)
            : p <= 8 ? gather_p<8>(a, tiles, s) : gather_p<16>(a, tiles, s);

@@ -85,6 +85,7 @@ struct GatherArgs {
     uint32_t shifted;      // bit r (not aligned): rank r's destinations share one offset within a
                            // 128-byte line; its tiles then follow their line grid (grid_tiles)
     uint32_t tile_bytes;   // kGatherTileBytes or kGatherWaveTileBytes: the launch's workgroup shape
+    uint32_t split_log2;   // each source tile's destinations go to 2^split_log2 workgroups (q mod 2^s)
     int nranks;
 };
 

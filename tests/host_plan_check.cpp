@@ -341,6 +341,8 @@ hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t)
 
 hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t) {
     g_launches++;
+    CHECK(a.split_log2 <= 2 && (uint64_t(tiles) << a.split_log2) <= 0x7FFFFFFFull, "gather: split %u of %u tiles",
+          a.split_log2, tiles);
     for (int r = 0; r < a.nranks; r++)
         if (a.bytes[r]) {
             g_gather_pieces.push_back(GatherPiece{static_cast<const char*>(a.src[r]), a.bytes[r],

@@ -90,6 +90,7 @@ MUTANTS = {
     "elems_second_range_dropped": ("            a.count2 = count - h - body;", "            a.count2 = 0;"),
     "hsdp_rs_done_never_recorded": ("    if (h->ar_stream != h->rs_stream &&\n        (st = check_hip(hipEventRecord(h->rs_done[cur_slot]",
                                     "    if (false &&\n        (st = check_hip(hipEventRecord(h->rs_done[cur_slot]"),
+    "gather_split_too_wide": ("    return nranks >= 9 ? 1u : 0u;", "    return nranks >= 9 ? 3u : 0u;"),
     "dims_wave_tiles_short": ("a.tiles_per_run = uint32_t((run_bytes + dt::kDimsWaveTileBytes - 1) / dt::kDimsWaveTileBytes);",
                               "a.tiles_per_run = uint32_t(run_bytes / dt::kDimsWaveTileBytes);"),
     # every piece claimed 16-byte aligned
