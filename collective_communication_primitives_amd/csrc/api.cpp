@@ -141,9 +141,14 @@ dt_status fan_out(const void* const* src, const size_t* counts, void* const* tab
 // sources (S bytes in all) are still in the 256 MB Infinity Cache when the
 // fan-out reads them.  Measured on the MI355X against the one-shot kernel
 // (in-process A/B, graph replay, fp32 unless noted):
-//   P = 16: 4-10% faster from 16 MiB per rank up;
+//   P = 16: 4-10% faster from 16 MiB per rank up; with the fan-out's two
+//     workgroups per tile (from 9 ranks on) also 5-8% faster at 12 MiB, and
+//     8-10% slower at 4-8 MiB;
+//   P = 11-15: with that fan-out 6-11% faster at 16 MiB (P = 12 bf16: 6%),
+//     within 1% at 12 MiB;
 //   P = 8: 2-15% faster from 24 to 256 MiB (bf16 at 96 MiB: 1-4% slower);
 //   P = 9, 12, 15: 3-15% faster from 24 MiB to 256 MiB, 2-14% slower at 8 MiB;
+//     P = 9 4% slower and P = 10 even at 16 MiB, P = 10 2% faster at 20 MiB;
 //   P = 5-7: 2-11% faster from 32 to 256 MiB, 2-24% slower at 8-16 MiB,
 //     within 5% at 24 MiB;
 //   P = 4: 0-7% faster at 128-192 MiB, mixed at 96 and 256 MiB, 18-26%
@@ -152,7 +157,8 @@ dt_status fan_out(const void* const* src, const size_t* counts, void* const* tab
 // costs more than the pattern saves.
 bool two_shot_pays(int nranks, uint64_t bytes_per_rank) {
     constexpr uint64_t MiB = 1ull << 20;
-    if (nranks >= 16) return bytes_per_rank >= 16 * MiB;
+    if (nranks >= 16) return bytes_per_rank >= 12 * MiB;
+    if (nranks >= 11) return bytes_per_rank >= 16 * MiB && bytes_per_rank <= 256 * MiB;
     if (nranks >= 8) return bytes_per_rank >= 24 * MiB && bytes_per_rank <= 256 * MiB;
     if (nranks >= 5) return bytes_per_rank >= 32 * MiB && bytes_per_rank <= 256 * MiB;
     if (nranks == 4) return bytes_per_rank >= 128 * MiB && bytes_per_rank <= 192 * MiB;

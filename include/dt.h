@@ -76,9 +76,10 @@ typedef enum {
  * sec. 2.3 (the same-device listing folds rank 0 then ranks 1..P-1 on one
  * rank and hands the result to all).  Usually one launch: each element is
  * read once per rank and written once per rank (the one-shot form of the
- * c10d page, sec. 9.4).  From 16 MiB per rank up for P >= 16, from 24 to
- * 256 MiB for 8 <= P < 16, from 32 to 256 MiB for 5 <= P <= 7 and from 128
- * to 192 MiB for P = 4, with 16-byte aligned buffers, it runs as a
+ * c10d page, sec. 9.4).  From 12 MiB per rank up for P >= 16, from 16 to
+ * 256 MiB for 11 <= P <= 15, from 24 to 256 MiB for 8 <= P <= 10, from 32
+ * to 256 MiB for 5 <= P <= 7 and from 128 to 192 MiB for P = 4, with
+ * 16-byte aligned buffers, it runs as a
  * ReduceScatter into chunk r of recv[r] (chunks of whole 1 KiB tiles, the
  * last one shorter) followed by an in-place AllGather of the chunks, which
  * is faster there (elements past the last whole vector take the element

@@ -979,15 +979,20 @@ void two_shot() {
         {8, DT_FLOAT32, 64 * M, false, 1},            // 256 MiB: the upper edge at P=8
         {8, DT_FLOAT32, 64 * M + 32, false, 2},       // beyond it: two 128 MiB windows and a one-shot tail
         {8, DT_BFLOAT16, 192 * M, true, 3},           // 384 MiB in place: three windows
-        {16, DT_FLOAT32, 4 * M, false, 1},            // 16 MiB: the lower edge at P=16
-        {16, DT_FLOAT32, 4 * M - 64, false, 0},       // just below it
+        {16, DT_FLOAT32, 3 * M, false, 1},            // 12 MiB: the lower edge at P=16
+        {16, DT_FLOAT32, 3 * M - 64, false, 0},       // just below it
+        {16, DT_FLOAT32, 4 * M, false, 1},            // 16 MiB
+        {12, DT_FLOAT32, 4 * M, false, 1},            // 16 MiB: the lower edge at P=11-15
+        {12, DT_FLOAT32, 4 * M - 64, false, 0},       // just below it
+        {10, DT_FLOAT32, 4 * M, false, 0},            // 16 MiB at P=10: one-shot
+        {11, DT_BFLOAT16, 8 * M, false, 1},           // 16 MiB at P=11
         {16, DT_FLOAT32, 8 * M, false, 1},            // 32 MiB
         {16, DT_FLOAT32, 64 * M, true, 1},            // 256 MiB: still one call
         {16, DT_FLOAT32, 96 * M + 64, false, 6},      // 384 MiB + 256 B: six 64 MiB windows and a one-shot tail
         {16, DT_FLOAT32, 80 * M + 4096, true, 5},     // 320 MiB + 16 KiB: five windows and a one-shot tail
         {12, DT_INT32, 48 * M, false, 1},             // 192 MiB
         {12, DT_INT32, 72 * M, false, 3},             // 288 MiB at P=12: windows of whole vectors per chunk
-        {12, DT_BFLOAT16, 200 * M + 96, false, 3},    // 400 MiB + 192 B at P=12: three windows, a one-shot tail
+        {12, DT_BFLOAT16, 200 * M + 96, false, 4},    // 400 MiB + 192 B at P=12: three windows, a two-shot 16 MiB tail
         {8, DT_BFLOAT16, 64 * M + 8, false, 1},       // not a multiple of P vectors: a shorter last chunk
         {12, DT_FLOAT32, 48 * M + 4, false, 1},       // 192 MiB + 16 B at P=12: chunks of whole 1 KiB tiles
         {8, DT_BFLOAT16, 64 * M + 4, false, 1},       // not a whole number of vectors: two-shot, an element tail
