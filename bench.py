@@ -263,7 +263,9 @@ def alpha_beta_fit(sizes, us, p: int) -> dict:
       B_cache: the same over the points whose footprint fits the Infinity
         Cache and whose time is at least 2 * alpha (below that, T - alpha is
         mostly noise).
-    Each B is a weighted mean of per-point rates, so it lies within them."""
+    B takes alpha off each point's time (the model), so it can sit a little
+    above the best measured rate (by about alpha / T); B_GBps_without_alpha
+    is the same weighted mean of the measured rates themselves."""
     s = [float(x) for x in sizes]
     t = [float(x) * 1e-6 for x in us]
     lat = [ti for si, ti in zip(s, t) if si <= 64 * 1024]
@@ -275,8 +277,12 @@ def alpha_beta_fit(sizes, us, p: int) -> dict:
             return None
         num = sum(x * x / (ti * ti) for x, ti in pts)
         den = sum(x * (ti - alpha) / (ti * ti) for x, ti in pts)
+        rates = [x / ti for x, ti in pts]
         return {"B_GBps": round(num / den / 1e9, 1) if den > 0 else None, "points": len(pts),
-                "best_point_GBps": round(max(x / ti for x, ti in pts) / 1e9, 1)}
+                "best_point_GBps": round(max(rates) / 1e9, 1),
+                # the same weights without the alpha correction: a weighted mean of
+                # the measured rates, so never above the best point
+                "B_GBps_without_alpha": round(sum(r * r for r in rates) / sum(rates) / 1e9, 1)}
 
     return {"alpha_us": round(alpha * 1e6, 3),
             "hbm": band(lambda si, ti: 2 * p * si > 512 * 2 ** 20),
