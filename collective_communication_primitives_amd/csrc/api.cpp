@@ -51,6 +51,10 @@ bool valid_op(dt_op o) { return o == DT_SUM || o == DT_MAX || o == DT_MIN || o =
 size_t esize_of(dt_dtype d) { return d == DT_BFLOAT16 ? 2 : 4; }
 size_t vec_elems(dt_dtype d) { return 16 / esize_of(d); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// The copy engines' stores start on the destination's 128-byte lines: a
+// destination off its lines (even at a 16-byte boundary) takes the line grid.
+bool line_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & (dt::kGridAlign - 1)) == 0; }
+bool elem_aligned(const void* p, size_t es) { return (reinterpret_cast<uintptr_t>(p) & (es - 1)) == 0; }
 const char* cptr(const void* p) { return static_cast<const char*>(p); }
 
 dt_status check_ranks(int nranks) {
@@ -192,6 +196,35 @@ uint64_t allreduce_window(int nranks, uint64_t bytes_per_rank) {
 }
 
 // Validated AllReduce over one contiguous range per rank, in one call.
+// ReduceScatter over the chunk outputs' line grids (dt::GridFoldArgs):
+// chunk c is elements [c * in_stride, c * in_stride + n_c) of every input,
+// n_c = count but last_count for the last chunk, folded into out[c].  For
+// element-aligned buffers that share no offset.
+dt_status reduce_scatter_grid(const void* const* send, void* const* out, int nranks, size_t in_stride, size_t count,
+                              size_t last_count, dt_dtype dtype, dt_op op, hipStream_t stream, const char* what) {
+    dt::GridFoldArgs g = {};
+    for (int r = 0; r < nranks; r++) {
+        g.src[r] = send[r];
+        g.dst[r] = out[r];
+        g.lead[r] = uint32_t(reinterpret_cast<uintptr_t>(out[r]) & (dt::kGridAlign - 1));
+    }
+    g.in_stride = in_stride;
+    g.count = count;
+    g.last_count = last_count;
+    g.nranks = nranks;
+    g.nchunks = nranks;
+    return check_hip(dt::launch_reduce_scatter_grid(g, dtype, op, stream), what);
+}
+
+// Bytes per rank from which an AllReduce over element-aligned buffers that
+// share no offset takes the two-shot form over line grids (the grid
+// ReduceScatter into each output's own chunk, then the fan-out) instead of
+// the element kernel.  Graph replays, outputs 2 bytes off and inputs aligned
+// (or the reverse): at 4 MiB per rank the two forms are even (P=8 bf16) or
+// the element kernel leads by 10-30% (P=4 fp32); at 16 MiB the two-shot
+// form leads by 25% (P=8 bf16, 51 against 68 us).
+constexpr uint64_t kGridTwoShotMinBytes = 8ull << 20;
+
 dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, size_t count, dt_dtype dtype,
                         dt_op op, hipStream_t stream) {
     dt::ReduceArgs a = {};
@@ -242,6 +275,28 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
         a.first = size_t(nv * v);  // the ragged end, fewer than one vector per rank: element path
         a.count = count - a.first;
         return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "allreduce (element path) launch");
+    }
+    if (!vec && nranks > 1 && uint64_t(count) * es >= kGridTwoShotMinBytes) {
+        bool el = true;
+        for (int r = 0; r < nranks; r++) el = el && elem_aligned(send[r], es) && elem_aligned(recv[r], es);
+        // chunks of whole 1 KiB of elements, all but the last, as above
+        const size_t te = size_t(dt::kGridFoldTileBytes) / es;
+        const size_t mce = ((count + nranks - 1) / nranks + te - 1) / te * te;
+        if (el && mce * size_t(nranks - 1) < count) {
+            const size_t last = count - mce * size_t(nranks - 1);
+            void* own[dt::kMaxRanksHost];
+            size_t counts[dt::kMaxRanksHost];
+            void* table[dt::kMaxRanksHost * dt::kMaxRanksHost];
+            for (int r = 0; r < nranks; r++) {
+                own[r] = static_cast<char*>(recv[r]) + r * mce * es;
+                counts[r] = r + 1 < nranks ? mce : last;
+                for (int q = 0; q < nranks; q++) table[size_t(r) * nranks + q] = static_cast<char*>(recv[q]) + r * mce * es;
+            }
+            dt_status st = reduce_scatter_grid(send, own, nranks, mce, mce, last, dtype, op, stream,
+                                               "allreduce (grid reduce_scatter) launch");
+            if (st != DT_OK) return st;
+            return fan_out(own, counts, table, nranks, es, stream, "allreduce (all_gather) launch");
+        }
     }
     size_t body = 0;
     if (vec) {
@@ -429,20 +484,19 @@ dt_status fan_out_launch(const void* const* src, const uint64_t* bytes, void* co
         a.src[k] = src[k];
         a.bytes[k] = bytes[k];
         a.tile_start[k] = uint32_t(tiles);
-        bool al = aligned16(src[k]);
         bool same = true;  // every destination at the same offset within a 128-byte line
         const uintptr_t md = bytes[k] ? reinterpret_cast<uintptr_t>(dst[k][0]) & (dt::kGridAlign - 1) : 0;
         for (int q = 0; q < nranks; q++) {
             void* d = bytes[k] ? dst[k][q] : nullptr;
             a.dst[k * nranks + q] = d;
-            al = al && aligned16(d);
             same = same && (reinterpret_cast<uintptr_t>(d) & (dt::kGridAlign - 1)) == md;
         }
-        if (al) {
+        if (same && md == 0 && aligned16(src[k])) {  // every destination on a line: tiles follow the source
             a.aligned |= 1u << k;
             tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;
-        } else if (same) {
+        } else if (same) {  // tiles over the destinations' line grid
             a.shifted |= 1u << k;
+            a.lead[k] = uint32_t(md) | uint32_t((reinterpret_cast<uintptr_t>(src[k]) - md) & 15u) << 16;
             tiles += dt::grid_tiles(bytes[k], md, tile_bytes);
         } else {
             tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;
@@ -532,10 +586,10 @@ dt_status copy_segments(const std::vector<const void*>& src, const std::vector<v
         a.dst[i] = dst[k];
         a.bytes[i] = bytes[k];
         a.tile_start[i] = uint32_t(tiles);
-        if (aligned16(src[k]) && aligned16(dst[k])) {
+        if (aligned16(src[k]) && line_aligned(dst[k])) {
             a.aligned |= 1ull << i;
             tiles += (bytes[k] + dt::kSegCopyTileBytes - 1) / dt::kSegCopyTileBytes;
-        } else {  // tiles over the destination's aligned grid
+        } else {  // tiles over the destination's line grid
             tiles += dt::grid_tiles(bytes[k], reinterpret_cast<uintptr_t>(dst[k]) & (dt::kGridAlign - 1),
                                     dt::kSegCopyTileBytes);
         }
@@ -754,6 +808,11 @@ dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nran
         a.count2 = recvcount - a.first2;
         return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "reduce_scatter (head and tail) launch");
     }
+    bool el = true;  // element-aligned buffers at offsets of their own: the line-grid kernel
+    for (int r = 0; r < nranks; r++) el = el && elem_aligned(send[r], es) && elem_aligned(recv[r], es);
+    if (el)
+        return reduce_scatter_grid(send, recv, nranks, recvcount, recvcount, recvcount, dtype, op, stream,
+                                   "reduce_scatter (grid) launch");
     a.first = 0;
     a.count = recvcount;
     return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "reduce_scatter (element path) launch");
@@ -1026,8 +1085,8 @@ dt_status dt_all_to_all(const void* const* send, void* const* recv, int nranks, 
             if (bytes > 0) {
                 const char* from = cptr(send[i]) + so;
                 char* to = static_cast<char*>(recv[j]) + recv_off[j];
-                const bool al = aligned16(from) && aligned16(to);
-                // an unaligned block's tiles cover its destination's aligned grid
+                const bool al = aligned16(from) && line_aligned(to);
+                // other blocks' tiles cover their destination's line grid
                 const uint64_t t = al ? (bytes + dt::kCopyTileBytes - 1) / dt::kCopyTileBytes
                                       : dt::grid_tiles(bytes, reinterpret_cast<uintptr_t>(to) & (dt::kGridAlign - 1),
                                                        dt::kCopyTileBytes);

@@ -69,68 +69,111 @@ __global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
             for (int q = 0; q < nr; q++)
                 if (dsts[q] != src) static_cast<char*>(dsts[q])[t] = c;
         }
-    } else if (part != 0) {
-        return;  // the shifted and byte paths run in the tile's first part only
     } else if ((a.shifted >> r) & 1u) {
-        // The destinations share one offset md within a 128-byte line: tile b
-        // covers bytes [b0, b0 + kTile) of their line grid, grid byte g being
-        // byte g - md of the piece.  A grid vector inside the piece is one
-        // aligned store to every destination, its source bytes joined from
-        // aligned loads (the source's misalignment is the same for all of
-        // them); the partial vectors at the two ends go byte by byte.
-        const uint32_t md = uint32_t(reinterpret_cast<uintptr_t>(dsts[0]) & (kGridAlign - 1));
-        const uint32_t sm = uint32_t((reinterpret_cast<uintptr_t>(src) - md) & 15u);
+        // The destinations share one offset, `lead` bytes into their grid:
+        // tile b covers bytes [b0, b0 + kTile) of the grid, grid byte g being
+        // byte g - lead of the piece.  A grid vector inside the piece is
+        // built from aligned loads of the source (the source sits sm bytes
+        // into a vector at the grid's vector starts) and stored with one
+        // aligned store to each destination of this part; the partial
+        // vectors at the piece's two ends are loaded through a window over
+        // the piece and stored byte by byte, in part 0, their loads all
+        // issued before any store.  Both offsets come from the host, so the
+        // first load waits on no destination pointer.
+        const uint32_t lead = a.lead[r] & 0xFFFFu;
+        const uint32_t sm = a.lead[r] >> 16;
         const int64_t bytes = int64_t(a.bytes[r]);
+        u32x4 x[U];
+        bool full[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const int64_t p0 = int64_t(b0) + int64_t(threadIdx.x + u * BLOCK) * 16 - int64_t(md);
-            if (p0 >= 0 && p0 + 16 <= bytes) {
-                // the aligned path's stores: buffer stores, non-temporal with
-                // device scope, addressed from the tile's grid start
-                const u32x4 x = load16_any<false>(src + p0, sm);
-                for (int q = 0; q < nr; q++) {
-                    if (dsts[q] == src) continue;
-                    const rsrc_t out = make_rsrc(static_cast<char*>(dsts[q]) - md + b0, uint32_t(kTile));
-                    bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * BLOCK) * 16, x);
-                }
-            } else if (p0 + 16 > 0 && p0 < bytes) {
-                const int64_t e = p0 + 16 < bytes ? p0 + 16 : bytes;
-                for (int64_t i = p0 > 0 ? p0 : 0; i < e; i++) {
-                    const char c = src[i];
+            const int64_t p0 = int64_t(b0) + int64_t(threadIdx.x + u * BLOCK) * 16 - int64_t(lead);
+            full[u] = p0 >= 0 && p0 + 16 <= bytes;
+            if (full[u]) x[u] = load16_any<false>(src + p0, sm);
+        }
+#pragma unroll
+        for (int q = 0; q < PMAX; q++) {
+            if (q < nr && (q & (nparts - 1)) == part && dsts[q] != src) {
+                // the aligned path's stores, addressed from the tile's grid start
+                const rsrc_t out = make_rsrc(static_cast<char*>(dsts[q]) - lead + b0, uint32_t(kTile));
+#pragma unroll
+                for (int u = 0; u < U; u++)
+                    if (full[u]) bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * BLOCK) * 16, x[u]);
+            }
+        }
+        if (part == 0 && (int64_t(b0) < int64_t(lead) || int64_t(b0) - lead + int64_t(kTile) > bytes)) {
+            // a tile at one of the piece's ends: its partial vectors, loaded
+            // through a window over the piece, stored byte by byte
+            const LoadWindow w = load_window(src, bytes, int64_t(b0) - lead - sm, int64_t(kTile) + 16);
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int64_t p0 = int64_t(b0) + int64_t(threadIdx.x + u * BLOCK) * 16 - int64_t(lead);
+                if (full[u] || p0 + 16 <= 0 || p0 >= bytes) continue;
+                const u32x4 y = window_load_shifted<0>(w, p0 - int64_t(sm), sm);
+#pragma unroll
+                for (int j = 0; j < 16; j++) {
+                    if (p0 + j < 0 || p0 + j >= bytes) continue;
+                    const char c = vec_byte(y, j);
                     for (int q = 0; q < nr; q++)
-                        if (dsts[q] != src) static_cast<char*>(dsts[q])[i] = c;
+                        if (dsts[q] != src) static_cast<char*>(dsts[q])[p0 + j] = c;
                 }
             }
         }
+    } else if (part != 0) {
+        return;  // the byte path runs in the tile's first part only
     } else {
-        for (uint64_t t = b0 + threadIdx.x; t < b1; t += BLOCK) {
-            const char c = src[t];
-            for (int q = 0; q < nr; q++)
-                if (dsts[q] != src) static_cast<char*>(dsts[q])[t] = c;
+        // Destinations at offsets of their own: each lane takes 16 bytes of
+        // the tile, loaded as one shifted vector (the window, as above), and
+        // stores them to every destination byte by byte.
+        const uint32_t sm = uint32_t(reinterpret_cast<uintptr_t>(src) & 15u);
+        const int64_t bytes = int64_t(a.bytes[r]);
+        const LoadWindow w = load_window(src, bytes, int64_t(b0) - sm, int64_t(kTile) + 16);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t p0 = int64_t(b0) + int64_t(threadIdx.x + u * BLOCK) * 16;
+            if (p0 >= bytes) continue;
+            const u32x4 x = window_load_shifted<0>(w, p0 - int64_t(sm), sm);
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                if (p0 + j >= bytes) continue;
+                const char c = vec_byte(x, j);
+                for (int q = 0; q < nr; q++)
+                    if (dsts[q] != src) static_cast<char*>(dsts[q])[p0 + j] = c;
+            }
         }
     }
 }
 
-// A 1:1 copy of `bytes` bytes from src to dst (not 16-byte aligned), tile
-// `tile` of TILE bytes over dst's 128-byte line grid (grid_tiles), THREADS
-// lanes with TILE / 16 / THREADS vectors each: aligned stores, sources joined
-// from aligned loads, the partial vectors at the two ends byte by byte.
+// A 1:1 copy of `bytes` bytes from src to dst (dst not on a 128-byte line
+// or src not 16-byte aligned), tile `tile` of TILE bytes over dst's line grid
+// (grid_tiles), THREADS lanes with TILE / 16 / THREADS vectors each: a
+// vector inside the copy is built from aligned loads of the source and
+// stored aligned; the partial vectors at the copy's two ends are loaded
+// through a window over the source (load_window) and stored byte by byte.
 template <int THREADS, uint64_t TILE>
 __device__ __forceinline__ void copy_shifted(const char* src, char* dst, uint64_t bytes, uint64_t tile) {
     constexpr int U = int(TILE / 16 / THREADS);
     const uint32_t md = uint32_t(reinterpret_cast<uintptr_t>(dst) & (kGridAlign - 1));
     const uint32_t sm = uint32_t((reinterpret_cast<uintptr_t>(src) - md) & 15u);
     const int64_t n = int64_t(bytes);
-    const rsrc_t out = make_rsrc(dst - md + tile * TILE, uint32_t(TILE));  // the tile's grid start
+    const int64_t g0 = int64_t(tile * TILE) - int64_t(md);  // copy byte at the tile's grid start
+    const rsrc_t out = make_rsrc(dst + g0, uint32_t(TILE));
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        const int64_t p0 = int64_t(tile * TILE) + int64_t(threadIdx.x + u * THREADS) * 16 - int64_t(md);
-        if (p0 >= 0 && p0 + 16 <= n) {
+        const int64_t p0 = g0 + int64_t(threadIdx.x + u * THREADS) * 16;
+        if (p0 >= 0 && p0 + 16 <= n)
             bstore16<kPolNT | kPolDevice>(out, (threadIdx.x + u * THREADS) * 16, load16_any<true>(src + p0, sm));
-        } else if (p0 + 16 > 0 && p0 < n) {
-            const int64_t e = p0 + 16 < n ? p0 + 16 : n;
-            for (int64_t i = p0 > 0 ? p0 : 0; i < e; i++) dst[i] = src[i];
-        }
+    }
+    if (g0 >= 0 && g0 + int64_t(TILE) <= n) return;
+    const LoadWindow w = load_window(src, n, g0 - int64_t(sm), int64_t(TILE) + 16);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t p0 = g0 + int64_t(threadIdx.x + u * THREADS) * 16;
+        if ((p0 >= 0 && p0 + 16 <= n) || p0 + 16 <= 0 || p0 >= n) continue;
+        const u32x4 x = window_load_shifted<kPolNT>(w, p0 - int64_t(sm), sm);
+#pragma unroll
+        for (int j = 0; j < 16; j++)
+            if (p0 + j >= 0 && p0 + j < n) dst[p0 + j] = vec_byte(x, j);
     }
 }
 
@@ -160,7 +203,7 @@ __global__ __launch_bounds__(kGatherBlock) void k_gather_touch(GatherArgs a) {
     } else if ((a.shifted >> r) & 1u) {
         // the same grid as k_gather: each lane reads the aligned source vector
         // holding the first byte its grid vector needs
-        const uint32_t md = uint32_t(reinterpret_cast<uintptr_t>(a.dst[r * nr]) & (kGridAlign - 1));
+        const uint32_t md = a.lead[r] & 0xFFFFu;
         const int64_t bytes = int64_t(a.bytes[r]);
 #pragma unroll
         for (int u = 0; u < U; u++) {

@@ -103,11 +103,41 @@ __device__ __forceinline__ u32x4 funnel16(u32x4 lo, u32x4 hi, uint32_t s) {
     return o;
 }
 
-// The 16 bytes at p, any alignment, from aligned loads only: the one aligned
-// vector holding them, or the two around them.  Each of those aligned
-// vectors holds at least one of the 16 requested bytes, so none reaches a
-// page that the requested bytes do not touch.  `misalign` is p & 15, passed
-// in because it is uniform across the lanes of a copy.
+// Aligned loads over the part of a byte range [s, s + n) that one tile
+// reads, for kernels that shift vectors: the tile's loads start at offset o_t
+// from s (o_t + s aligned, o_t may be negative) and span `span` bytes.  The
+// window is a buffer resource over the aligned vectors of that span which
+// hold at least one byte of the range, so a load at any offset outside them
+// (before the range's first vector or past its last) returns zeros without
+// touching memory, and the lanes at a range's two ends load like the rest.
+struct LoadWindow {
+    rsrc_t r;
+    int64_t b;  // offset from s of the resource's first byte
+};
+__device__ __forceinline__ LoadWindow load_window(const char* s, int64_t n, int64_t o_t, int64_t span) {
+    const int64_t head = int64_t(reinterpret_cast<uintptr_t>(s) & 15u);
+    const int64_t o_end = ((head + n + 15) & ~int64_t(15)) - head;  // past the range's last aligned vector
+    const int64_t b = o_t > -head ? o_t : -head;
+    const int64_t e = o_t + span < o_end ? o_t + span : o_end;
+    return LoadWindow{make_rsrc(s + b, uint32_t(e > b ? e - b : 0)), b};
+}
+// The aligned vector at s + o (o - w.b wraps to far past the window when o < w.b).
+template <int POL>
+__device__ __forceinline__ u32x4 window_load(const LoadWindow& w, int64_t o) {
+    return bload16<POL>(w.r, uint32_t(o - w.b));
+}
+// Bytes [o + sm, o + sm + 16) of the range: the aligned vectors at o and o + 16
+// joined (sm = 0: the one at o).
+template <int POL>
+__device__ __forceinline__ u32x4 window_load_shifted(const LoadWindow& w, int64_t o, uint32_t sm) {
+    const u32x4 lo = window_load<POL>(w, o);
+    if (sm == 0) return lo;
+    return funnel16(lo, window_load<POL>(w, o + 16), sm);
+}
+// The 16 bytes at p (p & 15 == misalign, uniform across the lanes) from
+// aligned loads: the one aligned vector holding them, or the two around them.
+// Each of those vectors holds at least one of the 16 bytes, so none reaches a
+// page that the bytes themselves do not touch.
 template <bool NT>
 __device__ __forceinline__ u32x4 load16_any(const char* p, uint32_t misalign) {
     const char* a = p - misalign;
@@ -115,6 +145,8 @@ __device__ __forceinline__ u32x4 load16_any(const char* p, uint32_t misalign) {
     if (misalign == 0) return lo;
     return funnel16(lo, load16_h<NT>(a + 16), misalign);
 }
+// Byte j of a vector.
+__device__ __forceinline__ char vec_byte(const u32x4& x, int j) { return char(x[j >> 2] >> ((j & 3) * 8)); }
 
 // ------------------------------------------------------------------- bf16 --
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -243,22 +275,45 @@ __device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[P], int nr) {
     return out;
 }
 
-// One element: fold element e of every live rank buffer (element-wise path).
-template <int DT, int OP>
-__device__ __forceinline__ void fold_elem(const void* const* src, int nr, size_t e, void* dst, size_t de) {
-    if constexpr (DT == kI32) {
-        int32_t acc = static_cast<const int32_t*>(src[0])[e];
-        for (int r = 1; r < nr; r++) acc = combine<OP>(acc, static_cast<const int32_t*>(src[r])[e]);
-        static_cast<int32_t*>(dst)[de] = finish<OP>(acc, nr);
-    } else if constexpr (DT == kF32) {
-        float acc = static_cast<const float*>(src[0])[e];
-        for (int r = 1; r < nr; r++) acc = combine<OP>(acc, static_cast<const float*>(src[r])[e]);
-        static_cast<float*>(dst)[de] = finish<OP>(acc, nr);
-    } else {
-        float acc = bf16_at(static_cast<const uint16_t*>(src[0])[e]);
-        for (int r = 1; r < nr; r++) acc = combine<OP>(acc, bf16_at(static_cast<const uint16_t*>(src[r])[e]));
-        static_cast<uint16_t*>(dst)[de] = uint16_t(to_bf16(finish<OP>(acc, nr)));
+// One element: fold element e of the P rank buffers (element-wise path),
+// returned as the result's bit pattern (bf16 in the low 16 bits).  P is a
+// compile-time count, so the P loads unroll and all go out before the fold
+// (with a run-time count the loop folded as it loaded and waited for each
+// load in turn).
+template <int DT, int OP, int P>
+__device__ __forceinline__ uint32_t fold_elem_bits(const void* const* src, size_t e) {
+    uint32_t w[P];
+#pragma unroll
+    for (int r = 0; r < P; r++) {
+        if constexpr (DT == kBF16) w[r] = static_cast<const uint16_t*>(src[r])[e];
+        else w[r] = static_cast<const uint32_t*>(src[r])[e];
     }
+    if constexpr (DT == kI32) {
+        int32_t acc = int32_t(w[0]);
+#pragma unroll
+        for (int r = 1; r < P; r++) acc = combine<OP>(acc, int32_t(w[r]));
+        return uint32_t(finish<OP>(acc, P));
+    } else if constexpr (DT == kF32) {
+        float acc = __uint_as_float(w[0]);
+#pragma unroll
+        for (int r = 1; r < P; r++) acc = combine<OP>(acc, __uint_as_float(w[r]));
+        return __float_as_uint(finish<OP>(acc, P));
+    } else {
+        float acc = bf16_at(uint16_t(w[0]));
+#pragma unroll
+        for (int r = 1; r < P; r++) acc = combine<OP>(acc, bf16_at(uint16_t(w[r])));
+        return to_bf16(finish<OP>(acc, P));
+    }
+}
+// Element de of dst takes the bits of one element.
+template <int DT>
+__device__ __forceinline__ void store_elem(void* dst, size_t de, uint32_t bits) {
+    if constexpr (DT == kBF16) static_cast<uint16_t*>(dst)[de] = uint16_t(bits);
+    else static_cast<uint32_t*>(dst)[de] = bits;
+}
+template <int DT, int OP, int P>
+__device__ __forceinline__ void fold_elem(const void* const* src, size_t e, void* dst, size_t de) {
+    store_elem<DT>(dst, de, fold_elem_bits<DT, OP, P>(src, e));
 }
 
 }  // namespace dt

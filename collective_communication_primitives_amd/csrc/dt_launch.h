@@ -26,6 +26,24 @@ struct ReduceArgs {
     int rs;                // 1: ReduceScatter (grid.y = chunk), 0: AllReduce
 };
 
+// ReduceScatter over each output chunk's 128-byte line grid, for element-
+// aligned buffers that share no offset (the vector kernels need every buffer
+// 16-byte aligned, or all at one offset).  Chunk c is elements
+// [c * in_stride, c * in_stride + n_c) of every input, n_c = count for every
+// chunk but the last (last_count); it goes to dst[c], whose first byte sits
+// lead[c] = dst[c] & (kGridAlign - 1) bytes into a line.
+struct GridFoldArgs {
+    const void* src[kMaxRanksHost];
+    void* dst[kMaxRanksHost];
+    uint32_t lead[kMaxRanksHost];
+    uint64_t in_stride;
+    uint64_t count;
+    uint64_t last_count;
+    int nranks;
+    int nchunks;
+};
+constexpr uint64_t kGridFoldTileBytes = 1024;  // one wave, one vector per lane
+
 // Multi-tensor pieces of one bucket.  Piece k of rank r starts at
 // ptr[k*nranks + r]; ws[r] + wpos[k] is its place in rank r's bucket buffer.
 constexpr int kPiecePtrs = 320;
@@ -81,19 +99,26 @@ struct GatherArgs {
     void* dst[kMaxRanksHost * kMaxRanksHost];
     uint64_t bytes[kMaxRanksHost];
     uint32_t tile_start[kMaxRanksHost + 1];
-    uint32_t aligned;      // bit r: rank r's piece and its destinations allow 16-byte vectors
+    uint32_t aligned;      // bit r: rank r's source is 16-byte aligned and every destination
+                           // starts on a 128-byte line; tiles follow the source
     uint32_t shifted;      // bit r (not aligned): rank r's destinations share one offset within a
-                           // 128-byte line; its tiles then follow their line grid (grid_tiles)
+                           // 128-byte line; its tiles then follow their grid (grid_tiles)
+    uint32_t lead[kMaxRanksHost];  // shifted piece r: bits 0-15 the grid bytes before its first byte
+                                   // (the destinations' offset within the grid's grain), bits 16-19
+                                   // the source's offset within a vector at the grid's vector starts
     uint32_t tile_bytes;   // kGatherTileBytes or kGatherWaveTileBytes: the launch's workgroup shape
     uint32_t split_log2;   // each source tile's destinations go to 2^split_log2 workgroups (q mod 2^s)
     int nranks;
 };
 
-// Tiles of a copy whose destination is not 16-byte aligned: the tiles cover
-// a grid that starts at the 128-byte line holding the destination's first
+// Tiles of a copy whose destination does not start on a 128-byte line: the
+// tiles cover a grid that starts at the line holding the destination's first
 // byte, md = dst & (kGridAlign - 1) bytes before it, so that no line is
 // written by two workgroups, and every interior 16-byte vector is one aligned
-// store, built from aligned loads of the source (funnel16).
+// store, built from aligned loads of the source (funnel16).  Stores that start
+// off the lines are costly even when 16-byte aligned: a fan-out to
+// destinations 16 or 32 bytes past a line ran 1.7x slower than on the line
+// grid (P=8 bf16, 24 MiB pieces, 444 against 282 us).
 constexpr uint64_t kGridAlign = 128;
 inline uint64_t grid_tiles(uint64_t bytes, uint64_t md, uint64_t tile_bytes) {
     return (md + bytes + tile_bytes - 1) / tile_bytes;
@@ -190,6 +215,7 @@ constexpr uint64_t kPieceTileVecs = 512;     // bucket pieces: 512 x 16 B
 // alignment and divisibility).
 hipError_t launch_reduce_vec(const ReduceArgs& a, int dtype, int op, hipStream_t s);
 hipError_t launch_reduce_elems(const ReduceArgs& a, int dtype, int op, hipStream_t s);
+hipError_t launch_reduce_scatter_grid(const GridFoldArgs& a, int dtype, int op, hipStream_t s);
 hipError_t launch_reduce_pieces(const PieceArgs& a, int dtype, int op, hipStream_t s);
 hipError_t launch_reduce_coalesced(const CoalescedArgs& a, int dtype, int op, hipStream_t s);
 hipError_t launch_copy_coalesced(const CoalescedArgs& a, int esize, int to_ws, hipStream_t s);

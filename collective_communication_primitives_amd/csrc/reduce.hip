@@ -121,25 +121,106 @@ __global__ __launch_bounds__(BLOCK) void k_reduce_scatter_vec(ReduceArgs a) {
 // Element-wise path for ragged tails and unaligned buffers.  Elements
 // [a.first, a.first + a.count) and [a.first2, a.first2 + a.count2) of chunk
 // blockIdx.y.
-template <int DT, int OP>
+template <int DT, int OP, int P>
 __global__ __launch_bounds__(kBlock) void k_reduce_elems(ReduceArgs a) {
     const uint64_t chunk = a.rs ? blockIdx.y : 0;
     const uint64_t in_base = chunk * a.chunk_elems;
-    const int nr = a.nranks;
     const uint64_t total = a.count + a.count2;
     for (uint64_t i = uint64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
          i += uint64_t(gridDim.x) * kBlock) {
         const uint64_t e = i < a.count ? a.first + i : a.first2 + (i - a.count);
         if (a.rs) {
-            fold_elem<DT, OP>(a.src, nr, in_base + e, a.dst[chunk], e);
+            fold_elem<DT, OP, P>(a.src, in_base + e, a.dst[chunk], e);
         } else {
-            fold_elem<DT, OP>(a.src, nr, e, a.dst[0], e);
-            for (int q = 1; q < nr; q++) {
-                if constexpr (DT == kBF16)
-                    static_cast<uint16_t*>(a.dst[q])[e] = static_cast<const uint16_t*>(a.dst[0])[e];
-                else
-                    static_cast<uint32_t*>(a.dst[q])[e] = static_cast<const uint32_t*>(a.dst[0])[e];
-            }
+            const uint32_t bits = fold_elem_bits<DT, OP, P>(a.src, e);
+#pragma unroll
+            for (int q = 0; q < P; q++) store_elem<DT>(a.dst[q], e, bits);
+        }
+    }
+}
+
+// ReduceScatter over each output chunk's line grid (GridFoldArgs), for
+// buffers that share no offset.  Tile t of chunk c covers bytes
+// [t * 1 KiB, (t + 1) * 1 KiB) of the grid that starts at the line holding
+// the chunk's first output byte, lead bytes before it; grid.y = chunk.  (An
+// XCD-contiguous tile order, for the line that neighbouring tiles' loads
+// share, ran 10% slower.)  Every lane builds its 16-byte grid vector of
+// every input from two aligned loads joined by a byte shift (each input's
+// shift is the same for all lanes, computed from the kernel arguments, so
+// the choice of shift is uniform) and folds; a vector inside the chunk is
+// one aligned store, and a partial one at either end (loaded through
+// windows) stores its elements inside the chunk one by one.  P=8 bf16
+// at 128 MiB per rank, outputs 2 bytes off and inputs aligned (or the
+// reverse): 215 us (0.70 of peak), against 556 us on the element kernel
+// these buffers took before and 181 us for aligned buffers.
+template <int DT, int OP, int P>
+__global__ __launch_bounds__(kWaveBlock) void k_reduce_scatter_grid(GridFoldArgs a) {
+    constexpr int64_t ES = DT == kBF16 ? 2 : 4;
+    constexpr int64_t kTile = int64_t(kGridFoldTileBytes);
+    const uint32_t c = blockIdx.y;
+    const int64_t n = int64_t(c + 1 == uint32_t(a.nchunks) ? a.last_count : a.count) * ES;  // chunk bytes
+    const int64_t lead = int64_t(a.lead[c]);
+    const int64_t g0 = int64_t(blockIdx.x) * kTile - lead;  // chunk byte at the tile's grid start
+    if (g0 >= n) return;                                    // past the end of this chunk
+    const int64_t p0 = g0 + int64_t(threadIdx.x) * 16;
+    if (p0 + 16 <= 0 || p0 >= n) return;  // a lane before the chunk's first grid vector or past its last
+    const uint64_t in_off = uint64_t(c) * a.in_stride * uint64_t(ES);
+    uint32_t sm[P];
+#pragma unroll
+    for (int r = 0; r < P; r++)
+        sm[r] = uint32_t((reinterpret_cast<uintptr_t>(a.src[r]) + in_off - uint64_t(lead)) & 15u);
+    u32x4 lo[P], hi[P];
+    if (p0 >= 0 && p0 + 16 <= n) {
+        // Both aligned vectors of every input are loaded before any is
+        // shifted, so all 2P loads are in flight at once.  An input at the
+        // grid's own offset (shift 0) loads its one vector twice rather than
+        // the next one, which may lie past the buffer.  Plain loads, so that
+        // the second vector (the next lane's first) is served by the caches:
+        // in-process A/B against non-temporal loads, P=8 bf16 with the
+        // outputs 2 bytes off 232 -> 215 us at 128 MiB per rank (and the
+        // two-shot AllReduce 10% faster at 16 MiB, 2.5% slower at 128 MiB,
+        // where the inputs then crowd its chunks out of the Infinity Cache).
+        // Taking the second vector from the next lane by a shuffle instead
+        // ran 20% slower.
+#pragma unroll
+        for (int r = 0; r < P; r++) {
+            const char* at = static_cast<const char*>(a.src[r]) + in_off + p0 - sm[r];
+            lo[r] = load16_h<false>(at);
+            hi[r] = load16_h<false>(at + (sm[r] != 0 ? 16 : 0));
+        }
+        // the shift's word choice branches once per input (uniform); a
+        // branch-free choice by selects ran 10% slower
+        u32x4 x[P];
+#pragma unroll
+        for (int r = 0; r < P; r++) x[r] = sm[r] != 0 ? funnel16(lo[r], hi[r], sm[r]) : lo[r];
+        const rsrc_t out = make_rsrc(static_cast<char*>(a.dst[c]) + g0, uint32_t(kTile));
+        bstore16<kPolDevice>(out, threadIdx.x * 16, fold_vec<DT, OP, P>(x, P));
+    } else {
+        // a partial vector at one of the chunk's ends: every input's vectors
+        // through a window over its chunk (load_window, nothing outside the
+        // chunk's aligned vectors is read), all loads before the fold, then
+        // the elements inside the chunk stored one by one
+#pragma unroll
+        for (int r = 0; r < P; r++) {
+            const char* s = static_cast<const char*>(a.src[r]) + in_off;
+            const LoadWindow w = load_window(s, n, g0 - int64_t(sm[r]), kTile + 16);
+            const int64_t o = p0 - int64_t(sm[r]);
+            lo[r] = window_load<0>(w, o);
+            hi[r] = window_load<0>(w, o + (sm[r] != 0 ? 16 : 0));
+        }
+        u32x4 x[P];
+#pragma unroll
+        for (int r = 0; r < P; r++) x[r] = sm[r] != 0 ? funnel16(lo[r], hi[r], sm[r]) : lo[r];
+        const u32x4 y = fold_vec<DT, OP, P>(x, P);
+        char* d = static_cast<char*>(a.dst[c]);
+#pragma unroll
+        for (int j = 0; j < int(16 / ES); j++) {
+            const int64_t b = p0 + j * ES;
+            if (b < 0 || b >= n) continue;
+            if constexpr (ES == 2)
+                *reinterpret_cast<uint16_t*>(d + b) = uint16_t(y[j >> 1] >> ((j & 1) * 16));
+            else
+                *reinterpret_cast<uint32_t*>(d + b) = y[j];
         }
     }
 }
@@ -221,23 +302,13 @@ __global__ __launch_bounds__(kBlock) void k_reduce_pieces(Args a) {
         }
         const uint64_t t = v1 * V + threadIdx.x;  // ragged end of the piece
         if (t < e1) {
-            fold_elem<DT, OP>(ptr, nr, t, ptr[0], t);
-            for (int q = 1; q < nr; q++) {
-                if constexpr (DT == kBF16)
-                    static_cast<uint16_t*>(ptr[q])[t] = static_cast<const uint16_t*>(ptr[0])[t];
-                else
-                    static_cast<uint32_t*>(ptr[q])[t] = static_cast<const uint32_t*>(ptr[0])[t];
-            }
+            const uint32_t bits = fold_elem_bits<DT, OP, P>(ptr, t);
+            for (int q = 0; q < nr; q++) store_elem<DT>(ptr[q], t, bits);
         }
     } else {
         for (uint64_t e = e0 + threadIdx.x; e < e1; e += kBlock) {
-            fold_elem<DT, OP>(ptr, nr, e, ptr[0], e);
-            for (int q = 1; q < nr; q++) {
-                if constexpr (DT == kBF16)
-                    static_cast<uint16_t*>(ptr[q])[e] = static_cast<const uint16_t*>(ptr[0])[e];
-                else
-                    static_cast<uint32_t*>(ptr[q])[e] = static_cast<const uint32_t*>(ptr[0])[e];
-            }
+            const uint32_t bits = fold_elem_bits<DT, OP, P>(ptr, e);
+            for (int q = 0; q < nr; q++) store_elem<DT>(ptr[q], e, bits);
         }
     }
 }
@@ -288,7 +359,7 @@ __global__ __launch_bounds__(kSegBlock) void k_reduce_scatter_segs(SegReduceScat
         const uint64_t e0 = uint64_t(tt) * per_tile;
         const uint64_t e1 = min(m, e0 + per_tile);
         for (uint64_t e = e0 + threadIdx.x; e < e1; e += kSegBlock)
-            fold_elem<DT, OP>(src, nr, uint64_t(j) * m + e, dst, e);
+            fold_elem<DT, OP, P>(src, uint64_t(j) * m + e, dst, e);
     }
 }
 
@@ -398,15 +469,20 @@ hipError_t reduce_vec_dt(const ReduceArgs& a, int op, hipStream_t s) {
     }
 }
 
-template <int DT, int OP>
-hipError_t reduce_elems_op(const ReduceArgs& a, hipStream_t s) {
+template <int DT, int OP, int P>
+hipError_t reduce_elems_p(const ReduceArgs& a, hipStream_t s) {
     const uint64_t total = a.count + a.count2;
     if (total == 0) return hipSuccess;
     uint64_t blocks = (total + kBlock - 1) / kBlock;
     if (blocks > 8192) blocks = 8192;
     dim3 grid(unsigned(blocks), a.rs ? unsigned(a.nranks) : 1u);
-    k_reduce_elems<DT, OP><<<grid, kBlock, 0, s>>>(a);
+    k_reduce_elems<DT, OP, P><<<grid, kBlock, 0, s>>>(a);
     return hipGetLastError();
+}
+
+template <int DT, int OP>
+hipError_t reduce_elems_op(const ReduceArgs& a, hipStream_t s) {
+    return with_ranks(a.nranks, [&](auto p) { return reduce_elems_p<DT, OP, decltype(p)::value>(a, s); });
 }
 
 template <int DT>
@@ -416,6 +492,35 @@ hipError_t reduce_elems_dt(const ReduceArgs& a, int op, hipStream_t s) {
         case kMax: return reduce_elems_op<DT, kMax>(a, s);
         case kMin: return reduce_elems_op<DT, kMin>(a, s);
         default: return reduce_elems_op<DT, kAvg>(a, s);
+    }
+}
+
+template <int DT, int OP, int P>
+hipError_t reduce_scatter_grid_p(const GridFoldArgs& a, hipStream_t s) {
+    uint64_t tiles = 0;
+    for (int c = 0; c < a.nchunks; c++) {
+        const uint64_t n = (c + 1 == a.nchunks ? a.last_count : a.count) * (DT == kBF16 ? 2 : 4);
+        const uint64_t t = (a.lead[c] + n + kGridFoldTileBytes - 1) / kGridFoldTileBytes;
+        tiles = t > tiles ? t : tiles;
+    }
+    if (tiles == 0) return hipSuccess;
+    if (tiles > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    k_reduce_scatter_grid<DT, OP, P><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kWaveBlock, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int DT, int OP>
+hipError_t reduce_scatter_grid_op(const GridFoldArgs& a, hipStream_t s) {
+    return with_ranks(a.nranks, [&](auto p) { return reduce_scatter_grid_p<DT, OP, decltype(p)::value>(a, s); });
+}
+
+template <int DT>
+hipError_t reduce_scatter_grid_dt(const GridFoldArgs& a, int op, hipStream_t s) {
+    switch (op) {
+        case kSum: return reduce_scatter_grid_op<DT, kSum>(a, s);
+        case kMax: return reduce_scatter_grid_op<DT, kMax>(a, s);
+        case kMin: return reduce_scatter_grid_op<DT, kMin>(a, s);
+        default: return reduce_scatter_grid_op<DT, kAvg>(a, s);
     }
 }
 
@@ -509,6 +614,18 @@ hipError_t launch_reduce_elems(const ReduceArgs& a, int dtype, int op, hipStream
         case kF32: return reduce_elems_dt<kF32>(a, op, s);
         case kBF16: return reduce_elems_dt<kBF16>(a, op, s);
         default: return reduce_elems_dt<kI32>(a, op, s);
+    }
+}
+
+hipError_t launch_reduce_scatter_grid(const GridFoldArgs& a, int dtype, int op, hipStream_t s) {
+    if (a.nranks < 1 || a.nranks > kMaxRanksHost || a.nchunks < 1 || a.nchunks > kMaxRanksHost)
+        return hipErrorInvalidValue;
+    for (int c = 0; c < a.nchunks; c++)
+        if (a.lead[c] >= kGridAlign) return hipErrorInvalidValue;
+    switch (dtype) {
+        case kF32: return reduce_scatter_grid_dt<kF32>(a, op, s);
+        case kBF16: return reduce_scatter_grid_dt<kBF16>(a, op, s);
+        default: return reduce_scatter_grid_dt<kI32>(a, op, s);
     }
 }
 

@@ -38,10 +38,17 @@
  *    boundary, with the ragged end, in one element launch and the rest the
  *    fast way; a two-shot AllReduce does the same for line-aligned buffers
  *    that share an offset within 1 KiB (its tiles then start on 1 KiB
- *    boundaries).  The copy engines build aligned stores from aligned loads
- *    whatever the source offset (the fan-out when all destinations of a
- *    piece share one offset within a 128-byte line).  Anything else is
- *    still correct but runs element-wise.
+ *    boundaries).  Folds over element-aligned buffers at offsets of their
+ *    own (inputs and outputs apart, or rank by rank) tile each output over
+ *    its 128-byte lines and shift every input into place from aligned
+ *    loads: the ReduceScatter always, the AllReduce from 8 MiB per rank (as
+ *    a ReduceScatter into each output's own chunk and a fan-out of the
+ *    chunks); smaller AllReduces fold element by element.  The copy engines
+ *    store whole 128-byte lines of every destination that does not start
+ *    on one, built from aligned loads whatever the source offset (the
+ *    fan-out when all destinations of a piece share one offset within a
+ *    line; otherwise its bytes go out one by one).  Every path gives the
+ *    same bits.
  */
 #ifndef DT_H
 #define DT_H
@@ -86,7 +93,9 @@ typedef enum {
  * path).  Beyond 256 MiB per rank for P >= 5 it runs window by
  * window (64 MiB per rank at P >= 16, 128 MiB at P = 5-15), each window an
  * AllReduce of its own in the two-shot form, so the window's chunks are
- * still in the Infinity Cache when they fan out.  All forms fold in the
+ * still in the Infinity Cache when they fan out.  Buffers at offsets of
+ * their own take the two-shot form over line grids from 8 MiB per rank
+ * (see the alignment convention above).  All forms fold in the
  * same order and give identical bits.  In place is allowed (send[r] ==
  * recv[r]); any other overlap of a recv buffer with a send or recv buffer
  * is refused (DT_ERR_ARG).  send[r] and recv[r] hold `count` elements. */

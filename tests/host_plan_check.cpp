@@ -74,6 +74,7 @@ void touch(const void* p, uint64_t off, uint64_t n, bool write, const char* what
 }
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool line_al(const void* p) { return (reinterpret_cast<uintptr_t>(p) & (dt::kGridAlign - 1)) == 0; }
 size_t esize(int dtype) { return dtype == DT_BFLOAT16 ? 2 : 4; }
 uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
@@ -299,6 +300,35 @@ hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, 
     return hipSuccess;
 }
 
+// The line-grid ReduceScatter: chunk c of every input (c * in_stride
+// elements in, count elements, last_count for the last chunk) folds into
+// dst[c], lead[c] bytes into its line.
+int g_grid_rs_launches = 0;
+hipError_t launch_reduce_scatter_grid(const GridFoldArgs& a, int dtype, int, hipStream_t) {
+    g_launches++;
+    g_grid_rs_launches++;
+    const uint64_t es = esize(dtype);
+    CHECK(a.nranks >= 1 && a.nranks <= kMaxRanksHost && a.nchunks == a.nranks, "grid rs: %d ranks, %d chunks",
+          a.nranks, a.nchunks);
+    CHECK(a.last_count >= 1 && a.last_count <= a.count && a.in_stride >= a.count,
+          "grid rs: chunks of %llu elements, the last %llu, stride %llu", (unsigned long long)a.count,
+          (unsigned long long)a.last_count, (unsigned long long)a.in_stride);
+    for (int c = 0; c < a.nchunks; c++) {
+        const uint64_t n = (c + 1 == a.nchunks ? a.last_count : a.count) * es;
+        const uintptr_t d = reinterpret_cast<uintptr_t>(a.dst[c]);
+        CHECK(a.lead[c] == (d & (kGridAlign - 1)), "grid rs: chunk %d lead %u for an output at %llu mod 128", c,
+              a.lead[c], (unsigned long long)(d & (kGridAlign - 1)));
+        CHECK(d % es == 0, "grid rs: output %d not element-aligned", c);
+        touch(a.dst[c], 0, n, true, "grid reduce_scatter write");
+        for (int r = 0; r < a.nranks; r++) {
+            CHECK(reinterpret_cast<uintptr_t>(a.src[r]) % es == 0, "grid rs: input %d not element-aligned", r);
+            touch(a.src[r], c * a.in_stride * es, n, false, "grid reduce_scatter read");
+        }
+    }
+    log_fold(a.dst[0], (a.nchunks == 1 ? a.last_count : a.count) * es);
+    return hipSuccess;
+}
+
 // Every gather piece launched since the last reset: (source, bytes, first
 // destination), for the coverage check of the windowed fan-out.
 struct GatherPiece {
@@ -316,12 +346,20 @@ uint64_t gather_tiles(const GatherArgs& a, int r) {
           a.tile_bytes);
     if (((a.shifted >> r) & 1u) && a.bytes[r]) {
         CHECK(!((a.aligned >> r) & 1u), "gather: piece %d both aligned and shifted", r);
-        const uintptr_t md = reinterpret_cast<uintptr_t>(a.dst[r * a.nranks]) & (kGridAlign - 1);
+        // the kernel stores grid vector v of destination q at dst[q] - lead +
+        // 16 v and loads the source at src + 16 v - lead - sm: every grid
+        // start must sit on a 128-byte line, and sm must put the loads on
+        // vectors
+        const uint32_t lead = a.lead[r] & 0xFFFFu, sm = a.lead[r] >> 16;
+        CHECK(lead < kGridAlign && sm < 16, "gather: piece %d lead %u sm %u", r, lead, sm);
         for (int q = 0; q < a.nranks; q++)
-            CHECK((reinterpret_cast<uintptr_t>(a.dst[r * a.nranks + q]) & (kGridAlign - 1)) == md,
-                  "gather: shifted piece %d with destinations of different alignment", r);
-        return ceil_div(md + a.bytes[r], a.tile_bytes);
+            CHECK(((reinterpret_cast<uintptr_t>(a.dst[r * a.nranks + q]) - lead) & (kGridAlign - 1)) == 0,
+                  "gather: shifted piece %d: destination %d off its grid (lead %u)", r, q, lead);
+        CHECK(((reinterpret_cast<uintptr_t>(a.src[r]) - lead - sm) & 15u) == 0,
+              "gather: shifted piece %d: source loads off the vectors (lead %u sm %u)", r, lead, sm);
+        return ceil_div(lead + a.bytes[r], a.tile_bytes);
     }
+    CHECK(a.lead[r] == 0, "gather: lead %u on piece %d that is not shifted", a.lead[r], r);
     return ceil_div(a.bytes[r], a.tile_bytes);
 }
 
@@ -357,7 +395,8 @@ hipError_t launch_gather(const GatherArgs& a, uint32_t tiles, hipStream_t) {
         touch(a.src[r], 0, a.bytes[r], false, "gather read");
         for (int q = 0; q < a.nranks; q++) {
             touch(a.dst[r * a.nranks + q], 0, a.bytes[r], true, "gather write");
-            if ((a.aligned >> r) & 1u) CHECK(al16(a.dst[r * a.nranks + q]), "gather: unaligned destination");
+            if ((a.aligned >> r) & 1u)
+                CHECK(line_al(a.dst[r * a.nranks + q]), "gather: aligned piece with a destination off its line");
         }
         if ((a.aligned >> r) & 1u) CHECK(al16(a.src[r]), "gather: unaligned source");
     }
@@ -389,7 +428,7 @@ hipError_t launch_all_to_all(const AllToAllArgs& a, uint32_t tiles, hipStream_t)
         touch(a.from[k], 0, a.bytes[k], false, "all_to_all read");
         touch(a.to[k], 0, a.bytes[k], true, "all_to_all write");
         if ((a.aligned[k >> 6] >> (k & 63)) & 1ull)
-            CHECK(al16(a.from[k]) && al16(a.to[k]), "all_to_all: aligned flag on an unaligned block");
+            CHECK(al16(a.from[k]) && line_al(a.to[k]), "all_to_all: aligned flag on a block off its lines");
         g_a2a_blocks.push_back(A2ABlock{static_cast<const char*>(a.from[k]), static_cast<const char*>(a.to[k]),
                                         a.bytes[k]});
     }
@@ -405,7 +444,7 @@ hipError_t launch_copy_segments(const SegCopyArgs& a, hipStream_t) {
         want.push_back(ceil_div((al ? 0 : reinterpret_cast<uintptr_t>(a.dst[k]) & (kGridAlign - 1)) + a.bytes[k], kSegCopyTileBytes));
         touch(a.src[k], 0, a.bytes[k], false, "copy_segments read");
         touch(a.dst[k], 0, a.bytes[k], true, "copy_segments write");
-        if ((a.aligned >> k) & 1ull) CHECK(al16(a.src[k]) && al16(a.dst[k]), "copy_segments: unaligned");
+        if ((a.aligned >> k) & 1ull) CHECK(al16(a.src[k]) && line_al(a.dst[k]), "copy_segments: off its lines");
     }
     check_tiles(a.tile_start, want, a.tile_start[a.nsegs], "copy_segments");
     return hipSuccess;
@@ -518,14 +557,19 @@ void reductions() {
         const dt_dtype dtype = dt_dtype(below(3));
         const dt_op op = dt_op(below(4));
         const size_t es = esize(dtype);
-        const size_t m = below(4) == 0 ? below(3) : below(3000);
-        const size_t skew = below(3) == 0 ? es * below(4) : 0;  // unaligned buffers sometimes
+        // sizes up to about 1 MiB per rank (past the line-grid two-shot
+        // threshold), buffers aligned, at one shared offset, or each at an
+        // offset of its own (up to 158 elements)
+        const size_t m = below(4) == 0 ? below(3) : below(5) == 0 ? 20000 + below(20000) : below(3000);
+        const int mode = int(below(3));
+        const size_t shared_skew = es * below(4);
+        auto skew = [&]() { return mode == 0 ? size_t(0) : mode == 1 ? shared_skew : es * below(80); };
         std::vector<const void*> send(p);
         std::vector<void*> recv(p), shard(p);
         for (int r = 0; r < p; r++) {
-            send[r] = pool.get(p * m * es, skew, false);
-            recv[r] = pool.get(p * m * es, skew, true);
-            shard[r] = pool.get(m * es, skew, true);
+            send[r] = pool.get(p * m * es, skew(), false);
+            recv[r] = pool.get(p * m * es, skew(), true);
+            shard[r] = pool.get(m * es, skew(), true);
         }
         expect(dt_allreduce(send.data(), recv.data(), p, p * m, dtype, op, nullptr), DT_OK, "allreduce");
         expect(dt_reduce_scatter(send.data(), shard.data(), p, m, dtype, op, nullptr), DT_OK, "reduce_scatter");
@@ -969,6 +1013,9 @@ void two_shot() {
         bool in_place;
         int windows;     // two-shot windows expected (0: one-shot only)
         size_t skew = 0; // bytes past a 4 KiB boundary, the same for every buffer: a peeled head
+        size_t send_skew = SIZE_MAX;  // the inputs' own offset (default: skew)
+        size_t rank_step = 0;         // rank r's buffers a further r * rank_step bytes in
+        int grid = 0;                 // line-grid ReduceScatter launches expected
     };
     const size_t M = size_t(1) << 20;
     const Case cases[] = {
@@ -1013,6 +1060,14 @@ void two_shot() {
         {8, DT_BFLOAT16, 64 * M, false, 1, 512},      // line-aligned, 512 bytes into a 1 KiB tile: a 1 KiB peel
         {16, DT_FLOAT32, 96 * M, true, 6, 256},       // the same before windows, in place
         {4, DT_FLOAT32, 16 * M, false, 0, 512},       // one-shot: no peel for line-aligned buffers
+        // offsets that differ between inputs and outputs or between ranks:
+        // the line-grid two-shot form from 8 MiB per rank, window by window
+        {8, DT_BFLOAT16, 4 * M + 5, false, 0, 0, 2, 0, 1},        // inputs 2 bytes off, 8 MiB + 10 B
+        {8, DT_BFLOAT16, 4 * M - 8, false, 0, 0, 2, 0, 0},        // just below 8 MiB: the element kernel
+        {16, DT_FLOAT32, 16 * M + 3, false, 0, 4, 0, 0, 1},       // outputs 4 bytes off
+        {3, DT_BFLOAT16, 8 * M + 1, true, 0, 0, 0, 2, 1},         // in place, rank r 2r bytes off
+        {5, DT_INT32, 4 * M + 7, false, 0, 16, 8, 4, 1},          // every buffer at an offset of its own
+        {8, DT_BFLOAT16, 160 * M + 3, false, 0, 2, 0, 0, 3},      // 320 MiB: three 128 MiB windows
     };
     char* base = reinterpret_cast<char*>(uintptr_t(1) << 45);  // fake, never dereferenced
     for (const Case& c : cases) {
@@ -1020,25 +1075,29 @@ void two_shot() {
         const size_t es = esize(c.dtype), bytes = c.count * es;
         const void* send[16];
         void* recv[16];
+        const size_t send_skew = c.send_skew == SIZE_MAX ? c.skew : c.send_skew;
         for (int r = 0; r < c.p; r++) {
-            recv[r] = base + (uint64_t(r) << 33) + c.skew;
+            recv[r] = base + (uint64_t(r) << 33) + c.skew + r * c.rank_step;
             reg(recv[r], bytes, true);
             if (c.in_place) {
                 send[r] = recv[r];
             } else {
-                send[r] = base + (uint64_t(32 + r) << 33) + c.skew;
+                send[r] = base + (uint64_t(32 + r) << 33) + send_skew + r * c.rank_step;
                 reg(send[r], bytes, false);
             }
         }
         g_gather_pieces.clear();
         dt::g_rs_launches = 0;
+        dt::g_grid_rs_launches = 0;
         dt::g_fold_log.clear();
         dt::g_log_folds = true;
         expect(dt_allreduce(send, recv, c.p, c.count, c.dtype, DT_SUM, nullptr), DT_OK, "two-shot allreduce");
         dt::g_log_folds = false;
         CHECK(dt::g_rs_launches == c.windows, "allreduce of %zu bytes per rank at P=%d: %d two-shot windows, expected %d",
               bytes, c.p, dt::g_rs_launches, c.windows);
-        if (c.windows == 0) CHECK(g_gather_pieces.empty(), "one-shot allreduce with a fan-out");
+        CHECK(dt::g_grid_rs_launches == c.grid, "allreduce of %zu bytes per rank at P=%d: %d line-grid launches, expected %d",
+              bytes, c.p, dt::g_grid_rs_launches, c.grid);
+        if (c.windows == 0 && c.grid == 0) CHECK(g_gather_pieces.empty(), "one-shot allreduce with a fan-out");
         // every fan-out piece: a range of rank r's own output, copied to the same offset of output 0
         for (const GatherPiece& g : g_gather_pieces) {
             int owner = -1;
@@ -1070,7 +1129,11 @@ int main() {
     overlaps();
     big_fan_out();
     two_shot();
+    dt::g_grid_rs_launches = 0;
     reductions();
+    // the random reductions reach the line-grid ReduceScatter (buffers at
+    // offsets of their own)
+    CHECK(dt::g_grid_rs_launches >= 20, "the line-grid ReduceScatter ran %d times", dt::g_grid_rs_launches);
     copies();
     buckets();
     bucket_big();

@@ -246,3 +246,88 @@ def test_reduce_scatter_shared_offset_peels(dt, p, dtype, m, off):
     for lo, hi in spans + [(ybig.numel(), ybig.numel())]:
         assert torch.equal(ybig[at:lo], outside[at:lo]), f"bytes [{at}, {lo}) outside the outputs changed"
         at = hi
+
+
+# per-rank element offsets (mod 64) by rule name
+_RULES = {"0": lambda r: 0, "1": lambda r: 1, "2": lambda r: 2, "8": lambda r: 8, "r": lambda r: r,
+          "2r+1": lambda r: 2 * r + 1, "3r+1": lambda r: 3 * r + 1, "3r": lambda r: 3 * r, "5r": lambda r: 5 * r,
+          "8r": lambda r: 8 * r}
+
+
+def _offsets(rule, p):
+    return [_RULES[rule](r) % 64 for r in range(p)]
+
+
+def _placed(src, offsets):
+    """Guarded copies of src, copy r placed offsets[r] elements past a 16-byte
+    aligned start."""
+    out = []
+    for x, off in zip(src, offsets):
+        g = Guarded(x.numel(), x.dtype, offset_elems=off)
+        g.t.copy_(x.reshape(-1))
+        out.append(g)
+    return out
+
+
+@pytest.mark.parametrize("p,dtype,n,send_off,recv_off,op,in_place", [
+    # the RS -> AG workload's size; inputs at offsets of their own, outputs aligned:
+    # the line-grid ReduceScatter, then the fan-out on its aligned path
+    (8, torch.bfloat16, 8192 * 8192, "r", "0", "sum", False),
+    # outputs at offsets of their own too: the fan-out's byte path
+    (8, torch.bfloat16, (1 << 22) + 5, "r", "3r+1", "sum", False),
+    # outputs 4 bytes off, inputs aligned; ragged
+    (16, torch.float32, (16 << 20) + 3, "0", "1", "sum", False),
+    # outputs 16 bytes past a line, inputs 2 bytes off
+    (4, torch.bfloat16, 1 << 22, "1", "8", "max", False),
+    (3, torch.bfloat16, (1 << 22) + 1, "2r+1", "r", "min", False),
+    (5, torch.int32, (1 << 21) + 1, "r", "2", "max", False),
+    (6, torch.float32, 1 << 21, "r", "r", "avg", True),    # in place, every rank at its own offset
+    # below the line-grid threshold (8 MiB per rank): the element kernel
+    (4, torch.bfloat16, 300001, "r", "0", "sum", False),
+    (4, torch.float32, 1000, "r", "0", "sum", False),
+])
+def test_allreduce_offsets_of_their_own(dt, orc, p, dtype, n, send_off, recv_off, op, in_place):
+    """Buffers at offsets that differ between ranks or between inputs and
+    outputs, so no peel aligns them all: the line-grid two-shot form (or the
+    element kernel below its threshold)."""
+    note(f"allreduce offsets of their own P={p} {dtype} n={n} send {send_off} recv {recv_off} {op} in_place={in_place}")
+    src = (synth.normal_ranks(p, (n,), seed=7 * p, device="cuda", dtype=dtype) if dtype == torch.bfloat16
+           else synth.int_ranks(p, n, seed=7 * p, device="cuda") if dtype == torch.int32
+           else synth.uniform_ranks(p, n, seed=7 * p, device="cuda"))
+    xs = _placed(src, _offsets(send_off, p))
+    ys = xs if in_place else [Guarded(n, dtype, offset_elems=o).poison() for o in _offsets(recv_off, p)]
+    dt.dt_allreduce([g.t for g in xs], [g.t for g in ys], op=op)
+    torch.cuda.synchronize()
+    want = orc.allreduce([to_np(x) for x in src], op)[0]
+    view = (lambda t: t.view(torch.int16)) if dtype == torch.bfloat16 else (lambda t: t.view(torch.int32))
+    compare(to_np(ys[0].t), want, "rank 0")
+    for q in range(p):
+        ys[q].check()
+        assert torch.equal(view(ys[q].t), view(ys[0].t)), f"rank {q} differs from rank 0"
+
+
+@pytest.mark.parametrize("p,dtype,m,send_off,recv_off,op", [
+    (8, torch.bfloat16, 8192 * 1024, "r", "2r+1", "sum"),   # the RS -> AG workload's size
+    (8, torch.float32, 4096 + 8, "0", "1", "sum"),           # outputs 4 bytes off only
+    (8, torch.bfloat16, 65536, "0", "8r", "sum"),            # outputs 16 bytes apart past their lines
+    (16, torch.bfloat16, 1000, "r", "5r", "max"),            # chunks shorter than a tile
+    (7, torch.int32, 12345, "3r", "r", "min"),
+    (2, torch.bfloat16, 3, "1", "0", "avg"),                 # shorter than one vector
+    (1, torch.float32, 777, "1", "2", "sum"),                # one rank: a copy
+])
+def test_reduce_scatter_offsets_of_their_own(dt, orc, p, dtype, m, send_off, recv_off, op):
+    """ReduceScatter over buffers whose offsets differ: the line-grid kernel
+    (each chunk tiled over its output's lines, every input shifted into
+    place)."""
+    note(f"reduce_scatter offsets of their own P={p} {dtype} m={m} send {send_off} recv {recv_off} {op}")
+    src = (synth.normal_ranks(p, (p * m,), seed=5 * p, device="cuda", dtype=dtype) if dtype == torch.bfloat16
+           else synth.int_ranks(p, p * m, seed=5 * p, device="cuda") if dtype == torch.int32
+           else synth.uniform_ranks(p, p * m, seed=5 * p, device="cuda"))
+    xs = _placed(src, _offsets(send_off, p))
+    ys = [Guarded(m, dtype, offset_elems=o).poison() for o in _offsets(recv_off, p)]
+    dt.dt_reduce_scatter([g.t for g in xs], [g.t for g in ys], op=op)
+    torch.cuda.synchronize()
+    want = orc.reduce_scatter([to_np(x) for x in src], op)
+    for r in range(p):
+        ys[r].check()
+        compare(to_np(ys[r].t), want[r], f"rank {r}")

@@ -98,6 +98,22 @@ MUTANTS = {
     # the previous layer's fused buffers, whose AllReduce is still pending, may be written again
     "hsdp_fused_reuse_allowed": ("            if (h->has_prev) add_span(rd, h->prev_fused[r], h->prev_total * es, ",
                                  "            if (false) add_span(rd, h->prev_fused[r], h->prev_total * es, "),
+    # a line-grid fan-out piece takes its source shift without the grid's lead
+    "shifted_gather_shift_without_lead": (
+        "a.lead[k] = uint32_t(md) | uint32_t((reinterpret_cast<uintptr_t>(src[k]) - md) & 15u) << 16;",
+        "a.lead[k] = uint32_t(md) | uint32_t(reinterpret_cast<uintptr_t>(src[k]) & 15u) << 16;"),
+    # fan-out destinations at a 16-byte boundary off their lines take the source-tiled path
+    "gather_aligned_off_line": ("if (same && md == 0 && aligned16(src[k])) {",
+                                "if (same && md % 16 == 0 && aligned16(src[k])) {"),
+    # all-to-all blocks at a 16-byte boundary off their lines take the source-tiled path
+    "a2a_aligned_off_line": ("const bool al = aligned16(from) && line_aligned(to);",
+                             "const bool al = aligned16(from) && aligned16(to);"),
+    # the line-grid ReduceScatter takes each chunk's grid from the inputs
+    "grid_rs_lead_from_send": ("g.lead[r] = uint32_t(reinterpret_cast<uintptr_t>(out[r]) & (dt::kGridAlign - 1));",
+                               "g.lead[r] = uint32_t(reinterpret_cast<uintptr_t>(send[r]) & (dt::kGridAlign - 1));"),
+    # the line-grid two-shot AllReduce gives its last chunk a full chunk
+    "grid_two_shot_last_chunk_full": ("            const size_t last = count - mce * size_t(nranks - 1);",
+                                      "            const size_t last = mce;"),
     # only exact pointer equality is refused: a partial overlap of outputs slips through
     "overlap_check_skipped": ("    for (size_t i = 1; i < writes.size(); i++) {",
                               "    for (size_t i = writes.size(); i < writes.size(); i++) {"),
