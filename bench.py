@@ -450,7 +450,14 @@ def configs(dt, torch, steps: int, warmup: int) -> dict:
     xs, ys = [b[1:1 + n] for b in base], [b[1:1 + n] for b in outb]
     measure("c2_allreduce_misaligned_p8_bf16", lambda: dt.dt_allreduce(xs, ys), 2 * P * n * 2, per_graph=4)
     out["c2_allreduce_misaligned_p8_bf16"]["note"] = "every buffer 2 bytes past 16-byte alignment"
-    del base, outb, xs, ys
+    xs = [b[:n] for b in base]
+    ro = [torch.empty(n // P + 8, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    rs_out = [r[1:n // P + 1] for r in ro]
+    measure("c2_reduce_scatter_outputs_misaligned_p8_bf16", lambda: dt.dt_reduce_scatter(xs, rs_out),
+            (P + 1) * n * 2, per_graph=4)
+    out["c2_reduce_scatter_outputs_misaligned_p8_bf16"]["note"] = \
+        "inputs aligned, outputs 2 bytes past 16-byte alignment: offsets that no peel can share"
+    del base, outb, xs, ys, ro, rs_out
     rows_odd = [int(c) * w + 2 * k + 1 for k, c in enumerate(counts)]
     xs = [torch.randn(c, device="cuda").to(torch.bfloat16) for c in rows_odd]
     ys = [torch.empty(sum(rows_odd), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
@@ -815,9 +822,11 @@ def probe_rows(dt, torch, reps: int = 3):
     P=8), one layer of the gradient pipeline (the segmented ReduceScatter
     at P=4 and the bucket folds at P=2), the AllToAll between shard
     dimensions of the bf16 [32768, 16384] tensor in both directions, the
-    ReplicateToShard of [8192, 8192] bf16 per rank and the AllReduce of the
-    bench step's inputs 2 bytes off alignment.  Prints one JSON line per
-    workload with its algorithmic bytes."""
+    ReplicateToShard of [8192, 8192] bf16 per rank, the AllReduce of the
+    bench step's inputs 2 bytes off alignment, the ReduceScatter of the same
+    inputs into outputs 2 bytes off (the line-grid kernel) and the uneven
+    AllGather in bf16 with odd counts.  Prints one JSON line per workload
+    with its algorithmic bytes."""
     import numpy as np
     import synth
     w = synth.ROW_WIDTH
@@ -889,7 +898,19 @@ def probe_rows(dt, torch, reps: int = 3):
         x[1:n + 1].copy_(src.reshape(-1))
     run("allreduce_misaligned_p8_bf16", lambda: dt.dt_allreduce([x[1:n + 1] for x in xo], [y[1:n + 1] for y in yo]),
         2 * P * s_bytes, ["k_reduce_elems", "k_reduce_scatter_vec<1, 0, 8, 64, 1>", "k_gather<8, true, 1, 64>"])
-    del xs, xo, yo
+    # the ReduceScatter with aligned inputs and outputs 2 bytes off: the line-grid kernel
+    ro = [torch.empty(n // P + 8, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    run("reduce_scatter_outputs_off_p8_bf16", lambda: dt.dt_reduce_scatter(xs, [r[1:n // P + 1] for r in ro]),
+        (P + 1) * s_bytes, ["k_reduce_scatter_grid<1, 0, 8>"])
+    del xs, xo, yo, ro
+    torch.cuda.empty_cache()
+    # the uneven AllGather in bf16 with odd counts (pieces 2 or 8 bytes off: the line-grid fan-out)
+    rows_odd = [int(c) * w + 2 * k + 1 for k, c in enumerate(counts)]
+    xs = [torch.randn(c, device="cuda").to(torch.bfloat16) for c in rows_odd]
+    ys = [torch.empty(sum(rows_odd), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    run("uneven_all_gather_odd_bf16_p8", lambda: dt.dt_all_gather(xs, ys), (1 + P) * sum(rows_odd) * 2,
+        ["k_gather<8, true, 1, 128>", "k_gather_touch"])
+    del xs, ys
     torch.cuda.empty_cache()
     a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
