@@ -196,17 +196,34 @@ uint64_t allreduce_window(int nranks, uint64_t bytes_per_rank) {
 }
 
 // Validated AllReduce over one contiguous range per rank, in one call.
-// ReduceScatter over the chunk outputs' line grids (dt::GridFoldArgs):
-// chunk c is elements [c * in_stride, c * in_stride + n_c) of every input,
-// n_c = count but last_count for the last chunk, folded into out[c].  For
-// element-aligned buffers that share no offset.
+// ReduceScatter over line grids (dt::GridFoldArgs): chunk c is elements
+// [c * in_stride, c * in_stride + n_c) of every input, n_c = count but
+// last_count for the last chunk, folded into out[c].  For element-aligned
+// buffers that share no offset.  The tiles follow the inputs' lines (one
+// aligned load per input and lane) when every input sits at one offset
+// within a line and, in every chunk, the output vectors then start on the
+// output's lines (the output at most 16 bytes before a line where a tile
+// starts); otherwise each output's lines.  P=8 bf16, 128 MiB per rank,
+// in-process A/B: inputs 6, 8 or 14 bytes off with aligned outputs 193-198 us
+// on the input grid against 220-224 us on the output grid, even at 2 bytes
+// off; but outputs 2-18 bytes off with aligned inputs 260-293 us on the
+// input grid (its vector stores then start inside a line) against 222-225.
 dt_status reduce_scatter_grid(const void* const* send, void* const* out, int nranks, size_t in_stride, size_t count,
                               size_t last_count, dt_dtype dtype, dt_op op, hipStream_t stream, const char* what) {
     dt::GridFoldArgs g = {};
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(send[0]) & (dt::kGridAlign - 1);
+    const uint64_t stride_bytes = uint64_t(in_stride) * esize_of(dtype);
+    g.src_grid = 1;
+    for (int r = 0; r < nranks; r++) {
+        if ((reinterpret_cast<uintptr_t>(send[r]) & (dt::kGridAlign - 1)) != s0) g.src_grid = 0;
+        const uint64_t h = (reinterpret_cast<uintptr_t>(out[r]) - (s0 + r * stride_bytes)) & (dt::kGridAlign - 1);
+        if (h != 0 && h < dt::kGridAlign - 16) g.src_grid = 0;
+    }
     for (int r = 0; r < nranks; r++) {
         g.src[r] = send[r];
         g.dst[r] = out[r];
-        g.lead[r] = uint32_t(reinterpret_cast<uintptr_t>(out[r]) & (dt::kGridAlign - 1));
+        g.lead[r] = g.src_grid ? uint32_t((s0 + r * stride_bytes) & (dt::kGridAlign - 1))
+                               : uint32_t(reinterpret_cast<uintptr_t>(out[r]) & (dt::kGridAlign - 1));
     }
     g.in_stride = in_stride;
     g.count = count;

@@ -145,6 +145,18 @@ __device__ __forceinline__ u32x4 load16_any(const char* p, uint32_t misalign) {
     if (misalign == 0) return lo;
     return funnel16(lo, load16_h<NT>(a + 16), misalign);
 }
+// Elements of v (ES bytes each, little endian) between its bytes j0 and j1
+// that fall inside [0, n) when v's byte 0 is byte `at` of a range at d:
+// one store each.
+template <int ES>
+__device__ __forceinline__ void store_vec_elems(char* d, int64_t at, const u32x4& v, int j0, int j1, int64_t n) {
+#pragma unroll
+    for (int j = 0; j < 16; j += ES) {
+        if (j < j0 || j >= j1 || at + j < 0 || at + j >= n) continue;
+        if constexpr (ES == 2) *reinterpret_cast<uint16_t*>(d + at + j) = uint16_t(v[j >> 2] >> ((j & 2) * 8));
+        else *reinterpret_cast<uint32_t*>(d + at + j) = v[j >> 2];
+    }
+}
 // Byte j of a vector.
 __device__ __forceinline__ char vec_byte(const u32x4& x, int j) { return char(x[j >> 2] >> ((j & 3) * 8)); }
 

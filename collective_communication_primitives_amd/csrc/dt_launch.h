@@ -26,12 +26,14 @@ struct ReduceArgs {
     int rs;                // 1: ReduceScatter (grid.y = chunk), 0: AllReduce
 };
 
-// ReduceScatter over each output chunk's 128-byte line grid, for element-
-// aligned buffers that share no offset (the vector kernels need every buffer
-// 16-byte aligned, or all at one offset).  Chunk c is elements
-// [c * in_stride, c * in_stride + n_c) of every input, n_c = count for every
-// chunk but the last (last_count); it goes to dst[c], whose first byte sits
-// lead[c] = dst[c] & (kGridAlign - 1) bytes into a line.
+// ReduceScatter over a 128-byte line grid, for element-aligned buffers that
+// share no offset (the vector kernels need every buffer 16-byte aligned, or
+// all at one offset).  Chunk c is elements [c * in_stride, c * in_stride +
+// n_c) of every input, n_c = count for every chunk but the last
+// (last_count); it goes to dst[c].  With src_grid, every input sits at one
+// offset within a line and the tiles follow the inputs' lines: lead[c] is
+// that offset at chunk c's start.  Otherwise the tiles follow each output's
+// lines: lead[c] = dst[c] & (kGridAlign - 1).
 struct GridFoldArgs {
     const void* src[kMaxRanksHost];
     void* dst[kMaxRanksHost];
@@ -41,6 +43,7 @@ struct GridFoldArgs {
     uint64_t last_count;
     int nranks;
     int nchunks;
+    int src_grid;
 };
 constexpr uint64_t kGridFoldTileBytes = 1024;  // one wave, one vector per lane
 

@@ -225,6 +225,75 @@ __global__ __launch_bounds__(kWaveBlock) void k_reduce_scatter_grid(GridFoldArgs
     }
 }
 
+// The same ReduceScatter when every input sits at one offset within a line
+// (src_grid): tile t of chunk c covers chunk bytes [A, A + 1 KiB), A =
+// t * 1 KiB - lead[c], which start on a line of every input, so each lane
+// loads one aligned vector per input (non-temporal buffer loads, as the
+// aligned kernel; windows at the chunk's ends) and no line is read by two
+// workgroups.  The folded vector y covers chunk bytes [A + 16 i, +16) of lane
+// i; when the output sits e bytes into a vector there, lane i stores the
+// aligned output vector made of y's last e bytes and the next lane's first
+// 16 - e (passed across by a shuffle of the result, once per lane), the
+// wave's last lane its own last e bytes, and lane 0 the tile's first 16 - e:
+// every output byte once, the partial vectors element by element.  The
+// output-grid kernel above loads two vectors per input and reads each
+// tile's boundary line twice (1.11 of the algorithmic bytes).
+template <int DT, int OP, int P>
+__global__ __launch_bounds__(kWaveBlock) void k_reduce_scatter_srcgrid(GridFoldArgs a) {
+    constexpr int ES = DT == kBF16 ? 2 : 4;
+    constexpr int64_t kTile = int64_t(kGridFoldTileBytes);
+    const uint32_t c = blockIdx.y;
+    const int64_t n = int64_t(c + 1 == uint32_t(a.nchunks) ? a.last_count : a.count) * ES;  // chunk bytes
+    const int64_t A = int64_t(blockIdx.x) * kTile - int64_t(a.lead[c]);  // a line of every input
+    if (A >= n) return;                                                   // past the end of this chunk
+    const int64_t q = A + int64_t(threadIdx.x) * 16;
+    const uint64_t in_off = uint64_t(c) * a.in_stride * uint64_t(ES);
+    u32x4 x[P];
+    if (A >= 0 && A + kTile <= n) {
+#pragma unroll
+        for (int r = 0; r < P; r++) {
+            const rsrc_t in = make_rsrc(static_cast<const char*>(a.src[r]) + in_off + A, uint32_t(kTile));
+            x[r] = bload16<kPolNT>(in, threadIdx.x * 16);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < P; r++) {
+            const LoadWindow w = load_window(static_cast<const char*>(a.src[r]) + in_off, n, A, kTile);
+            x[r] = window_load<kPolNT>(w, q);
+        }
+    }
+    const u32x4 y = fold_vec<DT, OP, P>(x, P);
+    char* d = static_cast<char*>(a.dst[c]);
+    const uint32_t e = uint32_t((reinterpret_cast<uintptr_t>(d) + uint64_t(A)) & 15u);  // uniform
+    if (e == 0) {
+        if (q >= 0 && q + 16 <= n) {
+            const rsrc_t out = make_rsrc(d + A, uint32_t(kTile));
+            bstore16<kPolDevice>(out, threadIdx.x * 16, y);
+        } else {
+            store_vec_elems<ES>(d, q, y, 0, 16, n);
+        }
+        return;
+    }
+    u32x4 y1;  // the next lane's vector (every lane takes part in the shuffle)
+    y1[0] = __shfl_down(y[0], 1u, 64);
+    y1[1] = __shfl_down(y[1], 1u, 64);
+    y1[2] = __shfl_down(y[2], 1u, 64);
+    y1[3] = __shfl_down(y[3], 1u, 64);
+    if (threadIdx.x == 0) store_vec_elems<ES>(d, q, y, 0, 16 - int(e), n);  // the tile's head
+    if (threadIdx.x + 1 == kWaveBlock) {
+        store_vec_elems<ES>(d, q, y, 16 - int(e), 16, n);  // the tile's tail
+        return;
+    }
+    const int64_t o = q + 16 - int64_t(e);  // chunk byte of this lane's aligned output vector
+    const u32x4 v = funnel16(y, y1, 16u - e);
+    if (o >= 0 && o + 16 <= n) {
+        const rsrc_t out = make_rsrc(d + A + 16 - int64_t(e), uint32_t(kTile));
+        bstore16<kPolDevice>(out, threadIdx.x * 16, v);
+    } else {
+        store_vec_elems<ES>(d, o, v, 0, 16, n);
+    }
+}
+
 // ------------------------------------------------------ bucket pieces ----
 // Piece tables come in two sizes: PieceArgs (32 pieces, 3.3 KiB of kernel
 // arguments, for buckets of a few large tensors) and CoalescedArgs (512
@@ -505,7 +574,10 @@ hipError_t reduce_scatter_grid_p(const GridFoldArgs& a, hipStream_t s) {
     }
     if (tiles == 0) return hipSuccess;
     if (tiles > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    k_reduce_scatter_grid<DT, OP, P><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kWaveBlock, 0, s>>>(a);
+    if (a.src_grid)
+        k_reduce_scatter_srcgrid<DT, OP, P><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kWaveBlock, 0, s>>>(a);
+    else
+        k_reduce_scatter_grid<DT, OP, P><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kWaveBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 

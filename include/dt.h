@@ -39,9 +39,11 @@
  *    fast way; a two-shot AllReduce does the same for line-aligned buffers
  *    that share an offset within 1 KiB (its tiles then start on 1 KiB
  *    boundaries).  Folds over element-aligned buffers at offsets of their
- *    own (inputs and outputs apart, or rank by rank) tile each output over
- *    its 128-byte lines and shift every input into place from aligned
- *    loads: the ReduceScatter always, the AllReduce from 8 MiB per rank (as
+ *    own (inputs and outputs apart, or rank by rank) tile over 128-byte
+ *    lines (the inputs' where they share one offset and the outputs' vectors
+ *    then start on lines, else each output's) and shift every vector into
+ *    place from aligned loads: the ReduceScatter always, the AllReduce from
+ *    8 MiB per rank (as
  *    a ReduceScatter into each output's own chunk and a fan-out of the
  *    chunks); smaller AllReduces fold element by element.  The copy engines
  *    store whole 128-byte lines of every destination that does not start

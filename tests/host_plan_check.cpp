@@ -304,9 +304,11 @@ hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, 
 // elements in, count elements, last_count for the last chunk) folds into
 // dst[c], lead[c] bytes into its line.
 int g_grid_rs_launches = 0;
+int g_grid_rs_src_grid = -1;  // the last launch's mode
 hipError_t launch_reduce_scatter_grid(const GridFoldArgs& a, int dtype, int, hipStream_t) {
     g_launches++;
     g_grid_rs_launches++;
+    g_grid_rs_src_grid = a.src_grid;
     const uint64_t es = esize(dtype);
     CHECK(a.nranks >= 1 && a.nranks <= kMaxRanksHost && a.nchunks == a.nranks, "grid rs: %d ranks, %d chunks",
           a.nranks, a.nchunks);
@@ -316,8 +318,21 @@ hipError_t launch_reduce_scatter_grid(const GridFoldArgs& a, int dtype, int, hip
     for (int c = 0; c < a.nchunks; c++) {
         const uint64_t n = (c + 1 == a.nchunks ? a.last_count : a.count) * es;
         const uintptr_t d = reinterpret_cast<uintptr_t>(a.dst[c]);
-        CHECK(a.lead[c] == (d & (kGridAlign - 1)), "grid rs: chunk %d lead %u for an output at %llu mod 128", c,
-              a.lead[c], (unsigned long long)(d & (kGridAlign - 1)));
+        if (a.src_grid) {
+            // every input at one offset within a line; lead is that offset at the
+            // chunk's start; the output then starts at most 16 bytes before a line
+            const uint64_t h = (d - a.lead[c]) & (kGridAlign - 1);
+            CHECK(h == 0 || h >= kGridAlign - 16, "grid rs (input grid): chunk %d output %llu bytes into a line", c,
+                  (unsigned long long)h);
+            for (int r = 0; r < a.nranks; r++) {
+                const uintptr_t s = reinterpret_cast<uintptr_t>(a.src[r]) + c * a.in_stride * es;
+                CHECK(a.lead[c] == (s & (kGridAlign - 1)), "grid rs (input grid): chunk %d lead %u, input %d at %llu mod 128",
+                      c, a.lead[c], r, (unsigned long long)(s & (kGridAlign - 1)));
+            }
+        } else {
+            CHECK(a.lead[c] == (d & (kGridAlign - 1)), "grid rs: chunk %d lead %u for an output at %llu mod 128", c,
+                  a.lead[c], (unsigned long long)(d & (kGridAlign - 1)));
+        }
         CHECK(d % es == 0, "grid rs: output %d not element-aligned", c);
         touch(a.dst[c], 0, n, true, "grid reduce_scatter write");
         for (int r = 0; r < a.nranks; r++) {
@@ -1124,11 +1139,59 @@ void two_shot() {
     g_bufs.clear();
 }
 
+// ReduceScatters whose buffers share no offset, with the grid each should
+// take: the inputs' lines when the inputs share one offset and every
+// chunk's output starts at most 16 bytes before a line of its grid, else the
+// outputs' lines.  Chunk strides off the lines make the input offset differ
+// from chunk to chunk.
+void grid_reduce_scatter() {
+    struct Case {
+        int p;
+        dt_dtype dtype;
+        size_t recvcount;
+        size_t send_skew[4];
+        size_t recv_skew[4];
+        int src_grid;
+    };
+    const Case cases[] = {
+        // bf16, 2000-byte chunks (80 mod 128): inputs 2 bytes off, outputs 2 bytes before each chunk's input line
+        {4, DT_BFLOAT16, 1000, {2, 2, 2, 2}, {0, 80, 32, 112}, 1},
+        // the outputs 4 bytes past each chunk's input offset instead: the output grid
+        {4, DT_BFLOAT16, 1000, {2, 2, 2, 2}, {6, 86, 38, 118}, 0},
+        // fp32, inputs at two offsets (4000-byte chunks, 32 mod 128), outputs on their chunks' lines
+        {2, DT_FLOAT32, 1000, {0, 4}, {0, 32}, 0},
+        // fp32, inputs 8 bytes off, outputs aligned, chunks of whole lines: 120 bytes into a line
+        {3, DT_FLOAT32, 4096 * 3, {8, 8, 8}, {0, 0, 0}, 1},
+        // the same with chunks 20 bytes past whole lines: later chunks' outputs fall inside lines
+        {3, DT_FLOAT32, 4096 * 3 + 5, {8, 8, 8}, {0, 0, 0}, 0},
+    };
+    char* base = reinterpret_cast<char*>(uintptr_t(5) << 44);  // fake, never dereferenced
+    for (const Case& c : cases) {
+        g_bufs.clear();
+        const size_t es = esize(c.dtype);
+        const void* send[4];
+        void* recv[4];
+        for (int r = 0; r < c.p; r++) {
+            send[r] = base + (uint64_t(r) << 33) + c.send_skew[r];
+            reg(send[r], c.p * c.recvcount * es, false);
+            recv[r] = base + (uint64_t(16 + r) << 33) + c.recv_skew[r];
+            reg(recv[r], c.recvcount * es, true);
+        }
+        dt::g_grid_rs_src_grid = -1;
+        expect(dt_reduce_scatter(send, recv, c.p, c.recvcount, c.dtype, DT_SUM, nullptr), DT_OK,
+               "reduce_scatter over line grids");
+        CHECK(dt::g_grid_rs_src_grid == c.src_grid, "reduce_scatter P=%d: grid mode %d, expected %d", c.p,
+              dt::g_grid_rs_src_grid, c.src_grid);
+    }
+    g_bufs.clear();
+}
+
 int main() {
     validation();
     overlaps();
     big_fan_out();
     two_shot();
+    grid_reduce_scatter();
     dt::g_grid_rs_launches = 0;
     reductions();
     // the random reductions reach the line-grid ReduceScatter (buffers at

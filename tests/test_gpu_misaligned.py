@@ -273,6 +273,8 @@ def _placed(src, offsets):
     # the RS -> AG workload's size; inputs at offsets of their own, outputs aligned:
     # the line-grid ReduceScatter, then the fan-out on its aligned path
     (8, torch.bfloat16, 8192 * 8192, "r", "0", "sum", False),
+    # inputs 2 bytes off, outputs aligned: the input-grid ReduceScatter, then the aligned fan-out
+    (8, torch.bfloat16, 8192 * 8192, "1", "0", "sum", False),
     # outputs at offsets of their own too: the fan-out's byte path
     (8, torch.bfloat16, (1 << 22) + 5, "r", "3r+1", "sum", False),
     # outputs 4 bytes off, inputs aligned; ragged
@@ -308,6 +310,8 @@ def test_allreduce_offsets_of_their_own(dt, orc, p, dtype, n, send_off, recv_off
 
 @pytest.mark.parametrize("p,dtype,m,send_off,recv_off,op", [
     (8, torch.bfloat16, 8192 * 1024, "r", "2r+1", "sum"),   # the RS -> AG workload's size
+    (8, torch.bfloat16, 8192 * 1024, "1", "0", "sum"),      # inputs 2 bytes off, outputs aligned: the input grid
+    (4, torch.float32, (1 << 20) + 32, "2", "0", "max"),    # inputs 8 bytes off; chunks end inside a tile
     (8, torch.float32, 4096 + 8, "0", "1", "sum"),           # outputs 4 bytes off only
     (8, torch.bfloat16, 65536, "0", "8r", "sum"),            # outputs 16 bytes apart past their lines
     (16, torch.bfloat16, 1000, "r", "5r", "max"),            # chunks shorter than a tile
