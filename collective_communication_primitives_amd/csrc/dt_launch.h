@@ -45,7 +45,7 @@ struct GridFoldArgs {
     int nchunks;
     int src_grid;
 };
-constexpr uint64_t kGridFoldTileBytes = 1024;  // one wave, one vector per lane
+constexpr uint64_t kGridFoldTileBytes = 1024;  // the input-grid tile: one wave, one vector per lane
 
 // Multi-tensor pieces of one bucket.  Piece k of rank r starts at
 // ptr[k*nranks + r]; ws[r] + wpos[k] is its place in rank r's bucket buffer.

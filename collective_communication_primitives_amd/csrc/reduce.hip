@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_elems(ReduceArgs a) {
 
 // ReduceScatter over each output chunk's line grid (GridFoldArgs), for
 // buffers that share no offset.  Tile t of chunk c covers bytes
-// [t * 1 KiB, (t + 1) * 1 KiB) of the grid that starts at the line holding
+// [t * 2 KiB, (t + 1) * 2 KiB) of the grid that starts at the line holding
 // the chunk's first output byte, lead bytes before it; grid.y = chunk.  (An
 // XCD-contiguous tile order, for the line that neighbouring tiles' loads
 // share, ran 10% slower.)  Every lane builds its 16-byte grid vector of
@@ -153,10 +153,16 @@ __global__ __launch_bounds__(kBlock) void k_reduce_elems(ReduceArgs a) {
 // at 128 MiB per rank, outputs 2 bytes off and inputs aligned (or the
 // reverse): 215 us (0.70 of peak), against 556 us on the element kernel
 // these buffers took before and 181 us for aligned buffers.
+// Two waves per workgroup (128 threads, a 2 KiB tile): the boundary line
+// that neighbouring tiles' loads share then lies between the two waves of
+// one workgroup at every other boundary.  In-process A/B at P=8 bf16, 128
+// MiB per rank, outputs 2-18 bytes off: 214-216 us against 222-229 us with
+// one wave and 229-232 us with four.
+constexpr int kGridOutBlock = 128;
 template <int DT, int OP, int P>
-__global__ __launch_bounds__(kWaveBlock) void k_reduce_scatter_grid(GridFoldArgs a) {
+__global__ __launch_bounds__(kGridOutBlock) void k_reduce_scatter_grid(GridFoldArgs a) {
     constexpr int64_t ES = DT == kBF16 ? 2 : 4;
-    constexpr int64_t kTile = int64_t(kGridFoldTileBytes);
+    constexpr int64_t kTile = int64_t(kGridOutBlock) * 16;
     const uint32_t c = blockIdx.y;
     const int64_t n = int64_t(c + 1 == uint32_t(a.nchunks) ? a.last_count : a.count) * ES;  // chunk bytes
     const int64_t lead = int64_t(a.lead[c]);
@@ -566,10 +572,11 @@ hipError_t reduce_elems_dt(const ReduceArgs& a, int op, hipStream_t s) {
 
 template <int DT, int OP, int P>
 hipError_t reduce_scatter_grid_p(const GridFoldArgs& a, hipStream_t s) {
+    const uint64_t tile = a.src_grid ? kGridFoldTileBytes : uint64_t(kGridOutBlock) * 16;
     uint64_t tiles = 0;
     for (int c = 0; c < a.nchunks; c++) {
         const uint64_t n = (c + 1 == a.nchunks ? a.last_count : a.count) * (DT == kBF16 ? 2 : 4);
-        const uint64_t t = (a.lead[c] + n + kGridFoldTileBytes - 1) / kGridFoldTileBytes;
+        const uint64_t t = (a.lead[c] + n + tile - 1) / tile;
         tiles = t > tiles ? t : tiles;
     }
     if (tiles == 0) return hipSuccess;
@@ -577,7 +584,7 @@ hipError_t reduce_scatter_grid_p(const GridFoldArgs& a, hipStream_t s) {
     if (a.src_grid)
         k_reduce_scatter_srcgrid<DT, OP, P><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kWaveBlock, 0, s>>>(a);
     else
-        k_reduce_scatter_grid<DT, OP, P><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kWaveBlock, 0, s>>>(a);
+        k_reduce_scatter_grid<DT, OP, P><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kGridOutBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 
