@@ -233,14 +233,17 @@ dt_status reduce_scatter_grid(const void* const* send, void* const* out, int nra
     return check_hip(dt::launch_reduce_scatter_grid(g, dtype, op, stream), what);
 }
 
-// Bytes per rank from which an AllReduce over element-aligned buffers that
-// share no offset takes the two-shot form over line grids (the grid
-// ReduceScatter into each output's own chunk, then the fan-out) instead of
-// the element kernel.  Graph replays, outputs 2 bytes off and inputs aligned
-// (or the reverse): at 4 MiB per rank the two forms are even (P=8 bf16) or
-// the element kernel leads by 10-30% (P=4 fp32); at 16 MiB the two-shot
-// form leads by 25% (P=8 bf16, 51 against 68 us).
-constexpr uint64_t kGridTwoShotMinBytes = 8ull << 20;
+// Whether an AllReduce over element-aligned buffers that share no offset
+// takes the two-shot form over line grids (the grid ReduceScatter into each
+// output's own chunk, then the fan-out) rather than the element kernel: once
+// its footprint, 2 * P * S bytes, no longer fits the Infinity Cache.  Graph
+// replays, outputs 2 bytes off and inputs aligned (or the reverse): P=8 bf16
+// at 16 MiB per rank 46 us on the element kernel against 50-52 us, at 32 MiB
+// 117-153 against 93-96 us; P=4 fp32 at 32 MiB 43 against 46-58 us, at 64 MiB
+// 105-121 against 90-119 us.
+bool grid_two_shot_pays(int nranks, uint64_t bytes_per_rank) {
+    return uint64_t(nranks) * bytes_per_rank >= (256ull << 20);
+}
 
 dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, size_t count, dt_dtype dtype,
                         dt_op op, hipStream_t stream) {
@@ -293,7 +296,7 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
         a.count = count - a.first;
         return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "allreduce (element path) launch");
     }
-    if (!vec && nranks > 1 && uint64_t(count) * es >= kGridTwoShotMinBytes) {
+    if (!vec && nranks > 1 && grid_two_shot_pays(nranks, uint64_t(count) * es)) {
         bool el = true;
         for (int r = 0; r < nranks; r++) el = el && elem_aligned(send[r], es) && elem_aligned(recv[r], es);
         // chunks of whole 1 KiB of elements, all but the last, as above

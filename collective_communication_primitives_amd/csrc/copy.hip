@@ -10,7 +10,10 @@
 // for the all-to-all.
 //
 // AllGather fans out: each source tile is read once and written to every
-// rank's output, (1 + P) bytes of HBM traffic per gathered byte.
+// rank's output, (1 + P) bytes of HBM traffic per gathered byte.  Stores go
+// out as whole 128-byte lines of the destinations: a destination that does
+// not start on a line (even at a 16-byte boundary) takes tiles over its line
+// grid, each vector built from aligned loads of the source.
 #include "dt_device.h"
 #include "dt_launch.h"
 

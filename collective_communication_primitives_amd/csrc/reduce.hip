@@ -150,14 +150,13 @@ __global__ __launch_bounds__(kBlock) void k_reduce_elems(ReduceArgs a) {
 // the choice of shift is uniform) and folds; a vector inside the chunk is
 // one aligned store, and a partial one at either end (loaded through
 // windows) stores its elements inside the chunk one by one.  P=8 bf16
-// at 128 MiB per rank, outputs 2 bytes off and inputs aligned (or the
-// reverse): 215 us (0.70 of peak), against 556 us on the element kernel
-// these buffers took before and 181 us for aligned buffers.
-// Two waves per workgroup (128 threads, a 2 KiB tile): the boundary line
-// that neighbouring tiles' loads share then lies between the two waves of
-// one workgroup at every other boundary.  In-process A/B at P=8 bf16, 128
-// MiB per rank, outputs 2-18 bytes off: 214-216 us against 222-229 us with
-// one wave and 229-232 us with four.
+// at 128 MiB per rank, outputs 2 bytes off and inputs aligned: 215 us (0.70
+// of peak), against 556 us on the element kernel these buffers took before
+// and 181 us for aligned buffers.  Two waves per workgroup (128 threads, a
+// 2 KiB tile), so that every other boundary line that neighbouring tiles'
+// loads share lies between two waves of one workgroup: in-process A/B with
+// the outputs 2-18 bytes off, 214-216 us against 222-229 us with one wave
+// and 229-232 us with four.
 constexpr int kGridOutBlock = 128;
 template <int DT, int OP, int P>
 __global__ __launch_bounds__(kGridOutBlock) void k_reduce_scatter_grid(GridFoldArgs a) {
@@ -217,17 +216,7 @@ __global__ __launch_bounds__(kGridOutBlock) void k_reduce_scatter_grid(GridFoldA
         u32x4 x[P];
 #pragma unroll
         for (int r = 0; r < P; r++) x[r] = sm[r] != 0 ? funnel16(lo[r], hi[r], sm[r]) : lo[r];
-        const u32x4 y = fold_vec<DT, OP, P>(x, P);
-        char* d = static_cast<char*>(a.dst[c]);
-#pragma unroll
-        for (int j = 0; j < int(16 / ES); j++) {
-            const int64_t b = p0 + j * ES;
-            if (b < 0 || b >= n) continue;
-            if constexpr (ES == 2)
-                *reinterpret_cast<uint16_t*>(d + b) = uint16_t(y[j >> 1] >> ((j & 1) * 16));
-            else
-                *reinterpret_cast<uint32_t*>(d + b) = y[j];
-        }
+        store_vec_elems<int(ES)>(static_cast<char*>(a.dst[c]), p0, fold_vec<DT, OP, P>(x, P), 0, 16, n);
     }
 }
 

@@ -43,7 +43,7 @@
  *    lines (the inputs' where they share one offset and the outputs' vectors
  *    then start on lines, else each output's) and shift every vector into
  *    place from aligned loads: the ReduceScatter always, the AllReduce from
- *    8 MiB per rank (as
+ *    P * S = 256 MiB (S the bytes per rank) on (as
  *    a ReduceScatter into each output's own chunk and a fan-out of the
  *    chunks); smaller AllReduces fold element by element.  The copy engines
  *    store whole 128-byte lines of every destination that does not start
@@ -96,8 +96,9 @@ typedef enum {
  * window (64 MiB per rank at P >= 16, 128 MiB at P = 5-15), each window an
  * AllReduce of its own in the two-shot form, so the window's chunks are
  * still in the Infinity Cache when they fan out.  Buffers at offsets of
- * their own take the two-shot form over line grids from 8 MiB per rank
- * (see the alignment convention above).  All forms fold in the
+ * their own take the two-shot form over line grids from nranks * count *
+ * element size = 256 MiB (see the alignment convention above).  All forms
+ * fold in the
  * same order and give identical bits.  In place is allowed (send[r] ==
  * recv[r]); any other overlap of a recv buffer with a send or recv buffer
  * is refused (DT_ERR_ARG).  send[r] and recv[r] hold `count` elements. */

@@ -1076,12 +1076,12 @@ void two_shot() {
         {16, DT_FLOAT32, 96 * M, true, 6, 256},       // the same before windows, in place
         {4, DT_FLOAT32, 16 * M, false, 0, 512},       // one-shot: no peel for line-aligned buffers
         // offsets that differ between inputs and outputs or between ranks:
-        // the line-grid two-shot form from 8 MiB per rank, window by window
-        {8, DT_BFLOAT16, 4 * M + 5, false, 0, 0, 2, 0, 1},        // inputs 2 bytes off, 8 MiB + 10 B
-        {8, DT_BFLOAT16, 4 * M - 8, false, 0, 0, 2, 0, 0},        // just below 8 MiB: the element kernel
+        // the line-grid two-shot form from P * S = 256 MiB, window by window
+        {8, DT_BFLOAT16, 16 * M + 5, false, 0, 0, 2, 0, 1},       // inputs 2 bytes off, 32 MiB + 10 B
+        {8, DT_BFLOAT16, 16 * M - 8, false, 0, 0, 2, 0, 0},       // just below: the element kernel
         {16, DT_FLOAT32, 16 * M + 3, false, 0, 4, 0, 0, 1},       // outputs 4 bytes off
-        {3, DT_BFLOAT16, 8 * M + 1, true, 0, 0, 0, 2, 1},         // in place, rank r 2r bytes off
-        {5, DT_INT32, 4 * M + 7, false, 0, 16, 8, 4, 1},          // every buffer at an offset of its own
+        {3, DT_BFLOAT16, 48 * M + 1, true, 0, 0, 0, 2, 1},        // in place, rank r 2r bytes off
+        {5, DT_INT32, 16 * M + 7, false, 0, 16, 8, 4, 1},         // every buffer at an offset of its own
         {8, DT_BFLOAT16, 160 * M + 3, false, 0, 2, 0, 0, 3},      // 320 MiB: three 128 MiB windows
     };
     char* base = reinterpret_cast<char*>(uintptr_t(1) << 45);  // fake, never dereferenced

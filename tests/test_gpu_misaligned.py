@@ -276,15 +276,16 @@ def _placed(src, offsets):
     # inputs 2 bytes off, outputs aligned: the input-grid ReduceScatter, then the aligned fan-out
     (8, torch.bfloat16, 8192 * 8192, "1", "0", "sum", False),
     # outputs at offsets of their own too: the fan-out's byte path
-    (8, torch.bfloat16, (1 << 22) + 5, "r", "3r+1", "sum", False),
+    (8, torch.bfloat16, (1 << 24) + 5, "r", "3r+1", "sum", False),
     # outputs 4 bytes off, inputs aligned; ragged
     (16, torch.float32, (16 << 20) + 3, "0", "1", "sum", False),
     # outputs 16 bytes past a line, inputs 2 bytes off
-    (4, torch.bfloat16, 1 << 22, "1", "8", "max", False),
-    (3, torch.bfloat16, (1 << 22) + 1, "2r+1", "r", "min", False),
-    (5, torch.int32, (1 << 21) + 1, "r", "2", "max", False),
-    (6, torch.float32, 1 << 21, "r", "r", "avg", True),    # in place, every rank at its own offset
-    # below the line-grid threshold (8 MiB per rank): the element kernel
+    (4, torch.bfloat16, 1 << 25, "1", "8", "max", False),
+    (3, torch.bfloat16, (1 << 26) + 1, "2r+1", "r", "min", False),
+    (5, torch.int32, (1 << 24) + 1, "r", "2", "max", False),
+    (6, torch.float32, 1 << 24, "r", "r", "avg", True),    # in place, every rank at its own offset
+    # below the line-grid threshold (P * S = 256 MiB): the element kernel
+    (8, torch.bfloat16, (1 << 23) + 3, "r", "0", "sum", False),
     (4, torch.bfloat16, 300001, "r", "0", "sum", False),
     (4, torch.float32, 1000, "r", "0", "sum", False),
 ])
