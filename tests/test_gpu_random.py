@@ -194,3 +194,42 @@ def test_random_shared_offsets(dt, orc, case):
         compare(to_np(rs[q]), want_rs[q], f"RS rank {q}")
     _outside_unchanged(ar, arbig, ar_before)
     _outside_unchanged(rs, rsbig, rs_before)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_large_offsets(dt, orc, case):
+    """AllReduce and ReduceScatter past the line-grid two-shot threshold
+    (P * S of 256-512 MiB) over buffers at offsets of their own: even cases
+    put every input at one offset (the input-grid ReduceScatter where the
+    outputs' vectors then start on lines), odd cases draw every offset."""
+    rng = np.random.default_rng(9000 + case)
+    dtype = ["f32", "bf16", "i32"][case % 3]
+    op = ["sum", "max", "min", "avg"][int(rng.integers(0, 4))]
+    p = int(rng.integers(2, 17))
+    es = 2 if dtype == "bf16" else 4
+    per_rank = int(rng.integers(256, 512)) * (1 << 20) // p
+    n = per_rank // es // p * p + int(rng.integers(0, 1000)) * p
+    shared = int(rng.integers(0, 64))
+    send_offs = [shared if case % 2 == 0 else int(rng.integers(0, 64)) for _ in range(p)]
+    note(f"random large offsets case={case} {dtype} {op} P={p} n={n} send offsets {send_offs[:4]}")
+    xs = []
+    for off in send_offs:
+        g = Guarded(n, DTYPES[dtype], offset_elems=off)
+        g.t.copy_(_data(rng, dtype, n))
+        xs.append(g)
+    host = [to_np(x.t) for x in xs]
+    ar = [Guarded(n, DTYPES[dtype], offset_elems=int(rng.integers(0, 64))).poison() for _ in range(p)]
+    dt.dt_allreduce([x.t for x in xs], [y.t for y in ar], op=op)
+    torch.cuda.synchronize()
+    want = orc.allreduce(host, op)[0]
+    for q in range(p):
+        ar[q].check()
+        compare(to_np(ar[q].t), want, f"AR rank {q}")
+    del ar
+    rs = [Guarded(n // p, DTYPES[dtype], offset_elems=int(rng.integers(0, 64))).poison() for _ in range(p)]
+    dt.dt_reduce_scatter([x.t for x in xs], [y.t for y in rs], op=op)
+    torch.cuda.synchronize()
+    want_rs = orc.reduce_scatter(host, op)
+    for r in range(p):
+        rs[r].check()
+        compare(to_np(rs[r].t), want_rs[r], f"RS rank {r}")
