@@ -448,7 +448,35 @@ __global__ __launch_bounds__(kBlock) void k_copy_pieces(Args a, int esize, int t
         const uint64_t t = v1 * 16 + threadIdx.x;
         if (t < b1) to[t] = from[t];
     } else {
-        for (uint64_t t = b0 + threadIdx.x; t < b1; t += kBlock) to[t] = from[t];
+        // Unaligned: each lane takes 16-byte slices of the tile, every slice
+        // one shifted vector loaded through a window over the piece (all of
+        // them before any store), stored in the widest words the
+        // destination's alignment allows.  (A byte loop here waited for
+        // each byte's load in turn.)
+        constexpr int U = int(kPieceTileVecs / kBlock);
+        const uint32_t sm = uint32_t(reinterpret_cast<uintptr_t>(from) & 15u);
+        const LoadWindow w = load_window(from, int64_t(bytes), int64_t(b0) - sm, int64_t(tile_bytes) + 16);
+        u32x4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint64_t v = b0 + (threadIdx.x + uint64_t(u) * kBlock) * 16;
+            if (v < b1) x[u] = window_load_shifted<kPolNT>(w, int64_t(v) - sm, sm);
+        }
+        const uint32_t ta = uint32_t(reinterpret_cast<uintptr_t>(to) & 3u);  // the same at every slice
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint64_t v = b0 + (threadIdx.x + uint64_t(u) * kBlock) * 16;
+            if (v >= b1) continue;
+            const int m = int(b1 - v < 16 ? b1 - v : 16);
+            if (ta == 0 && (m & 3) == 0) {
+                for (int j = 0; j < m; j += 4) *reinterpret_cast<uint32_t*>(to + v + j) = x[u][j >> 2];
+            } else if ((ta & 1) == 0 && (m & 1) == 0) {
+                for (int j = 0; j < m; j += 2)
+                    *reinterpret_cast<uint16_t*>(to + v + j) = uint16_t(x[u][j >> 2] >> ((j & 2) * 8));
+            } else {
+                for (int j = 0; j < m; j++) to[v + j] = vec_byte(x[u], j);
+            }
+        }
     }
 }
 
