@@ -1011,11 +1011,12 @@ dt_status dt_all_to_all_dims(const void* const* send, void* const* recv, int nra
         return copy_segments(src, dst, bytes, stream, "all_to_all_dims copy launch");
     }
     dt::DimsArgs a = {};
-    bool vec = true;
+    bool vec = true, el = true;
     for (int r = 0; r < nranks; r++) {
         a.src[r] = send[r];
         a.dst[r] = recv[r];
         vec = vec && aligned16(send[r]) && aligned16(recv[r]);
+        el = el && elem_aligned(send[r], es) && elem_aligned(recv[r], es);
     }
     a.rows = rows;
     a.cols = cols;
@@ -1027,6 +1028,7 @@ dt_status dt_all_to_all_dims(const void* const* send, void* const* recv, int nra
     a.nruns = uint64_t(rows) * P;
     const uint64_t run_bytes = a.cp * es;
     a.vec = (vec && run_bytes % 16 == 0) ? 1u : 0u;
+    a.elems = (!a.vec && el) ? 1u : 0u;
     uint64_t blocks;
     if (a.vec && run_bytes >= dt::kDimsWaveTileBytes) {
         a.wave = 1;

@@ -396,6 +396,36 @@ __global__ __launch_bounds__(kBlock) void k_all_to_all_dims(DimsArgs a) {
             for (int u = 0; u < U; u++)
                 if (to[u]) store16(to[u], x[u]);
         }
+    } else if (a.elems) {
+        // runs off 16-byte alignment at element-aligned bases: whole
+        // elements (runs are element multiples), U per thread with every
+        // load issued before the stores (a byte loop here waited for each
+        // byte's load in turn)
+        constexpr int U = 8;
+        const uint64_t es = a.esize;
+        const uint64_t ne = span / es;  // elements per run slice
+        const uint64_t total = nk * ne;
+        for (uint64_t t0 = threadIdx.x; t0 < total; t0 += uint64_t(kBlock) * U) {
+            uint32_t w[U];
+            char* to[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const uint64_t t = t0 + uint64_t(u) * kBlock;
+                to[u] = nullptr;
+                if (t < total) {
+                    const uint64_t rk = t / ne, c = (t - rk * ne) * es;
+                    w[u] = es == 2 ? uint32_t(*reinterpret_cast<const uint16_t*>(run_src[rk] + c))
+                                   : *reinterpret_cast<const uint32_t*>(run_src[rk] + c);
+                    to[u] = run_dst[rk] + c;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                if (!to[u]) continue;
+                if (es == 2) *reinterpret_cast<uint16_t*>(to[u]) = uint16_t(w[u]);
+                else *reinterpret_cast<uint32_t*>(to[u]) = w[u];
+            }
+        }
     } else {
         const uint64_t total = nk * span;
         for (uint64_t t = threadIdx.x; t < total; t += kBlock) {

@@ -156,6 +156,7 @@ struct DimsArgs {
     uint32_t runs_per_block;       // >= 1
     uint32_t tiles_per_run;        // >= 1 (only one of the two exceeds 1)
     uint32_t vec;                  // 1: runs and bases allow 16-byte vectors
+    uint32_t elems;                // 1 (vec 0): every base element-aligned, so runs copy whole elements
     uint32_t wave;                 // 1: one kDimsWaveTileBytes slice of one run per single-wave workgroup
     uint64_t nruns;
     int nranks;

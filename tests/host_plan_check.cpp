@@ -480,6 +480,11 @@ hipError_t launch_all_to_all_dims(const DimsArgs& a, uint32_t blocks, hipStream_
         CHECK(a.tiles_per_run == (run_bytes >= kDimsTileBytes ? ceil_div(run_bytes, kDimsTileBytes) : 1),
               "dims: tiles per run");
     }
+    CHECK(!(a.vec && a.elems), "dims: both the vector and the element path");
+    if (a.elems)  // whole-element copies need every base element-aligned
+        for (int r = 0; r < a.nranks; r++)
+            CHECK(reinterpret_cast<uintptr_t>(a.src[r]) % es == 0 && reinterpret_cast<uintptr_t>(a.dst[r]) % es == 0,
+                  "dims: element path with rank %d's buffers off element alignment", r);
     if (a.wave || a.tiles_per_run > 1)
         CHECK(blocks == a.nruns * a.tiles_per_run, "dims: grid %u", blocks);
     else

@@ -159,3 +159,27 @@ def test_all_to_all_dims_round_trip_full_size(dt, orc):
     for r in range(p):
         compare(to_np(mid[r]), want[r], f"rank {r}")
         assert torch.equal(back[r].view(torch.int16), xs[r].view(torch.int16)), r
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("p,rows,cols,off", [(8, 64, 8 * 1001, 1), (4, 256, 4 * 4097, 3), (16, 32, 16 * 33, 1)])
+def test_all_to_all_dims_off_alignment(dt, orc, dtype, p, rows, cols, off):
+    """Buffers an element or a few past 16-byte alignment and runs of odd
+    lengths: the element path (whole elements, all loads before the stores)."""
+    for src, dst in ((0, 1), (1, 0)):
+        note(f"all_to_all_dims off alignment {dtype} P={p} [{rows},{cols}] {src}->{dst} off={off}")
+        n_src = (rows // p) * cols if src == 0 else rows * (cols // p)
+        n_dst = (rows // p) * cols if dst == 0 else rows * (cols // p)
+        base = ranks(dtype, p, n_src, seed=rows + cols + 7 * src)
+        xs = []
+        for x in base:
+            g = Guarded(n_src, DTYPES[dtype], offset_elems=off)
+            g.t.copy_(x)
+            xs.append(g)
+        outs = [Guarded(n_dst, DTYPES[dtype], offset_elems=off + 1).poison() for _ in range(p)]
+        dt.dt_all_to_all_dims([g.t for g in xs], [o.t for o in outs], rows, cols, src, dst)
+        torch.cuda.synchronize()
+        want = orc.all_to_all_dims([to_np(x) for x in base], rows, cols, src, dst)
+        for r, o in enumerate(outs):
+            o.check()
+            np.testing.assert_array_equal(to_np(o.t).view(np.uint8), want[r].view(np.uint8))
