@@ -370,9 +370,23 @@ __global__ __launch_bounds__(kBlock) void k_reduce_pieces(Args a) {
             for (int q = 0; q < nr; q++) store_elem<DT>(ptr[q], t, bits);
         }
     } else {
-        for (uint64_t e = e0 + threadIdx.x; e < e1; e += kBlock) {
-            const uint32_t bits = fold_elem_bits<DT, OP, P>(ptr, e);
-            for (int q = 0; q < nr; q++) store_elem<DT>(ptr[q], e, bits);
+        // EU elements per thread and pass, their loads all issued before the
+        // folds: an element past the piece's end is clamped to its last one
+        // and not stored (one element per pass waited for every pass's loads)
+        constexpr int EU = 4;
+        for (uint64_t e = e0 + threadIdx.x; e < e1; e += uint64_t(kBlock) * EU) {
+            uint32_t bits[EU];
+#pragma unroll
+            for (int u = 0; u < EU; u++) {
+                const uint64_t eu = e + uint64_t(u) * kBlock;
+                bits[u] = fold_elem_bits<DT, OP, P>(ptr, eu < e1 ? eu : e1 - 1);
+            }
+#pragma unroll
+            for (int u = 0; u < EU; u++) {
+                const uint64_t eu = e + uint64_t(u) * kBlock;
+                if (eu < e1)
+                    for (int q = 0; q < nr; q++) store_elem<DT>(ptr[q], eu, bits[u]);
+            }
         }
     }
 }
@@ -422,8 +436,22 @@ __global__ __launch_bounds__(kSegBlock) void k_reduce_scatter_segs(SegReduceScat
         const uint64_t per_tile = uint64_t(kSegBlock) * U * V;
         const uint64_t e0 = uint64_t(tt) * per_tile;
         const uint64_t e1 = min(m, e0 + per_tile);
-        for (uint64_t e = e0 + threadIdx.x; e < e1; e += kSegBlock)
-            fold_elem<DT, OP, P>(src, uint64_t(j) * m + e, dst, e);
+        // EU elements per thread and pass, loads before folds (as for the
+        // unaligned bucket pieces)
+        constexpr int EU = 4;
+        for (uint64_t e = e0 + threadIdx.x; e < e1; e += uint64_t(kSegBlock) * EU) {
+            uint32_t bits[EU];
+#pragma unroll
+            for (int u = 0; u < EU; u++) {
+                const uint64_t eu = e + uint64_t(u) * kSegBlock;
+                bits[u] = fold_elem_bits<DT, OP, P>(src, uint64_t(j) * m + (eu < e1 ? eu : e1 - 1));
+            }
+#pragma unroll
+            for (int u = 0; u < EU; u++) {
+                const uint64_t eu = e + uint64_t(u) * kSegBlock;
+                if (eu < e1) store_elem<DT>(dst, eu, bits[u]);
+            }
+        }
     }
 }
 
