@@ -127,7 +127,8 @@ __global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
     } else {
         // Destinations at offsets of their own: each lane takes 16 bytes of
         // the tile, loaded as one shifted vector (the window, as above), and
-        // stores them to every destination byte by byte.
+        // stores them to every destination in the widest words that
+        // destination's alignment allows (4 or 2 bytes, else single bytes).
         const uint32_t sm = uint32_t(reinterpret_cast<uintptr_t>(src) & 15u);
         const int64_t bytes = int64_t(a.bytes[r]);
         const LoadWindow w = load_window(src, bytes, int64_t(b0) - sm, int64_t(kTile) + 16);
@@ -136,12 +137,24 @@ __global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
             const int64_t p0 = int64_t(b0) + int64_t(threadIdx.x + u * BLOCK) * 16;
             if (p0 >= bytes) continue;
             const u32x4 x = window_load_shifted<0>(w, p0 - int64_t(sm), sm);
+            const int m = int(bytes - p0 < 16 ? bytes - p0 : 16);
+            for (int q = 0; q < nr; q++) {
+                if (dsts[q] == src) continue;
+                char* d = static_cast<char*>(dsts[q]) + p0;
+                const uint32_t da = uint32_t(reinterpret_cast<uintptr_t>(d) & 3u);  // the same in every lane
+                int j = 0;  // bytes stored in words
+                if (da == 0) {
 #pragma unroll
-            for (int j = 0; j < 16; j++) {
-                if (p0 + j >= bytes) continue;
-                const char c = vec_byte(x, j);
-                for (int q = 0; q < nr; q++)
-                    if (dsts[q] != src) static_cast<char*>(dsts[q])[p0 + j] = c;
+                    for (int k = 0; k < 4; k++)
+                        if (4 * k + 4 <= m) *reinterpret_cast<uint32_t*>(d + 4 * k) = x[k];
+                    j = m & ~3;
+                } else if (da == 2) {
+#pragma unroll
+                    for (int k = 0; k < 8; k++)
+                        if (2 * k + 2 <= m) *reinterpret_cast<uint16_t*>(d + 2 * k) = uint16_t(x[k >> 1] >> ((k & 1) * 16));
+                    j = m & ~1;
+                }
+                for (; j < m; j++) d[j] = vec_byte(x, j);
             }
         }
     }
