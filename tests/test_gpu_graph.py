@@ -146,3 +146,64 @@ def test_graph_replays_large_argument_tables(dt):
         want_a = orc.all_to_all(host_a, split)
         for j in range(p16):
             compare(to_np(a_out[j]), want_a[j], f"replay {replay} all_to_all rank {j}")
+
+
+def test_graph_replays_offsets_of_their_own(dt):
+    """Buffers at offsets of their own captured in a graph: the line-grid
+    AllReduce (P=8 bf16, 32 MiB + 6 bytes per rank, inputs 2 bytes off,
+    outputs at 2(3q+1) bytes: the output-grid ReduceScatter and the fan-out
+    to destinations at offsets of their own), the input-grid ReduceScatter
+    (inputs 8 bytes off, outputs aligned) and the odd-count AllGather (the
+    line-grid fan-out with its windowed piece ends); every replay checked
+    against the oracle on that replay's inputs."""
+    orc = oracle.get()
+    p, n = 8, (16 << 20) + 3
+    m = n // p
+    xb = [torch.empty(n + 64, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    yb = [torch.empty(n + 64, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    rb = [torch.empty(m + 64, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    xs = [b[1:1 + n] for b in xb]
+    ys = [b[3 * q + 1:3 * q + 1 + n] for q, b in enumerate(yb)]
+    xs8 = [b[4:4 + p * m] for b in xb]
+    rs = [b[:m] for b in rb]
+    counts = [1001 + 2 * k for k in range(p)]
+    ag_in = [torch.empty(c, dtype=torch.bfloat16, device="cuda") for c in counts]
+    ag_out = [torch.empty(sum(counts), dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+
+    def work():
+        dt.dt_allreduce(xs, ys)
+        dt.dt_reduce_scatter(xs8, rs)
+        dt.dt_all_gather(ag_in, ag_out)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    note("graph capture of line-grid allreduce, input-grid reduce_scatter, odd-count all_gather")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for replay in range(3):
+        note(f"offsets graph replay {replay}")
+        vals = synth.normal_ranks(p, (n + 64,), seed=90 + replay, device="cuda", dtype=torch.bfloat16)
+        for b, v in zip(xb, vals):
+            b.copy_(v)  # eager work between replays
+        small = synth.normal_ranks(p, (max(counts),), seed=95 + replay, device="cuda", dtype=torch.bfloat16)
+        for t, v in zip(ag_in, small):
+            t.copy_(v[:t.numel()])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = orc.allreduce([to_np(x) for x in xs], "sum")[0]
+        view = lambda t: t.view(torch.int16)
+        compare(to_np(ys[0]), want, f"replay {replay} AR rank 0")
+        for q in range(1, p):
+            assert torch.equal(view(ys[q]), view(ys[0])), f"replay {replay} AR rank {q}"
+        want_rs = orc.reduce_scatter([to_np(x) for x in xs8], "sum")
+        for r in range(p):
+            compare(to_np(rs[r]), want_rs[r], f"replay {replay} RS rank {r}")
+        cat = np.concatenate([to_np(t) for t in ag_in])
+        for q in range(p):
+            assert np.array_equal(to_np(ag_out[q]), cat), f"replay {replay} AG rank {q}"
