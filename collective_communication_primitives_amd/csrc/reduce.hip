@@ -1,4 +1,6 @@
 // reduce.hip -- the rank-fold kernels: AllReduce (one-shot), ReduceScatter
+// (on 16-byte aligned buffers, or over 128-byte line grids with every input
+// shifted into place when the buffers share no offset), the element path
 // and the multi-tensor bucket reduce.
 //
 // Work layout.  Rank buffers are P separate contiguous allocations in HBM.
@@ -9,9 +11,9 @@
 // ReduceScatter).  Every HBM byte is
 // touched once: AllReduce moves 2*P*S bytes, ReduceScatter (P+1)*S.
 //
-// The rank count P (1..16) is a template parameter of every fold kernel, so
-// each fold is fully unrolled with no per-rank predicate and the P loads of
-// a vector go out back to back.  (With a runtime count below a template
+// The rank count P (1..16) is a template parameter of every fold kernel
+// (the element kernel's too), so each fold is fully unrolled with no
+// per-rank predicate and the P loads of a vector go out back to back.  (With a runtime count below a template
 // bound, the compiler turned the per-rank guards into branches and waited
 // for each load in turn: the ReduceScatter of P = 5-7 took 2x as long.)
 #include <type_traits>
