@@ -209,8 +209,10 @@ uint64_t allreduce_window(int nranks, uint64_t bytes_per_rank) {
 // off; but outputs 2-18 bytes off with aligned inputs 260-293 us on the
 // input grid (its vector stores then start inside a line) against 222-225.
 dt_status reduce_scatter_grid(const void* const* send, void* const* out, int nranks, size_t in_stride, size_t count,
-                              size_t last_count, dt_dtype dtype, dt_op op, hipStream_t stream, const char* what) {
+                              size_t last_count, dt_dtype dtype, dt_op op, bool fan_out_follows, hipStream_t stream,
+                              const char* what) {
     dt::GridFoldArgs g = {};
+    g.nt = fan_out_follows ? 1 : 0;
     const uintptr_t s0 = reinterpret_cast<uintptr_t>(send[0]) & (dt::kGridAlign - 1);
     const uint64_t stride_bytes = uint64_t(in_stride) * esize_of(dtype);
     g.src_grid = 1;
@@ -312,7 +314,7 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
                 counts[r] = r + 1 < nranks ? mce : last;
                 for (int q = 0; q < nranks; q++) table[size_t(r) * nranks + q] = static_cast<char*>(recv[q]) + r * mce * es;
             }
-            dt_status st = reduce_scatter_grid(send, own, nranks, mce, mce, last, dtype, op, stream,
+            dt_status st = reduce_scatter_grid(send, own, nranks, mce, mce, last, dtype, op, true, stream,
                                                "allreduce (grid reduce_scatter) launch");
             if (st != DT_OK) return st;
             return fan_out(own, counts, table, nranks, es, stream, "allreduce (all_gather) launch");
@@ -831,7 +833,7 @@ dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nran
     bool el = true;  // element-aligned buffers at offsets of their own: the line-grid kernel
     for (int r = 0; r < nranks; r++) el = el && elem_aligned(send[r], es) && elem_aligned(recv[r], es);
     if (el)
-        return reduce_scatter_grid(send, recv, nranks, recvcount, recvcount, recvcount, dtype, op, stream,
+        return reduce_scatter_grid(send, recv, nranks, recvcount, recvcount, recvcount, dtype, op, false, stream,
                                    "reduce_scatter (grid) launch");
     a.first = 0;
     a.count = recvcount;

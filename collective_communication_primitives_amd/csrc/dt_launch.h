@@ -44,6 +44,7 @@ struct GridFoldArgs {
     int nranks;
     int nchunks;
     int src_grid;
+    int nt;  // output grid: non-temporal input loads (a fan-out of the chunks follows)
 };
 constexpr uint64_t kGridFoldTileBytes = 1024;  // the input-grid tile: one wave, one vector per lane
 

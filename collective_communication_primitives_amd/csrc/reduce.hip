@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_elems(ReduceArgs a) {
 // the outputs 2-18 bytes off, 214-216 us against 222-229 us with one wave
 // and 229-232 us with four.
 constexpr int kGridOutBlock = 128;
-template <int DT, int OP, int P>
+template <int DT, int OP, int P, bool NT>
 __global__ __launch_bounds__(kGridOutBlock) void k_reduce_scatter_grid(GridFoldArgs a) {
     constexpr int64_t ES = DT == kBF16 ? 2 : 4;
     constexpr int64_t kTile = int64_t(kGridOutBlock) * 16;
@@ -184,16 +184,20 @@ __global__ __launch_bounds__(kGridOutBlock) void k_reduce_scatter_grid(GridFoldA
         // the next one, which may lie past the buffer.  Plain loads, so that
         // the second vector (the next lane's first) is served by the caches:
         // in-process A/B against non-temporal loads, P=8 bf16 with the
-        // outputs 2 bytes off 232 -> 215 us at 128 MiB per rank (and the
-        // two-shot AllReduce 10% faster at 16 MiB, 2.5% slower at 128 MiB,
-        // where the inputs then crowd its chunks out of the Infinity Cache).
-        // Taking the second vector from the next lane by a shuffle instead
-        // ran 20% slower.
+        // outputs 2 bytes off 233 -> 218 us at 128 MiB per rank.  But when a
+        // fan-out of the chunks follows (NT, the two-shot AllReduce), plain
+        // loads stream the inputs through the Infinity Cache and crowd out
+        // the chunks the fan-out then reads: there non-temporal loads win
+        // (the AllReduce 403 -> 391 us).  The choice is a template argument:
+        // a branch between the two forms of one load is merged by the
+        // compiler, which drops the non-temporal hint, and buffer-resource
+        // loads in the non-temporal branch gave no gain.  Taking the second
+        // vector from the next lane by a shuffle instead ran 20% slower.
 #pragma unroll
         for (int r = 0; r < P; r++) {
             const char* at = static_cast<const char*>(a.src[r]) + in_off + p0 - sm[r];
-            lo[r] = load16_h<false>(at);
-            hi[r] = load16_h<false>(at + (sm[r] != 0 ? 16 : 0));
+            lo[r] = load16_h<NT>(at);
+            hi[r] = load16_h<NT>(at + (sm[r] != 0 ? 16 : 0));
         }
         // the shift's word choice branches once per input (uniform); a
         // branch-free choice by selects ran 10% slower
@@ -630,8 +634,10 @@ hipError_t reduce_scatter_grid_p(const GridFoldArgs& a, hipStream_t s) {
     if (tiles > 0x7FFFFFFFull) return hipErrorInvalidValue;
     if (a.src_grid)
         k_reduce_scatter_srcgrid<DT, OP, P><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kWaveBlock, 0, s>>>(a);
+    else if (a.nt)
+        k_reduce_scatter_grid<DT, OP, P, true><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kGridOutBlock, 0, s>>>(a);
     else
-        k_reduce_scatter_grid<DT, OP, P><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kGridOutBlock, 0, s>>>(a);
+        k_reduce_scatter_grid<DT, OP, P, false><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kGridOutBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 
