@@ -901,7 +901,7 @@ def probe_rows(dt, torch, reps: int = 3):
     # the ReduceScatter with aligned inputs and outputs 2 bytes off: the line-grid kernel
     ro = [torch.empty(n // P + 8, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
     run("reduce_scatter_outputs_off_p8_bf16", lambda: dt.dt_reduce_scatter(xs, [r[1:n // P + 1] for r in ro]),
-        (P + 1) * s_bytes, ["k_reduce_scatter_grid<1, 0, 8, false>"])
+        (P + 1) * s_bytes, ["k_reduce_scatter_grid<1, 0, 8>"])
     del xs, xo, yo, ro
     torch.cuda.empty_cache()
     # the uneven AllGather in bf16 with odd counts (pieces 2 or 8 bytes off: the line-grid fan-out)

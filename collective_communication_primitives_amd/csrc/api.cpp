@@ -199,33 +199,16 @@ uint64_t allreduce_window(int nranks, uint64_t bytes_per_rank) {
 // ReduceScatter over line grids (dt::GridFoldArgs): chunk c is elements
 // [c * in_stride, c * in_stride + n_c) of every input, n_c = count but
 // last_count for the last chunk, folded into out[c].  For element-aligned
-// buffers that share no offset.  The tiles follow the inputs' lines (one
-// aligned load per input and lane) when every input sits at one offset
-// within a line and, in every chunk, the output vectors then start on the
-// output's lines (the output at most 16 bytes before a line where a tile
-// starts); otherwise each output's lines.  P=8 bf16, 128 MiB per rank,
-// in-process A/B: inputs 6, 8 or 14 bytes off with aligned outputs 193-198 us
-// on the input grid against 220-224 us on the output grid, even at 2 bytes
-// off; but outputs 2-18 bytes off with aligned inputs 260-293 us on the
-// input grid (its vector stores then start inside a line) against 222-225.
+// buffers that share no offset.  The tiles follow each output's lines; the
+// kernel loads every input's lines whole and shifts them in LDS, so both
+// sides move whole lines whatever the offsets.
 dt_status reduce_scatter_grid(const void* const* send, void* const* out, int nranks, size_t in_stride, size_t count,
-                              size_t last_count, dt_dtype dtype, dt_op op, bool fan_out_follows, hipStream_t stream,
-                              const char* what) {
+                              size_t last_count, dt_dtype dtype, dt_op op, hipStream_t stream, const char* what) {
     dt::GridFoldArgs g = {};
-    g.nt = fan_out_follows ? 1 : 0;
-    const uintptr_t s0 = reinterpret_cast<uintptr_t>(send[0]) & (dt::kGridAlign - 1);
-    const uint64_t stride_bytes = uint64_t(in_stride) * esize_of(dtype);
-    g.src_grid = 1;
-    for (int r = 0; r < nranks; r++) {
-        if ((reinterpret_cast<uintptr_t>(send[r]) & (dt::kGridAlign - 1)) != s0) g.src_grid = 0;
-        const uint64_t h = (reinterpret_cast<uintptr_t>(out[r]) - (s0 + r * stride_bytes)) & (dt::kGridAlign - 1);
-        if (h != 0 && h < dt::kGridAlign - 16) g.src_grid = 0;
-    }
     for (int r = 0; r < nranks; r++) {
         g.src[r] = send[r];
         g.dst[r] = out[r];
-        g.lead[r] = g.src_grid ? uint32_t((s0 + r * stride_bytes) & (dt::kGridAlign - 1))
-                               : uint32_t(reinterpret_cast<uintptr_t>(out[r]) & (dt::kGridAlign - 1));
+        g.lead[r] = uint32_t(reinterpret_cast<uintptr_t>(out[r]) & (dt::kGridAlign - 1));
     }
     g.in_stride = in_stride;
     g.count = count;
@@ -250,16 +233,23 @@ bool grid_two_shot_pays(int nranks, uint64_t bytes_per_rank) {
 dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, size_t count, dt_dtype dtype,
                         dt_op op, hipStream_t stream) {
     dt::ReduceArgs a = {};
-    bool vec = true;
+    bool vec = true, lines = true;
     for (int r = 0; r < nranks; r++) {
         a.src[r] = send[r];
         a.dst[r] = recv[r];
         vec = vec && aligned16(send[r]) && aligned16(recv[r]);
+        lines = lines && line_aligned(send[r]);
     }
     a.nranks = nranks;
     a.rs = 0;
     const size_t v = vec_elems(dtype);
     const size_t es = esize_of(dtype);
+    // Vector-aligned inputs off their lines: where the two-shot form runs
+    // past the Infinity Cache, its ReduceScatter goes over the line grid,
+    // which loads whole input lines (P=8 bf16 128 MiB per rank, inputs 16
+    // bytes off: 364 -> 343 us, in-process A/B).
+    const bool grid_first = vec && !lines && nranks > 1 && two_shot_pays(nranks, uint64_t(count) * es) &&
+                            grid_two_shot_pays(nranks, uint64_t(count) * es);
     // Two-shot chunks are whole multiples of kChunkVecs vectors (1 KiB, the
     // ReduceScatter tile), all but the last, which takes the rest: every
     // chunk then starts on a cache-line boundary at any rank count, so no
@@ -271,7 +261,7 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
     const uint64_t nv = count / v;
     const uint64_t per = (nv + nranks - 1) / nranks;                      // vectors per chunk, rounded up
     const uint64_t mc = (per + kChunkVecs - 1) / kChunkVecs * kChunkVecs;  // ... to whole tiles
-    if (vec && mc * uint64_t(nranks - 1) < nv && two_shot_pays(nranks, uint64_t(count) * es)) {
+    if (vec && !grid_first && mc * uint64_t(nranks - 1) < nv && two_shot_pays(nranks, uint64_t(count) * es)) {
         const uint64_t last = nv - mc * uint64_t(nranks - 1);  // 0 < last <= mc
         const uint64_t cb = mc * 16;                           // chunk stride in bytes
         dt::ReduceArgs rs = a;
@@ -298,11 +288,11 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
         a.count = count - a.first;
         return check_hip(dt::launch_reduce_elems(a, dtype, op, stream), "allreduce (element path) launch");
     }
-    if (!vec && nranks > 1 && grid_two_shot_pays(nranks, uint64_t(count) * es)) {
+    if ((!vec || grid_first) && nranks > 1 && grid_two_shot_pays(nranks, uint64_t(count) * es)) {
         bool el = true;
         for (int r = 0; r < nranks; r++) el = el && elem_aligned(send[r], es) && elem_aligned(recv[r], es);
         // chunks of whole 1 KiB of elements, all but the last, as above
-        const size_t te = size_t(dt::kGridFoldTileBytes) / es;
+        const size_t te = size_t(dt::kGridChunkGrain) / es;
         const size_t mce = ((count + nranks - 1) / nranks + te - 1) / te * te;
         if (el && mce * size_t(nranks - 1) < count) {
             const size_t last = count - mce * size_t(nranks - 1);
@@ -314,7 +304,7 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
                 counts[r] = r + 1 < nranks ? mce : last;
                 for (int q = 0; q < nranks; q++) table[size_t(r) * nranks + q] = static_cast<char*>(recv[q]) + r * mce * es;
             }
-            dt_status st = reduce_scatter_grid(send, own, nranks, mce, mce, last, dtype, op, true, stream,
+            dt_status st = reduce_scatter_grid(send, own, nranks, mce, mce, last, dtype, op, stream,
                                                "allreduce (grid reduce_scatter) launch");
             if (st != DT_OK) return st;
             return fan_out(own, counts, table, nranks, es, stream, "allreduce (all_gather) launch");
@@ -793,11 +783,16 @@ dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nran
         if ((st = check_disjoint(w, rd, "reduce_scatter")) != DT_OK) return st;
     }
     dt::ReduceArgs a = {};
-    bool vec = recvcount % vec_elems(dtype) == 0;
+    // The vector kernel where every chunk of every input starts on a line;
+    // inputs off their lines take the line grid, which loads whole input
+    // lines (P=8 bf16 128 MiB per rank, inputs 16 bytes off: 208 -> 191 us,
+    // in-process A/B).  Outputs off their lines cost the vector kernel
+    // nothing measurable.
+    bool vec = recvcount % vec_elems(dtype) == 0 && (recvcount * esize_of(dtype)) % dt::kGridAlign == 0;
     for (int r = 0; r < nranks; r++) {
         a.src[r] = send[r];
         a.dst[r] = recv[r];
-        vec = vec && aligned16(send[r]) && aligned16(recv[r]);
+        vec = vec && aligned16(send[r]) && aligned16(recv[r]) && line_aligned(send[r]);
     }
     a.nranks = nranks;
     a.rs = 1;
@@ -833,7 +828,7 @@ dt_status dt_reduce_scatter(const void* const* send, void* const* recv, int nran
     bool el = true;  // element-aligned buffers at offsets of their own: the line-grid kernel
     for (int r = 0; r < nranks; r++) el = el && elem_aligned(send[r], es) && elem_aligned(recv[r], es);
     if (el)
-        return reduce_scatter_grid(send, recv, nranks, recvcount, recvcount, recvcount, dtype, op, false, stream,
+        return reduce_scatter_grid(send, recv, nranks, recvcount, recvcount, recvcount, dtype, op, stream,
                                    "reduce_scatter (grid) launch");
     a.first = 0;
     a.count = recvcount;

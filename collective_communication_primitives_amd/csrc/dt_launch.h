@@ -30,10 +30,8 @@ struct ReduceArgs {
 // share no offset (the vector kernels need every buffer 16-byte aligned, or
 // all at one offset).  Chunk c is elements [c * in_stride, c * in_stride +
 // n_c) of every input, n_c = count for every chunk but the last
-// (last_count); it goes to dst[c].  With src_grid, every input sits at one
-// offset within a line and the tiles follow the inputs' lines: lead[c] is
-// that offset at chunk c's start.  Otherwise the tiles follow each output's
-// lines: lead[c] = dst[c] & (kGridAlign - 1).
+// (last_count); it goes to dst[c].  The tiles follow each output's lines:
+// lead[c] = dst[c] & (kGridAlign - 1).
 struct GridFoldArgs {
     const void* src[kMaxRanksHost];
     void* dst[kMaxRanksHost];
@@ -43,10 +41,10 @@ struct GridFoldArgs {
     uint64_t last_count;
     int nranks;
     int nchunks;
-    int src_grid;
-    int nt;  // output grid: non-temporal input loads (a fan-out of the chunks follows)
 };
-constexpr uint64_t kGridFoldTileBytes = 1024;  // the input-grid tile: one wave, one vector per lane
+// The AllReduce's grid two-shot form cuts its chunks in whole KiB, so every
+// chunk of a buffer sits at that buffer's offset within a line.
+constexpr uint64_t kGridChunkGrain = 1024;
 
 // Multi-tensor pieces of one bucket.  Piece k of rank r starts at
 // ptr[k*nranks + r]; ws[r] + wpos[k] is its place in rank r's bucket buffer.

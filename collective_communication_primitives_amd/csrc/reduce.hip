@@ -144,77 +144,107 @@ __global__ __launch_bounds__(kBlock) void k_reduce_elems(ReduceArgs a) {
 // ReduceScatter over each output chunk's line grid (GridFoldArgs), for
 // buffers that share no offset.  Tile t of chunk c covers bytes
 // [t * 2 KiB, (t + 1) * 2 KiB) of the grid that starts at the line holding
-// the chunk's first output byte, lead bytes before it; grid.y = chunk.  (An
-// XCD-contiguous tile order, for the line that neighbouring tiles' loads
-// share, ran 10% slower.)  Every lane builds its 16-byte grid vector of
-// every input from two aligned loads joined by a byte shift (each input's
-// shift is the same for all lanes, computed from the kernel arguments, so
-// the choice of shift is uniform) and folds; a vector inside the chunk is
-// one aligned store, and a partial one at either end (loaded through
-// windows) stores its elements inside the chunk one by one.  P=8 bf16
-// at 128 MiB per rank, outputs 2 bytes off and inputs aligned: 215 us (0.70
-// of peak), against 556 us on the element kernel these buffers took before
-// and 181 us for aligned buffers.  Two waves per workgroup (128 threads, a
-// 2 KiB tile), so that every other boundary line that neighbouring tiles'
-// loads share lies between two waves of one workgroup: in-process A/B with
-// the outputs 2-18 bytes off, 214-216 us against 222-229 us with one wave
-// and 229-232 us with four.
+// the chunk's first output byte, lead bytes before it; grid.y = chunk; two
+// waves per workgroup, one output vector per lane, so every store is an
+// aligned vector and each wave writes whole lines.
+//
+// A tile whose bytes all lie inside the chunk (every tile but the first and
+// last of a chunk) is staged: each input's bytes for the tile start d bytes
+// into one of its lines, and the workgroup loads those whole lines, d = 0
+// exactly the tile's 16 lines and else 17, one aligned vector per lane plus
+// eight, non-temporal, every load of every input issued before any use.
+// Each line loaded holds at least one byte of the tile's input, so nothing
+// beyond the pages that hold the buffer is touched.  The lines go to LDS;
+// after one barrier each lane takes its 16 bytes of every input from there
+// (the two aligned LDS vectors around byte d + 16 * lane, joined by a byte
+// shift that is uniform per input), folds and stores.  Against the earlier
+// form, which loaded the two aligned vectors around each lane's bytes from
+// memory directly (every wave's loads then straddle 9 lines for 8 lines of
+// data), in-process A/B at P=8 bf16, 128 MiB per rank: ReduceScatter with
+// the outputs 2 bytes off 216 -> 192 us (0.70 -> 0.78 of peak), with the
+// inputs 2 bytes off 218 -> 192 us, with every input at an offset of its own
+// 217 -> 190 us; the two-shot AllReduce over it 388 -> 344 us.  The
+// input-line grid that the shared-input-offset cases took before (one
+// aligned load per lane, the result shifted across lanes onto the outputs)
+// ran 216-219 us and is gone.
+//
+// The first and last tile of a chunk go lane by lane: a full vector from
+// two plain aligned loads per input joined by the same shift, a partial one
+// (at either end of the chunk) through windows over the input's chunk
+// (load_window: nothing outside the chunk's aligned vectors is read), its
+// elements inside the chunk stored one by one.
 constexpr int kGridOutBlock = 128;
-template <int DT, int OP, int P, bool NT>
+constexpr int64_t kGridTile = int64_t(kGridOutBlock) * 16;
+template <int DT, int OP, int P>
 __global__ __launch_bounds__(kGridOutBlock) void k_reduce_scatter_grid(GridFoldArgs a) {
     constexpr int64_t ES = DT == kBF16 ? 2 : 4;
-    constexpr int64_t kTile = int64_t(kGridOutBlock) * 16;
+    constexpr int kV = int(kGridTile / 16);  // vectors per tile, one per lane
     const uint32_t c = blockIdx.y;
     const int64_t n = int64_t(c + 1 == uint32_t(a.nchunks) ? a.last_count : a.count) * ES;  // chunk bytes
     const int64_t lead = int64_t(a.lead[c]);
-    const int64_t g0 = int64_t(blockIdx.x) * kTile - lead;  // chunk byte at the tile's grid start
-    if (g0 >= n) return;                                    // past the end of this chunk
-    const int64_t p0 = g0 + int64_t(threadIdx.x) * 16;
-    if (p0 + 16 <= 0 || p0 >= n) return;  // a lane before the chunk's first grid vector or past its last
+    const int64_t g0 = int64_t(blockIdx.x) * kGridTile - lead;  // chunk byte at the tile's grid start
+    if (g0 >= n) return;                                        // past the end of this chunk
     const uint64_t in_off = uint64_t(c) * a.in_stride * uint64_t(ES);
+    const int tid = int(threadIdx.x);
+    if (g0 >= 0 && g0 + kGridTile <= n) {  // uniform per workgroup: every lane reaches the barrier
+        __shared__ u32x4 stage[P][kV + 8];
+        uint32_t d[P];
+        u32x4 v[P], w[P];
+#pragma unroll
+        for (int r = 0; r < P; r++) {
+            const char* base = static_cast<const char*>(a.src[r]) + in_off + g0;
+            d[r] = uint32_t(reinterpret_cast<uintptr_t>(base) & uint64_t(kGridAlign - 1));
+            const char* line0 = base - d[r];
+            v[r] = load16(line0 + tid * 16);
+            if (tid < 8 && d[r] != 0) w[r] = load16(line0 + kGridTile + tid * 16);
+        }
+#pragma unroll
+        for (int r = 0; r < P; r++) {
+            stage[r][tid] = v[r];
+            if (tid < 8 && d[r] != 0) stage[r][kV + tid] = w[r];
+        }
+        __syncthreads();
+        u32x4 x[P];
+#pragma unroll
+        for (int r = 0; r < P; r++) {
+            const uint32_t q = d[r] + uint32_t(tid) * 16;  // at most 127 + 16 * 127: vectors 0 .. kV + 7
+            const uint32_t s = q & 15u;
+            const u32x4 l = stage[r][q >> 4];
+            // the shift's word choice branches once per input (uniform); a
+            // branch-free choice by selects ran 10% slower
+            x[r] = s != 0 ? funnel16(l, stage[r][(q >> 4) + 1], s) : l;
+        }
+        const rsrc_t out = make_rsrc(static_cast<char*>(a.dst[c]) + g0, uint32_t(kGridTile));
+        bstore16<kPolDevice>(out, uint32_t(tid) * 16, fold_vec<DT, OP, P>(x, P));
+        return;
+    }
+    const int64_t p0 = g0 + int64_t(tid) * 16;
+    if (p0 + 16 <= 0 || p0 >= n) return;  // a lane before the chunk's first grid vector or past its last
     uint32_t sm[P];
 #pragma unroll
     for (int r = 0; r < P; r++)
         sm[r] = uint32_t((reinterpret_cast<uintptr_t>(a.src[r]) + in_off - uint64_t(lead)) & 15u);
     u32x4 lo[P], hi[P];
     if (p0 >= 0 && p0 + 16 <= n) {
-        // Both aligned vectors of every input are loaded before any is
-        // shifted, so all 2P loads are in flight at once.  An input at the
-        // grid's own offset (shift 0) loads its one vector twice rather than
-        // the next one, which may lie past the buffer.  Plain loads, so that
-        // the second vector (the next lane's first) is served by the caches:
-        // in-process A/B against non-temporal loads, P=8 bf16 with the
-        // outputs 2 bytes off 233 -> 218 us at 128 MiB per rank.  But when a
-        // fan-out of the chunks follows (NT, the two-shot AllReduce), plain
-        // loads stream the inputs through the Infinity Cache and crowd out
-        // the chunks the fan-out then reads: there non-temporal loads win
-        // (the AllReduce 403 -> 391 us).  The choice is a template argument:
-        // a branch between the two forms of one load is merged by the
-        // compiler, which drops the non-temporal hint, and buffer-resource
-        // loads in the non-temporal branch gave no gain.  Taking the second
-        // vector from the next lane by a shuffle instead ran 20% slower.
+        // both aligned vectors of every input before any is shifted; an
+        // input at the grid's own offset (shift 0) loads its one vector
+        // twice rather than the next one, which may lie past the buffer
 #pragma unroll
         for (int r = 0; r < P; r++) {
             const char* at = static_cast<const char*>(a.src[r]) + in_off + p0 - sm[r];
-            lo[r] = load16_h<NT>(at);
-            hi[r] = load16_h<NT>(at + (sm[r] != 0 ? 16 : 0));
+            lo[r] = load16_h<false>(at);
+            hi[r] = load16_h<false>(at + (sm[r] != 0 ? 16 : 0));
         }
-        // the shift's word choice branches once per input (uniform); a
-        // branch-free choice by selects ran 10% slower
         u32x4 x[P];
 #pragma unroll
         for (int r = 0; r < P; r++) x[r] = sm[r] != 0 ? funnel16(lo[r], hi[r], sm[r]) : lo[r];
-        const rsrc_t out = make_rsrc(static_cast<char*>(a.dst[c]) + g0, uint32_t(kTile));
-        bstore16<kPolDevice>(out, threadIdx.x * 16, fold_vec<DT, OP, P>(x, P));
+        const rsrc_t out = make_rsrc(static_cast<char*>(a.dst[c]) + g0, uint32_t(kGridTile));
+        bstore16<kPolDevice>(out, uint32_t(tid) * 16, fold_vec<DT, OP, P>(x, P));
     } else {
-        // a partial vector at one of the chunk's ends: every input's vectors
-        // through a window over its chunk (load_window, nothing outside the
-        // chunk's aligned vectors is read), all loads before the fold, then
-        // the elements inside the chunk stored one by one
 #pragma unroll
         for (int r = 0; r < P; r++) {
             const char* s = static_cast<const char*>(a.src[r]) + in_off;
-            const LoadWindow w = load_window(s, n, g0 - int64_t(sm[r]), kTile + 16);
+            const LoadWindow w = load_window(s, n, g0 - int64_t(sm[r]), kGridTile + 16);
             const int64_t o = p0 - int64_t(sm[r]);
             lo[r] = window_load<0>(w, o);
             hi[r] = window_load<0>(w, o + (sm[r] != 0 ? 16 : 0));
@@ -223,75 +253,6 @@ __global__ __launch_bounds__(kGridOutBlock) void k_reduce_scatter_grid(GridFoldA
 #pragma unroll
         for (int r = 0; r < P; r++) x[r] = sm[r] != 0 ? funnel16(lo[r], hi[r], sm[r]) : lo[r];
         store_vec_elems<int(ES)>(static_cast<char*>(a.dst[c]), p0, fold_vec<DT, OP, P>(x, P), 0, 16, n);
-    }
-}
-
-// The same ReduceScatter when every input sits at one offset within a line
-// (src_grid): tile t of chunk c covers chunk bytes [A, A + 1 KiB), A =
-// t * 1 KiB - lead[c], which start on a line of every input, so each lane
-// loads one aligned vector per input (non-temporal buffer loads, as the
-// aligned kernel; windows at the chunk's ends) and no line is read by two
-// workgroups.  The folded vector y covers chunk bytes [A + 16 i, +16) of lane
-// i; when the output sits e bytes into a vector there, lane i stores the
-// aligned output vector made of y's last e bytes and the next lane's first
-// 16 - e (passed across by a shuffle of the result, once per lane), the
-// wave's last lane its own last e bytes, and lane 0 the tile's first 16 - e:
-// every output byte once, the partial vectors element by element.  The
-// output-grid kernel above loads two vectors per input and reads each
-// tile's boundary line twice (1.11 of the algorithmic bytes).
-template <int DT, int OP, int P>
-__global__ __launch_bounds__(kWaveBlock) void k_reduce_scatter_srcgrid(GridFoldArgs a) {
-    constexpr int ES = DT == kBF16 ? 2 : 4;
-    constexpr int64_t kTile = int64_t(kGridFoldTileBytes);
-    const uint32_t c = blockIdx.y;
-    const int64_t n = int64_t(c + 1 == uint32_t(a.nchunks) ? a.last_count : a.count) * ES;  // chunk bytes
-    const int64_t A = int64_t(blockIdx.x) * kTile - int64_t(a.lead[c]);  // a line of every input
-    if (A >= n) return;                                                   // past the end of this chunk
-    const int64_t q = A + int64_t(threadIdx.x) * 16;
-    const uint64_t in_off = uint64_t(c) * a.in_stride * uint64_t(ES);
-    u32x4 x[P];
-    if (A >= 0 && A + kTile <= n) {
-#pragma unroll
-        for (int r = 0; r < P; r++) {
-            const rsrc_t in = make_rsrc(static_cast<const char*>(a.src[r]) + in_off + A, uint32_t(kTile));
-            x[r] = bload16<kPolNT>(in, threadIdx.x * 16);
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < P; r++) {
-            const LoadWindow w = load_window(static_cast<const char*>(a.src[r]) + in_off, n, A, kTile);
-            x[r] = window_load<kPolNT>(w, q);
-        }
-    }
-    const u32x4 y = fold_vec<DT, OP, P>(x, P);
-    char* d = static_cast<char*>(a.dst[c]);
-    const uint32_t e = uint32_t((reinterpret_cast<uintptr_t>(d) + uint64_t(A)) & 15u);  // uniform
-    if (e == 0) {
-        if (q >= 0 && q + 16 <= n) {
-            const rsrc_t out = make_rsrc(d + A, uint32_t(kTile));
-            bstore16<kPolDevice>(out, threadIdx.x * 16, y);
-        } else {
-            store_vec_elems<ES>(d, q, y, 0, 16, n);
-        }
-        return;
-    }
-    u32x4 y1;  // the next lane's vector (every lane takes part in the shuffle)
-    y1[0] = __shfl_down(y[0], 1u, 64);
-    y1[1] = __shfl_down(y[1], 1u, 64);
-    y1[2] = __shfl_down(y[2], 1u, 64);
-    y1[3] = __shfl_down(y[3], 1u, 64);
-    if (threadIdx.x == 0) store_vec_elems<ES>(d, q, y, 0, 16 - int(e), n);  // the tile's head
-    if (threadIdx.x + 1 == kWaveBlock) {
-        store_vec_elems<ES>(d, q, y, 16 - int(e), 16, n);  // the tile's tail
-        return;
-    }
-    const int64_t o = q + 16 - int64_t(e);  // chunk byte of this lane's aligned output vector
-    const u32x4 v = funnel16(y, y1, 16u - e);
-    if (o >= 0 && o + 16 <= n) {
-        const rsrc_t out = make_rsrc(d + A + 16 - int64_t(e), uint32_t(kTile));
-        bstore16<kPolDevice>(out, threadIdx.x * 16, v);
-    } else {
-        store_vec_elems<ES>(d, o, v, 0, 16, n);
     }
 }
 
@@ -623,7 +584,7 @@ hipError_t reduce_elems_dt(const ReduceArgs& a, int op, hipStream_t s) {
 
 template <int DT, int OP, int P>
 hipError_t reduce_scatter_grid_p(const GridFoldArgs& a, hipStream_t s) {
-    const uint64_t tile = a.src_grid ? kGridFoldTileBytes : uint64_t(kGridOutBlock) * 16;
+    constexpr uint64_t tile = uint64_t(kGridTile);
     uint64_t tiles = 0;
     for (int c = 0; c < a.nchunks; c++) {
         const uint64_t n = (c + 1 == a.nchunks ? a.last_count : a.count) * (DT == kBF16 ? 2 : 4);
@@ -632,12 +593,7 @@ hipError_t reduce_scatter_grid_p(const GridFoldArgs& a, hipStream_t s) {
     }
     if (tiles == 0) return hipSuccess;
     if (tiles > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    if (a.src_grid)
-        k_reduce_scatter_srcgrid<DT, OP, P><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kWaveBlock, 0, s>>>(a);
-    else if (a.nt)
-        k_reduce_scatter_grid<DT, OP, P, true><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kGridOutBlock, 0, s>>>(a);
-    else
-        k_reduce_scatter_grid<DT, OP, P, false><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kGridOutBlock, 0, s>>>(a);
+    k_reduce_scatter_grid<DT, OP, P><<<dim3(unsigned(tiles), unsigned(a.nchunks)), kGridOutBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -39,13 +39,15 @@
  *    fast way; a two-shot AllReduce does the same for line-aligned buffers
  *    that share an offset within 1 KiB (its tiles then start on 1 KiB
  *    boundaries).  Folds over element-aligned buffers at offsets of their
- *    own (inputs and outputs apart, or rank by rank) tile over 128-byte
- *    lines (the inputs' where they share one offset and the outputs' vectors
- *    then start on lines, else each output's) and shift every vector into
- *    place from aligned loads: the ReduceScatter always, the AllReduce from
- *    P * S = 256 MiB (S the bytes per rank) on (as
- *    a ReduceScatter into each output's own chunk and a fan-out of the
- *    chunks); smaller AllReduces fold element by element.  The copy engines
+ *    own (inputs and outputs apart, or rank by rank), and ReduceScatters
+ *    whose chunks of the inputs do not all start on 128-byte lines, tile
+ *    over each output's 128-byte lines, load every input's lines whole and
+ *    shift them into place: the ReduceScatter always, the AllReduce from
+ *    P * S = 256 MiB (S the bytes per rank) on (as a ReduceScatter into
+ *    each output's own chunk and a fan-out of the chunks; 16-byte aligned
+ *    inputs off their lines take this form too where the two-shot form
+ *    pays); smaller AllReduces over buffers at offsets of their own fold
+ *    element by element.  The copy engines
  *    store whole 128-byte lines of every destination that does not start
  *    on one, built from aligned loads whatever the source offset (the
  *    fan-out when all destinations of a piece share one offset within a

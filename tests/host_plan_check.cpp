@@ -304,11 +304,9 @@ hipError_t launch_reduce_scatter_segs(const SegReduceScatterArgs& a, int dtype, 
 // elements in, count elements, last_count for the last chunk) folds into
 // dst[c], lead[c] bytes into its line.
 int g_grid_rs_launches = 0;
-int g_grid_rs_src_grid = -1;  // the last launch's mode
 hipError_t launch_reduce_scatter_grid(const GridFoldArgs& a, int dtype, int, hipStream_t) {
     g_launches++;
     g_grid_rs_launches++;
-    g_grid_rs_src_grid = a.src_grid;
     const uint64_t es = esize(dtype);
     CHECK(a.nranks >= 1 && a.nranks <= kMaxRanksHost && a.nchunks == a.nranks, "grid rs: %d ranks, %d chunks",
           a.nranks, a.nchunks);
@@ -318,21 +316,9 @@ hipError_t launch_reduce_scatter_grid(const GridFoldArgs& a, int dtype, int, hip
     for (int c = 0; c < a.nchunks; c++) {
         const uint64_t n = (c + 1 == a.nchunks ? a.last_count : a.count) * es;
         const uintptr_t d = reinterpret_cast<uintptr_t>(a.dst[c]);
-        if (a.src_grid) {
-            // every input at one offset within a line; lead is that offset at the
-            // chunk's start; the output then starts at most 16 bytes before a line
-            const uint64_t h = (d - a.lead[c]) & (kGridAlign - 1);
-            CHECK(h == 0 || h >= kGridAlign - 16, "grid rs (input grid): chunk %d output %llu bytes into a line", c,
-                  (unsigned long long)h);
-            for (int r = 0; r < a.nranks; r++) {
-                const uintptr_t s = reinterpret_cast<uintptr_t>(a.src[r]) + c * a.in_stride * es;
-                CHECK(a.lead[c] == (s & (kGridAlign - 1)), "grid rs (input grid): chunk %d lead %u, input %d at %llu mod 128",
-                      c, a.lead[c], r, (unsigned long long)(s & (kGridAlign - 1)));
-            }
-        } else {
-            CHECK(a.lead[c] == (d & (kGridAlign - 1)), "grid rs: chunk %d lead %u for an output at %llu mod 128", c,
-                  a.lead[c], (unsigned long long)(d & (kGridAlign - 1)));
-        }
+        // the tiles follow the output's lines: every store is a whole aligned vector
+        CHECK(a.lead[c] == (d & (kGridAlign - 1)), "grid rs: chunk %d lead %u for an output at %llu mod 128", c,
+              a.lead[c], (unsigned long long)(d & (kGridAlign - 1)));
         CHECK(d % es == 0, "grid rs: output %d not element-aligned", c);
         touch(a.dst[c], 0, n, true, "grid reduce_scatter write");
         for (int r = 0; r < a.nranks; r++) {
@@ -1088,6 +1074,13 @@ void two_shot() {
         {3, DT_BFLOAT16, 48 * M + 1, true, 0, 0, 0, 2, 1},        // in place, rank r 2r bytes off
         {5, DT_INT32, 16 * M + 7, false, 0, 16, 8, 4, 1},         // every buffer at an offset of its own
         {8, DT_BFLOAT16, 160 * M + 3, false, 0, 2, 0, 0, 3},      // 320 MiB: three 128 MiB windows
+        // vector-aligned inputs 16 bytes off their lines: the line grid where
+        // the two-shot form pays and P * S >= 256 MiB, else the vector forms
+        {8, DT_BFLOAT16, 64 * M, false, 0, 0, 16, 0, 1},          // 128 MiB per rank
+        {16, DT_FLOAT32, 4 * M, false, 0, 0, 16, 0, 1},           // 16 MiB at P=16: P * S = 256 MiB
+        {16, DT_FLOAT32, 3 * M, false, 1, 0, 16, 0, 0},           // 12 MiB at P=16: the vector two-shot
+        {8, DT_BFLOAT16, 160 * M, false, 0, 0, 16, 0, 3},         // 320 MiB: three windows on the grid
+        {4, DT_FLOAT32, 16 * M, false, 0, 0, 16, 0, 0},           // 64 MiB at P=4: one-shot
     };
     char* base = reinterpret_cast<char*>(uintptr_t(1) << 45);  // fake, never dereferenced
     for (const Case& c : cases) {
@@ -1156,19 +1149,22 @@ void grid_reduce_scatter() {
         size_t recvcount;
         size_t send_skew[4];
         size_t recv_skew[4];
-        int src_grid;
     };
     const Case cases[] = {
         // bf16, 2000-byte chunks (80 mod 128): inputs 2 bytes off, outputs 2 bytes before each chunk's input line
-        {4, DT_BFLOAT16, 1000, {2, 2, 2, 2}, {0, 80, 32, 112}, 1},
-        // the outputs 4 bytes past each chunk's input offset instead: the output grid
-        {4, DT_BFLOAT16, 1000, {2, 2, 2, 2}, {6, 86, 38, 118}, 0},
+        {4, DT_BFLOAT16, 1000, {2, 2, 2, 2}, {0, 80, 32, 112}},
+        // the outputs 4 bytes past each chunk's input offset instead
+        {4, DT_BFLOAT16, 1000, {2, 2, 2, 2}, {6, 86, 38, 118}},
         // fp32, inputs at two offsets (4000-byte chunks, 32 mod 128), outputs on their chunks' lines
-        {2, DT_FLOAT32, 1000, {0, 4}, {0, 32}, 0},
+        {2, DT_FLOAT32, 1000, {0, 4}, {0, 32}},
         // fp32, inputs 8 bytes off, outputs aligned, chunks of whole lines: 120 bytes into a line
-        {3, DT_FLOAT32, 4096 * 3, {8, 8, 8}, {0, 0, 0}, 1},
+        {3, DT_FLOAT32, 4096 * 3, {8, 8, 8}, {0, 0, 0}},
         // the same with chunks 20 bytes past whole lines: later chunks' outputs fall inside lines
-        {3, DT_FLOAT32, 4096 * 3 + 5, {8, 8, 8}, {0, 0, 0}, 0},
+        {3, DT_FLOAT32, 4096 * 3 + 5, {8, 8, 8}, {0, 0, 0}},
+        // vector-aligned inputs 16 bytes off their lines: the grid, not the vector kernel
+        {2, DT_FLOAT32, 4096, {16, 16}, {0, 0}},
+        // aligned buffers, chunks of 4000 bytes: later chunks' inputs off their lines
+        {2, DT_FLOAT32, 1000, {0, 0}, {0, 0}},
     };
     char* base = reinterpret_cast<char*>(uintptr_t(5) << 44);  // fake, never dereferenced
     for (const Case& c : cases) {
@@ -1182,11 +1178,11 @@ void grid_reduce_scatter() {
             recv[r] = base + (uint64_t(16 + r) << 33) + c.recv_skew[r];
             reg(recv[r], c.recvcount * es, true);
         }
-        dt::g_grid_rs_src_grid = -1;
+        const int before = dt::g_grid_rs_launches;
         expect(dt_reduce_scatter(send, recv, c.p, c.recvcount, c.dtype, DT_SUM, nullptr), DT_OK,
                "reduce_scatter over line grids");
-        CHECK(dt::g_grid_rs_src_grid == c.src_grid, "reduce_scatter P=%d: grid mode %d, expected %d", c.p,
-              dt::g_grid_rs_src_grid, c.src_grid);
+        CHECK(dt::g_grid_rs_launches == before + 1, "reduce_scatter P=%d: %d grid launches, expected one", c.p,
+              dt::g_grid_rs_launches - before);
     }
     g_bufs.clear();
 }

@@ -249,7 +249,7 @@ def test_reduce_scatter_shared_offset_peels(dt, p, dtype, m, off):
 
 
 # per-rank element offsets (mod 64) by rule name
-_RULES = {"0": lambda r: 0, "1": lambda r: 1, "2": lambda r: 2, "8": lambda r: 8, "r": lambda r: r,
+_RULES = {"0": lambda r: 0, "1": lambda r: 1, "2": lambda r: 2, "4": lambda r: 4, "8": lambda r: 8, "r": lambda r: r,
           "2r+1": lambda r: 2 * r + 1, "3r+1": lambda r: 3 * r + 1, "3r": lambda r: 3 * r, "5r": lambda r: 5 * r,
           "8r": lambda r: 8 * r}
 
@@ -273,8 +273,11 @@ def _placed(src, offsets):
     # the RS -> AG workload's size; inputs at offsets of their own, outputs aligned:
     # the line-grid ReduceScatter, then the fan-out on its aligned path
     (8, torch.bfloat16, 8192 * 8192, "r", "0", "sum", False),
-    # inputs 2 bytes off, outputs aligned: the input-grid ReduceScatter, then the aligned fan-out
+    # inputs 2 bytes off, outputs aligned: the line-grid ReduceScatter, then the aligned fan-out
     (8, torch.bfloat16, 8192 * 8192, "1", "0", "sum", False),
+    # vector-aligned inputs 16 bytes off their lines, past P * S = 256 MiB: the line grid, not the vector two-shot
+    (8, torch.bfloat16, 1 << 24, "8", "0", "sum", False),
+    (16, torch.float32, (1 << 22) + 4, "4", "0", "max", False),
     # outputs at offsets of their own too: the fan-out's byte path
     (8, torch.bfloat16, (1 << 24) + 5, "r", "3r+1", "sum", False),
     # outputs 4 bytes off, inputs aligned; ragged
@@ -311,7 +314,9 @@ def test_allreduce_offsets_of_their_own(dt, orc, p, dtype, n, send_off, recv_off
 
 @pytest.mark.parametrize("p,dtype,m,send_off,recv_off,op", [
     (8, torch.bfloat16, 8192 * 1024, "r", "2r+1", "sum"),   # the RS -> AG workload's size
-    (8, torch.bfloat16, 8192 * 1024, "1", "0", "sum"),      # inputs 2 bytes off, outputs aligned: the input grid
+    (8, torch.bfloat16, 8192 * 1024, "1", "0", "sum"),      # inputs 2 bytes off, outputs aligned
+    (8, torch.bfloat16, 1 << 20, "8", "0", "sum"),          # inputs 16 bytes off their lines: the grid, not the vector kernel
+    (4, torch.float32, 1000, "0", "0", "sum"),               # aligned, chunks of 4000 bytes: inputs off lines from chunk 1
     (4, torch.float32, (1 << 20) + 32, "2", "0", "max"),    # inputs 8 bytes off; chunks end inside a tile
     (8, torch.float32, 4096 + 8, "0", "1", "sum"),           # outputs 4 bytes off only
     (8, torch.bfloat16, 65536, "0", "8r", "sum"),            # outputs 16 bytes apart past their lines

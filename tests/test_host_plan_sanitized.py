@@ -108,17 +108,18 @@ MUTANTS = {
     # all-to-all blocks at a 16-byte boundary off their lines take the source-tiled path
     "a2a_aligned_off_line": ("const bool al = aligned16(from) && line_aligned(to);",
                              "const bool al = aligned16(from) && aligned16(to);"),
-    # the output-grid ReduceScatter takes each chunk's grid from the inputs
-    "grid_rs_lead_from_send": (": uint32_t(reinterpret_cast<uintptr_t>(out[r]) & (dt::kGridAlign - 1));",
-                               ": uint32_t(reinterpret_cast<uintptr_t>(send[r]) & (dt::kGridAlign - 1));"),
-    # the input-grid ReduceScatter takes every chunk's grid from the first chunk
-    "grid_rs_input_lead_without_stride": (
-        "g.lead[r] = g.src_grid ? uint32_t((s0 + r * stride_bytes) & (dt::kGridAlign - 1))",
-        "g.lead[r] = g.src_grid ? uint32_t(s0 & (dt::kGridAlign - 1))"),
-    # inputs at different offsets still take the input grid
-    "grid_rs_input_grid_for_mixed_inputs": (
-        "if ((reinterpret_cast<uintptr_t>(send[r]) & (dt::kGridAlign - 1)) != s0) g.src_grid = 0;",
-        "if (false) g.src_grid = 0;"),
+    # the line-grid ReduceScatter takes each chunk's grid from the inputs
+    "grid_rs_lead_from_send": ("g.lead[r] = uint32_t(reinterpret_cast<uintptr_t>(out[r]) & (dt::kGridAlign - 1));",
+                               "g.lead[r] = uint32_t(reinterpret_cast<uintptr_t>(send[r]) & (dt::kGridAlign - 1));"),
+    # vector-aligned AllReduce inputs off their lines keep the vector two-shot form
+    "allreduce_grid_ignores_input_lines": ("        lines = lines && line_aligned(send[r]);\n", "        lines = true;\n"),
+    # ReduceScatter inputs off their lines keep the vector kernel
+    "reduce_scatter_vec_ignores_input_lines": (
+        "vec = vec && aligned16(send[r]) && aligned16(recv[r]) && line_aligned(send[r]);",
+        "vec = vec && aligned16(send[r]) && aligned16(recv[r]);"),
+    # ReduceScatter chunks off the lines keep the vector kernel
+    "reduce_scatter_vec_ignores_chunk_lines": (
+        " && (recvcount * esize_of(dtype)) % dt::kGridAlign == 0;", ";"),
     # the line-grid two-shot AllReduce gives its last chunk a full chunk
     "grid_two_shot_last_chunk_full": ("            const size_t last = count - mce * size_t(nranks - 1);",
                                       "            const size_t last = mce;"),
