@@ -510,8 +510,8 @@ dt_status fan_out_launch(const void* const* src, const uint64_t* bytes, void* co
             a.shifted |= 1u << k;
             a.lead[k] = uint32_t(md) | uint32_t((reinterpret_cast<uintptr_t>(src[k]) - md) & 15u) << 16;
             tiles += dt::grid_tiles(bytes[k], md, tile_bytes);
-        } else {
-            tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;
+        } else {  // each destination over its own line grid: tiles for the deepest lead
+            tiles += bytes[k] ? dt::grid_tiles(bytes[k], dt::kGridAlign - 1, tile_bytes) : 0;
         }
         if ((tiles << a.split_log2) > 0x7FFFFFFFull) return fail(DT_ERR_ARG, "fan-out too large for one launch");
     }

@@ -11,9 +11,11 @@
 //
 // AllGather fans out: each source tile is read once and written to every
 // rank's output, (1 + P) bytes of HBM traffic per gathered byte.  Stores go
-// out as whole 128-byte lines of the destinations: a destination that does
-// not start on a line (even at a 16-byte boundary) takes tiles over its line
-// grid, each vector built from aligned loads of the source.
+// out as whole 128-byte lines of the destinations: destinations that do not
+// start on a line (even at a 16-byte boundary) take tiles over their line
+// grid, each vector built from aligned loads of the source; destinations
+// that share no offset within a line each take their own grid, their
+// vectors shifted out of the source lines staged in LDS.
 #include "dt_device.h"
 #include "dt_launch.h"
 
@@ -122,39 +124,61 @@ __global__ __launch_bounds__(BLOCK) void k_gather(GatherArgs a) {
                 }
             }
         }
-    } else if (part != 0) {
-        return;  // the byte path runs in the tile's first part only
     } else {
-        // Destinations at offsets of their own: each lane takes 16 bytes of
-        // the tile, loaded as one shifted vector (the window, as above), and
-        // stores them to every destination in the widest words that
-        // destination's alignment allows (4 or 2 bytes, else single bytes).
+        // Destinations at offsets of their own: each destination q tiles over
+        // its own line grid, tile b covering bytes [b0, b0 + kTile) of it,
+        // grid byte g being byte g - lead_q of the piece (lead_q = dsts[q]
+        // mod 128, so the host counts tiles for a lead of 127).  The piece
+        // bytes that any destination's tile b needs lie in [b0 - 127, b0 +
+        // kTile): the workgroup stages them once in LDS as aligned source
+        // vectors (through a window over the piece: nothing outside its
+        // aligned vectors is read), then each lane builds its vector for each
+        // destination of this part from two LDS vectors and one byte shift
+        // (uniform per destination) and stores it aligned, whole lines of
+        // the destination, or at the piece's two ends byte by byte.  The
+        // stage starts sm bytes before a vector boundary of the source, at
+        // piece byte b0 - 128 - sm, so the loads are aligned.
+        constexpr int V = U * BLOCK;  // vectors per tile
+        constexpr int SV = V + 9;     // staged: piece bytes [b0 - 128 - sm, b0 + kTile + 16 - sm)
+        __shared__ u32x4 stage[SV];
         const uint32_t sm = uint32_t(reinterpret_cast<uintptr_t>(src) & 15u);
         const int64_t bytes = int64_t(a.bytes[r]);
-        const LoadWindow w = load_window(src, bytes, int64_t(b0) - sm, int64_t(kTile) + 16);
+        const int64_t s_lo = int64_t(b0) - 128 - int64_t(sm);
+        const LoadWindow w = load_window(src, bytes, s_lo, int64_t(SV) * 16);
+        u32x4 y[U + 1];
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int64_t p0 = int64_t(b0) + int64_t(threadIdx.x + u * BLOCK) * 16;
-            if (p0 >= bytes) continue;
-            const u32x4 x = window_load_shifted<0>(w, p0 - int64_t(sm), sm);
-            const int m = int(bytes - p0 < 16 ? bytes - p0 : 16);
-            for (int q = 0; q < nr; q++) {
-                if (dsts[q] == src) continue;
-                char* d = static_cast<char*>(dsts[q]) + p0;
-                const uint32_t da = uint32_t(reinterpret_cast<uintptr_t>(d) & 3u);  // the same in every lane
-                int j = 0;  // bytes stored in words
-                if (da == 0) {
+        for (int u = 0; u <= U; u++) {
+            const int i = int(threadIdx.x) + u * BLOCK;
+            if (i < SV) y[u] = window_load<0>(w, s_lo + int64_t(i) * 16);
+        }
 #pragma unroll
-                    for (int k = 0; k < 4; k++)
-                        if (4 * k + 4 <= m) *reinterpret_cast<uint32_t*>(d + 4 * k) = x[k];
-                    j = m & ~3;
-                } else if (da == 2) {
+        for (int u = 0; u <= U; u++) {
+            const int i = int(threadIdx.x) + u * BLOCK;
+            if (i < SV) stage[i] = y[u];
+        }
+        __syncthreads();
 #pragma unroll
-                    for (int k = 0; k < 8; k++)
-                        if (2 * k + 2 <= m) *reinterpret_cast<uint16_t*>(d + 2 * k) = uint16_t(x[k >> 1] >> ((k & 1) * 16));
-                    j = m & ~1;
+        for (int q = 0; q < PMAX; q++) {
+            if (!(q < nr && (q & (nparts - 1)) == part && dsts[q] != src)) continue;
+            char* d = static_cast<char*>(dsts[q]);
+            const int64_t lead = int64_t(reinterpret_cast<uintptr_t>(d) & uint64_t(kGridAlign - 1));
+            const rsrc_t out = make_rsrc(d - lead + b0, uint32_t(kTile));
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int l = int(threadIdx.x) + u * BLOCK;
+                const int64_t s0 = int64_t(b0) + int64_t(l) * 16 - lead;  // the piece byte of this grid vector
+                if (s0 + 16 <= 0 || s0 >= bytes) continue;
+                const uint32_t o = uint32_t(int64_t(l) * 16 - lead + 128 + int64_t(sm));  // 1 .. 16 V + 127
+                const uint32_t s = o & 15u;
+                const u32x4 lo = stage[o >> 4];
+                const u32x4 x = s != 0 ? funnel16(lo, stage[(o >> 4) + 1], s) : lo;
+                if (s0 >= 0 && s0 + 16 <= bytes) {
+                    bstore16<kPolNT | kPolDevice>(out, uint32_t(l) * 16, x);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 16; j++)
+                        if (s0 + j >= 0 && s0 + j < bytes) d[s0 + j] = vec_byte(x, j);
                 }
-                for (; j < m; j++) d[j] = vec_byte(x, j);
             }
         }
     }

@@ -50,8 +50,8 @@
  *    element by element.  The copy engines
  *    store whole 128-byte lines of every destination that does not start
  *    on one, built from aligned loads whatever the source offset (the
- *    fan-out when all destinations of a piece share one offset within a
- *    line; otherwise its bytes go out one by one).  Every path gives the
+ *    fan-out over each destination's own line grid when the destinations
+ *    of a piece do not share one offset within a line).  Every path gives the
  *    same bits.
  */
 #ifndef DT_H

@@ -361,7 +361,10 @@ uint64_t gather_tiles(const GatherArgs& a, int r) {
         return ceil_div(lead + a.bytes[r], a.tile_bytes);
     }
     CHECK(a.lead[r] == 0, "gather: lead %u on piece %d that is not shifted", a.lead[r], r);
-    return ceil_div(a.bytes[r], a.tile_bytes);
+    if ((a.aligned >> r) & 1u) return ceil_div(a.bytes[r], a.tile_bytes);
+    // destinations at offsets of their own: each over its own line grid,
+    // grid byte g being piece byte g - (dst mod 128); tiles for a lead of 127
+    return a.bytes[r] ? ceil_div(kGridAlign - 1 + a.bytes[r], a.tile_bytes) : 0;
 }
 
 hipError_t launch_gather_touch(const GatherArgs& a, uint32_t tiles, hipStream_t) {

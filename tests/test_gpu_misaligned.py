@@ -101,6 +101,49 @@ def test_uneven_all_gather_odd_bf16_counts(dt, orc):
         assert np.array_equal(to_np(ys[q].t), want), f"output {q}"
 
 
+@pytest.mark.parametrize("p,dtype,counts,recv_off,src_off,in_place", [
+    # equal 16 MiB bf16 shards, output q 2(3q+1) bytes off: every destination on a line grid of its own
+    (8, torch.bfloat16, [8 << 20] * 8, "3r+1", "0", False),
+    # uneven fp32 pieces, sources off alignment too, pieces shorter than a vector and than a line
+    (5, torch.float32, [1, 7, 33, 100003, 0], "r", "2r+1", False),
+    (3, torch.int32, [4096 * 3 + 5, 1, 65537], "3r", "1", False),
+    # in place: each rank's piece already in its own slot, the slots at offsets of their own
+    (4, torch.bfloat16, [300001, 299999, 300003, 300000], "2r+1", "0", True),
+    # 384 MiB of sources: the windowed fan-out with its read passes
+    (8, torch.bfloat16, [24 << 20] * 8, "r", "0", False),
+])
+def test_all_gather_outputs_offsets_of_their_own(dt, orc, p, dtype, counts, recv_off, src_off, in_place):
+    """AllGather whose outputs sit at offsets of their own, so no piece's
+    destinations share a line offset: each destination takes the piece over
+    its own line grid, every vector shifted out of the source lines staged
+    in LDS."""
+    note(f"all_gather outputs at offsets of their own P={p} {dtype} counts={counts[:3]}.. recv {recv_off} "
+         f"src {src_off} in_place={in_place}")
+    total = sum(counts)
+    src = []
+    for k, c in enumerate(counts):
+        if dtype == torch.bfloat16:
+            src.append(synth.normal_ranks(1, (c,), seed=90 + k, device="cuda", dtype=dtype)[0])
+        elif dtype == torch.int32:
+            src.append(synth.int_ranks(1, c, seed=90 + k, device="cuda")[0])
+        else:
+            src.append(synth.uniform_ranks(1, c, seed=90 + k, device="cuda")[0])
+    ys = [Guarded(total, dtype, offset_elems=o).poison() for o in _offsets(recv_off, p)]
+    starts = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    if in_place:
+        for k in range(p):
+            ys[k].t[starts[k]:starts[k + 1]].copy_(src[k])
+        xs = [ys[k].t[starts[k]:starts[k + 1]] for k in range(p)]
+    else:
+        xs = [g.t for g in _placed(src, _offsets(src_off, p))]
+    dt.dt_all_gather(xs, [g.t for g in ys])
+    torch.cuda.synchronize()
+    want = orc.all_gather([to_np(x) for x in src])
+    for q in range(p):
+        ys[q].check()
+        assert np.array_equal(to_np(ys[q].t), want[q]), f"output {q}"
+
+
 @pytest.mark.parametrize("dtype,off_send,off_recv", [(torch.bfloat16, 0, 3), (torch.float32, 1, 2), (torch.int32, 3, 0)])
 def test_all_to_all_odd_splits(dt, orc, dtype, off_send, off_recv):
     """A split matrix of odd element counts: blocks start at every offset

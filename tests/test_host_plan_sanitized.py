@@ -120,6 +120,10 @@ MUTANTS = {
     # ReduceScatter chunks off the lines keep the vector kernel
     "reduce_scatter_vec_ignores_chunk_lines": (
         " && (recvcount * esize_of(dtype)) % dt::kGridAlign == 0;", ";"),
+    # a fan-out to destinations at offsets of their own counts its tiles over the source, not the deepest line grid
+    "gather_own_offsets_source_tiles": (
+        "tiles += bytes[k] ? dt::grid_tiles(bytes[k], dt::kGridAlign - 1, tile_bytes) : 0;",
+        "tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;"),
     # the line-grid two-shot AllReduce gives its last chunk a full chunk
     "grid_two_shot_last_chunk_full": ("            const size_t last = count - mce * size_t(nranks - 1);",
                                       "            const size_t last = mce;"),
