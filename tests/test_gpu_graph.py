@@ -151,9 +151,10 @@ def test_graph_replays_large_argument_tables(dt):
 def test_graph_replays_offsets_of_their_own(dt):
     """Buffers at offsets of their own captured in a graph: the line-grid
     AllReduce (P=8 bf16, 32 MiB + 6 bytes per rank, inputs 2 bytes off,
-    outputs at 2(3q+1) bytes: the output-grid ReduceScatter and the fan-out
-    to destinations at offsets of their own), the input-grid ReduceScatter
-    (inputs 8 bytes off, outputs aligned) and the odd-count AllGather (the
+    outputs at 2(3q+1) bytes: the staged line-grid ReduceScatter and the
+    fan-out to destinations at offsets of their own), the line-grid
+    ReduceScatter with inputs 8 bytes off and outputs aligned, and the
+    odd-count AllGather (the
     line-grid fan-out with its windowed piece ends); every replay checked
     against the oracle on that replay's inputs."""
     orc = oracle.get()
@@ -181,7 +182,7 @@ def test_graph_replays_offsets_of_their_own(dt):
         work()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    note("graph capture of line-grid allreduce, input-grid reduce_scatter, odd-count all_gather")
+    note("graph capture of line-grid allreduce, line-grid reduce_scatter, odd-count all_gather")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         work()

@@ -200,8 +200,8 @@ def test_random_shared_offsets(dt, orc, case):
 def test_random_large_offsets(dt, orc, case):
     """AllReduce and ReduceScatter past the line-grid two-shot threshold
     (P * S of 256-512 MiB) over buffers at offsets of their own: even cases
-    put every input at one offset (the input-grid ReduceScatter where the
-    outputs' vectors then start on lines), odd cases draw every offset."""
+    put every input at one offset, odd cases draw every offset; all take the
+    staged line-grid ReduceScatter."""
     rng = np.random.default_rng(9000 + case)
     dtype = ["f32", "bf16", "i32"][case % 3]
     op = ["sum", "max", "min", "avg"][int(rng.integers(0, 4))]
