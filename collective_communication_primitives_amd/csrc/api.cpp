@@ -221,13 +221,19 @@ dt_status reduce_scatter_grid(const void* const* send, void* const* out, int nra
 // Whether an AllReduce over element-aligned buffers that share no offset
 // takes the two-shot form over line grids (the grid ReduceScatter into each
 // output's own chunk, then the fan-out) rather than the element kernel: once
-// its footprint, 2 * P * S bytes, no longer fits the Infinity Cache.  Graph
-// replays, outputs 2 bytes off and inputs aligned (or the reverse): P=8 bf16
-// at 16 MiB per rank 46 us on the element kernel against 50-52 us, at 32 MiB
-// 117-153 against 93-96 us; P=4 fp32 at 32 MiB 43 against 46-58 us, at 64 MiB
-// 105-121 against 90-119 us.
+// its footprint, 2 * P * S bytes, has clearly left the 256 MB Infinity Cache.
+// Graph replays, outputs 2 bytes off and inputs aligned (or the reverse),
+// element kernel against the two-shot form: at P * S = 160 MiB, P=6 fp32
+// 57-60 against 55-58 us, P=8 bf16 79-88 against 62 us, P=10 bf16 70-77
+// against 64-70 us, P=12 bf16 76-82 against 75-81 us; but P=4 fp32 63-66
+// against 66-68 us and P=16 fp32 67-68 against 67-73 us, which only break
+// even from 192-240 MiB; at P * S = 128 MiB the element kernel wins at every
+// rank count measured (P=8 bf16 47 against 52-54 us, P=16 fp32 43 against
+// 54-61 us).
 bool grid_two_shot_pays(int nranks, uint64_t bytes_per_rank) {
-    return uint64_t(nranks) * bytes_per_rank >= (256ull << 20);
+    const uint64_t ps = uint64_t(nranks) * bytes_per_rank;
+    if (nranks >= 6 && nranks <= 12) return ps >= (160ull << 20);
+    return ps >= (256ull << 20);
 }
 
 dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, size_t count, dt_dtype dtype,

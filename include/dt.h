@@ -43,7 +43,8 @@
  *    whose chunks of the inputs do not all start on 128-byte lines, tile
  *    over each output's 128-byte lines, load every input's lines whole and
  *    shift them into place: the ReduceScatter always, the AllReduce from
- *    P * S = 256 MiB (S the bytes per rank) on (as a ReduceScatter into
+ *    P * S = 160 MiB for 6 <= P <= 12, 256 MiB otherwise (S the bytes per
+ *    rank) on (as a ReduceScatter into
  *    each output's own chunk and a fan-out of the chunks; 16-byte aligned
  *    inputs off their lines take this form too where the two-shot form
  *    pays); smaller AllReduces over buffers at offsets of their own fold
@@ -99,7 +100,8 @@ typedef enum {
  * AllReduce of its own in the two-shot form, so the window's chunks are
  * still in the Infinity Cache when they fan out.  Buffers at offsets of
  * their own take the two-shot form over line grids from nranks * count *
- * element size = 256 MiB (see the alignment convention above).  All forms
+ * element size = 160 MiB for 6 <= P <= 12, 256 MiB otherwise (see the
+ * alignment convention above).  All forms
  * fold in the
  * same order and give identical bits.  In place is allowed (send[r] ==
  * recv[r]); any other overlap of a recv buffer with a send or recv buffer

@@ -1072,7 +1072,13 @@ void two_shot() {
         // offsets that differ between inputs and outputs or between ranks:
         // the line-grid two-shot form from P * S = 256 MiB, window by window
         {8, DT_BFLOAT16, 16 * M + 5, false, 0, 0, 2, 0, 1},       // inputs 2 bytes off, 32 MiB + 10 B
-        {8, DT_BFLOAT16, 16 * M - 8, false, 0, 0, 2, 0, 0},       // just below: the element kernel
+        {8, DT_BFLOAT16, 10 * M, false, 0, 0, 2, 0, 1},           // P * S = 160 MiB: the edge at P = 6-12
+        {8, DT_BFLOAT16, 10 * M - 8, false, 0, 0, 2, 0, 0},       // just below: the element kernel
+        {12, DT_BFLOAT16, 6 * M + 3, false, 0, 0, 2, 0, 0},       // P=12, 144 MiB: the element kernel
+        {6, DT_FLOAT32, 7 * M, false, 0, 0, 4, 0, 1},             // P=6, 168 MiB
+        {4, DT_FLOAT32, 12 * M, false, 0, 0, 4, 0, 0},            // P=4, 192 MiB: the element kernel
+        {4, DT_FLOAT32, 16 * M, false, 0, 0, 4, 0, 1},            // P=4, 256 MiB
+        {16, DT_FLOAT32, 3 * M, false, 0, 0, 4, 0, 0},            // P=16, 192 MiB: the element kernel
         {16, DT_FLOAT32, 16 * M + 3, false, 0, 4, 0, 0, 1},       // outputs 4 bytes off
         {3, DT_BFLOAT16, 48 * M + 1, true, 0, 0, 0, 2, 1},        // in place, rank r 2r bytes off
         {5, DT_INT32, 16 * M + 7, false, 0, 16, 8, 4, 1},         // every buffer at an offset of its own

@@ -330,8 +330,12 @@ def _placed(src, offsets):
     (3, torch.bfloat16, (1 << 26) + 1, "2r+1", "r", "min", False),
     (5, torch.int32, (1 << 24) + 1, "r", "2", "max", False),
     (6, torch.float32, 1 << 24, "r", "r", "avg", True),    # in place, every rank at its own offset
-    # below the line-grid threshold (P * S = 256 MiB): the element kernel
+    # P * S = 160 MiB at P = 6-12: the line-grid two-shot form
+    (8, torch.bfloat16, (10 << 20) + 3, "r", "0", "sum", False),
+    (6, torch.float32, 7 << 20, "0", "1", "max", False),
+    # below the line-grid threshold (P * S = 160 MiB at P = 6-12, else 256 MiB): the element kernel
     (8, torch.bfloat16, (1 << 23) + 3, "r", "0", "sum", False),
+    (16, torch.float32, 3 << 20, "0", "1", "sum", False),
     (4, torch.bfloat16, 300001, "r", "0", "sum", False),
     (4, torch.float32, 1000, "r", "0", "sum", False),
 ])

@@ -124,6 +124,9 @@ MUTANTS = {
     "gather_own_offsets_source_tiles": (
         "tiles += bytes[k] ? dt::grid_tiles(bytes[k], dt::kGridAlign - 1, tile_bytes) : 0;",
         "tiles += (bytes[k] + tile_bytes - 1) / tile_bytes;"),
+    # the 160 MiB line-grid threshold applied at every rank count
+    "grid_two_shot_band_all_ranks": ("    if (nranks >= 6 && nranks <= 12) return ps >= (160ull << 20);",
+                                     "    return ps >= (160ull << 20);"),
     # the line-grid two-shot AllReduce gives its last chunk a full chunk
     "grid_two_shot_last_chunk_full": ("            const size_t last = count - mce * size_t(nranks - 1);",
                                       "            const size_t last = mce;"),
