@@ -451,6 +451,9 @@ def configs(dt, torch, steps: int, warmup: int) -> dict:
     measure("c2_allreduce_misaligned_p8_bf16", lambda: dt.dt_allreduce(xs, ys), 2 * P * n * 2, per_graph=4)
     out["c2_allreduce_misaligned_p8_bf16"]["note"] = "every buffer 2 bytes past 16-byte alignment"
     xs = [b[:n] for b in base]
+    measure("c2_allreduce_outputs_misaligned_p8_bf16", lambda: dt.dt_allreduce(xs, ys), 2 * P * n * 2, per_graph=4)
+    out["c2_allreduce_outputs_misaligned_p8_bf16"]["note"] = \
+        "inputs aligned, outputs 2 bytes past 16-byte alignment: the line-grid two-shot form"
     ro = [torch.empty(n // P + 8, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
     rs_out = [r[1:n // P + 1] for r in ro]
     measure("c2_reduce_scatter_outputs_misaligned_p8_bf16", lambda: dt.dt_reduce_scatter(xs, rs_out),
