@@ -316,8 +316,17 @@ dt_status allreduce_one(const void* const* send, void* const* recv, int nranks, 
             return fan_out(own, counts, table, nranks, es, stream, "allreduce (all_gather) launch");
         }
     }
+    // The one-shot vector kernel stores whole 16-byte vectors to every output;
+    // outputs 16, 32 or 48 bytes into a 64-byte half line make each wave's
+    // stores split lines unevenly, and the element kernel is faster there
+    // (graph replays, outputs 16 bytes off: P=8 bf16 256 KiB / 1 / 16 MiB per
+    // rank 4.4 / 5.5 / 51.4 -> 2.6 / 4.2 / 45.8 us, P=16 fp32 256 KiB / 1 / 4
+    // MiB 5.9 / 8.1 / 27.3 -> 2.9 / 6.2 / 23.0 us, P=4 fp32 4 / 16 MiB 6.5 /
+    // 24.5 -> 5.9 / 21.8 us; at 64 bytes off the two are even).
+    bool halves = true;
+    for (int r = 0; r < nranks; r++) halves = halves && (reinterpret_cast<uintptr_t>(recv[r]) & 63u) == 0;
     size_t body = 0;
-    if (vec) {
+    if (vec && halves) {
         a.first = 0;
         a.count = count / v;
         body = a.count * v;

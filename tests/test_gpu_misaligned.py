@@ -336,6 +336,10 @@ def _placed(src, offsets):
     # below the line-grid threshold (P * S = 160 MiB at P = 6-12, else 256 MiB): the element kernel
     (8, torch.bfloat16, (1 << 23) + 3, "r", "0", "sum", False),
     (16, torch.float32, 3 << 20, "0", "1", "sum", False),
+    # vector-aligned outputs 16 bytes into their lines at one-shot sizes: the element kernel
+    (8, torch.bfloat16, (1 << 20) + 8, "0", "8", "sum", False),
+    (16, torch.float32, 1 << 18, "0", "4", "max", False),
+    (4, torch.float32, (1 << 22) + 4, "r", "4", "avg", False),
     (4, torch.bfloat16, 300001, "r", "0", "sum", False),
     (4, torch.float32, 1000, "r", "0", "sum", False),
 ])
