@@ -375,6 +375,11 @@ def test_allreduce_offsets_of_their_own(dt, orc, p, dtype, n, send_off, recv_off
     (7, torch.int32, 12345, "3r", "r", "min"),
     (2, torch.bfloat16, 3, "1", "0", "avg"),                 # shorter than one vector
     (1, torch.float32, 777, "1", "2", "sum"),                # one rank: a copy
+    # chunks of many tiles, so the staged interior tiles run at these rank counts
+    (16, torch.float32, (1 << 18) + 5, "r", "3r+1", "sum"),
+    (1, torch.bfloat16, (1 << 20) + 3, "1", "2", "max"),
+    (3, torch.int32, 100003, "3r", "5r", "min"),
+    (12, torch.bfloat16, (1 << 19) + 7, "2r+1", "0", "avg"),
 ])
 def test_reduce_scatter_offsets_of_their_own(dt, orc, p, dtype, m, send_off, recv_off, op):
     """ReduceScatter over buffers whose offsets differ: the line-grid kernel
