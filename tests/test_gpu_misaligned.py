@@ -111,6 +111,10 @@ def test_uneven_all_gather_odd_bf16_counts(dt, orc):
     (4, torch.bfloat16, [300001, 299999, 300003, 300000], "2r+1", "0", True),
     # 384 MiB of sources: the windowed fan-out with its read passes
     (8, torch.bfloat16, [24 << 20] * 8, "r", "0", False),
+    # from 9 ranks on two workgroups share a tile, each staging the source for its half of the destinations
+    (16, torch.bfloat16, [(1 << 18) + k for k in range(16)], "3r+1", "0", False),
+    (12, torch.float32, [100000 + 7 * k for k in range(12)], "r", "3r", False),
+    (2, torch.int32, [1 << 20, 5], "1", "2r+1", False),
 ])
 def test_all_gather_outputs_offsets_of_their_own(dt, orc, p, dtype, counts, recv_off, src_off, in_place):
     """AllGather whose outputs sit at offsets of their own, so no piece's
